@@ -1,0 +1,428 @@
+"""CPU oracle of the FastMKA layer forward (prefill and decode).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import or call this module.  The
+HIP library never calls it, and it shares no code with the HIP library: the
+two meet only in the seeded input arrays of ``route_kv_memory_amd.inputs``.
+
+Plain NumPy in float64 throughout.  Inputs are the exact values the GPU
+receives (bf16 workloads: already rounded to bf16), widened to float64.
+Each function is the definition written out, in the order the pages give it;
+library primitives (matmul, erf, sort) are the only helpers.
+
+Sources (the two pages about the method):
+  * "MKA reading note" -- Paper-Notes page "MKA: Memory-Keyed Attention for
+    Efficient Long-Context Reasoning" (method sections 1-4).
+  * "MKA abstract page" -- the paper's landing page of the same title
+    (abstract, Tables 1-11 and their captions).
+
+Where the pages leave a step open, the reading taken is stated at the
+function.  The fixed readings: L2 is an exponential moving average with a
+stated decay; L3 is SimHash of past complete-block means, keyed by the
+SimHash of L2[t], keeping the top-R blocks by Hamming distance with ties
+broken towards the most recent block.
+
+Parity pins: every function here is pinned by a test in
+``tests/test_oracle_pins.py`` (closed forms, special cases, brute force on
+tiny inputs, invariants).  The composite ``prefill``/``decode`` with general
+router weights and non-empty L3 has no end-to-end worked example on the
+pages; it rests on its pinned parts plus the special cases (one-hot router
+equals causal GQA attention, decode continues prefill, causality) -- beyond
+those it is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import erf as _erf
+
+__all__ = [
+    "q_proj", "gelu", "router", "ema", "block_means", "simhash", "retrieve",
+    "l3_mean", "fuse", "kv_proj", "attention", "attention_online", "prefill",
+    "DecodeState", "decode_init", "decode_init_from_prefill", "decode_step",
+]
+
+_SQRT2 = math.sqrt(2.0)
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# Router: lambda = softmax(MLP(q)), one 3-vector per token and layer.
+# MKA reading note, section 2 (dynamic routing gate).
+# --------------------------------------------------------------------------
+
+def q_proj(x, w_q):
+    """Q = X W_q (no bias, no rotary encoding).  ``w_q`` is stored [out, in].
+
+    Reading: the "q" fed to the router is this same query projection of the
+    token hidden (the note introduces q per token and uses its per-head slices
+    q_h as attention queries); it cannot be taken from the fused input, since
+    the router output is what forms the fused input.
+    """
+    return _f64(x) @ _f64(w_q).T
+
+
+def gelu(z):
+    """Exact GELU, z * Phi(z) = z/2 * (1 + erf(z / sqrt 2))."""
+    z = _f64(z)
+    return 0.5 * z * (1.0 + _erf(z / _SQRT2))
+
+
+def _softmax(z):
+    z = _f64(z)
+    e = np.exp(z - z.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def router(q, w_r1, w_r2):
+    """lambda = softmax(GELU(q W_r1) W_r2) over the three memory tiers.
+
+    MKA reading note, section 2: a learned MLP of the query followed by a
+    softmax gives lambda in R^{B x S x 3}, per token and per layer.  Reading:
+    a two-layer MLP with an exact GELU between the layers and no biases.
+    Output [..., 3]; tier 0 = L1, 1 = L2, 2 = L3.
+    """
+    return _softmax(gelu(_f64(q) @ _f64(w_r1).T) @ _f64(w_r2).T)
+
+
+# --------------------------------------------------------------------------
+# L2 session memory: causal summary of the prefix.
+# MKA reading note, section 1 (three-tier memory; M2[t] = Summary(X[:, 1:t])).
+# --------------------------------------------------------------------------
+
+def ema(x, beta, state=None):
+    """Exponential moving average along the sequence axis.
+
+    s_{-1} = state (zeros if None); s_t = beta * s_{t-1} + (1 - beta) * x_t;
+    L2[t] = s_t.  The note allows "a low-rank summary or an EMA"; the EMA is
+    the reading taken.  The prefix includes token t itself (the note's
+    X[:, 1:t] in 1-based indexing), which uses no future token.
+
+    x: [B, N, D].  Returns (L2 [B, N, D], final state [B, D]).
+    """
+    x = _f64(x)
+    B, N, D = x.shape
+    s = np.zeros((B, D)) if state is None else _f64(state).copy()
+    out = np.empty((B, N, D))
+    for t in range(N):
+        s = beta * s + (1.0 - beta) * x[:, t]
+        out[:, t] = s
+    return out, s
+
+
+# --------------------------------------------------------------------------
+# L3 long-term memory: hashed retrieval of R past blocks.
+# MKA reading note, section 1 (vectorised hash index over past blocks,
+# recalling R << T blocks) and section 4 (blockwise evaluation);
+# MKA abstract page, Table 8 caption (R = 8 retrieved chunks per query).
+# --------------------------------------------------------------------------
+
+def block_means(x, block):
+    """Mean of the token hiddens over every complete block of ``block`` tokens.
+
+    Reading: blocks are fixed-size runs of tokens (the pages' content-defined
+    chunking is not specified), and a block is summarised by the mean of its
+    raw token hiddens, so that L3 lives in d_model space like L1 and L2.
+    x: [B, N, D] -> [B, N // block, D].
+    """
+    x = _f64(x)
+    B, N, D = x.shape
+    nb = N // block
+    return x[:, : nb * block].reshape(B, nb, block, D).mean(axis=2)
+
+
+def simhash(v, proj):
+    """SimHash code of each row of ``v`` against the hyperplanes in ``proj``.
+
+    p = v . proj_j for each hyperplane j; bit j of the code is 1 iff p_j > 0
+    (p_j = 0 gives 0).  proj: [nbits, D] with nbits <= 64.
+    Returns (codes uint64 [...], |p| [..., nbits]).
+    """
+    p = _f64(v) @ _f64(proj).T
+    nbits = p.shape[-1]
+    if nbits > 64:
+        raise ValueError("at most 64 hash bits")
+    bits = (p > 0).astype(np.uint64)
+    weights = np.left_shift(np.uint64(1), np.arange(nbits, dtype=np.uint64))
+    codes = (bits * weights).sum(axis=-1, dtype=np.uint64)
+    return codes, np.abs(p)
+
+
+def _popcount64(a):
+    a = np.asarray(a, dtype=np.uint64)
+    return np.bitwise_count(a).astype(np.int64)
+
+
+def retrieve(keys, block_hash, positions, block, top_r):
+    """Top-R past blocks for each token, by Hamming distance of SimHash codes.
+
+    For the token at position t, the eligible blocks are b < floor(t / block):
+    the complete blocks strictly before t's own block (t's own block is the
+    local window that L1 covers).  They are ranked by (popcount(key_t xor
+    hash_b) ascending, b descending) -- equal distances go to the most recent
+    block -- and the first min(R, #eligible) are kept, in rank order; the rest
+    of the R slots hold -1.
+
+    keys: [B, n] uint64 for tokens at ``positions`` [n]; block_hash [B, nb].
+    Returns idx int32 [B, n, R].
+    """
+    keys = np.asarray(keys, dtype=np.uint64)
+    block_hash = np.asarray(block_hash, dtype=np.uint64)
+    positions = np.asarray(positions, dtype=np.int64)
+    B, n = keys.shape
+    nb = block_hash.shape[1]
+    out = np.full((B, n, top_r), -1, dtype=np.int32)
+    for b in range(B):
+        for i in range(n):
+            ne = int(positions[i]) // block
+            if ne > nb:
+                raise ValueError("block index is missing eligible blocks")
+            if ne == 0:
+                continue
+            cand = np.arange(ne, dtype=np.int64)
+            dist = _popcount64(np.bitwise_xor(block_hash[b, :ne], keys[b, i]))
+            order = np.lexsort((-cand, dist))  # primary: dist asc; then b desc
+            sel = cand[order][:top_r]
+            out[b, i, : len(sel)] = sel
+    return out
+
+
+def l3_mean(means, idx):
+    """L3[t] = mean of the retrieved block means (zero when none is eligible).
+
+    means [B, nb, D]; idx [B, n, R] with -1 padding -> [B, n, D].
+    """
+    means = _f64(means)
+    B, n, R = idx.shape
+    out = np.zeros((B, n, means.shape[2]))
+    for b in range(B):
+        for i in range(n):
+            sel = idx[b, i][idx[b, i] >= 0]
+            if len(sel):
+                out[b, i] = means[b, sel].mean(axis=0)
+    return out
+
+
+# --------------------------------------------------------------------------
+# FastMKA: fuse the tiers before attention, project K and V from the fusion.
+# MKA reading note, section 3 (X_fused = sum_l lambda_l * L_l; K, V =
+# X_fused W_k, X_fused W_v; one causal attention; the fused K/V is cached);
+# MKA abstract page, abstract ("broadcast-routed": lambda is a per-token
+# scalar per tier, broadcast over d_model).
+# --------------------------------------------------------------------------
+
+def fuse(lam, l1, l2, l3):
+    """X_fused = lambda_1 L1 + lambda_2 L2 + lambda_3 L3, lambda broadcast over D.
+
+    L1 is the token's own hidden x_t.
+    """
+    lam = _f64(lam)
+    return lam[..., 0:1] * _f64(l1) + lam[..., 1:2] * _f64(l2) + lam[..., 2:3] * _f64(l3)
+
+
+def kv_proj(x_fused, w_k, w_v, n_kv_heads):
+    """K = X_fused W_k, V = X_fused W_v, returned head-major [B, G, n, dh]."""
+    xf = _f64(x_fused)
+    B, n, _ = xf.shape
+    k = xf @ _f64(w_k).T
+    v = xf @ _f64(w_v).T
+    dh = k.shape[-1] // n_kv_heads
+    k = k.reshape(B, n, n_kv_heads, dh).transpose(0, 2, 1, 3)
+    v = v.reshape(B, n, n_kv_heads, dh).transpose(0, 2, 1, 3)
+    return k, v
+
+
+# --------------------------------------------------------------------------
+# One standard causal attention over the fused K/V.
+# MKA reading note, section 3 (single attention path) and section 4 (online
+# max-shift); models are GQA (reading note, experimental setup).
+# --------------------------------------------------------------------------
+
+def _group_of(h, n_heads, n_kv_heads):
+    # Contiguous groups: query heads [g*H/G, (g+1)*H/G) share KV head g.
+    return h // (n_heads // n_kv_heads)
+
+
+def attention(q, k, v, positions, n_kv_heads):
+    """Causal GQA attention, explicit scores and a two-pass softmax.
+
+    O[t, h] = sum_{j <= t} softmax_j(q_{t,h} . k_{j,g(h)} / sqrt(dh)) v_{j,g(h)}.
+    The 1/sqrt(dh) scale is that of standard attention (the note's formula
+    omits it); the mask keeps j <= t, the token itself included.
+
+    q: [B, n, H, dh] for query tokens at ``positions`` [n];
+    k, v: [B, G, T, dh] with T > max(positions).  Returns [B, n, H, dh].
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, n, H, dh = q.shape
+    positions = np.asarray(positions, dtype=np.int64)
+    T = int(positions.max()) + 1
+    scale = 1.0 / math.sqrt(dh)
+    out = np.empty((B, n, H, dh))
+    future = np.arange(T)[None, :] > positions[:, None]  # [n, T]
+    for b in range(B):
+        for h in range(H):
+            g = _group_of(h, H, n_kv_heads)
+            s = (q[b, :, h] @ k[b, g, :T].T) * scale
+            s[future] = -np.inf
+            m = s.max(axis=1, keepdims=True)
+            p = np.exp(s - m)
+            out[b, :, h] = (p @ v[b, g, :T]) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def attention_online(q, k, v, positions, n_kv_heads, tile=64):
+    """The same attention evaluated key tile by key tile with the online max-shift.
+
+    MKA reading note, section 4: the running maximum mu is updated tile by
+    tile, and the running numerator and denominator are rescaled by
+    exp(mu_old - mu_new) whenever it grows.  Used to cross-check
+    ``attention``; shares none of its code.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, n, H, dh = q.shape
+    positions = np.asarray(positions, dtype=np.int64)
+    scale = 1.0 / math.sqrt(dh)
+    out = np.empty((B, n, H, dh))
+    for b in range(B):
+        for h in range(H):
+            g = _group_of(h, H, n_kv_heads)
+            for i in range(n):
+                t = int(positions[i])
+                mu = -np.inf
+                den = 0.0
+                num = np.zeros(dh)
+                for j0 in range(0, t + 1, tile):
+                    j1 = min(j0 + tile, t + 1)
+                    s = (k[b, g, j0:j1] @ q[b, i, h]) * scale
+                    mu_new = max(mu, float(s.max()))
+                    corr = math.exp(mu - mu_new) if mu != -np.inf else 0.0
+                    p = np.exp(s - mu_new)
+                    den = den * corr + p.sum()
+                    num = num * corr + p @ v[b, g, j0:j1]
+                    mu = mu_new
+                out[b, i, h] = num / den
+    return out
+
+
+# --------------------------------------------------------------------------
+# Whole layer
+# --------------------------------------------------------------------------
+
+def prefill(x, w_q, w_k, w_v, w_r1, w_r2, proj, *, n_heads, n_kv_heads, ema_decay,
+            block, top_r, rows=None, lam_override=None):
+    """FastMKA layer forward over a whole sequence (every step, in page order).
+
+    Returns a dict with q [B,N,H*dh], lam [B,N,3], l2 [B,N,D], block_means
+    [B,nb,D], block_hash [B,nb], block_abs [B,nb,nbits], keys [B,N],
+    key_abs [B,N,nbits], idx [B,N,R], l3 [B,N,D], x_fused [B,N,D],
+    k, v [B,G,N,dh], rows [n] and o [B,n,H,dh] (attention only at ``rows``;
+    every row otherwise).  ``lam_override`` [B,N,3] replaces the router output.
+    """
+    x = _f64(x)
+    B, N, D = x.shape
+    q = q_proj(x, w_q)
+    lam = router(q, w_r1, w_r2) if lam_override is None else _f64(lam_override)
+    l2, _ = ema(x, ema_decay)
+    means = block_means(x, block)
+    bhash, babs = simhash(means, proj)
+    keys, kabs = simhash(l2, proj)
+    idx = retrieve(keys, bhash, np.arange(N), block, top_r)
+    l3 = l3_mean(means, idx)
+    xf = fuse(lam, x, l2, l3)
+    k, v = kv_proj(xf, w_k, w_v, n_kv_heads)
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    dh = q.shape[-1] // n_heads
+    q_rows = q[:, rows].reshape(B, len(rows), n_heads, dh)
+    o = attention(q_rows, k, v, rows, n_kv_heads)
+    return dict(q=q, lam=lam, l2=l2, block_means=means, block_hash=bhash, block_abs=babs,
+                keys=keys, key_abs=kabs, idx=idx, l3=l3, x_fused=xf, k=k, v=v, rows=rows, o=o)
+
+
+class DecodeState:
+    """Carried decode state: fused KV cache, EMA state, partial block sum,
+    block means and their hashes, and the position of the next token."""
+
+    def __init__(self, k, v, ema_state, block_acc, means, pos):
+        self.k = _f64(k).copy()
+        self.v = _f64(v).copy()
+        self.ema_state = _f64(ema_state).copy()
+        self.block_acc = _f64(block_acc).copy()
+        self.means = _f64(means).copy()
+        self.pos = int(pos)
+        self.hash = None
+        self.hash_abs = None
+
+
+def decode_init(k_cache, v_cache, ema_state, block_acc, means, proj, *, t_cap):
+    """State for decoding after ``k_cache.shape[2]`` cached tokens.
+
+    Room for ``t_cap`` rows is reserved in the cache.  Block hashes are
+    computed here from the given block means.
+    """
+    k_cache, v_cache = _f64(k_cache), _f64(v_cache)
+    B, G, T0, dh = k_cache.shape
+    k = np.zeros((B, G, t_cap, dh))
+    v = np.zeros((B, G, t_cap, dh))
+    k[:, :, :T0] = k_cache
+    v[:, :, :T0] = v_cache
+    st = DecodeState(k, v, ema_state, block_acc, means, T0)
+    st.hash, st.hash_abs = simhash(st.means, proj)
+    return st
+
+
+def decode_init_from_prefill(x, ref, proj, *, block, t_cap):
+    """State after a prefill (``ref`` = the dict ``prefill`` returned)."""
+    x = _f64(x)
+    B, N, D = x.shape
+    nb = N // block
+    acc = x[:, nb * block:].sum(axis=1)
+    return decode_init(ref["k"], ref["v"], ref["l2"][:, -1], acc, ref["block_means"], proj,
+                       t_cap=t_cap)
+
+
+def decode_step(st, x_t, w_q, w_k, w_v, w_r1, w_r2, proj, *, n_heads, n_kv_heads, ema_decay,
+                block, top_r, attend=True):
+    """One decode step at position t = st.pos for the token hiddens x_t [B, D].
+
+    The same definitions as ``prefill`` applied to one token with the carried
+    state; the fused K/V row is appended to the cache.  When token t closes a
+    block ((t + 1) mod block == 0) the block mean is finalised, hashed and
+    appended to the index; it becomes eligible from the next block on.
+    Returns a dict with q, lam, l2, key, key_abs, idx, k_row, v_row and o
+    ([B, H, dh], or None when ``attend`` is False).
+    """
+    x_t = _f64(x_t)
+    B, D = x_t.shape
+    t = st.pos
+    q = q_proj(x_t, w_q)
+    lam = router(q, w_r1, w_r2)
+    l2_seq, st.ema_state = ema(x_t[:, None, :], ema_decay, st.ema_state)
+    l2 = l2_seq[:, 0]
+    st.block_acc = st.block_acc + x_t
+    key, kabs = simhash(l2, proj)
+    idx = retrieve(key[:, None], st.hash, np.array([t]), block, top_r)
+    l3 = l3_mean(st.means, idx)[:, 0]
+    xf = fuse(lam, x_t, l2, l3)
+    k_row, v_row = kv_proj(xf[:, None, :], w_k, w_v, n_kv_heads)
+    st.k[:, :, t] = k_row[:, :, 0]
+    st.v[:, :, t] = v_row[:, :, 0]
+    o = None
+    if attend:
+        dh = q.shape[-1] // n_heads
+        o = attention(q.reshape(B, 1, n_heads, dh), st.k, st.v, np.array([t]), n_kv_heads)[:, 0]
+    if (t + 1) % block == 0:
+        m = st.block_acc / block
+        h, habs = simhash(m, proj)
+        st.means = np.concatenate([st.means, m[:, None]], axis=1)
+        st.hash = np.concatenate([st.hash, h[:, None]], axis=1)
+        st.hash_abs = np.concatenate([st.hash_abs, habs[:, None]], axis=1)
+        st.block_acc = np.zeros_like(st.block_acc)
+    st.pos = t + 1
+    return dict(q=q, lam=lam, l2=l2, key=key, key_abs=kabs, idx=idx[:, 0], l3=l3,
+                x_fused=xf, k_row=k_row[:, :, 0], v_row=v_row[:, :, 0], o=o)
