@@ -1,0 +1,284 @@
+#!/usr/bin/env python3
+"""Benchmark of the FastMKA layer forward on one MI355X (gfx950).
+
+One step = one whole-layer prefill of the Qwen2.5-7B-shaped layer (batch 2,
+4096 tokens, D=3584, 28 query / 4 KV heads of 128, bf16): route (Q
+projection + router), EMA scan and block means, block index, retrieval,
+fusion + K/V projection, causal flash attention.  The stages are the C-ABI
+calls, issued back to back on one stream with HIP events between them; inputs
+are resident in HBM before timing starts.  ``value`` is prefill tokens/s.
+
+The same line carries the decode measurement (the 131072-token fused cache
+workload, 256 decode steps of ``mka_decode_step``: median microseconds per
+token), the roofline position of the dominant kernel and of decode
+attention, and the CPU oracle timed on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FastMKA layer prefill tokens/s + decode µs/tok at 1 GPU; % MFMA / HBM peak"
+PEAK_BF16_FLOPS = 2.5e15  # MI355X dense bf16 MFMA
+PEAK_HBM_BYTES = 8.0e12   # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_flops(s):
+    M = s.batch * s.seq
+    qw, kvw, D = s.q_width, s.kv_width, s.d_model
+    pairs = s.batch * s.n_heads * s.seq * (s.seq + 1) // 2
+    return {
+        "route": 2.0 * M * qw * D + 2.0 * M * qw * s.router_hidden,
+        "fuse_kv": 2.0 * M * 2 * kvw * D,
+        "attn": 4.0 * s.head_dim * pairs,
+    }
+
+
+def bench_prefill(s, steps, warmup):
+    import torch
+
+    from route_kv_memory_amd import mka
+    from route_kv_memory_amd.inputs import prefill_inputs
+    from route_kv_memory_amd.layer import Layer, to_device
+
+    log(f"prefill: generating {s.name} inputs")
+    inp = prefill_inputs(s)
+    N = s.seq
+    layer = Layer(s, inp, t_cap=N, nb_cap=N // s.block)
+    x = to_device(inp["x"], s.dtype)
+    del inp
+    out = layer.outputs(N)
+    d = layer.dims(N)
+    ws = layer.workspace(mka.mka_workspace_bytes(d, mka.MKA_OP_PREFILL))
+    nws = ws.numel()
+    st, w = layer.st, layer.w
+    stream = torch.cuda.current_stream()
+    names = ["route", "ema", "index", "retrieve", "fuse_kv", "attn"]
+    nb = N // s.block
+
+    def step(ev):
+        ev[0].record(stream)
+        mka.mka_route(d, x, w["w_q"], w["w_r1"], w["w_r2"], out["q"], out["lambda"], stream)
+        ev[1].record(stream)
+        mka.mka_ema_scan(d, x, 0, st["ema_state"], st["block_acc"], out["l2"], st["block_means"],
+                         layer.nb_cap, ws, nws, stream)
+        ev[2].record(stream)
+        mka.mka_l3_index(d, st["block_means"], layer.nb_cap, 0, nb, w["proj"], st["block_hash"],
+                         stream)
+        ev[3].record(stream)
+        mka.mka_l3_retrieve(d, out["l2"], w["proj"], st["block_hash"], layer.nb_cap, 0, out["key"],
+                            out["idx"], ws, nws, stream)
+        ev[4].record(stream)
+        mka.mka_fuse_kv_proj(d, x, out["l2"], st["block_means"], layer.nb_cap, out["idx"],
+                             out["lambda"], w["w_k"], w["w_v"], st["k_cache"], st["v_cache"], 0,
+                             layer.t_cap, ws, nws, stream)
+        ev[5].record(stream)
+        mka.mka_attn_prefill(d, out["q"], st["k_cache"], st["v_cache"], layer.t_cap, 0, out["o"],
+                             stream)
+        ev[6].record(stream)
+
+    def zero_state():
+        st["ema_state"].zero_()
+        st["block_acc"].zero_()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+    for _ in range(warmup):
+        zero_state()
+        step(evs[0])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        zero_state()  # every step starts from an empty prefix (pos0 = 0)
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    stage_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+                for i, n in enumerate(names)}
+    gpu_ms = float(np.mean([e[0].elapsed_time(e[6]) for e in evs]))
+    return dict(wall_ms=wall * 1e3, gpu_ms=gpu_ms, stage_ms=stage_ms)
+
+
+def bench_decode(s, steps, warmup):
+    import torch
+
+    from route_kv_memory_amd import mka
+    from route_kv_memory_amd.inputs import decode_inputs
+    from route_kv_memory_amd.layer import Layer, to_device
+
+    log(f"decode: generating {s.name} state")
+    dec = decode_inputs(s)
+    T0, n = s.decode_cached, s.decode_steps
+    t_cap = T0 + n
+    nb0 = T0 // s.block
+    layer = Layer(s, dec, t_cap=t_cap, nb_cap=t_cap // s.block + 1)
+    st = layer.st
+    st["k_cache"][:, :, :T0] = to_device(dec["k_cache"], s.dtype)
+    st["v_cache"][:, :, :T0] = to_device(dec["v_cache"], s.dtype)
+    init = {k: to_device(dec[k]) for k in ("ema_state", "block_acc")}
+    means0 = to_device(dec["block_means"])
+    tokens = to_device(dec["tokens"], s.dtype)
+    del dec
+    d1 = layer.dims(1)
+
+    def reset():
+        st["ema_state"].copy_(init["ema_state"])
+        st["block_acc"].copy_(init["block_acc"])
+        st["block_means"][:, :nb0].copy_(means0)
+        mka.mka_l3_index(d1, st["block_means"], layer.nb_cap, 0, nb0, layer.w["proj"],
+                         st["block_hash"])
+
+    out = layer.outputs(1)
+    stream = torch.cuda.current_stream()
+    reset()
+    for k in range(warmup):
+        layer.decode_step(tokens[k], T0 + k, out=out)
+    reset()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for k in range(steps):
+        layer.decode_step(tokens[k], T0 + k, out=out)
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    wall_us = (time.perf_counter() - t0) / steps * 1e6
+    step_us = np.array([ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(steps)])
+
+    # Decode attention alone at the first step's length, for its roofline.
+    L = T0 + 1
+    nbytes = mka.mka_workspace_bytes(d1, mka.MKA_OP_ATTN_DECODE, L)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(out["o"])
+    reps = 50
+    a_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for _ in range(5):
+        mka.mka_attn_decode(d1, out["q"], st["k_cache"], st["v_cache"], t_cap, L, o, ws, nbytes,
+                            stream)
+    a_ev[0].record(stream)
+    for _ in range(reps):
+        mka.mka_attn_decode(d1, out["q"], st["k_cache"], st["v_cache"], t_cap, L, o, ws, nbytes,
+                            stream)
+    a_ev[1].record(stream)
+    torch.cuda.synchronize()
+    attn_us = a_ev[0].elapsed_time(a_ev[1]) * 1e3 / reps
+    kv_bytes = 2.0 * L * s.n_kv_heads * s.head_dim * 2  # K and V rows, bf16
+    el = 2
+    step_bytes = (kv_bytes + (s.q_width * s.d_model + 2 * s.kv_width * s.d_model
+                              + s.router_hidden * s.q_width + 3 * s.router_hidden) * el
+                  + s.hash_bits * s.d_model * 4 + s.top_r * s.d_model * 4 + nb0 * 8)
+    return dict(median_us=float(np.median(step_us)), mean_us=float(step_us.mean()),
+                wall_us=wall_us, attn_us=attn_us, kv_bytes=kv_bytes, step_bytes=step_bytes,
+                cached=T0, steps=steps)
+
+
+def cpu_baseline(s, n_tokens):
+    """The oracle, as it stands, on the first n_tokens of sequence 0."""
+    from oracle import mka_oracle as O
+    from route_kv_memory_amd.inputs import prefill_inputs
+
+    inp = prefill_inputs(s.replace(batch=1), seq=n_tokens)
+    w = [inp[k] for k in ("w_q", "w_k", "w_v", "w_r1", "w_r2", "proj")]
+    kw = dict(n_heads=s.n_heads, n_kv_heads=s.n_kv_heads,
+              ema_decay=float(np.float32(s.ema_decay)), block=s.block, top_r=s.top_r)
+    t0 = time.perf_counter()
+    O.prefill(inp["x"], *w, **kw)
+    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return dict(value=n_tokens / dt, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"whole-layer prefill (every step, attention on every row) of the first "
+                       f"{n_tokens} tokens of sequence 0, fp64 NumPy, {dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen7b_prefill_4k")
+    ap.add_argument("--decode-workload", default="qwen7b_decode_128k")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the FastMKA layer path here has no multi-GPU "
+              "sharding (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from route_kv_memory_amd import inputs as I
+    from route_kv_memory_amd import mka
+
+    mka.lib()
+    torch.cuda.set_device(0)
+    s = I.workload(args.workload)
+    pf = bench_prefill(s, args.steps, args.warmup)
+    flops = prefill_flops(s)
+    tokens = s.batch * s.seq
+    ms = pf["wall_ms"]
+    stage_ms = pf["stage_ms"]
+    mfma_stages = {k: v for k, v in stage_ms.items() if k in flops}
+    dom = max(mfma_stages, key=mfma_stages.get)
+    achieved = flops[dom] / (stage_ms[dom] * 1e-3)
+    line = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if s.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) hiddens, N(0,1/d_in) weights)",
+        "config": {"workload": s.name, "batch": s.batch, "seq_len": s.seq, "d_model": s.d_model,
+                   "n_heads": s.n_heads, "n_kv_heads": s.n_kv_heads, "head_dim": s.head_dim,
+                   "block": s.block, "top_r": s.top_r, "hash_bits": s.hash_bits},
+        "gpu_ms_per_step": pf["gpu_ms"],
+        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "prefill_tflops": sum(flops.values()) / (pf["gpu_ms"] * 1e-3) / 1e12,
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved / 1e12,
+                     "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_FLOPS, "traffic": None},
+    }
+    if not args.no_decode:
+        ds = I.workload(args.decode_workload)
+        dc = bench_decode(ds, ds.decode_steps, 8)
+        attn_bw = dc["kv_bytes"] / (dc["attn_us"] * 1e-6)
+        step_bw = dc["step_bytes"] / (dc["median_us"] * 1e-6)
+        line["decode"] = {
+            "workload": ds.name, "cached_tokens": dc["cached"], "steps": dc["steps"],
+            "us_per_token_median": dc["median_us"], "us_per_token_mean": dc["mean_us"],
+            "us_per_token_wall": dc["wall_us"],
+            "step_hbm_frac": step_bw / PEAK_HBM_BYTES,
+            "roofline": {"kernel": "attn_decode", "bound": "hbm", "achieved": attn_bw / 1e9,
+                         "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                         "frac": attn_bw / PEAK_HBM_BYTES, "traffic": None,
+                         "us_per_launch": dc["attn_us"]},
+        }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on a bounded sample")
+        line["cpu_baseline"] = cpu_baseline(s, args.cpu_tokens)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

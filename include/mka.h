@@ -1,0 +1,244 @@
+/*
+ * mka.h -- C ABI of the FastMKA (route-fused memory-keyed attention) layer
+ * forward on MI355X (gfx950).
+ *
+ * Sources: the Paper-Notes reading note "MKA: Memory-Keyed Attention for
+ * Efficient Long-Context Reasoning" (method sections 1-4) and the paper's
+ * landing page of the same title (abstract; Tables 4, 5, 11).  Per token a
+ * router gives lambda = softmax(MLP(q)) over three memory tiers: L1, the
+ * token's own hidden; L2, an exponential moving average of the prefix; L3,
+ * the mean of the R past block means whose SimHash codes are nearest (in
+ * Hamming distance) to the SimHash of L2[t].  The tiers are fused,
+ * X_fused = sum_l lambda_l * L_l; K and V are projected from X_fused
+ * (grouped-query heads) and one causal attention runs over them.  Decode
+ * caches the fused K/V.
+ *
+ * Conventions for every call
+ *  - Pointers are device pointers unless stated; ``stream`` is a hipStream_t
+ *    (NULL = the default stream).  Every call is asynchronous on ``stream``.
+ *  - The caller allocates and owns every buffer (inputs, outputs, state,
+ *    workspace).  The library allocates no device memory, keeps no pointer
+ *    after a call returns and holds no state besides a thread-local string
+ *    describing the last HIP error.  Calls on different streams are
+ *    independent; calls that write the same buffers must be ordered by the
+ *    caller.
+ *  - Arrays are dense, row-major, contiguous.  Token-major activations are
+ *    [B, seq, width]; the fused KV cache is head-major [B, G, t_cap, dh].
+ *    Weight matrices are stored [out, in] (each output's weights contiguous).
+ *  - Storage type ``dtype`` (mka_dims) applies to x, q, o, the weights and
+ *    the KV cache.  lambda, L2, EMA state, block sums and means and the
+ *    SimHash hyperplanes are always float32; codes are uint64 (low
+ *    hash_bits bits used); block indices are int32.
+ *  - Return value: MKA_OK (0) or a negative MKA_ERR_* code.  Arguments are
+ *    validated before anything is launched: on an error nothing has been
+ *    enqueued.  Faults during execution surface at the caller's next
+ *    synchronisation of ``stream``.
+ */
+#ifndef MKA_H
+#define MKA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { MKA_F32 = 0, MKA_BF16 = 1 };
+
+enum {
+  MKA_OK = 0,
+  MKA_ERR_INVALID = -1,     /* null pointer, inconsistent or out-of-range sizes */
+  MKA_ERR_UNSUPPORTED = -2, /* valid but not implemented: head_dim, dtype, alignment */
+  MKA_ERR_WORKSPACE = -3,   /* workspace smaller than mka_workspace_bytes() */
+  MKA_ERR_HIP = -4          /* a HIP call failed; see mka_last_error() */
+};
+
+/* Workspace-using operations, for mka_workspace_bytes(). */
+enum { MKA_OP_EMA_SCAN = 0, MKA_OP_FUSE_KV = 1, MKA_OP_ATTN_DECODE = 2, MKA_OP_PREFILL = 3,
+       MKA_OP_DECODE_STEP = 4, MKA_OP_RETRIEVE = 5 };
+
+/* Shape of one layer call.
+ *   batch B >= 1; seq = tokens in this call (1 for a decode step) >= 1;
+ *   d_model D; n_heads H and n_kv_heads G with H % G == 0 (query head h uses
+ *   KV head h / (H/G)); head_dim dh in {64, 128}; the query width H*dh;
+ *   router_hidden r; block = block size Bs of the L3 bank; hash_bits in
+ *   [1, 64]; top_r = R >= 1; ema_decay beta in [0, 1); dtype MKA_F32 or
+ *   MKA_BF16.  bf16 calls need D % 64 == 0 and H*dh % 128 == 0. */
+typedef struct mka_dims {
+  int32_t batch;
+  int32_t seq;
+  int32_t d_model;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t router_hidden;
+  int32_t block;
+  int32_t hash_bits;
+  int32_t top_r;
+  float ema_decay;
+  int32_t dtype;
+} mka_dims;
+
+/* Router: Q = X W_q and lambda = softmax(GELU(Q W_r1) W_r2).
+ * (Reading note, method section 2: lambda = softmax(MLP(q)) in R^{B x S x 3},
+ * per token; q is the query projection of the token hidden.)
+ *   x       [B, seq, D]            dtype
+ *   w_q     [H*dh, D]              dtype
+ *   w_r1    [r, H*dh]              dtype
+ *   w_r2    [3, r]                 dtype
+ *   q_out   [B, seq, H, dh]        dtype (written)
+ *   lambda_out [B, seq, 3]         float32 (written; tier 0 = L1, 1 = L2, 2 = L3) */
+int mka_route(const mka_dims* d, const void* x, const void* w_q, const void* w_r1,
+              const void* w_r2, void* q_out, float* lambda_out, void* stream);
+
+/* L2 session summary and block means for tokens at positions pos0 .. pos0+seq-1.
+ * (Reading note, method section 1: the L2 tier is a causal summary of the
+ * prefix, here the EMA s_t = beta*s_{t-1} + (1-beta)*x_t, prefix inclusive of
+ * t, s_{-1} = 0; the L3 bank holds past blocks.)
+ *   x            [B, seq, D]   dtype
+ *   state_io     [B, D]        in: s_{pos0-1} (zeros when pos0 == 0); out: s_{pos0+seq-1}
+ *   block_acc_io [B, D]        in: sum of x over the tokens of pos0's block before pos0;
+ *                              out: the same sum for the block after the last token
+ *   l2_out       [B, seq, D]   float32 (written)
+ *   block_means  [B, nb_cap, D] float32: row b = mean of x over block b is written
+ *                              for every block whose last token is in this call
+ *   ws           >= mka_workspace_bytes(d, MKA_OP_EMA_SCAN, 0) bytes (may be NULL if 0)
+ * Requires the last completed block index < nb_cap. */
+int mka_ema_scan(const mka_dims* d, const void* x, int64_t pos0, float* state_io,
+                 float* block_acc_io, float* l2_out, float* block_means, int32_t nb_cap,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* SimHash codes of block means first_block .. first_block+n_blocks-1.
+ * (Reading note, method section 1: vectorised hash index of past blocks.)
+ * bit j of a code = [m . proj_j > 0]; the dot product is accumulated in float64
+ * from the float32 inputs.
+ *   block_means [B, nb_cap, D] float32; proj [hash_bits, D] float32 (row j = hyperplane j)
+ *   block_hash  [B, nb_cap]    uint64 (rows written) */
+int mka_l3_index(const mka_dims* d, const float* block_means, int32_t nb_cap,
+                 int32_t first_block, int32_t n_blocks, const float* proj,
+                 uint64_t* block_hash, void* stream);
+
+/* L3 retrieval for tokens at positions pos0 .. pos0+seq-1.
+ * (Reading note, method section 1: recall of R << T past blocks; landing page,
+ * Table 8 caption: top-R retrieved chunks per query.)
+ * key_t = SimHash(L2[t]) (float64 accumulation, as in mka_l3_index); eligible
+ * blocks b < floor(t / block); ranked by (popcount(key_t ^ hash_b) ascending,
+ * b descending); the first min(R, #eligible) are written in rank order, the
+ * remaining slots hold -1.  top_r <= 32.
+ *   l2       [B, seq, D] float32;   proj [hash_bits, D] float32
+ *   block_hash [B, nb_cap] uint64, valid for every eligible block
+ *   key_out  [B, seq] uint64 (written);  idx_out [B, seq, R] int32 (written)
+ *   ws >= mka_workspace_bytes(d, MKA_OP_RETRIEVE, 0) bytes
+ * Requires floor((pos0+seq-1)/block) <= nb_cap. */
+int mka_l3_retrieve(const mka_dims* d, const float* l2, const float* proj,
+                    const uint64_t* block_hash, int32_t nb_cap, int64_t pos0,
+                    uint64_t* key_out, int32_t* idx_out, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* Route fusion and K/V projection into the fused KV cache.
+ * (Reading note, method section 3: X_fused = sum_l lambda_l * L_l, K = X_fused W_k,
+ * V = X_fused W_v, the fused K/V is what the cache holds; landing page, abstract:
+ * lambda is broadcast over the hidden dimension.)
+ * L3[t] = mean of block_means rows idx[t, :] that are >= 0 (zero if none).
+ * X_fused is formed in float32 and rounded once to dtype before the projection.
+ *   x [B, seq, D] dtype; l2 [B, seq, D] f32; block_means [B, nb_cap, D] f32;
+ *   idx [B, seq, R] int32; lambda [B, seq, 3] f32; w_k, w_v [G*dh, D] dtype
+ *   k_cache, v_cache [B, G, t_cap, dh] dtype: rows pos0 .. pos0+seq-1 written
+ *   ws >= mka_workspace_bytes(d, MKA_OP_FUSE_KV, 0) bytes
+ * Requires pos0 + seq <= t_cap. */
+int mka_fuse_kv_proj(const mka_dims* d, const void* x, const float* l2,
+                     const float* block_means, int32_t nb_cap, const int32_t* idx,
+                     const float* lambda, const void* w_k, const void* w_v, void* k_cache,
+                     void* v_cache, int64_t pos0, int64_t t_cap, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Causal grouped-query flash attention for queries at positions pos0 .. pos0+seq-1
+ * over cache rows 0 .. pos0+seq-1.
+ * (Reading note, method sections 3-4: one standard causal attention over the fused
+ * K/V, evaluated blockwise with the online max-shift.)
+ * O[t,h] = sum_{j<=t} softmax_j(q_{t,h} . k_{j,g(h)} / sqrt(dh)) v_{j,g(h)}.
+ *   q [B, seq, H, dh] dtype; k_cache, v_cache [B, G, t_cap, dh] dtype;
+ *   o [B, seq, H, dh] dtype (written).  Requires pos0 + seq <= t_cap. */
+int mka_attn_prefill(const mka_dims* d, const void* q, const void* k_cache,
+                     const void* v_cache, int64_t t_cap, int64_t pos0, void* o, void* stream);
+
+/* Decode attention of one query token per sequence (d->seq must be 1) over cache rows
+ * 0 .. cache_len-1, split over the keys with a log-sum-exp merge of the parts.
+ * (Landing page, Table 5: decode reads the single fused KV tensor.)
+ *   q [B, 1, H, dh] dtype; o [B, 1, H, dh] dtype (written)
+ *   ws >= mka_workspace_bytes(d, MKA_OP_ATTN_DECODE, cache_len) bytes */
+int mka_attn_decode(const mka_dims* d, const void* q, const void* k_cache,
+                    const void* v_cache, int64_t t_cap, int64_t cache_len, void* o,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Composite: the whole layer over a prompt at positions pos0 .. pos0+seq-1 (the
+ * calls above in order: route, ema_scan, l3_index of the blocks completed here,
+ * l3_retrieve, fuse_kv_proj, attn_prefill).  Intermediates go to the caller's
+ * buffers, so the call both answers the prompt and leaves the decode state.
+ *   weights: w_q, w_k, w_v, w_r1, w_r2 (dtype), proj (f32), as above
+ *   state: state_io, block_acc_io [B, D] f32; block_means [B, nb_cap, D] f32;
+ *          block_hash [B, nb_cap] u64; k_cache, v_cache [B, G, t_cap, dh]
+ *   outputs: q [B,seq,H,dh], lambda [B,seq,3], l2 [B,seq,D], key [B,seq],
+ *            idx [B,seq,R], o [B,seq,H,dh]
+ *   ws >= mka_workspace_bytes(d, MKA_OP_PREFILL, 0) bytes */
+typedef struct mka_weights {
+  const void* w_q;
+  const void* w_k;
+  const void* w_v;
+  const void* w_r1;
+  const void* w_r2;
+  const float* proj;
+} mka_weights;
+
+typedef struct mka_state {
+  float* ema_state;      /* [B, D] */
+  float* block_acc;      /* [B, D] */
+  float* block_means;    /* [B, nb_cap, D] */
+  uint64_t* block_hash;  /* [B, nb_cap] */
+  void* k_cache;         /* [B, G, t_cap, dh] */
+  void* v_cache;         /* [B, G, t_cap, dh] */
+  int32_t nb_cap;
+  int64_t t_cap;
+} mka_state;
+
+typedef struct mka_outputs {
+  void* q;          /* [B, seq, H, dh] */
+  float* lambda;    /* [B, seq, 3] */
+  float* l2;        /* [B, seq, D] */
+  uint64_t* key;    /* [B, seq] */
+  int32_t* idx;     /* [B, seq, R] */
+  void* o;          /* [B, seq, H, dh] */
+} mka_outputs;
+
+int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weights* w,
+                const mka_state* st, const mka_outputs* out, void* ws, size_t ws_bytes,
+                void* stream);
+
+/* Composite: one decode step for the token at position ``pos`` (d->seq must be 1):
+ * route, EMA update, retrieval over the blocks before pos's block, fusion and K/V
+ * append at row pos, decode attention over rows 0..pos, and -- when pos closes a
+ * block ((pos+1) % block == 0) -- the block mean and its code appended to the bank.
+ * Same buffers as mka_prefill with seq = 1;
+ * ws >= mka_workspace_bytes(d, MKA_OP_DECODE_STEP, pos + 1) bytes. */
+int mka_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_weights* w,
+                    const mka_state* st, const mka_outputs* out, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* Workspace in bytes that ``op`` needs for the shape ``d`` (cache_len: decode only). */
+size_t mka_workspace_bytes(const mka_dims* d, int op, int64_t cache_len);
+
+/* Static description of a status code. */
+const char* mka_status_string(int status);
+
+/* Thread-local description of the last HIP failure seen by this thread ("" if none). */
+const char* mka_last_error(void);
+
+/* Library version string. */
+const char* mka_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MKA_H */

@@ -1,0 +1,536 @@
+// One causal grouped-query attention over the fused K/V (MKA reading note,
+// method section 3: a single attention path over the fused cache), evaluated
+// key tile by key tile with the online max-shift of method section 4: the
+// running maximum mu is raised tile by tile and the running numerator and
+// denominator are rescaled by exp(mu_old - mu_new).
+//
+// bf16 path (MFMA 32x32x16 on gfx950).  A wave owns 32 query rows and computes
+// S^T = K Q^T for a 64-key tile (keys as MFMA rows), so each lane owns one
+// query row: the row max and sum need a single cross-half exchange and the
+// rescale factor is lane-local.  K rows are fed to the MFMA in a permuted
+// order (rows 4..7 and 8..11 of every 16 swapped) which makes accumulator
+// register r of lane half hl hold key 16*(r/8) + 8*hl + r%8; the
+// probabilities then form, without any data movement, the B operand of
+// O^T = V^T P^T, whose A operand is read from a transposed V tile in LDS.
+// Scores use exp2 with log2(e)/sqrt(dh) folded into one scale.
+#include "kernels.h"
+
+namespace mka {
+
+__device__ __forceinline__ int kperm(int r) {
+  const int q = r & 15;
+  const int qq = (q >= 4 && q < 8) ? q + 4 : ((q >= 8 && q < 12) ? q - 4 : q);
+  return (r & ~15) | qq;
+}
+
+// 8 floats -> bf16x8 (round to nearest even).
+__device__ __forceinline__ bf16x8 to_bf16x8(const float* v) {
+  const u32x4 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                   pack_bf16x2(v[6], v[7])};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// Transpose a 4-key x 8-dim bf16 block (4 x 16-byte rows) into 8 rows of 4
+// keys and store them at Vt[(d0 + i) * pitch + k0].
+__device__ __forceinline__ void store_vt(bf16_t* Vt, int pitch, int d0, int k0, const u32x4* rv) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo01 = (rv[0][j] & 0xFFFFu) | (rv[1][j] << 16);
+    const uint32_t lo23 = (rv[2][j] & 0xFFFFu) | (rv[3][j] << 16);
+    const uint32_t hi01 = (rv[0][j] >> 16) | (rv[1][j] & 0xFFFF0000u);
+    const uint32_t hi23 = (rv[2][j] >> 16) | (rv[3][j] & 0xFFFF0000u);
+    *reinterpret_cast<u32x2*>(&Vt[(d0 + 2 * j) * pitch + k0]) = u32x2{lo01, lo23};
+    *reinterpret_cast<u32x2*>(&Vt[(d0 + 2 * j + 1) * pitch + k0]) = u32x2{hi01, hi23};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill, bf16.  Workgroup = 4 waves = 128 query rows of one head; K/V tiles
+// of 64 keys double-buffered in LDS.  Work order: units (query block, batch,
+// KV group) heaviest first; the H/G heads of a unit are consecutive slots of
+// one XCD so they read the same K/V tiles through that XCD's L2.
+// ---------------------------------------------------------------------------
+template <int DH>
+__global__ __launch_bounds__(256, 2) void attn_prefill_bf16_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
+    bf16_t* __restrict__ O, int B, int seq, int H, int G, int64_t t_cap, int64_t pos0, float sl2,
+    int n_qblk, int n_units) {
+  constexpr int BM = 128, BN = 64, KP = DH + 8, VP = BN + 8, NKS = DH / 16, NDB = DH / 32;
+  constexpr int KCH = BN * DH / 8 / 256;
+  constexpr int VITEMS = (BN / 4) * (DH / 8);
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][BN * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[2][DH * VP];
+
+  const int hpg = H / G;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int hh = slot % hpg, u = (slot / hpg) * 8 + xcd;
+  if (u >= n_units) return;
+  const int qb = n_qblk - 1 - u / (B * G);
+  const int bg = u % (B * G), b = bg / G, g = bg % G, h = g * hpg + hh;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5, l32 = lane & 31;
+  const int q_row = qb * BM + wave * 32 + l32;
+  const int64_t q_pos = pos0 + q_row;
+  const int64_t wave_pos0 = pos0 + qb * BM + wave * 32;
+  const int64_t kv_end = pos0 + min(qb * BM + BM, seq);
+  const int n_tiles = static_cast<int>((kv_end + BN - 1) / BN);
+
+  bf16x8 qf[NKS];
+  {
+    const bf16_t* qp = Q + (static_cast<int64_t>(b * seq + min(q_row, seq - 1)) * H + h) * DH + 8 * hl;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
+      if (q_row >= seq) qf[ks] = bf16x8{};
+    }
+  }
+  const bf16_t* kbase = Kc + (static_cast<int64_t>(b) * G + g) * t_cap * DH;
+  const bf16_t* vbase = Vc + (static_cast<int64_t>(b) * G + g) * t_cap * DH;
+
+  u32x4 rk[KCH], rv[4];
+  auto gload = [&](int64_t j0) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + 256 * i, row = c / (DH / 8), col = (c % (DH / 8)) * 8;
+      rk[i] = (j0 + row < kv_end) ? *reinterpret_cast<const u32x4*>(kbase + (j0 + row) * DH + col)
+                                  : u32x4{0, 0, 0, 0};
+    }
+    if (tid < VITEMS) {
+      const int kq = tid / (DH / 8), dc = tid % (DH / 8);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t key = j0 + 4 * kq + r;
+        rv[r] = key < kv_end ? *reinterpret_cast<const u32x4*>(vbase + key * DH + 8 * dc)
+                             : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + 256 * i, row = c / (DH / 8), col = (c % (DH / 8)) * 8;
+      *reinterpret_cast<u32x4*>(&Ks[buf][row * KP + col]) = rk[i];
+    }
+    if (tid < VITEMS) {
+      const int kq = tid / (DH / 8), dc = tid % (DH / 8);
+      store_vt(Vt[buf], VP, 8 * dc, 4 * kq, rv);
+    }
+  };
+
+  float m_i = -INFINITY, l_i = 0.f;
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int jt = 0; jt < n_tiles; ++jt) {
+    const int buf = jt & 1;
+    const int64_t j0 = static_cast<int64_t>(jt) * BN;
+    if (jt + 1 < n_tiles) gload(j0 + BN);
+
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      const bf16_t* kr = &Ks[buf][(kb * 32 + kperm(l32)) * KP + 8 * hl];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        s[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kr + 16 * ks), qf[ks], s[kb]);
+    }
+
+    const bool diag = (j0 + BN - 1) > wave_pos0;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = s[kb][r] * sl2;
+        if (diag) {
+          const int64_t key = j0 + kb * 32 + 16 * (r >> 3) + 8 * hl + (r & 7);
+          if (key > q_pos) v = -INFINITY;
+        }
+        s[kb][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_i, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_i - m_new);
+
+    bf16x8 pf[2][2];
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          p[j] = __builtin_amdgcn_exp2f(s[kb][8 * st + j] - m_new);
+          lsum += p[j];
+        }
+        pf[kb][st] = to_bf16x8(p);
+      }
+    l_i = l_i * alpha + lsum;
+    m_i = m_new;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const bf16_t* vr = &Vt[buf][(db * 32 + l32) * VP + 8 * hl];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+          acc[db] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(vr + kb * 32 + 16 * st),
+                                 pf[kb][st], acc[db]);
+    }
+    if (jt + 1 < n_tiles) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  l_i += __shfl_xor(l_i, 32, 64);
+  if (q_row < seq) {
+    const float inv = 1.0f / l_i;
+    bf16_t* op = O + (static_cast<int64_t>(b * seq + q_row) * H + h) * DH;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const float v[4] = {acc[db][4 * rq] * inv, acc[db][4 * rq + 1] * inv,
+                            acc[db][4 * rq + 2] * inv, acc[db][4 * rq + 3] * inv};
+        store4(op + db * 32 + 8 * rq + 4 * hl, v);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill, fp32: one thread per query row with the online max-shift over key
+// tiles staged in LDS (the reference-precision path of small fp32 layers).
+// ---------------------------------------------------------------------------
+template <int DH>
+__global__ __launch_bounds__(64) void attn_prefill_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ Kc, const float* __restrict__ Vc,
+    float* __restrict__ O, int seq, int H, int G, int64_t t_cap, int64_t pos0, float scale) {
+  constexpr int TK = 32;
+  __shared__ float Ks[TK][DH];
+  __shared__ float Vs[TK][DH];
+  const int tid = threadIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int t = blockIdx.x * 64 + tid;
+  const int g = h / (H / G);
+  const int64_t q_pos = pos0 + t;
+  const int64_t kv_end = pos0 + min(static_cast<int>(blockIdx.x) * 64 + 64, seq);
+  float q[DH], acc[DH];
+  const float* qp = Q + (static_cast<int64_t>(b * seq + min(t, seq - 1)) * H + h) * DH;
+#pragma unroll
+  for (int d = 0; d < DH; ++d) {
+    q[d] = qp[d];
+    acc[d] = 0.f;
+  }
+  const float* kb = Kc + (static_cast<int64_t>(b) * G + g) * t_cap * DH;
+  const float* vb = Vc + (static_cast<int64_t>(b) * G + g) * t_cap * DH;
+  float m = -INFINITY, l = 0.f;
+  for (int64_t j0 = 0; j0 < kv_end; j0 += TK) {
+    for (int e = tid; e < TK * DH; e += 64) {
+      const int r = e / DH, d = e % DH;
+      const bool ok = j0 + r < kv_end;
+      Ks[r][d] = ok ? kb[(j0 + r) * DH + d] : 0.f;
+      Vs[r][d] = ok ? vb[(j0 + r) * DH + d] : 0.f;
+    }
+    __syncthreads();
+    for (int jj = 0; jj < TK; ++jj) {
+      const int64_t j = j0 + jj;
+      if (j > q_pos || j >= kv_end) break;
+      float sdot = 0.f;
+#pragma unroll
+      for (int d = 0; d < DH; ++d) sdot = fmaf(q[d], Ks[jj][d], sdot);
+      const float sc = sdot * scale;
+      const float m_new = fmaxf(m, sc);
+      const float corr = expf(m - m_new);
+      const float p = expf(sc - m_new);
+      l = l * corr + p;
+#pragma unroll
+      for (int d = 0; d < DH; ++d) acc[d] = fmaf(p, Vs[jj][d], acc[d] * corr);
+      m = m_new;
+    }
+    __syncthreads();
+  }
+  if (t < seq) {
+    float* op = O + (static_cast<int64_t>(b * seq + t) * H + h) * DH;
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int d = 0; d < DH; ++d) op[d] = acc[d] * inv;
+  }
+}
+
+template <>
+hipError_t attn_prefill<bf16_t>(const bf16_t* q, const bf16_t* k, const bf16_t* v, bf16_t* o, int B,
+                                int seq, int H, int G, int dh, int64_t t_cap, int64_t pos0,
+                                hipStream_t s) {
+  const int n_qblk = (seq + 127) / 128;
+  const int n_units = n_qblk * B * G;
+  const int grid = ((n_units + 7) / 8) * 8 * (H / G);
+  const float sl2 = 1.4426950408889634f / sqrtf(static_cast<float>(dh));
+  if (dh == 128)
+    hipLaunchKernelGGL(attn_prefill_bf16_kernel<128>, dim3(grid), dim3(256), 0, s, q, k, v, o, B,
+                       seq, H, G, t_cap, pos0, sl2, n_qblk, n_units);
+  else
+    hipLaunchKernelGGL(attn_prefill_bf16_kernel<64>, dim3(grid), dim3(256), 0, s, q, k, v, o, B, seq,
+                       H, G, t_cap, pos0, sl2, n_qblk, n_units);
+  return hipGetLastError();
+}
+
+template <>
+hipError_t attn_prefill<float>(const float* q, const float* k, const float* v, float* o, int B,
+                               int seq, int H, int G, int dh, int64_t t_cap, int64_t pos0,
+                               hipStream_t s) {
+  const dim3 grid((seq + 63) / 64, H, B);
+  const float scale = 1.0f / sqrtf(static_cast<float>(dh));
+  if (dh == 128)
+    hipLaunchKernelGGL(attn_prefill_f32_kernel<128>, grid, dim3(64), 0, s, q, k, v, o, seq, H, G,
+                       t_cap, pos0, scale);
+  else
+    hipLaunchKernelGGL(attn_prefill_f32_kernel<64>, grid, dim3(64), 0, s, q, k, v, o, seq, H, G,
+                       t_cap, pos0, scale);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Decode, bf16: one query token per sequence.  A workgroup takes 1024 keys of
+// one (batch, KV group); each wave 256 of them as 4 tiles of 64 with all H/G
+// query heads of the group in its 32 MFMA columns.  K fragments come straight
+// from global (16 contiguous bytes per lane), V tiles are transposed through a
+// per-wave LDS region.  The 4 waves merge in LDS into one partial (max, sum,
+// unnormalised output) per head; a second kernel merges the partials of all
+// workgroups (log-sum-exp weights, fixed order).
+// ---------------------------------------------------------------------------
+constexpr int kMaxDecodeChunks = 4096;
+
+size_t attn_decode_ws_bytes(int B, int H, int dh, int64_t cache_len) {
+  const int64_t n_chunks = (cache_len + kDecodeChunk - 1) / kDecodeChunk;
+  return sizeof(float) * static_cast<size_t>(B) * H * n_chunks * (dh + 2);
+}
+
+template <int DH>
+__global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
+    int H, int G, int64_t t_cap, int64_t cache_len, float sl2, int n_chunks,
+    float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ part_o) {
+  constexpr int BN = 64, VP = BN + 8, NKS = DH / 16, NDB = DH / 32;
+  constexpr int TILES = kDecodeChunk / 4 / BN;
+  constexpr int VITEMS = (BN / 4) * (DH / 8);
+  constexpr int LDS_BYTES = 4 * DH * VP * 2;
+  static_assert(LDS_BYTES >= 4 * 32 * (DH + 2) * 4, "merge buffer must fit");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5, l32 = lane & 31;
+  const int hpg = H / G;
+  bf16_t* Vt = reinterpret_cast<bf16_t*>(lds) + wave * DH * VP;
+
+  bf16x8 qf[NKS];
+  {
+    const bf16_t* qp = Q + (static_cast<int64_t>(b) * H + g * hpg + min(l32, hpg - 1)) * DH + 8 * hl;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
+      if (l32 >= hpg) qf[ks] = bf16x8{};
+    }
+  }
+  const bf16_t* kbase = Kc + (static_cast<int64_t>(b) * G + g) * t_cap * DH;
+  const bf16_t* vbase = Vc + (static_cast<int64_t>(b) * G + g) * t_cap * DH;
+
+  float m_i = -INFINITY, l_i = 0.f;
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+
+  for (int tile = 0; tile < TILES; ++tile) {
+    const int64_t j0 = static_cast<int64_t>(c) * kDecodeChunk + wave * (kDecodeChunk / 4) + tile * BN;
+    const bool live = j0 < cache_len;
+    // V tile -> transposed per-wave LDS region.
+    if (live) {
+#pragma unroll
+      for (int it = 0; it < VITEMS / 64; ++it) {
+        const int item = lane + 64 * it, kq = item / (DH / 8), dc = item % (DH / 8);
+        u32x4 rv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t key = j0 + 4 * kq + r;
+          rv[r] = key < cache_len ? *reinterpret_cast<const u32x4*>(vbase + key * DH + 8 * dc)
+                                  : u32x4{0, 0, 0, 0};
+        }
+        store_vt(Vt, VP, 8 * dc, 4 * kq, rv);
+      }
+    }
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      const int64_t row = j0 + kb * 32 + kperm(l32);
+      const bf16_t* kr = kbase + min(row, cache_len - 1) * DH + 8 * hl;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + 16 * ks);
+        if (row >= cache_len) a = bf16x8{};
+        s[kb] = mfma32x32x16(a, qf[ks], s[kb]);
+      }
+    }
+    __syncthreads();  // V tile stores visible to the wave's lanes
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t key = j0 + kb * 32 + 16 * (r >> 3) + 8 * hl + (r & 7);
+        const float v = key < cache_len ? s[kb][r] * sl2 : -INFINITY;
+        s[kb][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_i, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_i - m_use);
+    bf16x8 pf[2][2];
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          p[j] = __builtin_amdgcn_exp2f(s[kb][8 * st + j] - m_use);
+          lsum += p[j];
+        }
+        pf[kb][st] = to_bf16x8(p);
+      }
+    l_i = l_i * alpha + lsum;
+    m_i = m_new;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+    if (live) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const bf16_t* vr = &Vt[(db * 32 + l32) * VP + 8 * hl];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+            acc[db] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(vr + kb * 32 + 16 * st),
+                                   pf[kb][st], acc[db]);
+      }
+    }
+    __syncthreads();  // reads done before the next tile overwrites the region
+  }
+
+  // Merge the 4 waves.
+  l_i += __shfl_xor(l_i, 32, 64);
+  float* red_m = reinterpret_cast<float*>(lds);
+  float* red_l = red_m + 4 * 32;
+  float* red_o = red_l + 4 * 32;  // [4][32][DH]
+  if (hl == 0) {
+    red_m[wave * 32 + l32] = m_i;
+    red_l[wave * 32 + l32] = l_i;
+  }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      red_o[(wave * 32 + l32) * DH + db * 32 + acc_row(r, hl)] = acc[db][r];
+  __syncthreads();
+  for (int e = tid; e < hpg * DH; e += 256) {
+    const int n = e / DH, d = e % DH;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w * 32 + n]);
+    float L = 0.f, acc_o = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float wt = red_m[w * 32 + n] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(red_m[w * 32 + n] - M);
+      L += wt * red_l[w * 32 + n];
+      acc_o += wt * red_o[(w * 32 + n) * DH + d];
+    }
+    const int64_t p = (static_cast<int64_t>(b) * H + g * hpg + n) * n_chunks + c;
+    part_o[p * DH + d] = acc_o;
+    if (d == 0) {
+      part_m[p] = M;
+      part_l[p] = L;
+    }
+  }
+}
+
+template <int DH>
+__global__ __launch_bounds__(256) void attn_decode_merge_kernel(const float* __restrict__ part_m,
+                                                                const float* __restrict__ part_l,
+                                                                const float* __restrict__ part_o,
+                                                                int H, int n_chunks,
+                                                                bf16_t* __restrict__ O) {
+  constexpr int GR = 256 / DH;
+  __shared__ float wts[kMaxDecodeChunks];
+  __shared__ float red[256];
+  __shared__ float osum[GR][DH];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int64_t p0 = (static_cast<int64_t>(b) * H + h) * n_chunks;
+  float mx = -INFINITY;
+  for (int c = tid; c < n_chunks; c += 256) mx = fmaxf(mx, part_m[p0 + c]);
+  red[tid] = mx;
+  __syncthreads();
+  for (int off = 128; off >= 1; off >>= 1) {
+    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  __syncthreads();
+  float ls = 0.f;
+  for (int c = tid; c < n_chunks; c += 256) {
+    const float w = __builtin_amdgcn_exp2f(part_m[p0 + c] - M);
+    wts[c] = w;
+    ls += w * part_l[p0 + c];
+  }
+  red[tid] = ls;
+  __syncthreads();
+  for (int off = 128; off >= 1; off >>= 1) {
+    if (tid < off) red[tid] += red[tid + off];
+    __syncthreads();
+  }
+  const float L = red[0];
+  const int d = tid % DH, grp = tid / DH;
+  float o = 0.f;
+  for (int c = grp; c < n_chunks; c += GR) o += wts[c] * part_o[(p0 + c) * DH + d];
+  osum[grp][d] = o;
+  __syncthreads();
+  if (tid < DH) {
+    float tot = 0.f;
+#pragma unroll
+    for (int gi = 0; gi < GR; ++gi) tot += osum[gi][tid];
+    O[(static_cast<int64_t>(b) * H + h) * DH + tid] = f32_to_bf16(tot / L);
+  }
+}
+
+hipError_t attn_decode_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* v, bf16_t* o, int B,
+                            int H, int G, int dh, int64_t t_cap, int64_t cache_len, void* ws,
+                            hipStream_t s) {
+  const int n_chunks = static_cast<int>((cache_len + kDecodeChunk - 1) / kDecodeChunk);
+  if (n_chunks > kMaxDecodeChunks) return hipErrorInvalidValue;
+  float* part_m = static_cast<float*>(ws);
+  float* part_l = part_m + static_cast<size_t>(B) * H * n_chunks;
+  float* part_o = part_l + static_cast<size_t>(B) * H * n_chunks;
+  const float sl2 = 1.4426950408889634f / sqrtf(static_cast<float>(dh));
+  const dim3 grid(n_chunks, G, B);
+  if (dh == 128) {
+    hipLaunchKernelGGL(attn_decode_split_kernel<128>, grid, dim3(256), 0, s, q, k, v, H, G, t_cap,
+                       cache_len, sl2, n_chunks, part_m, part_l, part_o);
+    hipLaunchKernelGGL(attn_decode_merge_kernel<128>, dim3(H, B), dim3(256), 0, s, part_m, part_l,
+                       part_o, H, n_chunks, o);
+  } else {
+    hipLaunchKernelGGL(attn_decode_split_kernel<64>, grid, dim3(256), 0, s, q, k, v, H, G, t_cap,
+                       cache_len, sl2, n_chunks, part_m, part_l, part_o);
+    hipLaunchKernelGGL(attn_decode_merge_kernel<64>, dim3(H, B), dim3(256), 0, s, part_m, part_l,
+                       part_o, H, n_chunks, o);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mka

@@ -1,0 +1,126 @@
+// Device-side helpers shared by the FastMKA kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mka {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// bfloat16 values travel as their 16-bit patterns.
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest even (finite inputs).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+// Two floats -> packed bf16 pair (lo in bits 0..15), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// Element-type traits: storage type T <-> float.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ float to_f32(float v) { return v; }
+  static __device__ __forceinline__ float from_f32(float v) { return v; }
+};
+template <> struct Elem<bf16_t> {
+  static __device__ __forceinline__ float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  static __device__ __forceinline__ float to_f32(bf16_t v) { return bf16_to_f32(v); }
+  static __device__ __forceinline__ bf16_t from_f32(float v) { return f32_to_bf16(v); }
+};
+
+// ---------------------------------------------------------------------------
+// MFMA 32x32x16 bf16 -> f32 (gfx950).  Operand layout for a wave of 64 lanes,
+// lane l, half h = l / 32:
+//   A (32 x 16): lane holds A[l % 32][8h .. 8h+7]
+//   B (16 x 32): lane holds B[8h .. 8h+7][l % 32]
+//   C (32 x 32): lane holds C[8*(r/4) + 4h + (r%4)][l % 32], r = 0..15
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row (within the 32x32 block) of accumulator register r for lane half h.
+__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// 16-byte vector load widened to float: 8 bf16 or 4 fp32 values.
+template <typename T> struct Vec16;
+template <> struct Vec16<bf16_t> {
+  static constexpr int kN = 8;
+  static __device__ __forceinline__ void load(const bf16_t* p, float* out) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+};
+template <> struct Vec16<float> {
+  static constexpr int kN = 4;
+  static __device__ __forceinline__ void load(const float* p, float* out) {
+    const f32x4 w = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = w[i];
+  }
+};
+
+// 4 consecutive values widened to float (8-byte or 16-byte load).
+__device__ __forceinline__ void load4(const bf16_t* p, float* out) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  out[0] = __uint_as_float(w[0] << 16);
+  out[1] = __uint_as_float(w[0] & 0xFFFF0000u);
+  out[2] = __uint_as_float(w[1] << 16);
+  out[3] = __uint_as_float(w[1] & 0xFFFF0000u);
+}
+__device__ __forceinline__ void load4(const float* p, float* out) {
+  const f32x4 w = *reinterpret_cast<const f32x4*>(p);
+  out[0] = w[0]; out[1] = w[1]; out[2] = w[2]; out[3] = w[3];
+}
+__device__ __forceinline__ void store4(bf16_t* p, const float* v) {
+  *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+__device__ __forceinline__ void store4(float* p, const float* v) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+}
+
+// Exact GELU, z * Phi(z), with the device erf.
+__device__ __forceinline__ float gelu(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+
+// Map a linear workgroup id to a work item so that each of the 8 XCDs (which
+// receive workgroups round-robin) works on a contiguous range of items: items
+// that share operands then share that XCD's L2.
+__device__ __forceinline__ int xcd_contiguous(int bid, int n) {
+  const int per = n / 8, rem = n % 8;
+  const int xcd = bid % 8, local = bid / 8;
+  return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local;
+}
+
+}  // namespace mka

@@ -1,0 +1,65 @@
+// Route fusion: X_fused[t] = lambda1 * x_t + lambda2 * L2[t] + lambda3 * L3[t],
+// with L3[t] the mean of the retrieved block means (zero when none).  MKA
+// reading note, method section 3 (fuse the tiers, then project once); the
+// landing page's abstract calls the variant broadcast-routed: each lambda is
+// one scalar per token and tier, applied to every channel.
+//
+// Formed in float32 and rounded once to the storage type, which is the operand
+// type of the K/V projection that follows.
+#include "kernels.h"
+
+namespace mka {
+
+template <typename T>
+__global__ __launch_bounds__(256) void fuse_mix_kernel(const T* __restrict__ x,
+                                                       const float* __restrict__ l2,
+                                                       const float* __restrict__ means, int nb_cap,
+                                                       const int32_t* __restrict__ idx,
+                                                       const float* __restrict__ lam, int seq, int D,
+                                                       int R, T* __restrict__ xf) {
+  const int64_t row = blockIdx.x;  // b * seq + t
+  const int b = static_cast<int>(row / seq);
+  const int ch = blockIdx.y * 1024 + threadIdx.x * 4;
+  if (ch >= D) return;
+  const float l1w = lam[row * 3 + 0], l2w = lam[row * 3 + 1], l3w = lam[row * 3 + 2];
+  const int32_t* sel = idx + row * R;
+  const float* mb = means + static_cast<int64_t>(b) * nb_cap * D + ch;
+  float l3[4] = {0.f, 0.f, 0.f, 0.f};
+  int cnt = 0;
+  for (int i = 0; i < R; ++i) {
+    const int blk = sel[i];
+    if (blk < 0) continue;
+    float m[4];
+    load4(mb + static_cast<int64_t>(blk) * D, m);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) l3[k] += m[k];
+    ++cnt;
+  }
+  float xv[4], sv[4], out[4];
+  load4(x + row * D + ch, xv);
+  load4(l2 + row * D + ch, sv);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float m = cnt ? l3[k] / static_cast<float>(cnt) : 0.f;
+    out[k] = l1w * xv[k] + l2w * sv[k] + l3w * m;
+  }
+  store4(xf + row * D + ch, out);
+}
+
+template <typename T>
+hipError_t fuse_mix(const T* x, const float* l2, const float* means, int nb_cap,
+                    const int32_t* idx, const float* lam, int B, int seq, int D, int R, T* xf,
+                    hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(B) * seq), (D + 1023) / 1024);
+  hipLaunchKernelGGL(fuse_mix_kernel<T>, grid, dim3(256), 0, s, x, l2, means, nb_cap, idx, lam, seq,
+                     D, R, xf);
+  return hipGetLastError();
+}
+
+template hipError_t fuse_mix<float>(const float*, const float*, const float*, int, const int32_t*,
+                                    const float*, int, int, int, int, float*, hipStream_t);
+template hipError_t fuse_mix<bf16_t>(const bf16_t*, const float*, const float*, int,
+                                     const int32_t*, const float*, int, int, int, int, bf16_t*,
+                                     hipStream_t);
+
+}  // namespace mka

@@ -1,0 +1,60 @@
+// Dense products used by the layer: Q = X W_q and [K|V] = X_fused [W_k|W_v].
+// Weights are stored [out, in], so both MFMA operands are contiguous along
+// the reduction dimension ("NT" product C[m][n] = sum_k A[m][k] * B[n][k]).
+#pragma once
+
+#include "common.h"
+
+namespace mka {
+
+// Row-major store C[m * ldc + n].
+template <typename T>
+struct EpiStore {
+  T* c;
+  int ldc;
+  __device__ __forceinline__ void operator()(int m, int n, float v) const {
+    c[static_cast<int64_t>(m) * ldc + n] = Elem<T>::from_f32(v);
+  }
+};
+
+// Scatter into the head-major fused KV cache [B, G, t_cap, dh]: row m is token
+// t = m % seq of sequence b = m / seq, stored at cache row pos0 + t; columns
+// [0, G*dh) are K and [G*dh, 2*G*dh) are V.
+template <typename T>
+struct EpiKV {
+  T* k;
+  T* v;
+  int seq;
+  int n_kv_heads;
+  int head_dim;
+  int64_t t_cap;
+  int64_t pos0;
+  __device__ __forceinline__ void operator()(int m, int n, float val) const {
+    const int kvw = n_kv_heads * head_dim;
+    T* base = n < kvw ? k : v;
+    const int nn = n < kvw ? n : n - kvw;
+    const int b = m / seq, t = m - b * seq;
+    const int g = nn / head_dim, d = nn - g * head_dim;
+    base[((static_cast<int64_t>(b) * n_kv_heads + g) * t_cap + pos0 + t) * head_dim + d] =
+        Elem<T>::from_f32(val);
+  }
+};
+
+// Launchers (defined in gemm.hip).  B rows [0, n_split) come from b0, rows
+// [n_split, N) from b1 (row n - n_split); pass n_split = N for one matrix.
+template <class Epi>
+hipError_t gemm_bf16(const bf16_t* a, int lda, const bf16_t* b0, const bf16_t* b1, int n_split,
+                     int M, int N, int K, const Epi& epi, hipStream_t s);
+template <class Epi>
+hipError_t gemm_f32(const float* a, int lda, const float* b0, const float* b1, int n_split,
+                    int M, int N, int K, const Epi& epi, hipStream_t s);
+// Small-M product (M <= 8), one wave per output column: the decode path.
+template <typename T, class Epi>
+hipError_t gemv(const T* a, int lda, int M, const T* b0, const T* b1, int n_split, int N, int K,
+                const Epi& epi, hipStream_t s);
+
+// Tile of gemm_bf16; it needs K % kGemmBK == 0 and 16-byte aligned rows
+// (checked by the host layer before launching).
+constexpr int kGemmBM = 128, kGemmBN = 128, kGemmBK = 64;
+
+}  // namespace mka

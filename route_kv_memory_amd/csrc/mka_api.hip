@@ -1,0 +1,460 @@
+// C ABI of the FastMKA layer forward: argument validation, workspace layout and
+// dispatch to the kernels.  Every check runs before the first launch of a call,
+// so a rejected call has enqueued nothing.
+#include <cmath>
+#include <initializer_list>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/mka.h"
+#include "gemm.h"
+#include "kernels.h"
+
+using namespace mka;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int hip_fail(const char* where, hipError_t e) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", where, hipGetErrorString(e),
+                static_cast<int>(e));
+  return MKA_ERR_HIP;
+}
+
+#define MKA_CHECK(cond, code) \
+  do {                        \
+    if (!(cond)) return (code); \
+  } while (0)
+
+#define MKA_LAUNCH(where, expr)                     \
+  do {                                              \
+    const hipError_t e_ = (expr);                   \
+    if (e_ != hipSuccess) return hip_fail(where, e_); \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t el_size(const mka_dims* d) { return d->dtype == MKA_BF16 ? 2 : 4; }
+
+size_t round256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+// Shape checks shared by every call.
+int check_dims(const mka_dims* d) {
+  MKA_CHECK(d != nullptr, MKA_ERR_INVALID);
+  MKA_CHECK(d->batch >= 1 && d->seq >= 1 && d->d_model >= 1 && d->n_heads >= 1 &&
+                d->n_kv_heads >= 1 && d->router_hidden >= 1 && d->block >= 1 && d->top_r >= 1,
+            MKA_ERR_INVALID);
+  MKA_CHECK(d->n_heads % d->n_kv_heads == 0, MKA_ERR_INVALID);
+  MKA_CHECK(d->hash_bits >= 1 && d->hash_bits <= 64, MKA_ERR_INVALID);
+  MKA_CHECK(std::isfinite(d->ema_decay) && d->ema_decay >= 0.f && d->ema_decay < 1.f,
+            MKA_ERR_INVALID);
+  MKA_CHECK(d->dtype == MKA_F32 || d->dtype == MKA_BF16, MKA_ERR_INVALID);
+  MKA_CHECK(d->head_dim == 64 || d->head_dim == 128, MKA_ERR_UNSUPPORTED);
+  MKA_CHECK(d->top_r <= 32, MKA_ERR_UNSUPPORTED);
+  MKA_CHECK(d->router_hidden <= 256, MKA_ERR_UNSUPPORTED);
+  MKA_CHECK(d->n_heads / d->n_kv_heads <= 32, MKA_ERR_UNSUPPORTED);
+  const int64_t qw = static_cast<int64_t>(d->n_heads) * d->head_dim;
+  MKA_CHECK(static_cast<int64_t>(d->batch) * d->seq <= (1LL << 31) - 1, MKA_ERR_INVALID);
+  if (d->dtype == MKA_BF16) {
+    MKA_CHECK(d->d_model % 64 == 0 && qw % 64 == 0, MKA_ERR_UNSUPPORTED);
+  } else {
+    MKA_CHECK(d->d_model % 4 == 0 && qw % 4 == 0, MKA_ERR_UNSUPPORTED);
+  }
+  return MKA_OK;
+}
+
+int rows_of(const mka_dims* d) { return d->batch * d->seq; }
+
+size_t ema_ws(const mka_dims* d) { return round256(ema_ws_bytes(d->batch, d->seq, d->d_model)); }
+size_t fuse_ws(const mka_dims* d) {
+  return round256(static_cast<size_t>(rows_of(d)) * d->d_model * el_size(d));
+}
+size_t retrieve_ws(const mka_dims* d) {
+  return rows_of(d) <= kFewRows ? round256(retrieve_few_ws_bytes(rows_of(d), d->d_model)) : 0;
+}
+size_t decode_ws(const mka_dims* d, int64_t cache_len) {
+  if (d->dtype != MKA_BF16) return 0;
+  return round256(attn_decode_ws_bytes(d->batch, d->n_heads, d->head_dim, cache_len));
+}
+
+// ---------------------------------------------------------------- per-step bodies
+// Each body assumes check_dims passed and its pointers were validated.
+
+int do_route(const mka_dims* d, const void* x, const void* w_q, const void* w_r1, const void* w_r2,
+             void* q_out, float* lam, hipStream_t s) {
+  const int M = rows_of(d), D = d->d_model, qw = d->n_heads * d->head_dim, r = d->router_hidden;
+  if (d->dtype == MKA_BF16) {
+    const bf16_t* xb = static_cast<const bf16_t*>(x);
+    const bf16_t* wq = static_cast<const bf16_t*>(w_q);
+    bf16_t* q = static_cast<bf16_t*>(q_out);
+    const EpiStore<bf16_t> epi{q, qw};
+    if (M <= kFewRows)
+      MKA_LAUNCH("route/q_gemv", gemv<bf16_t>(xb, D, M, wq, wq, qw, qw, D, epi, s));
+    else
+      MKA_LAUNCH("route/q_gemm", gemm_bf16(xb, D, wq, wq, qw, M, qw, D, epi, s));
+    const bf16_t* w1 = static_cast<const bf16_t*>(w_r1);
+    const bf16_t* w2 = static_cast<const bf16_t*>(w_r2);
+    if (M > kFewRows && (r == 32 || r == 64))
+      MKA_LAUNCH("route/router", router_bf16_mfma(q, M, qw, w1, r, w2, lam, s));
+    else
+      MKA_LAUNCH("route/router", router_rowwise<bf16_t>(q, M, qw, w1, r, w2, lam, s));
+  } else {
+    const float* xf = static_cast<const float*>(x);
+    const float* wq = static_cast<const float*>(w_q);
+    float* q = static_cast<float*>(q_out);
+    const EpiStore<float> epi{q, qw};
+    if (M <= kFewRows)
+      MKA_LAUNCH("route/q_gemv", gemv<float>(xf, D, M, wq, wq, qw, qw, D, epi, s));
+    else
+      MKA_LAUNCH("route/q_gemm", gemm_f32(xf, D, wq, wq, qw, M, qw, D, epi, s));
+    MKA_LAUNCH("route/router",
+               router_rowwise<float>(q, M, qw, static_cast<const float*>(w_r1), r,
+                                     static_cast<const float*>(w_r2), lam, s));
+  }
+  return MKA_OK;
+}
+
+int do_ema(const mka_dims* d, const void* x, int64_t pos0, float* state_io, float* acc_io,
+           float* l2, float* means, int nb_cap, void* ws, hipStream_t s) {
+  float* w = static_cast<float*>(ws);
+  if (d->dtype == MKA_BF16)
+    MKA_LAUNCH("ema_scan", ema_scan<bf16_t>(static_cast<const bf16_t*>(x), d->batch, d->seq,
+                                            d->d_model, pos0, d->block, d->ema_decay, state_io,
+                                            acc_io, l2, means, nb_cap, w, s));
+  else
+    MKA_LAUNCH("ema_scan", ema_scan<float>(static_cast<const float*>(x), d->batch, d->seq,
+                                           d->d_model, pos0, d->block, d->ema_decay, state_io,
+                                           acc_io, l2, means, nb_cap, w, s));
+  return MKA_OK;
+}
+
+int do_index(const mka_dims* d, const float* means, int nb_cap, int first, int n,
+             const float* proj, uint64_t* bh, hipStream_t s) {
+  if (n <= 0) return MKA_OK;
+  const int64_t D = d->d_model;
+  MKA_LAUNCH("l3_index", simhash_rows(means + first * D, static_cast<int64_t>(nb_cap) * D, n,
+                                      d->batch, d->d_model, proj, d->hash_bits, bh + first,
+                                      nb_cap, s));
+  return MKA_OK;
+}
+
+int do_retrieve(const mka_dims* d, const float* l2, const float* proj, const uint64_t* bh,
+                int nb_cap, int64_t pos0, uint64_t* keys, int32_t* idx, void* ws, hipStream_t s) {
+  const int rows = rows_of(d);
+  if (rows <= kFewRows) {
+    MKA_LAUNCH("l3_retrieve", retrieve_few(l2, d->batch, d->seq, d->d_model, proj, d->hash_bits, bh,
+                                           nb_cap, d->block, d->top_r, pos0, keys, idx, ws, s));
+  } else {
+    MKA_LAUNCH("l3_retrieve/keys",
+               simhash_rows(l2, static_cast<int64_t>(d->seq) * d->d_model, d->seq, d->batch,
+                            d->d_model, proj, d->hash_bits, keys, d->seq, s));
+    MKA_LAUNCH("l3_retrieve/topr", topr_rows(keys, d->batch, d->seq, pos0, bh, nb_cap, d->block,
+                                             d->top_r, idx, s));
+  }
+  return MKA_OK;
+}
+
+int do_fuse_kv(const mka_dims* d, const void* x, const float* l2, const float* means, int nb_cap,
+               const int32_t* idx, const float* lam, const void* w_k, const void* w_v, void* kc,
+               void* vc, int64_t pos0, int64_t t_cap, void* ws, hipStream_t s) {
+  const int M = rows_of(d), D = d->d_model, kvw = d->n_kv_heads * d->head_dim;
+  if (d->dtype == MKA_BF16) {
+    bf16_t* xf = static_cast<bf16_t*>(ws);
+    MKA_LAUNCH("fuse", fuse_mix<bf16_t>(static_cast<const bf16_t*>(x), l2, means, nb_cap, idx, lam,
+                                        d->batch, d->seq, D, d->top_r, xf, s));
+    const EpiKV<bf16_t> epi{static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), d->seq,
+                            d->n_kv_heads, d->head_dim, t_cap, pos0};
+    const bf16_t* wk = static_cast<const bf16_t*>(w_k);
+    const bf16_t* wv = static_cast<const bf16_t*>(w_v);
+    if (M <= kFewRows)
+      MKA_LAUNCH("kv_gemv", gemv<bf16_t>(xf, D, M, wk, wv, kvw, 2 * kvw, D, epi, s));
+    else
+      MKA_LAUNCH("kv_gemm", gemm_bf16(xf, D, wk, wv, kvw, M, 2 * kvw, D, epi, s));
+  } else {
+    float* xf = static_cast<float*>(ws);
+    MKA_LAUNCH("fuse", fuse_mix<float>(static_cast<const float*>(x), l2, means, nb_cap, idx, lam,
+                                       d->batch, d->seq, D, d->top_r, xf, s));
+    const EpiKV<float> epi{static_cast<float*>(kc), static_cast<float*>(vc), d->seq, d->n_kv_heads,
+                           d->head_dim, t_cap, pos0};
+    const float* wk = static_cast<const float*>(w_k);
+    const float* wv = static_cast<const float*>(w_v);
+    if (M <= kFewRows)
+      MKA_LAUNCH("kv_gemv", gemv<float>(xf, D, M, wk, wv, kvw, 2 * kvw, D, epi, s));
+    else
+      MKA_LAUNCH("kv_gemm", gemm_f32(xf, D, wk, wv, kvw, M, 2 * kvw, D, epi, s));
+  }
+  return MKA_OK;
+}
+
+int do_attn_prefill(const mka_dims* d, const void* q, const void* kc, const void* vc,
+                    int64_t t_cap, int64_t pos0, void* o, hipStream_t s) {
+  if (d->dtype == MKA_BF16)
+    MKA_LAUNCH("attn_prefill",
+               attn_prefill<bf16_t>(static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(kc),
+                                    static_cast<const bf16_t*>(vc), static_cast<bf16_t*>(o),
+                                    d->batch, d->seq, d->n_heads, d->n_kv_heads, d->head_dim,
+                                    t_cap, pos0, s));
+  else
+    MKA_LAUNCH("attn_prefill",
+               attn_prefill<float>(static_cast<const float*>(q), static_cast<const float*>(kc),
+                                   static_cast<const float*>(vc), static_cast<float*>(o), d->batch,
+                                   d->seq, d->n_heads, d->n_kv_heads, d->head_dim, t_cap, pos0, s));
+  return MKA_OK;
+}
+
+int do_attn_decode(const mka_dims* d, const void* q, const void* kc, const void* vc, int64_t t_cap,
+                   int64_t cache_len, void* o, void* ws, hipStream_t s) {
+  if (d->dtype == MKA_BF16)
+    MKA_LAUNCH("attn_decode",
+               attn_decode_bf16(static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(kc),
+                                static_cast<const bf16_t*>(vc), static_cast<bf16_t*>(o), d->batch,
+                                d->n_heads, d->n_kv_heads, d->head_dim, t_cap, cache_len, ws, s));
+  else  // one query row at position cache_len - 1
+    MKA_LAUNCH("attn_decode",
+               attn_prefill<float>(static_cast<const float*>(q), static_cast<const float*>(kc),
+                                   static_cast<const float*>(vc), static_cast<float*>(o), d->batch,
+                                   1, d->n_heads, d->n_kv_heads, d->head_dim, t_cap, cache_len - 1,
+                                   s));
+  return MKA_OK;
+}
+
+// Blocks whose last token lies in [pos0, pos0 + seq): [first, first + n).
+void completed_blocks(const mka_dims* d, int64_t pos0, int64_t* first, int64_t* n) {
+  *first = pos0 / d->block;
+  const int64_t end = (pos0 + d->seq) / d->block;  // one past the last completed block
+  *n = end > *first ? end - *first : 0;
+}
+
+bool ptrs_ok(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p == nullptr || !aligned16(p)) return false;
+  return true;
+}
+
+constexpr int64_t kMaxDecodeCache = static_cast<int64_t>(kDecodeChunk) * 4096;
+
+}  // namespace
+
+extern "C" {
+
+const char* mka_version(void) { return "mka 0.1.0 (gfx950)"; }
+
+const char* mka_last_error(void) { return g_last_error; }
+
+const char* mka_status_string(int status) {
+  switch (status) {
+    case MKA_OK: return "ok";
+    case MKA_ERR_INVALID: return "invalid argument";
+    case MKA_ERR_UNSUPPORTED: return "unsupported shape or type";
+    case MKA_ERR_WORKSPACE: return "workspace too small";
+    case MKA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+size_t mka_workspace_bytes(const mka_dims* d, int op, int64_t cache_len) {
+  if (check_dims(d) != MKA_OK) return 0;
+  switch (op) {
+    case MKA_OP_EMA_SCAN: return ema_ws(d);
+    case MKA_OP_FUSE_KV: return fuse_ws(d);
+    case MKA_OP_RETRIEVE: return retrieve_ws(d);
+    case MKA_OP_ATTN_DECODE: return cache_len > 0 ? decode_ws(d, cache_len) : 0;
+    case MKA_OP_PREFILL: {
+      size_t w = ema_ws(d);
+      if (fuse_ws(d) > w) w = fuse_ws(d);
+      if (retrieve_ws(d) > w) w = retrieve_ws(d);
+      return w;
+    }
+    case MKA_OP_DECODE_STEP: {
+      if (d->seq != 1) return 0;
+      size_t w = fuse_ws(d);
+      if (retrieve_ws(d) > w) w = retrieve_ws(d);
+      if (cache_len > 0 && decode_ws(d, cache_len) > w) w = decode_ws(d, cache_len);
+      return w;
+    }
+    default: return 0;
+  }
+}
+
+int mka_route(const mka_dims* d, const void* x, const void* w_q, const void* w_r1,
+              const void* w_r2, void* q_out, float* lambda_out, void* stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  MKA_CHECK(ptrs_ok({x, w_q, w_r1, w_r2, q_out, lambda_out}), MKA_ERR_INVALID);
+  return do_route(d, x, w_q, w_r1, w_r2, q_out, lambda_out, static_cast<hipStream_t>(stream));
+}
+
+int mka_ema_scan(const mka_dims* d, const void* x, int64_t pos0, float* state_io,
+                 float* block_acc_io, float* l2_out, float* block_means, int32_t nb_cap, void* ws,
+                 size_t ws_bytes, void* stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  MKA_CHECK(ptrs_ok({x, state_io, block_acc_io, l2_out}), MKA_ERR_INVALID);
+  MKA_CHECK(pos0 >= 0 && nb_cap >= 0, MKA_ERR_INVALID);
+  int64_t first, n;
+  completed_blocks(d, pos0, &first, &n);
+  if (n > 0) {
+    MKA_CHECK(ptrs_ok({block_means}), MKA_ERR_INVALID);
+    MKA_CHECK(first + n <= nb_cap, MKA_ERR_INVALID);
+  }
+  if (ema_ws(d) > 0) {
+    MKA_CHECK(ptrs_ok({ws}), MKA_ERR_WORKSPACE);
+    MKA_CHECK(ws_bytes >= ema_ws(d), MKA_ERR_WORKSPACE);
+  }
+  return do_ema(d, x, pos0, state_io, block_acc_io, l2_out, block_means, nb_cap, ws,
+                static_cast<hipStream_t>(stream));
+}
+
+int mka_l3_index(const mka_dims* d, const float* block_means, int32_t nb_cap, int32_t first_block,
+                 int32_t n_blocks, const float* proj, uint64_t* block_hash, void* stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  MKA_CHECK(first_block >= 0 && n_blocks >= 0 &&
+                static_cast<int64_t>(first_block) + n_blocks <= nb_cap,
+            MKA_ERR_INVALID);
+  if (n_blocks == 0) return MKA_OK;
+  MKA_CHECK(ptrs_ok({block_means, proj}) && block_hash != nullptr &&
+                (reinterpret_cast<uintptr_t>(block_hash) & 7u) == 0,
+            MKA_ERR_INVALID);
+  return do_index(d, block_means, nb_cap, first_block, n_blocks, proj, block_hash,
+                  static_cast<hipStream_t>(stream));
+}
+
+int mka_l3_retrieve(const mka_dims* d, const float* l2, const float* proj,
+                    const uint64_t* block_hash, int32_t nb_cap, int64_t pos0, uint64_t* key_out,
+                    int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  MKA_CHECK(ptrs_ok({l2, proj, key_out, idx_out}), MKA_ERR_INVALID);
+  MKA_CHECK(pos0 >= 0 && nb_cap >= 0, MKA_ERR_INVALID);
+  MKA_CHECK((pos0 + d->seq - 1) / d->block <= nb_cap, MKA_ERR_INVALID);
+  MKA_CHECK(nb_cap < 0xFFFFFF, MKA_ERR_UNSUPPORTED);
+  if ((pos0 + d->seq - 1) / d->block > 0)
+    MKA_CHECK(block_hash != nullptr && (reinterpret_cast<uintptr_t>(block_hash) & 7u) == 0,
+              MKA_ERR_INVALID);
+  if (retrieve_ws(d) > 0) {
+    MKA_CHECK(ptrs_ok({ws}), MKA_ERR_WORKSPACE);
+    MKA_CHECK(ws_bytes >= retrieve_ws(d), MKA_ERR_WORKSPACE);
+  }
+  return do_retrieve(d, l2, proj, block_hash, nb_cap, pos0, key_out, idx_out, ws,
+                     static_cast<hipStream_t>(stream));
+}
+
+int mka_fuse_kv_proj(const mka_dims* d, const void* x, const float* l2, const float* block_means,
+                     int32_t nb_cap, const int32_t* idx, const float* lambda, const void* w_k,
+                     const void* w_v, void* k_cache, void* v_cache, int64_t pos0, int64_t t_cap,
+                     void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  MKA_CHECK(ptrs_ok({x, l2, idx, lambda, w_k, w_v, k_cache, v_cache}), MKA_ERR_INVALID);
+  MKA_CHECK(pos0 >= 0 && nb_cap >= 0 && pos0 + d->seq <= t_cap, MKA_ERR_INVALID);
+  if ((pos0 + d->seq - 1) / d->block > 0) MKA_CHECK(ptrs_ok({block_means}), MKA_ERR_INVALID);
+  MKA_CHECK(ptrs_ok({ws}), MKA_ERR_WORKSPACE);
+  MKA_CHECK(ws_bytes >= fuse_ws(d), MKA_ERR_WORKSPACE);
+  return do_fuse_kv(d, x, l2, block_means, nb_cap, idx, lambda, w_k, w_v, k_cache, v_cache, pos0,
+                    t_cap, ws, static_cast<hipStream_t>(stream));
+}
+
+int mka_attn_prefill(const mka_dims* d, const void* q, const void* k_cache, const void* v_cache,
+                     int64_t t_cap, int64_t pos0, void* o, void* stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  MKA_CHECK(ptrs_ok({q, k_cache, v_cache, o}), MKA_ERR_INVALID);
+  MKA_CHECK(pos0 >= 0 && pos0 + d->seq <= t_cap, MKA_ERR_INVALID);
+  return do_attn_prefill(d, q, k_cache, v_cache, t_cap, pos0, o, static_cast<hipStream_t>(stream));
+}
+
+int mka_attn_decode(const mka_dims* d, const void* q, const void* k_cache, const void* v_cache,
+                    int64_t t_cap, int64_t cache_len, void* o, void* ws, size_t ws_bytes,
+                    void* stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  MKA_CHECK(d->seq == 1, MKA_ERR_INVALID);
+  MKA_CHECK(ptrs_ok({q, k_cache, v_cache, o}), MKA_ERR_INVALID);
+  MKA_CHECK(cache_len >= 1 && cache_len <= t_cap, MKA_ERR_INVALID);
+  MKA_CHECK(cache_len <= kMaxDecodeCache, MKA_ERR_UNSUPPORTED);
+  if (decode_ws(d, cache_len) > 0) {
+    MKA_CHECK(ptrs_ok({ws}), MKA_ERR_WORKSPACE);
+    MKA_CHECK(ws_bytes >= decode_ws(d, cache_len), MKA_ERR_WORKSPACE);
+  }
+  return do_attn_decode(d, q, k_cache, v_cache, t_cap, cache_len, o, ws,
+                        static_cast<hipStream_t>(stream));
+}
+
+static int check_layer_args(const mka_dims* d, const void* x, int64_t pos0, const mka_weights* w,
+                            const mka_state* st, const mka_outputs* out) {
+  MKA_CHECK(w != nullptr && st != nullptr && out != nullptr, MKA_ERR_INVALID);
+  MKA_CHECK(ptrs_ok({x, w->w_q, w->w_k, w->w_v, w->w_r1, w->w_r2, w->proj}), MKA_ERR_INVALID);
+  MKA_CHECK(ptrs_ok({st->ema_state, st->block_acc, st->block_means, st->k_cache, st->v_cache}),
+            MKA_ERR_INVALID);
+  MKA_CHECK(st->block_hash != nullptr && (reinterpret_cast<uintptr_t>(st->block_hash) & 7u) == 0,
+            MKA_ERR_INVALID);
+  MKA_CHECK(ptrs_ok({out->q, out->lambda, out->l2, out->key, out->idx, out->o}), MKA_ERR_INVALID);
+  MKA_CHECK(pos0 >= 0 && st->nb_cap >= 1 && st->nb_cap < 0xFFFFFF, MKA_ERR_INVALID);
+  MKA_CHECK(pos0 + d->seq <= st->t_cap, MKA_ERR_INVALID);
+  MKA_CHECK((pos0 + d->seq) / d->block <= st->nb_cap, MKA_ERR_INVALID);
+  return MKA_OK;
+}
+
+int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weights* w,
+                const mka_state* st, const mka_outputs* out, void* ws, size_t ws_bytes,
+                void* stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  rc = check_layer_args(d, x, pos0, w, st, out);
+  if (rc) return rc;
+  const size_t need = mka_workspace_bytes(d, MKA_OP_PREFILL, 0);
+  MKA_CHECK(ws_bytes >= need, MKA_ERR_WORKSPACE);
+  MKA_CHECK(need == 0 || ptrs_ok({ws}), MKA_ERR_WORKSPACE);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int64_t first, n;
+  completed_blocks(d, pos0, &first, &n);
+  if ((rc = do_route(d, x, w->w_q, w->w_r1, w->w_r2, out->q, out->lambda, s))) return rc;
+  if ((rc = do_ema(d, x, pos0, st->ema_state, st->block_acc, out->l2, st->block_means, st->nb_cap,
+                   ws, s)))
+    return rc;
+  if ((rc = do_index(d, st->block_means, st->nb_cap, static_cast<int>(first), static_cast<int>(n),
+                     w->proj, st->block_hash, s)))
+    return rc;
+  if ((rc = do_retrieve(d, out->l2, w->proj, st->block_hash, st->nb_cap, pos0, out->key, out->idx,
+                        ws, s)))
+    return rc;
+  if ((rc = do_fuse_kv(d, x, out->l2, st->block_means, st->nb_cap, out->idx, out->lambda, w->w_k,
+                       w->w_v, st->k_cache, st->v_cache, pos0, st->t_cap, ws, s)))
+    return rc;
+  return do_attn_prefill(d, out->q, st->k_cache, st->v_cache, st->t_cap, pos0, out->o, s);
+}
+
+int mka_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_weights* w,
+                    const mka_state* st, const mka_outputs* out, void* ws, size_t ws_bytes,
+                    void* stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  MKA_CHECK(d->seq == 1, MKA_ERR_INVALID);
+  rc = check_layer_args(d, x, pos, w, st, out);
+  if (rc) return rc;
+  MKA_CHECK(pos + 1 <= kMaxDecodeCache, MKA_ERR_UNSUPPORTED);
+  const size_t need = mka_workspace_bytes(d, MKA_OP_DECODE_STEP, pos + 1);
+  MKA_CHECK(ws_bytes >= need, MKA_ERR_WORKSPACE);
+  MKA_CHECK(need == 0 || ptrs_ok({ws}), MKA_ERR_WORKSPACE);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((rc = do_route(d, x, w->w_q, w->w_r1, w->w_r2, out->q, out->lambda, s))) return rc;
+  if ((rc = do_ema(d, x, pos, st->ema_state, st->block_acc, out->l2, st->block_means, st->nb_cap,
+                   nullptr, s)))
+    return rc;
+  if ((rc = do_retrieve(d, out->l2, w->proj, st->block_hash, st->nb_cap, pos, out->key, out->idx,
+                        ws, s)))
+    return rc;
+  if ((rc = do_fuse_kv(d, x, out->l2, st->block_means, st->nb_cap, out->idx, out->lambda, w->w_k,
+                       w->w_v, st->k_cache, st->v_cache, pos, st->t_cap, ws, s)))
+    return rc;
+  if ((rc = do_attn_decode(d, out->q, st->k_cache, st->v_cache, st->t_cap, pos + 1, out->o, ws, s)))
+    return rc;
+  if ((pos + 1) % d->block == 0)
+    return do_index(d, st->block_means, st->nb_cap, static_cast<int>((pos + 1) / d->block - 1), 1,
+                    w->proj, st->block_hash, s);
+  return MKA_OK;
+}
+
+}  // extern "C"

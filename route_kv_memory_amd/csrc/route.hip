@@ -1,0 +1,149 @@
+// Router of the FastMKA layer: lambda = softmax(GELU(q W_r1) W_r2), one
+// 3-vector per token over the tiers (L1, L2, L3).  MKA reading note, method
+// section 2 (routing gate from the query, per token and layer).
+#include "kernels.h"
+
+namespace mka {
+
+// Softmax of three logits, max-shifted.
+__device__ __forceinline__ void softmax3(const float* z, float* out) {
+  const float m = fmaxf(z[0], fmaxf(z[1], z[2]));
+  const float e0 = expf(z[0] - m), e1 = expf(z[1] - m), e2 = expf(z[2] - m);
+  const float inv = 1.0f / (e0 + e1 + e2);
+  out[0] = e0 * inv;
+  out[1] = e1 * inv;
+  out[2] = e2 * inv;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA router (bf16): a workgroup takes 32 tokens; its 4 waves split the
+// q-width reduction into quarters, each producing a 32 x r block of hidden
+// pre-activations with MFMA 32x32x16 (operands read straight from global:
+// the token's q row and the weight row are both contiguous along the
+// reduction).  The quarters are summed in LDS, GELU applied, then the r -> 3
+// layer and the softmax run one thread per token.
+// ---------------------------------------------------------------------------
+template <int NB>  // NB = r / 32 output blocks
+__global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restrict__ Q, int M, int qw,
+                                                          const bf16_t* __restrict__ W1,
+                                                          const bf16_t* __restrict__ W2,
+                                                          float* __restrict__ lam) {
+  constexpr int R = NB * 32;
+  __shared__ float part[4][32][R + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int row0 = blockIdx.x * 32;
+  const int row = row0 + l32;
+  const int quarter = qw / 4;
+  const int k_begin = wave * quarter;
+
+  f32x16 acc[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) acc[j] = f32x16{};
+  const bf16_t* qrow = Q + static_cast<int64_t>(row < M ? row : 0) * qw + 8 * h;
+  for (int k = k_begin; k < k_begin + quarter; k += 16) {
+    bf16x8 a = *reinterpret_cast<const bf16x8*>(qrow + k);
+    if (row >= M) a = bf16x8{};
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const bf16x8 b =
+          *reinterpret_cast<const bf16x8*>(W1 + static_cast<int64_t>(j * 32 + l32) * qw + k + 8 * h);
+      acc[j] = mfma32x32x16(a, b, acc[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part[wave][acc_row(r, h)][j * 32 + l32] = acc[j][r];
+  __syncthreads();
+  for (int e = tid; e < 32 * R; e += 256) {
+    const int rr = e / R, n = e % R;
+    const float z = part[0][rr][n] + part[1][rr][n] + part[2][rr][n] + part[3][rr][n];
+    part[0][rr][n] = gelu(z);
+  }
+  __syncthreads();
+  if (tid < 32 && row0 + tid < M) {
+    float z[3];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      float sum = 0.f;
+      for (int n = 0; n < R; ++n) sum = fmaf(part[0][tid][n], bf16_to_f32(W2[c * R + n]), sum);
+      z[c] = sum;
+    }
+    float out[3];
+    softmax3(z, out);
+    float* dst = lam + static_cast<int64_t>(row0 + tid) * 3;
+    dst[0] = out[0];
+    dst[1] = out[1];
+    dst[2] = out[2];
+  }
+}
+
+hipError_t router_bf16_mfma(const bf16_t* q, int M, int qw, const bf16_t* w1, int r,
+                            const bf16_t* w2, float* lam, hipStream_t s) {
+  const dim3 grid((M + 31) / 32);
+  if (r == 64)
+    hipLaunchKernelGGL(router_mfma_kernel<2>, grid, dim3(256), 0, s, q, M, qw, w1, w2, lam);
+  else
+    hipLaunchKernelGGL(router_mfma_kernel<1>, grid, dim3(256), 0, s, q, M, qw, w1, w2, lam);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Row-wise router: one workgroup per token.  Hidden unit n is a dot product
+// computed by one wave (lanes stride the q width), GELU, then thread 0 forms
+// the three logits and the softmax.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void router_rowwise_kernel(const T* __restrict__ Q, int qw,
+                                                             const T* __restrict__ W1, int r,
+                                                             const T* __restrict__ W2,
+                                                             float* __restrict__ lam) {
+  __shared__ float hid[256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const T* q = Q + row * qw;
+  constexpr int V = Vec16<T>::kN;
+  const int kv = (qw / V) * V;
+  for (int n = wave; n < r; n += 4) {
+    const T* w = W1 + static_cast<int64_t>(n) * qw;
+    float acc = 0.f;
+    for (int k = lane * V; k < kv; k += 64 * V) {
+      float a[V], b[V];
+      Vec16<T>::load(q + k, a);
+      Vec16<T>::load(w + k, b);
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc = fmaf(a[i], b[i], acc);
+    }
+    for (int k = kv + lane; k < qw; k += 64) acc = fmaf(Elem<T>::to_f32(q[k]), Elem<T>::to_f32(w[k]), acc);
+    acc = wave_sum(acc);
+    if (lane == 0) hid[n] = gelu(acc);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float z[3];
+    for (int c = 0; c < 3; ++c) {
+      float sum = 0.f;
+      for (int n = 0; n < r; ++n) sum = fmaf(hid[n], Elem<T>::to_f32(W2[c * r + n]), sum);
+      z[c] = sum;
+    }
+    float out[3];
+    softmax3(z, out);
+    lam[row * 3 + 0] = out[0];
+    lam[row * 3 + 1] = out[1];
+    lam[row * 3 + 2] = out[2];
+  }
+}
+
+template <typename T>
+hipError_t router_rowwise(const T* q, int M, int qw, const T* w1, int r, const T* w2, float* lam,
+                          hipStream_t s) {
+  hipLaunchKernelGGL(router_rowwise_kernel<T>, dim3(M), dim3(256), 0, s, q, qw, w1, r, w2, lam);
+  return hipGetLastError();
+}
+
+template hipError_t router_rowwise<float>(const float*, int, int, const float*, int, const float*,
+                                          float*, hipStream_t);
+template hipError_t router_rowwise<bf16_t>(const bf16_t*, int, int, const bf16_t*, int,
+                                           const bf16_t*, float*, hipStream_t);
+
+}  // namespace mka

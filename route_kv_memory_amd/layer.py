@@ -1,0 +1,96 @@
+"""Device buffers of one FastMKA layer, driven through the C ABI.
+
+``Layer`` owns the weights, the decode state (EMA state, partial block sum,
+block means and codes, fused KV cache) and per-call output buffers as torch
+tensors, and calls ``mka_prefill`` / ``mka_decode_step``.  It allocates and
+passes pointers; every step of the layer runs in the HIP library.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import mka
+
+_TORCH = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def to_device(a: np.ndarray, dtype: str | None = None, device="cuda") -> torch.Tensor:
+    """float32 numpy values -> device tensor of the storage type (exact for
+    values representable in it, which is what the input generators return)."""
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(_TORCH[dtype])
+    return t.to(device)
+
+
+class Layer:
+    def __init__(self, shape, weights: dict, *, t_cap: int, nb_cap: int, batch: int | None = None,
+                 device="cuda"):
+        self.shape = shape
+        self.batch = shape.batch if batch is None else batch
+        self.device = device
+        self.t_cap, self.nb_cap = int(t_cap), int(nb_cap)
+        dt = shape.dtype
+        self.tdtype = _TORCH[dt]
+        self.w = {k: to_device(weights[k], dt, device) for k in ("w_q", "w_k", "w_v", "w_r1", "w_r2")}
+        self.w["proj"] = to_device(weights["proj"], None, device)
+        self.weights = mka.Weights(**{k: v.data_ptr() for k, v in self.w.items()})
+        B, D, G, dh = self.batch, shape.d_model, shape.n_kv_heads, shape.head_dim
+        z = dict(device=device)
+        self.st = {
+            "ema_state": torch.zeros(B, D, dtype=torch.float32, **z),
+            "block_acc": torch.zeros(B, D, dtype=torch.float32, **z),
+            "block_means": torch.zeros(B, self.nb_cap, D, dtype=torch.float32, **z),
+            "block_hash": torch.zeros(B, self.nb_cap, dtype=torch.int64, **z),
+            "k_cache": torch.zeros(B, G, self.t_cap, dh, dtype=self.tdtype, **z),
+            "v_cache": torch.zeros(B, G, self.t_cap, dh, dtype=self.tdtype, **z),
+        }
+        self.state = mka.State(nb_cap=self.nb_cap, t_cap=self.t_cap,
+                               **{k: v.data_ptr() for k, v in self.st.items()})
+        self._ws = None
+
+    def dims(self, seq: int) -> mka.Dims:
+        return mka.dims(self.shape, seq=seq, batch=self.batch)
+
+    def outputs(self, seq: int) -> dict:
+        s, B, z = self.shape, self.batch, dict(device=self.device)
+        return {
+            "q": torch.empty(B, seq, s.n_heads, s.head_dim, dtype=self.tdtype, **z),
+            "lambda": torch.empty(B, seq, 3, dtype=torch.float32, **z),
+            "l2": torch.empty(B, seq, s.d_model, dtype=torch.float32, **z),
+            "key": torch.empty(B, seq, dtype=torch.int64, **z),
+            "idx": torch.empty(B, seq, s.top_r, dtype=torch.int32, **z),
+            "o": torch.empty(B, seq, s.n_heads, s.head_dim, dtype=self.tdtype, **z),
+        }
+
+    @staticmethod
+    def _out_struct(out: dict) -> mka.Outputs:
+        return mka.Outputs(q=out["q"].data_ptr(), lambda_=out["lambda"].data_ptr(),
+                           l2=out["l2"].data_ptr(), key=out["key"].data_ptr(),
+                           idx=out["idx"].data_ptr(), o=out["o"].data_ptr())
+
+    def workspace(self, nbytes: int) -> torch.Tensor:
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def prefill(self, x: torch.Tensor, pos0: int = 0, out: dict | None = None, stream=None) -> dict:
+        seq = x.shape[1]
+        d = self.dims(seq)
+        out = self.outputs(seq) if out is None else out
+        need = mka.mka_workspace_bytes(d, mka.MKA_OP_PREFILL)
+        ws = self.workspace(need)
+        mka.mka_prefill(d, x, pos0, self.weights, self.state, self._out_struct(out), ws,
+                        ws.numel(), stream)
+        return out
+
+    def decode_step(self, x_t: torch.Tensor, pos: int, out: dict | None = None, stream=None) -> dict:
+        d = self.dims(1)
+        out = self.outputs(1) if out is None else out
+        need = mka.mka_workspace_bytes(d, mka.MKA_OP_DECODE_STEP, pos + 1)
+        ws = self.workspace(need)
+        mka.mka_decode_step(d, x_t, pos, self.weights, self.state, self._out_struct(out), ws,
+                            ws.numel(), stream)
+        return out

@@ -1,0 +1,232 @@
+"""Thin ctypes binding of the FastMKA C ABI (``include/mka.h``).
+
+The functions carry the C names and arguments.  Array arguments are torch
+tensors on the GPU (contiguous; their device pointer is passed) or ``None``
+for a null pointer; ``stream`` defaults to torch's current stream.  Nothing
+here computes any part of the layer: it marshals arguments and raises
+``MkaError`` on a non-zero status.  The library must be built
+(``python -m route_kv_memory_amd.build``); loading fails loudly otherwise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+__all__ = [
+    "MkaError", "Dims", "Weights", "State", "Outputs", "lib", "dims", "exported_symbols",
+    "header_symbols", "MKA_F32", "MKA_BF16", "MKA_OK", "MKA_ERR_INVALID", "MKA_ERR_UNSUPPORTED",
+    "MKA_ERR_WORKSPACE", "MKA_ERR_HIP", "MKA_OP_EMA_SCAN", "MKA_OP_FUSE_KV", "MKA_OP_ATTN_DECODE",
+    "MKA_OP_PREFILL", "MKA_OP_DECODE_STEP", "MKA_OP_RETRIEVE",
+    "mka_route", "mka_ema_scan", "mka_l3_index", "mka_l3_retrieve", "mka_fuse_kv_proj",
+    "mka_attn_prefill", "mka_attn_decode", "mka_prefill", "mka_decode_step",
+    "mka_workspace_bytes", "mka_status_string", "mka_last_error", "mka_version",
+]
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmka.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "mka.h")
+
+MKA_F32, MKA_BF16 = 0, 1
+MKA_OK, MKA_ERR_INVALID, MKA_ERR_UNSUPPORTED, MKA_ERR_WORKSPACE, MKA_ERR_HIP = 0, -1, -2, -3, -4
+(MKA_OP_EMA_SCAN, MKA_OP_FUSE_KV, MKA_OP_ATTN_DECODE, MKA_OP_PREFILL, MKA_OP_DECODE_STEP,
+ MKA_OP_RETRIEVE) = range(6)
+
+
+class MkaError(RuntimeError):
+    def __init__(self, fn, status):
+        detail = mka_status_string(status)
+        if status == MKA_ERR_HIP:
+            detail += f" ({mka_last_error()})"
+        super().__init__(f"{fn} failed with status {status}: {detail}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("seq", ctypes.c_int32), ("d_model", ctypes.c_int32),
+        ("n_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("router_hidden", ctypes.c_int32), ("block", ctypes.c_int32), ("hash_bits", ctypes.c_int32),
+        ("top_r", ctypes.c_int32), ("ema_decay", ctypes.c_float), ("dtype", ctypes.c_int32),
+    ]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_q", "w_k", "w_v", "w_r1", "w_r2", "proj")]
+
+
+class State(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("ema_state", "block_acc", "block_means", "block_hash", "k_cache", "v_cache")] + [
+        ("nb_cap", ctypes.c_int32), ("t_cap", ctypes.c_int64)]
+
+
+class Outputs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("q", "lambda_", "l2", "key", "idx", "o")]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32, _I64, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_PD = ctypes.POINTER(Dims)
+
+_SIGS = {
+    "mka_route": (ctypes.c_int, [_PD, _P, _P, _P, _P, _P, _P, _P]),
+    "mka_ema_scan": (ctypes.c_int, [_PD, _P, _I64, _P, _P, _P, _P, _I32, _P, _SZ, _P]),
+    "mka_l3_index": (ctypes.c_int, [_PD, _P, _I32, _I32, _I32, _P, _P, _P]),
+    "mka_l3_retrieve": (ctypes.c_int, [_PD, _P, _P, _P, _I32, _I64, _P, _P, _P, _SZ, _P]),
+    "mka_fuse_kv_proj": (ctypes.c_int,
+                         [_PD, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _I64, _I64, _P, _SZ, _P]),
+    "mka_attn_prefill": (ctypes.c_int, [_PD, _P, _P, _P, _I64, _I64, _P, _P]),
+    "mka_attn_decode": (ctypes.c_int, [_PD, _P, _P, _P, _I64, _I64, _P, _P, _SZ, _P]),
+    "mka_prefill": (ctypes.c_int, [_PD, _P, _I64, ctypes.POINTER(Weights), ctypes.POINTER(State),
+                                   ctypes.POINTER(Outputs), _P, _SZ, _P]),
+    "mka_decode_step": (ctypes.c_int, [_PD, _P, _I64, ctypes.POINTER(Weights),
+                                       ctypes.POINTER(State), ctypes.POINTER(Outputs), _P, _SZ, _P]),
+    "mka_workspace_bytes": (ctypes.c_size_t, [_PD, ctypes.c_int, _I64]),
+    "mka_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "mka_last_error": (ctypes.c_char_p, []),
+    "mka_version": (ctypes.c_char_p, []),
+}
+
+
+def lib():
+    """Load libmka.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m route_kv_memory_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def header_symbols() -> list[str]:
+    """Function names declared in include/mka.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(mka_\w+)\(", text, re.M)))
+
+
+def exported_symbols() -> list[str]:
+    """Names from the header that the loaded library exports."""
+    handle = lib()
+    return [n for n in header_symbols() if hasattr(handle, n)]
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("tensor arguments must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor arguments must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn, rc):
+    if rc != MKA_OK:
+        raise MkaError(fn, rc)
+
+
+def dims(shape, seq=None, batch=None) -> Dims:
+    """mka_dims of a ``route_kv_memory_amd.inputs.LayerShape``."""
+    return Dims(batch=shape.batch if batch is None else batch,
+                seq=shape.seq if seq is None else seq, d_model=shape.d_model,
+                n_heads=shape.n_heads, n_kv_heads=shape.n_kv_heads, head_dim=shape.head_dim,
+                router_hidden=shape.router_hidden, block=shape.block, hash_bits=shape.hash_bits,
+                top_r=shape.top_r, ema_decay=shape.ema_decay,
+                dtype=MKA_BF16 if shape.dtype == "bf16" else MKA_F32)
+
+
+# ----------------------------------------------------------------- C entries
+
+def mka_route(d, x, w_q, w_r1, w_r2, q_out, lambda_out, stream=None):
+    _check("mka_route", lib().mka_route(ctypes.byref(d), _ptr(x), _ptr(w_q), _ptr(w_r1),
+                                        _ptr(w_r2), _ptr(q_out), _ptr(lambda_out), _stream(stream)))
+
+
+def mka_ema_scan(d, x, pos0, state_io, block_acc_io, l2_out, block_means, nb_cap, ws=None,
+                 ws_bytes=0, stream=None):
+    _check("mka_ema_scan", lib().mka_ema_scan(
+        ctypes.byref(d), _ptr(x), pos0, _ptr(state_io), _ptr(block_acc_io), _ptr(l2_out),
+        _ptr(block_means), nb_cap, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def mka_l3_index(d, block_means, nb_cap, first_block, n_blocks, proj, block_hash, stream=None):
+    _check("mka_l3_index", lib().mka_l3_index(
+        ctypes.byref(d), _ptr(block_means), nb_cap, first_block, n_blocks, _ptr(proj),
+        _ptr(block_hash), _stream(stream)))
+
+
+def mka_l3_retrieve(d, l2, proj, block_hash, nb_cap, pos0, key_out, idx_out, ws=None, ws_bytes=0,
+                    stream=None):
+    _check("mka_l3_retrieve", lib().mka_l3_retrieve(
+        ctypes.byref(d), _ptr(l2), _ptr(proj), _ptr(block_hash), nb_cap, pos0, _ptr(key_out),
+        _ptr(idx_out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def mka_fuse_kv_proj(d, x, l2, block_means, nb_cap, idx, lam, w_k, w_v, k_cache, v_cache, pos0,
+                     t_cap, ws, ws_bytes, stream=None):
+    _check("mka_fuse_kv_proj", lib().mka_fuse_kv_proj(
+        ctypes.byref(d), _ptr(x), _ptr(l2), _ptr(block_means), nb_cap, _ptr(idx), _ptr(lam),
+        _ptr(w_k), _ptr(w_v), _ptr(k_cache), _ptr(v_cache), pos0, t_cap, _ptr(ws), ws_bytes,
+        _stream(stream)))
+
+
+def mka_attn_prefill(d, q, k_cache, v_cache, t_cap, pos0, o, stream=None):
+    _check("mka_attn_prefill", lib().mka_attn_prefill(
+        ctypes.byref(d), _ptr(q), _ptr(k_cache), _ptr(v_cache), t_cap, pos0, _ptr(o),
+        _stream(stream)))
+
+
+def mka_attn_decode(d, q, k_cache, v_cache, t_cap, cache_len, o, ws=None, ws_bytes=0,
+                    stream=None):
+    _check("mka_attn_decode", lib().mka_attn_decode(
+        ctypes.byref(d), _ptr(q), _ptr(k_cache), _ptr(v_cache), t_cap, cache_len, _ptr(o),
+        _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def mka_prefill(d, x, pos0, weights, state, outputs, ws, ws_bytes, stream=None):
+    _check("mka_prefill", lib().mka_prefill(
+        ctypes.byref(d), _ptr(x), pos0, ctypes.byref(weights), ctypes.byref(state),
+        ctypes.byref(outputs), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def mka_decode_step(d, x, pos, weights, state, outputs, ws, ws_bytes, stream=None):
+    _check("mka_decode_step", lib().mka_decode_step(
+        ctypes.byref(d), _ptr(x), pos, ctypes.byref(weights), ctypes.byref(state),
+        ctypes.byref(outputs), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def mka_workspace_bytes(d, op, cache_len=0) -> int:
+    return int(lib().mka_workspace_bytes(ctypes.byref(d), op, cache_len))
+
+
+def mka_status_string(status) -> str:
+    return lib().mka_status_string(status).decode()
+
+
+def mka_last_error() -> str:
+    return lib().mka_last_error().decode()
+
+
+def mka_version() -> str:
+    return lib().mka_version().decode()

@@ -1,0 +1,122 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function that include/mka.h declares, and rejects bad arguments with
+the documented status codes before launching anything."""
+
+import ctypes
+
+import pytest
+import torch
+
+from route_kv_memory_amd import inputs as I
+from route_kv_memory_amd import mka
+
+
+def test_library_exports_every_declared_symbol():
+    declared = mka.header_symbols()
+    assert len(declared) >= 13
+    assert mka.exported_symbols() == declared
+    assert "gfx950" in mka.mka_version()
+
+
+def test_status_strings():
+    assert mka.mka_status_string(mka.MKA_OK) == "ok"
+    for code in (mka.MKA_ERR_INVALID, mka.MKA_ERR_UNSUPPORTED, mka.MKA_ERR_WORKSPACE,
+                 mka.MKA_ERR_HIP):
+        assert mka.mka_status_string(code) not in ("ok", "unknown status")
+    assert mka.mka_status_string(12345) == "unknown status"
+
+
+FAKE = 1 << 40  # aligned, non-null, never dereferenced: every call below is rejected first
+
+
+def _d(**kw):
+    d = mka.dims(I.workload("qwen7b_prefill_4k"))
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("batch", 0, mka.MKA_ERR_INVALID),
+    ("seq", 0, mka.MKA_ERR_INVALID),
+    ("n_kv_heads", 3, mka.MKA_ERR_INVALID),       # 28 % 3 != 0
+    ("hash_bits", 65, mka.MKA_ERR_INVALID),
+    ("hash_bits", 0, mka.MKA_ERR_INVALID),
+    ("ema_decay", 1.0, mka.MKA_ERR_INVALID),
+    ("ema_decay", -0.1, mka.MKA_ERR_INVALID),
+    ("dtype", 7, mka.MKA_ERR_INVALID),
+    ("head_dim", 96, mka.MKA_ERR_UNSUPPORTED),
+    ("top_r", 33, mka.MKA_ERR_UNSUPPORTED),
+    ("d_model", 3584 + 32, mka.MKA_ERR_UNSUPPORTED),  # bf16 needs D % 64 == 0
+])
+def test_bad_dims_rejected(field, value, code):
+    d = _d(**{field: value})
+    with pytest.raises(mka.MkaError) as e:
+        mka.mka_route(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == code
+
+
+def test_null_and_misaligned_pointers_rejected():
+    d = _d()
+    with pytest.raises(mka.MkaError) as e:
+        mka.mka_route(d, FAKE, None, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == mka.MKA_ERR_INVALID
+    with pytest.raises(mka.MkaError) as e:
+        mka.mka_attn_prefill(d, FAKE + 2, FAKE, FAKE, 4096, 0, FAKE, stream=0)
+    assert e.value.status == mka.MKA_ERR_INVALID
+
+
+def test_range_checks_rejected():
+    d = _d()
+    # cache too short for pos0 + seq
+    with pytest.raises(mka.MkaError) as e:
+        mka.mka_attn_prefill(d, FAKE, FAKE, FAKE, 4095, 0, FAKE, stream=0)
+    assert e.value.status == mka.MKA_ERR_INVALID
+    # decode needs seq == 1 and 1 <= cache_len <= t_cap
+    with pytest.raises(mka.MkaError) as e:
+        mka.mka_attn_decode(d, FAKE, FAKE, FAKE, 10, 5, FAKE, FAKE, 1 << 20, stream=0)
+    assert e.value.status == mka.MKA_ERR_INVALID
+    d1 = _d(seq=1)
+    with pytest.raises(mka.MkaError) as e:
+        mka.mka_attn_decode(d1, FAKE, FAKE, FAKE, 10, 11, FAKE, FAKE, 1 << 20, stream=0)
+    assert e.value.status == mka.MKA_ERR_INVALID
+    # too few block means for the blocks completed in this call
+    with pytest.raises(mka.MkaError) as e:
+        mka.mka_ema_scan(d, FAKE, 0, FAKE, FAKE, FAKE, FAKE, 31, FAKE, 1 << 30, stream=0)
+    assert e.value.status == mka.MKA_ERR_INVALID
+    # the index range must fit in nb_cap
+    with pytest.raises(mka.MkaError) as e:
+        mka.mka_l3_index(d, FAKE, 32, 30, 3, FAKE, FAKE, stream=0)
+    assert e.value.status == mka.MKA_ERR_INVALID
+
+
+def test_workspace_sizes_and_rejection():
+    d = _d()
+    ema = mka.mka_workspace_bytes(d, mka.MKA_OP_EMA_SCAN)
+    fuse = mka.mka_workspace_bytes(d, mka.MKA_OP_FUSE_KV)
+    assert fuse == 2 * 4096 * 3584 * 2                 # X_fused in bf16
+    assert ema == 2 * 4 * 2 * (4096 // 64) * 3584       # chunk carries, 2 floats
+    assert mka.mka_workspace_bytes(d, mka.MKA_OP_PREFILL) == max(ema, fuse)
+    dd = mka.dims(I.workload("qwen7b_decode_128k"))
+    dec = mka.mka_workspace_bytes(dd, mka.MKA_OP_ATTN_DECODE, 131073)
+    chunks = (131073 + 1023) // 1024
+    assert dec >= 4 * 28 * chunks * (128 + 2)
+    assert mka.mka_workspace_bytes(dd, mka.MKA_OP_DECODE_STEP, 131073) >= dec
+    with pytest.raises(mka.MkaError) as e:
+        mka.mka_ema_scan(d, FAKE, 0, FAKE, FAKE, FAKE, FAKE, 32, FAKE, ema - 1, stream=0)
+    assert e.value.status == mka.MKA_ERR_WORKSPACE
+    with pytest.raises(mka.MkaError) as e:
+        mka.mka_fuse_kv_proj(d, FAKE, FAKE, FAKE, 32, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0,
+                             4096, FAKE, fuse - 1, stream=0)
+    assert e.value.status == mka.MKA_ERR_WORKSPACE
+    assert mka.mka_workspace_bytes(_d(batch=0), mka.MKA_OP_PREFILL) == 0
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="launch failure is only safe without a GPU")
+def test_launch_without_device_reports_hip_error():
+    # A fully valid call on a host with no GPU must fail with MKA_ERR_HIP, not crash.
+    d = mka.dims(I.workload("tiny_f32"))
+    with pytest.raises(mka.MkaError) as e:
+        mka.mka_attn_prefill(d, FAKE, FAKE, FAKE, 256, 0, FAKE, stream=0)
+    assert e.value.status == mka.MKA_ERR_HIP
+    assert mka.mka_last_error() != ""
