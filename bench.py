@@ -73,13 +73,14 @@ def bench_prefill(s, steps, warmup):
 
     def step(ev):
         ev[0].record(stream)
-        mka.mka_route(d, x, w["w_q"], w["w_r1"], w["w_r2"], out["q"], out["lambda"], stream)
+        mka.mka_route(d, x, w["w_q"], w["w_r1"], w["w_r2"], out["q"], out["lambda"], ws, nws,
+                      stream)
         ev[1].record(stream)
         mka.mka_ema_scan(d, x, 0, st["ema_state"], st["block_acc"], out["l2"], st["block_means"],
                          layer.nb_cap, ws, nws, stream)
         ev[2].record(stream)
         mka.mka_l3_index(d, st["block_means"], layer.nb_cap, 0, nb, w["proj"], st["block_hash"],
-                         stream)
+                         ws, nws, stream)
         ev[3].record(stream)
         mka.mka_l3_retrieve(d, out["l2"], w["proj"], st["block_hash"], layer.nb_cap, 0, out["key"],
                             out["idx"], ws, nws, stream)
@@ -134,13 +135,15 @@ def bench_decode(s, steps, warmup):
     tokens = to_device(dec["tokens"], s.dtype)
     del dec
     d1 = layer.dims(1)
+    iws = layer.workspace(max(mka.mka_workspace_bytes(d1, mka.MKA_OP_INDEX, nb0),
+                              mka.mka_workspace_bytes(d1, mka.MKA_OP_DECODE_STEP, t_cap)))
 
     def reset():
         st["ema_state"].copy_(init["ema_state"])
         st["block_acc"].copy_(init["block_acc"])
         st["block_means"][:, :nb0].copy_(means0)
         mka.mka_l3_index(d1, st["block_means"], layer.nb_cap, 0, nb0, layer.w["proj"],
-                         st["block_hash"])
+                         st["block_hash"], iws, iws.numel())
 
     out = layer.outputs(1)
     stream = torch.cuda.current_stream()

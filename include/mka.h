@@ -56,7 +56,7 @@ enum {
 
 /* Workspace-using operations, for mka_workspace_bytes(). */
 enum { MKA_OP_EMA_SCAN = 0, MKA_OP_FUSE_KV = 1, MKA_OP_ATTN_DECODE = 2, MKA_OP_PREFILL = 3,
-       MKA_OP_DECODE_STEP = 4, MKA_OP_RETRIEVE = 5 };
+       MKA_OP_DECODE_STEP = 4, MKA_OP_RETRIEVE = 5, MKA_OP_INDEX = 6, MKA_OP_ROUTE = 7 };
 
 /* Shape of one layer call.
  *   batch B >= 1; seq = tokens in this call (1 for a decode step) >= 1;
@@ -64,7 +64,9 @@ enum { MKA_OP_EMA_SCAN = 0, MKA_OP_FUSE_KV = 1, MKA_OP_ATTN_DECODE = 2, MKA_OP_P
  *   KV head h / (H/G)); head_dim dh in {64, 128}; the query width H*dh;
  *   router_hidden r; block = block size Bs of the L3 bank; hash_bits in
  *   [1, 64]; top_r = R >= 1; ema_decay beta in [0, 1); dtype MKA_F32 or
- *   MKA_BF16.  bf16 calls need D % 64 == 0 and H*dh % 128 == 0. */
+ *   MKA_BF16.  bf16 calls need D % 64 == 0 and H*dh % 64 == 0; fp32 calls need
+ *   D % 4 == 0 and H*dh % 4 == 0 (MKA_ERR_UNSUPPORTED otherwise).  top_r <= 32,
+ *   router_hidden <= 256, H/G <= 32. */
 typedef struct mka_dims {
   int32_t batch;
   int32_t seq;
@@ -88,9 +90,11 @@ typedef struct mka_dims {
  *   w_r1    [r, H*dh]              dtype
  *   w_r2    [3, r]                 dtype
  *   q_out   [B, seq, H, dh]        dtype (written)
- *   lambda_out [B, seq, 3]         float32 (written; tier 0 = L1, 1 = L2, 2 = L3) */
+ *   lambda_out [B, seq, 3]         float32 (written; tier 0 = L1, 1 = L2, 2 = L3)
+ *   ws      >= mka_workspace_bytes(d, MKA_OP_ROUTE, 0) bytes (may be NULL if 0) */
 int mka_route(const mka_dims* d, const void* x, const void* w_q, const void* w_r1,
-              const void* w_r2, void* q_out, float* lambda_out, void* stream);
+              const void* w_r2, void* q_out, float* lambda_out, void* ws, size_t ws_bytes,
+              void* stream);
 
 /* L2 session summary and block means for tokens at positions pos0 .. pos0+seq-1.
  * (Reading note, method section 1: the L2 tier is a causal summary of the
@@ -112,12 +116,14 @@ int mka_ema_scan(const mka_dims* d, const void* x, int64_t pos0, float* state_io
 /* SimHash codes of block means first_block .. first_block+n_blocks-1.
  * (Reading note, method section 1: vectorised hash index of past blocks.)
  * bit j of a code = [m . proj_j > 0]; the dot product is accumulated in float64
- * from the float32 inputs.
+ * from the float32 inputs (fp64 MFMA; split over D, partial sums added in a
+ * fixed order, so results are deterministic).
  *   block_means [B, nb_cap, D] float32; proj [hash_bits, D] float32 (row j = hyperplane j)
- *   block_hash  [B, nb_cap]    uint64 (rows written) */
+ *   block_hash  [B, nb_cap]    uint64 (rows written)
+ *   ws >= mka_workspace_bytes(d, MKA_OP_INDEX, n_blocks) bytes (may be NULL if 0) */
 int mka_l3_index(const mka_dims* d, const float* block_means, int32_t nb_cap,
                  int32_t first_block, int32_t n_blocks, const float* proj,
-                 uint64_t* block_hash, void* stream);
+                 uint64_t* block_hash, void* ws, size_t ws_bytes, void* stream);
 
 /* L3 retrieval for tokens at positions pos0 .. pos0+seq-1.
  * (Reading note, method section 1: recall of R << T past blocks; landing page,
@@ -225,7 +231,9 @@ int mka_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_wei
                     const mka_state* st, const mka_outputs* out, void* ws, size_t ws_bytes,
                     void* stream);
 
-/* Workspace in bytes that ``op`` needs for the shape ``d`` (cache_len: decode only). */
+/* Workspace in bytes that ``op`` needs for the shape ``d``.  ``cache_len`` is the
+ * cache length for MKA_OP_ATTN_DECODE / MKA_OP_DECODE_STEP and the number of
+ * blocks for MKA_OP_INDEX; it is ignored otherwise. */
 size_t mka_workspace_bytes(const mka_dims* d, int op, int64_t cache_len);
 
 /* Static description of a status code. */

@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16_kernel(
     }
   };
 
-  float m_i = -INFINITY, l_i = 0.f;
+  float ms = -INFINITY, l_i = 0.f;
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
@@ -140,26 +140,37 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16_kernel(
         s[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kr + 16 * ks), qf[ks], s[kb]);
     }
 
+    // Online max-shift in the exp2 domain: ms is the running reference
+    // (scaled by log2(e)/sqrt(dh)).  It is raised only when a tile's maximum
+    // exceeds it by more than 8, so most tiles need no rescale; probabilities
+    // stay below 2^8, which fp32 sums and bf16 operands carry exactly as well.
     const bool diag = (j0 + BN - 1) > wave_pos0;
+    if (diag) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t key = j0 + kb * 32 + 16 * (r >> 3) + 8 * hl + (r & 7);
+          if (key > q_pos) s[kb][r] = -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = s[kb][r] * sl2;
-        if (diag) {
-          const int64_t key = j0 + kb * 32 + 16 * (r >> 3) + 8 * hl + (r & 7);
-          if (key > q_pos) v = -INFINITY;
-        }
-        s[kb][r] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_i, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_i - m_new);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+    const bool raise = mx > ms + 8.0f;
+    if (__any(raise)) {
+      const float ms_new = raise ? mx : ms;
+      const float alpha = raise ? __builtin_amdgcn_exp2f(ms - ms_new) : 1.0f;
+      l_i *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+      ms = ms_new;
+    }
 
     bf16x8 pf[2][2];
-    float lsum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -167,15 +178,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16_kernel(
         float p[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          p[j] = __builtin_amdgcn_exp2f(s[kb][8 * st + j] - m_new);
-          lsum += p[j];
+          p[j] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * st + j], sl2, -ms));
+          l_i += p[j];
         }
         pf[kb][st] = to_bf16x8(p);
       }
-    l_i = l_i * alpha + lsum;
-    m_i = m_new;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
 
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
@@ -384,11 +391,10 @@ __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t key = j0 + kb * 32 + 16 * (r >> 3) + 8 * hl + (r & 7);
-        const float v = key < cache_len ? s[kb][r] * sl2 : -INFINITY;
-        s[kb][r] = v;
-        mx = fmaxf(mx, v);
+        if (key >= cache_len) s[kb][r] = -INFINITY;
+        mx = fmaxf(mx, s[kb][r]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
     const float m_new = fmaxf(m_i, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_i - m_use);
@@ -401,7 +407,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(
         float p[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          p[j] = __builtin_amdgcn_exp2f(s[kb][8 * st + j] - m_use);
+          p[j] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * st + j], sl2, -m_use));
           lsum += p[j];
         }
         pf[kb][st] = to_bf16x8(p);
@@ -462,42 +468,41 @@ __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(
 }
 
 template <int DH>
-__global__ __launch_bounds__(256) void attn_decode_merge_kernel(const float* __restrict__ part_m,
+__global__ __launch_bounds__(512) void attn_decode_merge_kernel(const float* __restrict__ part_m,
                                                                 const float* __restrict__ part_l,
                                                                 const float* __restrict__ part_o,
                                                                 int H, int n_chunks,
                                                                 bf16_t* __restrict__ O) {
-  constexpr int GR = 256 / DH;
+  constexpr int NT = 512, GR = NT / DH;
   __shared__ float wts[kMaxDecodeChunks];
-  __shared__ float red[256];
+  __shared__ float red[NT];
   __shared__ float osum[GR][DH];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int64_t p0 = (static_cast<int64_t>(b) * H + h) * n_chunks;
   float mx = -INFINITY;
-  for (int c = tid; c < n_chunks; c += 256) mx = fmaxf(mx, part_m[p0 + c]);
-  red[tid] = mx;
+  for (int c = tid; c < n_chunks; c += NT) mx = fmaxf(mx, part_m[p0 + c]);
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
   __syncthreads();
-  for (int off = 128; off >= 1; off >>= 1) {
-    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
-    __syncthreads();
-  }
-  const float M = red[0];
+  float M = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) M = fmaxf(M, red[w]);
   __syncthreads();
   float ls = 0.f;
-  for (int c = tid; c < n_chunks; c += 256) {
+  for (int c = tid; c < n_chunks; c += NT) {
     const float w = __builtin_amdgcn_exp2f(part_m[p0 + c] - M);
     wts[c] = w;
     ls += w * part_l[p0 + c];
   }
-  red[tid] = ls;
+  ls = wave_sum(ls);
+  if ((tid & 63) == 0) red[tid >> 6] = ls;
   __syncthreads();
-  for (int off = 128; off >= 1; off >>= 1) {
-    if (tid < off) red[tid] += red[tid + off];
-    __syncthreads();
-  }
-  const float L = red[0];
+  float L = 0.f;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) L += red[w];
   const int d = tid % DH, grp = tid / DH;
   float o = 0.f;
+#pragma unroll 8
   for (int c = grp; c < n_chunks; c += GR) o += wts[c] * part_o[(p0 + c) * DH + d];
   osum[grp][d] = o;
   __syncthreads();
@@ -522,12 +527,12 @@ hipError_t attn_decode_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* v, b
   if (dh == 128) {
     hipLaunchKernelGGL(attn_decode_split_kernel<128>, grid, dim3(256), 0, s, q, k, v, H, G, t_cap,
                        cache_len, sl2, n_chunks, part_m, part_l, part_o);
-    hipLaunchKernelGGL(attn_decode_merge_kernel<128>, dim3(H, B), dim3(256), 0, s, part_m, part_l,
+    hipLaunchKernelGGL(attn_decode_merge_kernel<128>, dim3(H, B), dim3(512), 0, s, part_m, part_l,
                        part_o, H, n_chunks, o);
   } else {
     hipLaunchKernelGGL(attn_decode_split_kernel<64>, grid, dim3(256), 0, s, q, k, v, H, G, t_cap,
                        cache_len, sl2, n_chunks, part_m, part_l, part_o);
-    hipLaunchKernelGGL(attn_decode_merge_kernel<64>, dim3(H, B), dim3(256), 0, s, part_m, part_l,
+    hipLaunchKernelGGL(attn_decode_merge_kernel<64>, dim3(H, B), dim3(512), 0, s, part_m, part_l,
                        part_o, H, n_chunks, o);
   }
   return hipGetLastError();

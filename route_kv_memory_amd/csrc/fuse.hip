@@ -17,27 +17,34 @@ __global__ __launch_bounds__(256) void fuse_mix_kernel(const T* __restrict__ x,
                                                        const int32_t* __restrict__ idx,
                                                        const float* __restrict__ lam, int seq, int D,
                                                        int R, T* __restrict__ xf) {
+  constexpr int RMAX = 32;
   const int64_t row = blockIdx.x;  // b * seq + t
   const int b = static_cast<int>(row / seq);
-  const int ch = blockIdx.y * 1024 + threadIdx.x * 4;
+  const int ch = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
   if (ch >= D) return;
   const float l1w = lam[row * 3 + 0], l2w = lam[row * 3 + 1], l3w = lam[row * 3 + 2];
   const int32_t* sel = idx + row * R;
   const float* mb = means + static_cast<int64_t>(b) * nb_cap * D + ch;
-  float l3[4] = {0.f, 0.f, 0.f, 0.f};
-  int cnt = 0;
-  for (int i = 0; i < R; ++i) {
-    const int blk = sel[i];
-    if (blk < 0) continue;
-    float m[4];
-    load4(mb + static_cast<int64_t>(blk) * D, m);
+  int blk[RMAX];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) l3[k] += m[k];
-    ++cnt;
-  }
-  float xv[4], sv[4], out[4];
+  for (int i = 0; i < RMAX; ++i) blk[i] = i < R ? sel[i] : -1;
+  float xv[4], sv[4];
   load4(x + row * D + ch, xv);
   load4(l2 + row * D + ch, sv);
+  float l3[4] = {0.f, 0.f, 0.f, 0.f};
+  int cnt = 0;
+  // Retrieved rows in rank order; the loads are independent of each other.
+#pragma unroll
+  for (int i = 0; i < RMAX; ++i) {
+    if (blk[i] >= 0) {
+      float m[4];
+      load4(mb + static_cast<int64_t>(blk[i]) * D, m);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) l3[k] += m[k];
+      ++cnt;
+    }
+  }
+  float out[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const float m = cnt ? l3[k] / static_cast<float>(cnt) : 0.f;
@@ -50,9 +57,12 @@ template <typename T>
 hipError_t fuse_mix(const T* x, const float* l2, const float* means, int nb_cap,
                     const int32_t* idx, const float* lam, int B, int seq, int D, int R, T* xf,
                     hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(B) * seq), (D + 1023) / 1024);
-  hipLaunchKernelGGL(fuse_mix_kernel<T>, grid, dim3(256), 0, s, x, l2, means, nb_cap, idx, lam, seq,
-                     D, R, xf);
+  // Few tokens: narrow workgroups so that many of them share the row.
+  const int threads = static_cast<int64_t>(B) * seq <= 8 ? 64 : 256;
+  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(B) * seq),
+                  (D + 4 * threads - 1) / (4 * threads));
+  hipLaunchKernelGGL(fuse_mix_kernel<T>, grid, dim3(threads), 0, s, x, l2, means, nb_cap, idx, lam,
+                     seq, D, R, xf);
   return hipGetLastError();
 }
 

@@ -40,6 +40,15 @@ struct EpiKV {
   }
 };
 
+// GELU of the product into a float32 row-major buffer (router hidden layer).
+struct EpiGelu {
+  float* h;
+  int ld;
+  __device__ __forceinline__ void operator()(int m, int n, float v) const {
+    h[static_cast<int64_t>(m) * ld + n] = gelu(v);
+  }
+};
+
 // Launchers (defined in gemm.hip).  B rows [0, n_split) come from b0, rows
 // [n_split, N) from b1 (row n - n_split); pass n_split = N for one matrix.
 template <class Epi>

@@ -176,7 +176,27 @@ __global__ __launch_bounds__(256) void gemv_kernel(const T* __restrict__ A, int 
                               : B1 + static_cast<int64_t>(n - n_split) * K;
   float acc[8] = {};
   const int kv = (K / V) * V;
-  for (int k = lane * V; k < kv; k += 64 * V) {
+  constexpr int STEP = 64 * V, U = 4;
+  int k = lane * V;
+  // Four 16-byte weight loads in flight per lane before any arithmetic.
+  for (; k + (U - 1) * STEP < kv; k += U * STEP) {
+    float w[U][V];
+#pragma unroll
+    for (int u = 0; u < U; ++u) Vec16<T>::load(brow + k + u * STEP, w[u]);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      if (m < M) {
+        float a[U][V];
+#pragma unroll
+        for (int u = 0; u < U; ++u) Vec16<T>::load(A + static_cast<int64_t>(m) * lda + k + u * STEP, a[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[m] = fmaf(a[u][i], w[u][i], acc[m]);
+      }
+    }
+  }
+  for (; k < kv; k += STEP) {
     float w[V];
     Vec16<T>::load(brow + k, w);
 #pragma unroll
@@ -233,5 +253,9 @@ template hipError_t gemv<float, EpiStore<float>>(const float*, int, int, const f
                                                   hipStream_t);
 template hipError_t gemv<float, EpiKV<float>>(const float*, int, int, const float*, const float*,
                                                int, int, int, const EpiKV<float>&, hipStream_t);
+template hipError_t gemv<bf16_t, EpiGelu>(const bf16_t*, int, int, const bf16_t*, const bf16_t*, int,
+                                          int, int, const EpiGelu&, hipStream_t);
+template hipError_t gemv<float, EpiGelu>(const float*, int, int, const float*, const float*, int,
+                                         int, int, const EpiGelu&, hipStream_t);
 
 }  // namespace mka

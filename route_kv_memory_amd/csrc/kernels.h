@@ -10,7 +10,11 @@ namespace mka {
 // MFMA path: bf16, router_hidden in {32, 64}, q_width % 64 == 0.
 hipError_t router_bf16_mfma(const bf16_t* q, int M, int qw, const bf16_t* w1, int r,
                             const bf16_t* w2, float* lam, hipStream_t s);
-// One workgroup per token: any type, r <= 256 (fp32 path and decode).
+// Few tokens: the hidden layer comes from a small-M product (gemv with a GELU
+// epilogue); this applies the second layer and the softmax.
+template <typename T>
+hipError_t router_head(const float* hidden, int M, int r, const T* w2, float* lam, hipStream_t s);
+// One workgroup per token: any type, r <= 256 (fp32 path).
 template <typename T>
 hipError_t router_rowwise(const T* q, int M, int qw, const T* w1, int r, const T* w2, float* lam,
                           hipStream_t s);
@@ -25,9 +29,11 @@ size_t ema_ws_bytes(int B, int seq, int D);
 
 // ---- SimHash codes and top-R retrieval ---------------------------------------
 // codes[b * codes_bstride + i] = SimHash(v[b * v_bstride + i * D .. +D]) for i < rows.
+// Uses simhash_ws_bytes(rows, B, D) bytes of ``ws`` (none when that is 0).
+size_t simhash_ws_bytes(int rows, int B, int D);
 hipError_t simhash_rows(const float* v, int64_t v_bstride, int rows, int B, int D,
                         const float* proj, int nbits, uint64_t* codes, int64_t codes_bstride,
-                        hipStream_t s);
+                        void* ws, hipStream_t s);
 // Few rows (decode): split over D, partial projections in ws, then select.
 constexpr int kFewRows = 8;
 size_t retrieve_few_ws_bytes(int rows, int D);
@@ -39,6 +45,8 @@ hipError_t topr_rows(const uint64_t* keys, int B, int seq, int64_t pos0, const u
                      int nb_cap, int block, int R, int32_t* idx, hipStream_t s);
 
 // ---- route fusion -----------------------------------------------------------------
+// xf[row] for rows of B*seq tokens; ``ch_per_wg`` channels per workgroup (a
+// multiple of 4, at most 1024).
 template <typename T>
 hipError_t fuse_mix(const T* x, const float* l2, const float* means, int nb_cap,
                     const int32_t* idx, const float* lam, int B, int seq, int D, int R, T* xf,

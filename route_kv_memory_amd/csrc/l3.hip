@@ -35,67 +35,142 @@ __device__ __forceinline__ void insert_sorted(uint32_t (&top)[N], uint32_t v) {
 }
 
 // ---------------------------------------------------------------------------
-// SimHash of many rows: a workgroup takes 32 rows x 64 hyperplanes; k-tiles of
-// 64 channels of both operands are staged in LDS; a thread accumulates 4 rows
-// x 2 hyperplanes in float64; codes are assembled with wave ballots.
+// SimHash projections on fp64 MFMA (v_mfma_f64_16x16x4f64).  Operand layout,
+// lane l: A[l % 16][l / 16], B[l / 16][l % 16]; accumulator register r holds
+// C[4r + l/16][l % 16].  A workgroup computes 64 rows x 64 hyperplanes over one
+// slice of D: each wave 16 rows x 4 blocks of 16 hyperplanes.  k-tiles of 64
+// channels of both operands are staged in LDS as fp32 and widened to fp64 in
+// registers; every product of two fp32 values is exact in fp64.
+// With one slice the codes are written directly (signs gathered by ballot);
+// with several, each slice writes its partial sums and simhash_finalize adds
+// them in slice order.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void simhash_rows_kernel(const float* __restrict__ v,
-                                                           int64_t v_bstride, int rows, int D,
-                                                           const float* __restrict__ P, int nbits,
-                                                           uint64_t* __restrict__ codes,
-                                                           int64_t c_bstride) {
-  __shared__ float Vs[32][65];
-  __shared__ float Ps[64][65];
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+constexpr int kHashKT = 64, kHashPitch = kHashKT + 4;
+
+__global__ __launch_bounds__(256) void simhash_mfma_kernel(
+    const float* __restrict__ v, int64_t v_bstride, int rows, int D, const float* __restrict__ P,
+    int nbits, int k_per_split, uint64_t* __restrict__ codes, int64_t c_bstride,
+    double* __restrict__ part) {
+  __shared__ float Vs[64 * kHashPitch];
+  __shared__ float Ps[64 * kHashPitch];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int row0 = blockIdx.x * 32, b = blockIdx.y;
+  const int row0 = blockIdx.x * 64, split = blockIdx.y, b = blockIdx.z;
+  const int k_begin = split * k_per_split, k_end = min(D, k_begin + k_per_split);
   const float* vb = v + b * v_bstride;
-  const int rg = tid >> 5, bp = tid & 31;
-  double acc[4][2] = {};
-  for (int k0 = 0; k0 < D; k0 += 64) {
+  f64x4 acc[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = tid + 256 * i, r = e >> 6, kk = e & 63;
-      Vs[r][kk] = (row0 + r < rows && k0 + kk < D) ? vb[static_cast<int64_t>(row0 + r) * D + k0 + kk] : 0.f;
-    }
+  for (int j = 0; j < 4; ++j) acc[j] = f64x4{0.0, 0.0, 0.0, 0.0};
+  const int li = lane & 15, lk = lane >> 4;
+  for (int k0 = k_begin; k0 < k_end; k0 += kHashKT) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int e = tid + 256 * i, j = e >> 6, kk = e & 63;
-      Ps[j][kk] = (j < nbits && k0 + kk < D) ? P[static_cast<int64_t>(j) * D + k0 + kk] : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 256 * i, r = e >> 4, c = (e & 15) * 4;  // 64 rows x 16 float4
+      f32x4 a = {0.f, 0.f, 0.f, 0.f}, p = {0.f, 0.f, 0.f, 0.f};
+      if (row0 + r < rows && k0 + c < k_end)
+        a = *reinterpret_cast<const f32x4*>(vb + static_cast<int64_t>(row0 + r) * D + k0 + c);
+      if (r < nbits && k0 + c < k_end)
+        p = *reinterpret_cast<const f32x4*>(P + static_cast<int64_t>(r) * D + k0 + c);
+      *reinterpret_cast<f32x4*>(&Vs[r * kHashPitch + c]) = a;
+      *reinterpret_cast<f32x4*>(&Ps[r * kHashPitch + c]) = p;
     }
     __syncthreads();
 #pragma unroll 4
-    for (int kk = 0; kk < 64; ++kk) {
-      const double p0 = Ps[bp][kk], p1 = Ps[bp + 32][kk];
+    for (int kk = 0; kk < kHashKT; kk += 4) {
+      const double a = Vs[(wave * 16 + li) * kHashPitch + kk + lk];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const double a = Vs[4 * rg + i][kk];
-        acc[i][0] = fma(a, p0, acc[i][0]);
-        acc[i][1] = fma(a, p1, acc[i][1]);
+      for (int j = 0; j < 4; ++j) {
+        const double p = Ps[(j * 16 + li) * kHashPitch + kk + lk];
+        acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, p, acc[j], 0, 0, 0);
       }
     }
     __syncthreads();
   }
-  // Lanes 0..31 of wave w hold row group 2w, lanes 32..63 row group 2w+1; lane
-  // bit bp of a ballot is hyperplane bp (first ballot) or bp + 32 (second).
+  if (part != nullptr) {
+    // part[((split * B + b) * rows + row) * 64 + bit]
+    double* pb = part + (static_cast<int64_t>(split) * gridDim.z + b) * rows * 64;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint64_t lo = __ballot(acc[i][0] > 0.0);
-    const uint64_t hi = __ballot(acc[i][1] > 0.0);
-    const int r_even = row0 + 4 * (2 * wave) + i, r_odd = row0 + 4 * (2 * wave + 1) + i;
-    if (lane == 0 && r_even < rows)
-      codes[b * c_bstride + r_even] = (lo & 0xFFFFFFFFull) | (hi << 32);
-    if (lane == 32 && r_odd < rows)
-      codes[b * c_bstride + r_odd] = (lo >> 32) | (hi & 0xFFFFFFFF00000000ull);
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + wave * 16 + 4 * r + lk;
+        if (row < rows) pb[static_cast<int64_t>(row) * 64 + 16 * j + li] = acc[j][r];
+      }
+    return;
   }
+  // Lanes 16q..16q+15 of register r hold row 4r + q, hyperplanes 16j + (lane % 16).
+  uint64_t bal[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bal[j][r] = __ballot(acc[j][r] > 0.0);
+  if (lane < 16) {
+    const int r = lane >> 2, q = lane & 3;
+    const int row = row0 + wave * 16 + 4 * r + q;
+    uint64_t code = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint64_t bj = 0;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        if (rr == r) bj = bal[j][rr];
+      code |= ((bj >> (16 * q)) & 0xFFFFull) << (16 * j);
+    }
+    if (row < rows) codes[b * c_bstride + row] = code;
+  }
+}
+
+// Sum the slice partials in slice order and take the signs: one wave per row.
+__global__ __launch_bounds__(256) void simhash_finalize_kernel(const double* __restrict__ part,
+                                                               int rows, int B, int nsplit,
+                                                               int nbits,
+                                                               uint64_t* __restrict__ codes,
+                                                               int64_t c_bstride) {
+  const int lane = threadIdx.x & 63;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (e >= static_cast<int64_t>(B) * rows) return;
+  const int b = static_cast<int>(e / rows), row = static_cast<int>(e - static_cast<int64_t>(b) * rows);
+  double p = 0.0;
+  for (int s = 0; s < nsplit; ++s)
+    p += part[((static_cast<int64_t>(s) * B + b) * rows + row) * 64 + lane];
+  const uint64_t code = __ballot(lane < nbits && p > 0.0);
+  if (lane == 0) codes[b * c_bstride + row] = code;
+}
+
+int simhash_splits(int rows, int B, int D) {
+  const int tiles = ((rows + 63) / 64) * B;
+  const int ktiles = (D + kHashKT - 1) / kHashKT;
+  int ns = (512 + tiles - 1) / tiles;
+  return ns < 1 ? 1 : (ns > ktiles ? ktiles : ns);
+}
+
+size_t simhash_ws_bytes(int rows, int B, int D) {
+  const int ns = simhash_splits(rows, B, D);
+  return ns > 1 ? sizeof(double) * static_cast<size_t>(ns) * B * rows * 64 : 0;
+}
+
+// Launch the projections; with more than one slice the partials go to ``part``.
+static hipError_t simhash_launch(const float* v, int64_t v_bstride, int rows, int B, int D,
+                                 const float* proj, int nbits, int nsplit, uint64_t* codes,
+                                 int64_t codes_bstride, double* part, hipStream_t s) {
+  const int ktiles = (D + kHashKT - 1) / kHashKT;
+  const int k_per_split = ((ktiles + nsplit - 1) / nsplit) * kHashKT;
+  const int ns = (D + k_per_split - 1) / k_per_split;
+  hipLaunchKernelGGL(simhash_mfma_kernel, dim3((rows + 63) / 64, ns, B), dim3(256), 0, s, v,
+                     v_bstride, rows, D, proj, nbits, k_per_split, codes, codes_bstride,
+                     ns > 1 ? part : nullptr);
+  if (ns > 1 && codes != nullptr)
+    hipLaunchKernelGGL(simhash_finalize_kernel, dim3((B * rows + 3) / 4), dim3(256), 0, s, part,
+                       rows, B, ns, nbits, codes, codes_bstride);
+  return hipGetLastError();
 }
 
 hipError_t simhash_rows(const float* v, int64_t v_bstride, int rows, int B, int D,
                         const float* proj, int nbits, uint64_t* codes, int64_t codes_bstride,
-                        hipStream_t s) {
+                        void* ws, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(simhash_rows_kernel, dim3((rows + 31) / 32, B), dim3(256), 0, s, v, v_bstride,
-                     rows, D, proj, nbits, codes, codes_bstride);
-  return hipGetLastError();
+  return simhash_launch(v, v_bstride, rows, B, D, proj, nbits, simhash_splits(rows, B, D), codes,
+                        codes_bstride, static_cast<double*>(ws), s);
 }
 
 // ---------------------------------------------------------------------------
@@ -141,48 +216,20 @@ hipError_t topr_rows(const uint64_t* keys, int B, int seq, int64_t pos0, const u
 
 // ---------------------------------------------------------------------------
 // Few tokens (decode): the key projections are split over D across many
-// workgroups (partial sums in float64 in the workspace), then one workgroup
-// per token sums them, forms the key, and selects the top R among all its
-// eligible blocks (each thread keeps a sorted list of its own candidates; R
-// rounds of a workgroup minimum pop the best head).
+// workgroups (fp64 partial sums in the workspace); one workgroup per token
+// then sums them in slice order, forms the key, and selects the top R among
+// all its eligible blocks (each thread keeps a sorted list of its own
+// candidates; R rounds of a workgroup minimum pop the best head).
 // ---------------------------------------------------------------------------
-constexpr int kSliceCh = 128;
-
 size_t retrieve_few_ws_bytes(int rows, int D) {
-  const int n_slices = (D + kSliceCh - 1) / kSliceCh;
-  return sizeof(double) * static_cast<size_t>(n_slices) * rows * 64;
+  const int ns = (D + kHashKT - 1) / kHashKT;
+  return sizeof(double) * static_cast<size_t>(ns) * rows * 64;
 }
 
-__global__ __launch_bounds__(256) void hash_partial_kernel(const float* __restrict__ l2, int rows,
-                                                           int D, const float* __restrict__ P,
-                                                           int nbits, double* __restrict__ part) {
-  __shared__ float Ps[64][kSliceCh + 1];
-  __shared__ float Vs[kFewRows][kSliceCh];
-  __shared__ double red[4][kFewRows][64];
-  const int tid = threadIdx.x, s = blockIdx.x, c0 = s * kSliceCh;
-  for (int e = tid; e < 64 * kSliceCh; e += 256) {
-    const int j = e / kSliceCh, c = e % kSliceCh;
-    Ps[j][c] = (j < nbits && c0 + c < D) ? P[static_cast<int64_t>(j) * D + c0 + c] : 0.f;
-  }
-  for (int e = tid; e < rows * kSliceCh; e += 256) {
-    const int r = e / kSliceCh, c = e % kSliceCh;
-    Vs[r][c] = c0 + c < D ? l2[static_cast<int64_t>(r) * D + c0 + c] : 0.f;
-  }
-  __syncthreads();
-  const int j = tid & 63, cg = tid >> 6;
-  for (int r = 0; r < rows; ++r) {
-    double acc = 0.0;
-#pragma unroll 8
-    for (int c = cg * 32; c < cg * 32 + 32; ++c)
-      acc = fma(static_cast<double>(Vs[r][c]), static_cast<double>(Ps[j][c]), acc);
-    red[cg][r][j] = acc;
-  }
-  __syncthreads();
-  for (int e = tid; e < rows * 64; e += 256) {
-    const int r = e / 64, jj = e % 64;
-    part[(static_cast<int64_t>(s) * rows + r) * 64 + jj] =
-        ((red[0][r][jj] + red[1][r][jj]) + red[2][r][jj]) + red[3][r][jj];
-  }
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  for (int off = 32; off >= 1; off >>= 1)
+    v = min(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off, 64)));
+  return v;
 }
 
 template <int RMAX>
@@ -193,13 +240,14 @@ __global__ __launch_bounds__(256) void select_few_kernel(const double* __restric
                                                          uint64_t* __restrict__ keys,
                                                          int32_t* __restrict__ idx) {
   __shared__ uint64_t key_s;
-  __shared__ uint32_t wmin[4];
+  __shared__ uint32_t cand[4][RMAX];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = blockIdx.x;  // row = b * seq + t
   const int b = r / seq;
   const int64_t t = r - static_cast<int64_t>(b) * seq;
   if (wave == 0) {
     double p = 0.0;
+#pragma unroll 8
     for (int s = 0; s < n_slices; ++s) p += part[(static_cast<int64_t>(s) * rows + r) * 64 + lane];
     const uint64_t code = __ballot(lane < nbits && p > 0.0);
     if (lane == 0) {
@@ -215,20 +263,35 @@ __global__ __launch_bounds__(256) void select_few_kernel(const double* __restric
 #pragma unroll
   for (int i = 0; i < RMAX; ++i) top[i] = kEmpty;
   for (int j = tid; j < ne; j += 256) insert_sorted(top, cand_key(key, codes[j], j));
-  int32_t* out = idx + static_cast<int64_t>(r) * R;
+  // Each wave pops its R best (keys are unique, so exactly one lane pops).
   for (int i = 0; i < R; ++i) {
-    uint32_t m = top[0];
-    for (int off = 32; off >= 1; off >>= 1) m = min(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off, 64)));
-    if (lane == 0) wmin[wave] = m;
-    __syncthreads();
-    const uint32_t best = min(min(wmin[0], wmin[1]), min(wmin[2], wmin[3]));
-    __syncthreads();
-    if (top[0] == best && best != kEmpty) {
+    const uint32_t m = wave_min_u32(top[0]);
+    if (top[0] == m && m != kEmpty) {
 #pragma unroll
       for (int k = 0; k < RMAX - 1; ++k) top[k] = top[k + 1];
       top[RMAX - 1] = kEmpty;
     }
-    if (tid == 0) out[i] = best == kEmpty ? -1 : cand_block(best);
+    if (lane == 0) cand[wave][i] = m;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  // Wave 0 merges the 4 sorted lists: lane l holds entries l and l + 64.
+  const uint32_t* flat = &cand[0][0];
+  uint32_t c0 = kEmpty, c1 = kEmpty;
+  {
+    const int e0 = lane, e1 = lane + 64;
+    if (e0 < 4 * R) c0 = flat[(e0 / R) * RMAX + e0 % R];
+    if (e1 < 4 * R) c1 = flat[(e1 / R) * RMAX + e1 % R];
+    if (c1 < c0) { const uint32_t tmp = c0; c0 = c1; c1 = tmp; }
+  }
+  int32_t* out = idx + static_cast<int64_t>(r) * R;
+  for (int i = 0; i < R; ++i) {
+    const uint32_t m = wave_min_u32(c0);
+    if (c0 == m && m != kEmpty) {
+      c0 = c1;
+      c1 = kEmpty;
+    }
+    if (lane == 0) out[i] = m == kEmpty ? -1 : cand_block(m);
   }
 }
 
@@ -236,10 +299,11 @@ hipError_t retrieve_few(const float* l2, int B, int seq, int D, const float* pro
                         const uint64_t* bh, int nb_cap, int block, int R, int64_t pos0,
                         uint64_t* keys, int32_t* idx, void* ws, hipStream_t s) {
   const int rows = B * seq;
-  const int n_slices = (D + kSliceCh - 1) / kSliceCh;
+  const int n_slices = (D + kHashKT - 1) / kHashKT;
   double* part = static_cast<double*>(ws);
-  hipLaunchKernelGGL(hash_partial_kernel, dim3(n_slices), dim3(256), 0, s, l2, rows, D, proj, nbits,
-                     part);
+  // rows are contiguous [B*seq, D]: one "batch" of B*seq rows, one slice per k-tile
+  const hipError_t e = simhash_launch(l2, 0, rows, 1, D, proj, nbits, n_slices, nullptr, 0, part, s);
+  if (e != hipSuccess) return e;
   if (R <= 16)
     hipLaunchKernelGGL(select_few_kernel<16>, dim3(rows), dim3(256), 0, s, part, rows, n_slices,
                        nbits, seq, pos0, bh, nb_cap, block, R, keys, idx);

@@ -71,7 +71,17 @@ size_t fuse_ws(const mka_dims* d) {
   return round256(static_cast<size_t>(rows_of(d)) * d->d_model * el_size(d));
 }
 size_t retrieve_ws(const mka_dims* d) {
-  return rows_of(d) <= kFewRows ? round256(retrieve_few_ws_bytes(rows_of(d), d->d_model)) : 0;
+  return rows_of(d) <= kFewRows ? round256(retrieve_few_ws_bytes(rows_of(d), d->d_model))
+                                : round256(simhash_ws_bytes(d->seq, d->batch, d->d_model));
+}
+size_t index_ws(const mka_dims* d, int64_t n_blocks) {
+  return n_blocks > 0 ? round256(simhash_ws_bytes(static_cast<int>(n_blocks), d->batch, d->d_model))
+                      : 0;
+}
+size_t route_ws(const mka_dims* d) {
+  return rows_of(d) <= kFewRows
+             ? round256(static_cast<size_t>(rows_of(d)) * d->router_hidden * sizeof(float))
+             : 0;
 }
 size_t decode_ws(const mka_dims* d, int64_t cache_len) {
   if (d->dtype != MKA_BF16) return 0;
@@ -82,7 +92,7 @@ size_t decode_ws(const mka_dims* d, int64_t cache_len) {
 // Each body assumes check_dims passed and its pointers were validated.
 
 int do_route(const mka_dims* d, const void* x, const void* w_q, const void* w_r1, const void* w_r2,
-             void* q_out, float* lam, hipStream_t s) {
+             void* q_out, float* lam, void* ws, hipStream_t s) {
   const int M = rows_of(d), D = d->d_model, qw = d->n_heads * d->head_dim, r = d->router_hidden;
   if (d->dtype == MKA_BF16) {
     const bf16_t* xb = static_cast<const bf16_t*>(x);
@@ -95,22 +105,31 @@ int do_route(const mka_dims* d, const void* x, const void* w_q, const void* w_r1
       MKA_LAUNCH("route/q_gemm", gemm_bf16(xb, D, wq, wq, qw, M, qw, D, epi, s));
     const bf16_t* w1 = static_cast<const bf16_t*>(w_r1);
     const bf16_t* w2 = static_cast<const bf16_t*>(w_r2);
-    if (M > kFewRows && (r == 32 || r == 64))
+    if (M <= kFewRows) {
+      float* hid = static_cast<float*>(ws);
+      MKA_LAUNCH("route/hidden", gemv<bf16_t>(q, qw, M, w1, w1, r, r, qw, EpiGelu{hid, r}, s));
+      MKA_LAUNCH("route/head", router_head<bf16_t>(hid, M, r, w2, lam, s));
+    } else if (r == 32 || r == 64) {
       MKA_LAUNCH("route/router", router_bf16_mfma(q, M, qw, w1, r, w2, lam, s));
-    else
+    } else {
       MKA_LAUNCH("route/router", router_rowwise<bf16_t>(q, M, qw, w1, r, w2, lam, s));
+    }
   } else {
     const float* xf = static_cast<const float*>(x);
     const float* wq = static_cast<const float*>(w_q);
     float* q = static_cast<float*>(q_out);
     const EpiStore<float> epi{q, qw};
-    if (M <= kFewRows)
+    const float* w1 = static_cast<const float*>(w_r1);
+    const float* w2 = static_cast<const float*>(w_r2);
+    if (M <= kFewRows) {
       MKA_LAUNCH("route/q_gemv", gemv<float>(xf, D, M, wq, wq, qw, qw, D, epi, s));
-    else
+      float* hid = static_cast<float*>(ws);
+      MKA_LAUNCH("route/hidden", gemv<float>(q, qw, M, w1, w1, r, r, qw, EpiGelu{hid, r}, s));
+      MKA_LAUNCH("route/head", router_head<float>(hid, M, r, w2, lam, s));
+    } else {
       MKA_LAUNCH("route/q_gemm", gemm_f32(xf, D, wq, wq, qw, M, qw, D, epi, s));
-    MKA_LAUNCH("route/router",
-               router_rowwise<float>(q, M, qw, static_cast<const float*>(w_r1), r,
-                                     static_cast<const float*>(w_r2), lam, s));
+      MKA_LAUNCH("route/router", router_rowwise<float>(q, M, qw, w1, r, w2, lam, s));
+    }
   }
   return MKA_OK;
 }
@@ -130,12 +149,12 @@ int do_ema(const mka_dims* d, const void* x, int64_t pos0, float* state_io, floa
 }
 
 int do_index(const mka_dims* d, const float* means, int nb_cap, int first, int n,
-             const float* proj, uint64_t* bh, hipStream_t s) {
+             const float* proj, uint64_t* bh, void* ws, hipStream_t s) {
   if (n <= 0) return MKA_OK;
   const int64_t D = d->d_model;
   MKA_LAUNCH("l3_index", simhash_rows(means + first * D, static_cast<int64_t>(nb_cap) * D, n,
                                       d->batch, d->d_model, proj, d->hash_bits, bh + first,
-                                      nb_cap, s));
+                                      nb_cap, ws, s));
   return MKA_OK;
 }
 
@@ -148,7 +167,7 @@ int do_retrieve(const mka_dims* d, const float* l2, const float* proj, const uin
   } else {
     MKA_LAUNCH("l3_retrieve/keys",
                simhash_rows(l2, static_cast<int64_t>(d->seq) * d->d_model, d->seq, d->batch,
-                            d->d_model, proj, d->hash_bits, keys, d->seq, s));
+                            d->d_model, proj, d->hash_bits, keys, d->seq, ws, s));
     MKA_LAUNCH("l3_retrieve/topr", topr_rows(keys, d->batch, d->seq, pos0, bh, nb_cap, d->block,
                                              d->top_r, idx, s));
   }
@@ -259,17 +278,24 @@ size_t mka_workspace_bytes(const mka_dims* d, int op, int64_t cache_len) {
     case MKA_OP_EMA_SCAN: return ema_ws(d);
     case MKA_OP_FUSE_KV: return fuse_ws(d);
     case MKA_OP_RETRIEVE: return retrieve_ws(d);
+    case MKA_OP_INDEX: return index_ws(d, cache_len);
+    case MKA_OP_ROUTE: return route_ws(d);
     case MKA_OP_ATTN_DECODE: return cache_len > 0 ? decode_ws(d, cache_len) : 0;
     case MKA_OP_PREFILL: {
+      // blocks completed by a call at any pos0: at most seq / block + 1
       size_t w = ema_ws(d);
       if (fuse_ws(d) > w) w = fuse_ws(d);
       if (retrieve_ws(d) > w) w = retrieve_ws(d);
+      if (route_ws(d) > w) w = route_ws(d);
+      if (index_ws(d, d->seq / d->block + 1) > w) w = index_ws(d, d->seq / d->block + 1);
       return w;
     }
     case MKA_OP_DECODE_STEP: {
       if (d->seq != 1) return 0;
       size_t w = fuse_ws(d);
       if (retrieve_ws(d) > w) w = retrieve_ws(d);
+      if (index_ws(d, 1) > w) w = index_ws(d, 1);
+      if (route_ws(d) > w) w = route_ws(d);
       if (cache_len > 0 && decode_ws(d, cache_len) > w) w = decode_ws(d, cache_len);
       return w;
     }
@@ -278,11 +304,16 @@ size_t mka_workspace_bytes(const mka_dims* d, int op, int64_t cache_len) {
 }
 
 int mka_route(const mka_dims* d, const void* x, const void* w_q, const void* w_r1,
-              const void* w_r2, void* q_out, float* lambda_out, void* stream) {
+              const void* w_r2, void* q_out, float* lambda_out, void* ws, size_t ws_bytes,
+              void* stream) {
   int rc = check_dims(d);
   if (rc) return rc;
   MKA_CHECK(ptrs_ok({x, w_q, w_r1, w_r2, q_out, lambda_out}), MKA_ERR_INVALID);
-  return do_route(d, x, w_q, w_r1, w_r2, q_out, lambda_out, static_cast<hipStream_t>(stream));
+  if (route_ws(d) > 0) {
+    MKA_CHECK(ptrs_ok({ws}), MKA_ERR_WORKSPACE);
+    MKA_CHECK(ws_bytes >= route_ws(d), MKA_ERR_WORKSPACE);
+  }
+  return do_route(d, x, w_q, w_r1, w_r2, q_out, lambda_out, ws, static_cast<hipStream_t>(stream));
 }
 
 int mka_ema_scan(const mka_dims* d, const void* x, int64_t pos0, float* state_io,
@@ -307,7 +338,8 @@ int mka_ema_scan(const mka_dims* d, const void* x, int64_t pos0, float* state_io
 }
 
 int mka_l3_index(const mka_dims* d, const float* block_means, int32_t nb_cap, int32_t first_block,
-                 int32_t n_blocks, const float* proj, uint64_t* block_hash, void* stream) {
+                 int32_t n_blocks, const float* proj, uint64_t* block_hash, void* ws,
+                 size_t ws_bytes, void* stream) {
   int rc = check_dims(d);
   if (rc) return rc;
   MKA_CHECK(first_block >= 0 && n_blocks >= 0 &&
@@ -317,7 +349,11 @@ int mka_l3_index(const mka_dims* d, const float* block_means, int32_t nb_cap, in
   MKA_CHECK(ptrs_ok({block_means, proj}) && block_hash != nullptr &&
                 (reinterpret_cast<uintptr_t>(block_hash) & 7u) == 0,
             MKA_ERR_INVALID);
-  return do_index(d, block_means, nb_cap, first_block, n_blocks, proj, block_hash,
+  if (index_ws(d, n_blocks) > 0) {
+    MKA_CHECK(ptrs_ok({ws}), MKA_ERR_WORKSPACE);
+    MKA_CHECK(ws_bytes >= index_ws(d, n_blocks), MKA_ERR_WORKSPACE);
+  }
+  return do_index(d, block_means, nb_cap, first_block, n_blocks, proj, block_hash, ws,
                   static_cast<hipStream_t>(stream));
 }
 
@@ -410,12 +446,12 @@ int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weight
   hipStream_t s = static_cast<hipStream_t>(stream);
   int64_t first, n;
   completed_blocks(d, pos0, &first, &n);
-  if ((rc = do_route(d, x, w->w_q, w->w_r1, w->w_r2, out->q, out->lambda, s))) return rc;
+  if ((rc = do_route(d, x, w->w_q, w->w_r1, w->w_r2, out->q, out->lambda, ws, s))) return rc;
   if ((rc = do_ema(d, x, pos0, st->ema_state, st->block_acc, out->l2, st->block_means, st->nb_cap,
                    ws, s)))
     return rc;
   if ((rc = do_index(d, st->block_means, st->nb_cap, static_cast<int>(first), static_cast<int>(n),
-                     w->proj, st->block_hash, s)))
+                     w->proj, st->block_hash, ws, s)))
     return rc;
   if ((rc = do_retrieve(d, out->l2, w->proj, st->block_hash, st->nb_cap, pos0, out->key, out->idx,
                         ws, s)))
@@ -439,7 +475,7 @@ int mka_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_wei
   MKA_CHECK(ws_bytes >= need, MKA_ERR_WORKSPACE);
   MKA_CHECK(need == 0 || ptrs_ok({ws}), MKA_ERR_WORKSPACE);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((rc = do_route(d, x, w->w_q, w->w_r1, w->w_r2, out->q, out->lambda, s))) return rc;
+  if ((rc = do_route(d, x, w->w_q, w->w_r1, w->w_r2, out->q, out->lambda, ws, s))) return rc;
   if ((rc = do_ema(d, x, pos, st->ema_state, st->block_acc, out->l2, st->block_means, st->nb_cap,
                    nullptr, s)))
     return rc;
@@ -453,7 +489,7 @@ int mka_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_wei
     return rc;
   if ((pos + 1) % d->block == 0)
     return do_index(d, st->block_means, st->nb_cap, static_cast<int>((pos + 1) / d->block - 1), 1,
-                    w->proj, st->block_hash, s);
+                    w->proj, st->block_hash, ws, s);
   return MKA_OK;
 }
 

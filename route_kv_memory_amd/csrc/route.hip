@@ -141,6 +141,37 @@ hipError_t router_rowwise(const T* q, int M, int qw, const T* w1, int r, const T
   return hipGetLastError();
 }
 
+// Second router layer and softmax for few tokens, from the hidden layer that
+// a small-M product (one wave per hidden unit) left in ``hidden`` [M, r].
+template <typename T>
+__global__ __launch_bounds__(64) void router_head_kernel(const float* __restrict__ hidden, int r,
+                                                         const T* __restrict__ W2,
+                                                         float* __restrict__ lam) {
+  const int lane = threadIdx.x, row = blockIdx.x;
+  float z[3];
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    float sum = 0.f;
+    for (int n = lane; n < r; n += 64) sum = fmaf(hidden[static_cast<int64_t>(row) * r + n], Elem<T>::to_f32(W2[c * r + n]), sum);
+    z[c] = wave_sum(sum);
+  }
+  if (lane == 0) {
+    float out[3];
+    softmax3(z, out);
+    lam[static_cast<int64_t>(row) * 3 + 0] = out[0];
+    lam[static_cast<int64_t>(row) * 3 + 1] = out[1];
+    lam[static_cast<int64_t>(row) * 3 + 2] = out[2];
+  }
+}
+
+template <typename T>
+hipError_t router_head(const float* hidden, int M, int r, const T* w2, float* lam, hipStream_t s) {
+  hipLaunchKernelGGL(router_head_kernel<T>, dim3(M), dim3(64), 0, s, hidden, r, w2, lam);
+  return hipGetLastError();
+}
+template hipError_t router_head<float>(const float*, int, int, const float*, float*, hipStream_t);
+template hipError_t router_head<bf16_t>(const float*, int, int, const bf16_t*, float*, hipStream_t);
+
 template hipError_t router_rowwise<float>(const float*, int, int, const float*, int, const float*,
                                           float*, hipStream_t);
 template hipError_t router_rowwise<bf16_t>(const bf16_t*, int, int, const bf16_t*, int,

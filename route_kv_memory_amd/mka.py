@@ -18,7 +18,7 @@ __all__ = [
     "MkaError", "Dims", "Weights", "State", "Outputs", "lib", "dims", "exported_symbols",
     "header_symbols", "MKA_F32", "MKA_BF16", "MKA_OK", "MKA_ERR_INVALID", "MKA_ERR_UNSUPPORTED",
     "MKA_ERR_WORKSPACE", "MKA_ERR_HIP", "MKA_OP_EMA_SCAN", "MKA_OP_FUSE_KV", "MKA_OP_ATTN_DECODE",
-    "MKA_OP_PREFILL", "MKA_OP_DECODE_STEP", "MKA_OP_RETRIEVE",
+    "MKA_OP_PREFILL", "MKA_OP_DECODE_STEP", "MKA_OP_RETRIEVE", "MKA_OP_INDEX", "MKA_OP_ROUTE",
     "mka_route", "mka_ema_scan", "mka_l3_index", "mka_l3_retrieve", "mka_fuse_kv_proj",
     "mka_attn_prefill", "mka_attn_decode", "mka_prefill", "mka_decode_step",
     "mka_workspace_bytes", "mka_status_string", "mka_last_error", "mka_version",
@@ -31,7 +31,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "mka.h")
 MKA_F32, MKA_BF16 = 0, 1
 MKA_OK, MKA_ERR_INVALID, MKA_ERR_UNSUPPORTED, MKA_ERR_WORKSPACE, MKA_ERR_HIP = 0, -1, -2, -3, -4
 (MKA_OP_EMA_SCAN, MKA_OP_FUSE_KV, MKA_OP_ATTN_DECODE, MKA_OP_PREFILL, MKA_OP_DECODE_STEP,
- MKA_OP_RETRIEVE) = range(6)
+ MKA_OP_RETRIEVE, MKA_OP_INDEX, MKA_OP_ROUTE) = range(8)
 
 
 class MkaError(RuntimeError):
@@ -72,9 +72,9 @@ _I32, _I64, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _PD = ctypes.POINTER(Dims)
 
 _SIGS = {
-    "mka_route": (ctypes.c_int, [_PD, _P, _P, _P, _P, _P, _P, _P]),
+    "mka_route": (ctypes.c_int, [_PD, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mka_ema_scan": (ctypes.c_int, [_PD, _P, _I64, _P, _P, _P, _P, _I32, _P, _SZ, _P]),
-    "mka_l3_index": (ctypes.c_int, [_PD, _P, _I32, _I32, _I32, _P, _P, _P]),
+    "mka_l3_index": (ctypes.c_int, [_PD, _P, _I32, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "mka_l3_retrieve": (ctypes.c_int, [_PD, _P, _P, _P, _I32, _I64, _P, _P, _P, _SZ, _P]),
     "mka_fuse_kv_proj": (ctypes.c_int,
                          [_PD, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _I64, _I64, _P, _SZ, _P]),
@@ -158,9 +158,10 @@ def dims(shape, seq=None, batch=None) -> Dims:
 
 # ----------------------------------------------------------------- C entries
 
-def mka_route(d, x, w_q, w_r1, w_r2, q_out, lambda_out, stream=None):
+def mka_route(d, x, w_q, w_r1, w_r2, q_out, lambda_out, ws=None, ws_bytes=0, stream=None):
     _check("mka_route", lib().mka_route(ctypes.byref(d), _ptr(x), _ptr(w_q), _ptr(w_r1),
-                                        _ptr(w_r2), _ptr(q_out), _ptr(lambda_out), _stream(stream)))
+                                        _ptr(w_r2), _ptr(q_out), _ptr(lambda_out), _ptr(ws),
+                                        ws_bytes, _stream(stream)))
 
 
 def mka_ema_scan(d, x, pos0, state_io, block_acc_io, l2_out, block_means, nb_cap, ws=None,
@@ -170,10 +171,11 @@ def mka_ema_scan(d, x, pos0, state_io, block_acc_io, l2_out, block_means, nb_cap
         _ptr(block_means), nb_cap, _ptr(ws), ws_bytes, _stream(stream)))
 
 
-def mka_l3_index(d, block_means, nb_cap, first_block, n_blocks, proj, block_hash, stream=None):
+def mka_l3_index(d, block_means, nb_cap, first_block, n_blocks, proj, block_hash, ws=None,
+                 ws_bytes=0, stream=None):
     _check("mka_l3_index", lib().mka_l3_index(
         ctypes.byref(d), _ptr(block_means), nb_cap, first_block, n_blocks, _ptr(proj),
-        _ptr(block_hash), _stream(stream)))
+        _ptr(block_hash), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def mka_l3_retrieve(d, l2, proj, block_hash, nb_cap, pos0, key_out, idx_out, ws=None, ws_bytes=0,

@@ -52,14 +52,14 @@ def _d(**kw):
 def test_bad_dims_rejected(field, value, code):
     d = _d(**{field: value})
     with pytest.raises(mka.MkaError) as e:
-        mka.mka_route(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+        mka.mka_route(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, stream=0)
     assert e.value.status == code
 
 
 def test_null_and_misaligned_pointers_rejected():
     d = _d()
     with pytest.raises(mka.MkaError) as e:
-        mka.mka_route(d, FAKE, None, FAKE, FAKE, FAKE, FAKE, stream=0)
+        mka.mka_route(d, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, stream=0)
     assert e.value.status == mka.MKA_ERR_INVALID
     with pytest.raises(mka.MkaError) as e:
         mka.mka_attn_prefill(d, FAKE + 2, FAKE, FAKE, 4096, 0, FAKE, stream=0)
@@ -86,7 +86,7 @@ def test_range_checks_rejected():
     assert e.value.status == mka.MKA_ERR_INVALID
     # the index range must fit in nb_cap
     with pytest.raises(mka.MkaError) as e:
-        mka.mka_l3_index(d, FAKE, 32, 30, 3, FAKE, FAKE, stream=0)
+        mka.mka_l3_index(d, FAKE, 32, 30, 3, FAKE, FAKE, FAKE, 1 << 30, stream=0)
     assert e.value.status == mka.MKA_ERR_INVALID
 
 
@@ -96,7 +96,10 @@ def test_workspace_sizes_and_rejection():
     fuse = mka.mka_workspace_bytes(d, mka.MKA_OP_FUSE_KV)
     assert fuse == 2 * 4096 * 3584 * 2                 # X_fused in bf16
     assert ema == 2 * 4 * 2 * (4096 // 64) * 3584       # chunk carries, 2 floats
-    assert mka.mka_workspace_bytes(d, mka.MKA_OP_PREFILL) == max(ema, fuse)
+    retr = mka.mka_workspace_bytes(d, mka.MKA_OP_RETRIEVE)
+    idx = mka.mka_workspace_bytes(d, mka.MKA_OP_INDEX, 33)
+    assert mka.mka_workspace_bytes(d, mka.MKA_OP_PREFILL) == max(ema, fuse, retr, idx)
+    assert idx > 0  # few blocks: the projections are split over d_model
     dd = mka.dims(I.workload("qwen7b_decode_128k"))
     dec = mka.mka_workspace_bytes(dd, mka.MKA_OP_ATTN_DECODE, 131073)
     chunks = (131073 + 1023) // 1024

@@ -1,0 +1,141 @@
+"""GPU parity at the workloads' full sizes, against the oracle.
+
+Prefill: the Qwen2.5-7B-shaped layer at 4096 tokens x 2 sequences and at
+32768 tokens (with drift), and the Llama-3.1-8B-shaped layer at 65536
+tokens.  The oracle computes every step for every row (later rows need the
+earlier ones) and attention on sampled rows; router weights, L2, block
+means, codes and retrieved blocks are compared on every row, Q/K/V/O on the
+sampled rows.  Decode: the 131072-token fused-cache workload, 256 steps,
+compared at sampled steps and on the final state.  The launch configuration
+is the one bench.py times.
+"""
+
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mka_oracle as O
+from route_kv_memory_amd import inputs as I
+from route_kv_memory_amd import mka
+from route_kv_memory_amd.layer import Layer, to_device
+
+from .gpu_common import to_np
+from .parity import (check_close, check_codes, check_idx, check_idx_conditional, log,
+                     oracle_kwargs)
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+WEIGHTS = ("w_q", "w_k", "w_v", "w_r1", "w_r2", "proj")
+
+
+def _rows(s):
+    if s.n_sampled:
+        return I.sampled_rows(s)
+    return I.sampled_rows(s.replace(n_sampled=512))
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("name", ["qwen7b_prefill_4k", "qwen7b_prefill_32k", "llama8b_prefill_64k"])
+def test_full_prefill(name):
+    s = I.workload(name)
+    log(f"[{name}] generating inputs")
+    inp = I.prefill_inputs(s)
+    rows = _rows(s)
+    N, B = s.seq, s.batch
+    layer = Layer(s, inp, t_cap=N, nb_cap=N // s.block)
+    log(f"[{name}] gpu: mka_prefill B={B} N={N}")
+    out = layer.prefill(to_device(inp["x"], s.dtype))
+    torch.cuda.synchronize()
+    g = {
+        "lam": to_np(out["lambda"]),
+        "key": to_np(out["key"]).view(np.uint64),
+        "idx": to_np(out["idx"]),
+        "l2": to_np(out["l2"]),
+        "q": to_np(out["q"][:, rows]).reshape(B, len(rows), -1),
+        "o": to_np(out["o"][:, rows]),
+        "k": to_np(layer.st["k_cache"][:, :, rows]),
+        "v": to_np(layer.st["v_cache"][:, :, rows]),
+        "means": to_np(layer.st["block_means"]),
+        "bhash": to_np(layer.st["block_hash"]).view(np.uint64),
+    }
+    del out, layer
+    torch.cuda.empty_cache()
+    log(f"[{name}] oracle (every step on every row, attention on {len(rows)} rows)")
+    ref = O.prefill(inp["x"], *[inp[k] for k in WEIGHTS], rows=rows, **oracle_kwargs(s))
+    check_close("lambda", g["lam"], ref["lam"], s.dtype)
+    check_close("l2 (sampled rows)", g["l2"][:, rows], ref["l2"][:, rows], "f32")
+    check_close("block_means", g["means"], ref["block_means"], "f32")
+    check_codes("block_hash", g["bhash"], ref["block_hash"], ref["block_abs"], s.hash_bits)
+    check_codes("keys", g["key"], ref["keys"], ref["key_abs"], s.hash_bits)
+    check_idx("idx", g["idx"], ref["keys"], ref["key_abs"], ref["block_hash"], ref["block_abs"],
+              np.arange(N), s.block, s.top_r, s.hash_bits)
+    check_idx_conditional("idx|gpu", g["idx"], g["key"], g["l2"], g["means"], g["bhash"],
+                          inp["proj"], np.arange(N), s.block, s.top_r, s.hash_bits)
+    check_close("q (sampled rows)", g["q"], ref["q"][:, rows], s.dtype)
+    check_close("k (sampled rows)", g["k"], ref["k"][:, :, rows], s.dtype)
+    check_close("v (sampled rows)", g["v"], ref["v"][:, :, rows], s.dtype)
+    check_close("o (sampled rows)", g["o"], ref["o"], s.dtype)
+    del ref, g, inp
+    gc.collect()
+
+
+@pytest.mark.timeout(1200)
+def test_full_decode_128k():
+    s = I.workload("qwen7b_decode_128k")
+    log("[decode] generating state")
+    dec = I.decode_inputs(s)
+    T0, n = s.decode_cached, s.decode_steps
+    t_cap = T0 + n
+    nb0 = T0 // s.block
+    sample = {0, 1, 126, 127, 128, 129, 254, 255}
+    layer = Layer(s, dec, t_cap=t_cap, nb_cap=t_cap // s.block + 1)
+    st = layer.st
+    st["k_cache"][:, :, :T0] = to_device(dec["k_cache"], s.dtype)
+    st["v_cache"][:, :, :T0] = to_device(dec["v_cache"], s.dtype)
+    st["ema_state"].copy_(to_device(dec["ema_state"]))
+    st["block_acc"].copy_(to_device(dec["block_acc"]))
+    st["block_means"][:, :nb0].copy_(to_device(dec["block_means"]))
+    d1 = layer.dims(1)
+    ws = layer.workspace(max(mka.mka_workspace_bytes(d1, mka.MKA_OP_INDEX, nb0),
+                             mka.mka_workspace_bytes(d1, mka.MKA_OP_DECODE_STEP, t_cap)))
+    mka.mka_l3_index(d1, st["block_means"], layer.nb_cap, 0, nb0, layer.w["proj"],
+                     st["block_hash"], ws, ws.numel())
+    tokens = to_device(dec["tokens"], s.dtype)
+    log(f"[decode] gpu: {n} mka_decode_step calls from position {T0}")
+    got = {}
+    for k in range(n):
+        out = layer.decode_step(tokens[k], T0 + k)
+        if k in sample:
+            torch.cuda.synchronize()
+            got[k] = {kk: to_np(v) for kk, v in out.items()}
+            got[k]["key"] = got[k]["key"].view(np.uint64)
+    torch.cuda.synchronize()
+    fin = {"k": to_np(st["k_cache"][:, :, T0:]), "v": to_np(st["v_cache"][:, :, T0:]),
+           "means": to_np(st["block_means"][:, :nb0 + 2]),
+           "bhash": to_np(st["block_hash"][:, :nb0 + 2]).view(np.uint64)}
+    del layer, st, tokens
+    torch.cuda.empty_cache()
+
+    log("[decode] oracle: 256 steps of state, attention at the sampled steps")
+    w = [dec[k] for k in WEIGHTS]
+    kw = oracle_kwargs(s)
+    ost = O.decode_init(dec["k_cache"], dec["v_cache"], dec["ema_state"], dec["block_acc"],
+                        dec["block_means"], dec["proj"], t_cap=t_cap)
+    for k in range(n):
+        r = O.decode_step(ost, dec["tokens"][k], *w, attend=k in sample, **kw)
+        if k in sample:
+            gk = got[k]
+            log(f"  step {k} (position {T0 + k})")
+            check_close("o", gk["o"][:, 0], r["o"], s.dtype)
+            check_close("lambda", gk["lambda"][:, 0], r["lam"], s.dtype)
+            check_close("l2", gk["l2"][:, 0], r["l2"], "f32")
+            check_codes("key", gk["key"][:, 0], r["key"], r["key_abs"], s.hash_bits)
+            check_idx("idx", gk["idx"], r["key"][:, None], r["key_abs"][:, None], ost.hash,
+                      ost.hash_abs, np.array([T0 + k]), s.block, s.top_r, s.hash_bits)
+    check_close("k rows appended", fin["k"], ost.k[:, :, T0:], s.dtype)
+    check_close("v rows appended", fin["v"], ost.v[:, :, T0:], s.dtype)
+    check_close("block means (incl. the two completed)", fin["means"], ost.means, "f32")
+    check_codes("block codes (incl. the two completed)", fin["bhash"], ost.hash, ost.hash_abs,
+                s.hash_bits)
