@@ -57,7 +57,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16_kernel(
     int n_qblk, int n_units) {
   constexpr int BM = 128, BN = 64, KP = DH + 8, VP = BN + 8, NKS = DH / 16, NDB = DH / 32;
   constexpr int KCH = BN * DH / 8 / 256;
-  constexpr int VITEMS = (BN / 4) * (DH / 8);
+  constexpr int VITEMS = (BN / 4) * (DH / 8);  // 16 key quads x DH/8 dim chunks
+  static_assert(BN == 64, "V store mapping assumes 16 key quads");
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][BN * KP];
   __shared__ __attribute__((aligned(16))) bf16_t Vt[2][DH * VP];
 
@@ -86,33 +87,35 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16_kernel(
   }
   const bf16_t* kbase = Kc + (static_cast<int64_t>(b) * G + g) * t_cap * DH;
   const bf16_t* vbase = Vc + (static_cast<int64_t>(b) * G + g) * t_cap * DH;
+  // Keys at or beyond kv_end read as zeros through the buffer range.
+  const uint32_t kv_bytes = static_cast<uint32_t>(kv_end * DH * 2);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, kv_bytes), vrs = make_rsrc(vbase, kv_bytes);
 
   u32x4 rk[KCH], rv[4];
-  auto gload = [&](int64_t j0) {
+  auto gload = [&](int j0) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int c = tid + 256 * i, row = c / (DH / 8), col = (c % (DH / 8)) * 8;
-      rk[i] = (j0 + row < kv_end) ? *reinterpret_cast<const u32x4*>(kbase + (j0 + row) * DH + col)
-                                  : u32x4{0, 0, 0, 0};
+      rk[i] = buffer_load16(krs, static_cast<uint32_t>((j0 + row) * DH + col) * 2);
     }
     if (tid < VITEMS) {
-      const int kq = tid / (DH / 8), dc = tid % (DH / 8);
+      const int kq = tid & 15, dc = tid >> 4;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t key = j0 + 4 * kq + r;
-        rv[r] = key < kv_end ? *reinterpret_cast<const u32x4*>(vbase + key * DH + 8 * dc)
-                             : u32x4{0, 0, 0, 0};
-      }
+      for (int r = 0; r < 4; ++r)
+        rv[r] = buffer_load16(vrs, static_cast<uint32_t>((j0 + 4 * kq + r) * DH + 8 * dc) * 2);
     }
   };
+  // K row j of the tile goes to LDS row kperm(j), so the MFMA reads of
+  // consecutive lanes hit consecutive rows.  V threads are laid out so that the
+  // 64 lanes of one transposing store cover 16 key quads of 4 d-rows.
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int c = tid + 256 * i, row = c / (DH / 8), col = (c % (DH / 8)) * 8;
-      *reinterpret_cast<u32x4*>(&Ks[buf][row * KP + col]) = rk[i];
+      *reinterpret_cast<u32x4*>(&Ks[buf][kperm(row) * KP + col]) = rk[i];
     }
     if (tid < VITEMS) {
-      const int kq = tid / (DH / 8), dc = tid % (DH / 8);
+      const int kq = tid & 15, dc = tid >> 4;
       store_vt(Vt[buf], VP, 8 * dc, 4 * kq, rv);
     }
   };
@@ -127,14 +130,14 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16_kernel(
   __syncthreads();
   for (int jt = 0; jt < n_tiles; ++jt) {
     const int buf = jt & 1;
-    const int64_t j0 = static_cast<int64_t>(jt) * BN;
+    const int j0 = jt * BN;
     if (jt + 1 < n_tiles) gload(j0 + BN);
 
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
-      const bf16_t* kr = &Ks[buf][(kb * 32 + kperm(l32)) * KP + 8 * hl];
+      const bf16_t* kr = &Ks[buf][(kb * 32 + l32) * KP + 8 * hl];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
         s[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kr + 16 * ks), qf[ks], s[kb]);
@@ -146,13 +149,12 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16_kernel(
     // stay below 2^8, which fp32 sums and bf16 operands carry exactly as well.
     const bool diag = (j0 + BN - 1) > wave_pos0;
     if (diag) {
+      const int q_rel = static_cast<int>(q_pos - j0);  // keys of the tile after the query
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t key = j0 + kb * 32 + 16 * (r >> 3) + 8 * hl + (r & 7);
-          if (key > q_pos) s[kb][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 16 * (r >> 3) + 8 * hl + (r & 7) > q_rel) s[kb][r] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -347,6 +349,11 @@ __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(
   }
   const bf16_t* kbase = Kc + (static_cast<int64_t>(b) * G + g) * t_cap * DH;
   const bf16_t* vbase = Vc + (static_cast<int64_t>(b) * G + g) * t_cap * DH;
+  // Rows of this workgroup's chunk, as a byte range: rows past cache_len read as zeros.
+  const int64_t c0 = static_cast<int64_t>(c) * kDecodeChunk;
+  const int rows_here = static_cast<int>(min<int64_t>(kDecodeChunk, cache_len - c0));
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase + c0 * DH, static_cast<uint32_t>(rows_here) * DH * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase + c0 * DH, static_cast<uint32_t>(rows_here) * DH * 2);
 
   float m_i = -INFINITY, l_i = 0.f;
   f32x16 acc[NDB];
@@ -354,20 +361,17 @@ __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
   for (int tile = 0; tile < TILES; ++tile) {
-    const int64_t j0 = static_cast<int64_t>(c) * kDecodeChunk + wave * (kDecodeChunk / 4) + tile * BN;
-    const bool live = j0 < cache_len;
+    const int jr = wave * (kDecodeChunk / 4) + tile * BN;  // first key of the tile, chunk-relative
+    const bool live = jr < rows_here;
     // V tile -> transposed per-wave LDS region.
     if (live) {
 #pragma unroll
       for (int it = 0; it < VITEMS / 64; ++it) {
-        const int item = lane + 64 * it, kq = item / (DH / 8), dc = item % (DH / 8);
+        const int item = lane + 64 * it, kq = item & 15, dc = item >> 4;
         u32x4 rv[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t key = j0 + 4 * kq + r;
-          rv[r] = key < cache_len ? *reinterpret_cast<const u32x4*>(vbase + key * DH + 8 * dc)
-                                  : u32x4{0, 0, 0, 0};
-        }
+        for (int r = 0; r < 4; ++r)
+          rv[r] = buffer_load16(vrs, static_cast<uint32_t>((jr + 4 * kq + r) * DH + 8 * dc) * 2);
         store_vt(Vt, VP, 8 * dc, 4 * kq, rv);
       }
     }
@@ -375,14 +379,11 @@ __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
-      const int64_t row = j0 + kb * 32 + kperm(l32);
-      const bf16_t* kr = kbase + min(row, cache_len - 1) * DH + 8 * hl;
+      const uint32_t rowoff = static_cast<uint32_t>((jr + kb * 32 + kperm(l32)) * DH + 8 * hl) * 2;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + 16 * ks);
-        if (row >= cache_len) a = bf16x8{};
-        s[kb] = mfma32x32x16(a, qf[ks], s[kb]);
-      }
+      for (int ks = 0; ks < NKS; ++ks)
+        s[kb] = mfma32x32x16(__builtin_bit_cast(bf16x8, buffer_load16(krs, rowoff + 32 * ks)), qf[ks],
+                             s[kb]);
     }
     __syncthreads();  // V tile stores visible to the wave's lanes
     float mx = -INFINITY;
@@ -390,8 +391,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t key = j0 + kb * 32 + 16 * (r >> 3) + 8 * hl + (r & 7);
-        if (key >= cache_len) s[kb][r] = -INFINITY;
+        if (jr + kb * 32 + 16 * (r >> 3) + 8 * hl + (r & 7) >= rows_here) s[kb][r] = -INFINITY;
         mx = fmaxf(mx, s[kb][r]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;

@@ -15,6 +15,15 @@ struct EpiStore {
   __device__ __forceinline__ void operator()(int m, int n, float v) const {
     c[static_cast<int64_t>(m) * ldc + n] = Elem<T>::from_f32(v);
   }
+  // Columns n .. n+3 (n % 4 == 0); those at or past N are dropped.
+  __device__ __forceinline__ void store4(int m, int n, const float* v, int N) const {
+    T* p = c + static_cast<int64_t>(m) * ldc + n;
+    if (n + 3 < N) {
+      mka::store4(p, v);
+    } else {
+      for (int i = 0; i < 4 && n + i < N; ++i) p[i] = Elem<T>::from_f32(v[i]);
+    }
+  }
 };
 
 // Scatter into the head-major fused KV cache [B, G, t_cap, dh]: row m is token
@@ -37,6 +46,17 @@ struct EpiKV {
     const int g = nn / head_dim, d = nn - g * head_dim;
     base[((static_cast<int64_t>(b) * n_kv_heads + g) * t_cap + pos0 + t) * head_dim + d] =
         Elem<T>::from_f32(val);
+  }
+  // Columns n .. n+3 (n % 4 == 0) lie in one head row since head_dim % 4 == 0.
+  __device__ __forceinline__ void store4(int m, int n, const float* vals, int N) const {
+    if (n >= N) return;
+    const int kvw = n_kv_heads * head_dim;
+    T* base = n < kvw ? k : v;
+    const int nn = n < kvw ? n : n - kvw;
+    const int b = m / seq, t = m - b * seq;
+    const int g = nn / head_dim, d = nn - g * head_dim;
+    mka::store4(base + ((static_cast<int64_t>(b) * n_kv_heads + g) * t_cap + pos0 + t) * head_dim + d,
+                vals);
   }
 };
 
@@ -62,8 +82,8 @@ template <typename T, class Epi>
 hipError_t gemv(const T* a, int lda, int M, const T* b0, const T* b1, int n_split, int N, int K,
                 const Epi& epi, hipStream_t s);
 
-// Tile of gemm_bf16; it needs K % kGemmBK == 0 and 16-byte aligned rows
-// (checked by the host layer before launching).
-constexpr int kGemmBM = 128, kGemmBN = 128, kGemmBK = 64;
+// k-tile of gemm_bf16; it needs K % kGemmBK == 0, N % 4 == 0 and 16-byte
+// aligned rows (checked by the host layer before launching).
+constexpr int kGemmBK = 64;
 
 }  // namespace mka

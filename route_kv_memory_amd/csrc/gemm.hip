@@ -5,16 +5,21 @@
 namespace mka {
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA GEMM.  Workgroup tile 128 x 128, k-tile 64, 4 waves in a 2 x 2
-// layout, each wave 64 x 64 = 2 x 2 MFMA 32x32x16 blocks.  Operand tiles are
-// staged in LDS (double buffered, rows padded by 16 bytes so the 16-byte
-// fragment reads of 16 consecutive rows hit distinct banks).
+// bf16 MFMA GEMM.  Workgroup tile 256 (M) x BN (N) x 64 (K), BN = 128 with 4
+// waves or 256 with 8 waves; each wave owns 128 x 64 of C as 4 x 2 blocks of
+// MFMA 32x32x16, so a k-step reads 6 fragments for 8 MFMAs.  The MFMA computes
+// C^T blocks (B rows as its A operand), which leaves 4 consecutive output
+// columns of one output row in each lane: the epilogue stores 8 bytes per lane.
+// Operand tiles go through registers into double-buffered LDS (rows padded by
+// 16 bytes: the fragment reads of 16 consecutive rows hit distinct banks);
+// global reads are buffer loads whose range makes rows past M or N read zero.
 // ---------------------------------------------------------------------------
-template <class Epi>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
+template <int BN, class Epi>
+__global__ __launch_bounds__(BN * 2) void gemm_bf16_kernel(
     const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B0,
     const bf16_t* __restrict__ B1, int n_split, int M, int N, int K, Epi epi) {
-  constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK, P = BK + 8;
+  constexpr int BM = 256, BK = kGemmBK, P = BK + 8, NT = BN * 2;
+  constexpr int ACH = BM * BK / 8 / NT, BCH = BN * BK / 8 / NT;  // 16-byte chunks per thread
   __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * P];
   __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * P];
 
@@ -25,34 +30,58 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, l32 = lane & 31;
+  const int wm = wave & 1, wn = wave >> 1, h = lane >> 5, l32 = lane & 31;
 
-  // Global -> register staging: 4 chunks of 16 bytes per operand per thread.
-  u32x4 ra[4], rb[4];
+  // A rows [m0, min(M, m0 + BM)) and B rows of this tile as buffer ranges.
+  const uint32_t a_rows = static_cast<uint32_t>(min(BM, M - m0));
+  const __amdgpu_buffer_rsrc_t ars =
+      make_rsrc(A + static_cast<int64_t>(m0) * lda, a_rows * static_cast<uint32_t>(lda) * 2);
+  // B rows come from b0 below n_split and b1 above; a tile never straddles
+  // n_split when n_split % BN == 0, otherwise rows are fetched one by one.
+  const bool straddle = n0 < n_split && n0 + BN > n_split;
+  const bf16_t* bbase = n0 < n_split ? B0 + static_cast<int64_t>(n0) * K
+                                     : B1 + static_cast<int64_t>(n0 - n_split) * K;
+  const int b_valid = min(BN, (n0 < n_split ? n_split : N) - n0);
+  const __amdgpu_buffer_rsrc_t brs =
+      make_rsrc(bbase, static_cast<uint32_t>(b_valid) * static_cast<uint32_t>(K) * 2);
+
+  u32x4 ra[ACH], rb[BCH];
   auto gload = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (tid >> 3) + 32 * i, col = (tid & 7) * 8;
-      const int gm = m0 + row, gn = n0 + row;
-      ra[i] = gm < M ? *reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(gm) * lda + k0 + col)
-                     : u32x4{0, 0, 0, 0};
-      const bf16_t* brow = gn < n_split ? B0 + static_cast<int64_t>(gn) * K
+    for (int i = 0; i < ACH; ++i) {
+      const int c = tid + NT * i, row = c >> 3, col = (c & 7) * 8;
+      ra[i] = buffer_load16(ars, static_cast<uint32_t>(row * lda + k0 + col) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) {
+      const int c = tid + NT * i, row = c >> 3, col = (c & 7) * 8;
+      if (!straddle) {
+        rb[i] = buffer_load16(brs, static_cast<uint32_t>(row * K + k0 + col) * 2);
+      } else {
+        const int gn = n0 + row;
+        const bf16_t* br = gn < n_split ? B0 + static_cast<int64_t>(gn) * K
                                         : B1 + static_cast<int64_t>(gn - n_split) * K;
-      rb[i] = gn < N ? *reinterpret_cast<const u32x4*>(brow + k0 + col) : u32x4{0, 0, 0, 0};
+        rb[i] = gn < N ? *reinterpret_cast<const u32x4*>(br + k0 + col) : u32x4{0, 0, 0, 0};
+      }
     }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (tid >> 3) + 32 * i, col = (tid & 7) * 8;
+    for (int i = 0; i < ACH; ++i) {
+      const int c = tid + NT * i, row = c >> 3, col = (c & 7) * 8;
       *reinterpret_cast<u32x4*>(&As[buf][row * P + col]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) {
+      const int c = tid + NT * i, row = c >> 3, col = (c & 7) * 8;
       *reinterpret_cast<u32x4*>(&Bs[buf][row * P + col]) = rb[i];
     }
   };
 
-  f32x16 acc[2][2];
+  // acc[i][j]: C^T block of output rows m0 + wm*128 + 32i .., columns n0 + wn*64 + 32j ..
+  f32x16 acc[4][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
@@ -65,40 +94,51 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(
     if (kt + 1 < nk) gload((kt + 1) * BK);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 fa[2], fb[2];
+      bf16x8 fa[4], fb[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8*>(&As[buf][(wm * 64 + i * 32 + l32) * P + ks * 16 + 8 * h]);
+      for (int i = 0; i < 4; ++i)
+        fa[i] = *reinterpret_cast<const bf16x8*>(&As[buf][(wm * 128 + i * 32 + l32) * P + ks * 16 + 8 * h]);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         fb[j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(wn * 64 + j * 32 + l32) * P + ks * 16 + 8 * h]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(fb[j], fa[i], acc[i][j]);
     }
     if (kt + 1 < nk) sstore(buf ^ 1);
     __syncthreads();
   }
 
+  // Lane holds output row m = ... + l32 and columns n = ... + 8*(r/4) + 4h + (r%4).
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + wm * 128 + i * 32 + l32;
+    if (m >= M) continue;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + i * 32 + acc_row(r, h);
-        const int n = n0 + wn * 64 + j * 32 + l32;
-        if (m < M && n < N) epi(m, n, acc[i][j][r]);
+      for (int rq = 0; rq < 4; ++rq) {
+        const int n = n0 + wn * 64 + j * 32 + 8 * rq + 4 * h;
+        const float v[4] = {acc[i][j][4 * rq], acc[i][j][4 * rq + 1], acc[i][j][4 * rq + 2],
+                            acc[i][j][4 * rq + 3]};
+        epi.store4(m, n, v, N);
       }
+  }
 }
 
 template <class Epi>
 hipError_t gemm_bf16(const bf16_t* a, int lda, const bf16_t* b0, const bf16_t* b1, int n_split,
                      int M, int N, int K, const Epi& epi, hipStream_t s) {
-  const int tiles = ((N + kGemmBN - 1) / kGemmBN) * ((M + kGemmBM - 1) / kGemmBM);
-  hipLaunchKernelGGL(gemm_bf16_kernel<Epi>, dim3(tiles), dim3(256), 0, s, a, lda, b0, b1, n_split,
-                     M, N, K, epi);
+  const int tiles256 = ((N + 255) / 256) * ((M + 255) / 256);
+  if (tiles256 >= 256) {
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, Epi>), dim3(tiles256), dim3(512), 0, s, a, lda, b0,
+                       b1, n_split, M, N, K, epi);
+  } else {
+    const int tiles = ((N + 127) / 128) * ((M + 255) / 256);
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, Epi>), dim3(tiles), dim3(256), 0, s, a, lda, b0, b1,
+                       n_split, M, N, K, epi);
+  }
   return hipGetLastError();
 }
 
