@@ -101,9 +101,11 @@ int mka_route(const mka_dims* d, const void* x, const void* w_q, const void* w_r
  * prefix, here the EMA s_t = beta*s_{t-1} + (1-beta)*x_t, prefix inclusive of
  * t, s_{-1} = 0; the L3 bank holds past blocks.)
  *   x            [B, seq, D]   dtype
- *   state_io     [B, D]        in: s_{pos0-1} (zeros when pos0 == 0); out: s_{pos0+seq-1}
- *   block_acc_io [B, D]        in: sum of x over the tokens of pos0's block before pos0;
- *                              out: the same sum for the block after the last token
+ *   state_io     [B, D]        in: s_{pos0-1} (not read when pos0 == 0: the prefix is
+ *                              empty); out: s_{pos0+seq-1}
+ *   block_acc_io [B, D]        in: sum of x over the tokens of pos0's block before pos0 (not
+ *                              read when pos0 % block == 0); out: the same sum for the block
+ *                              after the last token
  *   l2_out       [B, seq, D]   float32 (written)
  *   block_means  [B, nb_cap, D] float32: row b = mean of x over block b is written
  *                              for every block whose last token is in this call
@@ -226,7 +228,13 @@ int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weight
  * append at row pos, decode attention over rows 0..pos, and -- when pos closes a
  * block ((pos+1) % block == 0) -- the block mean and its code appended to the bank.
  * Same buffers as mka_prefill with seq = 1;
- * ws >= mka_workspace_bytes(d, MKA_OP_DECODE_STEP, pos + 1) bytes. */
+ * ws >= mka_workspace_bytes(d, MKA_OP_DECODE_STEP, pos + 1) bytes.
+ * bf16: the attention over rows 0..pos-1 needs only q, so it runs on ``stream`` while
+ * the rest of the step runs on an auxiliary stream of the library (one per device,
+ * created on the device's first decode step with two events, kept until the process
+ * ends); the step's last kernel, on ``stream``, merges both.  Completion is still
+ * signalled on ``stream`` alone.  Concurrent calls on one device serialise their
+ * enqueueing. */
 int mka_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_weights* w,
                     const mka_state* st, const mka_outputs* out, void* ws, size_t ws_bytes,
                     void* stream);

@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmka.so")
 
-SOURCES = ["mka_api.hip", "gemm.hip", "route.hip", "ema.hip", "l3.hip", "fuse.hip", "attn.hip"]
+SOURCES = ["mka_api.hip", "gemm.hip", "route.hip", "ema.hip", "l3.hip", "fuse.hip", "attn.hip",
+           "decode.hip"]
 
 ARCH = os.environ.get("MKA_OFFLOAD_ARCH", "gfx950")
 

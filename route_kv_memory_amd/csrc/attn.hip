@@ -468,25 +468,38 @@ __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(
 }
 
 template <int DH>
-__global__ __launch_bounds__(512) void attn_decode_merge_kernel(const float* __restrict__ part_m,
-                                                                const float* __restrict__ part_l,
-                                                                const float* __restrict__ part_o,
-                                                                int H, int n_chunks,
-                                                                bf16_t* __restrict__ O) {
+__global__ __launch_bounds__(512) void attn_decode_merge_kernel(
+    const float* __restrict__ part_m, const float* __restrict__ part_l,
+    const float* __restrict__ part_o, int H, int G, int n_chunks, const bf16_t* __restrict__ Q,
+    const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc, int64_t t_cap,
+    int64_t extra_row, float sl2, bf16_t* __restrict__ O) {
   constexpr int NT = 512, GR = NT / DH;
   __shared__ float wts[kMaxDecodeChunks];
   __shared__ float red[NT];
   __shared__ float osum[GR][DH];
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  __shared__ float sx_s;
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int g = h / (H / G);
   const int64_t p0 = (static_cast<int64_t>(b) * H + h) * n_chunks;
+  const bf16_t* krow = Kc + ((static_cast<int64_t>(b) * G + g) * t_cap + extra_row) * DH;
+  const bf16_t* vrow = Vc + ((static_cast<int64_t>(b) * G + g) * t_cap + extra_row) * DH;
+  // Score of the extra row (the token's own fused K/V), scaled like the parts.
+  if (extra_row >= 0 && tid < 64) {
+    const bf16_t* qh = Q + (static_cast<int64_t>(b) * H + h) * DH;
+    float dot = 0.f;
+    for (int d = lane; d < DH; d += 64) dot = fmaf(bf16_to_f32(qh[d]), bf16_to_f32(krow[d]), dot);
+    dot = wave_sum(dot);
+    if (lane == 0) sx_s = dot * sl2;
+  }
   float mx = -INFINITY;
   for (int c = tid; c < n_chunks; c += NT) mx = fmaxf(mx, part_m[p0 + c]);
   mx = wave_max(mx);
-  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  if (lane == 0) red[tid >> 6] = mx;
   __syncthreads();
-  float M = red[0];
+  const float sx = extra_row >= 0 ? sx_s : -INFINITY;
+  float M = sx;
 #pragma unroll
-  for (int w = 1; w < NT / 64; ++w) M = fmaxf(M, red[w]);
+  for (int w = 0; w < NT / 64; ++w) M = fmaxf(M, red[w]);
   __syncthreads();
   float ls = 0.f;
   for (int c = tid; c < n_chunks; c += NT) {
@@ -495,9 +508,10 @@ __global__ __launch_bounds__(512) void attn_decode_merge_kernel(const float* __r
     ls += w * part_l[p0 + c];
   }
   ls = wave_sum(ls);
-  if ((tid & 63) == 0) red[tid >> 6] = ls;
+  if (lane == 0) red[tid >> 6] = ls;
   __syncthreads();
-  float L = 0.f;
+  const float wx = extra_row >= 0 ? __builtin_amdgcn_exp2f(sx - M) : 0.f;
+  float L = wx;
 #pragma unroll
   for (int w = 0; w < NT / 64; ++w) L += red[w];
   const int d = tid % DH, grp = tid / DH;
@@ -507,35 +521,60 @@ __global__ __launch_bounds__(512) void attn_decode_merge_kernel(const float* __r
   osum[grp][d] = o;
   __syncthreads();
   if (tid < DH) {
-    float tot = 0.f;
+    float tot = extra_row >= 0 ? wx * bf16_to_f32(vrow[tid]) : 0.f;
 #pragma unroll
     for (int gi = 0; gi < GR; ++gi) tot += osum[gi][tid];
     O[(static_cast<int64_t>(b) * H + h) * DH + tid] = f32_to_bf16(tot / L);
   }
 }
 
-hipError_t attn_decode_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* v, bf16_t* o, int B,
-                            int H, int G, int dh, int64_t t_cap, int64_t cache_len, void* ws,
-                            hipStream_t s) {
-  const int n_chunks = static_cast<int>((cache_len + kDecodeChunk - 1) / kDecodeChunk);
+static int decode_chunks(int64_t n) { return static_cast<int>((n + kDecodeChunk - 1) / kDecodeChunk); }
+
+hipError_t attn_decode_split_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* v, int B, int H,
+                                  int G, int dh, int64_t t_cap, int64_t n_old, void* ws,
+                                  hipStream_t s) {
+  const int n_chunks = decode_chunks(n_old);
+  if (n_chunks == 0) return hipSuccess;
   if (n_chunks > kMaxDecodeChunks) return hipErrorInvalidValue;
   float* part_m = static_cast<float*>(ws);
   float* part_l = part_m + static_cast<size_t>(B) * H * n_chunks;
   float* part_o = part_l + static_cast<size_t>(B) * H * n_chunks;
   const float sl2 = 1.4426950408889634f / sqrtf(static_cast<float>(dh));
   const dim3 grid(n_chunks, G, B);
-  if (dh == 128) {
+  if (dh == 128)
     hipLaunchKernelGGL(attn_decode_split_kernel<128>, grid, dim3(256), 0, s, q, k, v, H, G, t_cap,
-                       cache_len, sl2, n_chunks, part_m, part_l, part_o);
-    hipLaunchKernelGGL(attn_decode_merge_kernel<128>, dim3(H, B), dim3(512), 0, s, part_m, part_l,
-                       part_o, H, n_chunks, o);
-  } else {
+                       n_old, sl2, n_chunks, part_m, part_l, part_o);
+  else
     hipLaunchKernelGGL(attn_decode_split_kernel<64>, grid, dim3(256), 0, s, q, k, v, H, G, t_cap,
-                       cache_len, sl2, n_chunks, part_m, part_l, part_o);
-    hipLaunchKernelGGL(attn_decode_merge_kernel<64>, dim3(H, B), dim3(512), 0, s, part_m, part_l,
-                       part_o, H, n_chunks, o);
-  }
+                       n_old, sl2, n_chunks, part_m, part_l, part_o);
   return hipGetLastError();
+}
+
+hipError_t attn_decode_merge_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* v, bf16_t* o,
+                                  int B, int H, int G, int dh, int64_t t_cap, int64_t n_old,
+                                  int64_t extra_row, void* ws, hipStream_t s) {
+  const int n_chunks = decode_chunks(n_old);
+  if (n_chunks > kMaxDecodeChunks) return hipErrorInvalidValue;
+  float* part_m = static_cast<float*>(ws);
+  float* part_l = part_m + static_cast<size_t>(B) * H * n_chunks;
+  float* part_o = part_l + static_cast<size_t>(B) * H * n_chunks;
+  const float sl2 = 1.4426950408889634f / sqrtf(static_cast<float>(dh));
+  if (dh == 128)
+    hipLaunchKernelGGL(attn_decode_merge_kernel<128>, dim3(H, B), dim3(512), 0, s, part_m, part_l,
+                       part_o, H, G, n_chunks, q, k, v, t_cap, extra_row, sl2, o);
+  else
+    hipLaunchKernelGGL(attn_decode_merge_kernel<64>, dim3(H, B), dim3(512), 0, s, part_m, part_l,
+                       part_o, H, G, n_chunks, q, k, v, t_cap, extra_row, sl2, o);
+  return hipGetLastError();
+}
+
+// Rows [0, cache_len - 1) through the split kernel; the last row in the merge.
+hipError_t attn_decode_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* v, bf16_t* o, int B,
+                            int H, int G, int dh, int64_t t_cap, int64_t cache_len, void* ws,
+                            hipStream_t s) {
+  const hipError_t e = attn_decode_split_bf16(q, k, v, B, H, G, dh, t_cap, cache_len - 1, ws, s);
+  if (e != hipSuccess) return e;
+  return attn_decode_merge_bf16(q, k, v, o, B, H, G, dh, t_cap, cache_len - 1, cache_len - 1, ws, s);
 }
 
 }  // namespace mka

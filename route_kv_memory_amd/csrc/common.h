@@ -59,13 +59,31 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b,
 // Row (within the 32x32 block) of accumulator register r for lane half h.
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-__device__ __forceinline__ float wave_max(float v) {
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
+// Wave-wide reductions through DPP lane moves (xor-1 and xor-2 within quads,
+// mirrors within rows of 16, row broadcasts), read back from lane 63: every lane
+// gets the result.  Lanes without a DPP source contribute the identity.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float identity, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(v), CTRL,
+                                                    ROW_MASK, 0xF, false));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  v += dpp_f32<0xB1, 0xF>(0.f, v);
+  v += dpp_f32<0x4E, 0xF>(0.f, v);
+  v += dpp_f32<0x141, 0xF>(0.f, v);
+  v += dpp_f32<0x140, 0xF>(0.f, v);
+  v += dpp_f32<0x142, 0xA>(0.f, v);
+  v += dpp_f32<0x143, 0xC>(0.f, v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1, 0xF>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<0x4E, 0xF>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<0x141, 0xF>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<0x140, 0xF>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<0x142, 0xA>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<0x143, 0xC>(-INFINITY, v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }

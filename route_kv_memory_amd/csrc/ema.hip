@@ -60,7 +60,9 @@ __global__ __launch_bounds__(256) void ema_pass2(float* __restrict__ agg_s, floa
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= B * D) return;
   const int b = e / D, ch = e - b * D;
-  float cs = state_in[e], ca = acc_in[e];
+  // An empty prefix (pos0 == 0) and an empty partial block (pos0 at a block
+  // start) contribute zero whatever the buffers hold.
+  float cs = pos0 == 0 ? 0.f : state_in[e], ca = pos0 % block == 0 ? 0.f : acc_in[e];
   float* ps = agg_s + static_cast<int64_t>(b) * n_chunks * D + ch;
   float* pa = agg_a + static_cast<int64_t>(b) * n_chunks * D + ch;
   for (int c = 0; c < n_chunks; ++c) {
@@ -87,9 +89,9 @@ __global__ __launch_bounds__(kEmaThreads) void ema_pass3(
   const int t0 = c * kEmaChunk, t1 = min(t0 + kEmaChunk, seq);
   const int64_t co = carry_chunks ? (static_cast<int64_t>(b) * carry_chunks + c) * D + ch
                                   : static_cast<int64_t>(b) * D + ch;
-  float s[4], a[4];
-  load4(carry_s + co, s);
-  load4(carry_a + co, a);
+  float s[4] = {0.f, 0.f, 0.f, 0.f}, a[4] = {0.f, 0.f, 0.f, 0.f};
+  if (carry_chunks || pos0 != 0) load4(carry_s + co, s);
+  if (carry_chunks || pos0 % block != 0) load4(carry_a + co, a);
   const T* xp = x + (static_cast<int64_t>(b) * seq + t0) * D + ch;
   float* lp = l2 + (static_cast<int64_t>(b) * seq + t0) * D + ch;
   for (int t = t0; t < t1; ++t, xp += D, lp += D) {
@@ -116,6 +118,75 @@ __global__ __launch_bounds__(kEmaThreads) void ema_pass3(
     store4(acc_out + static_cast<int64_t>(b) * D + ch, a);
   }
 }
+
+// ---------------------------------------------------------------------------
+// Decode: one token per sequence.  A workgroup takes 128 channels of one
+// sequence: EMA update (and block mean when the token closes a block), then
+// the fp64 partial projections of the new L2 row onto every hyperplane over
+// its channels, written to part[(slice * B + b) * 64 + j] for the retrieval's
+// selection step to sum in slice order.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(128) void ema_hash_decode_kernel(
+    const T* __restrict__ x, int D, int64_t pos, int block, float beta, float omb,
+    float* __restrict__ state, float* __restrict__ acc, float* __restrict__ l2,
+    float* __restrict__ means, int nb_cap, const float* __restrict__ P, int nbits,
+    double* __restrict__ part) {
+  __shared__ float Ps[64][129];
+  __shared__ float Ls[128];
+  __shared__ double red[2][64];
+  const int tid = threadIdx.x, slice = blockIdx.x, b = blockIdx.y, B = gridDim.y;
+  const int c0 = slice * 128, ch = c0 + tid;
+  for (int e = tid; e < 64 * 128; e += 128) {
+    const int j = e >> 7, c = e & 127;
+    Ps[j][c] = (j < nbits && c0 + c < D) ? P[static_cast<int64_t>(j) * D + c0 + c] : 0.f;
+  }
+  float sv = 0.f;
+  if (ch < D) {
+    const int64_t o = static_cast<int64_t>(b) * D + ch;
+    const float xv = Elem<T>::to_f32(x[o]);
+    sv = fmaf(beta, pos == 0 ? 0.f : state[o], omb * xv);
+    float a = (pos % block == 0 ? 0.f : acc[o]) + xv;
+    state[o] = sv;
+    l2[o] = sv;
+    if ((pos + 1) % block == 0) {
+      means[(static_cast<int64_t>(b) * nb_cap + (pos + 1) / block - 1) * D + ch] =
+          a / static_cast<float>(block);
+      a = 0.f;
+    }
+    acc[o] = a;
+  }
+  Ls[tid] = sv;
+  __syncthreads();
+  const int j = tid & 63, half = tid >> 6;
+  double p = 0.0;
+#pragma unroll 8
+  for (int c = half * 64; c < half * 64 + 64; ++c)
+    p = fma(static_cast<double>(Ls[c]), static_cast<double>(Ps[j][c]), p);
+  red[half][j] = p;
+  __syncthreads();
+  if (tid < 64) part[(static_cast<int64_t>(slice) * B + b) * 64 + tid] = red[0][tid] + red[1][tid];
+}
+
+size_t ema_hash_decode_ws_bytes(int B, int D) {
+  return sizeof(double) * static_cast<size_t>((D + 127) / 128) * B * 64;
+}
+
+template <typename T>
+hipError_t ema_hash_decode(const T* x, int B, int D, int64_t pos, int block, float beta,
+                           float* state, float* acc, float* l2, float* means, int nb_cap,
+                           const float* proj, int nbits, double* part, hipStream_t s) {
+  hipLaunchKernelGGL(ema_hash_decode_kernel<T>, dim3((D + 127) / 128, B), dim3(128), 0, s, x, D,
+                     pos, block, beta, 1.0f - beta, state, acc, l2, means, nb_cap, proj, nbits,
+                     part);
+  return hipGetLastError();
+}
+template hipError_t ema_hash_decode<float>(const float*, int, int, int64_t, int, float, float*,
+                                           float*, float*, float*, int, const float*, int, double*,
+                                           hipStream_t);
+template hipError_t ema_hash_decode<bf16_t>(const bf16_t*, int, int, int64_t, int, float, float*,
+                                            float*, float*, float*, int, const float*, int,
+                                            double*, hipStream_t);
 
 size_t ema_ws_bytes(int B, int seq, int D) {
   const int n_chunks = (seq + kEmaChunk - 1) / kEmaChunk;

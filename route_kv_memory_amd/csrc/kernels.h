@@ -26,6 +26,13 @@ hipError_t ema_scan(const T* x, int B, int seq, int D, int64_t pos0, int block, 
                     float* state_io, float* acc_io, float* l2, float* means, int nb_cap,
                     float* ws, hipStream_t s);
 size_t ema_ws_bytes(int B, int seq, int D);
+// Decode (one token per sequence): EMA update + block finalise + fp64 partial
+// key projections over 128-channel slices (summed by select_codes_topr).
+size_t ema_hash_decode_ws_bytes(int B, int D);
+template <typename T>
+hipError_t ema_hash_decode(const T* x, int B, int D, int64_t pos, int block, float beta,
+                           float* state, float* acc, float* l2, float* means, int nb_cap,
+                           const float* proj, int nbits, double* part, hipStream_t s);
 
 // ---- SimHash codes and top-R retrieval ---------------------------------------
 // codes[b * codes_bstride + i] = SimHash(v[b * v_bstride + i * D .. +D]) for i < rows.
@@ -40,6 +47,11 @@ size_t retrieve_few_ws_bytes(int rows, int D);
 hipError_t retrieve_few(const float* l2, int B, int seq, int D, const float* proj, int nbits,
                         const uint64_t* bh, int nb_cap, int block, int R, int64_t pos0,
                         uint64_t* keys, int32_t* idx, void* ws, hipStream_t s);
+// Select from partial key projections already in ``part`` (n_slices slices of
+// rows x 64 fp64 sums): one workgroup per token sums, forms the key, picks top R.
+hipError_t select_codes_topr(const double* part, int rows, int n_slices, int nbits, int seq,
+                             int64_t pos0, const uint64_t* bh, int nb_cap, int block, int R,
+                             uint64_t* keys, int32_t* idx, hipStream_t s);
 // Many rows (prefill): keys already computed, one lane per token.
 hipError_t topr_rows(const uint64_t* keys, int B, int seq, int64_t pos0, const uint64_t* bh,
                      int nb_cap, int block, int R, int32_t* idx, hipStream_t s);
@@ -57,10 +69,19 @@ template <typename T>
 hipError_t attn_prefill(const T* q, const T* k, const T* v, T* o, int B, int seq, int H, int G,
                         int dh, int64_t t_cap, int64_t pos0, hipStream_t s);
 // Split decode (bf16): partials in ws, merged by a second kernel.
-constexpr int kDecodeChunk = 1024;  // keys per workgroup
+constexpr int kDecodeChunk = 2048;  // keys per workgroup
 size_t attn_decode_ws_bytes(int B, int H, int dh, int64_t cache_len);
 hipError_t attn_decode_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* v, bf16_t* o, int B,
                             int H, int G, int dh, int64_t t_cap, int64_t cache_len, void* ws,
                             hipStream_t s);
+// The same in two halves, so that work can run between them: the split over
+// cache rows [0, n_old) (nothing when n_old == 0), then the merge, which also
+// folds in row n_old (written in between) as one more part.
+hipError_t attn_decode_split_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* v, int B, int H,
+                                  int G, int dh, int64_t t_cap, int64_t n_old, void* ws,
+                                  hipStream_t s);
+hipError_t attn_decode_merge_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* v, bf16_t* o,
+                                  int B, int H, int G, int dh, int64_t t_cap, int64_t n_old,
+                                  int64_t extra_row, void* ws, hipStream_t s);
 
 }  // namespace mka

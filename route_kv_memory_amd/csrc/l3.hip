@@ -295,6 +295,18 @@ __global__ __launch_bounds__(256) void select_few_kernel(const double* __restric
   }
 }
 
+hipError_t select_codes_topr(const double* part, int rows, int n_slices, int nbits, int seq,
+                             int64_t pos0, const uint64_t* bh, int nb_cap, int block, int R,
+                             uint64_t* keys, int32_t* idx, hipStream_t s) {
+  if (R <= 16)
+    hipLaunchKernelGGL(select_few_kernel<16>, dim3(rows), dim3(256), 0, s, part, rows, n_slices,
+                       nbits, seq, pos0, bh, nb_cap, block, R, keys, idx);
+  else
+    hipLaunchKernelGGL(select_few_kernel<32>, dim3(rows), dim3(256), 0, s, part, rows, n_slices,
+                       nbits, seq, pos0, bh, nb_cap, block, R, keys, idx);
+  return hipGetLastError();
+}
+
 hipError_t retrieve_few(const float* l2, int B, int seq, int D, const float* proj, int nbits,
                         const uint64_t* bh, int nb_cap, int block, int R, int64_t pos0,
                         uint64_t* keys, int32_t* idx, void* ws, hipStream_t s) {

@@ -5,8 +5,13 @@
 #include <initializer_list>
 #include <cstdio>
 #include <cstring>
+#include <memory>
+#include <mutex>
+#include <type_traits>
+#include <unordered_map>
 
 #include "../../include/mka.h"
+#include "decode.h"
 #include "gemm.h"
 #include "kernels.h"
 
@@ -91,18 +96,33 @@ size_t decode_ws(const mka_dims* d, int64_t cache_len) {
 // ---------------------------------------------------------------- per-step bodies
 // Each body assumes check_dims passed and its pointers were validated.
 
-int do_route(const mka_dims* d, const void* x, const void* w_q, const void* w_r1, const void* w_r2,
-             void* q_out, float* lam, void* ws, hipStream_t s) {
-  const int M = rows_of(d), D = d->d_model, qw = d->n_heads * d->head_dim, r = d->router_hidden;
+int do_qproj(const mka_dims* d, const void* x, const void* w_q, void* q_out, hipStream_t s) {
+  const int M = rows_of(d), D = d->d_model, qw = d->n_heads * d->head_dim;
   if (d->dtype == MKA_BF16) {
     const bf16_t* xb = static_cast<const bf16_t*>(x);
     const bf16_t* wq = static_cast<const bf16_t*>(w_q);
-    bf16_t* q = static_cast<bf16_t*>(q_out);
-    const EpiStore<bf16_t> epi{q, qw};
+    const EpiStore<bf16_t> epi{static_cast<bf16_t*>(q_out), qw};
     if (M <= kFewRows)
       MKA_LAUNCH("route/q_gemv", gemv<bf16_t>(xb, D, M, wq, wq, qw, qw, D, epi, s));
     else
       MKA_LAUNCH("route/q_gemm", gemm_bf16(xb, D, wq, wq, qw, M, qw, D, epi, s));
+  } else {
+    const float* xf = static_cast<const float*>(x);
+    const float* wq = static_cast<const float*>(w_q);
+    const EpiStore<float> epi{static_cast<float*>(q_out), qw};
+    if (M <= kFewRows)
+      MKA_LAUNCH("route/q_gemv", gemv<float>(xf, D, M, wq, wq, qw, qw, D, epi, s));
+    else
+      MKA_LAUNCH("route/q_gemm", gemm_f32(xf, D, wq, wq, qw, M, qw, D, epi, s));
+  }
+  return MKA_OK;
+}
+
+int do_router(const mka_dims* d, const void* q_in, const void* w_r1, const void* w_r2, float* lam,
+              void* ws, hipStream_t s) {
+  const int M = rows_of(d), qw = d->n_heads * d->head_dim, r = d->router_hidden;
+  if (d->dtype == MKA_BF16) {
+    const bf16_t* q = static_cast<const bf16_t*>(q_in);
     const bf16_t* w1 = static_cast<const bf16_t*>(w_r1);
     const bf16_t* w2 = static_cast<const bf16_t*>(w_r2);
     if (M <= kFewRows) {
@@ -115,23 +135,25 @@ int do_route(const mka_dims* d, const void* x, const void* w_q, const void* w_r1
       MKA_LAUNCH("route/router", router_rowwise<bf16_t>(q, M, qw, w1, r, w2, lam, s));
     }
   } else {
-    const float* xf = static_cast<const float*>(x);
-    const float* wq = static_cast<const float*>(w_q);
-    float* q = static_cast<float*>(q_out);
-    const EpiStore<float> epi{q, qw};
+    const float* q = static_cast<const float*>(q_in);
     const float* w1 = static_cast<const float*>(w_r1);
     const float* w2 = static_cast<const float*>(w_r2);
     if (M <= kFewRows) {
-      MKA_LAUNCH("route/q_gemv", gemv<float>(xf, D, M, wq, wq, qw, qw, D, epi, s));
       float* hid = static_cast<float*>(ws);
       MKA_LAUNCH("route/hidden", gemv<float>(q, qw, M, w1, w1, r, r, qw, EpiGelu{hid, r}, s));
       MKA_LAUNCH("route/head", router_head<float>(hid, M, r, w2, lam, s));
     } else {
-      MKA_LAUNCH("route/q_gemm", gemm_f32(xf, D, wq, wq, qw, M, qw, D, epi, s));
       MKA_LAUNCH("route/router", router_rowwise<float>(q, M, qw, w1, r, w2, lam, s));
     }
   }
   return MKA_OK;
+}
+
+int do_route(const mka_dims* d, const void* x, const void* w_q, const void* w_r1, const void* w_r2,
+             void* q_out, float* lam, void* ws, hipStream_t s) {
+  int rc = do_qproj(d, x, w_q, q_out, s);
+  if (rc) return rc;
+  return do_router(d, q_out, w_r1, w_r2, lam, ws, s);
 }
 
 int do_ema(const mka_dims* d, const void* x, int64_t pos0, float* state_io, float* acc_io,
@@ -253,6 +275,59 @@ bool ptrs_ok(std::initializer_list<const void*> ps) {
 
 constexpr int64_t kMaxDecodeCache = static_cast<int64_t>(kDecodeChunk) * 4096;
 
+// Per-device auxiliary stream and fork/join events of mka_decode_step,
+// created on a device's first decode step and kept until the process ends.
+// The enqueueing of one decode step holds the device's lock, so concurrent
+// callers cannot interleave their fork/join records.
+struct Aux {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex lock;
+};
+
+Aux* aux_for_current_device(int* rc) {
+  static std::mutex table_lock;
+  static std::unordered_map<int, std::unique_ptr<Aux>> table;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *rc = hip_fail("decode/aux", e);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> g(table_lock);
+  auto it = table.find(dev);
+  if (it != table.end()) return it->second.get();
+  auto a = std::make_unique<Aux>();
+  if ((e = hipStreamCreateWithFlags(&a->stream, hipStreamNonBlocking)) != hipSuccess ||
+      (e = hipEventCreateWithFlags(&a->fork, hipEventDisableTiming)) != hipSuccess ||
+      (e = hipEventCreateWithFlags(&a->join, hipEventDisableTiming)) != hipSuccess) {
+    *rc = hip_fail("decode/aux", e);
+    return nullptr;
+  }
+  Aux* p = a.get();
+  table.emplace(dev, std::move(a));
+  return p;
+}
+
+// Workspace of the overlapped bf16 decode step: the attention partials (used
+// on the caller's stream) and the bookkeeping chain's buffers (auxiliary
+// stream) are disjoint.
+struct DecodeWs {
+  size_t attn, hid, part, xf, index, total;
+};
+DecodeWs decode_layout(const mka_dims* d, int64_t cache_len) {
+  DecodeWs w{};
+  w.attn = d->dtype == MKA_BF16
+               ? round256(attn_decode_ws_bytes(d->batch, d->n_heads, d->head_dim, cache_len))
+               : 0;
+  w.hid = round256(static_cast<size_t>(d->batch) * d->router_hidden * sizeof(float));
+  w.part = round256(sizeof(double) * static_cast<size_t>(decode_slices(d->d_model)) * d->batch * 64);
+  w.xf = fuse_ws(d);
+  w.index = index_ws(d, 1);
+  w.total = w.attn + w.hid + w.part + w.xf + w.index;
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -290,15 +365,8 @@ size_t mka_workspace_bytes(const mka_dims* d, int op, int64_t cache_len) {
       if (index_ws(d, d->seq / d->block + 1) > w) w = index_ws(d, d->seq / d->block + 1);
       return w;
     }
-    case MKA_OP_DECODE_STEP: {
-      if (d->seq != 1) return 0;
-      size_t w = fuse_ws(d);
-      if (retrieve_ws(d) > w) w = retrieve_ws(d);
-      if (index_ws(d, 1) > w) w = index_ws(d, 1);
-      if (route_ws(d) > w) w = route_ws(d);
-      if (cache_len > 0 && decode_ws(d, cache_len) > w) w = decode_ws(d, cache_len);
-      return w;
-    }
+    case MKA_OP_DECODE_STEP:
+      return d->seq == 1 && cache_len > 0 ? decode_layout(d, cache_len).total : 0;
     default: return 0;
   }
 }
@@ -474,22 +542,101 @@ int mka_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_wei
   const size_t need = mka_workspace_bytes(d, MKA_OP_DECODE_STEP, pos + 1);
   MKA_CHECK(ws_bytes >= need, MKA_ERR_WORKSPACE);
   MKA_CHECK(need == 0 || ptrs_ok({ws}), MKA_ERR_WORKSPACE);
+  MKA_CHECK(d->batch <= kFewRowsDec, MKA_ERR_UNSUPPORTED);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((rc = do_route(d, x, w->w_q, w->w_r1, w->w_r2, out->q, out->lambda, ws, s))) return rc;
-  if ((rc = do_ema(d, x, pos, st->ema_state, st->block_acc, out->l2, st->block_means, st->nb_cap,
-                   nullptr, s)))
+  const DecodeWs L = decode_layout(d, pos + 1);
+  char* base = static_cast<char*>(ws);
+  void* w_attn = base;
+  float* w_hid = reinterpret_cast<float*>(base + L.attn);
+  double* w_part = reinterpret_cast<double*>(base + L.attn + L.hid);
+  void* w_xf = base + L.attn + L.hid + L.part;
+  void* w_index = base + L.attn + L.hid + L.part + L.xf;
+  const int B = d->batch, D = d->d_model, qw = d->n_heads * d->head_dim, kvw = d->n_kv_heads * d->head_dim;
+  const bool closes = (pos + 1) % d->block == 0;
+  const int closed_block = static_cast<int>((pos + 1) / d->block - 1);
+
+  auto fill = [&](auto* tag) {
+    using T = std::remove_pointer_t<decltype(tag)>;
+    DecodeArgs<T> a{};
+    a.x = static_cast<const T*>(x);
+    a.w_q = static_cast<const T*>(w->w_q);
+    a.q = static_cast<T*>(out->q);
+    a.D = D;
+    a.qw = qw;
+    a.B = B;
+    a.state = st->ema_state;
+    a.acc = st->block_acc;
+    a.l2 = out->l2;
+    a.means = st->block_means;
+    a.nb_cap = st->nb_cap;
+    a.pos = pos;
+    a.block = d->block;
+    a.beta = d->ema_decay;
+    a.omb = 1.0f - d->ema_decay;
+    a.proj = w->proj;
+    a.nbits = d->hash_bits;
+    a.n_slices = decode_slices(D);
+    a.part = w_part;
+    a.w_r1 = static_cast<const T*>(w->w_r1);
+    a.w_r2 = static_cast<const T*>(w->w_r2);
+    a.r = d->router_hidden;
+    a.hidden = w_hid;
+    a.lam = out->lambda;
+    a.bhash = st->block_hash;
+    a.key = out->key;
+    a.idx = out->idx;
+    a.R = d->top_r;
+    a.xf = static_cast<T*>(w_xf);
+    return a;
+  };
+
+  if (d->dtype != MKA_BF16) {  // fp32 layers: the same kernels in order on one stream
+    const DecodeArgs<float> a = fill(static_cast<float*>(nullptr));
+    MKA_LAUNCH("decode/front", decode_front<float>(a, s));
+    MKA_LAUNCH("decode/mid", decode_mid<float>(a, s));
+    MKA_LAUNCH("decode/fuse", decode_fuse<float>(a, s));
+    const EpiKV<float> epi{static_cast<float*>(st->k_cache), static_cast<float*>(st->v_cache), 1,
+                           d->n_kv_heads, d->head_dim, st->t_cap, pos};
+    MKA_LAUNCH("decode/kv", gemv<float>(a.xf, D, B, static_cast<const float*>(w->w_k),
+                                        static_cast<const float*>(w->w_v), kvw, 2 * kvw, D, epi, s));
+    if ((rc = do_attn_decode(d, out->q, st->k_cache, st->v_cache, st->t_cap, pos + 1, out->o,
+                             nullptr, s)))
+      return rc;
+    if (closes)
+      return do_index(d, st->block_means, st->nb_cap, closed_block, 1, w->proj, st->block_hash,
+                      w_index, s);
+    return MKA_OK;
+  }
+  // bf16: the split attention over rows [0, pos) needs only q, so it runs on the
+  // caller's stream while the rest of the step (router, top-R, fusion, K/V
+  // append of row pos, block finalise) runs on the auxiliary stream; the merge
+  // then folds in row pos.
+  Aux* aux = aux_for_current_device(&rc);
+  if (aux == nullptr) return rc;
+  std::lock_guard<std::mutex> guard(aux->lock);
+  hipStream_t s2 = aux->stream;
+  const DecodeArgs<bf16_t> a = fill(static_cast<bf16_t*>(nullptr));
+  const bf16_t* kc = static_cast<const bf16_t*>(st->k_cache);
+  const bf16_t* vc = static_cast<const bf16_t*>(st->v_cache);
+  MKA_LAUNCH("decode/front", decode_front<bf16_t>(a, s));
+  MKA_LAUNCH("decode/fork", hipEventRecord(aux->fork, s));
+  MKA_LAUNCH("decode/fork", hipStreamWaitEvent(s2, aux->fork, 0));
+  MKA_LAUNCH("decode/attn_split", attn_decode_split_bf16(a.q, kc, vc, B, d->n_heads, d->n_kv_heads,
+                                                         d->head_dim, st->t_cap, pos, w_attn, s));
+  MKA_LAUNCH("decode/mid", decode_mid<bf16_t>(a, s2));
+  MKA_LAUNCH("decode/fuse", decode_fuse<bf16_t>(a, s2));
+  const EpiKV<bf16_t> epi{static_cast<bf16_t*>(st->k_cache), static_cast<bf16_t*>(st->v_cache), 1,
+                          d->n_kv_heads, d->head_dim, st->t_cap, pos};
+  MKA_LAUNCH("decode/kv", gemv<bf16_t>(a.xf, D, B, static_cast<const bf16_t*>(w->w_k),
+                                       static_cast<const bf16_t*>(w->w_v), kvw, 2 * kvw, D, epi, s2));
+  if (closes && (rc = do_index(d, st->block_means, st->nb_cap, closed_block, 1, w->proj,
+                               st->block_hash, w_index, s2)))
     return rc;
-  if ((rc = do_retrieve(d, out->l2, w->proj, st->block_hash, st->nb_cap, pos, out->key, out->idx,
-                        ws, s)))
-    return rc;
-  if ((rc = do_fuse_kv(d, x, out->l2, st->block_means, st->nb_cap, out->idx, out->lambda, w->w_k,
-                       w->w_v, st->k_cache, st->v_cache, pos, st->t_cap, ws, s)))
-    return rc;
-  if ((rc = do_attn_decode(d, out->q, st->k_cache, st->v_cache, st->t_cap, pos + 1, out->o, ws, s)))
-    return rc;
-  if ((pos + 1) % d->block == 0)
-    return do_index(d, st->block_means, st->nb_cap, static_cast<int>((pos + 1) / d->block - 1), 1,
-                    w->proj, st->block_hash, ws, s);
+  MKA_LAUNCH("decode/join", hipEventRecord(aux->join, s2));
+  MKA_LAUNCH("decode/join", hipStreamWaitEvent(s, aux->join, 0));
+  MKA_LAUNCH("decode/attn_merge",
+             attn_decode_merge_bf16(a.q, kc, vc, static_cast<bf16_t*>(out->o), B, d->n_heads,
+                                    d->n_kv_heads, d->head_dim, st->t_cap, pos, pos, w_attn, s));
   return MKA_OK;
 }
 

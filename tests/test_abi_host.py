@@ -102,7 +102,7 @@ def test_workspace_sizes_and_rejection():
     assert idx > 0  # few blocks: the projections are split over d_model
     dd = mka.dims(I.workload("qwen7b_decode_128k"))
     dec = mka.mka_workspace_bytes(dd, mka.MKA_OP_ATTN_DECODE, 131073)
-    chunks = (131073 + 1023) // 1024
+    chunks = (131073 + 2047) // 2048  # 2048-key chunks
     assert dec >= 4 * 28 * chunks * (128 + 2)
     assert mka.mka_workspace_bytes(dd, mka.MKA_OP_DECODE_STEP, 131073) >= dec
     with pytest.raises(mka.MkaError) as e:

@@ -92,11 +92,14 @@ def test_chunked_prefill_equals_whole(name):
     np.testing.assert_allclose(cs["k"], ws["k"], atol=1e-5 if s.dtype == "f32" else 1e-2)
 
 
-def test_decode_continues_prefill_tiny():
-    s = SMALL["tiny_f32"]
+@pytest.mark.parametrize("name,n1", [("tiny_f32", 128), ("small_bf16_dh128", 190),
+                                     ("tiny_bf16", 1)])
+def test_decode_continues_prefill(name, n1):
+    # prefill(n1) then one mka_decode_step per token == prefill of the whole
+    # sequence, across block completions (bf16: the overlapped two-stream step).
+    s = SMALL[name]
     inp = I.prefill_inputs(s)
     ref = oracle_for(s, inp)
-    n1 = 128
     layer = Layer(s, inp, t_cap=s.seq, nb_cap=s.seq // s.block)
     gpu_prefill(s, inp, x=inp["x"][:, :n1], layer=layer)
     xs = to_device(inp["x"], s.dtype)
@@ -108,13 +111,19 @@ def test_decode_continues_prefill_tiny():
     torch.cuda.synchronize()
     o = np.concatenate([r["o"] for r in outs], axis=1)
     check_close("decode o", o, ref["o"][:, n1:], s.dtype)
-    check_close("decode lambda", np.concatenate([r["lambda"] for r in outs], 1), ref["lam"][:, n1:], "f32")
+    check_close("decode lambda", np.concatenate([r["lambda"] for r in outs], 1), ref["lam"][:, n1:],
+                s.dtype)
+    check_close("decode l2", np.concatenate([r["l2"] for r in outs], 1), ref["l2"][:, n1:], "f32")
     idx = np.concatenate([r["idx"] for r in outs], 1)
     check_idx("decode idx", idx, ref["keys"][:, n1:], ref["key_abs"][:, n1:], ref["block_hash"],
               ref["block_abs"], np.arange(n1, s.seq), s.block, s.top_r, s.hash_bits)
     st = state_np(layer)
     check_close("decode k", st["k"], ref["k"], s.dtype)
-    check_codes("decode block_hash", st["bhash"], ref["block_hash"], ref["block_abs"], s.hash_bits)
+    check_close("decode v", st["v"], ref["v"], s.dtype)
+    nb = ref["block_means"].shape[1]
+    check_close("decode block means", st["means"][:, :nb], ref["block_means"], "f32")
+    check_codes("decode block_hash", st["bhash"][:, :nb], ref["block_hash"], ref["block_abs"],
+                s.hash_bits)
 
 
 @pytest.mark.parametrize("name", ["tiny_f32", "tiny_bf16", "small_bf16_dh128"])
