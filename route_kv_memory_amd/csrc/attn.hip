@@ -323,7 +323,7 @@ size_t attn_decode_ws_bytes(int B, int H, int dh, int64_t cache_len) {
 }
 
 template <int DH>
-__global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(
+__global__ __launch_bounds__(256, 1) void attn_decode_split_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
     int H, int G, int64_t t_cap, int64_t cache_len, float sl2, int n_chunks,
     float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ part_o) {
@@ -360,30 +360,43 @@ __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
-  for (int tile = 0; tile < TILES; ++tile) {
+  // Register double buffer: the next tile's K fragments and V rows are in
+  // flight while the current tile is computed.
+  constexpr int VL = VITEMS / 64;  // V load items per lane per tile
+  u32x4 kbuf[2][2 * NKS], vbuf[2][VL * 4];
+  auto issue = [&](int tile, u32x4* kb_, u32x4* vb_) {
+    const int jr = wave * (kDecodeChunk / 4) + tile * BN;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint32_t rowoff = static_cast<uint32_t>((jr + kb * 32 + kperm(l32)) * DH + 8 * hl) * 2;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) kb_[kb * NKS + ks] = buffer_load16(krs, rowoff + 32 * ks);
+    }
+#pragma unroll
+    for (int it = 0; it < VL; ++it) {
+      const int item = lane + 64 * it, kq = item & 15, dc = item >> 4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        vb_[it * 4 + r] = buffer_load16(vrs, static_cast<uint32_t>((jr + 4 * kq + r) * DH + 8 * dc) * 2);
+    }
+  };
+  auto compute = [&](int tile, const u32x4* kb_, const u32x4* vb_) {
     const int jr = wave * (kDecodeChunk / 4) + tile * BN;  // first key of the tile, chunk-relative
     const bool live = jr < rows_here;
-    // V tile -> transposed per-wave LDS region.
     if (live) {
 #pragma unroll
-      for (int it = 0; it < VITEMS / 64; ++it) {
+      for (int it = 0; it < VL; ++it) {
         const int item = lane + 64 * it, kq = item & 15, dc = item >> 4;
-        u32x4 rv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          rv[r] = buffer_load16(vrs, static_cast<uint32_t>((jr + 4 * kq + r) * DH + 8 * dc) * 2);
-        store_vt(Vt, VP, 8 * dc, 4 * kq, rv);
+        store_vt(Vt, VP, 8 * dc, 4 * kq, vb_ + it * 4);
       }
     }
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
-      const uint32_t rowoff = static_cast<uint32_t>((jr + kb * 32 + kperm(l32)) * DH + 8 * hl) * 2;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
-        s[kb] = mfma32x32x16(__builtin_bit_cast(bf16x8, buffer_load16(krs, rowoff + 32 * ks)), qf[ks],
-                             s[kb]);
+        s[kb] = mfma32x32x16(__builtin_bit_cast(bf16x8, kb_[kb * NKS + ks]), qf[ks], s[kb]);
     }
     __syncthreads();  // V tile stores visible to the wave's lanes
     float mx = -INFINITY;
@@ -429,6 +442,14 @@ __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(
       }
     }
     __syncthreads();  // reads done before the next tile overwrites the region
+  };
+  static_assert(TILES % 2 == 0, "tiles are processed in pairs");
+  issue(0, kbuf[0], vbuf[0]);
+  for (int tile = 0; tile < TILES; tile += 2) {
+    issue(tile + 1, kbuf[1], vbuf[1]);
+    compute(tile, kbuf[0], vbuf[0]);
+    if (tile + 2 < TILES) issue(tile + 2, kbuf[0], vbuf[0]);
+    compute(tile + 1, kbuf[1], vbuf[1]);
   }
 
   // Merge the 4 waves.
