@@ -38,6 +38,100 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# Hardware-counter traffic (rocprofv3 FETCH_SIZE / WRITE_SIZE, KiB per dispatch)
+# is taken in two profiled runs of this script and summarised into a JSON file
+# under profiles/; the counters are scaled by what they read for a plain copy
+# kernel of known size.  Each kernel's entry records a hash of the sources it
+# is built from, and a figure is reported only while that hash still matches.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qwen7b_prefill4k_decode128k.json")
+CSRC = os.path.join(ROOT, "route_kv_memory_amd", "csrc")
+KERNEL_SOURCES = {
+    "attn_prefill_bf16_kernel": ["attn.hip"],
+    "attn_decode_split_kernel": ["attn.hip"],
+    "gemm_bf16_kernel<256": ["gemm.hip", "gemm.h"],  # Q projection
+    "gemm_bf16_kernel<128": ["gemm.hip", "gemm.h"],  # fused K/V projection
+}
+ROOFLINE_KERNEL = "attn_prefill_bf16_kernel"
+COPY_KERNEL = "neg_kernel"  # torch.neg(out=): one read and one write per element
+
+
+def source_hash(kernel):
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel] + ["common.h", "kernels.h"]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    from route_kv_memory_amd.build import HIPCC_FLAGS
+
+    h.update(" ".join(HIPCC_FLAGS[:-2]).encode())  # flags, without the include path
+    return h.hexdigest()[:16]
+
+
+def copy_calibration(mib):
+    """A plain copy of ``mib`` MiB (fp32 in, fp32 out), three launches."""
+    import torch
+
+    n = mib * 2**20 // 4
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def traffic_summary(fetch_csv, write_csv, copy_mib, commands):
+    """Per-dispatch HBM bytes of the kernels in KERNEL_SOURCES from two
+    rocprofv3 --pmc runs, each counter scaled by its copy-kernel reading."""
+    import csv
+    import collections
+
+    def per_kernel(path, counter):
+        acc = collections.defaultdict(list)
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return acc
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+
+    def mean_of(acc, sub):
+        vals = [v for k, vs in acc.items() if sub in k for v in vs]
+        if not vals:
+            raise SystemExit(f"no dispatch of {sub} in the counter file; kernels: {sorted(acc)[:8]}")
+        return float(np.mean(vals)), len(vals)
+
+    copy_kib = copy_mib * 1024.0
+    cf, _ = mean_of(fetch, COPY_KERNEL)
+    cw, _ = mean_of(write, COPY_KERNEL)
+    out = {"commands": commands, "copy_kernel": f"torch.neg, {copy_mib} MiB in and out",
+           "copy_fetch_kib": cf, "copy_write_kib": cw,
+           "fetch_scale": copy_kib / cf, "write_scale": copy_kib / cw, "kernels": {}}
+    for k in KERNEL_SOURCES:
+        try:
+            fk, nf = mean_of(fetch, k)
+            wk, nw = mean_of(write, k)
+        except SystemExit:
+            continue
+        byt = (fk * out["fetch_scale"] + wk * out["write_scale"]) * 1024.0
+        out["kernels"][k] = {"fetch_kib": fk, "write_kib": wk, "dispatches": [nf, nw],
+                             "bytes_per_launch": byt, "source_hash": source_hash(k)}
+    return out
+
+
+def traffic_for(kernel):
+    """Calibrated HBM bytes per launch of ``kernel``, or None when no counters
+    were taken for the current source of that kernel."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            entry = json.load(fh)["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    return entry["bytes_per_launch"] if entry["source_hash"] == source_hash(kernel) else None
+
+
 def prefill_flops(s):
     M = s.batch * s.seq
     qw, kvw, D = s.q_width, s.kv_width, s.d_model
@@ -189,12 +283,12 @@ def bench_decode(s, steps, warmup):
                 cached=T0, steps=steps)
 
 
-def cpu_baseline(s, n_tokens):
-    """The oracle, as it stands, on the first n_tokens of sequence 0."""
+def cpu_baseline(s, n_tokens, batch):
+    """The oracle, as it stands, on the first ``n_tokens`` of ``batch`` sequences."""
     from oracle import mka_oracle as O
     from route_kv_memory_amd.inputs import prefill_inputs
 
-    inp = prefill_inputs(s.replace(batch=1), seq=n_tokens)
+    inp = prefill_inputs(s.replace(batch=batch), seq=n_tokens)
     w = [inp[k] for k in ("w_q", "w_k", "w_v", "w_r1", "w_r2", "proj")]
     kw = dict(n_heads=s.n_heads, n_kv_heads=s.n_kv_heads,
               ema_decay=float(np.float32(s.ema_decay)), block=s.block, top_r=s.top_r)
@@ -202,9 +296,12 @@ def cpu_baseline(s, n_tokens):
     O.prefill(inp["x"], *w, **kw)
     dt = time.perf_counter() - t0
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-    return dict(value=n_tokens / dt, unit="tokens/s", cores=cores, kind="oracle",
-                sample=f"whole-layer prefill (every step, attention on every row) of the first "
-                       f"{n_tokens} tokens of sequence 0, fp64 NumPy, {dt:.1f} s")
+    whole = batch == s.batch and n_tokens == s.seq
+    what = ("the whole step" if whole else
+            f"the first {n_tokens} tokens of {batch} of the {s.batch} sequences")
+    return dict(value=batch * n_tokens / dt, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"whole-layer prefill (every stage, attention on every row) over {what} "
+                       f"({batch}x{n_tokens} tokens, same seeded inputs), fp64 NumPy, {dt:.1f} s")
 
 
 def main():
@@ -215,9 +312,26 @@ def main():
     ap.add_argument("--workload", default="qwen7b_prefill_4k")
     ap.add_argument("--decode-workload", default="qwen7b_decode_128k")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run a plain copy of MIB MiB (counter calibration)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic file under profiles/ from two rocprofv3 --pmc "
+                         "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE); no GPU use")
+    ap.add_argument("--summary-command", action="append", default=[],
+                    help="with --traffic-summary: the profiling commands, recorded verbatim")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle tokens per sequence "
+                    "(0: the whole sequence)")
+    ap.add_argument("--cpu-batch", type=int, default=0, help="oracle sequences (0: all)")
     args = ap.parse_args()
+    if args.traffic_summary:
+        res = traffic_summary(*args.traffic_summary, args.copy_calibration or 1024,
+                              args.summary_command)
+        with open(TRAFFIC_FILE, "w") as fh:
+            json.dump(res, fh, indent=1)
+            fh.write("\n")
+        print(json.dumps(res["kernels"], indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the FastMKA layer path here has no multi-GPU "
               "sharding (run with --gpus 1)", file=sys.stderr)
@@ -230,14 +344,17 @@ def main():
 
     mka.lib()
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
     s = I.workload(args.workload)
     pf = bench_prefill(s, args.steps, args.warmup)
     flops = prefill_flops(s)
     tokens = s.batch * s.seq
     ms = pf["wall_ms"]
     stage_ms = pf["stage_ms"]
-    mfma_stages = {k: v for k, v in stage_ms.items() if k in flops}
-    dom = max(mfma_stages, key=mfma_stages.get)
+    # The dominant kernel is causal attention: the "attn" stage is exactly one
+    # launch of it, timed by HIP events on the stream it is launched on.
+    dom = "attn"
     achieved = flops[dom] / (stage_ms[dom] * 1e-3)
     line = {
         "metric": METRIC,
@@ -258,9 +375,9 @@ def main():
         "gpu_ms_per_step": pf["gpu_ms"],
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "prefill_tflops": sum(flops.values()) / (pf["gpu_ms"] * 1e-3) / 1e12,
-        "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved / 1e12,
+        "roofline": {"kernel": ROOFLINE_KERNEL, "bound": "mfma", "achieved": achieved / 1e12,
                      "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_FLOPS, "traffic": None},
+                     "frac": achieved / PEAK_BF16_FLOPS, "traffic": traffic_for(ROOFLINE_KERNEL)},
     }
     if not args.no_decode:
         ds = I.workload(args.decode_workload)
@@ -274,12 +391,13 @@ def main():
             "step_hbm_frac": step_bw / PEAK_HBM_BYTES,
             "roofline": {"kernel": "attn_decode", "bound": "hbm", "achieved": attn_bw / 1e9,
                          "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
-                         "frac": attn_bw / PEAK_HBM_BYTES, "traffic": None,
+                         "frac": attn_bw / PEAK_HBM_BYTES,
+                         "traffic": traffic_for("attn_decode_split_kernel"),
                          "us_per_launch": dc["attn_us"]},
         }
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a bounded sample")
-        line["cpu_baseline"] = cpu_baseline(s, args.cpu_tokens)
+        line["cpu_baseline"] = cpu_baseline(s, args.cpu_tokens or s.seq, args.cpu_batch or s.batch)
     print(json.dumps(line), flush=True)
 
 
