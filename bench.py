@@ -252,6 +252,7 @@ def bench_decode(s, steps, warmup):
     for k in range(steps):
         layer.decode_step(tokens[k], T0 + k, out=out)
         ev[k + 1].record(stream)
+    host_us = (time.perf_counter() - t0) / steps * 1e6  # enqueue cost per step
     torch.cuda.synchronize()
     wall_us = (time.perf_counter() - t0) / steps * 1e6
     step_us = np.array([ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(steps)])
@@ -279,7 +280,7 @@ def bench_decode(s, steps, warmup):
                               + s.router_hidden * s.q_width + 3 * s.router_hidden) * el
                   + s.hash_bits * s.d_model * 4 + s.top_r * s.d_model * 4 + nb0 * 8)
     return dict(median_us=float(np.median(step_us)), mean_us=float(step_us.mean()),
-                wall_us=wall_us, attn_us=attn_us, kv_bytes=kv_bytes, step_bytes=step_bytes,
+                wall_us=wall_us, host_us=host_us, attn_us=attn_us, kv_bytes=kv_bytes, step_bytes=step_bytes,
                 cached=T0, steps=steps)
 
 
@@ -387,7 +388,7 @@ def main():
         line["decode"] = {
             "workload": ds.name, "cached_tokens": dc["cached"], "steps": dc["steps"],
             "us_per_token_median": dc["median_us"], "us_per_token_mean": dc["mean_us"],
-            "us_per_token_wall": dc["wall_us"],
+            "us_per_token_wall": dc["wall_us"], "us_per_token_host_enqueue": dc["host_us"],
             "step_hbm_frac": step_bw / PEAK_HBM_BYTES,
             "roofline": {"kernel": "attn_decode", "bound": "hbm", "achieved": attn_bw / 1e9,
                          "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",

@@ -316,22 +316,28 @@ hipError_t attn_prefill<float>(const float* q, const float* k, const float* v, f
 // workgroups (log-sum-exp weights, fixed order).
 // ---------------------------------------------------------------------------
 constexpr int kMaxDecodeChunks = 4096;
+constexpr int kDecodeTile = 32;  // keys per wave per step of the split kernel
 
 size_t attn_decode_ws_bytes(int B, int H, int dh, int64_t cache_len) {
   const int64_t n_chunks = (cache_len + kDecodeChunk - 1) / kDecodeChunk;
   return sizeof(float) * static_cast<size_t>(B) * H * n_chunks * (dh + 2);
 }
 
-template <int DH>
+// Orders a wave's own LDS accesses (the V region is private to the wave, so
+// no workgroup barrier is needed): LDS operations of one wave complete in
+// issue order; the fence keeps the compiler from moving them across.
+__device__ __forceinline__ void wave_lds_sync() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup"); }
+
+template <int DH, int BN>
 __global__ __launch_bounds__(256, 1) void attn_decode_split_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
     int H, int G, int64_t t_cap, int64_t cache_len, float sl2, int n_chunks,
     float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ part_o) {
-  constexpr int BN = 64, VP = BN + 8, NKS = DH / 16, NDB = DH / 32;
+  constexpr int VP = BN + 8, NKS = DH / 16, NDB = DH / 32, KB = BN / 32, KQ = BN / 4;
   constexpr int TILES = kDecodeChunk / 4 / BN;
-  constexpr int VITEMS = (BN / 4) * (DH / 8);
-  constexpr int LDS_BYTES = 4 * DH * VP * 2;
-  static_assert(LDS_BYTES >= 4 * 32 * (DH + 2) * 4, "merge buffer must fit");
+  constexpr int VITEMS = KQ * (DH / 8);
+  constexpr int VT_BYTES = 4 * DH * VP * 2, RED_BYTES = 4 * 32 * (DH + 2) * 4;
+  constexpr int LDS_BYTES = VT_BYTES > RED_BYTES ? VT_BYTES : RED_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5, l32 = lane & 31;
@@ -363,18 +369,18 @@ __global__ __launch_bounds__(256, 1) void attn_decode_split_kernel(
   // Register double buffer: the next tile's K fragments and V rows are in
   // flight while the current tile is computed.
   constexpr int VL = VITEMS / 64;  // V load items per lane per tile
-  u32x4 kbuf[2][2 * NKS], vbuf[2][VL * 4];
+  u32x4 kbuf[2][KB * NKS], vbuf[2][VL * 4];
   auto issue = [&](int tile, u32x4* kb_, u32x4* vb_) {
     const int jr = wave * (kDecodeChunk / 4) + tile * BN;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
       const uint32_t rowoff = static_cast<uint32_t>((jr + kb * 32 + kperm(l32)) * DH + 8 * hl) * 2;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) kb_[kb * NKS + ks] = buffer_load16(krs, rowoff + 32 * ks);
     }
 #pragma unroll
     for (int it = 0; it < VL; ++it) {
-      const int item = lane + 64 * it, kq = item & 15, dc = item >> 4;
+      const int item = lane + 64 * it, kq = item % KQ, dc = item / KQ;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         vb_[it * 4 + r] = buffer_load16(vrs, static_cast<uint32_t>((jr + 4 * kq + r) * DH + 8 * dc) * 2);
@@ -386,22 +392,22 @@ __global__ __launch_bounds__(256, 1) void attn_decode_split_kernel(
     if (live) {
 #pragma unroll
       for (int it = 0; it < VL; ++it) {
-        const int item = lane + 64 * it, kq = item & 15, dc = item >> 4;
+        const int item = lane + 64 * it, kq = item % KQ, dc = item / KQ;
         store_vt(Vt, VP, 8 * dc, 4 * kq, vb_ + it * 4);
       }
     }
-    f32x16 s[2];
+    f32x16 s[KB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
       s[kb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
         s[kb] = mfma32x32x16(__builtin_bit_cast(bf16x8, kb_[kb * NKS + ks]), qf[ks], s[kb]);
     }
-    __syncthreads();  // V tile stores visible to the wave's lanes
+    wave_lds_sync();  // V tile stores before the wave's reads of them
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         if (jr + kb * 32 + 16 * (r >> 3) + 8 * hl + (r & 7) >= rows_here) s[kb][r] = -INFINITY;
@@ -411,10 +417,10 @@ __global__ __launch_bounds__(256, 1) void attn_decode_split_kernel(
     const float m_new = fmaxf(m_i, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_i - m_use);
-    bf16x8 pf[2][2];
+    bf16x8 pf[KB][2];
     float lsum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         float p[8];
@@ -434,14 +440,14 @@ __global__ __launch_bounds__(256, 1) void attn_decode_split_kernel(
       for (int db = 0; db < NDB; ++db) {
         const bf16_t* vr = &Vt[(db * 32 + l32) * VP + 8 * hl];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int st = 0; st < 2; ++st)
             acc[db] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(vr + kb * 32 + 16 * st),
                                    pf[kb][st], acc[db]);
       }
     }
-    __syncthreads();  // reads done before the next tile overwrites the region
+    wave_lds_sync();  // the reads of this tile before the next tile's stores
   };
   static_assert(TILES % 2 == 0, "tiles are processed in pairs");
   issue(0, kbuf[0], vbuf[0]);
@@ -452,7 +458,8 @@ __global__ __launch_bounds__(256, 1) void attn_decode_split_kernel(
     compute(tile + 1, kbuf[1], vbuf[1]);
   }
 
-  // Merge the 4 waves.
+  // Merge the 4 waves (the V regions are reused for the exchange).
+  __syncthreads();
   l_i += __shfl_xor(l_i, 32, 64);
   float* red_m = reinterpret_cast<float*>(lds);
   float* red_l = red_m + 4 * 32;
@@ -563,10 +570,10 @@ hipError_t attn_decode_split_bf16(const bf16_t* q, const bf16_t* k, const bf16_t
   const float sl2 = 1.4426950408889634f / sqrtf(static_cast<float>(dh));
   const dim3 grid(n_chunks, G, B);
   if (dh == 128)
-    hipLaunchKernelGGL(attn_decode_split_kernel<128>, grid, dim3(256), 0, s, q, k, v, H, G, t_cap,
+    hipLaunchKernelGGL((attn_decode_split_kernel<128, kDecodeTile>), grid, dim3(256), 0, s, q, k, v, H, G, t_cap,
                        n_old, sl2, n_chunks, part_m, part_l, part_o);
   else
-    hipLaunchKernelGGL(attn_decode_split_kernel<64>, grid, dim3(256), 0, s, q, k, v, H, G, t_cap,
+    hipLaunchKernelGGL((attn_decode_split_kernel<64, kDecodeTile>), grid, dim3(256), 0, s, q, k, v, H, G, t_cap,
                        n_old, sl2, n_chunks, part_m, part_l, part_o);
   return hipGetLastError();
 }
