@@ -175,6 +175,8 @@ def bench_prefill(s, steps, warmup):
         ev[2].record(stream)
         mka.mka_l3_index(d, st["block_means"], layer.nb_cap, 0, nb, w["proj"], st["block_hash"],
                          ws, nws, stream)
+        mka.mka_l3_block_kv(d, st["block_means"], layer.nb_cap, 0, nb, w["w_k"], w["w_v"],
+                            st["block_kv"], stream)
         ev[3].record(stream)
         mka.mka_l3_retrieve(d, out["l2"], w["proj"], st["block_hash"], layer.nb_cap, 0, out["key"],
                             out["idx"], ws, nws, stream)
@@ -236,8 +238,7 @@ def bench_decode(s, steps, warmup):
         st["ema_state"].copy_(init["ema_state"])
         st["block_acc"].copy_(init["block_acc"])
         st["block_means"][:, :nb0].copy_(means0)
-        mka.mka_l3_index(d1, st["block_means"], layer.nb_cap, 0, nb0, layer.w["proj"],
-                         st["block_hash"], iws, iws.numel())
+        layer.index_blocks(0, nb0)
 
     out = layer.outputs(1)
     stream = torch.cuda.current_stream()

@@ -127,6 +127,19 @@ int mka_l3_index(const mka_dims* d, const float* block_means, int32_t nb_cap,
                  int32_t first_block, int32_t n_blocks, const float* proj,
                  uint64_t* block_hash, void* ws, size_t ws_bytes, void* stream);
 
+/* Projected block means: block_kv[b, blk, :] = block_means[b, blk, :] [W_k; W_v]^T
+ * (float32; the first G*dh entries are the K projection, the rest the V projection)
+ * for blocks first_block .. first_block+n_blocks-1.  The decode step forms the L3
+ * part of the new K/V row as the mean of the retrieved blocks' rows (reading note,
+ * method section 3: K and V are linear in X_fused, whose L3 term is a mean of
+ * block means).
+ *   block_means [B, nb_cap, D] f32;  w_k, w_v [G*dh, D] dtype
+ *   block_kv    [B, nb_cap, 2*G*dh] f32 (rows written)
+ * Requires first_block + n_blocks <= nb_cap. */
+int mka_l3_block_kv(const mka_dims* d, const float* block_means, int32_t nb_cap,
+                    int32_t first_block, int32_t n_blocks, const void* w_k, const void* w_v,
+                    float* block_kv, void* stream);
+
 /* L3 retrieval for tokens at positions pos0 .. pos0+seq-1.
  * (Reading note, method section 1: recall of R << T past blocks; landing page,
  * Table 8 caption: top-R retrieved chunks per query.)
@@ -181,12 +194,13 @@ int mka_attn_decode(const mka_dims* d, const void* q, const void* k_cache,
                     void* ws, size_t ws_bytes, void* stream);
 
 /* Composite: the whole layer over a prompt at positions pos0 .. pos0+seq-1 (the
- * calls above in order: route, ema_scan, l3_index of the blocks completed here,
- * l3_retrieve, fuse_kv_proj, attn_prefill).  Intermediates go to the caller's
+ * calls above in order: route, ema_scan, l3_index and l3_block_kv of the blocks
+ * completed here, l3_retrieve, fuse_kv_proj, attn_prefill).  Intermediates go to the caller's
  * buffers, so the call both answers the prompt and leaves the decode state.
  *   weights: w_q, w_k, w_v, w_r1, w_r2 (dtype), proj (f32), as above
  *   state: state_io, block_acc_io [B, D] f32; block_means [B, nb_cap, D] f32;
- *          block_hash [B, nb_cap] u64; k_cache, v_cache [B, G, t_cap, dh]
+ *          block_hash [B, nb_cap] u64; block_kv [B, nb_cap, 2*G*dh] f32 (rows of the
+ *          completed blocks written, as mka_l3_block_kv); k_cache, v_cache [B, G, t_cap, dh]
  *   outputs: q [B,seq,H,dh], lambda [B,seq,3], l2 [B,seq,D], key [B,seq],
  *            idx [B,seq,R], o [B,seq,H,dh]
  *   ws >= mka_workspace_bytes(d, MKA_OP_PREFILL, 0) bytes */
@@ -204,6 +218,7 @@ typedef struct mka_state {
   float* block_acc;      /* [B, D] */
   float* block_means;    /* [B, nb_cap, D] */
   uint64_t* block_hash;  /* [B, nb_cap] */
+  float* block_kv;       /* [B, nb_cap, 2*G*dh]: row b = block_means[b] [W_k; W_v]^T */
   void* k_cache;         /* [B, G, t_cap, dh] */
   void* v_cache;         /* [B, G, t_cap, dh] */
   int32_t nb_cap;
@@ -226,15 +241,14 @@ int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weight
 /* Composite: one decode step for the token at position ``pos`` (d->seq must be 1):
  * route, EMA update, retrieval over the blocks before pos's block, fusion and K/V
  * append at row pos, decode attention over rows 0..pos, and -- when pos closes a
- * block ((pos+1) % block == 0) -- the block mean and its code appended to the bank.
- * Same buffers as mka_prefill with seq = 1;
- * ws >= mka_workspace_bytes(d, MKA_OP_DECODE_STEP, pos + 1) bytes.
- * bf16: the attention over rows 0..pos-1 needs only q, so it runs on ``stream`` while
- * the rest of the step runs on an auxiliary stream of the library (one per device,
- * created on the device's first decode step with two events, kept until the process
- * ends); the step's last kernel, on ``stream``, merges both.  Completion is still
- * signalled on ``stream`` alone.  Concurrent calls on one device serialise their
- * enqueueing. */
+ * block ((pos+1) % block == 0) -- the block mean, its code and its projection
+ * (mka_l3_block_kv) appended to the bank.  Same buffers as mka_prefill with
+ * seq = 1; ws >= mka_workspace_bytes(d, MKA_OP_DECODE_STEP, pos + 1) bytes.
+ * bf16 layers form the K/V row by linearity,
+ *   [K|V] = lambda1 (x W) + lambda2 (L2 W) + lambda3 mean_b(block_kv[b]),
+ * equal to (X_fused W) up to float32 rounding (the row is not rounded through
+ * X_fused), so that the products need no lambda and run beside the attention;
+ * float32 layers take the steps in order.  Everything runs on ``stream``. */
 int mka_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_weights* w,
                     const mka_state* st, const mka_outputs* out, void* ws, size_t ws_bytes,
                     void* stream);

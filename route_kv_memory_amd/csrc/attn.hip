@@ -13,7 +13,7 @@
 // probabilities then form, without any data movement, the B operand of
 // O^T = V^T P^T, whose A operand is read from a transposed V tile in LDS.
 // Scores use exp2 with log2(e)/sqrt(dh) folded into one scale.
-#include "kernels.h"
+#include "attn_split.h"
 
 namespace mka {
 
@@ -23,26 +23,6 @@ __device__ __forceinline__ int kperm(int r) {
   return (r & ~15) | qq;
 }
 
-// 8 floats -> bf16x8 (round to nearest even).
-__device__ __forceinline__ bf16x8 to_bf16x8(const float* v) {
-  const u32x4 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                   pack_bf16x2(v[6], v[7])};
-  return __builtin_bit_cast(bf16x8, w);
-}
-
-// Transpose a 4-key x 8-dim bf16 block (4 x 16-byte rows) into 8 rows of 4
-// keys and store them at Vt[(d0 + i) * pitch + k0].
-__device__ __forceinline__ void store_vt(bf16_t* Vt, int pitch, int d0, int k0, const u32x4* rv) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t lo01 = (rv[0][j] & 0xFFFFu) | (rv[1][j] << 16);
-    const uint32_t lo23 = (rv[2][j] & 0xFFFFu) | (rv[3][j] << 16);
-    const uint32_t hi01 = (rv[0][j] >> 16) | (rv[1][j] & 0xFFFF0000u);
-    const uint32_t hi23 = (rv[2][j] >> 16) | (rv[3][j] & 0xFFFF0000u);
-    *reinterpret_cast<u32x2*>(&Vt[(d0 + 2 * j) * pitch + k0]) = u32x2{lo01, lo23};
-    *reinterpret_cast<u32x2*>(&Vt[(d0 + 2 * j + 1) * pitch + k0]) = u32x2{hi01, hi23};
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Prefill, bf16.  Workgroup = 4 waves = 128 query rows of one head; K/V tiles
@@ -116,7 +96,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16_kernel(
     }
     if (tid < VITEMS) {
       const int kq = tid & 15, dc = tid >> 4;
-      store_vt(Vt[buf], VP, 8 * dc, 4 * kq, rv);
+      store_v_transposed(Vt[buf], VP, 8 * dc, 4 * kq, rv);
     }
   };
 
@@ -183,7 +163,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16_kernel(
           p[j] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * st + j], sl2, -ms));
           l_i += p[j];
         }
-        pf[kb][st] = to_bf16x8(p);
+        pf[kb][st] = pack_bf16x8(p);
       }
 
 #pragma unroll
@@ -307,292 +287,87 @@ hipError_t attn_prefill<float>(const float* q, const float* k, const float* v, f
 }
 
 // ---------------------------------------------------------------------------
-// Decode, bf16: one query token per sequence.  A workgroup takes 1024 keys of
-// one (batch, KV group); each wave 256 of them as 4 tiles of 64 with all H/G
-// query heads of the group in its 32 MFMA columns.  K fragments come straight
-// from global (16 contiguous bytes per lane), V tiles are transposed through a
-// per-wave LDS region.  The 4 waves merge in LDS into one partial (max, sum,
-// unnormalised output) per head; a second kernel merges the partials of all
-// workgroups (log-sum-exp weights, fixed order).
+// Decode, bf16: the split kernel (one chunk of keys per workgroup, see
+// attn_split.h) and the merge of its partials with the last cache row.
 // ---------------------------------------------------------------------------
-constexpr int kMaxDecodeChunks = 4096;
-constexpr int kDecodeTile = 32;  // keys per wave per step of the split kernel
+static int decode_units(int B, int H, int G) { return B * G * ((H / G + kSplitHeads - 1) / kSplitHeads); }
 
-size_t attn_decode_ws_bytes(int B, int H, int dh, int64_t cache_len) {
-  const int64_t n_chunks = (cache_len + kDecodeChunk - 1) / kDecodeChunk;
+size_t attn_decode_ws_bytes(int B, int H, int G, int dh, int64_t n_rows) {
+  const int64_t n_chunks = n_rows > 0 ? decode_n_chunks(decode_units(B, H, G), n_rows) : 0;
   return sizeof(float) * static_cast<size_t>(B) * H * n_chunks * (dh + 2);
 }
 
-// Orders a wave's own LDS accesses (the V region is private to the wave, so
-// no workgroup barrier is needed): LDS operations of one wave complete in
-// issue order; the fence keeps the compiler from moving them across.
-__device__ __forceinline__ void wave_lds_sync() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup"); }
-
-template <int DH, int BN>
-__global__ __launch_bounds__(256, 1) void attn_decode_split_kernel(
+template <int DH>
+__global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
-    int H, int G, int64_t t_cap, int64_t cache_len, float sl2, int n_chunks,
+    int H, int G, int64_t t_cap, int64_t n_rows, float sl2, int chunk, int n_chunks, int n_hb,
     float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ part_o) {
-  constexpr int VP = BN + 8, NKS = DH / 16, NDB = DH / 32, KB = BN / 32, KQ = BN / 4;
-  constexpr int TILES = kDecodeChunk / 4 / BN;
-  constexpr int VITEMS = KQ * (DH / 8);
-  constexpr int VT_BYTES = 4 * DH * VP * 2, RED_BYTES = 4 * 32 * (DH + 2) * 4;
-  constexpr int LDS_BYTES = VT_BYTES > RED_BYTES ? VT_BYTES : RED_BYTES;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5, l32 = lane & 31;
-  const int hpg = H / G;
-  bf16_t* Vt = reinterpret_cast<bf16_t*>(lds) + wave * DH * VP;
-
-  bf16x8 qf[NKS];
-  {
-    const bf16_t* qp = Q + (static_cast<int64_t>(b) * H + g * hpg + min(l32, hpg - 1)) * DH + 8 * hl;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
-      if (l32 >= hpg) qf[ks] = bf16x8{};
-    }
-  }
-  const bf16_t* kbase = Kc + (static_cast<int64_t>(b) * G + g) * t_cap * DH;
-  const bf16_t* vbase = Vc + (static_cast<int64_t>(b) * G + g) * t_cap * DH;
-  // Rows of this workgroup's chunk, as a byte range: rows past cache_len read as zeros.
-  const int64_t c0 = static_cast<int64_t>(c) * kDecodeChunk;
-  const int rows_here = static_cast<int>(min<int64_t>(kDecodeChunk, cache_len - c0));
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase + c0 * DH, static_cast<uint32_t>(rows_here) * DH * 2);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase + c0 * DH, static_cast<uint32_t>(rows_here) * DH * 2);
-
-  float m_i = -INFINITY, l_i = 0.f;
-  f32x16 acc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
-
-  // Register double buffer: the next tile's K fragments and V rows are in
-  // flight while the current tile is computed.
-  constexpr int VL = VITEMS / 64;  // V load items per lane per tile
-  u32x4 kbuf[2][KB * NKS], vbuf[2][VL * 4];
-  auto issue = [&](int tile, u32x4* kb_, u32x4* vb_) {
-    const int jr = wave * (kDecodeChunk / 4) + tile * BN;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const uint32_t rowoff = static_cast<uint32_t>((jr + kb * 32 + kperm(l32)) * DH + 8 * hl) * 2;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) kb_[kb * NKS + ks] = buffer_load16(krs, rowoff + 32 * ks);
-    }
-#pragma unroll
-    for (int it = 0; it < VL; ++it) {
-      const int item = lane + 64 * it, kq = item % KQ, dc = item / KQ;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vb_[it * 4 + r] = buffer_load16(vrs, static_cast<uint32_t>((jr + 4 * kq + r) * DH + 8 * dc) * 2);
-    }
-  };
-  auto compute = [&](int tile, const u32x4* kb_, const u32x4* vb_) {
-    const int jr = wave * (kDecodeChunk / 4) + tile * BN;  // first key of the tile, chunk-relative
-    const bool live = jr < rows_here;
-    if (live) {
-#pragma unroll
-      for (int it = 0; it < VL; ++it) {
-        const int item = lane + 64 * it, kq = item % KQ, dc = item / KQ;
-        store_vt(Vt, VP, 8 * dc, 4 * kq, vb_ + it * 4);
-      }
-    }
-    f32x16 s[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      s[kb] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        s[kb] = mfma32x32x16(__builtin_bit_cast(bf16x8, kb_[kb * NKS + ks]), qf[ks], s[kb]);
-    }
-    wave_lds_sync();  // V tile stores before the wave's reads of them
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (jr + kb * 32 + 16 * (r >> 3) + 8 * hl + (r & 7) >= rows_here) s[kb][r] = -INFINITY;
-        mx = fmaxf(mx, s[kb][r]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
-    const float m_new = fmaxf(m_i, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_i - m_use);
-    bf16x8 pf[KB][2];
-    float lsum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        float p[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          p[j] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * st + j], sl2, -m_use));
-          lsum += p[j];
-        }
-        pf[kb][st] = to_bf16x8(p);
-      }
-    l_i = l_i * alpha + lsum;
-    m_i = m_new;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
-    if (live) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const bf16_t* vr = &Vt[(db * 32 + l32) * VP + 8 * hl];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int st = 0; st < 2; ++st)
-            acc[db] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(vr + kb * 32 + 16 * st),
-                                   pf[kb][st], acc[db]);
-      }
-    }
-    wave_lds_sync();  // the reads of this tile before the next tile's stores
-  };
-  static_assert(TILES % 2 == 0, "tiles are processed in pairs");
-  issue(0, kbuf[0], vbuf[0]);
-  for (int tile = 0; tile < TILES; tile += 2) {
-    issue(tile + 1, kbuf[1], vbuf[1]);
-    compute(tile, kbuf[0], vbuf[0]);
-    if (tile + 2 < TILES) issue(tile + 2, kbuf[0], vbuf[0]);
-    compute(tile + 1, kbuf[1], vbuf[1]);
-  }
-
-  // Merge the 4 waves (the V regions are reused for the exchange).
-  __syncthreads();
-  l_i += __shfl_xor(l_i, 32, 64);
-  float* red_m = reinterpret_cast<float*>(lds);
-  float* red_l = red_m + 4 * 32;
-  float* red_o = red_l + 4 * 32;  // [4][32][DH]
-  if (hl == 0) {
-    red_m[wave * 32 + l32] = m_i;
-    red_l[wave * 32 + l32] = l_i;
-  }
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      red_o[(wave * 32 + l32) * DH + db * 32 + acc_row(r, hl)] = acc[db][r];
-  __syncthreads();
-  for (int e = tid; e < hpg * DH; e += 256) {
-    const int n = e / DH, d = e % DH;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w * 32 + n]);
-    float L = 0.f, acc_o = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float wt = red_m[w * 32 + n] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(red_m[w * 32 + n] - M);
-      L += wt * red_l[w * 32 + n];
-      acc_o += wt * red_o[(w * 32 + n) * DH + d];
-    }
-    const int64_t p = (static_cast<int64_t>(b) * H + g * hpg + n) * n_chunks + c;
-    part_o[p * DH + d] = acc_o;
-    if (d == 0) {
-      part_m[p] = M;
-      part_l[p] = L;
-    }
-  }
+  __shared__ __attribute__((aligned(16))) unsigned char lds[split_lds_bytes<DH>()];
+  const int g = blockIdx.y / n_hb, hb = blockIdx.y % n_hb;
+  decode_split_chunk<DH>(Q, Kc, Vc, H, G, t_cap, n_rows, sl2, chunk, n_chunks, blockIdx.x, g, hb,
+                         blockIdx.z, part_m, part_l, part_o, lds);
 }
 
+// The extra row comes from the cache (row ``extra_row``; none if negative).
 template <int DH>
-__global__ __launch_bounds__(512) void attn_decode_merge_kernel(
+__global__ __launch_bounds__(kMergeThreads) void attn_decode_merge_kernel(
     const float* __restrict__ part_m, const float* __restrict__ part_l,
     const float* __restrict__ part_o, int H, int G, int n_chunks, const bf16_t* __restrict__ Q,
     const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc, int64_t t_cap,
     int64_t extra_row, float sl2, bf16_t* __restrict__ O) {
-  constexpr int NT = 512, GR = NT / DH;
-  __shared__ float wts[kMaxDecodeChunks];
-  __shared__ float red[NT];
-  __shared__ float osum[GR][DH];
-  __shared__ float sx_s;
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
-  const int g = h / (H / G);
-  const int64_t p0 = (static_cast<int64_t>(b) * H + h) * n_chunks;
-  const bf16_t* krow = Kc + ((static_cast<int64_t>(b) * G + g) * t_cap + extra_row) * DH;
-  const bf16_t* vrow = Vc + ((static_cast<int64_t>(b) * G + g) * t_cap + extra_row) * DH;
-  // Score of the extra row (the token's own fused K/V), scaled like the parts.
-  if (extra_row >= 0 && tid < 64) {
-    const bf16_t* qh = Q + (static_cast<int64_t>(b) * H + h) * DH;
-    float dot = 0.f;
-    for (int d = lane; d < DH; d += 64) dot = fmaf(bf16_to_f32(qh[d]), bf16_to_f32(krow[d]), dot);
-    dot = wave_sum(dot);
-    if (lane == 0) sx_s = dot * sl2;
-  }
-  float mx = -INFINITY;
-  for (int c = tid; c < n_chunks; c += NT) mx = fmaxf(mx, part_m[p0 + c]);
-  mx = wave_max(mx);
-  if (lane == 0) red[tid >> 6] = mx;
-  __syncthreads();
-  const float sx = extra_row >= 0 ? sx_s : -INFINITY;
-  float M = sx;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) M = fmaxf(M, red[w]);
-  __syncthreads();
-  float ls = 0.f;
-  for (int c = tid; c < n_chunks; c += NT) {
-    const float w = __builtin_amdgcn_exp2f(part_m[p0 + c] - M);
-    wts[c] = w;
-    ls += w * part_l[p0 + c];
-  }
-  ls = wave_sum(ls);
-  if (lane == 0) red[tid >> 6] = ls;
-  __syncthreads();
-  const float wx = extra_row >= 0 ? __builtin_amdgcn_exp2f(sx - M) : 0.f;
-  float L = wx;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) L += red[w];
-  const int d = tid % DH, grp = tid / DH;
-  float o = 0.f;
-#pragma unroll 8
-  for (int c = grp; c < n_chunks; c += GR) o += wts[c] * part_o[(p0 + c) * DH + d];
-  osum[grp][d] = o;
-  __syncthreads();
-  if (tid < DH) {
-    float tot = extra_row >= 0 ? wx * bf16_to_f32(vrow[tid]) : 0.f;
-#pragma unroll
-    for (int gi = 0; gi < GR; ++gi) tot += osum[gi][tid];
-    O[(static_cast<int64_t>(b) * H + h) * DH + tid] = f32_to_bf16(tot / L);
-  }
+  __shared__ MergeLds<DH> sm;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int64_t row = ((static_cast<int64_t>(b) * G + h / (H / G)) * t_cap + extra_row) * DH;
+  decode_merge_head<DH>(part_m, part_l, part_o, H, n_chunks, h, b, Q, sl2, O, sm,
+                        [&](float* kx, float* vx) {
+                          if (extra_row < 0) return false;
+                          const int tid = threadIdx.x;
+                          if (tid < DH) {
+                            kx[tid] = bf16_to_f32(Kc[row + tid]);
+                            vx[tid] = bf16_to_f32(Vc[row + tid]);
+                          }
+                          return true;
+                        });
 }
 
-static int decode_chunks(int64_t n) { return static_cast<int>((n + kDecodeChunk - 1) / kDecodeChunk); }
 
 hipError_t attn_decode_split_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* v, int B, int H,
                                   int G, int dh, int64_t t_cap, int64_t n_old, void* ws,
                                   hipStream_t s) {
-  const int n_chunks = decode_chunks(n_old);
-  if (n_chunks == 0) return hipSuccess;
+  if (n_old <= 0) return hipSuccess;
+  const int chunk = decode_chunk_keys(decode_units(B, H, G), n_old);
+  const int n_chunks = decode_n_chunks(decode_units(B, H, G), n_old);
   if (n_chunks > kMaxDecodeChunks) return hipErrorInvalidValue;
   float* part_m = static_cast<float*>(ws);
   float* part_l = part_m + static_cast<size_t>(B) * H * n_chunks;
   float* part_o = part_l + static_cast<size_t>(B) * H * n_chunks;
   const float sl2 = 1.4426950408889634f / sqrtf(static_cast<float>(dh));
-  const dim3 grid(n_chunks, G, B);
+  const int n_hb = (H / G + kSplitHeads - 1) / kSplitHeads;
+  const dim3 grid(n_chunks, G * n_hb, B);
   if (dh == 128)
-    hipLaunchKernelGGL((attn_decode_split_kernel<128, kDecodeTile>), grid, dim3(256), 0, s, q, k, v, H, G, t_cap,
-                       n_old, sl2, n_chunks, part_m, part_l, part_o);
+    hipLaunchKernelGGL(attn_decode_split_kernel<128>, grid, dim3(256), 0, s, q, k, v, H, G, t_cap,
+                       n_old, sl2, chunk, n_chunks, n_hb, part_m, part_l, part_o);
   else
-    hipLaunchKernelGGL((attn_decode_split_kernel<64, kDecodeTile>), grid, dim3(256), 0, s, q, k, v, H, G, t_cap,
-                       n_old, sl2, n_chunks, part_m, part_l, part_o);
+    hipLaunchKernelGGL(attn_decode_split_kernel<64>, grid, dim3(256), 0, s, q, k, v, H, G, t_cap,
+                       n_old, sl2, chunk, n_chunks, n_hb, part_m, part_l, part_o);
   return hipGetLastError();
 }
 
 hipError_t attn_decode_merge_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* v, bf16_t* o,
                                   int B, int H, int G, int dh, int64_t t_cap, int64_t n_old,
                                   int64_t extra_row, void* ws, hipStream_t s) {
-  const int n_chunks = decode_chunks(n_old);
+  const int n_chunks = n_old > 0 ? decode_n_chunks(decode_units(B, H, G), n_old) : 0;
   if (n_chunks > kMaxDecodeChunks) return hipErrorInvalidValue;
   float* part_m = static_cast<float*>(ws);
   float* part_l = part_m + static_cast<size_t>(B) * H * n_chunks;
   float* part_o = part_l + static_cast<size_t>(B) * H * n_chunks;
   const float sl2 = 1.4426950408889634f / sqrtf(static_cast<float>(dh));
   if (dh == 128)
-    hipLaunchKernelGGL(attn_decode_merge_kernel<128>, dim3(H, B), dim3(512), 0, s, part_m, part_l,
-                       part_o, H, G, n_chunks, q, k, v, t_cap, extra_row, sl2, o);
+    hipLaunchKernelGGL(attn_decode_merge_kernel<128>, dim3(H, B), dim3(kMergeThreads), 0, s, part_m,
+                       part_l, part_o, H, G, n_chunks, q, k, v, t_cap, extra_row, sl2, o);
   else
-    hipLaunchKernelGGL(attn_decode_merge_kernel<64>, dim3(H, B), dim3(512), 0, s, part_m, part_l,
-                       part_o, H, G, n_chunks, q, k, v, t_cap, extra_row, sl2, o);
+    hipLaunchKernelGGL(attn_decode_merge_kernel<64>, dim3(H, B), dim3(kMergeThreads), 0, s, part_m,
+                       part_l, part_o, H, G, n_chunks, q, k, v, t_cap, extra_row, sl2, o);
   return hipGetLastError();
 }
 

@@ -1,0 +1,319 @@
+// Split-K decode attention over one chunk of the fused KV cache (landing page,
+// Table 5: decode streams the single fused K/V tensor; reading note, method
+// section 4: online max-shift).  Shared by the standalone decode attention and
+// the fused decode-step kernel.
+//
+// A workgroup takes one chunk of keys of one (batch, KV group) for a block of
+// up to 16 query heads of that group; its 4 waves take the chunk's 32-key
+// tiles in turn (tile t to wave t % 4), each with its next tile's K and V
+// loads in flight while the current one is computed.  Chunks are sized so that
+// a launch has about one workgroup per CU (decode_chunk_keys): a CU streams
+// one chunk at the rate its memory pipeline allows, so a second chunk on any
+// CU would double the launch time.  Scores are S^T = K Q^T on MFMA 16x16x32 (keys
+// as rows, the heads as the 16 columns).  The K rows of a tile are fed in the
+// order key(kb, i) = 8*(i/4) + 4*kb + i%4 for MFMA row i of sub-block kb, which
+// leaves lane l holding keys 8*(l/16) .. 8*(l/16)+7 of head l%16: exactly the
+// B operand of O^T = V^T P^T, so the probabilities go to the second product
+// without data movement.  V is transposed through a per-wave LDS region.
+// The 4 waves merge in LDS into one partial (max, sum, unnormalised output)
+// per head; the partials of all chunks are merged by a second kernel.
+#pragma once
+
+#include "kernels.h"
+
+namespace mka {
+
+constexpr int kSplitTile = 32;  // keys per wave per step
+constexpr int kSplitHeads = 16; // query heads per workgroup (MFMA columns)
+constexpr int kDecodeTargetWgs = 256;  // one workgroup per CU of the MI355X
+constexpr int kMinDecodeChunk = 256;
+
+// Keys per chunk for n_rows cache rows split over ``units`` = B * G * (head
+// blocks) independent streams: about kDecodeTargetWgs chunks in all, a
+// multiple of the tile, at least kMinDecodeChunk.  Host and device.
+__host__ __device__ inline int decode_chunk_keys(int units, int64_t n_rows) {
+  const int per_unit = units >= kDecodeTargetWgs ? 1 : kDecodeTargetWgs / units;
+  int64_t c = (n_rows + per_unit - 1) / per_unit;
+  c = (c + kSplitTile - 1) / kSplitTile * kSplitTile;
+  return static_cast<int>(c < kMinDecodeChunk ? kMinDecodeChunk : c);
+}
+__host__ __device__ inline int decode_n_chunks(int units, int64_t n_rows) {
+  const int c = decode_chunk_keys(units, n_rows);
+  return static_cast<int>((n_rows + c - 1) / c);
+}
+
+template <int DH>
+constexpr int split_lds_bytes() {
+  // per-wave transposed V tiles; the 4-wave merge reuses the region
+  return 4 * DH * (kSplitTile + 8) * 2;
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 8 floats -> bf16x8 (round to nearest even).
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* v) {
+  const u32x4 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                   pack_bf16x2(v[6], v[7])};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// Transpose a 4-key x 8-dim bf16 block (4 x 16-byte rows) into 8 rows of 4
+// keys and store them at Vt[(d0 + i) * pitch + k0].
+__device__ __forceinline__ void store_v_transposed(bf16_t* Vt, int pitch, int d0, int k0,
+                                                   const u32x4* rv) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo01 = (rv[0][j] & 0xFFFFu) | (rv[1][j] << 16);
+    const uint32_t lo23 = (rv[2][j] & 0xFFFFu) | (rv[3][j] << 16);
+    const uint32_t hi01 = (rv[0][j] >> 16) | (rv[1][j] & 0xFFFF0000u);
+    const uint32_t hi23 = (rv[2][j] >> 16) | (rv[3][j] & 0xFFFF0000u);
+    *reinterpret_cast<u32x2*>(&Vt[(d0 + 2 * j) * pitch + k0]) = u32x2{lo01, lo23};
+    *reinterpret_cast<u32x2*>(&Vt[(d0 + 2 * j + 1) * pitch + k0]) = u32x2{hi01, hi23};
+  }
+}
+
+// Orders a wave's own LDS accesses: LDS operations of one wave complete in
+// issue order and the fence keeps the compiler from moving them across.  The
+// V regions are private to their wave, so no workgroup barrier is needed.
+__device__ __forceinline__ void wave_lds_sync() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup"); }
+
+// Partials of chunk c (``chunk`` keys) for heads hb*16 .. of KV group g,
+// sequence b, over cache rows [c*chunk, min((c+1)*chunk, n_rows)).  Partial p
+// of query head h lives at (b*H + h) * n_chunks + c of part_m / part_l and
+// p*DH of part_o.  Uses 256 threads and split_lds_bytes<DH>() bytes of ``lds``.
+template <int DH>
+__device__ __forceinline__ void decode_split_chunk(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
+    int H, int G, int64_t t_cap, int64_t n_rows, float sl2, int chunk, int n_chunks, int c, int g,
+    int hb, int b, float* __restrict__ part_m, float* __restrict__ part_l,
+    float* __restrict__ part_o, unsigned char* lds) {
+  constexpr int BN = kSplitTile, VP = BN + 8, NKS = DH / 32, NDB = DH / 16, KQ = BN / 4;
+  constexpr int VL = KQ * (DH / 8) / 64;  // V load items per lane per tile
+  static_assert(4 * kSplitHeads * (DH + 2) * 4 <= split_lds_bytes<DH>(), "merge buffer must fit");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
+  const int hpg = H / G, h_lo = hb * kSplitHeads;
+  const int nh = min(kSplitHeads, hpg - h_lo);
+  bf16_t* Vt = reinterpret_cast<bf16_t*>(lds) + wave * DH * VP;
+
+  // Q^T fragments: lane holds q[head l16][32*ks + 8*q4 .. +7].
+  bf16x8 qf[NKS];
+  {
+    const bf16_t* qp =
+        Q + (static_cast<int64_t>(b) * H + g * hpg + h_lo + min(l16, nh - 1)) * DH + 8 * q4;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks);
+      if (l16 >= nh) qf[ks] = bf16x8{};
+    }
+  }
+  const int64_t c0 = static_cast<int64_t>(c) * chunk;
+  const int rows_here = static_cast<int>(min<int64_t>(chunk, n_rows - c0));
+  const int n_tiles = (rows_here + BN - 1) / BN;
+  const int my_tiles = (n_tiles - wave + 3) / 4;  // tiles wave, wave + 4, ...
+  const int64_t head0 = (static_cast<int64_t>(b) * G + g) * t_cap + c0;
+  // Rows past the chunk's end read as zeros (buffer range check).
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kc + head0 * DH, static_cast<uint32_t>(rows_here) * DH * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vc + head0 * DH, static_cast<uint32_t>(rows_here) * DH * 2);
+
+  float m_i = -INFINITY, l_i = 0.f;
+  f32x4 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x4{};
+
+  const int krow = 8 * (l16 >> 2) + (l16 & 3);  // key of MFMA row l16 in sub-block 0
+  u32x4 kbuf[2][2 * NKS], vbuf[2][VL * 4];
+  auto issue = [&](int tile, u32x4* kb_, u32x4* vb_) {
+    const int jr = (wave + 4 * tile) * BN;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint32_t off = static_cast<uint32_t>((jr + krow + 4 * kb) * DH + 8 * q4) * 2;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) kb_[kb * NKS + ks] = buffer_load16(krs, off + 64 * ks);
+    }
+#pragma unroll
+    for (int it = 0; it < VL; ++it) {
+      const int item = lane + 64 * it, kq = item % KQ, dc = item / KQ;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        vb_[it * 4 + r] = buffer_load16(vrs, static_cast<uint32_t>((jr + 4 * kq + r) * DH + 8 * dc) * 2);
+    }
+  };
+  auto compute = [&](int tile, const u32x4* kb_, const u32x4* vb_) {
+    const int jr = (wave + 4 * tile) * BN;  // first key of the tile, chunk-relative
+    const bool live = jr < rows_here;
+    if (live) {
+#pragma unroll
+      for (int it = 0; it < VL; ++it) {
+        const int item = lane + 64 * it, kq = item % KQ, dc = item / KQ;
+        store_v_transposed(Vt, VP, 8 * dc, 4 * kq, vb_ + it * 4);
+      }
+    }
+    f32x4 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x4{};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        s[kb] = mfma16x16x32(__builtin_bit_cast(bf16x8, kb_[kb * NKS + ks]), qf[ks], s[kb]);
+    }
+    wave_lds_sync();  // V tile stores before the wave's reads of them
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (jr + 8 * q4 + 4 * kb + r >= rows_here) s[kb][r] = -INFINITY;
+        mx = fmaxf(mx, s[kb][r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+    const float m_new = fmaxf(m_i, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_i - m_use);
+    float p[8], lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[4 * kb + r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], sl2, -m_use));
+        lsum += p[4 * kb + r];
+      }
+    const bf16x8 pf = pack_bf16x8(p);
+    l_i = l_i * alpha + lsum;
+    m_i = m_new;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+    if (live) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        acc[db] = mfma16x16x32(*reinterpret_cast<const bf16x8*>(&Vt[(16 * db + l16) * VP + 8 * q4]),
+                               pf, acc[db]);
+    }
+    wave_lds_sync();  // the reads of this tile before the next tile's stores
+  };
+  if (my_tiles > 0) issue(0, kbuf[0], vbuf[0]);
+  for (int tile = 0; tile < my_tiles; tile += 2) {
+    if (tile + 1 < my_tiles) issue(tile + 1, kbuf[1], vbuf[1]);
+    compute(tile, kbuf[0], vbuf[0]);
+    if (tile + 2 < my_tiles) issue(tile + 2, kbuf[0], vbuf[0]);
+    if (tile + 1 < my_tiles) compute(tile + 1, kbuf[1], vbuf[1]);
+  }
+
+  // Merge the 4 waves (the V regions are reused for the exchange).
+  __syncthreads();
+  l_i += __shfl_xor(l_i, 16, 64);
+  l_i += __shfl_xor(l_i, 32, 64);
+  float* red_m = reinterpret_cast<float*>(lds);
+  float* red_l = red_m + 4 * kSplitHeads;
+  float* red_o = red_l + 4 * kSplitHeads;  // [4][16][DH]
+  if (q4 == 0) {
+    red_m[wave * kSplitHeads + l16] = m_i;
+    red_l[wave * kSplitHeads + l16] = l_i;
+  }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red_o[(wave * kSplitHeads + l16) * DH + 16 * db + 4 * q4 + r] = acc[db][r];
+  __syncthreads();
+  for (int e = tid; e < nh * DH; e += 256) {
+    const int n = e / DH, d = e % DH;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w * kSplitHeads + n]);
+    float L = 0.f, acc_o = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = red_m[w * kSplitHeads + n];
+      const float wt = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      L += wt * red_l[w * kSplitHeads + n];
+      acc_o += wt * red_o[(w * kSplitHeads + n) * DH + d];
+    }
+    const int64_t p = (static_cast<int64_t>(b) * H + g * hpg + h_lo + n) * n_chunks + c;
+    part_o[p * DH + d] = acc_o;
+    if (d == 0) {
+      part_m[p] = M;
+      part_l[p] = L;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge for query head h of sequence b (512 threads): the chunk partials and
+// one extra key/value row, combined with log-sum-exp weights in a fixed order.
+// ``extra(kx, vx)`` is called by every thread; it fills kx[0..DH) and
+// vx[0..DH) (LDS, float) and returns whether the extra row exists.  It may use
+// __syncthreads.  Output o[b, h, :] = sum / denominator, rounded to bf16.
+// ---------------------------------------------------------------------------
+constexpr int kMaxDecodeChunks = 4096;
+constexpr int kMergeThreads = 512;
+
+template <int DH>
+struct MergeLds {
+  float wts[kMaxDecodeChunks];
+  float red[kMergeThreads / 64];
+  float osum[kMergeThreads / DH][DH];
+  float kx[DH], vx[DH];
+  float lam[4];
+  float sx;
+};
+
+template <int DH, typename Extra>
+__device__ __forceinline__ void decode_merge_head(const float* __restrict__ part_m,
+                                                  const float* __restrict__ part_l,
+                                                  const float* __restrict__ part_o, int H,
+                                                  int n_chunks, int h, int b,
+                                                  const bf16_t* __restrict__ Q, float sl2,
+                                                  bf16_t* __restrict__ O, MergeLds<DH>& sm,
+                                                  Extra extra) {
+  constexpr int NT = kMergeThreads, GR = NT / DH;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t p0 = (static_cast<int64_t>(b) * H + h) * n_chunks;
+  const bool has_extra = extra(sm.kx, sm.vx);
+  __syncthreads();
+  if (has_extra && tid < 64) {  // score of the extra row, scaled like the partials
+    const bf16_t* qh = Q + (static_cast<int64_t>(b) * H + h) * DH;
+    float dot = 0.f;
+    for (int d = lane; d < DH; d += 64) dot = fmaf(bf16_to_f32(qh[d]), sm.kx[d], dot);
+    dot = wave_sum(dot);
+    if (lane == 0) sm.sx = dot * sl2;
+  }
+  float mx = -INFINITY;
+  for (int c = tid; c < n_chunks; c += NT) mx = fmaxf(mx, part_m[p0 + c]);
+  mx = wave_max(mx);
+  if (lane == 0) sm.red[tid >> 6] = mx;
+  __syncthreads();
+  const float sx = has_extra ? sm.sx : -INFINITY;
+  float M = sx;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) M = fmaxf(M, sm.red[w]);
+  __syncthreads();
+  float ls = 0.f;
+  for (int c = tid; c < n_chunks; c += NT) {
+    const float w = __builtin_amdgcn_exp2f(part_m[p0 + c] - M);
+    sm.wts[c] = w;
+    ls += w * part_l[p0 + c];
+  }
+  ls = wave_sum(ls);
+  if (lane == 0) sm.red[tid >> 6] = ls;
+  __syncthreads();
+  const float wx = has_extra ? __builtin_amdgcn_exp2f(sx - M) : 0.f;
+  float L = wx;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) L += sm.red[w];
+  const int d = tid % DH, grp = tid / DH;
+  float o = 0.f;
+#pragma unroll 8
+  for (int c = grp; c < n_chunks; c += GR) o += sm.wts[c] * part_o[(p0 + c) * DH + d];
+  sm.osum[grp][d] = o;
+  __syncthreads();
+  if (tid < DH) {
+    float tot = has_extra ? wx * sm.vx[tid] : 0.f;
+#pragma unroll
+    for (int gi = 0; gi < GR; ++gi) tot += sm.osum[gi][tid];
+    O[(static_cast<int64_t>(b) * H + h) * DH + tid] = f32_to_bf16(tot / L);
+  }
+}
+
+}  // namespace mka

@@ -7,6 +7,7 @@ namespace mka {
 
 constexpr int kDecSlice = 128;   // channels per EMA/key-projection workgroup
 constexpr int kFewRowsDec = 8;   // tokens per decode step (batch) at most
+constexpr int kGemvCols = 4;     // output columns per wave in the decode products
 
 template <typename T>
 struct DecodeArgs {
@@ -38,13 +39,40 @@ struct DecodeArgs {
   uint64_t* key;          // [B]
   int32_t* idx;           // [B, R]
   int R;
-  // fusion
+  // fusion (sequential path): X_fused
   T* xf;           // [B, D]
+  // fused K/V row by linearity (overlapped path): the projections of x, L2 and
+  // L3 through [W_k; W_v], each [B, 2*kvw] (K columns, then V columns)
+  const T* w_k;    // [kvw, D]
+  const T* w_v;    // [kvw, D]
+  int kvw;
+  float* kvx;
+  float* kvl2;
+  float* kvl3;
+  const float* block_kv;  // [B, nb_cap, 2*kvw] projected block means
+  // cache and attention
+  T* k_cache;      // [B, G, t_cap, dh]
+  T* v_cache;
+  int H, G, dh;
+  int64_t t_cap;
+  float sl2;       // log2(e) / sqrt(dh)
+  float* part_m;   // split partials over rows [0, pos)
+  float* part_l;
+  float* part_o;
+  int chunk, n_chunks, n_hb;  // keys per split chunk, chunks, 16-head blocks per group
+  T* o;            // [B, H, dh] attention output
 };
 
+// Sequential path (float32 layers): front, mid, fuse, then the K/V product and
+// attention.
 template <typename T> hipError_t decode_front(const DecodeArgs<T>& a, hipStream_t s);
 template <typename T> hipError_t decode_mid(const DecodeArgs<T>& a, hipStream_t s);
 template <typename T> hipError_t decode_fuse(const DecodeArgs<T>& a, hipStream_t s);
+
+// Overlapped path (bf16 layers): three launches per step.
+hipError_t decode_inputs_bf16(const DecodeArgs<bf16_t>& a, hipStream_t s);
+hipError_t decode_attend_bf16(const DecodeArgs<bf16_t>& a, hipStream_t s);
+hipError_t decode_merge_bf16(const DecodeArgs<bf16_t>& a, hipStream_t s);
 
 inline int decode_slices(int D) { return (D + kDecSlice - 1) / kDecSlice; }
 

@@ -2,18 +2,28 @@
 //
 // The step's dependencies are: x -> {q, L2 (EMA), key projections};
 // q -> router hidden -> lambda; key projections -> key -> top-R blocks;
-// (lambda, blocks, L2, x) -> X_fused -> K/V row.  Each kernel below holds
-// workgroups of different roles that share a dependency level, so the step
-// needs three launches before the K/V product instead of eight:
-//   decode_front   Q = x W_q (one wave per output)  |  EMA update, block
-//                  finalise and fp64 partial key projections per 128 channels
-//   decode_mid     router hidden GELU(q W_r1) (one wave per unit)  |  per
-//                  token: sum key partials, key, top-R selection
-//   decode_fuse    lambda = softmax(hidden W_r2) (recomputed by each
-//                  workgroup from the 64 hidden values), then X_fused
-// (MKA reading note, method sections 1-3; the abstract page's Table 11 counts
-// three launches per token for its own kernels.)
+// (lambda, blocks, L2, x) -> X_fused -> K/V row.  (MKA reading note, method
+// sections 1-3; the abstract page's Table 11 counts three launches per token
+// for its own kernels.)
+//
+// bf16 layers use three launches.  The K/V row is linear in X_fused:
+//   [K|V] = lambda1 (x W) + lambda2 (L2 W) + lambda3 (L3 W),  W = [W_k; W_v],
+// and L3 W is the mean of the retrieved blocks' projected means m_b W, which
+// are kept beside the bank (computed when a block is indexed).  So only the
+// last kernel waits for the router:
+//   decode_inputs   Q = x W_q  |  [x; L2] W  |  EMA update, block finalise
+//                   and fp64 partial key projections per 128 channels
+//   decode_attend   split attention over cache rows [0, pos)  |  router
+//                   hidden GELU(q W_r1)  |  per token: key, top-R, L3 W,
+//                   EMA state commit
+//   decode_merge    lambda, the new K/V row (written to the cache at pos),
+//                   its score, and the merge of the attention partials
+// float32 layers run the same steps as sequential kernels:
+//   decode_front    Q (one wave per output) | EMA, block finalise, key partials
+//   decode_mid      router hidden | key, top-R
+//   decode_fuse     lambda, X_fused; then the K/V product and attention.
 #include "decode.h"
+#include "attn_split.h"
 
 namespace mka {
 
@@ -295,11 +305,416 @@ hipError_t decode_fuse(const DecodeArgs<T>& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template hipError_t decode_front<bf16_t>(const DecodeArgs<bf16_t>&, hipStream_t);
-template hipError_t decode_mid<bf16_t>(const DecodeArgs<bf16_t>&, hipStream_t);
-template hipError_t decode_fuse<bf16_t>(const DecodeArgs<bf16_t>&, hipStream_t);
 template hipError_t decode_front<float>(const DecodeArgs<float>&, hipStream_t);
 template hipError_t decode_mid<float>(const DecodeArgs<float>&, hipStream_t);
 template hipError_t decode_fuse<float>(const DecodeArgs<float>&, hipStream_t);
+
+// ===========================================================================
+// bf16 step in three launches.
+// ===========================================================================
+
+// Products of kGemvCols consecutive rows of the weight matrix selected by
+// ``wrow`` with the step's token rows: one wave, lanes stride the reduction
+// with 16-byte loads.  The weight loads of up to 8 strides are all issued
+// before the first product (buffer loads: zero past D); ``feed(b, k, xv)``
+// supplies 8 inputs of token b at k (k < D - 7).
+template <int NIN, typename WRow, typename Feed>
+__device__ __forceinline__ void decode_products(int D, int B, WRow wrow, Feed feed,
+                                                float (&acc)[NIN][kGemvCols][kFewRowsDec]) {
+  constexpr int V = 8, IT = 8;
+  const int lane = threadIdx.x & 63;
+  __amdgpu_buffer_rsrc_t wr[kGemvCols];
+#pragma unroll
+  for (int c = 0; c < kGemvCols; ++c) wr[c] = make_rsrc(wrow(c), static_cast<uint32_t>(D) * 2);
+  for (int k0 = 0; k0 < D; k0 += 64 * V * IT) {
+    u32x4 wraw[IT][kGemvCols];
+#pragma unroll
+    for (int it = 0; it < IT; ++it)
+#pragma unroll
+      for (int c = 0; c < kGemvCols; ++c)
+        wraw[it][c] = buffer_load16(wr[c], static_cast<uint32_t>(k0 + it * 64 * V + lane * V) * 2);
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      if (k0 + it * 64 * V >= D) break;  // the whole stride is past the end
+      const int k = min(k0 + it * 64 * V + lane * V, D - V);  // weights there are zero
+      float wv[kGemvCols][V];
+#pragma unroll
+      for (int c = 0; c < kGemvCols; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wv[c][2 * e] = __uint_as_float(wraw[it][c][e] << 16);
+          wv[c][2 * e + 1] = __uint_as_float(wraw[it][c][e] & 0xFFFF0000u);
+        }
+#pragma unroll
+      for (int b = 0; b < kFewRowsDec; ++b) {
+        if (b < B) {
+          float xv[NIN][V];
+          feed(b, k, xv);
+#pragma unroll
+          for (int j = 0; j < NIN; ++j)
+#pragma unroll
+            for (int c = 0; c < kGemvCols; ++c)
+#pragma unroll
+              for (int i = 0; i < V; ++i) acc[j][c][b] = fmaf(xv[j][i], wv[c][i], acc[j][c][b]);
+        }
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void decode_inputs_kernel(DecodeArgs<bf16_t> a) {
+  __shared__ float Ls[kDecSlice];
+  __shared__ double red[4][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nq_wg = (a.qw + 4 * kGemvCols - 1) / (4 * kGemvCols);
+  const int nkv = 2 * a.kvw, nkv_wg = (nkv + 4 * kGemvCols - 1) / (4 * kGemvCols);
+  int wg = blockIdx.x;
+  if (wg < nq_wg) {
+    // ---- Q = x W_q: kGemvCols output columns per wave.
+    const int n0 = (wg * 4 + wave) * kGemvCols;
+    if (n0 >= a.qw) return;
+    float acc[1][kGemvCols][kFewRowsDec] = {};
+    decode_products<1>(
+        a.D, a.B,
+        [&](int c) { return a.w_q + static_cast<int64_t>(min(n0 + c, a.qw - 1)) * a.D; },
+        [&](int b, int k, float (&xv)[1][8]) { Vec16<bf16_t>::load(a.x + static_cast<int64_t>(b) * a.D + k, xv[0]); },
+        acc);
+#pragma unroll
+    for (int c = 0; c < kGemvCols; ++c)
+#pragma unroll
+      for (int b = 0; b < kFewRowsDec; ++b) {
+        if (b < a.B) {
+          const float v = wave_sum(acc[0][c][b]);
+          if (lane == 0 && n0 + c < a.qw) a.q[static_cast<int64_t>(b) * a.qw + n0 + c] = f32_to_bf16(v);
+        }
+      }
+    return;
+  }
+  wg -= nq_wg;
+  if (wg < nkv_wg) {
+    // ---- [x; L2] [W_k; W_v]^T, with L2 = beta * s_{pos-1} + (1 - beta) * x formed
+    // here exactly as the EMA workgroups form it.
+    const int n0 = (wg * 4 + wave) * kGemvCols;
+    if (n0 >= nkv) return;
+    float acc[2][kGemvCols][kFewRowsDec] = {};
+    decode_products<2>(
+        a.D, a.B,
+        [&](int c) {
+          const int col = min(n0 + c, nkv - 1);
+          return col < a.kvw ? a.w_k + static_cast<int64_t>(col) * a.D
+                             : a.w_v + static_cast<int64_t>(col - a.kvw) * a.D;
+        },
+        [&](int b, int k, float (&xv)[2][8]) {
+          const int64_t o = static_cast<int64_t>(b) * a.D + k;
+          Vec16<bf16_t>::load(a.x + o, xv[0]);
+          float sv[8];
+          if (a.pos == 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sv[i] = 0.f;
+          } else {
+            load4(a.state + o, sv);
+            load4(a.state + o + 4, sv + 4);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) xv[1][i] = fmaf(a.beta, sv[i], a.omb * xv[0][i]);
+        },
+        acc);
+#pragma unroll
+    for (int c = 0; c < kGemvCols; ++c)
+#pragma unroll
+      for (int b = 0; b < kFewRowsDec; ++b) {
+        if (b < a.B) {
+          const float vx = wave_sum(acc[0][c][b]);
+          const float vl = wave_sum(acc[1][c][b]);
+          if (lane == 0 && n0 + c < nkv) {
+            a.kvx[static_cast<int64_t>(b) * nkv + n0 + c] = vx;
+            a.kvl2[static_cast<int64_t>(b) * nkv + n0 + c] = vl;
+          }
+        }
+      }
+    return;
+  }
+  wg -= nkv_wg;
+  // ---- EMA update + block finalise + partial key projections for one slice.
+  // The state itself is committed by decode_attend (the workgroups above read
+  // s_{pos-1} from it in this launch).
+  const int slice = wg % a.n_slices, b = wg / a.n_slices;
+  const int c0 = slice * kDecSlice;
+  float sv = 0.f;
+  if (tid < kDecSlice && c0 + tid < a.D) {
+    const int64_t o = static_cast<int64_t>(b) * a.D + c0 + tid;
+    const float xv = bf16_to_f32(a.x[o]);
+    sv = fmaf(a.beta, a.pos == 0 ? 0.f : a.state[o], a.omb * xv);
+    float acc = (a.pos % a.block == 0 ? 0.f : a.acc[o]) + xv;
+    a.l2[o] = sv;
+    if ((a.pos + 1) % a.block == 0) {
+      a.means[(static_cast<int64_t>(b) * a.nb_cap + (a.pos + 1) / a.block - 1) * a.D + c0 + tid] =
+          acc / static_cast<float>(a.block);
+      acc = 0.f;
+    }
+    a.acc[o] = acc;
+  }
+  if (tid < kDecSlice) Ls[tid] = sv;
+  __syncthreads();
+  const int j = lane, quarter = wave;
+  double p = 0.0;
+  if (j < a.nbits) {
+    // the 32 hyperplane entries are loaded before the (in-order) products
+    const float* prow = a.proj + static_cast<int64_t>(j) * a.D + c0 + quarter * 32;
+    const int cend = min(32, a.D - c0 - quarter * 32);
+    float pv[32];
+    if (cend == 32) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) load4(prow + 4 * i, pv + 4 * i);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 32; ++c) pv[c] = c < cend ? prow[c] : 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < 32; ++c)
+      p = fma(static_cast<double>(Ls[quarter * 32 + c]), static_cast<double>(pv[c]), p);
+  }
+  red[quarter][j] = p;
+  __syncthreads();
+  if (tid < 64)
+    a.part[(static_cast<int64_t>(slice) * a.B + b) * 64 + tid] =
+        ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+}
+
+template <int DH, int RMAX>
+__global__ __launch_bounds__(256, 2) void decode_attend_kernel(DecodeArgs<bf16_t> a) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[split_lds_bytes<DH>()];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nh_wg = (a.r + 3) / 4;
+  int wg = blockIdx.x;
+  if (wg < nh_wg) {
+    // ---- router hidden unit n for every token: GELU(q . W_r1[n]).
+    const int n = wg * 4 + wave;
+    if (n >= a.r) return;
+    const bf16_t* w = a.w_r1 + static_cast<int64_t>(n) * a.qw;
+    float acc[kFewRowsDec] = {};
+#pragma unroll 4
+    for (int k = lane * 8; k < a.qw; k += 512) {
+      float wv[8];
+      Vec16<bf16_t>::load(w + k, wv);
+#pragma unroll
+      for (int b = 0; b < kFewRowsDec; ++b) {
+        if (b < a.B) {
+          float qv[8];
+          Vec16<bf16_t>::load(a.q + static_cast<int64_t>(b) * a.qw + k, qv);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[b] = fmaf(qv[i], wv[i], acc[b]);
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kFewRowsDec; ++b) {
+      if (b < a.B) {
+        const float v = wave_sum(acc[b]);
+        if (lane == 0) a.hidden[b * a.r + n] = gelu(v);
+      }
+    }
+    return;
+  }
+  wg -= nh_wg;
+  if (wg < a.B) {
+    // ---- token b: key, top-R blocks, L3 W (mean of the projected block means)
+    // and the EMA state commit.
+    const int b = wg;
+    uint64_t* key_s = reinterpret_cast<uint64_t*>(lds);
+    uint32_t* cand = reinterpret_cast<uint32_t*>(lds + 16);             // [4][RMAX]
+    int32_t* sel = reinterpret_cast<int32_t*>(lds + 16 + 16 * RMAX);    // [RMAX]
+    const int ne = static_cast<int>(a.pos / a.block);
+    const uint64_t* codes = a.bhash + static_cast<int64_t>(b) * a.nb_cap;
+    // this thread's first 4 block codes are in flight during the key reduction
+    uint64_t cv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) cv[u] = ne > 0 ? codes[min(tid + 256 * u, ne - 1)] : 0;
+    if (wave == 0) {
+      // partial projections of all slices, loaded first, added in slice order
+      double p = 0.0;
+      for (int s0 = 0; s0 < a.n_slices; s0 += 8) {
+        double v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          v[u] = a.part[(static_cast<int64_t>(min(s0 + u, a.n_slices - 1)) * a.B + b) * 64 + lane];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (s0 + u < a.n_slices) p += v[u];
+      }
+      const uint64_t code = __ballot(lane < a.nbits && p > 0.0);
+      if (lane == 0) {
+        *key_s = code;
+        a.key[b] = code;
+      }
+    }
+    __syncthreads();
+    const uint64_t key = *key_s;
+    uint32_t top[RMAX];
+#pragma unroll
+    for (int i = 0; i < RMAX; ++i) top[i] = kEmptyKey;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (tid + 256 * u < ne) insert_sorted(top, cand_key(key, cv[u], tid + 256 * u));
+    for (int jb = tid + 1024; jb < ne; jb += 256) insert_sorted(top, cand_key(key, codes[jb], jb));
+    for (int i = 0; i < a.R; ++i) {
+      const uint32_t m = wave_min_dpp(top[0]);
+      if (top[0] == m && m != kEmptyKey) {
+#pragma unroll
+        for (int k = 0; k < RMAX - 1; ++k) top[k] = top[k + 1];
+        top[RMAX - 1] = kEmptyKey;
+      }
+      if (lane == 0) cand[wave * RMAX + i] = m;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t c0 = kEmptyKey, c1 = kEmptyKey;
+      if (lane < 4 * a.R) c0 = cand[(lane / a.R) * RMAX + lane % a.R];
+      if (lane + 64 < 4 * a.R) c1 = cand[((lane + 64) / a.R) * RMAX + (lane + 64) % a.R];
+      if (c1 < c0) {
+        const uint32_t t = c0;
+        c0 = c1;
+        c1 = t;
+      }
+      int32_t* out = a.idx + static_cast<int64_t>(b) * a.R;
+      for (int i = 0; i < a.R; ++i) {
+        const uint32_t m = wave_min_dpp(c0);
+        if (c0 == m && m != kEmptyKey) {
+          c0 = c1;
+          c1 = kEmptyKey;
+        }
+        const int blk = m == kEmptyKey ? -1 : static_cast<int>(0xFFFFFFu - (m & 0xFFFFFFu));
+        if (lane == 0) {
+          out[i] = blk;
+          sel[i] = blk;
+        }
+      }
+    }
+    __syncthreads();
+    // L3 W = mean of the selected blocks' projected means, in rank order; the
+    // selection is held in registers and every row load is issued up front
+    // (rows of unfilled slots are read at block 0 and not added).
+    const int nkv = 2 * a.kvw;
+    int blk[RMAX], cnt = 0;
+#pragma unroll
+    for (int i = 0; i < RMAX; ++i) {
+      blk[i] = i < a.R ? sel[i] : -1;
+      cnt += blk[i] >= 0;
+    }
+    const float inv = cnt ? 1.0f / static_cast<float>(cnt) : 0.f;
+    const float* pb = a.block_kv + static_cast<int64_t>(b) * a.nb_cap * nkv;
+    for (int n = tid; n < nkv; n += 256) {
+      float v[RMAX];
+#pragma unroll
+      for (int i = 0; i < RMAX; ++i) v[i] = pb[static_cast<int64_t>(max(blk[i], 0)) * nkv + n];
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < RMAX; ++i) sum += blk[i] >= 0 ? v[i] : 0.f;
+      a.kvl3[static_cast<int64_t>(b) * nkv + n] = cnt ? sum * inv : 0.f;
+    }
+    // EMA state commit (the L2 row of this token)
+    const float* l2r = a.l2 + static_cast<int64_t>(b) * a.D;
+    float* str = a.state + static_cast<int64_t>(b) * a.D;
+    for (int c0 = 4 * tid; c0 < a.D; c0 += 4 * 256) {
+      float v4[4];
+      load4(l2r + c0, v4);
+      store4(str + c0, v4);
+    }
+    return;
+  }
+  wg -= a.B;
+  // ---- attention over cache rows [0, pos): one chunk per workgroup.
+  const int per_b = a.n_chunks * a.G * a.n_hb;
+  const int b = wg / per_b, rest = wg % per_b;
+  const int c = rest % a.n_chunks, ghb = rest / a.n_chunks;
+  decode_split_chunk<DH>(a.q, a.k_cache, a.v_cache, a.H, a.G, a.t_cap, a.pos, a.sl2, a.chunk,
+                         a.n_chunks, c, ghb / a.n_hb, ghb % a.n_hb, b, a.part_m, a.part_l,
+                         a.part_o, lds);
+}
+
+template <int DH>
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs<bf16_t> a) {
+  __shared__ MergeLds<DH> sm;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int hpg = a.H / a.G, g = h / hpg;
+  decode_merge_head<DH>(
+      a.part_m, a.part_l, a.part_o, a.H, a.n_chunks, h, b, a.q, a.sl2, a.o, sm,
+      [&](float* kx, float* vx) {
+        const int tid = threadIdx.x, lane = tid & 63;
+        // the token's projected rows, loaded before lambda is known
+        const int64_t rb = static_cast<int64_t>(b) * 2 * a.kvw;
+        const int nk = g * DH + min(tid, DH - 1), nv = a.kvw + nk;
+        const float kx1 = a.kvx[rb + nk], kx2 = a.kvl2[rb + nk], kx3 = a.kvl3[rb + nk];
+        const float vx1 = a.kvx[rb + nv], vx2 = a.kvl2[rb + nv], vx3 = a.kvl3[rb + nv];
+        if (tid < 64) {  // lambda = softmax(hidden W_r2)
+          float z[3];
+#pragma unroll
+          for (int c = 0; c < 3; ++c) {
+            float sum = 0.f;
+            for (int n = lane; n < a.r; n += 64)
+              sum = fmaf(a.hidden[b * a.r + n], bf16_to_f32(a.w_r2[c * a.r + n]), sum);
+            z[c] = wave_sum(sum);
+          }
+          const float zm = fmaxf(z[0], fmaxf(z[1], z[2]));
+          const float e0 = expf(z[0] - zm), e1 = expf(z[1] - zm), e2 = expf(z[2] - zm);
+          const float inv = 1.0f / (e0 + e1 + e2);
+          if (lane == 0) {
+            sm.lam[0] = e0 * inv;
+            sm.lam[1] = e1 * inv;
+            sm.lam[2] = e2 * inv;
+            if (h == 0) {
+              a.lam[b * 3 + 0] = e0 * inv;
+              a.lam[b * 3 + 1] = e1 * inv;
+              a.lam[b * 3 + 2] = e2 * inv;
+            }
+          }
+        }
+        __syncthreads();
+        if (tid < DH) {  // the fused K/V row of the token, rounded as the cache stores it
+          const float l1 = sm.lam[0], l2 = sm.lam[1], l3 = sm.lam[2];
+          const bf16_t kb = f32_to_bf16(l1 * kx1 + l2 * kx2 + l3 * kx3);
+          const bf16_t vb = f32_to_bf16(l1 * vx1 + l2 * vx2 + l3 * vx3);
+          kx[tid] = bf16_to_f32(kb);
+          vx[tid] = bf16_to_f32(vb);
+          if (h % hpg == 0) {
+            const int64_t ro = ((static_cast<int64_t>(b) * a.G + g) * a.t_cap + a.pos) * DH + tid;
+            a.k_cache[ro] = kb;
+            a.v_cache[ro] = vb;
+          }
+        }
+        return true;
+      });
+}
+
+hipError_t decode_inputs_bf16(const DecodeArgs<bf16_t>& a, hipStream_t s) {
+  const int per_wg = 4 * kGemvCols;
+  const int grid = (a.qw + per_wg - 1) / per_wg + (2 * a.kvw + per_wg - 1) / per_wg + a.n_slices * a.B;
+  hipLaunchKernelGGL(decode_inputs_kernel, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t decode_attend_bf16(const DecodeArgs<bf16_t>& a, hipStream_t s) {
+  const int grid = (a.r + 3) / 4 + a.B + a.n_chunks * a.G * a.n_hb * a.B;
+  if (a.dh == 128) {
+    if (a.R <= 16)
+      hipLaunchKernelGGL((decode_attend_kernel<128, 16>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_attend_kernel<128, 32>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    if (a.R <= 16)
+      hipLaunchKernelGGL((decode_attend_kernel<64, 16>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_attend_kernel<64, 32>), dim3(grid), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t decode_merge_bf16(const DecodeArgs<bf16_t>& a, hipStream_t s) {
+  if (a.dh == 128)
+    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(a.H, a.B), dim3(kMergeThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(a.H, a.B), dim3(kMergeThreads), 0, s, a);
+  return hipGetLastError();
+}
 
 }  // namespace mka

@@ -64,13 +64,18 @@ hipError_t fuse_mix(const T* x, const float* l2, const float* means, int nb_cap,
                     const int32_t* idx, const float* lam, int B, int seq, int D, int R, T* xf,
                     hipStream_t s);
 
+// block_kv[b, blk, :] = m_blk [W_k; W_v]^T (float32) for blocks first .. first+n_blocks-1.
+template <typename T>
+hipError_t block_kv_project(const float* means, int nb_cap, int first, int n_blocks, const T* w_k,
+                            const T* w_v, int kvw, int D, int B, float* out, hipStream_t s);
+
 // ---- attention --------------------------------------------------------------------
 template <typename T>
 hipError_t attn_prefill(const T* q, const T* k, const T* v, T* o, int B, int seq, int H, int G,
                         int dh, int64_t t_cap, int64_t pos0, hipStream_t s);
-// Split decode (bf16): partials in ws, merged by a second kernel.
-constexpr int kDecodeChunk = 2048;  // keys per workgroup
-size_t attn_decode_ws_bytes(int B, int H, int dh, int64_t cache_len);
+// Split decode (bf16): partials in ws (for n_rows rows split into chunks),
+// merged by a second kernel.
+size_t attn_decode_ws_bytes(int B, int H, int G, int dh, int64_t n_rows);
 hipError_t attn_decode_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* v, bf16_t* o, int B,
                             int H, int G, int dh, int64_t t_cap, int64_t cache_len, void* ws,
                             hipStream_t s);

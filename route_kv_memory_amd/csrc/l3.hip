@@ -325,4 +325,75 @@ hipError_t retrieve_few(const float* l2, int B, int seq, int D, const float* pro
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Projected block means: block_kv[b, blk, n] = m_blk . W[n] for the columns of
+// W = [W_k; W_v] (n < kvw: row n of W_k, else row n - kvw of W_v).  A wave
+// computes 4 columns for up to 8 blocks; lanes stride D with 16-byte loads of
+// the weights.  Kept beside the bank so that a decode step can form L3 W as a
+// mean of R rows instead of a product with W.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void block_kv_kernel(const float* __restrict__ means, int nb_cap,
+                                                       int first, int n_blocks,
+                                                       const T* __restrict__ w_k,
+                                                       const T* __restrict__ w_v, int kvw, int D,
+                                                       float* __restrict__ out) {
+  constexpr int NC = 4, NB = 8, V = Vec16<T>::kN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nkv = 2 * kvw;
+  const int n0 = (blockIdx.x * 4 + wave) * NC;
+  if (n0 >= nkv) return;
+  const int blk0 = first + blockIdx.y * NB, nb = min(NB, first + n_blocks - blk0);
+  const int b = blockIdx.z;
+  const T* w[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int col = min(n0 + c, nkv - 1);
+    w[c] = col < kvw ? w_k + static_cast<int64_t>(col) * D : w_v + static_cast<int64_t>(col - kvw) * D;
+  }
+  const float* mrow = means + (static_cast<int64_t>(b) * nb_cap + blk0) * D;
+  float acc[NC][NB] = {};
+  for (int k = lane * V; k < D; k += 64 * V) {
+    float wv[NC][V];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) Vec16<T>::load(w[c] + k, wv[c]);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (j < nb) {
+        float mv[V];
+#pragma unroll
+        for (int i = 0; i < V; i += 4) load4(mrow + static_cast<int64_t>(j) * D + k + i, mv + i);
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[c][j] = fmaf(mv[i], wv[c][i], acc[c][j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (j < nb) {
+        const float v = wave_sum(acc[c][j]);
+        if (lane == 0 && n0 + c < nkv)
+          out[(static_cast<int64_t>(b) * nb_cap + blk0 + j) * nkv + n0 + c] = v;
+      }
+    }
+}
+
+template <typename T>
+hipError_t block_kv_project(const float* means, int nb_cap, int first, int n_blocks, const T* w_k,
+                            const T* w_v, int kvw, int D, int B, float* out, hipStream_t s) {
+  if (n_blocks <= 0) return hipSuccess;
+  const dim3 grid((2 * kvw + 15) / 16, (n_blocks + 7) / 8, B);
+  hipLaunchKernelGGL(block_kv_kernel<T>, grid, dim3(256), 0, s, means, nb_cap, first, n_blocks,
+                     w_k, w_v, kvw, D, out);
+  return hipGetLastError();
+}
+template hipError_t block_kv_project<float>(const float*, int, int, int, const float*,
+                                            const float*, int, int, int, float*, hipStream_t);
+template hipError_t block_kv_project<bf16_t>(const float*, int, int, int, const bf16_t*,
+                                             const bf16_t*, int, int, int, float*, hipStream_t);
+
 }  // namespace mka

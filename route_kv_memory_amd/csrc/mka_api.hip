@@ -5,15 +5,13 @@
 #include <initializer_list>
 #include <cstdio>
 #include <cstring>
-#include <memory>
-#include <mutex>
 #include <type_traits>
-#include <unordered_map>
 
 #include "../../include/mka.h"
 #include "decode.h"
 #include "gemm.h"
 #include "kernels.h"
+#include "attn_split.h"
 
 using namespace mka;
 
@@ -90,7 +88,18 @@ size_t route_ws(const mka_dims* d) {
 }
 size_t decode_ws(const mka_dims* d, int64_t cache_len) {
   if (d->dtype != MKA_BF16) return 0;
-  return round256(attn_decode_ws_bytes(d->batch, d->n_heads, d->head_dim, cache_len));
+  // the split covers rows [0, cache_len - 1); the last row joins in the merge
+  return round256(attn_decode_ws_bytes(d->batch, d->n_heads, d->n_kv_heads, d->head_dim,
+                                       cache_len - 1));
+}
+
+// The split kernel addresses one chunk of a KV head with 32-bit byte offsets.
+bool decode_chunk_fits(const mka_dims* d, int64_t n_rows) {
+  if (d->dtype != MKA_BF16 || n_rows <= 0) return true;
+  const int units = d->batch * d->n_kv_heads *
+                    ((d->n_heads / d->n_kv_heads + kSplitHeads - 1) / kSplitHeads);
+  return (static_cast<int64_t>(decode_chunk_keys(units, n_rows)) + kSplitTile) * d->head_dim * 2 <
+         (static_cast<int64_t>(1) << 31);
 }
 
 // ---------------------------------------------------------------- per-step bodies
@@ -177,6 +186,23 @@ int do_index(const mka_dims* d, const float* means, int nb_cap, int first, int n
   MKA_LAUNCH("l3_index", simhash_rows(means + first * D, static_cast<int64_t>(nb_cap) * D, n,
                                       d->batch, d->d_model, proj, d->hash_bits, bh + first,
                                       nb_cap, ws, s));
+  return MKA_OK;
+}
+
+int do_block_kv(const mka_dims* d, const float* means, int nb_cap, int first, int n,
+                const void* w_k, const void* w_v, float* block_kv, hipStream_t s) {
+  if (n <= 0) return MKA_OK;
+  const int kvw = d->n_kv_heads * d->head_dim;
+  if (d->dtype == MKA_BF16)
+    MKA_LAUNCH("l3_block_kv", block_kv_project<bf16_t>(means, nb_cap, first, n,
+                                                       static_cast<const bf16_t*>(w_k),
+                                                       static_cast<const bf16_t*>(w_v), kvw,
+                                                       d->d_model, d->batch, block_kv, s));
+  else
+    MKA_LAUNCH("l3_block_kv", block_kv_project<float>(means, nb_cap, first, n,
+                                                      static_cast<const float*>(w_k),
+                                                      static_cast<const float*>(w_v), kvw,
+                                                      d->d_model, d->batch, block_kv, s));
   return MKA_OK;
 }
 
@@ -273,58 +299,29 @@ bool ptrs_ok(std::initializer_list<const void*> ps) {
   return true;
 }
 
-constexpr int64_t kMaxDecodeCache = static_cast<int64_t>(kDecodeChunk) * 4096;
+constexpr int64_t kMaxDecodeCache = static_cast<int64_t>(1) << 26;  // rows
 
-// Per-device auxiliary stream and fork/join events of mka_decode_step,
-// created on a device's first decode step and kept until the process ends.
-// The enqueueing of one decode step holds the device's lock, so concurrent
-// callers cannot interleave their fork/join records.
-struct Aux {
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  std::mutex lock;
-};
-
-Aux* aux_for_current_device(int* rc) {
-  static std::mutex table_lock;
-  static std::unordered_map<int, std::unique_ptr<Aux>> table;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) {
-    *rc = hip_fail("decode/aux", e);
-    return nullptr;
-  }
-  std::lock_guard<std::mutex> g(table_lock);
-  auto it = table.find(dev);
-  if (it != table.end()) return it->second.get();
-  auto a = std::make_unique<Aux>();
-  if ((e = hipStreamCreateWithFlags(&a->stream, hipStreamNonBlocking)) != hipSuccess ||
-      (e = hipEventCreateWithFlags(&a->fork, hipEventDisableTiming)) != hipSuccess ||
-      (e = hipEventCreateWithFlags(&a->join, hipEventDisableTiming)) != hipSuccess) {
-    *rc = hip_fail("decode/aux", e);
-    return nullptr;
-  }
-  Aux* p = a.get();
-  table.emplace(dev, std::move(a));
-  return p;
-}
-
-// Workspace of the overlapped bf16 decode step: the attention partials (used
-// on the caller's stream) and the bookkeeping chain's buffers (auxiliary
-// stream) are disjoint.
+// Workspace of a decode step.  bf16: the attention partials over rows [0, pos),
+// the router hidden layer, the partial key projections and the three
+// projected rows (x, L2, L3) of the new K/V row; float32: hidden, partial key
+// projections, X_fused.  Both end with the block index's own workspace.
 struct DecodeWs {
-  size_t attn, hid, part, xf, index, total;
+  size_t attn, hid, part, kv, xf, index, total;
 };
 DecodeWs decode_layout(const mka_dims* d, int64_t cache_len) {
   DecodeWs w{};
-  w.attn = d->dtype == MKA_BF16
-               ? round256(attn_decode_ws_bytes(d->batch, d->n_heads, d->head_dim, cache_len))
-               : 0;
+  const bool bf = d->dtype == MKA_BF16;
+  w.attn = bf ? round256(attn_decode_ws_bytes(d->batch, d->n_heads, d->n_kv_heads, d->head_dim,
+                                               cache_len - 1))
+              : 0;
   w.hid = round256(static_cast<size_t>(d->batch) * d->router_hidden * sizeof(float));
   w.part = round256(sizeof(double) * static_cast<size_t>(decode_slices(d->d_model)) * d->batch * 64);
-  w.xf = fuse_ws(d);
+  w.kv = bf ? round256(3 * sizeof(float) * static_cast<size_t>(d->batch) * 2 * d->n_kv_heads *
+                       d->head_dim)
+            : 0;
+  w.xf = bf ? 0 : fuse_ws(d);
   w.index = index_ws(d, 1);
-  w.total = w.attn + w.hid + w.part + w.xf + w.index;
+  w.total = w.attn + w.hid + w.part + w.kv + w.xf + w.index;
   return w;
 }
 
@@ -425,6 +422,20 @@ int mka_l3_index(const mka_dims* d, const float* block_means, int32_t nb_cap, in
                   static_cast<hipStream_t>(stream));
 }
 
+int mka_l3_block_kv(const mka_dims* d, const float* block_means, int32_t nb_cap,
+                    int32_t first_block, int32_t n_blocks, const void* w_k, const void* w_v,
+                    float* block_kv, void* stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  MKA_CHECK(first_block >= 0 && n_blocks >= 0 &&
+                static_cast<int64_t>(first_block) + n_blocks <= nb_cap,
+            MKA_ERR_INVALID);
+  if (n_blocks == 0) return MKA_OK;
+  MKA_CHECK(ptrs_ok({block_means, w_k, w_v, block_kv}), MKA_ERR_INVALID);
+  return do_block_kv(d, block_means, nb_cap, first_block, n_blocks, w_k, w_v, block_kv,
+                     static_cast<hipStream_t>(stream));
+}
+
 int mka_l3_retrieve(const mka_dims* d, const float* l2, const float* proj,
                     const uint64_t* block_hash, int32_t nb_cap, int64_t pos0, uint64_t* key_out,
                     int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
@@ -477,7 +488,8 @@ int mka_attn_decode(const mka_dims* d, const void* q, const void* k_cache, const
   MKA_CHECK(d->seq == 1, MKA_ERR_INVALID);
   MKA_CHECK(ptrs_ok({q, k_cache, v_cache, o}), MKA_ERR_INVALID);
   MKA_CHECK(cache_len >= 1 && cache_len <= t_cap, MKA_ERR_INVALID);
-  MKA_CHECK(cache_len <= kMaxDecodeCache, MKA_ERR_UNSUPPORTED);
+  MKA_CHECK(cache_len <= kMaxDecodeCache && decode_chunk_fits(d, cache_len - 1),
+            MKA_ERR_UNSUPPORTED);
   if (decode_ws(d, cache_len) > 0) {
     MKA_CHECK(ptrs_ok({ws}), MKA_ERR_WORKSPACE);
     MKA_CHECK(ws_bytes >= decode_ws(d, cache_len), MKA_ERR_WORKSPACE);
@@ -490,7 +502,8 @@ static int check_layer_args(const mka_dims* d, const void* x, int64_t pos0, cons
                             const mka_state* st, const mka_outputs* out) {
   MKA_CHECK(w != nullptr && st != nullptr && out != nullptr, MKA_ERR_INVALID);
   MKA_CHECK(ptrs_ok({x, w->w_q, w->w_k, w->w_v, w->w_r1, w->w_r2, w->proj}), MKA_ERR_INVALID);
-  MKA_CHECK(ptrs_ok({st->ema_state, st->block_acc, st->block_means, st->k_cache, st->v_cache}),
+  MKA_CHECK(ptrs_ok({st->ema_state, st->block_acc, st->block_means, st->block_kv, st->k_cache,
+                     st->v_cache}),
             MKA_ERR_INVALID);
   MKA_CHECK(st->block_hash != nullptr && (reinterpret_cast<uintptr_t>(st->block_hash) & 7u) == 0,
             MKA_ERR_INVALID);
@@ -521,6 +534,9 @@ int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weight
   if ((rc = do_index(d, st->block_means, st->nb_cap, static_cast<int>(first), static_cast<int>(n),
                      w->proj, st->block_hash, ws, s)))
     return rc;
+  if ((rc = do_block_kv(d, st->block_means, st->nb_cap, static_cast<int>(first),
+                        static_cast<int>(n), w->w_k, w->w_v, st->block_kv, s)))
+    return rc;
   if ((rc = do_retrieve(d, out->l2, w->proj, st->block_hash, st->nb_cap, pos0, out->key, out->idx,
                         ws, s)))
     return rc;
@@ -538,7 +554,7 @@ int mka_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_wei
   MKA_CHECK(d->seq == 1, MKA_ERR_INVALID);
   rc = check_layer_args(d, x, pos, w, st, out);
   if (rc) return rc;
-  MKA_CHECK(pos + 1 <= kMaxDecodeCache, MKA_ERR_UNSUPPORTED);
+  MKA_CHECK(pos + 1 <= kMaxDecodeCache && decode_chunk_fits(d, pos), MKA_ERR_UNSUPPORTED);
   const size_t need = mka_workspace_bytes(d, MKA_OP_DECODE_STEP, pos + 1);
   MKA_CHECK(ws_bytes >= need, MKA_ERR_WORKSPACE);
   MKA_CHECK(need == 0 || ptrs_ok({ws}), MKA_ERR_WORKSPACE);
@@ -546,12 +562,14 @@ int mka_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_wei
   hipStream_t s = static_cast<hipStream_t>(stream);
   const DecodeWs L = decode_layout(d, pos + 1);
   char* base = static_cast<char*>(ws);
-  void* w_attn = base;
+  float* w_attn = reinterpret_cast<float*>(base);
   float* w_hid = reinterpret_cast<float*>(base + L.attn);
   double* w_part = reinterpret_cast<double*>(base + L.attn + L.hid);
-  void* w_xf = base + L.attn + L.hid + L.part;
-  void* w_index = base + L.attn + L.hid + L.part + L.xf;
-  const int B = d->batch, D = d->d_model, qw = d->n_heads * d->head_dim, kvw = d->n_kv_heads * d->head_dim;
+  float* w_kv = reinterpret_cast<float*>(base + L.attn + L.hid + L.part);
+  void* w_xf = base + L.attn + L.hid + L.part + L.kv;
+  void* w_index = base + L.attn + L.hid + L.part + L.kv + L.xf;
+  const int B = d->batch, D = d->d_model, H = d->n_heads, G = d->n_kv_heads, dh = d->head_dim;
+  const int qw = H * dh, kvw = G * dh;
   const bool closes = (pos + 1) % d->block == 0;
   const int closed_block = static_cast<int>((pos + 1) / d->block - 1);
 
@@ -587,56 +605,59 @@ int mka_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_wei
     a.idx = out->idx;
     a.R = d->top_r;
     a.xf = static_cast<T*>(w_xf);
+    a.w_k = static_cast<const T*>(w->w_k);
+    a.w_v = static_cast<const T*>(w->w_v);
+    a.kvw = kvw;
+    a.kvx = w_kv;
+    a.kvl2 = w_kv + static_cast<size_t>(B) * 2 * kvw;
+    a.kvl3 = w_kv + static_cast<size_t>(2) * B * 2 * kvw;
+    a.block_kv = st->block_kv;
+    a.k_cache = static_cast<T*>(st->k_cache);
+    a.v_cache = static_cast<T*>(st->v_cache);
+    a.H = H;
+    a.G = G;
+    a.dh = dh;
+    a.t_cap = st->t_cap;
+    a.sl2 = 1.4426950408889634f / sqrtf(static_cast<float>(dh));
+    a.n_hb = (H / G + kSplitHeads - 1) / kSplitHeads;
+    a.chunk = decode_chunk_keys(B * G * a.n_hb, pos);
+    a.n_chunks = pos > 0 ? decode_n_chunks(B * G * a.n_hb, pos) : 0;
+    const size_t np = static_cast<size_t>(B) * H * a.n_chunks;
+    a.part_m = w_attn;
+    a.part_l = w_attn + np;
+    a.part_o = w_attn + 2 * np;
+    a.o = static_cast<T*>(out->o);
     return a;
   };
 
-  if (d->dtype != MKA_BF16) {  // fp32 layers: the same kernels in order on one stream
+  if (d->dtype != MKA_BF16) {  // fp32 layers: the sequential kernels in order
     const DecodeArgs<float> a = fill(static_cast<float*>(nullptr));
     MKA_LAUNCH("decode/front", decode_front<float>(a, s));
     MKA_LAUNCH("decode/mid", decode_mid<float>(a, s));
     MKA_LAUNCH("decode/fuse", decode_fuse<float>(a, s));
     const EpiKV<float> epi{static_cast<float*>(st->k_cache), static_cast<float*>(st->v_cache), 1,
-                           d->n_kv_heads, d->head_dim, st->t_cap, pos};
+                           G, dh, st->t_cap, pos};
     MKA_LAUNCH("decode/kv", gemv<float>(a.xf, D, B, static_cast<const float*>(w->w_k),
                                         static_cast<const float*>(w->w_v), kvw, 2 * kvw, D, epi, s));
     if ((rc = do_attn_decode(d, out->q, st->k_cache, st->v_cache, st->t_cap, pos + 1, out->o,
                              nullptr, s)))
       return rc;
-    if (closes)
-      return do_index(d, st->block_means, st->nb_cap, closed_block, 1, w->proj, st->block_hash,
-                      w_index, s);
-    return MKA_OK;
+  } else {
+    // bf16: inputs (Q, [x; L2] W, EMA, key partials) -> attention over rows
+    // [0, pos) with the router, top-R and L3 W beside it -> merge with the
+    // new row, which is formed (lambda applied), cached and scored there.
+    const DecodeArgs<bf16_t> a = fill(static_cast<bf16_t*>(nullptr));
+    MKA_LAUNCH("decode/inputs", decode_inputs_bf16(a, s));
+    MKA_LAUNCH("decode/attend", decode_attend_bf16(a, s));
+    MKA_LAUNCH("decode/merge", decode_merge_bf16(a, s));
   }
-  // bf16: the split attention over rows [0, pos) needs only q, so it runs on the
-  // caller's stream while the rest of the step (router, top-R, fusion, K/V
-  // append of row pos, block finalise) runs on the auxiliary stream; the merge
-  // then folds in row pos.
-  Aux* aux = aux_for_current_device(&rc);
-  if (aux == nullptr) return rc;
-  std::lock_guard<std::mutex> guard(aux->lock);
-  hipStream_t s2 = aux->stream;
-  const DecodeArgs<bf16_t> a = fill(static_cast<bf16_t*>(nullptr));
-  const bf16_t* kc = static_cast<const bf16_t*>(st->k_cache);
-  const bf16_t* vc = static_cast<const bf16_t*>(st->v_cache);
-  MKA_LAUNCH("decode/front", decode_front<bf16_t>(a, s));
-  MKA_LAUNCH("decode/fork", hipEventRecord(aux->fork, s));
-  MKA_LAUNCH("decode/fork", hipStreamWaitEvent(s2, aux->fork, 0));
-  MKA_LAUNCH("decode/attn_split", attn_decode_split_bf16(a.q, kc, vc, B, d->n_heads, d->n_kv_heads,
-                                                         d->head_dim, st->t_cap, pos, w_attn, s));
-  MKA_LAUNCH("decode/mid", decode_mid<bf16_t>(a, s2));
-  MKA_LAUNCH("decode/fuse", decode_fuse<bf16_t>(a, s2));
-  const EpiKV<bf16_t> epi{static_cast<bf16_t*>(st->k_cache), static_cast<bf16_t*>(st->v_cache), 1,
-                          d->n_kv_heads, d->head_dim, st->t_cap, pos};
-  MKA_LAUNCH("decode/kv", gemv<bf16_t>(a.xf, D, B, static_cast<const bf16_t*>(w->w_k),
-                                       static_cast<const bf16_t*>(w->w_v), kvw, 2 * kvw, D, epi, s2));
-  if (closes && (rc = do_index(d, st->block_means, st->nb_cap, closed_block, 1, w->proj,
-                               st->block_hash, w_index, s2)))
-    return rc;
-  MKA_LAUNCH("decode/join", hipEventRecord(aux->join, s2));
-  MKA_LAUNCH("decode/join", hipStreamWaitEvent(s, aux->join, 0));
-  MKA_LAUNCH("decode/attn_merge",
-             attn_decode_merge_bf16(a.q, kc, vc, static_cast<bf16_t*>(out->o), B, d->n_heads,
-                                    d->n_kv_heads, d->head_dim, st->t_cap, pos, pos, w_attn, s));
+  if (closes) {  // the block this token closes joins the bank for the next tokens
+    if ((rc = do_index(d, st->block_means, st->nb_cap, closed_block, 1, w->proj, st->block_hash,
+                       w_index, s)))
+      return rc;
+    return do_block_kv(d, st->block_means, st->nb_cap, closed_block, 1, w->w_k, w->w_v,
+                       st->block_kv, s);
+  }
   return MKA_OK;
 }
 

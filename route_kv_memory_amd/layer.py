@@ -44,12 +44,24 @@ class Layer:
             "block_acc": torch.zeros(B, D, dtype=torch.float32, **z),
             "block_means": torch.zeros(B, self.nb_cap, D, dtype=torch.float32, **z),
             "block_hash": torch.zeros(B, self.nb_cap, dtype=torch.int64, **z),
+            "block_kv": torch.zeros(B, self.nb_cap, 2 * G * dh, dtype=torch.float32, **z),
             "k_cache": torch.zeros(B, G, self.t_cap, dh, dtype=self.tdtype, **z),
             "v_cache": torch.zeros(B, G, self.t_cap, dh, dtype=self.tdtype, **z),
         }
         self.state = mka.State(nb_cap=self.nb_cap, t_cap=self.t_cap,
                                **{k: v.data_ptr() for k, v in self.st.items()})
         self._ws = None
+
+    def index_blocks(self, first: int, n: int, stream=None) -> None:
+        """Codes and projections of block means first .. first+n-1 (already in
+        ``st["block_means"]``): what a prefill leaves for the blocks it completes."""
+        d = self.dims(1)
+        ws = self.workspace(mka.mka_workspace_bytes(d, mka.MKA_OP_INDEX, n))
+        st = self.st
+        mka.mka_l3_index(d, st["block_means"], self.nb_cap, first, n, self.w["proj"],
+                         st["block_hash"], ws, ws.numel(), stream)
+        mka.mka_l3_block_kv(d, st["block_means"], self.nb_cap, first, n, self.w["w_k"],
+                            self.w["w_v"], st["block_kv"], stream)
 
     def dims(self, seq: int) -> mka.Dims:
         return mka.dims(self.shape, seq=seq, batch=self.batch)

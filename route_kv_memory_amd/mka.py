@@ -19,7 +19,8 @@ __all__ = [
     "header_symbols", "MKA_F32", "MKA_BF16", "MKA_OK", "MKA_ERR_INVALID", "MKA_ERR_UNSUPPORTED",
     "MKA_ERR_WORKSPACE", "MKA_ERR_HIP", "MKA_OP_EMA_SCAN", "MKA_OP_FUSE_KV", "MKA_OP_ATTN_DECODE",
     "MKA_OP_PREFILL", "MKA_OP_DECODE_STEP", "MKA_OP_RETRIEVE", "MKA_OP_INDEX", "MKA_OP_ROUTE",
-    "mka_route", "mka_ema_scan", "mka_l3_index", "mka_l3_retrieve", "mka_fuse_kv_proj",
+    "mka_route", "mka_ema_scan", "mka_l3_index", "mka_l3_block_kv", "mka_l3_retrieve",
+    "mka_fuse_kv_proj",
     "mka_attn_prefill", "mka_attn_decode", "mka_prefill", "mka_decode_step",
     "mka_workspace_bytes", "mka_status_string", "mka_last_error", "mka_version",
 ]
@@ -58,7 +59,8 @@ class Weights(ctypes.Structure):
 
 class State(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("ema_state", "block_acc", "block_means", "block_hash", "k_cache", "v_cache")] + [
+                ("ema_state", "block_acc", "block_means", "block_hash", "block_kv", "k_cache",
+                 "v_cache")] + [
         ("nb_cap", ctypes.c_int32), ("t_cap", ctypes.c_int64)]
 
 
@@ -75,6 +77,7 @@ _SIGS = {
     "mka_route": (ctypes.c_int, [_PD, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mka_ema_scan": (ctypes.c_int, [_PD, _P, _I64, _P, _P, _P, _P, _I32, _P, _SZ, _P]),
     "mka_l3_index": (ctypes.c_int, [_PD, _P, _I32, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "mka_l3_block_kv": (ctypes.c_int, [_PD, _P, _I32, _I32, _I32, _P, _P, _P, _P]),
     "mka_l3_retrieve": (ctypes.c_int, [_PD, _P, _P, _P, _I32, _I64, _P, _P, _P, _SZ, _P]),
     "mka_fuse_kv_proj": (ctypes.c_int,
                          [_PD, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _I64, _I64, _P, _SZ, _P]),
@@ -176,6 +179,13 @@ def mka_l3_index(d, block_means, nb_cap, first_block, n_blocks, proj, block_hash
     _check("mka_l3_index", lib().mka_l3_index(
         ctypes.byref(d), _ptr(block_means), nb_cap, first_block, n_blocks, _ptr(proj),
         _ptr(block_hash), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def mka_l3_block_kv(d, block_means, nb_cap, first_block, n_blocks, w_k, w_v, block_kv,
+                    stream=None):
+    _check("mka_l3_block_kv", lib().mka_l3_block_kv(
+        ctypes.byref(d), _ptr(block_means), nb_cap, first_block, n_blocks, _ptr(w_k), _ptr(w_v),
+        _ptr(block_kv), _stream(stream)))
 
 
 def mka_l3_retrieve(d, l2, proj, block_hash, nb_cap, pos0, key_out, idx_out, ws=None, ws_bytes=0,

@@ -36,6 +36,7 @@ def state_np(layer):
     st = layer.st
     return dict(k=to_np(st["k_cache"]), v=to_np(st["v_cache"]),
                 means=to_np(st["block_means"]), bhash=to_np(st["block_hash"]).view(np.uint64),
+                block_kv=to_np(st["block_kv"]),
                 ema=to_np(st["ema_state"]), acc=to_np(st["block_acc"]))
 
 

@@ -88,6 +88,12 @@ def test_range_checks_rejected():
     with pytest.raises(mka.MkaError) as e:
         mka.mka_l3_index(d, FAKE, 32, 30, 3, FAKE, FAKE, FAKE, 1 << 30, stream=0)
     assert e.value.status == mka.MKA_ERR_INVALID
+    with pytest.raises(mka.MkaError) as e:
+        mka.mka_l3_block_kv(d, FAKE, 32, 30, 3, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == mka.MKA_ERR_INVALID
+    with pytest.raises(mka.MkaError) as e:  # null projected-means buffer
+        mka.mka_l3_block_kv(d, FAKE, 32, 0, 3, FAKE, FAKE, None, stream=0)
+    assert e.value.status == mka.MKA_ERR_INVALID
 
 
 def test_workspace_sizes_and_rejection():
@@ -102,7 +108,7 @@ def test_workspace_sizes_and_rejection():
     assert idx > 0  # few blocks: the projections are split over d_model
     dd = mka.dims(I.workload("qwen7b_decode_128k"))
     dec = mka.mka_workspace_bytes(dd, mka.MKA_OP_ATTN_DECODE, 131073)
-    chunks = (131073 + 2047) // 2048  # 2048-key chunks
+    chunks = 256 // 4  # the split's 131072 rows: one chunk per CU over the 4 KV heads
     assert dec >= 4 * 28 * chunks * (128 + 2)
     assert mka.mka_workspace_bytes(dd, mka.MKA_OP_DECODE_STEP, 131073) >= dec
     with pytest.raises(mka.MkaError) as e:

@@ -100,8 +100,7 @@ def test_full_decode_128k():
     d1 = layer.dims(1)
     ws = layer.workspace(max(mka.mka_workspace_bytes(d1, mka.MKA_OP_INDEX, nb0),
                              mka.mka_workspace_bytes(d1, mka.MKA_OP_DECODE_STEP, t_cap)))
-    mka.mka_l3_index(d1, st["block_means"], layer.nb_cap, 0, nb0, layer.w["proj"],
-                     st["block_hash"], ws, ws.numel())
+    layer.index_blocks(0, nb0)
     tokens = to_device(dec["tokens"], s.dtype)
     log(f"[decode] gpu: {n} mka_decode_step calls from position {T0}")
     got = {}

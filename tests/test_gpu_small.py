@@ -69,6 +69,13 @@ def test_small_layer_prefill(name):
     compare_layer(s, inp["proj"], ref, outputs_np(out), state_np(layer))
     st = state_np(layer)
     check_close("ema_state", st["ema"], ref["l2"][:, -1], "f32")
+    # projected block means: row b = m_b [W_k; W_v]^T, recomputed in float64 from
+    # the GPU's own block means (a property of the kept rows, at any size)
+    nb = ref["block_means"].shape[1]
+    if nb:
+        w_kv = np.concatenate([inp["w_k"], inp["w_v"]], axis=0).astype(np.float64)
+        want = st["means"][:, :nb].astype(np.float64) @ w_kv.T
+        check_close("block_kv", st["block_kv"][:, :nb], want, "f32")
 
 
 @pytest.mark.parametrize("name", ["tiny_f32", "small_bf16_dh128"])
