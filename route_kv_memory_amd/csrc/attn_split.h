@@ -245,9 +245,11 @@ __device__ __forceinline__ void decode_split_chunk(
 // ``extra(kx, vx)`` is called by every thread; it fills kx[0..DH) and
 // vx[0..DH) (LDS, float) and returns whether the extra row exists.  It may use
 // __syncthreads.  Output o[b, h, :] = sum / denominator, rounded to bf16.
+// Every partial is loaded before the extra row is formed (at most one
+// (max, sum) pair per thread: n_chunks <= kMaxDecodeChunks).
 // ---------------------------------------------------------------------------
-constexpr int kMaxDecodeChunks = 4096;
 constexpr int kMergeThreads = 512;
+constexpr int kMaxDecodeChunks = kMergeThreads;
 
 template <int DH>
 struct MergeLds {
@@ -267,21 +269,28 @@ __device__ __forceinline__ void decode_merge_head(const float* __restrict__ part
                                                   const bf16_t* __restrict__ Q, float sl2,
                                                   bf16_t* __restrict__ O, MergeLds<DH>& sm,
                                                   Extra extra) {
-  constexpr int NT = kMergeThreads, GR = NT / DH;
+  constexpr int NT = kMergeThreads, GR = NT / DH, KO = 16;
   const int tid = threadIdx.x, lane = tid & 63;
+  const int d = tid % DH, grp = tid / DH;
   const int64_t p0 = (static_cast<int64_t>(b) * H + h) * n_chunks;
+  const float pm = tid < n_chunks ? part_m[p0 + tid] : -INFINITY;
+  const float pl = tid < n_chunks ? part_l[p0 + tid] : 0.f;
+  float po[KO];  // this thread's first KO chunks of output column d
+#pragma unroll
+  for (int i = 0; i < KO; ++i) {
+    const int c = grp + GR * i;
+    po[i] = c < n_chunks ? part_o[(p0 + c) * DH + d] : 0.f;
+  }
   const bool has_extra = extra(sm.kx, sm.vx);
   __syncthreads();
   if (has_extra && tid < 64) {  // score of the extra row, scaled like the partials
     const bf16_t* qh = Q + (static_cast<int64_t>(b) * H + h) * DH;
     float dot = 0.f;
-    for (int d = lane; d < DH; d += 64) dot = fmaf(bf16_to_f32(qh[d]), sm.kx[d], dot);
+    for (int e = lane; e < DH; e += 64) dot = fmaf(bf16_to_f32(qh[e]), sm.kx[e], dot);
     dot = wave_sum(dot);
     if (lane == 0) sm.sx = dot * sl2;
   }
-  float mx = -INFINITY;
-  for (int c = tid; c < n_chunks; c += NT) mx = fmaxf(mx, part_m[p0 + c]);
-  mx = wave_max(mx);
+  const float mx = wave_max(pm);
   if (lane == 0) sm.red[tid >> 6] = mx;
   __syncthreads();
   const float sx = has_extra ? sm.sx : -INFINITY;
@@ -289,23 +298,22 @@ __device__ __forceinline__ void decode_merge_head(const float* __restrict__ part
 #pragma unroll
   for (int w = 0; w < NT / 64; ++w) M = fmaxf(M, sm.red[w]);
   __syncthreads();
-  float ls = 0.f;
-  for (int c = tid; c < n_chunks; c += NT) {
-    const float w = __builtin_amdgcn_exp2f(part_m[p0 + c] - M);
-    sm.wts[c] = w;
-    ls += w * part_l[p0 + c];
-  }
-  ls = wave_sum(ls);
+  const float wgt = tid < n_chunks ? __builtin_amdgcn_exp2f(pm - M) : 0.f;
+  if (tid < n_chunks) sm.wts[tid] = wgt;
+  const float ls = wave_sum(wgt * pl);
   if (lane == 0) sm.red[tid >> 6] = ls;
   __syncthreads();
   const float wx = has_extra ? __builtin_amdgcn_exp2f(sx - M) : 0.f;
   float L = wx;
 #pragma unroll
   for (int w = 0; w < NT / 64; ++w) L += sm.red[w];
-  const int d = tid % DH, grp = tid / DH;
   float o = 0.f;
-#pragma unroll 8
-  for (int c = grp; c < n_chunks; c += GR) o += sm.wts[c] * part_o[(p0 + c) * DH + d];
+#pragma unroll
+  for (int i = 0; i < KO; ++i) {
+    const int c = grp + GR * i;
+    if (c < n_chunks) o += sm.wts[c] * po[i];
+  }
+  for (int c = grp + GR * KO; c < n_chunks; c += GR) o += sm.wts[c] * part_o[(p0 + c) * DH + d];
   sm.osum[grp][d] = o;
   __syncthreads();
   if (tid < DH) {

@@ -11,11 +11,11 @@
 // and L3 W is the mean of the retrieved blocks' projected means m_b W, which
 // are kept beside the bank (computed when a block is indexed).  So only the
 // last kernel waits for the router:
-//   decode_inputs   Q = x W_q  |  [x; L2] W  |  EMA update, block finalise
-//                   and fp64 partial key projections per 128 channels
+//   decode_inputs   Q = x W_q  |  EMA update, block finalise and fp64
+//                   partial key projections per 128 channels
 //   decode_attend   split attention over cache rows [0, pos)  |  router
-//                   hidden GELU(q W_r1)  |  per token: key, top-R, L3 W,
-//                   EMA state commit
+//                   hidden GELU(q W_r1)  |  [x; L2] W  |  per token: key,
+//                   top-R, L3 W, EMA state commit
 //   decode_merge    lambda, the new K/V row (written to the cache at pos),
 //                   its score, and the merge of the attention partials
 // float32 layers run the same steps as sequential kernels:
@@ -315,13 +315,14 @@ template hipError_t decode_fuse<float>(const DecodeArgs<float>&, hipStream_t);
 
 // Products of kGemvCols consecutive rows of the weight matrix selected by
 // ``wrow`` with the step's token rows: one wave, lanes stride the reduction
-// with 16-byte loads.  The weight loads of up to 8 strides are all issued
-// before the first product (buffer loads: zero past D); ``feed(b, k, xv)``
-// supplies 8 inputs of token b at k (k < D - 7).
+// with 16-byte loads.  The weight loads of IT strides are all issued before
+// the first product (buffer loads: zero past D), and for each token its IT
+// strides of inputs are loaded together; ``feed(b, k, xv)`` supplies NIN rows
+// of 8 inputs of token b at k (k <= D - 8).
 template <int NIN, typename WRow, typename Feed>
 __device__ __forceinline__ void decode_products(int D, int B, WRow wrow, Feed feed,
                                                 float (&acc)[NIN][kGemvCols][kFewRowsDec]) {
-  constexpr int V = 8, IT = 8;
+  constexpr int V = 8, IT = NIN == 1 ? 8 : 4;
   const int lane = threadIdx.x & 63;
   __amdgpu_buffer_rsrc_t wr[kGemvCols];
 #pragma unroll
@@ -334,28 +335,28 @@ __device__ __forceinline__ void decode_products(int D, int B, WRow wrow, Feed fe
       for (int c = 0; c < kGemvCols; ++c)
         wraw[it][c] = buffer_load16(wr[c], static_cast<uint32_t>(k0 + it * 64 * V + lane * V) * 2);
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      if (k0 + it * 64 * V >= D) break;  // the whole stride is past the end
-      const int k = min(k0 + it * 64 * V + lane * V, D - V);  // weights there are zero
-      float wv[kGemvCols][V];
+    for (int b = 0; b < kFewRowsDec; ++b) {
+      if (b < B) {
+        float xv[IT][NIN][V];
 #pragma unroll
-      for (int c = 0; c < kGemvCols; ++c)
+        for (int it = 0; it < IT; ++it) feed(b, min(k0 + it * 64 * V + lane * V, D - V), xv[it]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          wv[c][2 * e] = __uint_as_float(wraw[it][c][e] << 16);
-          wv[c][2 * e + 1] = __uint_as_float(wraw[it][c][e] & 0xFFFF0000u);
-        }
+        for (int it = 0; it < IT; ++it) {
+          if (k0 + it * 64 * V < D) {  // strides past the end hold no weights
 #pragma unroll
-      for (int b = 0; b < kFewRowsDec; ++b) {
-        if (b < B) {
-          float xv[NIN][V];
-          feed(b, k, xv);
+            for (int c = 0; c < kGemvCols; ++c) {
+              float wv[V];
 #pragma unroll
-          for (int j = 0; j < NIN; ++j)
+              for (int e = 0; e < 4; ++e) {
+                wv[2 * e] = __uint_as_float(wraw[it][c][e] << 16);
+                wv[2 * e + 1] = __uint_as_float(wraw[it][c][e] & 0xFFFF0000u);
+              }
 #pragma unroll
-            for (int c = 0; c < kGemvCols; ++c)
+              for (int j = 0; j < NIN; ++j)
 #pragma unroll
-              for (int i = 0; i < V; ++i) acc[j][c][b] = fmaf(xv[j][i], wv[c][i], acc[j][c][b]);
+                for (int i = 0; i < V; ++i) acc[j][c][b] = fmaf(xv[it][j][i], wv[i], acc[j][c][b]);
+            }
+          }
         }
       }
     }
@@ -367,7 +368,6 @@ __global__ __launch_bounds__(256) void decode_inputs_kernel(DecodeArgs<bf16_t> a
   __shared__ double red[4][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nq_wg = (a.qw + 4 * kGemvCols - 1) / (4 * kGemvCols);
-  const int nkv = 2 * a.kvw, nkv_wg = (nkv + 4 * kGemvCols - 1) / (4 * kGemvCols);
   int wg = blockIdx.x;
   if (wg < nq_wg) {
     // ---- Q = x W_q: kGemvCols output columns per wave.
@@ -391,53 +391,8 @@ __global__ __launch_bounds__(256) void decode_inputs_kernel(DecodeArgs<bf16_t> a
     return;
   }
   wg -= nq_wg;
-  if (wg < nkv_wg) {
-    // ---- [x; L2] [W_k; W_v]^T, with L2 = beta * s_{pos-1} + (1 - beta) * x formed
-    // here exactly as the EMA workgroups form it.
-    const int n0 = (wg * 4 + wave) * kGemvCols;
-    if (n0 >= nkv) return;
-    float acc[2][kGemvCols][kFewRowsDec] = {};
-    decode_products<2>(
-        a.D, a.B,
-        [&](int c) {
-          const int col = min(n0 + c, nkv - 1);
-          return col < a.kvw ? a.w_k + static_cast<int64_t>(col) * a.D
-                             : a.w_v + static_cast<int64_t>(col - a.kvw) * a.D;
-        },
-        [&](int b, int k, float (&xv)[2][8]) {
-          const int64_t o = static_cast<int64_t>(b) * a.D + k;
-          Vec16<bf16_t>::load(a.x + o, xv[0]);
-          float sv[8];
-          if (a.pos == 0) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) sv[i] = 0.f;
-          } else {
-            load4(a.state + o, sv);
-            load4(a.state + o + 4, sv + 4);
-          }
-#pragma unroll
-          for (int i = 0; i < 8; ++i) xv[1][i] = fmaf(a.beta, sv[i], a.omb * xv[0][i]);
-        },
-        acc);
-#pragma unroll
-    for (int c = 0; c < kGemvCols; ++c)
-#pragma unroll
-      for (int b = 0; b < kFewRowsDec; ++b) {
-        if (b < a.B) {
-          const float vx = wave_sum(acc[0][c][b]);
-          const float vl = wave_sum(acc[1][c][b]);
-          if (lane == 0 && n0 + c < nkv) {
-            a.kvx[static_cast<int64_t>(b) * nkv + n0 + c] = vx;
-            a.kvl2[static_cast<int64_t>(b) * nkv + n0 + c] = vl;
-          }
-        }
-      }
-    return;
-  }
-  wg -= nkv_wg;
   // ---- EMA update + block finalise + partial key projections for one slice.
-  // The state itself is committed by decode_attend (the workgroups above read
-  // s_{pos-1} from it in this launch).
+  // The state itself is committed by decode_attend.
   const int slice = wg % a.n_slices, b = wg / a.n_slices;
   const int c0 = slice * kDecSlice;
   float sv = 0.f;
@@ -517,6 +472,43 @@ __global__ __launch_bounds__(256, 2) void decode_attend_kernel(DecodeArgs<bf16_t
     return;
   }
   wg -= nh_wg;
+  const int nkv = 2 * a.kvw, nkv_wg = (nkv + 4 * kGemvCols - 1) / (4 * kGemvCols);
+  if (wg < nkv_wg) {
+    // ---- [x; L2] [W_k; W_v]^T (L2 as decode_inputs wrote it); not needed
+    // before decode_merge, so it runs beside the attention.
+    const int n0 = (wg * 4 + wave) * kGemvCols;
+    if (n0 >= nkv) return;
+    float acc[2][kGemvCols][kFewRowsDec] = {};
+    decode_products<2>(
+        a.D, a.B,
+        [&](int c) {
+          const int col = min(n0 + c, nkv - 1);
+          return col < a.kvw ? a.w_k + static_cast<int64_t>(col) * a.D
+                             : a.w_v + static_cast<int64_t>(col - a.kvw) * a.D;
+        },
+        [&](int b, int k, float (&xv)[2][8]) {
+          const int64_t o = static_cast<int64_t>(b) * a.D + k;
+          Vec16<bf16_t>::load(a.x + o, xv[0]);
+          load4(a.l2 + o, xv[1]);
+          load4(a.l2 + o + 4, xv[1] + 4);
+        },
+        acc);
+#pragma unroll
+    for (int c = 0; c < kGemvCols; ++c)
+#pragma unroll
+      for (int b = 0; b < kFewRowsDec; ++b) {
+        if (b < a.B) {
+          const float vx = wave_sum(acc[0][c][b]);
+          const float vl = wave_sum(acc[1][c][b]);
+          if (lane == 0 && n0 + c < nkv) {
+            a.kvx[static_cast<int64_t>(b) * nkv + n0 + c] = vx;
+            a.kvl2[static_cast<int64_t>(b) * nkv + n0 + c] = vl;
+          }
+        }
+      }
+    return;
+  }
+  wg -= nkv_wg;
   if (wg < a.B) {
     // ---- token b: key, top-R blocks, L3 W (mean of the projected block means)
     // and the EMA state commit.
@@ -594,7 +586,6 @@ __global__ __launch_bounds__(256, 2) void decode_attend_kernel(DecodeArgs<bf16_t
     // L3 W = mean of the selected blocks' projected means, in rank order; the
     // selection is held in registers and every row load is issued up front
     // (rows of unfilled slots are read at block 0 and not added).
-    const int nkv = 2 * a.kvw;
     int blk[RMAX], cnt = 0;
 #pragma unroll
     for (int i = 0; i < RMAX; ++i) {
@@ -688,13 +679,15 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs<
 
 hipError_t decode_inputs_bf16(const DecodeArgs<bf16_t>& a, hipStream_t s) {
   const int per_wg = 4 * kGemvCols;
-  const int grid = (a.qw + per_wg - 1) / per_wg + (2 * a.kvw + per_wg - 1) / per_wg + a.n_slices * a.B;
+  const int grid = (a.qw + per_wg - 1) / per_wg + a.n_slices * a.B;
   hipLaunchKernelGGL(decode_inputs_kernel, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t decode_attend_bf16(const DecodeArgs<bf16_t>& a, hipStream_t s) {
-  const int grid = (a.r + 3) / 4 + a.B + a.n_chunks * a.G * a.n_hb * a.B;
+  const int per_wg = 4 * kGemvCols;
+  const int grid = (a.r + 3) / 4 + (2 * a.kvw + per_wg - 1) / per_wg + a.B +
+                   a.n_chunks * a.G * a.n_hb * a.B;
   if (a.dh == 128) {
     if (a.R <= 16)
       hipLaunchKernelGGL((decode_attend_kernel<128, 16>), dim3(grid), dim3(256), 0, s, a);
