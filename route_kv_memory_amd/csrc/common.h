@@ -129,6 +129,23 @@ __device__ __forceinline__ void store4(float* p, const float* v) {
   *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at ``lds`` + 16*l (``lds`` must be the same for the whole wave).  A plain
+// device function, so that kernel templates using it keep their host stubs.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void global_load_lds16(const void* src, lds_void_t* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
+// s_waitcnt immediate that waits until at most N vector-memory operations of
+// the wave are outstanding (expcnt and lgkmcnt left at their maxima): vmcnt
+// occupies bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
+template <int N>
+constexpr int kVmcntPending() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  return (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+
 // Raw buffer resource over [base, base + bytes): 16-byte loads through it
 // return zeros for any part outside the range, with no memory access there.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {

@@ -7,7 +7,7 @@
 // mean of x over tokens [b*Bs, (b+1)*Bs).
 //
 // Chunked scan, channel-parallel and coalesced: a thread owns 4 adjacent
-// channels, a workgroup 512 channels of one 64-token chunk.
+// channels (8 in pass 1), a workgroup 512 (1024) channels of one 64-token chunk.
 //   pass 1  each chunk's local result from a zero start: the EMA end value and
 //           the block-sum tail (sum since the chunk's last block end);
 //   pass 2  per channel, a sequential scan over chunks turns those into the
@@ -23,6 +23,22 @@
 namespace mka {
 
 constexpr int kEmaThreads = 128, kEmaVec = 4, kEmaSlab = kEmaThreads * kEmaVec;
+constexpr int kEmaUnroll = 8, kEmaBatch = 16;
+
+// 8 consecutive values at p as floats, loaded unconditionally (a guarded load
+// would be waited for on its own); the upper 4 count only when ``hi`` (the
+// row has them).  bf16 rows have D % 64 == 0, so all 8 always exist.
+__device__ __forceinline__ void load8(const bf16_t* p, bool, float* out) {
+  Vec16<bf16_t>::load(p, out);
+}
+__device__ __forceinline__ void load8(const float* p, bool hi, float* out) {
+  load4(p, out);
+  load4(p + (hi ? 4 : 0), out + 4);
+  if (!hi) out[4] = out[5] = out[6] = out[7] = 0.f;
+}
+
+// Pass 1 takes 8 channels per thread (16-byte loads of bf16 rows).
+constexpr int kEma1Vec = 8, kEma1Slab = kEmaThreads * kEma1Vec;
 
 template <typename T>
 __global__ __launch_bounds__(kEmaThreads) void ema_pass1(const T* __restrict__ x, int seq, int D,
@@ -31,32 +47,50 @@ __global__ __launch_bounds__(kEmaThreads) void ema_pass1(const T* __restrict__ x
                                                           float* __restrict__ agg_a,
                                                           int n_chunks) {
   const int c = blockIdx.x, b = blockIdx.z;
-  const int ch = blockIdx.y * kEmaSlab + threadIdx.x * kEmaVec;
+  const int ch = blockIdx.y * kEma1Slab + threadIdx.x * kEma1Vec;
   if (ch >= D) return;
+  const bool hi = ch + 4 < D;
   const int t0 = c * kEmaChunk, t1 = min(t0 + kEmaChunk, seq);
-  float s[4] = {0.f, 0.f, 0.f, 0.f}, a[4] = {0.f, 0.f, 0.f, 0.f};
+  float s[8] = {}, a[8] = {};
   const T* xp = x + (static_cast<int64_t>(b) * seq + t0) * D + ch;
-  for (int t = t0; t < t1; ++t, xp += D) {
-    float xv[4];
-    load4(xp, xv);
+  int in_blk = static_cast<int>((pos0 + t0) % block);  // tokens of the current block so far
+  // kEmaUnroll tokens' loads are issued before their (sequential) updates
+  for (int tb = t0; tb < t1; tb += kEmaUnroll, xp += kEmaUnroll * static_cast<int64_t>(D)) {
+    float xv[kEmaUnroll][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s[i] = fmaf(beta, s[i], omb * xv[i]);
-      a[i] += xv[i];
+    for (int u = 0; u < kEmaUnroll; ++u)  // rows past the chunk re-read its last row (unused)
+      load8(xp + min(u, t1 - 1 - tb) * static_cast<int64_t>(D), hi, xv[u]);
+#pragma unroll
+    for (int u = 0; u < kEmaUnroll; ++u) {
+      if (tb + u < t1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          s[i] = fmaf(beta, s[i], omb * xv[u][i]);
+          a[i] += xv[u][i];
+        }
+        if (++in_blk == block) {
+          in_blk = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) a[i] = 0.f;
+        }
+      }
     }
-    if ((pos0 + t + 1) % block == 0) a[0] = a[1] = a[2] = a[3] = 0.f;
   }
   const int64_t o = (static_cast<int64_t>(b) * n_chunks + c) * D + ch;
   store4(agg_s + o, s);
   store4(agg_a + o, a);
+  if (hi) {
+    store4(agg_s + o + 4, s + 4);
+    store4(agg_a + o + 4, a + 4);
+  }
 }
 
 // One thread per (batch, channel): exclusive scan of the chunk results, in place.
-__global__ __launch_bounds__(256) void ema_pass2(float* __restrict__ agg_s, float* __restrict__ agg_a,
+__global__ __launch_bounds__(64) void ema_pass2(float* __restrict__ agg_s, float* __restrict__ agg_a,
                                                  const float* __restrict__ state_in,
                                                  const float* __restrict__ acc_in, int B, int D,
-                                                 int seq, int64_t pos0, int block, float beta_L,
-                                                 int n_chunks) {
+                                                 int seq, int64_t pos0, int pos_rem, int block,
+                                                 float beta_L, int n_chunks) {
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= B * D) return;
   const int b = e / D, ch = e - b * D;
@@ -65,16 +99,33 @@ __global__ __launch_bounds__(256) void ema_pass2(float* __restrict__ agg_s, floa
   float cs = pos0 == 0 ? 0.f : state_in[e], ca = pos0 % block == 0 ? 0.f : acc_in[e];
   float* ps = agg_s + static_cast<int64_t>(b) * n_chunks * D + ch;
   float* pa = agg_a + static_cast<int64_t>(b) * n_chunks * D + ch;
-  for (int c = 0; c < n_chunks; ++c) {
-    const int64_t o = static_cast<int64_t>(c) * D;
-    const float sc = ps[o], ac = pa[o];
-    ps[o] = cs;
-    pa[o] = ca;
-    const int64_t t0 = pos0 + static_cast<int64_t>(c) * kEmaChunk;
-    const int64_t t1 = pos0 + min((c + 1) * kEmaChunk, seq);
-    const bool closes = (t1 / block) > (t0 / block);  // a block ends in [t0, t1)
-    cs = fmaf(beta_L, cs, sc);
-    ca = closes ? ac : ca + ac;
+  // position of the next token within its block, kept without divisions
+  int rem = pos_rem;
+  const int step = kEmaChunk % block;
+  // chunk results are loaded kEmaBatch at a time before the sequential carry
+  for (int c0 = 0; c0 < n_chunks; c0 += kEmaBatch) {
+    float sc[kEmaBatch], ac[kEmaBatch];
+#pragma unroll
+    for (int u = 0; u < kEmaBatch; ++u) {
+      const int64_t o = static_cast<int64_t>(min(c0 + u, n_chunks - 1)) * D;
+      sc[u] = ps[o];
+      ac[u] = pa[o];
+    }
+#pragma unroll
+    for (int u = 0; u < kEmaBatch; ++u) {
+      const int c = c0 + u;
+      if (c < n_chunks) {
+        const int64_t o = static_cast<int64_t>(c) * D;
+        ps[o] = cs;
+        pa[o] = ca;
+        const int len = min((c + 1) * kEmaChunk, seq) - c * kEmaChunk;
+        const bool closes = rem + len >= block;  // a block ends inside this chunk
+        cs = fmaf(beta_L, cs, sc[u]);
+        ca = closes ? ac[u] : ca + ac[u];
+        rem += step;
+        if (rem >= block) rem -= block;
+      }
+    }
   }
 }
 
@@ -94,24 +145,35 @@ __global__ __launch_bounds__(kEmaThreads) void ema_pass3(
   if (carry_chunks || pos0 % block != 0) load4(carry_a + co, a);
   const T* xp = x + (static_cast<int64_t>(b) * seq + t0) * D + ch;
   float* lp = l2 + (static_cast<int64_t>(b) * seq + t0) * D + ch;
-  for (int t = t0; t < t1; ++t, xp += D, lp += D) {
-    float xv[4];
-    load4(xp, xv);
+  int in_blk = static_cast<int>((pos0 + t0) % block);
+  int64_t blk = (pos0 + t0) / block;  // block of the next token
+  for (int tb = t0; tb < t1; tb += kEmaUnroll) {
+    float xv[kEmaUnroll][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s[i] = fmaf(beta, s[i], omb * xv[i]);
-      a[i] += xv[i];
-    }
-    store4(lp, s);
-    const int64_t p = pos0 + t;
-    if ((p + 1) % block == 0) {
-      const int64_t blk = (p + 1) / block - 1;
-      float m[4];
+    for (int u = 0; u < kEmaUnroll; ++u)  // rows past the chunk re-read its last row (unused)
+      load4(xp + min(u, t1 - 1 - tb) * static_cast<int64_t>(D), xv[u]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) m[i] = a[i] / static_cast<float>(block);
-      store4(means + (static_cast<int64_t>(b) * nb_cap + blk) * D + ch, m);
-      a[0] = a[1] = a[2] = a[3] = 0.f;
+    for (int u = 0; u < kEmaUnroll; ++u) {
+      if (tb + u < t1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          s[i] = fmaf(beta, s[i], omb * xv[u][i]);
+          a[i] += xv[u][i];
+        }
+        store4(lp + u * static_cast<int64_t>(D), s);
+        if (++in_blk == block) {
+          float m[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m[i] = a[i] / static_cast<float>(block);
+          store4(means + (static_cast<int64_t>(b) * nb_cap + blk) * D + ch, m);
+          a[0] = a[1] = a[2] = a[3] = 0.f;
+          in_blk = 0;
+          ++blk;
+        }
+      }
     }
+    xp += kEmaUnroll * static_cast<int64_t>(D);
+    lp += kEmaUnroll * static_cast<int64_t>(D);
   }
   if (c == n_chunks - 1) {
     store4(state_out + static_cast<int64_t>(b) * D + ch, s);
@@ -208,12 +270,15 @@ hipError_t ema_scan(const T* x, int B, int seq, int D, int64_t pos0, int block, 
   }
   float* agg_s = ws;
   float* agg_a = ws + static_cast<size_t>(B) * n_chunks * D;
-  hipLaunchKernelGGL(ema_pass1<T>, grid, dim3(kEmaThreads), 0, s, x, seq, D, pos0, block, beta, omb,
-                     agg_s, agg_a, n_chunks);
+  const dim3 grid1(n_chunks, (D + kEma1Slab - 1) / kEma1Slab, B);
+  hipLaunchKernelGGL(ema_pass1<T>, grid1, dim3(kEmaThreads), 0, s, x, seq, D, pos0, block, beta,
+                     omb, agg_s, agg_a, n_chunks);
   double bl = 1.0;
   for (int i = 0; i < kEmaChunk; ++i) bl *= static_cast<double>(beta);
-  hipLaunchKernelGGL(ema_pass2, dim3((B * D + 255) / 256), dim3(256), 0, s, agg_s, agg_a, state_io,
-                     acc_io, B, D, seq, pos0, block, static_cast<float>(bl), n_chunks);
+  // one channel per thread, 64-thread workgroups: the scan is spread over many CUs
+  hipLaunchKernelGGL(ema_pass2, dim3((B * D + 63) / 64), dim3(64), 0, s, agg_s, agg_a, state_io,
+                     acc_io, B, D, seq, pos0, static_cast<int>(pos0 % block), block,
+                     static_cast<float>(bl), n_chunks);
   hipLaunchKernelGGL(ema_pass3<T>, grid, dim3(kEmaThreads), 0, s, x, seq, D, pos0, block, beta, omb,
                      agg_s, agg_a, n_chunks, l2, means, nb_cap, state_io, acc_io, n_chunks);
   return hipGetLastError();

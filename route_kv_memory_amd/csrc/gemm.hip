@@ -5,23 +5,38 @@
 namespace mka {
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA GEMM.  Workgroup tile 256 (M) x BN (N) x 64 (K), BN = 128 with 4
-// waves or 256 with 8 waves; each wave owns 128 x 64 of C as 4 x 2 blocks of
-// MFMA 32x32x16, so a k-step reads 6 fragments for 8 MFMAs.  The MFMA computes
+// bf16 MFMA GEMM.  Workgroup tile 256 (M) x BN (N), 8 waves; each wave owns
+// 128 x BN/4 of C as 4 x BN/128 blocks of MFMA 32x32x16.  The MFMA computes
 // C^T blocks (B rows as its A operand), which leaves 4 consecutive output
 // columns of one output row in each lane: the epilogue stores 8 bytes per lane.
-// Operand tiles go through registers into double-buffered LDS (rows padded by
-// 16 bytes: the fragment reads of 16 consecutive rows hit distinct banks);
-// global reads are buffer loads whose range makes rows past M or N read zero.
+//
+// Operands stream global -> LDS directly (global_load_lds, 16 bytes per lane,
+// no registers) through a ring of STAGES k-slices of 32, so the loads of a
+// slice are issued STAGES-1 slices before it is used.  A row of a slice is 64
+// bytes (4 chunks of 16); chunk c of row r is stored at position
+// c ^ ((r >> 2) & 3), which keeps both the 1 KB contiguous LDS writes of a
+// load instruction and the 16-row fragment reads of the MFMA free of bank
+// conflicts.  Rows past M or N are read from the last valid row; their outputs
+// are not stored.
 // ---------------------------------------------------------------------------
+template <int BN>
+struct GemmCfg {
+  static constexpr int BM = 256, BK = 32, ROWB = BK * 2;  // bytes per row per slice
+  static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
+  static constexpr int SLICE = A_BYTES + B_BYTES;
+  static constexpr int STAGES = (144 * 1024) / SLICE;      // 4 for BN=256, 6 for BN=128
+  static constexpr int LOADS = SLICE / 1024 / 8;            // load instructions per wave per slice
+  static constexpr int NB = BN / 128;                       // MFMA blocks per wave in N
+};
+
 template <int BN, class Epi>
-__global__ __launch_bounds__(BN * 2) void gemm_bf16_kernel(
+__global__ __launch_bounds__(512) void gemm_bf16_kernel(
     const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B0,
     const bf16_t* __restrict__ B1, int n_split, int M, int N, int K, Epi epi) {
-  constexpr int BM = 256, BK = kGemmBK, P = BK + 8, NT = BN * 2;
-  constexpr int ACH = BM * BK / 8 / NT, BCH = BN * BK / 8 / NT;  // 16-byte chunks per thread
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * P];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * P];
+  using C = GemmCfg<BN>;
+  constexpr int BM = C::BM, BK = C::BK, ROWB = C::ROWB, STAGES = C::STAGES, NB = C::NB;
+  static_assert(C::LOADS * 8 * 1024 == C::SLICE, "slice must split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[STAGES * C::SLICE];
 
   const int tiles_n = (N + BN - 1) / BN;
   const int tiles = tiles_n * ((M + BM - 1) / BM);
@@ -32,82 +47,77 @@ __global__ __launch_bounds__(BN * 2) void gemm_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1, h = lane >> 5, l32 = lane & 31;
 
-  // A rows [m0, min(M, m0 + BM)) and B rows of this tile as buffer ranges.
-  const uint32_t a_rows = static_cast<uint32_t>(min(BM, M - m0));
-  const __amdgpu_buffer_rsrc_t ars =
-      make_rsrc(A + static_cast<int64_t>(m0) * lda, a_rows * static_cast<uint32_t>(lda) * 2);
-  // B rows come from b0 below n_split and b1 above; a tile never straddles
-  // n_split when n_split % BN == 0, otherwise rows are fetched one by one.
-  const bool straddle = n0 < n_split && n0 + BN > n_split;
-  const bf16_t* bbase = n0 < n_split ? B0 + static_cast<int64_t>(n0) * K
-                                     : B1 + static_cast<int64_t>(n0 - n_split) * K;
-  const int b_valid = min(BN, (n0 < n_split ? n_split : N) - n0);
-  const __amdgpu_buffer_rsrc_t brs =
-      make_rsrc(bbase, static_cast<uint32_t>(b_valid) * static_cast<uint32_t>(K) * 2);
-
-  u32x4 ra[ACH], rb[BCH];
-  auto gload = [&](int k0) {
+  // This lane's rows and byte offsets for each of its load instructions of a
+  // slice: instruction j of wave w covers 16 rows of A (first A_BYTES/1024
+  // instructions) or of B; lane l takes row 16*ri + l/4, chunk (l%4) ^ swizzle.
+  const bf16_t* src[C::LOADS];
+  int dst[C::LOADS];
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-      const int c = tid + NT * i, row = c >> 3, col = (c & 7) * 8;
-      ra[i] = buffer_load16(ars, static_cast<uint32_t>(row * lda + k0 + col) * 2);
+  for (int j = 0; j < C::LOADS; ++j) {
+    const int gi = wave * C::LOADS + j;  // instruction index within the slice
+    const bool is_a = gi < C::A_BYTES / 1024;
+    const int ri = is_a ? gi : gi - C::A_BYTES / 1024;
+    const int row = 16 * ri + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+    if (is_a) {
+      const int gm = min(m0 + row, M - 1);
+      src[j] = A + static_cast<int64_t>(gm) * lda + chunk * 8;
+    } else {
+      const int gn = min(n0 + row, N - 1);
+      src[j] = (gn < n_split ? B0 + static_cast<int64_t>(gn) * K
+                             : B1 + static_cast<int64_t>(gn - n_split) * K) + chunk * 8;
     }
+    dst[j] = (is_a ? 0 : C::A_BYTES) + ri * 1024;  // lane's 16 bytes land at +16*lane
+  }
+  auto issue = [&](int slice, int stage) {
+    unsigned char* base = lds + stage * C::SLICE;
 #pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-      const int c = tid + NT * i, row = c >> 3, col = (c & 7) * 8;
-      if (!straddle) {
-        rb[i] = buffer_load16(brs, static_cast<uint32_t>(row * K + k0 + col) * 2);
-      } else {
-        const int gn = n0 + row;
-        const bf16_t* br = gn < n_split ? B0 + static_cast<int64_t>(gn) * K
-                                        : B1 + static_cast<int64_t>(gn - n_split) * K;
-        rb[i] = gn < N ? *reinterpret_cast<const u32x4*>(br + k0 + col) : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-      const int c = tid + NT * i, row = c >> 3, col = (c & 7) * 8;
-      *reinterpret_cast<u32x4*>(&As[buf][row * P + col]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-      const int c = tid + NT * i, row = c >> 3, col = (c & 7) * 8;
-      *reinterpret_cast<u32x4*>(&Bs[buf][row * P + col]) = rb[i];
-    }
+    for (int j = 0; j < C::LOADS; ++j)
+      global_load_lds16(src[j] + slice * BK, (lds_void_t*)(base + dst[j]));
   };
 
-  // acc[i][j]: C^T block of output rows m0 + wm*128 + 32i .., columns n0 + wn*64 + 32j ..
-  f32x16 acc[4][2];
+  // acc[i][j]: C^T block of output rows m0 + wm*128 + 32i .., columns n0 + wn*(BN/4) + 32j ..
+  f32x16 acc[4][NB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
+
+  // fragment byte offset of row r, chunk c (16 bytes) within a slice operand
+  auto frag = [](int r, int c) { return r * ROWB + ((c ^ ((r >> 2) & 3)) << 4); };
 
   const int nk = K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue(s, s);
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+    // slice kt has landed once at most the STAGES-2 younger slices are pending
+    if (kt + STAGES - 2 < nk) {
+      __builtin_amdgcn_s_waitcnt(kVmcntPending<C::LOADS * (STAGES - 2)>());
+    } else {
+      __builtin_amdgcn_s_waitcnt(kVmcntPending<0>());
+    }
+    // Every wave's part of slice kt is in LDS (each waited for its own loads)
+    // and every wave is done reading slice kt-1 (its MFMAs consumed the
+    // reads).  A bare barrier: a fence here would wait for the prefetches too.
+    __builtin_amdgcn_s_barrier();
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+    const unsigned char* As = lds + (kt % STAGES) * C::SLICE;
+    const unsigned char* Bs = As + C::A_BYTES;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 fa[4], fb[2];
+      bf16x8 fa[4], fb[NB];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8*>(&As[buf][(wm * 128 + i * 32 + l32) * P + ks * 16 + 8 * h]);
+        fa[i] = *reinterpret_cast<const bf16x8*>(As + frag(wm * 128 + i * 32 + l32, 2 * ks + h));
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(wn * 64 + j * 32 + l32) * P + ks * 16 + 8 * h]);
+      for (int j = 0; j < NB; ++j)
+        fb[j] = *reinterpret_cast<const bf16x8*>(Bs + frag(wn * (BN / 4) + j * 32 + l32, 2 * ks + h));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(fb[j], fa[i], acc[i][j]);
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma32x32x16(fb[j], fa[i], acc[i][j]);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
   }
 
   // Lane holds output row m = ... + l32 and columns n = ... + 8*(r/4) + 4h + (r%4).
@@ -116,10 +126,10 @@ __global__ __launch_bounds__(BN * 2) void gemm_bf16_kernel(
     const int m = m0 + wm * 128 + i * 32 + l32;
     if (m >= M) continue;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const int n = n0 + wn * 64 + j * 32 + 8 * rq + 4 * h;
+        const int n = n0 + wn * (BN / 4) + j * 32 + 8 * rq + 4 * h;
         const float v[4] = {acc[i][j][4 * rq], acc[i][j][4 * rq + 1], acc[i][j][4 * rq + 2],
                             acc[i][j][4 * rq + 3]};
         epi.store4(m, n, v, N);
@@ -136,7 +146,7 @@ hipError_t gemm_bf16(const bf16_t* a, int lda, const bf16_t* b0, const bf16_t* b
                        b1, n_split, M, N, K, epi);
   } else {
     const int tiles = ((N + 127) / 128) * ((M + 255) / 256);
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, Epi>), dim3(tiles), dim3(256), 0, s, a, lda, b0, b1,
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, Epi>), dim3(tiles), dim3(512), 0, s, a, lda, b0, b1,
                        n_split, M, N, K, epi);
   }
   return hipGetLastError();

@@ -130,9 +130,17 @@ __global__ __launch_bounds__(256) void simhash_finalize_kernel(const double* __r
   const int64_t e = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (e >= static_cast<int64_t>(B) * rows) return;
   const int b = static_cast<int>(e / rows), row = static_cast<int>(e - static_cast<int64_t>(b) * rows);
+  // partials loaded 8 at a time, added in split order
   double p = 0.0;
-  for (int s = 0; s < nsplit; ++s)
-    p += part[((static_cast<int64_t>(s) * B + b) * rows + row) * 64 + lane];
+  for (int s0 = 0; s0 < nsplit; s0 += 8) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = part[((static_cast<int64_t>(min(s0 + u, nsplit - 1)) * B + b) * rows + row) * 64 + lane];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < nsplit) p += v[u];
+  }
   const uint64_t code = __ballot(lane < nbits && p > 0.0);
   if (lane == 0) codes[b * c_bstride + row] = code;
 }
