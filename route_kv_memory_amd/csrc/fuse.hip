@@ -10,14 +10,13 @@
 
 namespace mka {
 
-template <typename T>
+template <typename T, int RMAX>
 __global__ __launch_bounds__(256) void fuse_mix_kernel(const T* __restrict__ x,
                                                        const float* __restrict__ l2,
                                                        const float* __restrict__ means, int nb_cap,
                                                        const int32_t* __restrict__ idx,
                                                        const float* __restrict__ lam, int seq, int D,
                                                        int R, T* __restrict__ xf) {
-  constexpr int RMAX = 32;
   const int64_t row = blockIdx.x;  // b * seq + t
   const int b = static_cast<int>(row / seq);
   const int ch = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
@@ -31,24 +30,25 @@ __global__ __launch_bounds__(256) void fuse_mix_kernel(const T* __restrict__ x,
   float xv[4], sv[4];
   load4(x + row * D + ch, xv);
   load4(l2 + row * D + ch, sv);
+  // Every retrieved row is loaded unconditionally (unfilled slots read block 0
+  // and are not added), so the loads are in flight together; rank order.
+  float m[RMAX][4];
+#pragma unroll
+  for (int i = 0; i < RMAX; ++i) load4(mb + static_cast<int64_t>(max(blk[i], 0)) * D, m[i]);
   float l3[4] = {0.f, 0.f, 0.f, 0.f};
   int cnt = 0;
-  // Retrieved rows in rank order; the loads are independent of each other.
 #pragma unroll
   for (int i = 0; i < RMAX; ++i) {
-    if (blk[i] >= 0) {
-      float m[4];
-      load4(mb + static_cast<int64_t>(blk[i]) * D, m);
+    const bool on = blk[i] >= 0;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) l3[k] += m[k];
-      ++cnt;
-    }
+    for (int k = 0; k < 4; ++k) l3[k] += on ? m[i][k] : 0.f;
+    cnt += on;
   }
   float out[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const float m = cnt ? l3[k] / static_cast<float>(cnt) : 0.f;
-    out[k] = l1w * xv[k] + l2w * sv[k] + l3w * m;
+    const float mean = cnt ? l3[k] / static_cast<float>(cnt) : 0.f;
+    out[k] = l1w * xv[k] + l2w * sv[k] + l3w * mean;
   }
   store4(xf + row * D + ch, out);
 }
@@ -61,8 +61,18 @@ hipError_t fuse_mix(const T* x, const float* l2, const float* means, int nb_cap,
   const int threads = static_cast<int64_t>(B) * seq <= 8 ? 64 : 256;
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(B) * seq),
                   (D + 4 * threads - 1) / (4 * threads));
-  hipLaunchKernelGGL(fuse_mix_kernel<T>, grid, dim3(threads), 0, s, x, l2, means, nb_cap, idx, lam,
-                     seq, D, R, xf);
+  if (R <= 4)
+    hipLaunchKernelGGL((fuse_mix_kernel<T, 4>), grid, dim3(threads), 0, s, x, l2, means, nb_cap,
+                       idx, lam, seq, D, R, xf);
+  else if (R <= 8)
+    hipLaunchKernelGGL((fuse_mix_kernel<T, 8>), grid, dim3(threads), 0, s, x, l2, means, nb_cap,
+                       idx, lam, seq, D, R, xf);
+  else if (R <= 16)
+    hipLaunchKernelGGL((fuse_mix_kernel<T, 16>), grid, dim3(threads), 0, s, x, l2, means, nb_cap,
+                       idx, lam, seq, D, R, xf);
+  else
+    hipLaunchKernelGGL((fuse_mix_kernel<T, 32>), grid, dim3(threads), 0, s, x, l2, means, nb_cap,
+                       idx, lam, seq, D, R, xf);
   return hipGetLastError();
 }
 

@@ -19,29 +19,41 @@ namespace mka {
 // conflicts.  Rows past M or N are read from the last valid row; their outputs
 // are not stored.
 // ---------------------------------------------------------------------------
-template <int BN>
+template <int BN, int NW>
 struct GemmCfg {
   static constexpr int BM = 256, BK = 32, ROWB = BK * 2;  // bytes per row per slice
   static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
   static constexpr int SLICE = A_BYTES + B_BYTES;
-  static constexpr int STAGES = (144 * 1024) / SLICE;      // 4 for BN=256, 6 for BN=128
-  static constexpr int LOADS = SLICE / 1024 / 8;            // load instructions per wave per slice
-  static constexpr int NB = BN / 128;                       // MFMA blocks per wave in N
+  static constexpr int STAGES = (160 * 1024) / SLICE;      // 5 for BN=256, 6 for BN=128
+  static constexpr int LOADS = SLICE / 1024 / NW;           // load instructions per wave per slice
+  static constexpr int WN = BN / (NW / 2);                  // wave tile: 128 x WN
+  static constexpr int NB = WN / 32;                        // MFMA blocks per wave in N
 };
 
-template <int BN, class Epi>
-__global__ __launch_bounds__(512) void gemm_bf16_kernel(
+template <int BN, int NW, class Epi>
+__global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(
     const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B0,
     const bf16_t* __restrict__ B1, int n_split, int M, int N, int K, Epi epi) {
-  using C = GemmCfg<BN>;
+  using C = GemmCfg<BN, NW>;
   constexpr int BM = C::BM, BK = C::BK, ROWB = C::ROWB, STAGES = C::STAGES, NB = C::NB;
-  static_assert(C::LOADS * 8 * 1024 == C::SLICE, "slice must split evenly over the waves");
+  constexpr int WN = C::WN;
+  static_assert(C::LOADS * NW * 1024 == C::SLICE, "slice must split evenly over the waves");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[STAGES * C::SLICE];
 
-  const int tiles_n = (N + BN - 1) / BN;
-  const int tiles = tiles_n * ((M + BM - 1) / BM);
-  const int item = xcd_contiguous(blockIdx.x, tiles);
-  const int tm = item / tiles_n, tn = item % tiles_n;
+  const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
+  int tm, tn;
+  if (tiles_m % 4 == 0 && tiles_n % 2 == 0) {
+    // Workgroups reach the 8 XCDs round-robin; XCD x takes the block of tiles
+    // rows [x/2 * tiles_m/4, +tiles_m/4) x columns [x%2 * tiles_n/2, +tiles_n/2),
+    // so its concurrent tiles share few A and B panels in its L2.
+    const int xcd = blockIdx.x % 8, local = blockIdx.x / 8, bn = tiles_n / 2;
+    tm = (xcd >> 1) * (tiles_m / 4) + local / bn;
+    tn = (xcd & 1) * bn + local % bn;
+  } else {
+    const int item = xcd_contiguous(blockIdx.x, tiles_n * tiles_m);
+    tm = item / tiles_n;
+    tn = item % tiles_n;
+  }
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -76,7 +88,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(
       global_load_lds16(src[j] + slice * BK, (lds_void_t*)(base + dst[j]));
   };
 
-  // acc[i][j]: C^T block of output rows m0 + wm*128 + 32i .., columns n0 + wn*(BN/4) + 32j ..
+  // acc[i][j]: C^T block of output rows m0 + wm*128 + 32i .., columns n0 + wn*WN + 32j ..
   f32x16 acc[4][NB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -112,7 +124,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(
         fa[i] = *reinterpret_cast<const bf16x8*>(As + frag(wm * 128 + i * 32 + l32, 2 * ks + h));
 #pragma unroll
       for (int j = 0; j < NB; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8*>(Bs + frag(wn * (BN / 4) + j * 32 + l32, 2 * ks + h));
+        fb[j] = *reinterpret_cast<const bf16x8*>(Bs + frag(wn * WN + j * 32 + l32, 2 * ks + h));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -129,7 +141,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const int n = n0 + wn * (BN / 4) + j * 32 + 8 * rq + 4 * h;
+        const int n = n0 + wn * WN + j * 32 + 8 * rq + 4 * h;
         const float v[4] = {acc[i][j][4 * rq], acc[i][j][4 * rq + 1], acc[i][j][4 * rq + 2],
                             acc[i][j][4 * rq + 3]};
         epi.store4(m, n, v, N);
@@ -137,17 +149,19 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(
   }
 }
 
+constexpr int kGemmWaves256 = 8;
+
 template <class Epi>
 hipError_t gemm_bf16(const bf16_t* a, int lda, const bf16_t* b0, const bf16_t* b1, int n_split,
                      int M, int N, int K, const Epi& epi, hipStream_t s) {
   const int tiles256 = ((N + 255) / 256) * ((M + 255) / 256);
   if (tiles256 >= 256) {
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, Epi>), dim3(tiles256), dim3(512), 0, s, a, lda, b0,
-                       b1, n_split, M, N, K, epi);
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, kGemmWaves256, Epi>), dim3(tiles256),
+                       dim3(kGemmWaves256 * 64), 0, s, a, lda, b0, b1, n_split, M, N, K, epi);
   } else {
     const int tiles = ((N + 127) / 128) * ((M + 255) / 256);
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, Epi>), dim3(tiles), dim3(512), 0, s, a, lda, b0, b1,
-                       n_split, M, N, K, epi);
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 8, Epi>), dim3(tiles), dim3(512), 0, s, a, lda, b0,
+                       b1, n_split, M, N, K, epi);
   }
   return hipGetLastError();
 }

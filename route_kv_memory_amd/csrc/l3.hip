@@ -62,19 +62,32 @@ __global__ __launch_bounds__(256) void simhash_mfma_kernel(
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = f64x4{0.0, 0.0, 0.0, 0.0};
   const int li = lane & 15, lk = lane >> 4;
-  for (int k0 = k_begin; k0 < k_end; k0 += kHashKT) {
+  // Tile loads are unconditional (rows and channels past the ends read a
+  // valid address and are replaced by zero), and tile k+1 is loaded into
+  // registers while tile k is multiplied.
+  f32x4 ra[4], rp[4];
+  auto load_tile = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = tid + 256 * i, r = e >> 4, c = (e & 15) * 4;  // 64 rows x 16 float4
-      f32x4 a = {0.f, 0.f, 0.f, 0.f}, p = {0.f, 0.f, 0.f, 0.f};
-      if (row0 + r < rows && k0 + c < k_end)
-        a = *reinterpret_cast<const f32x4*>(vb + static_cast<int64_t>(row0 + r) * D + k0 + c);
-      if (r < nbits && k0 + c < k_end)
-        p = *reinterpret_cast<const f32x4*>(P + static_cast<int64_t>(r) * D + k0 + c);
-      *reinterpret_cast<f32x4*>(&Vs[r * kHashPitch + c]) = a;
-      *reinterpret_cast<f32x4*>(&Ps[r * kHashPitch + c]) = p;
+      const bool kin = k0 + c < k_end;
+      const int kc = kin ? k0 + c : k_begin;
+      ra[i] = *reinterpret_cast<const f32x4*>(vb + static_cast<int64_t>(min(row0 + r, rows - 1)) * D + kc);
+      rp[i] = *reinterpret_cast<const f32x4*>(P + static_cast<int64_t>(min(r, nbits - 1)) * D + kc);
+      if (!(row0 + r < rows && kin)) ra[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (!(r < nbits && kin)) rp[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  if (k_begin < k_end) load_tile(k_begin);
+  for (int k0 = k_begin; k0 < k_end; k0 += kHashKT) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 256 * i, r = e >> 4, c = (e & 15) * 4;
+      *reinterpret_cast<f32x4*>(&Vs[r * kHashPitch + c]) = ra[i];
+      *reinterpret_cast<f32x4*>(&Ps[r * kHashPitch + c]) = rp[i];
     }
     __syncthreads();
+    if (k0 + kHashKT < k_end) load_tile(k0 + kHashKT);
 #pragma unroll 4
     for (int kk = 0; kk < kHashKT; kk += 4) {
       const double a = Vs[(wave * 16 + li) * kHashPitch + kk + lk];
@@ -365,18 +378,19 @@ __global__ __launch_bounds__(256) void block_kv_kernel(const float* __restrict__
     float wv[NC][V];
 #pragma unroll
     for (int c = 0; c < NC; ++c) Vec16<T>::load(w[c] + k, wv[c]);
+    // the block rows are loaded unconditionally (past the range: the last
+    // block again, not stored) so the loads are in flight together
+    float mv[NB][V];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      if (j < nb) {
-        float mv[V];
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int i = 0; i < V; i += 4) load4(mrow + static_cast<int64_t>(j) * D + k + i, mv + i);
+      for (int i = 0; i < V; i += 4) load4(mrow + static_cast<int64_t>(min(j, nb - 1)) * D + k + i, mv[j] + i);
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
-          for (int i = 0; i < V; ++i) acc[c][j] = fmaf(mv[i], wv[c][i], acc[c][j]);
-      }
-    }
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[c][j] = fmaf(mv[j][i], wv[c][i], acc[c][j]);
   }
 #pragma unroll
   for (int c = 0; c < NC; ++c)
