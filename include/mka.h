@@ -17,11 +17,12 @@
  *  - Pointers are device pointers unless stated; ``stream`` is a hipStream_t
  *    (NULL = the default stream).  Every call is asynchronous on ``stream``.
  *  - The caller allocates and owns every buffer (inputs, outputs, state,
- *    workspace).  The library allocates no device memory, keeps no pointer
- *    after a call returns and holds no state besides a thread-local string
- *    describing the last HIP error.  Calls on different streams are
- *    independent; calls that write the same buffers must be ordered by the
- *    caller.
+ *    workspace).  The library allocates no device memory and keeps no pointer
+ *    after a call returns.  Its only state is a thread-local string describing
+ *    the last HIP error and, per device, one auxiliary stream with three events
+ *    that mka_prefill creates on its first call there and keeps until the
+ *    process ends.  Calls on different streams are independent; calls that
+ *    write the same buffers must be ordered by the caller.
  *  - Arrays are dense, row-major, contiguous.  Token-major activations are
  *    [B, seq, width]; the fused KV cache is head-major [B, G, t_cap, dh].
  *    Weight matrices are stored [out, in] (each output's weights contiguous).
@@ -194,8 +195,12 @@ int mka_attn_decode(const mka_dims* d, const void* q, const void* k_cache,
                     void* ws, size_t ws_bytes, void* stream);
 
 /* Composite: the whole layer over a prompt at positions pos0 .. pos0+seq-1 (the
- * calls above in order: route, ema_scan, l3_index and l3_block_kv of the blocks
- * completed here, l3_retrieve, fuse_kv_proj, attn_prefill).  Intermediates go to the caller's
+ * calls above: route, ema_scan, l3_index and l3_block_kv of the blocks completed
+ * here, l3_retrieve, fuse_kv_proj, attn_prefill).  ema_scan, l3_index and
+ * l3_block_kv need only x, so they run on the device's auxiliary stream
+ * (forked from ``stream`` and joined back into it with events) beside route;
+ * completion is signalled on ``stream`` alone.  Concurrent calls on one device
+ * serialise their enqueueing.  Intermediates go to the caller's
  * buffers, so the call both answers the prompt and leaves the decode state.
  *   weights: w_q, w_k, w_v, w_r1, w_r2 (dtype), proj (f32), as above
  *   state: state_io, block_acc_io [B, D] f32; block_means [B, nb_cap, D] f32;

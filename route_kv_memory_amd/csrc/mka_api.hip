@@ -5,7 +5,10 @@
 #include <initializer_list>
 #include <cstdio>
 #include <cstring>
+#include <memory>
+#include <mutex>
 #include <type_traits>
+#include <unordered_map>
 
 #include "../../include/mka.h"
 #include "decode.h"
@@ -301,6 +304,55 @@ bool ptrs_ok(std::initializer_list<const void*> ps) {
 
 constexpr int64_t kMaxDecodeCache = static_cast<int64_t>(1) << 26;  // rows
 
+// Per-device auxiliary stream and fork/join/done events of mka_prefill, created on
+// a device's first prefill and kept until the process ends.  Enqueueing one
+// prefill holds the device's lock, so concurrent callers cannot interleave
+// their fork/join records.
+struct Aux {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, done = nullptr;
+  std::mutex lock;
+};
+
+Aux* aux_for_current_device(int* rc) {
+  static std::mutex table_lock;
+  static std::unordered_map<int, std::unique_ptr<Aux>> table;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *rc = hip_fail("prefill/aux", e);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> g(table_lock);
+  auto it = table.find(dev);
+  if (it != table.end()) return it->second.get();
+  auto a = std::make_unique<Aux>();
+  if ((e = hipStreamCreateWithFlags(&a->stream, hipStreamNonBlocking)) != hipSuccess ||
+      (e = hipEventCreateWithFlags(&a->fork, hipEventDisableTiming)) != hipSuccess ||
+      (e = hipEventCreateWithFlags(&a->join, hipEventDisableTiming)) != hipSuccess ||
+      (e = hipEventCreateWithFlags(&a->done, hipEventDisableTiming)) != hipSuccess) {
+    *rc = hip_fail("prefill/aux", e);
+    return nullptr;
+  }
+  Aux* p = a.get();
+  table.emplace(dev, std::move(a));
+  return p;
+}
+
+// Workspace of a prefill: the EMA scan and block index run on the auxiliary
+// stream beside the query product, so the two streams have disjoint regions:
+// [EMA scan, index | route, retrieval, fusion].
+size_t prefill_chain_ws(const mka_dims* d) {
+  const size_t w = ema_ws(d), wi = index_ws(d, d->seq / d->block + 1);
+  return w > wi ? w : wi;
+}
+size_t prefill_main_ws(const mka_dims* d) {
+  size_t w = fuse_ws(d);
+  if (route_ws(d) > w) w = route_ws(d);
+  if (retrieve_ws(d) > w) w = retrieve_ws(d);
+  return w;
+}
+
 // Workspace of a decode step.  bf16: the attention partials over rows [0, pos),
 // the router hidden layer, the partial key projections and the three
 // projected rows (x, L2, L3) of the new K/V row; float32: hidden, partial key
@@ -353,15 +405,8 @@ size_t mka_workspace_bytes(const mka_dims* d, int op, int64_t cache_len) {
     case MKA_OP_INDEX: return index_ws(d, cache_len);
     case MKA_OP_ROUTE: return route_ws(d);
     case MKA_OP_ATTN_DECODE: return cache_len > 0 ? decode_ws(d, cache_len) : 0;
-    case MKA_OP_PREFILL: {
-      // blocks completed by a call at any pos0: at most seq / block + 1
-      size_t w = ema_ws(d);
-      if (fuse_ws(d) > w) w = fuse_ws(d);
-      if (retrieve_ws(d) > w) w = retrieve_ws(d);
-      if (route_ws(d) > w) w = route_ws(d);
-      if (index_ws(d, d->seq / d->block + 1) > w) w = index_ws(d, d->seq / d->block + 1);
-      return w;
-    }
+    case MKA_OP_PREFILL:  // blocks completed by a call at any pos0: at most seq / block + 1
+      return prefill_chain_ws(d) + prefill_main_ws(d);
     case MKA_OP_DECODE_STEP:
       return d->seq == 1 && cache_len > 0 ? decode_layout(d, cache_len).total : 0;
     default: return 0;
@@ -527,23 +572,43 @@ int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weight
   hipStream_t s = static_cast<hipStream_t>(stream);
   int64_t first, n;
   completed_blocks(d, pos0, &first, &n);
-  if ((rc = do_route(d, x, w->w_q, w->w_r1, w->w_r2, out->q, out->lambda, ws, s))) return rc;
+  char* ws_chain = static_cast<char*>(ws);
+  char* ws_main = ws_chain + prefill_chain_ws(d);
+  // The EMA scan and the block codes need only x and use no LDS, so they run
+  // on the auxiliary stream beside the query product (which fills every CU's
+  // LDS) and the block projections, needed only by later decode steps, follow
+  // them there; the retrieval joins the scan and codes after the router.  (The
+  // retrieval's fp64 products need LDS: beside the query product they would
+  // get only the CUs of its last tile round.)
+  Aux* aux = aux_for_current_device(&rc);
+  if (aux == nullptr) return rc;
+  std::lock_guard<std::mutex> guard(aux->lock);
+  hipStream_t s2 = aux->stream;
+  MKA_LAUNCH("prefill/fork", hipEventRecord(aux->fork, s));
+  MKA_LAUNCH("prefill/fork", hipStreamWaitEvent(s2, aux->fork, 0));
   if ((rc = do_ema(d, x, pos0, st->ema_state, st->block_acc, out->l2, st->block_means, st->nb_cap,
-                   ws, s)))
+                   ws_chain, s2)))
     return rc;
   if ((rc = do_index(d, st->block_means, st->nb_cap, static_cast<int>(first), static_cast<int>(n),
-                     w->proj, st->block_hash, ws, s)))
+                     w->proj, st->block_hash, ws_chain, s2)))
     return rc;
+  MKA_LAUNCH("prefill/join", hipEventRecord(aux->join, s2));
   if ((rc = do_block_kv(d, st->block_means, st->nb_cap, static_cast<int>(first),
-                        static_cast<int>(n), w->w_k, w->w_v, st->block_kv, s)))
+                        static_cast<int>(n), w->w_k, w->w_v, st->block_kv, s2)))
     return rc;
+  MKA_LAUNCH("prefill/join", hipEventRecord(aux->done, s2));
+  if ((rc = do_route(d, x, w->w_q, w->w_r1, w->w_r2, out->q, out->lambda, ws_main, s))) return rc;
+  MKA_LAUNCH("prefill/join", hipStreamWaitEvent(s, aux->join, 0));
   if ((rc = do_retrieve(d, out->l2, w->proj, st->block_hash, st->nb_cap, pos0, out->key, out->idx,
-                        ws, s)))
+                        ws_main, s)))
     return rc;
   if ((rc = do_fuse_kv(d, x, out->l2, st->block_means, st->nb_cap, out->idx, out->lambda, w->w_k,
-                       w->w_v, st->k_cache, st->v_cache, pos0, st->t_cap, ws, s)))
+                       w->w_v, st->k_cache, st->v_cache, pos0, st->t_cap, ws_main, s)))
     return rc;
-  return do_attn_prefill(d, out->q, st->k_cache, st->v_cache, st->t_cap, pos0, out->o, s);
+  if ((rc = do_attn_prefill(d, out->q, st->k_cache, st->v_cache, st->t_cap, pos0, out->o, s)))
+    return rc;
+  MKA_LAUNCH("prefill/join", hipStreamWaitEvent(s, aux->done, 0));
+  return MKA_OK;
 }
 
 int mka_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_weights* w,
