@@ -25,18 +25,19 @@ __device__ __forceinline__ int kperm(int r) {
 
 
 // ---------------------------------------------------------------------------
-// Prefill, bf16.  Workgroup = 4 waves = 128 query rows of one head; K/V tiles
+// Prefill, bf16.  Workgroup = NW waves = 32*NW query rows of one head; K/V tiles
 // of 64 keys double-buffered in LDS.  Work order: units (query block, batch,
 // KV group) heaviest first; the H/G heads of a unit are consecutive slots of
 // one XCD so they read the same K/V tiles through that XCD's L2.
 // ---------------------------------------------------------------------------
-template <int DH>
-__global__ __launch_bounds__(256, 2) void attn_prefill_bf16_kernel(
+template <int DH, int NW>
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
     bf16_t* __restrict__ O, int B, int seq, int H, int G, int64_t t_cap, int64_t pos0, float sl2,
     int n_qblk, int n_units) {
-  constexpr int BM = 128, BN = 64, KP = DH + 8, VP = BN + 8, NKS = DH / 16, NDB = DH / 32;
-  constexpr int KCH = BN * DH / 8 / 256;
+  constexpr int NT = NW * 64, BM = 32 * NW, BN = 64, KP = DH + 8, VP = BN + 8, NKS = DH / 16,
+                NDB = DH / 32;
+  constexpr int KCH = BN * DH / 8 / NT;
   constexpr int VITEMS = (BN / 4) * (DH / 8);  // 16 key quads x DH/8 dim chunks
   static_assert(BN == 64, "V store mapping assumes 16 key quads");
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][BN * KP];
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16_kernel(
   auto gload = [&](int j0) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i, row = c / (DH / 8), col = (c % (DH / 8)) * 8;
+      const int c = tid + NT * i, row = c / (DH / 8), col = (c % (DH / 8)) * 8;
       rk[i] = buffer_load16(krs, static_cast<uint32_t>((j0 + row) * DH + col) * 2);
     }
     if (tid < VITEMS) {
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_bf16_kernel(
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i, row = c / (DH / 8), col = (c % (DH / 8)) * 8;
+      const int c = tid + NT * i, row = c / (DH / 8), col = (c % (DH / 8)) * 8;
       *reinterpret_cast<u32x4*>(&Ks[buf][kperm(row) * KP + col]) = rk[i];
     }
     if (tid < VITEMS) {
@@ -254,20 +255,26 @@ __global__ __launch_bounds__(64) void attn_prefill_f32_kernel(
   }
 }
 
+// Waves per workgroup (32 query rows each).  4: two workgroups share a CU and
+// their softmax and MFMA phases overlap on the SIMDs; 8 waves per workgroup
+// measured no faster.
+constexpr int kAttnWaves = 4;
+
 template <>
 hipError_t attn_prefill<bf16_t>(const bf16_t* q, const bf16_t* k, const bf16_t* v, bf16_t* o, int B,
                                 int seq, int H, int G, int dh, int64_t t_cap, int64_t pos0,
                                 hipStream_t s) {
-  const int n_qblk = (seq + 127) / 128;
+  constexpr int NW = kAttnWaves;
+  const int n_qblk = (seq + 32 * NW - 1) / (32 * NW);
   const int n_units = n_qblk * B * G;
   const int grid = ((n_units + 7) / 8) * 8 * (H / G);
   const float sl2 = 1.4426950408889634f / sqrtf(static_cast<float>(dh));
   if (dh == 128)
-    hipLaunchKernelGGL(attn_prefill_bf16_kernel<128>, dim3(grid), dim3(256), 0, s, q, k, v, o, B,
-                       seq, H, G, t_cap, pos0, sl2, n_qblk, n_units);
+    hipLaunchKernelGGL((attn_prefill_bf16_kernel<128, NW>), dim3(grid), dim3(NW * 64), 0, s, q, k,
+                       v, o, B, seq, H, G, t_cap, pos0, sl2, n_qblk, n_units);
   else
-    hipLaunchKernelGGL(attn_prefill_bf16_kernel<64>, dim3(grid), dim3(256), 0, s, q, k, v, o, B, seq,
-                       H, G, t_cap, pos0, sl2, n_qblk, n_units);
+    hipLaunchKernelGGL((attn_prefill_bf16_kernel<64, NW>), dim3(grid), dim3(NW * 64), 0, s, q, k,
+                       v, o, B, seq, H, G, t_cap, pos0, sl2, n_qblk, n_units);
   return hipGetLastError();
 }
 
