@@ -28,7 +28,11 @@ tiny inputs, invariants).  The composite ``prefill``/``decode`` with general
 router weights and non-empty L3 has no end-to-end worked example on the
 pages; it rests on its pinned parts plus the special cases (one-hot router
 equals causal GQA attention, decode continues prefill, causality) -- beyond
-those it is "parity unpinned".
+those it is "parity unpinned".  The routing variants (``route_weights``) are
+pinned to scipy's softmax over the enabled tiers, a brute force over tier
+subsets, hand-made ties, torch's attention for L1 alone, and invariances
+(fixed routing ignores the router weights; without L3 the hash index does
+not matter).
 """
 
 from __future__ import annotations
@@ -39,7 +43,8 @@ import numpy as np
 from scipy.special import erf as _erf
 
 __all__ = [
-    "q_proj", "gelu", "router", "ema", "block_means", "simhash", "retrieve",
+    "q_proj", "gelu", "router", "router_logits", "route_weights", "ROUTE_MODES", "TIER_SETS",
+    "ema", "block_means", "simhash", "retrieve",
     "l3_mean", "fuse", "kv_proj", "attention", "attention_online", "prefill",
     "DecodeState", "decode_init", "decode_init_from_prefill", "decode_step",
 ]
@@ -79,15 +84,78 @@ def _softmax(z):
     return e / e.sum(axis=-1, keepdims=True)
 
 
-def router(q, w_r1, w_r2):
+# Routing variants of the abstract page's ablations: Table 10 compares the
+# learned soft router with a fixed lambda = 1/3 and hard top-2 / top-1
+# routing; Table 9 removes tiers (L1+L2, L1+L3, L1 alone, the last being
+# plain multi-head attention).
+ROUTE_MODES = ("soft", "fixed", "top1", "top2")
+TIER_SETS = {
+    "l1l2l3": (True, True, True),
+    "l1l2": (True, True, False),
+    "l1l3": (True, False, True),
+    "l1": (True, False, False),
+}
+
+
+def router_logits(q, w_r1, w_r2):
+    """z = GELU(q W_r1) W_r2, the three tier logits before the softmax.
+
+    MKA reading note, section 2: a learned MLP of the query gives the gate.
+    Reading: a two-layer MLP with an exact GELU between the layers and no
+    biases.  Output [..., 3]; tier 0 = L1, 1 = L2, 2 = L3.
+    """
+    return gelu(_f64(q) @ _f64(w_r1).T) @ _f64(w_r2).T
+
+
+def route_weights(z, mode="soft", tiers="l1l2l3"):
+    """lambda from the logits z [..., 3] under a routing variant.
+
+    ``tiers`` names the enabled tiers (L1 is always one); the others get
+    lambda = 0.  ``mode``:
+      soft  -- softmax of z over the enabled tiers (with all three: the
+               learned router of the reading note, section 2);
+      fixed -- 1 / (number of enabled tiers) on each, z unused (abstract
+               page, Table 10: lambda = 1/3 with all three);
+      top1, top2 -- the k enabled tiers with the largest logits (ties to the
+               lower tier index) and a softmax over those k alone (Table 10's
+               hard routing).  Readings: the kept weights are renormalised,
+               as a softmax restricted to the kept tiers; top-1 is therefore
+               one-hot, and top-k with k >= the enabled count is soft.
+    """
+    z = _f64(z)
+    en = TIER_SETS[tiers]
+    on = [i for i in range(3) if en[i]]
+    lam = np.zeros(z.shape)
+    if mode == "fixed":
+        for i in on:
+            lam[..., i] = 1.0 / len(on)
+        return lam
+    k = {"soft": 3, "top1": 1, "top2": 2}[mode]
+    keep = np.zeros(z.shape, dtype=bool)
+    for i in on:
+        # rank of tier i among the enabled tiers: how many beat it
+        rank = np.zeros(z.shape[:-1], dtype=np.int64)
+        for j in on:
+            if j != i:
+                beats = (z[..., j] > z[..., i]) | ((z[..., j] == z[..., i]) & (j < i))
+                rank += beats.astype(np.int64)
+        keep[..., i] = rank < k
+    zk = np.where(keep, z, -np.inf)
+    e = np.where(keep, np.exp(zk - zk.max(axis=-1, keepdims=True)), 0.0)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def router(q, w_r1, w_r2, mode="soft", tiers="l1l2l3"):
     """lambda = softmax(GELU(q W_r1) W_r2) over the three memory tiers.
 
     MKA reading note, section 2: a learned MLP of the query followed by a
-    softmax gives lambda in R^{B x S x 3}, per token and per layer.  Reading:
-    a two-layer MLP with an exact GELU between the layers and no biases.
+    softmax gives lambda in R^{B x S x 3}, per token and per layer.  Other
+    ``mode`` / ``tiers`` values give the ablation variants (``route_weights``).
     Output [..., 3]; tier 0 = L1, 1 = L2, 2 = L3.
     """
-    return _softmax(gelu(_f64(q) @ _f64(w_r1).T) @ _f64(w_r2).T)
+    if mode == "soft" and tiers == "l1l2l3":
+        return _softmax(router_logits(q, w_r1, w_r2))
+    return route_weights(router_logits(q, w_r1, w_r2), mode, tiers)
 
 
 # --------------------------------------------------------------------------
@@ -315,19 +383,23 @@ def attention_online(q, k, v, positions, n_kv_heads, tile=64):
 # --------------------------------------------------------------------------
 
 def prefill(x, w_q, w_k, w_v, w_r1, w_r2, proj, *, n_heads, n_kv_heads, ema_decay,
-            block, top_r, rows=None, lam_override=None):
+            block, top_r, rows=None, lam_override=None, route_mode="soft", tiers="l1l2l3"):
     """FastMKA layer forward over a whole sequence (every step, in page order).
 
     Returns a dict with q [B,N,H*dh], lam [B,N,3], l2 [B,N,D], block_means
     [B,nb,D], block_hash [B,nb], block_abs [B,nb,nbits], keys [B,N],
     key_abs [B,N,nbits], idx [B,N,R], l3 [B,N,D], x_fused [B,N,D],
     k, v [B,G,N,dh], rows [n] and o [B,n,H,dh] (attention only at ``rows``;
-    every row otherwise).  ``lam_override`` [B,N,3] replaces the router output.
+    every row otherwise).  ``lam_override`` [B,N,3] replaces the router output;
+    ``route_mode`` and ``tiers`` select a routing variant (``route_weights``).
+    Every tier is computed whatever the variant; a disabled tier enters the
+    fusion with lambda = 0.
     """
     x = _f64(x)
     B, N, D = x.shape
     q = q_proj(x, w_q)
-    lam = router(q, w_r1, w_r2) if lam_override is None else _f64(lam_override)
+    lam = (router(q, w_r1, w_r2, route_mode, tiers) if lam_override is None
+           else _f64(lam_override))
     l2, _ = ema(x, ema_decay)
     means = block_means(x, block)
     bhash, babs = simhash(means, proj)
@@ -387,7 +459,7 @@ def decode_init_from_prefill(x, ref, proj, *, block, t_cap):
 
 
 def decode_step(st, x_t, w_q, w_k, w_v, w_r1, w_r2, proj, *, n_heads, n_kv_heads, ema_decay,
-                block, top_r, attend=True):
+                block, top_r, attend=True, route_mode="soft", tiers="l1l2l3"):
     """One decode step at position t = st.pos for the token hiddens x_t [B, D].
 
     The same definitions as ``prefill`` applied to one token with the carried
@@ -401,7 +473,7 @@ def decode_step(st, x_t, w_q, w_k, w_v, w_r1, w_r2, proj, *, n_heads, n_kv_heads
     B, D = x_t.shape
     t = st.pos
     q = q_proj(x_t, w_q)
-    lam = router(q, w_r1, w_r2)
+    lam = router(q, w_r1, w_r2, route_mode, tiers)
     l2_seq, st.ema_state = ema(x_t[:, None, :], ema_decay, st.ema_state)
     l2 = l2_seq[:, 0]
     st.block_acc = st.block_acc + x_t

@@ -412,3 +412,160 @@ def test_decode_continues_prefill():
     np.testing.assert_allclose(st.k, full["k"], rtol=1e-10, atol=1e-13)
     np.testing.assert_allclose(st.means, full["block_means"], rtol=1e-12, atol=1e-14)
     np.testing.assert_array_equal(st.hash, full["block_hash"])
+
+
+# ------------------------------------------------- routing and tier variants
+# Abstract page, Table 10 (fixed lambda = 1/3, hard top-2 / top-1 routing) and
+# Table 9 (L1+L2, L1+L3, L1 alone = multi-head attention).
+
+_SUBSETS = {"l1l2l3": [0, 1, 2], "l1l2": [0, 1], "l1l3": [0, 2], "l1": [0]}
+
+
+@pytest.mark.parametrize("tiers", list(_SUBSETS))
+def test_soft_routing_over_a_tier_subset_is_scipy_softmax(tiers):
+    from scipy.special import softmax
+    z = rng(30).standard_normal((5, 7, 3)) * 3.0
+    lam = O.route_weights(z, "soft", tiers)
+    on = _SUBSETS[tiers]
+    off = [i for i in range(3) if i not in on]
+    np.testing.assert_allclose(lam[..., on], softmax(z[..., on], axis=-1), rtol=1e-14, atol=1e-16)
+    assert np.all(lam[..., off] == 0.0)
+
+
+def test_soft_routing_all_tiers_is_the_router_softmax():
+    r = rng(31)
+    q, w1, w2 = r.standard_normal((4, 16)), r.standard_normal((8, 16)), r.standard_normal((3, 8))
+    from scipy.special import softmax
+    np.testing.assert_allclose(O.router(q, w1, w2, "soft", "l1l2l3"),
+                               softmax(O.router_logits(q, w1, w2), axis=-1), rtol=1e-14)
+    np.testing.assert_allclose(O.route_weights(O.router_logits(q, w1, w2)),
+                               O.router(q, w1, w2), rtol=1e-14)
+
+
+@pytest.mark.parametrize("tiers", list(_SUBSETS))
+def test_fixed_routing_is_uniform_over_enabled_tiers(tiers):
+    z = rng(32).standard_normal((3, 11, 3)) * 10.0
+    lam = O.route_weights(z, "fixed", tiers)
+    on = _SUBSETS[tiers]
+    want = np.zeros(3)
+    want[on] = 1.0 / len(on)
+    np.testing.assert_array_equal(lam, np.broadcast_to(want, lam.shape))
+
+
+@pytest.mark.parametrize("mode,k", [("top1", 1), ("top2", 2)])
+@pytest.mark.parametrize("tiers", list(_SUBSETS))
+def test_hard_routing_bruteforce_over_subsets(mode, k, tiers):
+    # Brute force: among the k-subsets of the enabled tiers take the one with
+    # the largest logit sum (the top-k set when the logits are distinct), and a
+    # scipy softmax over it.
+    import itertools
+    from scipy.special import softmax
+    z = rng(33).standard_normal((60, 3))
+    lam = O.route_weights(z, mode, tiers)
+    on = _SUBSETS[tiers]
+    kk = min(k, len(on))
+    for row in range(z.shape[0]):
+        best = max(itertools.combinations(on, kk), key=lambda c: sum(z[row, i] for i in c))
+        want = np.zeros(3)
+        want[list(best)] = softmax(z[row, list(best)])
+        np.testing.assert_allclose(lam[row], want, rtol=1e-14, atol=1e-16)
+
+
+def test_hard_routing_ties_go_to_the_lower_tier():
+    z = np.array([[1.0, 1.0, 0.0], [0.0, 2.0, 2.0], [3.0, 3.0, 3.0]])
+    np.testing.assert_array_equal(O.route_weights(z, "top1"),
+                                  [[1, 0, 0], [0, 1, 0], [1, 0, 0]])
+    np.testing.assert_allclose(O.route_weights(z, "top2"),
+                               [[0.5, 0.5, 0], [0, 0.5, 0.5], [0.5, 0.5, 0]])
+    # L1+L3 with L2 largest: L2 is not a candidate
+    np.testing.assert_array_equal(O.route_weights(np.array([[0.0, 9.0, 1.0]]), "top1", "l1l3"),
+                                  [[0, 0, 1]])
+
+
+def test_hard_top1_keeps_the_soft_argmax_and_top2_drops_the_soft_argmin():
+    z = rng(34).standard_normal((200, 3))
+    soft = O.route_weights(z)
+    t1 = O.route_weights(z, "top1")
+    np.testing.assert_array_equal(np.argmax(t1, -1), np.argmax(soft, -1))
+    assert np.all(t1.max(-1) == 1.0)
+    t2 = O.route_weights(z, "top2")
+    np.testing.assert_array_equal(t2[np.arange(200), np.argmin(soft, -1)], 0.0)
+    # the kept pair keeps the soft ratio
+    lo = np.argmin(soft, -1)
+    a, b = (lo + 1) % 3, (lo + 2) % 3
+    i = np.arange(200)
+    np.testing.assert_allclose(t2[i, a] / t2[i, b], soft[i, a] / soft[i, b], rtol=1e-12)
+
+
+def test_layer_l1_tier_alone_is_causal_gqa_attention_whatever_the_router():
+    # Table 9's "L1 only (=MHA)": lambda = (1, 0, 0) for every mode, so the
+    # layer is torch's causal attention of X W_q against X W_k, X W_v.
+    s, d, args = _tiny()
+    x = torch.from_numpy(d["x"].astype(np.float64))
+    q = (x @ torch.from_numpy(d["w_q"].astype(np.float64)).T).view(1, s.seq, s.n_heads, s.head_dim)
+    k = (x @ torch.from_numpy(d["w_k"].astype(np.float64)).T).view(1, s.seq, s.n_kv_heads, s.head_dim)
+    v = (x @ torch.from_numpy(d["w_v"].astype(np.float64)).T).view(1, s.seq, s.n_kv_heads, s.head_dim)
+    rep = s.n_heads // s.n_kv_heads
+    want = torch.nn.functional.scaled_dot_product_attention(
+        q.transpose(1, 2), k.transpose(1, 2).repeat_interleave(rep, 1),
+        v.transpose(1, 2).repeat_interleave(rep, 1), is_causal=True).transpose(1, 2).numpy()
+    w = [d[n] for n in ("w_q", "w_k", "w_v", "w_r1", "w_r2", "proj")]
+    for mode in O.ROUTE_MODES:
+        ref = O.prefill(d["x"], *w, route_mode=mode, tiers="l1", **args)
+        np.testing.assert_allclose(ref["o"], want, rtol=1e-10, atol=1e-12, err_msg=mode)
+        np.testing.assert_array_equal(ref["lam"][..., 0], 1.0)
+
+
+def test_layer_fixed_routing_ignores_the_router_and_equals_a_zero_output_layer():
+    # Fixed lambda = 1/3 is the soft router with W_r2 = 0 (equal logits), and
+    # it does not depend on W_r1, W_r2 at all.
+    s, d, args = _tiny()
+    w = [d[n] for n in ("w_q", "w_k", "w_v", "w_r1", "w_r2", "proj")]
+    fixed = O.prefill(d["x"], *w, route_mode="fixed", **args)
+    w0 = list(w)
+    w0[4] = np.zeros_like(d["w_r2"])
+    zero_out = O.prefill(d["x"], *w0, **args)
+    np.testing.assert_allclose(fixed["o"], zero_out["o"], rtol=1e-12, atol=1e-14)
+    w1 = list(w)
+    w1[3] = rng(35).standard_normal(d["w_r1"].shape)
+    other = O.prefill(d["x"], *w1, route_mode="fixed", **args)
+    np.testing.assert_array_equal(fixed["o"], other["o"])
+
+
+def test_layer_hard_top1_fuses_exactly_one_tier_per_token():
+    s, d, args = _tiny()
+    w = [d[n] for n in ("w_q", "w_k", "w_v", "w_r1", "w_r2", "proj")]
+    ref = O.prefill(d["x"], *w, route_mode="top1", **args)
+    tiers = [np.asarray(d["x"], np.float64), ref["l2"], ref["l3"]]
+    pick = np.argmax(ref["lam"], -1)
+    for t in range(s.seq):
+        np.testing.assert_array_equal(ref["x_fused"][0, t], tiers[pick[0, t]][0, t])
+
+
+def test_layer_without_l3_ignores_the_hash_index():
+    # L1+L2: the output cannot depend on the hyperplanes or on R.
+    s, d, args = _tiny()
+    w = [d[n] for n in ("w_q", "w_k", "w_v", "w_r1", "w_r2", "proj")]
+    ref = O.prefill(d["x"], *w, tiers="l1l2", **args)
+    w2 = list(w)
+    w2[5] = rng(36).standard_normal(d["proj"].shape)
+    args2 = dict(args, top_r=1)
+    alt = O.prefill(d["x"], *w2, tiers="l1l2", **args2)
+    np.testing.assert_array_equal(ref["o"], alt["o"])
+    full = O.prefill(d["x"], *w2, **args2)
+    assert not np.array_equal(full["o"], ref["o"])
+
+
+@pytest.mark.parametrize("mode,tiers", [("top2", "l1l3"), ("fixed", "l1l2"), ("soft", "l1")])
+def test_decode_continues_prefill_for_variants(mode, tiers):
+    s, d, args = _tiny()
+    args = dict(args, route_mode=mode, tiers=tiers)
+    w = [d[k] for k in ("w_q", "w_k", "w_v", "w_r1", "w_r2", "proj")]
+    full = O.prefill(d["x"], *w, **args)
+    n1 = 180
+    part = O.prefill(d["x"][:, :n1], *w, **args)
+    st = O.decode_init_from_prefill(d["x"][:, :n1], part, d["proj"], block=s.block, t_cap=s.seq)
+    for t in range(n1, s.seq):
+        r = O.decode_step(st, d["x"][:, t], *w, **args)
+        np.testing.assert_allclose(r["o"], full["o"][:, t], rtol=1e-10, atol=1e-13)
+        np.testing.assert_allclose(r["lam"], full["lam"][:, t], rtol=1e-12, atol=1e-15)
