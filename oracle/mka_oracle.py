@@ -43,7 +43,8 @@ import numpy as np
 from scipy.special import erf as _erf
 
 __all__ = [
-    "q_proj", "gelu", "router", "router_logits", "route_weights", "ROUTE_MODES", "TIER_SETS",
+    "q_proj", "gelu", "router", "router_logits", "route_weights", "round_bf16", "ROUTE_MODES",
+    "TIER_SETS",
     "ema", "block_means", "simhash", "retrieve",
     "l3_mean", "fuse", "kv_proj", "attention", "attention_online", "prefill",
     "DecodeState", "decode_init", "decode_init_from_prefill", "decode_step",
@@ -107,7 +108,19 @@ def router_logits(q, w_r1, w_r2):
     return gelu(_f64(q) @ _f64(w_r1).T) @ _f64(w_r2).T
 
 
-def route_weights(z, mode="soft", tiers="l1l2l3"):
+def round_bf16(a):
+    """Values rounded to bfloat16 (round to nearest, ties to even), as float64.
+
+    A float64 value is first rounded to float32, then the low 16 bits of the
+    float32 pattern are rounded off.  Finite inputs only.
+    """
+    f = np.asarray(a, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def route_weights(z, mode="soft", tiers="l1l2l3", z_decide=None):
     """lambda from the logits z [..., 3] under a routing variant.
 
     ``tiers`` names the enabled tiers (L1 is always one); the others get
@@ -121,8 +134,11 @@ def route_weights(z, mode="soft", tiers="l1l2l3"):
                hard routing).  Readings: the kept weights are renormalised,
                as a softmax restricted to the kept tiers; top-1 is therefore
                one-hot, and top-k with k >= the enabled count is soft.
+    ``z_decide`` (default z): the logits that choose the kept tiers, when that
+    choice is taken in another precision than the weights.
     """
     z = _f64(z)
+    zd = z if z_decide is None else _f64(z_decide)
     en = TIER_SETS[tiers]
     on = [i for i in range(3) if en[i]]
     lam = np.zeros(z.shape)
@@ -137,7 +153,7 @@ def route_weights(z, mode="soft", tiers="l1l2l3"):
         rank = np.zeros(z.shape[:-1], dtype=np.int64)
         for j in on:
             if j != i:
-                beats = (z[..., j] > z[..., i]) | ((z[..., j] == z[..., i]) & (j < i))
+                beats = (zd[..., j] > zd[..., i]) | ((zd[..., j] == zd[..., i]) & (j < i))
                 rank += beats.astype(np.int64)
         keep[..., i] = rank < k
     zk = np.where(keep, z, -np.inf)
@@ -145,17 +161,25 @@ def route_weights(z, mode="soft", tiers="l1l2l3"):
     return e / e.sum(axis=-1, keepdims=True)
 
 
-def router(q, w_r1, w_r2, mode="soft", tiers="l1l2l3"):
+def router(q, w_r1, w_r2, mode="soft", tiers="l1l2l3", decide_q="f64"):
     """lambda = softmax(GELU(q W_r1) W_r2) over the three memory tiers.
 
     MKA reading note, section 2: a learned MLP of the query followed by a
     softmax gives lambda in R^{B x S x 3}, per token and per layer.  Other
     ``mode`` / ``tiers`` values give the ablation variants (``route_weights``).
     Output [..., 3]; tier 0 = L1, 1 = L2, 2 = L3.
+
+    ``decide_q = "bf16"``: hard routing chooses its tiers from the logits of q
+    rounded to bfloat16, the query as a bf16 layer stores it; the weights of
+    the kept tiers still come from the float64 logits.  (The pages fix no
+    precision for this choice; taking it from the stored query is how a layer
+    that keeps q in bf16 takes it.)
     """
+    z = router_logits(q, w_r1, w_r2)
     if mode == "soft" and tiers == "l1l2l3":
-        return _softmax(router_logits(q, w_r1, w_r2))
-    return route_weights(router_logits(q, w_r1, w_r2), mode, tiers)
+        return _softmax(z)
+    zd = router_logits(round_bf16(q), w_r1, w_r2) if decide_q == "bf16" else None
+    return route_weights(z, mode, tiers, z_decide=zd)
 
 
 # --------------------------------------------------------------------------
@@ -383,7 +407,8 @@ def attention_online(q, k, v, positions, n_kv_heads, tile=64):
 # --------------------------------------------------------------------------
 
 def prefill(x, w_q, w_k, w_v, w_r1, w_r2, proj, *, n_heads, n_kv_heads, ema_decay,
-            block, top_r, rows=None, lam_override=None, route_mode="soft", tiers="l1l2l3"):
+            block, top_r, rows=None, lam_override=None, route_mode="soft", tiers="l1l2l3",
+            decide_q="f64"):
     """FastMKA layer forward over a whole sequence (every step, in page order).
 
     Returns a dict with q [B,N,H*dh], lam [B,N,3], l2 [B,N,D], block_means
@@ -391,14 +416,15 @@ def prefill(x, w_q, w_k, w_v, w_r1, w_r2, proj, *, n_heads, n_kv_heads, ema_deca
     key_abs [B,N,nbits], idx [B,N,R], l3 [B,N,D], x_fused [B,N,D],
     k, v [B,G,N,dh], rows [n] and o [B,n,H,dh] (attention only at ``rows``;
     every row otherwise).  ``lam_override`` [B,N,3] replaces the router output;
-    ``route_mode`` and ``tiers`` select a routing variant (``route_weights``).
+    ``route_mode`` and ``tiers`` select a routing variant (``route_weights``;
+    ``decide_q`` as in ``router``).
     Every tier is computed whatever the variant; a disabled tier enters the
     fusion with lambda = 0.
     """
     x = _f64(x)
     B, N, D = x.shape
     q = q_proj(x, w_q)
-    lam = (router(q, w_r1, w_r2, route_mode, tiers) if lam_override is None
+    lam = (router(q, w_r1, w_r2, route_mode, tiers, decide_q) if lam_override is None
            else _f64(lam_override))
     l2, _ = ema(x, ema_decay)
     means = block_means(x, block)
@@ -459,7 +485,7 @@ def decode_init_from_prefill(x, ref, proj, *, block, t_cap):
 
 
 def decode_step(st, x_t, w_q, w_k, w_v, w_r1, w_r2, proj, *, n_heads, n_kv_heads, ema_decay,
-                block, top_r, attend=True, route_mode="soft", tiers="l1l2l3"):
+                block, top_r, attend=True, route_mode="soft", tiers="l1l2l3", decide_q="f64"):
     """One decode step at position t = st.pos for the token hiddens x_t [B, D].
 
     The same definitions as ``prefill`` applied to one token with the carried
@@ -473,7 +499,7 @@ def decode_step(st, x_t, w_q, w_k, w_v, w_r1, w_r2, proj, *, n_heads, n_kv_heads
     B, D = x_t.shape
     t = st.pos
     q = q_proj(x_t, w_q)
-    lam = router(q, w_r1, w_r2, route_mode, tiers)
+    lam = router(q, w_r1, w_r2, route_mode, tiers, decide_q)
     l2_seq, st.ema_state = ema(x_t[:, None, :], ema_decay, st.ema_state)
     l2 = l2_seq[:, 0]
     st.block_acc = st.block_acc + x_t

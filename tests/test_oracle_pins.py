@@ -569,3 +569,28 @@ def test_decode_continues_prefill_for_variants(mode, tiers):
         r = O.decode_step(st, d["x"][:, t], *w, **args)
         np.testing.assert_allclose(r["o"], full["o"][:, t], rtol=1e-10, atol=1e-13)
         np.testing.assert_allclose(r["lam"], full["lam"][:, t], rtol=1e-12, atol=1e-15)
+
+
+def test_round_bf16_matches_torch_conversion():
+    r = rng(37)
+    a = np.concatenate([r.standard_normal(4000) * 10.0 ** r.integers(-8, 8, 4000),
+                        [0.0, -0.0, 1.0, -1.0, 1.00390625, 1.01171875, 65504.0, 3e38]])
+    want = torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(O.round_bf16(a), want)
+
+
+def test_hard_routing_decision_precision():
+    # The choice follows z_decide, the weights follow z; with z_decide = z it is
+    # the plain definition, and bf16-representable queries decide identically.
+    r = rng(38)
+    z = r.standard_normal((50, 3))
+    zd = z.copy()
+    zd[:, 0] += 10.0  # force L1 to be chosen
+    lam = O.route_weights(z, "top1", z_decide=zd)
+    np.testing.assert_array_equal(lam[:, 0], 1.0)
+    np.testing.assert_array_equal(O.route_weights(z, "top2", z_decide=z), O.route_weights(z, "top2"))
+    q = O.round_bf16(r.standard_normal((20, 16)))
+    w1, w2 = r.standard_normal((8, 16)), r.standard_normal((3, 8))
+    for mode in ("top1", "top2"):
+        np.testing.assert_array_equal(O.router(q, w1, w2, mode, decide_q="bf16"),
+                                      O.router(q, w1, w2, mode))
