@@ -59,6 +59,24 @@ enum {
 enum { MKA_OP_EMA_SCAN = 0, MKA_OP_FUSE_KV = 1, MKA_OP_ATTN_DECODE = 2, MKA_OP_PREFILL = 3,
        MKA_OP_DECODE_STEP = 4, MKA_OP_RETRIEVE = 5, MKA_OP_INDEX = 6, MKA_OP_ROUTE = 7 };
 
+/* Routing variant (mka_dims.route_mode) and enabled tiers (mka_dims.tiers):
+ * the ablations of the abstract page, Table 10 (fixed lambda = 1/3, hard
+ * top-2 and top-1 routing against the learned soft router) and Table 9
+ * (L1+L2, L1+L3, L1 alone = plain multi-head attention).  From the router
+ * logits z = GELU(q W_r1) W_r2:
+ *   MKA_ROUTE_SOFT   softmax of z over the enabled tiers (with all three
+ *                    tiers: the learned router of the reading note, method
+ *                    section 2);
+ *   MKA_ROUTE_FIXED  1 / (number of enabled tiers) on each, the router unused;
+ *   MKA_ROUTE_TOP1/2 the 1 or 2 enabled tiers with the largest logits (ties
+ *                    to the lower tier index) and a softmax over those alone:
+ *                    top-1 is one-hot; the others get lambda = 0.
+ * A disabled tier always has lambda = 0 and its steps do not run: without L3
+ * no block codes, block projections or retrieval; with L1 alone also no EMA
+ * and no router.  Zero-initialised fields give the full method. */
+enum { MKA_ROUTE_SOFT = 0, MKA_ROUTE_FIXED = 1, MKA_ROUTE_TOP1 = 2, MKA_ROUTE_TOP2 = 3 };
+enum { MKA_TIERS_ALL = 0, MKA_TIERS_L1_L2 = 1, MKA_TIERS_L1_L3 = 2, MKA_TIERS_L1 = 3 };
+
 /* Shape of one layer call.
  *   batch B >= 1; seq = tokens in this call (1 for a decode step) >= 1;
  *   d_model D; n_heads H and n_kv_heads G with H % G == 0 (query head h uses
@@ -81,6 +99,8 @@ typedef struct mka_dims {
   int32_t top_r;
   float ema_decay;
   int32_t dtype;
+  int32_t route_mode; /* MKA_ROUTE_* (0 = the learned soft router) */
+  int32_t tiers;      /* MKA_TIERS_* (0 = L1, L2 and L3) */
 } mka_dims;
 
 /* Router: Q = X W_q and lambda = softmax(GELU(Q W_r1) W_r2).
@@ -168,6 +188,8 @@ int mka_l3_retrieve(const mka_dims* d, const float* l2, const float* proj,
  *   idx [B, seq, R] int32; lambda [B, seq, 3] f32; w_k, w_v [G*dh, D] dtype
  *   k_cache, v_cache [B, G, t_cap, dh] dtype: rows pos0 .. pos0+seq-1 written
  *   ws >= mka_workspace_bytes(d, MKA_OP_FUSE_KV, 0) bytes
+ * Inputs of disabled tiers (d->tiers) are not read and may be NULL: l2 without
+ * L2; idx and block_means without L3.  With L1 alone X_fused = x.
  * Requires pos0 + seq <= t_cap. */
 int mka_fuse_kv_proj(const mka_dims* d, const void* x, const float* l2,
                      const float* block_means, int32_t nb_cap, const int32_t* idx,
@@ -208,7 +230,12 @@ int mka_attn_decode(const mka_dims* d, const void* q, const void* k_cache,
  *          completed blocks written, as mka_l3_block_kv); k_cache, v_cache [B, G, t_cap, dh]
  *   outputs: q [B,seq,H,dh], lambda [B,seq,3], l2 [B,seq,D], key [B,seq],
  *            idx [B,seq,R], o [B,seq,H,dh]
- *   ws >= mka_workspace_bytes(d, MKA_OP_PREFILL, 0) bytes */
+ *   ws >= mka_workspace_bytes(d, MKA_OP_PREFILL, 0) bytes
+ * Routing variants (d->route_mode, d->tiers): q, lambda, o and the KV cache
+ * are always written.  Without L3, key, idx, block_hash and block_kv are not
+ * written.  With L1 alone, l2 and the EMA state, block sums and block means
+ * are not written either.  A session uses one variant for all its calls: the
+ * state a variant does not keep is not valid for another. */
 typedef struct mka_weights {
   const void* w_q;
   const void* w_k;
@@ -253,7 +280,8 @@ int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weight
  *   [K|V] = lambda1 (x W) + lambda2 (L2 W) + lambda3 mean_b(block_kv[b]),
  * equal to (X_fused W) up to float32 rounding (the row is not rounded through
  * X_fused), so that the products need no lambda and run beside the attention;
- * float32 layers take the steps in order.  Everything runs on ``stream``. */
+ * float32 layers take the steps in order.  Everything runs on ``stream``.
+ * Routing variants write and keep what mka_prefill does under them. */
 int mka_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_weights* w,
                     const mka_state* st, const mka_outputs* out, void* ws, size_t ws_bytes,
                     void* stream);

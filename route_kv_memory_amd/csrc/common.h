@@ -168,4 +168,62 @@ __device__ __forceinline__ int xcd_contiguous(int bid, int n) {
   return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local;
 }
 
+
+// ---- routing variants ------------------------------------------------------
+// The abstract page's ablations: Table 10 compares the learned soft router
+// with a fixed lambda = 1/3 and hard top-2 / top-1 routing; Table 9 removes
+// tiers (L1+L2, L1+L3, L1 alone).  Values equal the C ABI's MKA_ROUTE_* and
+// MKA_TIERS_* constants.
+constexpr int kRouteSoft = 0, kRouteFixed = 1, kRouteTop1 = 2, kRouteTop2 = 3;
+constexpr int kTiersAll = 0, kTiersL1L2 = 1, kTiersL1L3 = 2, kTiersL1 = 3;
+
+struct Routing {
+  int mode = kRouteSoft;
+  int tiers = kTiersAll;
+  __host__ __device__ bool l2() const { return tiers == kTiersAll || tiers == kTiersL1L2; }
+  __host__ __device__ bool l3() const { return tiers == kTiersAll || tiers == kTiersL1L3; }
+  // the EMA runs when L2 is mixed or keys the L3 retrieval
+  __host__ __device__ bool ema() const { return tiers != kTiersL1; }
+  // lambda depends on the router MLP
+  __host__ __device__ bool learned() const { return mode != kRouteFixed && tiers != kTiersL1; }
+  // lambda when it does not depend on the router: 1 / (enabled tiers) on each
+  __host__ __device__ float fixed_weight(int i) const {
+    const bool on = i == 0 || (i == 1 && l2()) || (i == 2 && l3());
+    return on ? 1.0f / static_cast<float>(1 + l2() + l3()) : 0.0f;
+  }
+};
+
+// lambda from the three router logits: the k enabled tiers with the largest
+// logits (k = 3 soft, 2 or 1 hard; ties to the lower tier index), softmax over
+// those, zero elsewhere.  With every tier kept it is the max-shifted softmax
+// of the three logits.
+__device__ __forceinline__ void route_weights(const float* z, Routing rt, float* out) {
+  if (!rt.learned()) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) out[i] = rt.fixed_weight(i);
+    return;
+  }
+  const bool on[3] = {true, rt.l2(), rt.l3()};
+  const int k = rt.mode == kRouteTop1 ? 1 : rt.mode == kRouteTop2 ? 2 : 3;
+  bool keep[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    int rank = 0;
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j != i && on[j]) rank += (z[j] > z[i] || (z[j] == z[i] && j < i)) ? 1 : 0;
+    keep[i] = on[i] && rank < k;
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+    if (keep[i]) m = fmaxf(m, z[i]);
+  float e[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) e[i] = keep[i] ? expf(z[i] - m) : 0.0f;
+  const float inv = 1.0f / (e[0] + e[1] + e[2]);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) out[i] = e[i] * inv;
+}
+
 }  // namespace mka

@@ -61,6 +61,8 @@ struct DecodeArgs {
   float* part_o;
   int chunk, n_chunks, n_hb;  // keys per split chunk, chunks, 16-head blocks per group
   T* o;            // [B, H, dh] attention output
+  // routing variant: steps of disabled tiers are skipped, their inputs unread
+  Routing rt;
 };
 
 // Sequential path (float32 layers): front, mid, fuse, then the K/V product and

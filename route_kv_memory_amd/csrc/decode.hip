@@ -121,6 +121,7 @@ __global__ __launch_bounds__(256) void decode_front_kernel(DecodeArgs<T> a) {
     }
     a.acc[o] = acc;
   }
+  if (!a.rt.l3()) return;  // no retrieval: the key is not needed
   if (tid < kDecSlice) Ls[tid] = sv;
   __syncthreads();
   // thread (j = hyperplane, quarter of the slice): 32 channels of row j of P.
@@ -148,7 +149,7 @@ __global__ __launch_bounds__(256) void decode_mid_kernel(DecodeArgs<T> a) {
   __shared__ uint64_t key_s;
   __shared__ uint32_t cand[4][RMAX];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nh_wg = (a.r + 3) / 4;
+  const int nh_wg = a.rt.learned() ? (a.r + 3) / 4 : 0;
   if (static_cast<int>(blockIdx.x) < nh_wg) {
     // ---- router hidden unit n for every token: GELU(q . W_r1[n]).
     const int n = blockIdx.x * 4 + wave;
@@ -237,18 +238,19 @@ template <typename T>
 __global__ __launch_bounds__(64) void decode_fuse_kernel(DecodeArgs<T> a) {
   constexpr int RMAX = 32;
   const int lane = threadIdx.x, b = blockIdx.y;
-  float z[3];
+  float z[3] = {0.f, 0.f, 0.f};
+  if (a.rt.learned()) {
 #pragma unroll
-  for (int c = 0; c < 3; ++c) {
-    float sum = 0.f;
-    for (int n = lane; n < a.r; n += 64)
-      sum = fmaf(a.hidden[b * a.r + n], Elem<T>::to_f32(a.w_r2[c * a.r + n]), sum);
-    z[c] = wave_sum(sum);
+    for (int c = 0; c < 3; ++c) {
+      float sum = 0.f;
+      for (int n = lane; n < a.r; n += 64)
+        sum = fmaf(a.hidden[b * a.r + n], Elem<T>::to_f32(a.w_r2[c * a.r + n]), sum);
+      z[c] = wave_sum(sum);
+    }
   }
-  const float zm = fmaxf(z[0], fmaxf(z[1], z[2]));
-  const float e0 = expf(z[0] - zm), e1 = expf(z[1] - zm), e2 = expf(z[2] - zm);
-  const float inv = 1.0f / (e0 + e1 + e2);
-  const float l1w = e0 * inv, l2w = e1 * inv, l3w = e2 * inv;
+  float lw[3];
+  route_weights(z, a.rt, lw);
+  const float l1w = lw[0], l2w = lw[1], l3w = lw[2];
   if (blockIdx.x == 0 && lane == 0) {
     a.lam[b * 3 + 0] = l1w;
     a.lam[b * 3 + 1] = l2w;
@@ -259,11 +261,12 @@ __global__ __launch_bounds__(64) void decode_fuse_kernel(DecodeArgs<T> a) {
   const int32_t* sel = a.idx + static_cast<int64_t>(b) * a.R;
   const float* mb = a.means + static_cast<int64_t>(b) * a.nb_cap * a.D + ch;
   int blk[RMAX];
+  const int R = a.rt.l3() ? a.R : 0;  // disabled tiers are not read
 #pragma unroll
-  for (int i = 0; i < RMAX; ++i) blk[i] = i < a.R ? sel[i] : -1;
-  float xv[4], sv[4], l3[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < RMAX; ++i) blk[i] = i < R ? sel[i] : -1;
+  float xv[4], sv[4] = {0.f, 0.f, 0.f, 0.f}, l3[4] = {0.f, 0.f, 0.f, 0.f};
   load4(a.x + static_cast<int64_t>(b) * a.D + ch, xv);
-  load4(a.l2 + static_cast<int64_t>(b) * a.D + ch, sv);
+  if (a.rt.l2()) load4(a.l2 + static_cast<int64_t>(b) * a.D + ch, sv);
   int cnt = 0;
 #pragma unroll
   for (int i = 0; i < RMAX; ++i) {
@@ -286,13 +289,14 @@ __global__ __launch_bounds__(64) void decode_fuse_kernel(DecodeArgs<T> a) {
 
 template <typename T>
 hipError_t decode_front(const DecodeArgs<T>& a, hipStream_t s) {
-  const int grid = (a.qw + 3) / 4 + a.n_slices * a.B;
+  const int grid = (a.qw + 3) / 4 + (a.rt.ema() ? a.n_slices * a.B : 0);
   hipLaunchKernelGGL(decode_front_kernel<T>, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 template <typename T>
 hipError_t decode_mid(const DecodeArgs<T>& a, hipStream_t s) {
-  const int grid = (a.r + 3) / 4 + a.B;
+  const int grid = (a.rt.learned() ? (a.r + 3) / 4 : 0) + (a.rt.l3() ? a.B : 0);
+  if (grid == 0) return hipSuccess;
   if (a.R <= 16)
     hipLaunchKernelGGL((decode_mid_kernel<T, 16>), dim3(grid), dim3(256), 0, s, a);
   else
@@ -409,6 +413,7 @@ __global__ __launch_bounds__(256) void decode_inputs_kernel(DecodeArgs<bf16_t> a
     }
     a.acc[o] = acc;
   }
+  if (!a.rt.l3()) return;  // no retrieval: the key is not needed
   if (tid < kDecSlice) Ls[tid] = sv;
   __syncthreads();
   const int j = lane, quarter = wave;
@@ -440,7 +445,7 @@ template <int DH, int RMAX>
 __global__ __launch_bounds__(256, 2) void decode_attend_kernel(DecodeArgs<bf16_t> a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[split_lds_bytes<DH>()];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nh_wg = (a.r + 3) / 4;
+  const int nh_wg = a.rt.learned() ? (a.r + 3) / 4 : 0;
   int wg = blockIdx.x;
   if (wg < nh_wg) {
     // ---- router hidden unit n for every token: GELU(q . W_r1[n]).
@@ -478,14 +483,33 @@ __global__ __launch_bounds__(256, 2) void decode_attend_kernel(DecodeArgs<bf16_t
     // before decode_merge, so it runs beside the attention.
     const int n0 = (wg * 4 + wave) * kGemvCols;
     if (n0 >= nkv) return;
+    const auto wrow = [&](int c) {
+      const int col = min(n0 + c, nkv - 1);
+      return col < a.kvw ? a.w_k + static_cast<int64_t>(col) * a.D
+                         : a.w_v + static_cast<int64_t>(col - a.kvw) * a.D;
+    };
+    if (!a.rt.l2()) {  // L2 not mixed: x W alone
+      float acc[1][kGemvCols][kFewRowsDec] = {};
+      decode_products<1>(
+          a.D, a.B, wrow,
+          [&](int b, int k, float (&xv)[1][8]) {
+            Vec16<bf16_t>::load(a.x + static_cast<int64_t>(b) * a.D + k, xv[0]);
+          },
+          acc);
+#pragma unroll
+      for (int c = 0; c < kGemvCols; ++c)
+#pragma unroll
+        for (int b = 0; b < kFewRowsDec; ++b) {
+          if (b < a.B) {
+            const float vx = wave_sum(acc[0][c][b]);
+            if (lane == 0 && n0 + c < nkv) a.kvx[static_cast<int64_t>(b) * nkv + n0 + c] = vx;
+          }
+        }
+      return;
+    }
     float acc[2][kGemvCols][kFewRowsDec] = {};
     decode_products<2>(
-        a.D, a.B,
-        [&](int c) {
-          const int col = min(n0 + c, nkv - 1);
-          return col < a.kvw ? a.w_k + static_cast<int64_t>(col) * a.D
-                             : a.w_v + static_cast<int64_t>(col - a.kvw) * a.D;
-        },
+        a.D, a.B, wrow,
         [&](int b, int k, float (&xv)[2][8]) {
           const int64_t o = static_cast<int64_t>(b) * a.D + k;
           Vec16<bf16_t>::load(a.x + o, xv[0]);
@@ -511,97 +535,101 @@ __global__ __launch_bounds__(256, 2) void decode_attend_kernel(DecodeArgs<bf16_t
   wg -= nkv_wg;
   if (wg < a.B) {
     // ---- token b: key, top-R blocks, L3 W (mean of the projected block means)
-    // and the EMA state commit.
+    // and the EMA state commit (only the commit without L3; nothing without
+    // the EMA).
+    if (!a.rt.ema()) return;
     const int b = wg;
-    uint64_t* key_s = reinterpret_cast<uint64_t*>(lds);
-    uint32_t* cand = reinterpret_cast<uint32_t*>(lds + 16);             // [4][RMAX]
-    int32_t* sel = reinterpret_cast<int32_t*>(lds + 16 + 16 * RMAX);    // [RMAX]
-    const int ne = static_cast<int>(a.pos / a.block);
-    const uint64_t* codes = a.bhash + static_cast<int64_t>(b) * a.nb_cap;
-    // this thread's first 4 block codes are in flight during the key reduction
-    uint64_t cv[4];
+    if (a.rt.l3()) {
+      uint64_t* key_s = reinterpret_cast<uint64_t*>(lds);
+      uint32_t* cand = reinterpret_cast<uint32_t*>(lds + 16);             // [4][RMAX]
+      int32_t* sel = reinterpret_cast<int32_t*>(lds + 16 + 16 * RMAX);    // [RMAX]
+      const int ne = static_cast<int>(a.pos / a.block);
+      const uint64_t* codes = a.bhash + static_cast<int64_t>(b) * a.nb_cap;
+      // this thread's first 4 block codes are in flight during the key reduction
+      uint64_t cv[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) cv[u] = ne > 0 ? codes[min(tid + 256 * u, ne - 1)] : 0;
-    if (wave == 0) {
-      // partial projections of all slices, loaded first, added in slice order
-      double p = 0.0;
-      for (int s0 = 0; s0 < a.n_slices; s0 += 8) {
-        double v[8];
+      for (int u = 0; u < 4; ++u) cv[u] = ne > 0 ? codes[min(tid + 256 * u, ne - 1)] : 0;
+      if (wave == 0) {
+        // partial projections of all slices, loaded first, added in slice order
+        double p = 0.0;
+        for (int s0 = 0; s0 < a.n_slices; s0 += 8) {
+          double v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          v[u] = a.part[(static_cast<int64_t>(min(s0 + u, a.n_slices - 1)) * a.B + b) * 64 + lane];
+          for (int u = 0; u < 8; ++u)
+            v[u] = a.part[(static_cast<int64_t>(min(s0 + u, a.n_slices - 1)) * a.B + b) * 64 + lane];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (s0 + u < a.n_slices) p += v[u];
-      }
-      const uint64_t code = __ballot(lane < a.nbits && p > 0.0);
-      if (lane == 0) {
-        *key_s = code;
-        a.key[b] = code;
-      }
-    }
-    __syncthreads();
-    const uint64_t key = *key_s;
-    uint32_t top[RMAX];
-#pragma unroll
-    for (int i = 0; i < RMAX; ++i) top[i] = kEmptyKey;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (tid + 256 * u < ne) insert_sorted(top, cand_key(key, cv[u], tid + 256 * u));
-    for (int jb = tid + 1024; jb < ne; jb += 256) insert_sorted(top, cand_key(key, codes[jb], jb));
-    for (int i = 0; i < a.R; ++i) {
-      const uint32_t m = wave_min_dpp(top[0]);
-      if (top[0] == m && m != kEmptyKey) {
-#pragma unroll
-        for (int k = 0; k < RMAX - 1; ++k) top[k] = top[k + 1];
-        top[RMAX - 1] = kEmptyKey;
-      }
-      if (lane == 0) cand[wave * RMAX + i] = m;
-    }
-    __syncthreads();
-    if (wave == 0) {
-      uint32_t c0 = kEmptyKey, c1 = kEmptyKey;
-      if (lane < 4 * a.R) c0 = cand[(lane / a.R) * RMAX + lane % a.R];
-      if (lane + 64 < 4 * a.R) c1 = cand[((lane + 64) / a.R) * RMAX + (lane + 64) % a.R];
-      if (c1 < c0) {
-        const uint32_t t = c0;
-        c0 = c1;
-        c1 = t;
-      }
-      int32_t* out = a.idx + static_cast<int64_t>(b) * a.R;
-      for (int i = 0; i < a.R; ++i) {
-        const uint32_t m = wave_min_dpp(c0);
-        if (c0 == m && m != kEmptyKey) {
-          c0 = c1;
-          c1 = kEmptyKey;
+          for (int u = 0; u < 8; ++u)
+            if (s0 + u < a.n_slices) p += v[u];
         }
-        const int blk = m == kEmptyKey ? -1 : static_cast<int>(0xFFFFFFu - (m & 0xFFFFFFu));
+        const uint64_t code = __ballot(lane < a.nbits && p > 0.0);
         if (lane == 0) {
-          out[i] = blk;
-          sel[i] = blk;
+          *key_s = code;
+          a.key[b] = code;
         }
       }
-    }
-    __syncthreads();
-    // L3 W = mean of the selected blocks' projected means, in rank order; the
-    // selection is held in registers and every row load is issued up front
-    // (rows of unfilled slots are read at block 0 and not added).
-    int blk[RMAX], cnt = 0;
+      __syncthreads();
+      const uint64_t key = *key_s;
+      uint32_t top[RMAX];
 #pragma unroll
-    for (int i = 0; i < RMAX; ++i) {
-      blk[i] = i < a.R ? sel[i] : -1;
-      cnt += blk[i] >= 0;
-    }
-    const float inv = cnt ? 1.0f / static_cast<float>(cnt) : 0.f;
-    const float* pb = a.block_kv + static_cast<int64_t>(b) * a.nb_cap * nkv;
-    for (int n = tid; n < nkv; n += 256) {
-      float v[RMAX];
+      for (int i = 0; i < RMAX; ++i) top[i] = kEmptyKey;
 #pragma unroll
-      for (int i = 0; i < RMAX; ++i) v[i] = pb[static_cast<int64_t>(max(blk[i], 0)) * nkv + n];
-      float sum = 0.f;
+      for (int u = 0; u < 4; ++u)
+        if (tid + 256 * u < ne) insert_sorted(top, cand_key(key, cv[u], tid + 256 * u));
+      for (int jb = tid + 1024; jb < ne; jb += 256) insert_sorted(top, cand_key(key, codes[jb], jb));
+      for (int i = 0; i < a.R; ++i) {
+        const uint32_t m = wave_min_dpp(top[0]);
+        if (top[0] == m && m != kEmptyKey) {
 #pragma unroll
-      for (int i = 0; i < RMAX; ++i) sum += blk[i] >= 0 ? v[i] : 0.f;
-      a.kvl3[static_cast<int64_t>(b) * nkv + n] = cnt ? sum * inv : 0.f;
+          for (int k = 0; k < RMAX - 1; ++k) top[k] = top[k + 1];
+          top[RMAX - 1] = kEmptyKey;
+        }
+        if (lane == 0) cand[wave * RMAX + i] = m;
+      }
+      __syncthreads();
+      if (wave == 0) {
+        uint32_t c0 = kEmptyKey, c1 = kEmptyKey;
+        if (lane < 4 * a.R) c0 = cand[(lane / a.R) * RMAX + lane % a.R];
+        if (lane + 64 < 4 * a.R) c1 = cand[((lane + 64) / a.R) * RMAX + (lane + 64) % a.R];
+        if (c1 < c0) {
+          const uint32_t t = c0;
+          c0 = c1;
+          c1 = t;
+        }
+        int32_t* out = a.idx + static_cast<int64_t>(b) * a.R;
+        for (int i = 0; i < a.R; ++i) {
+          const uint32_t m = wave_min_dpp(c0);
+          if (c0 == m && m != kEmptyKey) {
+            c0 = c1;
+            c1 = kEmptyKey;
+          }
+          const int blk = m == kEmptyKey ? -1 : static_cast<int>(0xFFFFFFu - (m & 0xFFFFFFu));
+          if (lane == 0) {
+            out[i] = blk;
+            sel[i] = blk;
+          }
+        }
+      }
+      __syncthreads();
+      // L3 W = mean of the selected blocks' projected means, in rank order; the
+      // selection is held in registers and every row load is issued up front
+      // (rows of unfilled slots are read at block 0 and not added).
+      int blk[RMAX], cnt = 0;
+#pragma unroll
+      for (int i = 0; i < RMAX; ++i) {
+        blk[i] = i < a.R ? sel[i] : -1;
+        cnt += blk[i] >= 0;
+      }
+      const float inv = cnt ? 1.0f / static_cast<float>(cnt) : 0.f;
+      const float* pb = a.block_kv + static_cast<int64_t>(b) * a.nb_cap * nkv;
+      for (int n = tid; n < nkv; n += 256) {
+        float v[RMAX];
+#pragma unroll
+        for (int i = 0; i < RMAX; ++i) v[i] = pb[static_cast<int64_t>(max(blk[i], 0)) * nkv + n];
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < RMAX; ++i) sum += blk[i] >= 0 ? v[i] : 0.f;
+        a.kvl3[static_cast<int64_t>(b) * nkv + n] = cnt ? sum * inv : 0.f;
+      }
     }
     // EMA state commit (the L2 row of this token)
     const float* l2r = a.l2 + static_cast<int64_t>(b) * a.D;
@@ -637,34 +665,38 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs<
         const int nk = g * DH + min(tid, DH - 1), nv = a.kvw + nk;
         const float kx1 = a.kvx[rb + nk], kx2 = a.kvl2[rb + nk], kx3 = a.kvl3[rb + nk];
         const float vx1 = a.kvx[rb + nv], vx2 = a.kvl2[rb + nv], vx3 = a.kvl3[rb + nv];
-        if (tid < 64) {  // lambda = softmax(hidden W_r2)
-          float z[3];
+        if (tid < 64) {  // lambda = softmax(hidden W_r2), under the routing variant
+          float z[3] = {0.f, 0.f, 0.f};
+          if (a.rt.learned()) {
 #pragma unroll
-          for (int c = 0; c < 3; ++c) {
-            float sum = 0.f;
-            for (int n = lane; n < a.r; n += 64)
-              sum = fmaf(a.hidden[b * a.r + n], bf16_to_f32(a.w_r2[c * a.r + n]), sum);
-            z[c] = wave_sum(sum);
+            for (int c = 0; c < 3; ++c) {
+              float sum = 0.f;
+              for (int n = lane; n < a.r; n += 64)
+                sum = fmaf(a.hidden[b * a.r + n], bf16_to_f32(a.w_r2[c * a.r + n]), sum);
+              z[c] = wave_sum(sum);
+            }
           }
-          const float zm = fmaxf(z[0], fmaxf(z[1], z[2]));
-          const float e0 = expf(z[0] - zm), e1 = expf(z[1] - zm), e2 = expf(z[2] - zm);
-          const float inv = 1.0f / (e0 + e1 + e2);
+          float lw[3];
+          route_weights(z, a.rt, lw);
           if (lane == 0) {
-            sm.lam[0] = e0 * inv;
-            sm.lam[1] = e1 * inv;
-            sm.lam[2] = e2 * inv;
+            sm.lam[0] = lw[0];
+            sm.lam[1] = lw[1];
+            sm.lam[2] = lw[2];
             if (h == 0) {
-              a.lam[b * 3 + 0] = e0 * inv;
-              a.lam[b * 3 + 1] = e1 * inv;
-              a.lam[b * 3 + 2] = e2 * inv;
+              a.lam[b * 3 + 0] = lw[0];
+              a.lam[b * 3 + 1] = lw[1];
+              a.lam[b * 3 + 2] = lw[2];
             }
           }
         }
         __syncthreads();
         if (tid < DH) {  // the fused K/V row of the token, rounded as the cache stores it
           const float l1 = sm.lam[0], l2 = sm.lam[1], l3 = sm.lam[2];
-          const bf16_t kb = f32_to_bf16(l1 * kx1 + l2 * kx2 + l3 * kx3);
-          const bf16_t vb = f32_to_bf16(l1 * vx1 + l2 * vx2 + l3 * vx3);
+          // rows of disabled tiers were not computed this step: exact zeros
+          const float k2 = a.rt.l2() ? kx2 : 0.f, v2 = a.rt.l2() ? vx2 : 0.f;
+          const float k3 = a.rt.l3() ? kx3 : 0.f, v3 = a.rt.l3() ? vx3 : 0.f;
+          const bf16_t kb = f32_to_bf16(l1 * kx1 + l2 * k2 + l3 * k3);
+          const bf16_t vb = f32_to_bf16(l1 * vx1 + l2 * v2 + l3 * v3);
           kx[tid] = bf16_to_f32(kb);
           vx[tid] = bf16_to_f32(vb);
           if (h % hpg == 0) {
@@ -679,15 +711,15 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs<
 
 hipError_t decode_inputs_bf16(const DecodeArgs<bf16_t>& a, hipStream_t s) {
   const int per_wg = 4 * kGemvCols;
-  const int grid = (a.qw + per_wg - 1) / per_wg + a.n_slices * a.B;
+  const int grid = (a.qw + per_wg - 1) / per_wg + (a.rt.ema() ? a.n_slices * a.B : 0);
   hipLaunchKernelGGL(decode_inputs_kernel, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t decode_attend_bf16(const DecodeArgs<bf16_t>& a, hipStream_t s) {
   const int per_wg = 4 * kGemvCols;
-  const int grid = (a.r + 3) / 4 + (2 * a.kvw + per_wg - 1) / per_wg + a.B +
-                   a.n_chunks * a.G * a.n_hb * a.B;
+  const int grid = (a.rt.learned() ? (a.r + 3) / 4 : 0) + (2 * a.kvw + per_wg - 1) / per_wg +
+                   a.B + a.n_chunks * a.G * a.n_hb * a.B;
   if (a.dh == 128) {
     if (a.R <= 16)
       hipLaunchKernelGGL((decode_attend_kernel<128, 16>), dim3(grid), dim3(256), 0, s, a);

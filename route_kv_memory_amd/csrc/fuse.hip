@@ -10,7 +10,10 @@
 
 namespace mka {
 
-template <typename T, int RMAX>
+// RMAX = 0: L3 disabled (no index or block read); USE_L2 = false: L2 disabled
+// (not read).  A disabled tier contributes an exact zero, as lambda = 0 with a
+// zero tier value, so the sum keeps its form and no unread value enters it.
+template <typename T, int RMAX, bool USE_L2>
 __global__ __launch_bounds__(256) void fuse_mix_kernel(const T* __restrict__ x,
                                                        const float* __restrict__ l2,
                                                        const float* __restrict__ means, int nb_cap,
@@ -22,64 +25,80 @@ __global__ __launch_bounds__(256) void fuse_mix_kernel(const T* __restrict__ x,
   const int ch = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
   if (ch >= D) return;
   const float l1w = lam[row * 3 + 0], l2w = lam[row * 3 + 1], l3w = lam[row * 3 + 2];
-  const int32_t* sel = idx + row * R;
-  const float* mb = means + static_cast<int64_t>(b) * nb_cap * D + ch;
-  int blk[RMAX];
-#pragma unroll
-  for (int i = 0; i < RMAX; ++i) blk[i] = i < R ? sel[i] : -1;
-  float xv[4], sv[4];
+  float xv[4], sv[4] = {0.f, 0.f, 0.f, 0.f}, mean[4] = {0.f, 0.f, 0.f, 0.f};
   load4(x + row * D + ch, xv);
-  load4(l2 + row * D + ch, sv);
-  // Every retrieved row is loaded unconditionally (unfilled slots read block 0
-  // and are not added), so the loads are in flight together; rank order.
-  float m[RMAX][4];
+  if constexpr (USE_L2) load4(l2 + row * D + ch, sv);
+  if constexpr (RMAX > 0) {
+    const int32_t* sel = idx + row * R;
+    const float* mb = means + static_cast<int64_t>(b) * nb_cap * D + ch;
+    int blk[RMAX];
 #pragma unroll
-  for (int i = 0; i < RMAX; ++i) load4(mb + static_cast<int64_t>(max(blk[i], 0)) * D, m[i]);
-  float l3[4] = {0.f, 0.f, 0.f, 0.f};
-  int cnt = 0;
+    for (int i = 0; i < RMAX; ++i) blk[i] = i < R ? sel[i] : -1;
+    // Every retrieved row is loaded unconditionally (unfilled slots read block
+    // 0 and are not added), so the loads are in flight together; rank order.
+    float m[RMAX][4];
 #pragma unroll
-  for (int i = 0; i < RMAX; ++i) {
-    const bool on = blk[i] >= 0;
+    for (int i = 0; i < RMAX; ++i) load4(mb + static_cast<int64_t>(max(blk[i], 0)) * D, m[i]);
+    float l3[4] = {0.f, 0.f, 0.f, 0.f};
+    int cnt = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) l3[k] += on ? m[i][k] : 0.f;
-    cnt += on;
+    for (int i = 0; i < RMAX; ++i) {
+      const bool on = blk[i] >= 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) l3[k] += on ? m[i][k] : 0.f;
+      cnt += on;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) mean[k] = cnt ? l3[k] / static_cast<float>(cnt) : 0.f;
   }
   float out[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float mean = cnt ? l3[k] / static_cast<float>(cnt) : 0.f;
-    out[k] = l1w * xv[k] + l2w * sv[k] + l3w * mean;
-  }
+  for (int k = 0; k < 4; ++k) out[k] = l1w * xv[k] + l2w * sv[k] + l3w * mean[k];
   store4(xf + row * D + ch, out);
+}
+
+template <typename T, bool USE_L2>
+hipError_t fuse_mix_launch(dim3 grid, int threads, const T* x, const float* l2,
+                           const float* means, int nb_cap, const int32_t* idx, const float* lam,
+                           int seq, int D, int R, bool use_l3, T* xf, hipStream_t s) {
+  if (!use_l3)
+    hipLaunchKernelGGL((fuse_mix_kernel<T, 0, USE_L2>), grid, dim3(threads), 0, s, x, l2, means,
+                       nb_cap, idx, lam, seq, D, R, xf);
+  else if (R <= 4)
+    hipLaunchKernelGGL((fuse_mix_kernel<T, 4, USE_L2>), grid, dim3(threads), 0, s, x, l2, means,
+                       nb_cap, idx, lam, seq, D, R, xf);
+  else if (R <= 8)
+    hipLaunchKernelGGL((fuse_mix_kernel<T, 8, USE_L2>), grid, dim3(threads), 0, s, x, l2, means,
+                       nb_cap, idx, lam, seq, D, R, xf);
+  else if (R <= 16)
+    hipLaunchKernelGGL((fuse_mix_kernel<T, 16, USE_L2>), grid, dim3(threads), 0, s, x, l2, means,
+                       nb_cap, idx, lam, seq, D, R, xf);
+  else
+    hipLaunchKernelGGL((fuse_mix_kernel<T, 32, USE_L2>), grid, dim3(threads), 0, s, x, l2, means,
+                       nb_cap, idx, lam, seq, D, R, xf);
+  return hipGetLastError();
 }
 
 template <typename T>
 hipError_t fuse_mix(const T* x, const float* l2, const float* means, int nb_cap,
-                    const int32_t* idx, const float* lam, int B, int seq, int D, int R, T* xf,
-                    hipStream_t s) {
+                    const int32_t* idx, const float* lam, int B, int seq, int D, int R,
+                    Routing rt, T* xf, hipStream_t s) {
   // Few tokens: narrow workgroups so that many of them share the row.
   const int threads = static_cast<int64_t>(B) * seq <= 8 ? 64 : 256;
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(B) * seq),
                   (D + 4 * threads - 1) / (4 * threads));
-  if (R <= 4)
-    hipLaunchKernelGGL((fuse_mix_kernel<T, 4>), grid, dim3(threads), 0, s, x, l2, means, nb_cap,
-                       idx, lam, seq, D, R, xf);
-  else if (R <= 8)
-    hipLaunchKernelGGL((fuse_mix_kernel<T, 8>), grid, dim3(threads), 0, s, x, l2, means, nb_cap,
-                       idx, lam, seq, D, R, xf);
-  else if (R <= 16)
-    hipLaunchKernelGGL((fuse_mix_kernel<T, 16>), grid, dim3(threads), 0, s, x, l2, means, nb_cap,
-                       idx, lam, seq, D, R, xf);
-  else
-    hipLaunchKernelGGL((fuse_mix_kernel<T, 32>), grid, dim3(threads), 0, s, x, l2, means, nb_cap,
-                       idx, lam, seq, D, R, xf);
-  return hipGetLastError();
+  if (rt.l2())
+    return fuse_mix_launch<T, true>(grid, threads, x, l2, means, nb_cap, idx, lam, seq, D, R,
+                                    rt.l3(), xf, s);
+  return fuse_mix_launch<T, false>(grid, threads, x, l2, means, nb_cap, idx, lam, seq, D, R,
+                                   rt.l3(), xf, s);
 }
 
 template hipError_t fuse_mix<float>(const float*, const float*, const float*, int, const int32_t*,
-                                    const float*, int, int, int, int, float*, hipStream_t);
+                                    const float*, int, int, int, int, Routing, float*,
+                                    hipStream_t);
 template hipError_t fuse_mix<bf16_t>(const bf16_t*, const float*, const float*, int,
-                                     const int32_t*, const float*, int, int, int, int, bf16_t*,
-                                     hipStream_t);
+                                     const int32_t*, const float*, int, int, int, int, Routing,
+                                     bf16_t*, hipStream_t);
 
 }  // namespace mka

@@ -7,17 +7,21 @@
 namespace mka {
 
 // ---- router: lambda = softmax(GELU(Q W_r1) W_r2) ---------------------------
+// Every router applies the routing variant ``rt`` to the logits.
 // MFMA path: bf16, router_hidden in {32, 64}, q_width % 64 == 0.
 hipError_t router_bf16_mfma(const bf16_t* q, int M, int qw, const bf16_t* w1, int r,
-                            const bf16_t* w2, float* lam, hipStream_t s);
+                            const bf16_t* w2, float* lam, Routing rt, hipStream_t s);
 // Few tokens: the hidden layer comes from a small-M product (gemv with a GELU
 // epilogue); this applies the second layer and the softmax.
 template <typename T>
-hipError_t router_head(const float* hidden, int M, int r, const T* w2, float* lam, hipStream_t s);
+hipError_t router_head(const float* hidden, int M, int r, const T* w2, float* lam, Routing rt,
+                       hipStream_t s);
 // One workgroup per token: any type, r <= 256 (fp32 path).
 template <typename T>
 hipError_t router_rowwise(const T* q, int M, int qw, const T* w1, int r, const T* w2, float* lam,
-                          hipStream_t s);
+                          Routing rt, hipStream_t s);
+// Variants whose lambda does not depend on the router: the constant vector.
+hipError_t lambda_fixed(float* lam, int M, Routing rt, hipStream_t s);
 
 // ---- EMA scan and block means ------------------------------------------------
 constexpr int kEmaChunk = 64;  // tokens per scan chunk
@@ -61,8 +65,8 @@ hipError_t topr_rows(const uint64_t* keys, int B, int seq, int64_t pos0, const u
 // multiple of 4, at most 1024).
 template <typename T>
 hipError_t fuse_mix(const T* x, const float* l2, const float* means, int nb_cap,
-                    const int32_t* idx, const float* lam, int B, int seq, int D, int R, T* xf,
-                    hipStream_t s);
+                    const int32_t* idx, const float* lam, int B, int seq, int D, int R,
+                    Routing rt, T* xf, hipStream_t s);
 
 // block_kv[b, blk, :] = m_blk [W_k; W_v]^T (float32) for blocks first .. first+n_blocks-1.
 template <typename T>

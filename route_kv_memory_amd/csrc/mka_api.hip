@@ -18,6 +18,13 @@
 
 using namespace mka;
 
+static_assert(MKA_ROUTE_SOFT == kRouteSoft && MKA_ROUTE_FIXED == kRouteFixed &&
+                  MKA_ROUTE_TOP1 == kRouteTop1 && MKA_ROUTE_TOP2 == kRouteTop2,
+              "routing modes");
+static_assert(MKA_TIERS_ALL == kTiersAll && MKA_TIERS_L1_L2 == kTiersL1L2 &&
+                  MKA_TIERS_L1_L3 == kTiersL1L3 && MKA_TIERS_L1 == kTiersL1,
+              "tier sets");
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -56,6 +63,8 @@ int check_dims(const mka_dims* d) {
   MKA_CHECK(std::isfinite(d->ema_decay) && d->ema_decay >= 0.f && d->ema_decay < 1.f,
             MKA_ERR_INVALID);
   MKA_CHECK(d->dtype == MKA_F32 || d->dtype == MKA_BF16, MKA_ERR_INVALID);
+  MKA_CHECK(d->route_mode >= MKA_ROUTE_SOFT && d->route_mode <= MKA_ROUTE_TOP2, MKA_ERR_INVALID);
+  MKA_CHECK(d->tiers >= MKA_TIERS_ALL && d->tiers <= MKA_TIERS_L1, MKA_ERR_INVALID);
   MKA_CHECK(d->head_dim == 64 || d->head_dim == 128, MKA_ERR_UNSUPPORTED);
   MKA_CHECK(d->top_r <= 32, MKA_ERR_UNSUPPORTED);
   MKA_CHECK(d->router_hidden <= 256, MKA_ERR_UNSUPPORTED);
@@ -71,6 +80,8 @@ int check_dims(const mka_dims* d) {
 }
 
 int rows_of(const mka_dims* d) { return d->batch * d->seq; }
+
+Routing routing_of(const mka_dims* d) { return Routing{d->route_mode, d->tiers}; }
 
 size_t ema_ws(const mka_dims* d) { return round256(ema_ws_bytes(d->batch, d->seq, d->d_model)); }
 size_t fuse_ws(const mka_dims* d) {
@@ -133,6 +144,11 @@ int do_qproj(const mka_dims* d, const void* x, const void* w_q, void* q_out, hip
 int do_router(const mka_dims* d, const void* q_in, const void* w_r1, const void* w_r2, float* lam,
               void* ws, hipStream_t s) {
   const int M = rows_of(d), qw = d->n_heads * d->head_dim, r = d->router_hidden;
+  const Routing rt = routing_of(d);
+  if (!rt.learned()) {
+    MKA_LAUNCH("route/fixed", lambda_fixed(lam, M, rt, s));
+    return MKA_OK;
+  }
   if (d->dtype == MKA_BF16) {
     const bf16_t* q = static_cast<const bf16_t*>(q_in);
     const bf16_t* w1 = static_cast<const bf16_t*>(w_r1);
@@ -140,11 +156,11 @@ int do_router(const mka_dims* d, const void* q_in, const void* w_r1, const void*
     if (M <= kFewRows) {
       float* hid = static_cast<float*>(ws);
       MKA_LAUNCH("route/hidden", gemv<bf16_t>(q, qw, M, w1, w1, r, r, qw, EpiGelu{hid, r}, s));
-      MKA_LAUNCH("route/head", router_head<bf16_t>(hid, M, r, w2, lam, s));
+      MKA_LAUNCH("route/head", router_head<bf16_t>(hid, M, r, w2, lam, rt, s));
     } else if (r == 32 || r == 64) {
-      MKA_LAUNCH("route/router", router_bf16_mfma(q, M, qw, w1, r, w2, lam, s));
+      MKA_LAUNCH("route/router", router_bf16_mfma(q, M, qw, w1, r, w2, lam, rt, s));
     } else {
-      MKA_LAUNCH("route/router", router_rowwise<bf16_t>(q, M, qw, w1, r, w2, lam, s));
+      MKA_LAUNCH("route/router", router_rowwise<bf16_t>(q, M, qw, w1, r, w2, lam, rt, s));
     }
   } else {
     const float* q = static_cast<const float*>(q_in);
@@ -153,9 +169,9 @@ int do_router(const mka_dims* d, const void* q_in, const void* w_r1, const void*
     if (M <= kFewRows) {
       float* hid = static_cast<float*>(ws);
       MKA_LAUNCH("route/hidden", gemv<float>(q, qw, M, w1, w1, r, r, qw, EpiGelu{hid, r}, s));
-      MKA_LAUNCH("route/head", router_head<float>(hid, M, r, w2, lam, s));
+      MKA_LAUNCH("route/head", router_head<float>(hid, M, r, w2, lam, rt, s));
     } else {
-      MKA_LAUNCH("route/router", router_rowwise<float>(q, M, qw, w1, r, w2, lam, s));
+      MKA_LAUNCH("route/router", router_rowwise<float>(q, M, qw, w1, r, w2, lam, rt, s));
     }
   }
   return MKA_OK;
@@ -229,10 +245,16 @@ int do_fuse_kv(const mka_dims* d, const void* x, const float* l2, const float* m
                const int32_t* idx, const float* lam, const void* w_k, const void* w_v, void* kc,
                void* vc, int64_t pos0, int64_t t_cap, void* ws, hipStream_t s) {
   const int M = rows_of(d), D = d->d_model, kvw = d->n_kv_heads * d->head_dim;
+  const Routing rt = routing_of(d);
+  // L1 alone: X_fused = x (lambda = (1, 0, 0)), projected without a fusion pass
   if (d->dtype == MKA_BF16) {
-    bf16_t* xf = static_cast<bf16_t*>(ws);
-    MKA_LAUNCH("fuse", fuse_mix<bf16_t>(static_cast<const bf16_t*>(x), l2, means, nb_cap, idx, lam,
-                                        d->batch, d->seq, D, d->top_r, xf, s));
+    const bf16_t* xf = static_cast<const bf16_t*>(x);
+    if (rt.ema()) {
+      bf16_t* mix = static_cast<bf16_t*>(ws);
+      MKA_LAUNCH("fuse", fuse_mix<bf16_t>(static_cast<const bf16_t*>(x), l2, means, nb_cap, idx,
+                                          lam, d->batch, d->seq, D, d->top_r, rt, mix, s));
+      xf = mix;
+    }
     const EpiKV<bf16_t> epi{static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), d->seq,
                             d->n_kv_heads, d->head_dim, t_cap, pos0};
     const bf16_t* wk = static_cast<const bf16_t*>(w_k);
@@ -242,9 +264,13 @@ int do_fuse_kv(const mka_dims* d, const void* x, const float* l2, const float* m
     else
       MKA_LAUNCH("kv_gemm", gemm_bf16(xf, D, wk, wv, kvw, M, 2 * kvw, D, epi, s));
   } else {
-    float* xf = static_cast<float*>(ws);
-    MKA_LAUNCH("fuse", fuse_mix<float>(static_cast<const float*>(x), l2, means, nb_cap, idx, lam,
-                                       d->batch, d->seq, D, d->top_r, xf, s));
+    const float* xf = static_cast<const float*>(x);
+    if (rt.ema()) {
+      float* mix = static_cast<float*>(ws);
+      MKA_LAUNCH("fuse", fuse_mix<float>(static_cast<const float*>(x), l2, means, nb_cap, idx,
+                                         lam, d->batch, d->seq, D, d->top_r, rt, mix, s));
+      xf = mix;
+    }
     const EpiKV<float> epi{static_cast<float*>(kc), static_cast<float*>(vc), d->seq, d->n_kv_heads,
                            d->head_dim, t_cap, pos0};
     const float* wk = static_cast<const float*>(w_k);
@@ -507,9 +533,13 @@ int mka_fuse_kv_proj(const mka_dims* d, const void* x, const float* l2, const fl
                      void* ws, size_t ws_bytes, void* stream) {
   int rc = check_dims(d);
   if (rc) return rc;
-  MKA_CHECK(ptrs_ok({x, l2, idx, lambda, w_k, w_v, k_cache, v_cache}), MKA_ERR_INVALID);
+  const Routing rt = routing_of(d);  // inputs of disabled tiers are not read
+  MKA_CHECK(ptrs_ok({x, lambda, w_k, w_v, k_cache, v_cache}), MKA_ERR_INVALID);
+  MKA_CHECK(!rt.l2() || ptrs_ok({l2}), MKA_ERR_INVALID);
+  MKA_CHECK(!rt.l3() || ptrs_ok({idx}), MKA_ERR_INVALID);
   MKA_CHECK(pos0 >= 0 && nb_cap >= 0 && pos0 + d->seq <= t_cap, MKA_ERR_INVALID);
-  if ((pos0 + d->seq - 1) / d->block > 0) MKA_CHECK(ptrs_ok({block_means}), MKA_ERR_INVALID);
+  if (rt.l3() && (pos0 + d->seq - 1) / d->block > 0)
+    MKA_CHECK(ptrs_ok({block_means}), MKA_ERR_INVALID);
   MKA_CHECK(ptrs_ok({ws}), MKA_ERR_WORKSPACE);
   MKA_CHECK(ws_bytes >= fuse_ws(d), MKA_ERR_WORKSPACE);
   return do_fuse_kv(d, x, l2, block_means, nb_cap, idx, lambda, w_k, w_v, k_cache, v_cache, pos0,
@@ -570,8 +600,10 @@ int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weight
   MKA_CHECK(ws_bytes >= need, MKA_ERR_WORKSPACE);
   MKA_CHECK(need == 0 || ptrs_ok({ws}), MKA_ERR_WORKSPACE);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const Routing rt = routing_of(d);
   int64_t first, n;
   completed_blocks(d, pos0, &first, &n);
+  if (!rt.l3()) n = 0;  // no block codes or projections without L3
   char* ws_chain = static_cast<char*>(ws);
   char* ws_main = ws_chain + prefill_chain_ws(d);
   // The EMA scan and the block codes need only x and use no LDS, so they run
@@ -586,8 +618,8 @@ int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weight
   hipStream_t s2 = aux->stream;
   MKA_LAUNCH("prefill/fork", hipEventRecord(aux->fork, s));
   MKA_LAUNCH("prefill/fork", hipStreamWaitEvent(s2, aux->fork, 0));
-  if ((rc = do_ema(d, x, pos0, st->ema_state, st->block_acc, out->l2, st->block_means, st->nb_cap,
-                   ws_chain, s2)))
+  if (rt.ema() && (rc = do_ema(d, x, pos0, st->ema_state, st->block_acc, out->l2,
+                               st->block_means, st->nb_cap, ws_chain, s2)))
     return rc;
   if ((rc = do_index(d, st->block_means, st->nb_cap, static_cast<int>(first), static_cast<int>(n),
                      w->proj, st->block_hash, ws_chain, s2)))
@@ -599,8 +631,8 @@ int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weight
   MKA_LAUNCH("prefill/join", hipEventRecord(aux->done, s2));
   if ((rc = do_route(d, x, w->w_q, w->w_r1, w->w_r2, out->q, out->lambda, ws_main, s))) return rc;
   MKA_LAUNCH("prefill/join", hipStreamWaitEvent(s, aux->join, 0));
-  if ((rc = do_retrieve(d, out->l2, w->proj, st->block_hash, st->nb_cap, pos0, out->key, out->idx,
-                        ws_main, s)))
+  if (rt.l3() && (rc = do_retrieve(d, out->l2, w->proj, st->block_hash, st->nb_cap, pos0,
+                                   out->key, out->idx, ws_main, s)))
     return rc;
   if ((rc = do_fuse_kv(d, x, out->l2, st->block_means, st->nb_cap, out->idx, out->lambda, w->w_k,
                        w->w_v, st->k_cache, st->v_cache, pos0, st->t_cap, ws_main, s)))
@@ -635,7 +667,8 @@ int mka_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_wei
   void* w_index = base + L.attn + L.hid + L.part + L.kv + L.xf;
   const int B = d->batch, D = d->d_model, H = d->n_heads, G = d->n_kv_heads, dh = d->head_dim;
   const int qw = H * dh, kvw = G * dh;
-  const bool closes = (pos + 1) % d->block == 0;
+  const Routing rt = routing_of(d);
+  const bool closes = rt.l3() && (pos + 1) % d->block == 0;
   const int closed_block = static_cast<int>((pos + 1) / d->block - 1);
 
   auto fill = [&](auto* tag) {
@@ -692,6 +725,7 @@ int mka_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_wei
     a.part_l = w_attn + np;
     a.part_o = w_attn + 2 * np;
     a.o = static_cast<T*>(out->o);
+    a.rt = rt;
     return a;
   };
 
@@ -716,7 +750,7 @@ int mka_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_wei
     MKA_LAUNCH("decode/attend", decode_attend_bf16(a, s));
     MKA_LAUNCH("decode/merge", decode_merge_bf16(a, s));
   }
-  if (closes) {  // the block this token closes joins the bank for the next tokens
+  if (closes) {  // the block this token closes joins the L3 bank for the next tokens
     if ((rc = do_index(d, st->block_means, st->nb_cap, closed_block, 1, w->proj, st->block_hash,
                        w_index, s)))
       return rc;

@@ -1,19 +1,11 @@
 // Router of the FastMKA layer: lambda = softmax(GELU(q W_r1) W_r2), one
 // 3-vector per token over the tiers (L1, L2, L3).  MKA reading note, method
-// section 2 (routing gate from the query, per token and layer).
+// section 2 (routing gate from the query, per token and layer).  The last
+// step applies the routing variant (route_weights): the plain softmax, or
+// hard top-k / a tier subset as in the abstract page's Tables 9 and 10.
 #include "kernels.h"
 
 namespace mka {
-
-// Softmax of three logits, max-shifted.
-__device__ __forceinline__ void softmax3(const float* z, float* out) {
-  const float m = fmaxf(z[0], fmaxf(z[1], z[2]));
-  const float e0 = expf(z[0] - m), e1 = expf(z[1] - m), e2 = expf(z[2] - m);
-  const float inv = 1.0f / (e0 + e1 + e2);
-  out[0] = e0 * inv;
-  out[1] = e1 * inv;
-  out[2] = e2 * inv;
-}
 
 // ---------------------------------------------------------------------------
 // MFMA router (bf16): a workgroup takes 32 tokens; its 4 waves split the
@@ -27,7 +19,7 @@ template <int NB>  // NB = r / 32 output blocks
 __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restrict__ Q, int M, int qw,
                                                           const bf16_t* __restrict__ W1,
                                                           const bf16_t* __restrict__ W2,
-                                                          float* __restrict__ lam) {
+                                                          float* __restrict__ lam, Routing rt) {
   constexpr int R = NB * 32;
   __shared__ float part[4][32][R + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
@@ -70,7 +62,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restri
       z[c] = sum;
     }
     float out[3];
-    softmax3(z, out);
+    route_weights(z, rt, out);
     float* dst = lam + static_cast<int64_t>(row0 + tid) * 3;
     dst[0] = out[0];
     dst[1] = out[1];
@@ -79,12 +71,12 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restri
 }
 
 hipError_t router_bf16_mfma(const bf16_t* q, int M, int qw, const bf16_t* w1, int r,
-                            const bf16_t* w2, float* lam, hipStream_t s) {
+                            const bf16_t* w2, float* lam, Routing rt, hipStream_t s) {
   const dim3 grid((M + 31) / 32);
   if (r == 64)
-    hipLaunchKernelGGL(router_mfma_kernel<2>, grid, dim3(256), 0, s, q, M, qw, w1, w2, lam);
+    hipLaunchKernelGGL(router_mfma_kernel<2>, grid, dim3(256), 0, s, q, M, qw, w1, w2, lam, rt);
   else
-    hipLaunchKernelGGL(router_mfma_kernel<1>, grid, dim3(256), 0, s, q, M, qw, w1, w2, lam);
+    hipLaunchKernelGGL(router_mfma_kernel<1>, grid, dim3(256), 0, s, q, M, qw, w1, w2, lam, rt);
   return hipGetLastError();
 }
 
@@ -97,7 +89,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void router_rowwise_kernel(const T* __restrict__ Q, int qw,
                                                              const T* __restrict__ W1, int r,
                                                              const T* __restrict__ W2,
-                                                             float* __restrict__ lam) {
+                                                             float* __restrict__ lam, Routing rt) {
   __shared__ float hid[256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row = blockIdx.x;
@@ -127,7 +119,7 @@ __global__ __launch_bounds__(256) void router_rowwise_kernel(const T* __restrict
       z[c] = sum;
     }
     float out[3];
-    softmax3(z, out);
+    route_weights(z, rt, out);
     lam[row * 3 + 0] = out[0];
     lam[row * 3 + 1] = out[1];
     lam[row * 3 + 2] = out[2];
@@ -136,8 +128,8 @@ __global__ __launch_bounds__(256) void router_rowwise_kernel(const T* __restrict
 
 template <typename T>
 hipError_t router_rowwise(const T* q, int M, int qw, const T* w1, int r, const T* w2, float* lam,
-                          hipStream_t s) {
-  hipLaunchKernelGGL(router_rowwise_kernel<T>, dim3(M), dim3(256), 0, s, q, qw, w1, r, w2, lam);
+                          Routing rt, hipStream_t s) {
+  hipLaunchKernelGGL(router_rowwise_kernel<T>, dim3(M), dim3(256), 0, s, q, qw, w1, r, w2, lam, rt);
   return hipGetLastError();
 }
 
@@ -146,7 +138,7 @@ hipError_t router_rowwise(const T* q, int M, int qw, const T* w1, int r, const T
 template <typename T>
 __global__ __launch_bounds__(64) void router_head_kernel(const float* __restrict__ hidden, int r,
                                                          const T* __restrict__ W2,
-                                                         float* __restrict__ lam) {
+                                                         float* __restrict__ lam, Routing rt) {
   const int lane = threadIdx.x, row = blockIdx.x;
   float z[3];
 #pragma unroll
@@ -157,7 +149,7 @@ __global__ __launch_bounds__(64) void router_head_kernel(const float* __restrict
   }
   if (lane == 0) {
     float out[3];
-    softmax3(z, out);
+    route_weights(z, rt, out);
     lam[static_cast<int64_t>(row) * 3 + 0] = out[0];
     lam[static_cast<int64_t>(row) * 3 + 1] = out[1];
     lam[static_cast<int64_t>(row) * 3 + 2] = out[2];
@@ -165,16 +157,32 @@ __global__ __launch_bounds__(64) void router_head_kernel(const float* __restrict
 }
 
 template <typename T>
-hipError_t router_head(const float* hidden, int M, int r, const T* w2, float* lam, hipStream_t s) {
-  hipLaunchKernelGGL(router_head_kernel<T>, dim3(M), dim3(64), 0, s, hidden, r, w2, lam);
+hipError_t router_head(const float* hidden, int M, int r, const T* w2, float* lam, Routing rt,
+                       hipStream_t s) {
+  hipLaunchKernelGGL(router_head_kernel<T>, dim3(M), dim3(64), 0, s, hidden, r, w2, lam, rt);
   return hipGetLastError();
 }
-template hipError_t router_head<float>(const float*, int, int, const float*, float*, hipStream_t);
-template hipError_t router_head<bf16_t>(const float*, int, int, const bf16_t*, float*, hipStream_t);
+template hipError_t router_head<float>(const float*, int, int, const float*, float*, Routing,
+                                       hipStream_t);
+template hipError_t router_head<bf16_t>(const float*, int, int, const bf16_t*, float*, Routing,
+                                        hipStream_t);
 
 template hipError_t router_rowwise<float>(const float*, int, int, const float*, int, const float*,
-                                          float*, hipStream_t);
+                                          float*, Routing, hipStream_t);
 template hipError_t router_rowwise<bf16_t>(const bf16_t*, int, int, const bf16_t*, int,
-                                           const bf16_t*, float*, hipStream_t);
+                                           const bf16_t*, float*, Routing, hipStream_t);
+
+// lambda of the variants that do not use the router (fixed weights, or L1
+// alone): the same 3-vector for every token.
+__global__ __launch_bounds__(256) void lambda_fixed_kernel(float* __restrict__ lam, int M,
+                                                           Routing rt) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e < 3 * M) lam[e] = rt.fixed_weight(e % 3);
+}
+
+hipError_t lambda_fixed(float* lam, int M, Routing rt, hipStream_t s) {
+  hipLaunchKernelGGL(lambda_fixed_kernel, dim3((3 * M + 255) / 256), dim3(256), 0, s, lam, M, rt);
+  return hipGetLastError();
+}
 
 }  // namespace mka

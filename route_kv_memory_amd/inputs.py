@@ -88,6 +88,8 @@ class LayerShape:
     n_sampled: int = 0  # >0: full-size checks look at this many sampled rows
     decode_cached: int = 0  # >0: a decode workload with this many cached tokens
     decode_steps: int = 0
+    route_mode: str = "soft"  # "soft", "fixed", "top1", "top2"
+    tiers: str = "l1l2l3"  # enabled tiers: "l1l2l3", "l1l2", "l1l3", "l1"
 
     @property
     def n_blocks(self) -> int:

@@ -17,7 +17,9 @@ import re
 __all__ = [
     "MkaError", "Dims", "Weights", "State", "Outputs", "lib", "dims", "exported_symbols",
     "header_symbols", "MKA_F32", "MKA_BF16", "MKA_OK", "MKA_ERR_INVALID", "MKA_ERR_UNSUPPORTED",
-    "MKA_ERR_WORKSPACE", "MKA_ERR_HIP", "MKA_OP_EMA_SCAN", "MKA_OP_FUSE_KV", "MKA_OP_ATTN_DECODE",
+    "MKA_ERR_WORKSPACE", "MKA_ERR_HIP", "MKA_ROUTE_SOFT", "MKA_ROUTE_FIXED", "MKA_ROUTE_TOP1",
+    "MKA_ROUTE_TOP2", "MKA_TIERS_ALL", "MKA_TIERS_L1_L2", "MKA_TIERS_L1_L3", "MKA_TIERS_L1",
+    "ROUTE_MODES", "TIER_SETS", "MKA_OP_EMA_SCAN", "MKA_OP_FUSE_KV", "MKA_OP_ATTN_DECODE",
     "MKA_OP_PREFILL", "MKA_OP_DECODE_STEP", "MKA_OP_RETRIEVE", "MKA_OP_INDEX", "MKA_OP_ROUTE",
     "mka_route", "mka_ema_scan", "mka_l3_index", "mka_l3_block_kv", "mka_l3_retrieve",
     "mka_fuse_kv_proj",
@@ -30,6 +32,12 @@ LIB_PATH = os.path.join(PKG, "libmka.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "mka.h")
 
 MKA_F32, MKA_BF16 = 0, 1
+MKA_ROUTE_SOFT, MKA_ROUTE_FIXED, MKA_ROUTE_TOP1, MKA_ROUTE_TOP2 = range(4)
+MKA_TIERS_ALL, MKA_TIERS_L1_L2, MKA_TIERS_L1_L3, MKA_TIERS_L1 = range(4)
+ROUTE_MODES = {"soft": MKA_ROUTE_SOFT, "fixed": MKA_ROUTE_FIXED, "top1": MKA_ROUTE_TOP1,
+               "top2": MKA_ROUTE_TOP2}
+TIER_SETS = {"l1l2l3": MKA_TIERS_ALL, "l1l2": MKA_TIERS_L1_L2, "l1l3": MKA_TIERS_L1_L3,
+             "l1": MKA_TIERS_L1}
 MKA_OK, MKA_ERR_INVALID, MKA_ERR_UNSUPPORTED, MKA_ERR_WORKSPACE, MKA_ERR_HIP = 0, -1, -2, -3, -4
 (MKA_OP_EMA_SCAN, MKA_OP_FUSE_KV, MKA_OP_ATTN_DECODE, MKA_OP_PREFILL, MKA_OP_DECODE_STEP,
  MKA_OP_RETRIEVE, MKA_OP_INDEX, MKA_OP_ROUTE) = range(8)
@@ -50,6 +58,7 @@ class Dims(ctypes.Structure):
         ("n_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("router_hidden", ctypes.c_int32), ("block", ctypes.c_int32), ("hash_bits", ctypes.c_int32),
         ("top_r", ctypes.c_int32), ("ema_decay", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("route_mode", ctypes.c_int32), ("tiers", ctypes.c_int32),
     ]
 
 
@@ -156,7 +165,8 @@ def dims(shape, seq=None, batch=None) -> Dims:
                 n_heads=shape.n_heads, n_kv_heads=shape.n_kv_heads, head_dim=shape.head_dim,
                 router_hidden=shape.router_hidden, block=shape.block, hash_bits=shape.hash_bits,
                 top_r=shape.top_r, ema_decay=shape.ema_decay,
-                dtype=MKA_BF16 if shape.dtype == "bf16" else MKA_F32)
+                dtype=MKA_BF16 if shape.dtype == "bf16" else MKA_F32,
+                route_mode=ROUTE_MODES[shape.route_mode], tiers=TIER_SETS[shape.tiers])
 
 
 # ----------------------------------------------------------------- C entries

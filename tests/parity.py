@@ -30,7 +30,9 @@ def log(msg):
 def oracle_kwargs(s):
     """Hyper-parameters as the GPU receives them (the decay as float32)."""
     return dict(n_heads=s.n_heads, n_kv_heads=s.n_kv_heads,
-                ema_decay=float(np.float32(s.ema_decay)), block=s.block, top_r=s.top_r)
+                ema_decay=float(np.float32(s.ema_decay)), block=s.block, top_r=s.top_r,
+                route_mode=s.route_mode, tiers=s.tiers,
+                decide_q="bf16" if s.dtype == "bf16" else "f64")
 
 
 def check_close(name, got, ref, dtype, max_abs=None, mean_abs=None, rel_l2=None):
@@ -135,3 +137,21 @@ def check_idx_conditional(name, got_idx, got_keys, gpu_l2, gpu_means, gpu_bhash,
     bad = np.argwhere(np.any(ref != np.asarray(got_idx), axis=-1))
     assert len(bad) == 0, f"{name}: {len(bad)} rows differ from the oracle ranking of the GPU's codes"
     log(f"  {name}: conditional retrieval exact on {ref.shape[0] * ref.shape[1]} rows")
+
+
+def decision_margin(s, inp):
+    """Smallest gap, over the tokens of the seeded inputs ``inp``, between the
+    router logits on either side of the hard-routing cut (the k-th and
+    (k+1)-th largest enabled logits), in the precision the decision is taken
+    in (oracle arithmetic); inf when the variant takes no decision."""
+    k = {"top1": 1, "top2": 2}.get(s.route_mode)
+    on = {"l1l2l3": [0, 1, 2], "l1l2": [0, 1], "l1l3": [0, 2], "l1": [0]}[s.tiers]
+    if k is None or k >= len(on):
+        return np.inf
+    from oracle import mka_oracle as O
+    q = O.q_proj(inp["x"], inp["w_q"])
+    if s.dtype == "bf16":
+        q = O.round_bf16(q)
+    z = O.router_logits(q, inp["w_r1"], inp["w_r2"])[..., on]
+    zs = -np.sort(-z, axis=-1)
+    return float((zs[..., k - 1] - zs[..., k]).min())

@@ -45,6 +45,10 @@ def _d(**kw):
     ("ema_decay", 1.0, mka.MKA_ERR_INVALID),
     ("ema_decay", -0.1, mka.MKA_ERR_INVALID),
     ("dtype", 7, mka.MKA_ERR_INVALID),
+    ("route_mode", 4, mka.MKA_ERR_INVALID),
+    ("route_mode", -1, mka.MKA_ERR_INVALID),
+    ("tiers", 4, mka.MKA_ERR_INVALID),
+    ("tiers", -1, mka.MKA_ERR_INVALID),
     ("head_dim", 96, mka.MKA_ERR_UNSUPPORTED),
     ("top_r", 33, mka.MKA_ERR_UNSUPPORTED),
     ("d_model", 3584 + 32, mka.MKA_ERR_UNSUPPORTED),  # bf16 needs D % 64 == 0
@@ -131,3 +135,18 @@ def test_launch_without_device_reports_hip_error():
         mka.mka_attn_prefill(d, FAKE, FAKE, FAKE, 256, 0, FAKE, stream=0)
     assert e.value.status == mka.MKA_ERR_HIP
     assert mka.mka_last_error() != ""
+
+
+def test_routing_fields_follow_the_header():
+    # mka_dims ends with route_mode and tiers; zero means the full method.
+    assert [f[0] for f in mka.Dims._fields_][-2:] == ["route_mode", "tiers"]
+    assert ctypes.sizeof(mka.Dims) == 14 * 4
+    d = mka.dims(I.workload("tiny_f32"))
+    assert (d.route_mode, d.tiers) == (mka.MKA_ROUTE_SOFT, mka.MKA_TIERS_ALL)
+    text = open(mka.HEADER).read()
+    for name in ("MKA_ROUTE_SOFT = 0", "MKA_ROUTE_FIXED = 1", "MKA_ROUTE_TOP1 = 2",
+                 "MKA_ROUTE_TOP2 = 3", "MKA_TIERS_ALL = 0", "MKA_TIERS_L1_L2 = 1",
+                 "MKA_TIERS_L1_L3 = 2", "MKA_TIERS_L1 = 3"):
+        assert name in text
+        key, val = name.split(" = ")
+        assert getattr(mka, key) == int(val)
