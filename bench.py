@@ -6,8 +6,11 @@ One step = one whole-layer prefill of the Qwen2.5-7B-shaped layer (batch 2,
 C-ABI call mka_prefill: route (Q projection + router), EMA scan and block
 means, block index and projections, retrieval, fusion + K/V projection, causal
 flash attention.  Inputs are resident in HBM before timing starts.  ``value``
-is prefill tokens/s.  A second loop issues the stage calls one by one with HIP
-events between them for the per-stage breakdown and the attention roofline.
+is prefill tokens/s.  Before the warmup, untimed back-to-back steps run for
+``--settle-ms`` (the GPU's clocks ramp up over tens of milliseconds of load
+after an idle spell).  A second loop issues the stage calls one by one with
+HIP events between them for the per-stage breakdown and the attention
+roofline.  ``--variants`` adds the routing and tier variants.
 
 The same line carries the decode measurement (the 131072-token fused cache
 workload, 256 decode steps of ``mka_decode_step``: median microseconds per
@@ -53,6 +56,10 @@ KERNEL_SOURCES = {
     "gemm_bf16_kernel<128": ["gemm.hip", "gemm.h"],  # fused K/V projection
 }
 ROOFLINE_KERNEL = "attn_prefill_bf16_kernel"
+# The abstract page's ablations: Table 10 (fixed lambda = 1/3, hard top-2,
+# hard top-1) and Table 9 (L1+L2, L1+L3, L1 alone), as (route_mode, tiers).
+VARIANTS = [("fixed", "l1l2l3"), ("top2", "l1l2l3"), ("top1", "l1l2l3"), ("soft", "l1l2"),
+            ("soft", "l1l3"), ("soft", "l1")]
 COPY_KERNEL = "neg_kernel"  # torch.neg(out=): one read and one write per element
 
 
@@ -144,7 +151,22 @@ def prefill_flops(s):
     }
 
 
-def bench_prefill(s, steps, warmup):
+def settle(step_fn, ms):
+    """Untimed back-to-back steps for ``ms`` milliseconds of wall time: after an
+    idle spell the GPU's clocks take tens of milliseconds of load to come back
+    up, which a few warmup steps do not cover.  Returns the steps run."""
+    import torch
+
+    n, t0 = 0, time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            step_fn()
+        n += 8
+        torch.cuda.synchronize()
+    return n
+
+
+def bench_prefill(s, steps, warmup, variants=(), settle_ms=0.0):
     import torch
 
     from route_kv_memory_amd import mka
@@ -193,18 +215,30 @@ def bench_prefill(s, steps, warmup):
     # Timed: the composite mka_prefill (the summary chain on the library's
     # auxiliary stream beside the query product).  Every step starts from an
     # empty prefix (pos0 = 0), for which the state buffers are not read.
-    ev_step = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    for _ in range(warmup):
-        layer.prefill(x, 0, out=out, stream=stream)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(steps):
-        ev_step[k][0].record(stream)
-        layer.prefill(x, 0, out=out, stream=stream)
-        ev_step[k][1].record(stream)
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / steps
-    gpu_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev_step]))
+    settled = settle(lambda: layer.prefill(x, 0, out=out, stream=stream), settle_ms)
+
+    def composite():
+        ev_step = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for _ in range(warmup):
+            layer.prefill(x, 0, out=out, stream=stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            ev_step[k][0].record(stream)
+            layer.prefill(x, 0, out=out, stream=stream)
+            ev_step[k][1].record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        return wall * 1e3, float(np.mean([e[0].elapsed_time(e[1]) for e in ev_step]))
+
+    wall_ms, gpu_ms = composite()
+    # Routing variants: the same buffers and inputs, the layer's shape swapped.
+    var_ms = {}
+    for mode, tiers in variants:
+        layer.shape = s.replace(route_mode=mode, tiers=tiers)
+        var_ms[f"{mode}/{tiers}"] = composite()[0]
+        log(f"prefill variant {mode}/{tiers}: {var_ms[f'{mode}/{tiers}']:.4f} ms")
+    layer.shape = s
 
     # Breakdown: the same calls one by one on one stream, HIP events between
     # them (the attention stage is exactly one kernel launch).
@@ -217,10 +251,11 @@ def bench_prefill(s, steps, warmup):
     stage_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
                 for i, n in enumerate(names)}
     seq_ms = float(np.mean([e[0].elapsed_time(e[6]) for e in evs]))
-    return dict(wall_ms=wall * 1e3, gpu_ms=gpu_ms, stage_ms=stage_ms, sequential_ms=seq_ms)
+    return dict(wall_ms=wall_ms, gpu_ms=gpu_ms, stage_ms=stage_ms, sequential_ms=seq_ms,
+                variants_ms=var_ms, settle_steps=settled)
 
 
-def bench_decode(s, steps, warmup):
+def bench_decode(s, steps, warmup, variants=()):
     import torch
 
     from route_kv_memory_amd import mka
@@ -252,21 +287,33 @@ def bench_decode(s, steps, warmup):
 
     out = layer.outputs(1)
     stream = torch.cuda.current_stream()
-    reset()
-    for k in range(warmup):
-        layer.decode_step(tokens[k], T0 + k, out=out)
-    reset()
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    t0 = time.perf_counter()
-    ev[0].record(stream)
-    for k in range(steps):
-        layer.decode_step(tokens[k], T0 + k, out=out)
-        ev[k + 1].record(stream)
-    host_us = (time.perf_counter() - t0) / steps * 1e6  # enqueue cost per step
-    torch.cuda.synchronize()
-    wall_us = (time.perf_counter() - t0) / steps * 1e6
-    step_us = np.array([ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(steps)])
+
+    def run():
+        reset()
+        for k in range(warmup):
+            layer.decode_step(tokens[k], T0 + k, out=out)
+        reset()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        t0 = time.perf_counter()
+        ev[0].record(stream)
+        for k in range(steps):
+            layer.decode_step(tokens[k], T0 + k, out=out)
+            ev[k + 1].record(stream)
+        host_us = (time.perf_counter() - t0) / steps * 1e6  # enqueue cost per step
+        torch.cuda.synchronize()
+        wall_us = (time.perf_counter() - t0) / steps * 1e6
+        return np.array([ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(steps)]), host_us, wall_us
+
+    # Routing variants first (the same cache and state, the layer's shape
+    # swapped); the main measurement runs last, from a reset state.
+    var_us = {}
+    for mode, tiers in variants:
+        layer.shape = s.replace(route_mode=mode, tiers=tiers)
+        var_us[f"{mode}/{tiers}"] = float(np.median(run()[0]))
+        log(f"decode variant {mode}/{tiers}: {var_us[f'{mode}/{tiers}']:.1f} us/token")
+    layer.shape = s
+    step_us, host_us, wall_us = run()
 
     # Decode attention alone at the first step's length, for its roofline.
     L = T0 + 1
@@ -292,7 +339,7 @@ def bench_decode(s, steps, warmup):
                   + s.hash_bits * s.d_model * 4 + s.top_r * s.d_model * 4 + nb0 * 8)
     return dict(median_us=float(np.median(step_us)), mean_us=float(step_us.mean()),
                 wall_us=wall_us, host_us=host_us, attn_us=attn_us, kv_bytes=kv_bytes, step_bytes=step_bytes,
-                cached=T0, steps=steps)
+                cached=T0, steps=steps, variants_us=var_us)
 
 
 def cpu_baseline(s, n_tokens, batch):
@@ -335,6 +382,12 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle tokens per sequence "
                     "(0: the whole sequence)")
     ap.add_argument("--cpu-batch", type=int, default=0, help="oracle sequences (0: all)")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed back-to-back prefill steps for this long before the warmup "
+                         "(GPU clocks ramp up under load)")
+    ap.add_argument("--variants", action="store_true",
+                    help="also time the routing and tier variants (fixed, hard top-1/top-2; "
+                         "L1+L2, L1+L3, L1 alone) on the same workloads")
     args = ap.parse_args()
     if args.traffic_summary:
         res = traffic_summary(*args.traffic_summary, args.copy_calibration or 1024,
@@ -359,7 +412,8 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
     s = I.workload(args.workload)
-    pf = bench_prefill(s, args.steps, args.warmup)
+    variants = VARIANTS if args.variants else ()
+    pf = bench_prefill(s, args.steps, args.warmup, variants, args.settle_ms)
     flops = prefill_flops(s)
     tokens = s.batch * s.seq
     ms = pf["wall_ms"]
@@ -385,6 +439,9 @@ def main():
                    "n_heads": s.n_heads, "n_kv_heads": s.n_kv_heads, "head_dim": s.head_dim,
                    "block": s.block, "top_r": s.top_r, "hash_bits": s.hash_bits},
         "gpu_ms_per_step": pf["gpu_ms"],
+        "settle": {"ms": args.settle_ms, "steps": pf["settle_steps"],
+                   "note": "untimed back-to-back steps before the warmup, so that the timed "
+                           "steps run at the clocks of a loaded GPU"},
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "stages_note": "stage calls one by one on one stream (the timed composite overlaps the "
                        "ema/index/retrieve chain with route)",
@@ -396,7 +453,7 @@ def main():
     }
     if not args.no_decode:
         ds = I.workload(args.decode_workload)
-        dc = bench_decode(ds, ds.decode_steps, 8)
+        dc = bench_decode(ds, ds.decode_steps, 8, variants)
         attn_bw = dc["kv_bytes"] / (dc["attn_us"] * 1e-6)
         step_bw = dc["step_bytes"] / (dc["median_us"] * 1e-6)
         line["decode"] = {
@@ -410,6 +467,11 @@ def main():
                          "traffic": traffic_for("attn_decode_split_kernel"),
                          "us_per_launch": dc["attn_us"]},
         }
+    if variants:
+        line["variants"] = {
+            k: {"prefill_tokens_per_s": tokens / (v * 1e-3), "prefill_ms": v,
+                "decode_us_per_token": dc["variants_us"].get(k) if not args.no_decode else None}
+            for k, v in pf["variants_ms"].items()}
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a bounded sample")
         line["cpu_baseline"] = cpu_baseline(s, args.cpu_tokens or s.seq, args.cpu_batch or s.batch)
