@@ -342,6 +342,42 @@ def bench_decode(s, steps, warmup, variants=()):
                 cached=T0, steps=steps, variants_us=var_us)
 
 
+def onbox_peaks():
+    """Measured ceilings beside the published peaks: the library's dense bf16
+    MFMA loop (two workgroups per CU, ~20 ms) and a streaming read of 4 GiB
+    (beyond the last-level cache), each the median of 5 timed runs."""
+    import torch
+
+    from route_kv_memory_amd import mka
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    wg, iters = 2 * cus, 40000
+    sink = torch.empty(max(wg, mka.PROBE_STREAM_WORKGROUPS), dtype=torch.float32, device="cuda")
+    flops = wg * 4 * iters * 4 * 32768.0
+
+    def timed(fn, reps=5):
+        fn()
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(out))
+
+    t_mfma = timed(lambda: mka.mka_probe_mfma_bf16(wg, iters, sink, stream))
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    t_read = timed(lambda: mka.mka_probe_stream_read(buf, nbytes, sink, stream))
+    del buf
+    return {"mfma_bf16_tflops": flops / t_mfma / 1e12, "hbm_read_gbs": nbytes / t_read / 1e9,
+            "note": "library probes: dense 32x32x16 bf16 MFMA loop (clocks drop under "
+                    "sustained matrix load) and a 4 GiB streaming read"}
+
+
 def cpu_baseline(s, n_tokens, batch):
     """The oracle, as it stands, on the first ``n_tokens`` of ``batch`` sequences."""
     from oracle import mka_oracle as O
@@ -415,6 +451,9 @@ def main():
     variants = VARIANTS if args.variants else ()
     pf = bench_prefill(s, args.steps, args.warmup, variants, args.settle_ms)
     flops = prefill_flops(s)
+    onbox = onbox_peaks()
+    log(f"on-box peaks: {onbox['mfma_bf16_tflops']:.0f} TFLOP/s bf16 MFMA, "
+        f"{onbox['hbm_read_gbs']:.0f} GB/s streaming read")
     tokens = s.batch * s.seq
     ms = pf["wall_ms"]
     stage_ms = pf["stage_ms"]
@@ -449,7 +488,10 @@ def main():
         "prefill_tflops": sum(flops.values()) / (pf["gpu_ms"] * 1e-3) / 1e12,
         "roofline": {"kernel": ROOFLINE_KERNEL, "bound": "mfma", "achieved": achieved / 1e12,
                      "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_FLOPS, "traffic": traffic_for(ROOFLINE_KERNEL)},
+                     "frac": achieved / PEAK_BF16_FLOPS, "traffic": traffic_for(ROOFLINE_KERNEL),
+                     "onbox_peak": onbox["mfma_bf16_tflops"],
+                     "frac_onbox": achieved / 1e12 / onbox["mfma_bf16_tflops"]},
+        "onbox_peaks": onbox,
     }
     if not args.no_decode:
         ds = I.workload(args.decode_workload)
@@ -465,7 +507,9 @@ def main():
                          "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
                          "frac": attn_bw / PEAK_HBM_BYTES,
                          "traffic": traffic_for("attn_decode_split_kernel"),
-                         "us_per_launch": dc["attn_us"]},
+                         "us_per_launch": dc["attn_us"],
+                         "onbox_peak": onbox["hbm_read_gbs"],
+                         "frac_onbox": attn_bw / 1e9 / onbox["hbm_read_gbs"]},
         }
     if variants:
         line["variants"] = {

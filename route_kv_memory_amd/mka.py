@@ -25,11 +25,13 @@ __all__ = [
     "mka_fuse_kv_proj",
     "mka_attn_prefill", "mka_attn_decode", "mka_prefill", "mka_decode_step",
     "mka_workspace_bytes", "mka_status_string", "mka_last_error", "mka_version",
+    "mka_probe_mfma_bf16", "mka_probe_stream_read", "PROBE_STREAM_WORKGROUPS",
 ]
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmka.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "mka.h")
+HEADERS = [HEADER, os.path.join(os.path.dirname(PKG), "include", "mka_probe.h")]
 
 MKA_F32, MKA_BF16 = 0, 1
 MKA_ROUTE_SOFT, MKA_ROUTE_FIXED, MKA_ROUTE_TOP1, MKA_ROUTE_TOP2 = range(4)
@@ -100,6 +102,8 @@ _SIGS = {
     "mka_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mka_last_error": (ctypes.c_char_p, []),
     "mka_version": (ctypes.c_char_p, []),
+    "mka_probe_mfma_bf16": (ctypes.c_int, [_I32, _I32, _P, _P]),
+    "mka_probe_stream_read": (ctypes.c_int, [_P, _SZ, _P, _P]),
 }
 
 
@@ -120,8 +124,8 @@ def lib():
 
 
 def header_symbols() -> list[str]:
-    """Function names declared in include/mka.h."""
-    text = open(HEADER).read()
+    """Function names declared in include/*.h."""
+    text = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(mka_\w+)\(", text, re.M)))
 
 
@@ -252,3 +256,18 @@ def mka_last_error() -> str:
 
 def mka_version() -> str:
     return lib().mka_version().decode()
+
+
+# ------------------------------------------------------------ peak probes
+
+PROBE_STREAM_WORKGROUPS = 2048  # sink floats mka_probe_stream_read writes
+
+
+def mka_probe_mfma_bf16(workgroups, iters, sink, stream=None):
+    _check("mka_probe_mfma_bf16", lib().mka_probe_mfma_bf16(workgroups, iters, _ptr(sink),
+                                                            _stream(stream)))
+
+
+def mka_probe_stream_read(src, nbytes, sink, stream=None):
+    _check("mka_probe_stream_read", lib().mka_probe_stream_read(_ptr(src), nbytes, _ptr(sink),
+                                                                _stream(stream)))

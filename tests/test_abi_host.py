@@ -150,3 +150,13 @@ def test_routing_fields_follow_the_header():
         assert name in text
         key, val = name.split(" = ")
         assert getattr(mka, key) == int(val)
+
+
+def test_probe_arguments_rejected():
+    lib = mka.lib()
+    assert lib.mka_probe_mfma_bf16(0, 10, FAKE, None) == mka.MKA_ERR_INVALID
+    assert lib.mka_probe_mfma_bf16(4, 0, FAKE, None) == mka.MKA_ERR_INVALID
+    assert lib.mka_probe_mfma_bf16(4, 10, None, None) == mka.MKA_ERR_INVALID
+    assert lib.mka_probe_stream_read(FAKE + 8, 1024, FAKE, None) == mka.MKA_ERR_INVALID
+    assert lib.mka_probe_stream_read(FAKE, 1000, FAKE, None) == mka.MKA_ERR_INVALID
+    assert lib.mka_probe_stream_read(None, 1024, FAKE, None) == mka.MKA_ERR_INVALID

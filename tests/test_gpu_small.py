@@ -214,3 +214,15 @@ def test_decode_attention_matches_prefill_row():
                             L, o, ws, ws.numel())
         torch.cuda.synchronize()
         check_close(f"decode attn L={L}", to_np(o), ref, "bf16", max_abs=1e-2, mean_abs=1e-3)
+
+
+def test_peak_probes_run():
+    # The measurement probes complete and write their sinks (values carry no meaning).
+    sink = torch.full((mka.PROBE_STREAM_WORKGROUPS,), float("nan"), device="cuda")
+    mka.mka_probe_mfma_bf16(8, 16, sink)
+    torch.cuda.synchronize()
+    assert torch.isfinite(sink[:8]).all()
+    buf = torch.arange(1 << 20, dtype=torch.int32, device="cuda")
+    mka.mka_probe_stream_read(buf, buf.numel() * 4, sink)
+    torch.cuda.synchronize()
+    assert torch.isfinite(sink).all()
