@@ -32,7 +32,10 @@ those it is "parity unpinned".  The routing variants (``route_weights``) are
 pinned to scipy's softmax over the enabled tiers, a brute force over tier
 subsets, hand-made ties, torch's attention for L1 alone, and invariances
 (fixed routing ignores the router weights; without L3 the hash index does
-not matter).
+not matter).  Full MKA (``full_prefill``, ``full_decode_step``) is pinned
+path by path to torch's attention over each tier's keys and values, to
+FastMKA and plain GQA where the tiers coincide, and by decode continuing
+prefill.
 """
 
 from __future__ import annotations
@@ -48,6 +51,7 @@ __all__ = [
     "ema", "block_means", "simhash", "retrieve",
     "l3_mean", "fuse", "kv_proj", "attention", "attention_online", "prefill",
     "DecodeState", "decode_init", "decode_init_from_prefill", "decode_step",
+    "full_prefill", "FullDecodeState", "full_decode_init_from_prefill", "full_decode_step",
 ]
 
 _SQRT2 = math.sqrt(2.0)
@@ -524,3 +528,124 @@ def decode_step(st, x_t, w_q, w_k, w_v, w_r1, w_r2, proj, *, n_heads, n_kv_heads
     st.pos = t + 1
     return dict(q=q, lam=lam, l2=l2, key=key, key_abs=kabs, idx=idx[:, 0], l3=l3,
                 x_fused=xf, k_row=k_row[:, :, 0], v_row=v_row[:, :, 0], o=o)
+
+
+# --------------------------------------------------------------------------
+# Full MKA: three attention paths, mixed after attention.
+# MKA reading note, section 2 (O_h = sum_l lambda_l * a_l, a_l = softmax(q_h
+# k_l^T) v_l, the attention output of memory tier l); section 3 contrasts it
+# with FastMKA, which fuses the tiers before one attention; the abstract
+# page's Table 11 counts 3 attention paths and 9 launches for it.
+#
+# Reading: tier l's keys and values at position j are L_l[j] W_k and
+# L_l[j] W_v, with the same tiers L1 = x, L2 = EMA, L3 = mean of the
+# retrieved block means as in FastMKA and the same W_k, W_v; each path is one
+# causal attention over its own cache; lambda (per token and tier) is
+# broadcast over heads and head dimensions.  A disabled tier (``tiers``) has
+# lambda = 0 and its path is left out.
+# --------------------------------------------------------------------------
+
+def full_prefill(x, w_q, w_k, w_v, w_r1, w_r2, proj, *, n_heads, n_kv_heads, ema_decay,
+                 block, top_r, rows=None, route_mode="soft", tiers="l1l2l3", decide_q="f64"):
+    """Full MKA forward over a whole sequence.
+
+    Returns a dict with q, lam, l2, block_means, block_hash, block_abs, keys,
+    key_abs, idx, l3 (as ``prefill``), k3 and v3 (lists of the three tiers'
+    [B,G,N,dh] caches; None for a disabled tier), a3 (the three paths'
+    attention outputs at ``rows``, [B,n,H,dh]; None when disabled), rows and
+    o = sum_l lambda_l a_l [B,n,H,dh].
+    """
+    x = _f64(x)
+    B, N, D = x.shape
+    q = q_proj(x, w_q)
+    lam = router(q, w_r1, w_r2, route_mode, tiers, decide_q)
+    l2, _ = ema(x, ema_decay)
+    means = block_means(x, block)
+    bhash, babs = simhash(means, proj)
+    keys, kabs = simhash(l2, proj)
+    idx = retrieve(keys, bhash, np.arange(N), block, top_r)
+    l3 = l3_mean(means, idx)
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    dh = q.shape[-1] // n_heads
+    q_rows = q[:, rows].reshape(B, len(rows), n_heads, dh)
+    on = TIER_SETS[tiers]
+    k3, v3, a3 = [None] * 3, [None] * 3, [None] * 3
+    o = np.zeros((B, len(rows), n_heads, dh))
+    for ell, tier in enumerate((x, l2, l3)):
+        if not on[ell]:
+            continue
+        k3[ell], v3[ell] = kv_proj(tier, w_k, w_v, n_kv_heads)
+        a3[ell] = attention(q_rows, k3[ell], v3[ell], rows, n_kv_heads)
+        o = o + lam[:, rows, ell][:, :, None, None] * a3[ell]
+    return dict(q=q, lam=lam, l2=l2, block_means=means, block_hash=bhash, block_abs=babs,
+                keys=keys, key_abs=kabs, idx=idx, l3=l3, k3=k3, v3=v3, a3=a3, rows=rows, o=o)
+
+
+class FullDecodeState(DecodeState):
+    """Decode state of full MKA: the three tiers' caches (k3, v3: lists of
+    [B,G,t_cap,dh], None for a disabled tier) instead of the fused one."""
+
+    def __init__(self, k3, v3, ema_state, block_acc, means, pos):
+        super().__init__(np.zeros(1), np.zeros(1), ema_state, block_acc, means, pos)
+        self.k3 = [None if k is None else _f64(k).copy() for k in k3]
+        self.v3 = [None if v is None else _f64(v).copy() for v in v3]
+
+
+def full_decode_init_from_prefill(x, ref, proj, *, block, t_cap):
+    """Full-MKA decode state after ``full_prefill`` (``ref``) of x."""
+    x = _f64(x)
+    B, N, D = x.shape
+    nb = N // block
+
+    def grow(c):
+        if c is None:
+            return None
+        out = np.zeros(c.shape[:2] + (t_cap,) + c.shape[3:])
+        out[:, :, :N] = c
+        return out
+
+    st = FullDecodeState([grow(k) for k in ref["k3"]], [grow(v) for v in ref["v3"]],
+                         ref["l2"][:, -1], x[:, nb * block:].sum(axis=1), ref["block_means"], N)
+    st.hash, st.hash_abs = simhash(st.means, proj)
+    return st
+
+
+def full_decode_step(st, x_t, w_q, w_k, w_v, w_r1, w_r2, proj, *, n_heads, n_kv_heads,
+                     ema_decay, block, top_r, route_mode="soft", tiers="l1l2l3", decide_q="f64"):
+    """One full-MKA decode step at position t = st.pos: the tiers of the token,
+    one K/V row appended to each enabled tier's cache, the three attentions over
+    rows 0..t and their lambda-weighted sum.  Block finalisation as in
+    ``decode_step``.  Returns q, lam, l2, key, idx, a3 and o ([B, H, dh])."""
+    x_t = _f64(x_t)
+    B, D = x_t.shape
+    t = st.pos
+    q = q_proj(x_t, w_q)
+    lam = router(q, w_r1, w_r2, route_mode, tiers, decide_q)
+    l2_seq, st.ema_state = ema(x_t[:, None, :], ema_decay, st.ema_state)
+    l2 = l2_seq[:, 0]
+    st.block_acc = st.block_acc + x_t
+    key, kabs = simhash(l2, proj)
+    idx = retrieve(key[:, None], st.hash, np.array([t]), block, top_r)
+    l3 = l3_mean(st.means, idx)[:, 0]
+    dh = q.shape[-1] // n_heads
+    qh = q.reshape(B, 1, n_heads, dh)
+    on = TIER_SETS[tiers]
+    a3 = [None] * 3
+    o = np.zeros((B, n_heads, dh))
+    for ell, tier in enumerate((x_t, l2, l3)):
+        if not on[ell]:
+            continue
+        k_row, v_row = kv_proj(tier[:, None, :], w_k, w_v, n_kv_heads)
+        st.k3[ell][:, :, t] = k_row[:, :, 0]
+        st.v3[ell][:, :, t] = v_row[:, :, 0]
+        a3[ell] = attention(qh, st.k3[ell], st.v3[ell], np.array([t]), n_kv_heads)[:, 0]
+        o = o + lam[:, ell][:, None, None] * a3[ell]
+    if (t + 1) % block == 0:
+        m = st.block_acc / block
+        h, habs = simhash(m, proj)
+        st.means = np.concatenate([st.means, m[:, None]], axis=1)
+        st.hash = np.concatenate([st.hash, h[:, None]], axis=1)
+        st.hash_abs = np.concatenate([st.hash_abs, habs[:, None]], axis=1)
+        st.block_acc = np.zeros_like(st.block_acc)
+    st.pos = t + 1
+    return dict(q=q, lam=lam, l2=l2, key=key, key_abs=kabs, idx=idx[:, 0], l3=l3, a3=a3, o=o)

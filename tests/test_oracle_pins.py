@@ -594,3 +594,75 @@ def test_hard_routing_decision_precision():
     for mode in ("top1", "top2"):
         np.testing.assert_array_equal(O.router(q, w1, w2, mode, decide_q="bf16"),
                                       O.router(q, w1, w2, mode))
+
+
+# ----------------------------------------------------- full MKA (three paths)
+# Reading note, section 2: O_h = sum_l lambda_l a_l with a_l = softmax(q_h k_l^T) v_l.
+
+def _sdpa(q, k, v, n_heads, n_kv_heads, head_dim):
+    """torch's causal attention of q [B,N,H*dh] against head-major k, v [B,G,N,dh]."""
+    B, N = q.shape[:2]
+    tq = torch.from_numpy(q).view(B, N, n_heads, head_dim).transpose(1, 2)
+    rep = n_heads // n_kv_heads
+    tk = torch.from_numpy(k).repeat_interleave(rep, 1)
+    tv = torch.from_numpy(v).repeat_interleave(rep, 1)
+    return torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True) \
+        .transpose(1, 2).numpy()
+
+
+def test_full_mka_paths_are_torch_attention_over_each_tier():
+    s, d, args = _tiny()
+    w = [d[n] for n in ("w_q", "w_k", "w_v", "w_r1", "w_r2", "proj")]
+    ref = O.full_prefill(d["x"], *w, **args)
+    x = np.asarray(d["x"], np.float64)
+    o = np.zeros_like(ref["o"])
+    for ell, tier in enumerate((x, ref["l2"], ref["l3"])):
+        # the tier's keys and values by explicit head-major products
+        kk = (tier @ np.asarray(d["w_k"], np.float64).T).reshape(1, s.seq, s.n_kv_heads, s.head_dim)
+        vv = (tier @ np.asarray(d["w_v"], np.float64).T).reshape(1, s.seq, s.n_kv_heads, s.head_dim)
+        kk, vv = kk.transpose(0, 2, 1, 3), vv.transpose(0, 2, 1, 3)
+        np.testing.assert_allclose(ref["k3"][ell], kk, rtol=1e-12, atol=1e-13)
+        a = _sdpa(ref["q"], kk, vv, s.n_heads, s.n_kv_heads, s.head_dim)
+        np.testing.assert_allclose(ref["a3"][ell], a, rtol=1e-10, atol=1e-12)
+        o += ref["lam"][..., ell][..., None, None] * a
+    np.testing.assert_allclose(ref["o"], o, rtol=1e-10, atol=1e-12)
+    # three different paths: the mixture is not FastMKA's single attention
+    fast = O.prefill(d["x"], *w, **args)
+    assert np.abs(fast["o"] - ref["o"]).max() > 1e-4
+
+
+def test_full_mka_equals_fastmka_when_the_tiers_coincide():
+    # beta = 0 makes L2 = x; with L1 and L2 enabled both paths attend over the
+    # same K/V, so the mixture and FastMKA's fused attention are both GQA of x.
+    s, d, args = _tiny(ema_decay=0.0)
+    w = [d[n] for n in ("w_q", "w_k", "w_v", "w_r1", "w_r2", "proj")]
+    full = O.full_prefill(d["x"], *w, tiers="l1l2", **args)
+    fast = O.prefill(d["x"], *w, tiers="l1l2", **args)
+    l1 = O.prefill(d["x"], *w, tiers="l1", **args)
+    np.testing.assert_allclose(full["o"], fast["o"], rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(full["o"], l1["o"], rtol=1e-9, atol=1e-12)
+    # and with L1 alone every variant of both is plain GQA
+    full1 = O.full_prefill(d["x"], *w, tiers="l1", **args)
+    np.testing.assert_allclose(full1["o"], l1["o"], rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("mode,tiers", [("soft", "l1l2l3"), ("top1", "l1l3")])
+def test_full_mka_decode_continues_prefill(mode, tiers):
+    s, d, args = _tiny()
+    args = dict(args, route_mode=mode, tiers=tiers)
+    w = [d[k] for k in ("w_q", "w_k", "w_v", "w_r1", "w_r2", "proj")]
+    full = O.full_prefill(d["x"], *w, **args)
+    n1 = 180
+    part = O.full_prefill(d["x"][:, :n1], *w, **args)
+    st = O.full_decode_init_from_prefill(d["x"][:, :n1], part, d["proj"], block=s.block,
+                                         t_cap=s.seq)
+    for t in range(n1, s.seq):
+        r = O.full_decode_step(st, d["x"][:, t], *w, **args)
+        np.testing.assert_allclose(r["o"], full["o"][:, t], rtol=1e-10, atol=1e-13)
+        np.testing.assert_array_equal(r["idx"], full["idx"][:, t])
+    for ell in range(3):
+        if full["k3"][ell] is None:
+            assert st.k3[ell] is None
+        else:
+            np.testing.assert_allclose(st.k3[ell], full["k3"][ell], rtol=1e-10, atol=1e-13)
+            np.testing.assert_allclose(st.v3[ell], full["v3"][ell], rtol=1e-10, atol=1e-13)
