@@ -166,7 +166,7 @@ def settle(step_fn, ms):
     return n
 
 
-def bench_prefill(s, steps, warmup, variants=(), settle_ms=0.0):
+def bench_prefill(s, steps, warmup, variants=(), settle_ms=0.0, full=False):
     import torch
 
     from route_kv_memory_amd import mka
@@ -176,7 +176,7 @@ def bench_prefill(s, steps, warmup, variants=(), settle_ms=0.0):
     log(f"prefill: generating {s.name} inputs")
     inp = prefill_inputs(s)
     N = s.seq
-    layer = Layer(s, inp, t_cap=N, nb_cap=N // s.block)
+    layer = Layer(s, inp, t_cap=N, nb_cap=N // s.block, full=full)
     x = to_device(inp["x"], s.dtype)
     del inp
     out = layer.outputs(N)
@@ -217,15 +217,15 @@ def bench_prefill(s, steps, warmup, variants=(), settle_ms=0.0):
     # empty prefix (pos0 = 0), for which the state buffers are not read.
     settled = settle(lambda: layer.prefill(x, 0, out=out, stream=stream), settle_ms)
 
-    def composite():
+    def composite(fn=layer.prefill):
         ev_step = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
         for _ in range(warmup):
-            layer.prefill(x, 0, out=out, stream=stream)
+            fn(x, 0, out=out, stream=stream)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for k in range(steps):
             ev_step[k][0].record(stream)
-            layer.prefill(x, 0, out=out, stream=stream)
+            fn(x, 0, out=out, stream=stream)
             ev_step[k][1].record(stream)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / steps
@@ -239,6 +239,10 @@ def bench_prefill(s, steps, warmup, variants=(), settle_ms=0.0):
         var_ms[f"{mode}/{tiers}"] = composite()[0]
         log(f"prefill variant {mode}/{tiers}: {var_ms[f'{mode}/{tiers}']:.4f} ms")
     layer.shape = s
+    # Full MKA (three attention paths) on the same inputs.
+    full_ms = composite(layer.full_prefill)[0] if full else None
+    if full:
+        log(f"prefill full MKA: {full_ms:.4f} ms")
 
     # Breakdown: the same calls one by one on one stream, HIP events between
     # them (the attention stage is exactly one kernel launch).
@@ -252,10 +256,10 @@ def bench_prefill(s, steps, warmup, variants=(), settle_ms=0.0):
                 for i, n in enumerate(names)}
     seq_ms = float(np.mean([e[0].elapsed_time(e[6]) for e in evs]))
     return dict(wall_ms=wall_ms, gpu_ms=gpu_ms, stage_ms=stage_ms, sequential_ms=seq_ms,
-                variants_ms=var_ms, settle_steps=settled)
+                variants_ms=var_ms, settle_steps=settled, full_ms=full_ms)
 
 
-def bench_decode(s, steps, warmup, variants=()):
+def bench_decode(s, steps, warmup, variants=(), full=False):
     import torch
 
     from route_kv_memory_amd import mka
@@ -267,10 +271,14 @@ def bench_decode(s, steps, warmup, variants=()):
     T0, n = s.decode_cached, s.decode_steps
     t_cap = T0 + n
     nb0 = T0 // s.block
-    layer = Layer(s, dec, t_cap=t_cap, nb_cap=t_cap // s.block + 1)
+    layer = Layer(s, dec, t_cap=t_cap, nb_cap=t_cap // s.block + 1, full=full)
     st = layer.st
     st["k_cache"][:, :, :T0] = to_device(dec["k_cache"], s.dtype)
     st["v_cache"][:, :, :T0] = to_device(dec["v_cache"], s.dtype)
+    if full:  # the three tiers' caches hold the same synthetic rows (timing only)
+        for c in ("k", "v"):
+            for t in layer.kv3[c]:
+                t[:, :, :T0].copy_(st[f"{c}_cache"][:, :, :T0])
     init = {k: to_device(dec[k]) for k in ("ema_state", "block_acc")}
     means0 = to_device(dec["block_means"])
     tokens = to_device(dec["tokens"], s.dtype)
@@ -288,17 +296,17 @@ def bench_decode(s, steps, warmup, variants=()):
     out = layer.outputs(1)
     stream = torch.cuda.current_stream()
 
-    def run():
+    def run(fn=layer.decode_step):
         reset()
         for k in range(warmup):
-            layer.decode_step(tokens[k], T0 + k, out=out)
+            fn(tokens[k], T0 + k, out=out)
         reset()
         torch.cuda.synchronize()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         t0 = time.perf_counter()
         ev[0].record(stream)
         for k in range(steps):
-            layer.decode_step(tokens[k], T0 + k, out=out)
+            fn(tokens[k], T0 + k, out=out)
             ev[k + 1].record(stream)
         host_us = (time.perf_counter() - t0) / steps * 1e6  # enqueue cost per step
         torch.cuda.synchronize()
@@ -313,6 +321,11 @@ def bench_decode(s, steps, warmup, variants=()):
         var_us[f"{mode}/{tiers}"] = float(np.median(run()[0]))
         log(f"decode variant {mode}/{tiers}: {var_us[f'{mode}/{tiers}']:.1f} us/token")
     layer.shape = s
+    full_us = None
+    if full:
+        f_us, f_host, _ = run(layer.full_decode_step)
+        full_us = {"median_us": float(np.median(f_us)), "host_us": f_host}
+        log(f"decode full MKA: {full_us['median_us']:.1f} us/token")
     step_us, host_us, wall_us = run()
 
     # Decode attention alone at the first step's length, for its roofline.
@@ -339,7 +352,7 @@ def bench_decode(s, steps, warmup, variants=()):
                   + s.hash_bits * s.d_model * 4 + s.top_r * s.d_model * 4 + nb0 * 8)
     return dict(median_us=float(np.median(step_us)), mean_us=float(step_us.mean()),
                 wall_us=wall_us, host_us=host_us, attn_us=attn_us, kv_bytes=kv_bytes, step_bytes=step_bytes,
-                cached=T0, steps=steps, variants_us=var_us)
+                cached=T0, steps=steps, variants_us=var_us, full=full_us)
 
 
 def onbox_peaks():
@@ -421,6 +434,9 @@ def main():
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed back-to-back prefill steps for this long before the warmup "
                          "(GPU clocks ramp up under load)")
+    ap.add_argument("--full-mka", action="store_true",
+                    help="also time full MKA (three attention paths mixed by lambda) on the same "
+                         "workloads")
     ap.add_argument("--variants", action="store_true",
                     help="also time the routing and tier variants (fixed, hard top-1/top-2; "
                          "L1+L2, L1+L3, L1 alone) on the same workloads")
@@ -449,7 +465,7 @@ def main():
         copy_calibration(args.copy_calibration)
     s = I.workload(args.workload)
     variants = VARIANTS if args.variants else ()
-    pf = bench_prefill(s, args.steps, args.warmup, variants, args.settle_ms)
+    pf = bench_prefill(s, args.steps, args.warmup, variants, args.settle_ms, args.full_mka)
     flops = prefill_flops(s)
     onbox = onbox_peaks()
     log(f"on-box peaks: {onbox['mfma_bf16_tflops']:.0f} TFLOP/s bf16 MFMA, "
@@ -495,7 +511,7 @@ def main():
     }
     if not args.no_decode:
         ds = I.workload(args.decode_workload)
-        dc = bench_decode(ds, ds.decode_steps, 8, variants)
+        dc = bench_decode(ds, ds.decode_steps, 8, variants, args.full_mka)
         attn_bw = dc["kv_bytes"] / (dc["attn_us"] * 1e-6)
         step_bw = dc["step_bytes"] / (dc["median_us"] * 1e-6)
         line["decode"] = {
@@ -516,6 +532,13 @@ def main():
             k: {"prefill_tokens_per_s": tokens / (v * 1e-3), "prefill_ms": v,
                 "decode_us_per_token": dc["variants_us"].get(k) if not args.no_decode else None}
             for k, v in pf["variants_ms"].items()}
+    if args.full_mka:
+        line["full_mka"] = {
+            "prefill_ms": pf["full_ms"], "prefill_tokens_per_s": tokens / (pf["full_ms"] * 1e-3),
+            "decode_us_per_token": dc["full"]["median_us"] if not args.no_decode else None,
+            "decode_host_us_per_token": dc["full"]["host_us"] if not args.no_decode else None,
+            "note": "three attention paths (one K/V cache per tier) mixed by lambda; same "
+                    "inputs as the FastMKA figures of this line"}
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a bounded sample")
         line["cpu_baseline"] = cpu_baseline(s, args.cpu_tokens or s.seq, args.cpu_batch or s.batch)

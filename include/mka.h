@@ -57,7 +57,8 @@ enum {
 
 /* Workspace-using operations, for mka_workspace_bytes(). */
 enum { MKA_OP_EMA_SCAN = 0, MKA_OP_FUSE_KV = 1, MKA_OP_ATTN_DECODE = 2, MKA_OP_PREFILL = 3,
-       MKA_OP_DECODE_STEP = 4, MKA_OP_RETRIEVE = 5, MKA_OP_INDEX = 6, MKA_OP_ROUTE = 7 };
+       MKA_OP_DECODE_STEP = 4, MKA_OP_RETRIEVE = 5, MKA_OP_INDEX = 6, MKA_OP_ROUTE = 7,
+       MKA_OP_FULL_PREFILL = 8, MKA_OP_FULL_DECODE_STEP = 9 };
 
 /* Routing variant (mka_dims.route_mode) and enabled tiers (mka_dims.tiers):
  * the ablations of the abstract page, Table 10 (fixed lambda = 1/3, hard
@@ -285,6 +286,41 @@ int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weight
 int mka_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_weights* w,
                     const mka_state* st, const mka_outputs* out, void* ws, size_t ws_bytes,
                     void* stream);
+
+/* Full MKA, the three-path form that FastMKA replaces: each memory tier is
+ * attended separately and the outputs are mixed, O_h = sum_l lambda_l a_l with
+ * a_l = softmax(q_h k_l^T / sqrt(dh)) v_l (reading note, method section 2; the
+ * abstract page's Table 11 counts 3 attention paths and 9 launches for it).
+ * Reading: tier l's keys and values at position j are L_l[j] W_k and
+ * L_l[j] W_v -- the tiers of FastMKA (L1 = x, L2 = EMA, L3 = mean of the
+ * retrieved block means), each rounded once to dtype, the same W_k and W_v --
+ * and each path is one causal attention over its own cache.  Provided as the
+ * comparison workload of the three-path design.
+ *
+ * mka_full_prefill: the layer over positions pos0 .. pos0+seq-1 -- route,
+ * ema_scan and l3_index on the auxiliary stream (as mka_prefill), retrieval,
+ * then per enabled tier: its rows, the K/V product into that tier's cache,
+ * causal attention; finally the lambda mix into out->o.  State and outputs as
+ * mka_prefill, except: the fused cache st->k_cache / v_cache and st->block_kv
+ * are not used (may be NULL); the three tiers' caches are ``kv`` (entries of
+ * disabled tiers may be NULL).  Routing variants apply as in mka_prefill.
+ *   ws >= mka_workspace_bytes(d, MKA_OP_FULL_PREFILL, 0) bytes
+ * mka_full_decode_step: one token at position ``pos`` (d->seq == 1), the same
+ * steps in order on ``stream`` (no auxiliary stream), each tier's K/V row
+ * appended at row pos and decode attention over rows 0..pos of each cache;
+ * when pos closes a block its mean and code join the bank.
+ *   ws >= mka_workspace_bytes(d, MKA_OP_FULL_DECODE_STEP, pos + 1) bytes */
+typedef struct mka_tier_cache {
+  void* k_cache[3]; /* tier l (0 = L1, 1 = L2, 2 = L3): [B, G, t_cap, dh] dtype */
+  void* v_cache[3];
+} mka_tier_cache;
+
+int mka_full_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weights* w,
+                     const mka_state* st, const mka_tier_cache* kv, const mka_outputs* out,
+                     void* ws, size_t ws_bytes, void* stream);
+int mka_full_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_weights* w,
+                         const mka_state* st, const mka_tier_cache* kv, const mka_outputs* out,
+                         void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace in bytes that ``op`` needs for the shape ``d``.  ``cache_len`` is the
  * cache length for MKA_OP_ATTN_DECODE / MKA_OP_DECODE_STEP and the number of

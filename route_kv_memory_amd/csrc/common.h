@@ -177,6 +177,11 @@ __device__ __forceinline__ int xcd_contiguous(int bid, int n) {
 constexpr int kRouteSoft = 0, kRouteFixed = 1, kRouteTop1 = 2, kRouteTop2 = 3;
 constexpr int kTiersAll = 0, kTiersL1L2 = 1, kTiersL1L3 = 2, kTiersL1 = 3;
 
+// A constant lambda vector passed by value.
+struct Lam3 {
+  float v[3] = {0.f, 0.f, 0.f};
+};
+
 struct Routing {
   int mode = kRouteSoft;
   int tiers = kTiersAll;

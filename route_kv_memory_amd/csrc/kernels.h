@@ -67,6 +67,17 @@ template <typename T>
 hipError_t fuse_mix(const T* x, const float* l2, const float* means, int nb_cap,
                     const int32_t* idx, const float* lam, int B, int seq, int D, int R,
                     Routing rt, T* xf, hipStream_t s);
+// One tier's rows alone, rounded once to the storage type: tier 1 = L2, tier 2 =
+// L3 (mean of the retrieved block means).  Full MKA projects each tier apart.
+template <typename T>
+hipError_t tier_rows(const T* x, const float* l2, const float* means, int nb_cap,
+                     const int32_t* idx, int tier, int B, int seq, int D, int R, T* out,
+                     hipStream_t s);
+// Full MKA: o[m, :] = sum_l lam[m, l] a_l[m, :] over M rows of HD values; null
+// paths are skipped.  HD % 4 == 0.
+template <typename T>
+hipError_t mix_paths(const T* a0, const T* a1, const T* a2, const float* lam, int64_t M, int HD,
+                     T* o, hipStream_t s);
 
 // block_kv[b, blk, :] = m_blk [W_k; W_v]^T (float32) for blocks first .. first+n_blocks-1.
 template <typename T>

@@ -241,45 +241,91 @@ int do_retrieve(const mka_dims* d, const float* l2, const float* proj, const uin
   return MKA_OK;
 }
 
+int do_kv_proj(const mka_dims* d, const void* src, const void* w_k, const void* w_v, void* kc,
+               void* vc, int64_t pos0, int64_t t_cap, hipStream_t s);
+
 int do_fuse_kv(const mka_dims* d, const void* x, const float* l2, const float* means, int nb_cap,
                const int32_t* idx, const float* lam, const void* w_k, const void* w_v, void* kc,
                void* vc, int64_t pos0, int64_t t_cap, void* ws, hipStream_t s) {
-  const int M = rows_of(d), D = d->d_model, kvw = d->n_kv_heads * d->head_dim;
   const Routing rt = routing_of(d);
   // L1 alone: X_fused = x (lambda = (1, 0, 0)), projected without a fusion pass
-  if (d->dtype == MKA_BF16) {
-    const bf16_t* xf = static_cast<const bf16_t*>(x);
-    if (rt.ema()) {
-      bf16_t* mix = static_cast<bf16_t*>(ws);
+  const void* src = x;
+  if (rt.ema()) {
+    if (d->dtype == MKA_BF16)
       MKA_LAUNCH("fuse", fuse_mix<bf16_t>(static_cast<const bf16_t*>(x), l2, means, nb_cap, idx,
-                                          lam, d->batch, d->seq, D, d->top_r, rt, mix, s));
-      xf = mix;
-    }
-    const EpiKV<bf16_t> epi{static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), d->seq,
-                            d->n_kv_heads, d->head_dim, t_cap, pos0};
+                                          lam, d->batch, d->seq, d->d_model, d->top_r, rt,
+                                          static_cast<bf16_t*>(ws), s));
+    else
+      MKA_LAUNCH("fuse", fuse_mix<float>(static_cast<const float*>(x), l2, means, nb_cap, idx,
+                                         lam, d->batch, d->seq, d->d_model, d->top_r, rt,
+                                         static_cast<float*>(ws), s));
+    src = ws;
+  }
+  return do_kv_proj(d, src, w_k, w_v, kc, vc, pos0, t_cap, s);
+}
+
+// [K|V] rows pos0 .. pos0+seq-1 of one cache from the rows ``src`` [B, seq, D].
+int do_kv_proj(const mka_dims* d, const void* src, const void* w_k, const void* w_v, void* kc,
+               void* vc, int64_t pos0, int64_t t_cap, hipStream_t s) {
+  const int M = rows_of(d), D = d->d_model, kvw = d->n_kv_heads * d->head_dim;
+  if (d->dtype == MKA_BF16) {
+    const bf16_t* xs = static_cast<const bf16_t*>(src);
     const bf16_t* wk = static_cast<const bf16_t*>(w_k);
     const bf16_t* wv = static_cast<const bf16_t*>(w_v);
+    const EpiKV<bf16_t> epi{static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), d->seq,
+                            d->n_kv_heads, d->head_dim, t_cap, pos0};
     if (M <= kFewRows)
-      MKA_LAUNCH("kv_gemv", gemv<bf16_t>(xf, D, M, wk, wv, kvw, 2 * kvw, D, epi, s));
+      MKA_LAUNCH("kv_gemv", gemv<bf16_t>(xs, D, M, wk, wv, kvw, 2 * kvw, D, epi, s));
     else
-      MKA_LAUNCH("kv_gemm", gemm_bf16(xf, D, wk, wv, kvw, M, 2 * kvw, D, epi, s));
+      MKA_LAUNCH("kv_gemm", gemm_bf16(xs, D, wk, wv, kvw, M, 2 * kvw, D, epi, s));
   } else {
-    const float* xf = static_cast<const float*>(x);
-    if (rt.ema()) {
-      float* mix = static_cast<float*>(ws);
-      MKA_LAUNCH("fuse", fuse_mix<float>(static_cast<const float*>(x), l2, means, nb_cap, idx,
-                                         lam, d->batch, d->seq, D, d->top_r, rt, mix, s));
-      xf = mix;
-    }
-    const EpiKV<float> epi{static_cast<float*>(kc), static_cast<float*>(vc), d->seq, d->n_kv_heads,
-                           d->head_dim, t_cap, pos0};
+    const float* xs = static_cast<const float*>(src);
     const float* wk = static_cast<const float*>(w_k);
     const float* wv = static_cast<const float*>(w_v);
+    const EpiKV<float> epi{static_cast<float*>(kc), static_cast<float*>(vc), d->seq, d->n_kv_heads,
+                           d->head_dim, t_cap, pos0};
     if (M <= kFewRows)
-      MKA_LAUNCH("kv_gemv", gemv<float>(xf, D, M, wk, wv, kvw, 2 * kvw, D, epi, s));
+      MKA_LAUNCH("kv_gemv", gemv<float>(xs, D, M, wk, wv, kvw, 2 * kvw, D, epi, s));
     else
-      MKA_LAUNCH("kv_gemm", gemm_f32(xf, D, wk, wv, kvw, M, 2 * kvw, D, epi, s));
+      MKA_LAUNCH("kv_gemm", gemm_f32(xs, D, wk, wv, kvw, M, 2 * kvw, D, epi, s));
   }
+  return MKA_OK;
+}
+
+// One tier's rows (tier 0 = x itself; 1 = L2; 2 = L3) into ``rows`` when they
+// need forming; returns the rows to project.
+const void* tier_source(const mka_dims* d, int tier, const void* x, const float* l2,
+                        const float* means, int nb_cap, const int32_t* idx, void* rows,
+                        hipStream_t s, int* rc) {
+  *rc = MKA_OK;
+  if (tier == 0) return x;
+  hipError_t e;
+  if (d->dtype == MKA_BF16)
+    e = tier_rows<bf16_t>(static_cast<const bf16_t*>(x), l2, means, nb_cap, idx, tier, d->batch,
+                          d->seq, d->d_model, d->top_r, static_cast<bf16_t*>(rows), s);
+  else
+    e = tier_rows<float>(static_cast<const float*>(x), l2, means, nb_cap, idx, tier, d->batch,
+                         d->seq, d->d_model, d->top_r, static_cast<float*>(rows), s);
+  if (e != hipSuccess) {
+    *rc = hip_fail("full/tier_rows", e);
+    return nullptr;
+  }
+  return rows;
+}
+
+int do_mix(const mka_dims* d, void* const a[3], const float* lam, void* o, hipStream_t s) {
+  const int64_t M = rows_of(d);
+  const int HD = d->n_heads * d->head_dim;
+  if (d->dtype == MKA_BF16)
+    MKA_LAUNCH("full/mix", mix_paths<bf16_t>(static_cast<const bf16_t*>(a[0]),
+                                             static_cast<const bf16_t*>(a[1]),
+                                             static_cast<const bf16_t*>(a[2]), lam, M, HD,
+                                             static_cast<bf16_t*>(o), s));
+  else
+    MKA_LAUNCH("full/mix", mix_paths<float>(static_cast<const float*>(a[0]),
+                                            static_cast<const float*>(a[1]),
+                                            static_cast<const float*>(a[2]), lam, M, HD,
+                                            static_cast<float*>(o), s));
   return MKA_OK;
 }
 
@@ -403,6 +449,47 @@ DecodeWs decode_layout(const mka_dims* d, int64_t cache_len) {
   return w;
 }
 
+// Workspace of full MKA.  Prefill: [EMA scan, index | route, retrieval | tier
+// rows | a_1 | a_2 | a_3]; decode: [the sequential steps' shared region | tier
+// rows | a_1 | a_2 | a_3] (the steps run in order on one stream).
+struct FullWs {
+  size_t chain, main, rows, path, total;
+};
+FullWs full_layout(const mka_dims* d, bool decode, int64_t cache_len) {
+  FullWs w{};
+  if (decode) {
+    size_t m = route_ws(d);
+    for (size_t v : {ema_ws(d), retrieve_ws(d), decode_ws(d, cache_len), index_ws(d, 1)})
+      if (v > m) m = v;
+    w.main = m;
+  } else {
+    w.chain = prefill_chain_ws(d);
+    w.main = route_ws(d) > retrieve_ws(d) ? route_ws(d) : retrieve_ws(d);
+  }
+  w.rows = fuse_ws(d);
+  w.path = round256(static_cast<size_t>(rows_of(d)) * d->n_heads * d->head_dim * el_size(d));
+  w.total = w.chain + w.main + w.rows + 3 * w.path;
+  return w;
+}
+
+int check_full_args(const mka_dims* d, const void* x, int64_t pos0, const mka_weights* w,
+                    const mka_state* st, const mka_tier_cache* kv, const mka_outputs* out) {
+  MKA_CHECK(w != nullptr && st != nullptr && kv != nullptr && out != nullptr, MKA_ERR_INVALID);
+  MKA_CHECK(ptrs_ok({x, w->w_q, w->w_k, w->w_v, w->w_r1, w->w_r2, w->proj}), MKA_ERR_INVALID);
+  MKA_CHECK(ptrs_ok({st->ema_state, st->block_acc, st->block_means}), MKA_ERR_INVALID);
+  MKA_CHECK(st->block_hash != nullptr && (reinterpret_cast<uintptr_t>(st->block_hash) & 7u) == 0,
+            MKA_ERR_INVALID);
+  MKA_CHECK(ptrs_ok({out->q, out->lambda, out->l2, out->key, out->idx, out->o}), MKA_ERR_INVALID);
+  const Routing rt = routing_of(d);
+  const bool on[3] = {true, rt.l2(), rt.l3()};
+  for (int l = 0; l < 3; ++l)
+    if (on[l]) MKA_CHECK(ptrs_ok({kv->k_cache[l], kv->v_cache[l]}), MKA_ERR_INVALID);
+  MKA_CHECK(pos0 >= 0 && st->nb_cap >= 1 && st->nb_cap < 0xFFFFFF, MKA_ERR_INVALID);
+  MKA_CHECK(pos0 + d->seq <= st->t_cap, MKA_ERR_INVALID);
+  MKA_CHECK((pos0 + d->seq) / d->block <= st->nb_cap, MKA_ERR_INVALID);
+  return MKA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -435,6 +522,9 @@ size_t mka_workspace_bytes(const mka_dims* d, int op, int64_t cache_len) {
       return prefill_chain_ws(d) + prefill_main_ws(d);
     case MKA_OP_DECODE_STEP:
       return d->seq == 1 && cache_len > 0 ? decode_layout(d, cache_len).total : 0;
+    case MKA_OP_FULL_PREFILL: return full_layout(d, false, 0).total;
+    case MKA_OP_FULL_DECODE_STEP:
+      return d->seq == 1 && cache_len > 0 ? full_layout(d, true, cache_len).total : 0;
     default: return 0;
   }
 }
@@ -757,6 +847,109 @@ int mka_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_wei
     return do_block_kv(d, st->block_means, st->nb_cap, closed_block, 1, w->w_k, w->w_v,
                        st->block_kv, s);
   }
+  return MKA_OK;
+}
+
+int mka_full_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weights* w,
+                     const mka_state* st, const mka_tier_cache* kv, const mka_outputs* out,
+                     void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  rc = check_full_args(d, x, pos0, w, st, kv, out);
+  if (rc) return rc;
+  const FullWs L = full_layout(d, false, 0);
+  MKA_CHECK(ws_bytes >= L.total && ptrs_ok({ws}), MKA_ERR_WORKSPACE);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Routing rt = routing_of(d);
+  int64_t first, n;
+  completed_blocks(d, pos0, &first, &n);
+  if (!rt.l3()) n = 0;
+  char* base = static_cast<char*>(ws);
+  char* ws_chain = base;
+  char* ws_main = base + L.chain;
+  void* rows = base + L.chain + L.main;
+  char* paths = base + L.chain + L.main + L.rows;
+  // The scan and block codes run beside the query product, as in mka_prefill.
+  Aux* aux = aux_for_current_device(&rc);
+  if (aux == nullptr) return rc;
+  std::lock_guard<std::mutex> guard(aux->lock);
+  hipStream_t s2 = aux->stream;
+  MKA_LAUNCH("full/fork", hipEventRecord(aux->fork, s));
+  MKA_LAUNCH("full/fork", hipStreamWaitEvent(s2, aux->fork, 0));
+  if (rt.ema() && (rc = do_ema(d, x, pos0, st->ema_state, st->block_acc, out->l2,
+                               st->block_means, st->nb_cap, ws_chain, s2)))
+    return rc;
+  if ((rc = do_index(d, st->block_means, st->nb_cap, static_cast<int>(first), static_cast<int>(n),
+                     w->proj, st->block_hash, ws_chain, s2)))
+    return rc;
+  MKA_LAUNCH("full/join", hipEventRecord(aux->join, s2));
+  if ((rc = do_route(d, x, w->w_q, w->w_r1, w->w_r2, out->q, out->lambda, ws_main, s))) return rc;
+  MKA_LAUNCH("full/join", hipStreamWaitEvent(s, aux->join, 0));
+  if (rt.l3() && (rc = do_retrieve(d, out->l2, w->proj, st->block_hash, st->nb_cap, pos0,
+                                   out->key, out->idx, ws_main, s)))
+    return rc;
+  const bool on[3] = {true, rt.l2(), rt.l3()};
+  void* a[3] = {nullptr, nullptr, nullptr};
+  for (int l = 0; l < 3; ++l) {
+    if (!on[l]) continue;
+    const void* src = tier_source(d, l, x, out->l2, st->block_means, st->nb_cap, out->idx, rows,
+                                  s, &rc);
+    if (rc) return rc;
+    if ((rc = do_kv_proj(d, src, w->w_k, w->w_v, kv->k_cache[l], kv->v_cache[l], pos0, st->t_cap,
+                         s)))
+      return rc;
+    a[l] = paths + l * L.path;
+    if ((rc = do_attn_prefill(d, out->q, kv->k_cache[l], kv->v_cache[l], st->t_cap, pos0, a[l],
+                              s)))
+      return rc;
+  }
+  return do_mix(d, a, out->lambda, out->o, s);
+}
+
+int mka_full_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_weights* w,
+                         const mka_state* st, const mka_tier_cache* kv, const mka_outputs* out,
+                         void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  MKA_CHECK(d->seq == 1, MKA_ERR_INVALID);
+  rc = check_full_args(d, x, pos, w, st, kv, out);
+  if (rc) return rc;
+  MKA_CHECK(pos + 1 <= kMaxDecodeCache && decode_chunk_fits(d, pos), MKA_ERR_UNSUPPORTED);
+  MKA_CHECK(rows_of(d) <= kFewRows, MKA_ERR_UNSUPPORTED);
+  const FullWs L = full_layout(d, true, pos + 1);
+  MKA_CHECK(ws_bytes >= L.total && ptrs_ok({ws}), MKA_ERR_WORKSPACE);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Routing rt = routing_of(d);
+  char* base = static_cast<char*>(ws);
+  void* shared = base;
+  void* rows = base + L.main;
+  char* paths = base + L.main + L.rows;
+  if ((rc = do_route(d, x, w->w_q, w->w_r1, w->w_r2, out->q, out->lambda, shared, s))) return rc;
+  if (rt.ema() && (rc = do_ema(d, x, pos, st->ema_state, st->block_acc, out->l2, st->block_means,
+                               st->nb_cap, shared, s)))
+    return rc;
+  if (rt.l3() && (rc = do_retrieve(d, out->l2, w->proj, st->block_hash, st->nb_cap, pos,
+                                   out->key, out->idx, shared, s)))
+    return rc;
+  const bool on[3] = {true, rt.l2(), rt.l3()};
+  void* a[3] = {nullptr, nullptr, nullptr};
+  for (int l = 0; l < 3; ++l) {
+    if (!on[l]) continue;
+    const void* src = tier_source(d, l, x, out->l2, st->block_means, st->nb_cap, out->idx, rows,
+                                  s, &rc);
+    if (rc) return rc;
+    if ((rc = do_kv_proj(d, src, w->w_k, w->w_v, kv->k_cache[l], kv->v_cache[l], pos, st->t_cap,
+                         s)))
+      return rc;
+    a[l] = paths + l * L.path;
+    if ((rc = do_attn_decode(d, out->q, kv->k_cache[l], kv->v_cache[l], st->t_cap, pos + 1, a[l],
+                             shared, s)))
+      return rc;
+  }
+  if ((rc = do_mix(d, a, out->lambda, out->o, s))) return rc;
+  if (rt.l3() && (pos + 1) % d->block == 0)  // the closed block joins the bank
+    return do_index(d, st->block_means, st->nb_cap, static_cast<int>((pos + 1) / d->block - 1), 1,
+                    w->proj, st->block_hash, shared, s);
   return MKA_OK;
 }
 

@@ -27,7 +27,7 @@ def to_device(a: np.ndarray, dtype: str | None = None, device="cuda") -> torch.T
 
 class Layer:
     def __init__(self, shape, weights: dict, *, t_cap: int, nb_cap: int, batch: int | None = None,
-                 device="cuda"):
+                 device="cuda", full: bool = False):
         self.shape = shape
         self.batch = shape.batch if batch is None else batch
         self.device = device
@@ -51,6 +51,16 @@ class Layer:
         self.state = mka.State(nb_cap=self.nb_cap, t_cap=self.t_cap,
                                **{k: v.data_ptr() for k, v in self.st.items()})
         self._ws = None
+        # full MKA: one K/V cache per memory tier (tier 0 = L1, 1 = L2, 2 = L3)
+        self.kv3 = None
+        if full:
+            self.kv3 = {c: [torch.zeros(B, G, self.t_cap, dh, dtype=self.tdtype, **z)
+                            for _ in range(3)] for c in ("k", "v")}
+            tc = mka.TierCache()
+            for i in range(3):
+                tc.k_cache[i] = self.kv3["k"][i].data_ptr()
+                tc.v_cache[i] = self.kv3["v"][i].data_ptr()
+            self.tier_cache = tc
 
     def index_blocks(self, first: int, n: int, stream=None) -> None:
         """Codes and projections of block means first .. first+n-1 (already in
@@ -105,4 +115,24 @@ class Layer:
         ws = self.workspace(need)
         mka.mka_decode_step(d, x_t, pos, self.weights, self.state, self._out_struct(out), ws,
                             ws.numel(), stream)
+        return out
+
+    def full_prefill(self, x: torch.Tensor, pos0: int = 0, out: dict | None = None,
+                     stream=None) -> dict:
+        """Full MKA (three attention paths) over x; the layer needs ``full=True``."""
+        seq = x.shape[1]
+        d = self.dims(seq)
+        out = self.outputs(seq) if out is None else out
+        ws = self.workspace(mka.mka_workspace_bytes(d, mka.MKA_OP_FULL_PREFILL))
+        mka.mka_full_prefill(d, x, pos0, self.weights, self.state, self.tier_cache,
+                             self._out_struct(out), ws, ws.numel(), stream)
+        return out
+
+    def full_decode_step(self, x_t: torch.Tensor, pos: int, out: dict | None = None,
+                         stream=None) -> dict:
+        d = self.dims(1)
+        out = self.outputs(1) if out is None else out
+        ws = self.workspace(mka.mka_workspace_bytes(d, mka.MKA_OP_FULL_DECODE_STEP, pos + 1))
+        mka.mka_full_decode_step(d, x_t, pos, self.weights, self.state, self.tier_cache,
+                                 self._out_struct(out), ws, ws.numel(), stream)
         return out

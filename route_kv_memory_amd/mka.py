@@ -23,7 +23,8 @@ __all__ = [
     "MKA_OP_PREFILL", "MKA_OP_DECODE_STEP", "MKA_OP_RETRIEVE", "MKA_OP_INDEX", "MKA_OP_ROUTE",
     "mka_route", "mka_ema_scan", "mka_l3_index", "mka_l3_block_kv", "mka_l3_retrieve",
     "mka_fuse_kv_proj",
-    "mka_attn_prefill", "mka_attn_decode", "mka_prefill", "mka_decode_step",
+    "mka_attn_prefill", "mka_attn_decode", "mka_prefill", "mka_decode_step", "TierCache",
+    "mka_full_prefill", "mka_full_decode_step", "MKA_OP_FULL_PREFILL", "MKA_OP_FULL_DECODE_STEP",
     "mka_workspace_bytes", "mka_status_string", "mka_last_error", "mka_version",
     "mka_probe_mfma_bf16", "mka_probe_stream_read", "PROBE_STREAM_WORKGROUPS",
 ]
@@ -42,7 +43,7 @@ TIER_SETS = {"l1l2l3": MKA_TIERS_ALL, "l1l2": MKA_TIERS_L1_L2, "l1l3": MKA_TIERS
              "l1": MKA_TIERS_L1}
 MKA_OK, MKA_ERR_INVALID, MKA_ERR_UNSUPPORTED, MKA_ERR_WORKSPACE, MKA_ERR_HIP = 0, -1, -2, -3, -4
 (MKA_OP_EMA_SCAN, MKA_OP_FUSE_KV, MKA_OP_ATTN_DECODE, MKA_OP_PREFILL, MKA_OP_DECODE_STEP,
- MKA_OP_RETRIEVE, MKA_OP_INDEX, MKA_OP_ROUTE) = range(8)
+ MKA_OP_RETRIEVE, MKA_OP_INDEX, MKA_OP_ROUTE, MKA_OP_FULL_PREFILL, MKA_OP_FULL_DECODE_STEP) = range(10)
 
 
 class MkaError(RuntimeError):
@@ -75,6 +76,10 @@ class State(ctypes.Structure):
         ("nb_cap", ctypes.c_int32), ("t_cap", ctypes.c_int64)]
 
 
+class TierCache(ctypes.Structure):
+    _fields_ = [("k_cache", ctypes.c_void_p * 3), ("v_cache", ctypes.c_void_p * 3)]
+
+
 class Outputs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("q", "lambda_", "l2", "key", "idx", "o")]
 
@@ -102,6 +107,12 @@ _SIGS = {
     "mka_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mka_last_error": (ctypes.c_char_p, []),
     "mka_version": (ctypes.c_char_p, []),
+    "mka_full_prefill": (ctypes.c_int, [_PD, _P, _I64, ctypes.POINTER(Weights),
+                                        ctypes.POINTER(State), ctypes.POINTER(TierCache),
+                                        ctypes.POINTER(Outputs), _P, _SZ, _P]),
+    "mka_full_decode_step": (ctypes.c_int, [_PD, _P, _I64, ctypes.POINTER(Weights),
+                                            ctypes.POINTER(State), ctypes.POINTER(TierCache),
+                                            ctypes.POINTER(Outputs), _P, _SZ, _P]),
     "mka_probe_mfma_bf16": (ctypes.c_int, [_I32, _I32, _P, _P]),
     "mka_probe_stream_read": (ctypes.c_int, [_P, _SZ, _P, _P]),
 }
@@ -240,6 +251,18 @@ def mka_decode_step(d, x, pos, weights, state, outputs, ws, ws_bytes, stream=Non
     _check("mka_decode_step", lib().mka_decode_step(
         ctypes.byref(d), _ptr(x), pos, ctypes.byref(weights), ctypes.byref(state),
         ctypes.byref(outputs), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def mka_full_prefill(d, x, pos0, weights, state, tiers, outputs, ws, ws_bytes, stream=None):
+    _check("mka_full_prefill", lib().mka_full_prefill(
+        ctypes.byref(d), _ptr(x), pos0, ctypes.byref(weights), ctypes.byref(state),
+        ctypes.byref(tiers), ctypes.byref(outputs), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def mka_full_decode_step(d, x, pos, weights, state, tiers, outputs, ws, ws_bytes, stream=None):
+    _check("mka_full_decode_step", lib().mka_full_decode_step(
+        ctypes.byref(d), _ptr(x), pos, ctypes.byref(weights), ctypes.byref(state),
+        ctypes.byref(tiers), ctypes.byref(outputs), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def mka_workspace_bytes(d, op, cache_len=0) -> int:

@@ -160,3 +160,33 @@ def test_probe_arguments_rejected():
     assert lib.mka_probe_stream_read(FAKE + 8, 1024, FAKE, None) == mka.MKA_ERR_INVALID
     assert lib.mka_probe_stream_read(FAKE, 1000, FAKE, None) == mka.MKA_ERR_INVALID
     assert lib.mka_probe_stream_read(None, 1024, FAKE, None) == mka.MKA_ERR_INVALID
+
+
+def test_full_mka_arguments_rejected():
+    d = _d()
+    w = mka.Weights(*([FAKE] * 6))
+    st = mka.State(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, nb_cap=64, t_cap=8192)
+    out = mka.Outputs(*([FAKE] * 6))
+    tc = mka.TierCache()  # null caches
+    with pytest.raises(mka.MkaError) as e:
+        mka.mka_full_prefill(d, FAKE, 0, w, st, tc, out, FAKE, 1 << 40, 0)
+    assert e.value.status == mka.MKA_ERR_INVALID
+    for i in range(3):
+        tc.k_cache[i] = FAKE
+        tc.v_cache[i] = FAKE
+    with pytest.raises(mka.MkaError) as e:  # workspace too small
+        mka.mka_full_prefill(d, FAKE, 0, w, st, tc, out, FAKE, 16, 0)
+    assert e.value.status == mka.MKA_ERR_WORKSPACE
+    with pytest.raises(mka.MkaError) as e:  # decode needs seq == 1
+        mka.mka_full_decode_step(d, FAKE, 10, w, st, tc, out, FAKE, 1 << 40, 0)
+    assert e.value.status == mka.MKA_ERR_INVALID
+    # L1 alone needs only the first tier's cache
+    d1 = _d(seq=1, tiers=mka.MKA_TIERS_L1)
+    tc2 = mka.TierCache()
+    tc2.k_cache[0] = FAKE
+    with pytest.raises(mka.MkaError) as e:  # v_cache[0] missing
+        mka.mka_full_decode_step(d1, FAKE, 10, w, st, tc2, out, FAKE, 1 << 40, 0)
+    assert e.value.status == mka.MKA_ERR_INVALID
+    assert mka.mka_workspace_bytes(d, mka.MKA_OP_FULL_PREFILL) > 0
+    assert mka.mka_workspace_bytes(d1, mka.MKA_OP_FULL_DECODE_STEP, 100) > 0
+    assert mka.mka_workspace_bytes(d, mka.MKA_OP_FULL_DECODE_STEP, 100) == 0  # seq != 1
