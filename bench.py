@@ -259,7 +259,33 @@ def bench_prefill(s, steps, warmup, variants=(), settle_ms=0.0, full=False):
                 variants_ms=var_ms, settle_steps=settled, full_ms=full_ms)
 
 
-def bench_decode(s, steps, warmup, variants=(), full=False):
+def bench_prefill_paged(s, steps, warmup, page_size, settle_ms=0.0):
+    """The composite prefill with a paged fused cache (pages of ``page_size``
+    rows, a seeded random order with spare pages in the pool)."""
+    import torch
+
+    from route_kv_memory_amd.inputs import prefill_inputs
+    from route_kv_memory_amd.layer import Layer, to_device
+
+    inp = prefill_inputs(s)
+    layer = Layer(s, inp, t_cap=s.seq, nb_cap=s.seq // s.block, page_size=page_size,
+                  spare_pages=8)
+    x = to_device(inp["x"], s.dtype)
+    del inp
+    out = layer.outputs(s.seq)
+    stream = torch.cuda.current_stream()
+    settle(lambda: layer.prefill(x, 0, out=out, stream=stream), settle_ms)
+    for _ in range(warmup):
+        layer.prefill(x, 0, out=out, stream=stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.prefill(x, 0, out=out, stream=stream)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e3
+
+
+def bench_decode(s, steps, warmup, variants=(), full=False, page_size=None):
     import torch
 
     from route_kv_memory_amd import mka
@@ -271,10 +297,11 @@ def bench_decode(s, steps, warmup, variants=(), full=False):
     T0, n = s.decode_cached, s.decode_steps
     t_cap = T0 + n
     nb0 = T0 // s.block
-    layer = Layer(s, dec, t_cap=t_cap, nb_cap=t_cap // s.block + 1, full=full)
+    layer = Layer(s, dec, t_cap=t_cap, nb_cap=t_cap // s.block + 1, full=full, page_size=page_size,
+                  spare_pages=8 if page_size else 0)
     st = layer.st
-    st["k_cache"][:, :, :T0] = to_device(dec["k_cache"], s.dtype)
-    st["v_cache"][:, :, :T0] = to_device(dec["v_cache"], s.dtype)
+    layer.load_cache("k", to_device(dec["k_cache"], s.dtype))
+    layer.load_cache("v", to_device(dec["v_cache"], s.dtype))
     if full:  # the three tiers' caches hold the same synthetic rows (timing only)
         for c in ("k", "v"):
             for t in layer.kv3[c]:
@@ -328,6 +355,9 @@ def bench_decode(s, steps, warmup, variants=(), full=False):
         log(f"decode full MKA: {full_us['median_us']:.1f} us/token")
     step_us, host_us, wall_us = run()
 
+    if page_size:  # the single-call attention entry takes contiguous caches
+        return dict(median_us=float(np.median(step_us)), host_us=host_us, cached=T0,
+                    steps=steps)
     # Decode attention alone at the first step's length, for its roofline.
     L = T0 + 1
     nbytes = mka.mka_workspace_bytes(d1, mka.MKA_OP_ATTN_DECODE, L)
@@ -345,11 +375,14 @@ def bench_decode(s, steps, warmup, variants=(), full=False):
     a_ev[1].record(stream)
     torch.cuda.synchronize()
     attn_us = a_ev[0].elapsed_time(a_ev[1]) * 1e3 / reps
-    kv_bytes = 2.0 * L * s.n_kv_heads * s.head_dim * 2  # K and V rows, bf16
+    B = s.batch
+    kv_bytes = 2.0 * L * s.n_kv_heads * s.head_dim * 2 * B  # K and V rows of every sequence, bf16
     el = 2
+    # weights and hyperplanes once per step; cache rows, retrieved block rows and
+    # block codes per sequence
     step_bytes = (kv_bytes + (s.q_width * s.d_model + 2 * s.kv_width * s.d_model
                               + s.router_hidden * s.q_width + 3 * s.router_hidden) * el
-                  + s.hash_bits * s.d_model * 4 + s.top_r * s.d_model * 4 + nb0 * 8)
+                  + s.hash_bits * s.d_model * 4 + B * (s.top_r * s.d_model * 4 + nb0 * 8))
     return dict(median_us=float(np.median(step_us)), mean_us=float(step_us.mean()),
                 wall_us=wall_us, host_us=host_us, attn_us=attn_us, kv_bytes=kv_bytes, step_bytes=step_bytes,
                 cached=T0, steps=steps, variants_us=var_us, full=full_us)
@@ -437,6 +470,11 @@ def main():
     ap.add_argument("--full-mka", action="store_true",
                     help="also time full MKA (three attention paths mixed by lambda) on the same "
                          "workloads")
+    ap.add_argument("--paged", type=int, default=0, metavar="ROWS",
+                    help="also time prefill and decode with a paged fused cache of pages of "
+                         "ROWS rows")
+    ap.add_argument("--decode-batch", action="store_true",
+                    help="also time batched decode (4 sequences, 32K cached tokens each)")
     ap.add_argument("--variants", action="store_true",
                     help="also time the routing and tier variants (fixed, hard top-1/top-2; "
                          "L1+L2, L1+L3, L1 alone) on the same workloads")
@@ -532,6 +570,28 @@ def main():
             k: {"prefill_tokens_per_s": tokens / (v * 1e-3), "prefill_ms": v,
                 "decode_us_per_token": dc["variants_us"].get(k) if not args.no_decode else None}
             for k, v in pf["variants_ms"].items()}
+    if args.paged:
+        pms = bench_prefill_paged(s, args.steps, args.warmup, args.paged, args.settle_ms)
+        log(f"paged prefill (pages of {args.paged}): {pms:.4f} ms")
+        line["paged"] = {"page_size": args.paged, "prefill_ms": pms,
+                         "prefill_tokens_per_s": tokens / (pms * 1e-3)}
+        if not args.no_decode:
+            ds = I.workload(args.decode_workload)
+            pdc = bench_decode(ds, ds.decode_steps, 8, page_size=args.paged)
+            log(f"paged decode: {pdc['median_us']:.1f} us/token")
+            line["paged"].update(decode_us_per_token=pdc["median_us"],
+                                 decode_host_us_per_token=pdc["host_us"])
+    if args.decode_batch:
+        bs = I.workload("qwen7b_decode_32k_b4")
+        bdc = bench_decode(bs, bs.decode_steps, 8)
+        log(f"batched decode B={bs.batch}: {bdc['median_us']:.1f} us/step")
+        line["decode_batch"] = {
+            "workload": bs.name, "batch": bs.batch, "cached_tokens": bdc["cached"],
+            "us_per_step_median": bdc["median_us"],
+            "tokens_per_s": bs.batch / (bdc["median_us"] * 1e-6),
+            "step_hbm_frac": bdc["step_bytes"] / (bdc["median_us"] * 1e-6) / PEAK_HBM_BYTES,
+            "attn_us_per_launch": bdc["attn_us"],
+            "attn_hbm_frac": bdc["kv_bytes"] / (bdc["attn_us"] * 1e-6) / PEAK_HBM_BYTES}
     if args.full_mka:
         line["full_mka"] = {
             "prefill_ms": pf["full_ms"], "prefill_tokens_per_s": tokens / (pf["full_ms"] * 1e-3),

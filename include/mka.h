@@ -252,10 +252,25 @@ typedef struct mka_state {
   float* block_means;    /* [B, nb_cap, D] */
   uint64_t* block_hash;  /* [B, nb_cap] */
   float* block_kv;       /* [B, nb_cap, 2*G*dh]: row b = block_means[b] [W_k; W_v]^T */
-  void* k_cache;         /* [B, G, t_cap, dh] */
-  void* v_cache;         /* [B, G, t_cap, dh] */
+  void* k_cache;         /* [B, G, t_cap, dh], or a page pool (see page_table) */
+  void* v_cache;         /* [B, G, t_cap, dh], or a page pool */
   int32_t nb_cap;
   int64_t t_cap;
+  /* Paged fused KV cache (abstract page, Table 4 caption: the measurements use a
+   * contiguous KV layout up to 32K tokens and a paged one beyond).  NULL: the
+   * contiguous layout above.  Otherwise k_cache and v_cache are pools of pages
+   * [n_pages, G, page_size, dh] (dtype) and page_table [B, pages_per_seq]
+   * (int32, device) maps logical page p of sequence b to a pool page: row t of
+   * sequence b is row t % page_size of page page_table[b][t / page_size].
+   * page_size is a power of two in [64, 2^20]; t_cap must equal
+   * pages_per_seq * page_size.  Entries must be valid pool pages; the pages
+   * of rows a call writes must not be shared by other live rows.  Only
+   * mka_prefill and mka_decode_step take a paged state (the full-MKA calls
+   * return MKA_ERR_UNSUPPORTED for one; the single-step calls take
+   * contiguous caches). */
+  const int32_t* page_table;
+  int32_t page_size;
+  int32_t pages_per_seq;
 } mka_state;
 
 typedef struct mka_outputs {

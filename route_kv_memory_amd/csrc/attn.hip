@@ -30,10 +30,10 @@ __device__ __forceinline__ int kperm(int r) {
 // KV group) heaviest first; the H/G heads of a unit are consecutive slots of
 // one XCD so they read the same K/V tiles through that XCD's L2.
 // ---------------------------------------------------------------------------
-template <int DH, int NW>
+template <int DH, int NW, bool PAGED>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
-    bf16_t* __restrict__ O, int B, int seq, int H, int G, int64_t t_cap, int64_t pos0, float sl2,
+    bf16_t* __restrict__ O, int B, int seq, int H, int G, KvLayout kv, int64_t pos0, float sl2,
     int n_qblk, int n_units) {
   constexpr int NT = NW * 64, BM = 32 * NW, BN = 64, KP = DH + 8, VP = BN + 8, NKS = DH / 16,
                 NDB = DH / 32;
@@ -66,24 +66,25 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
       if (q_row >= seq) qf[ks] = bf16x8{};
     }
   }
-  const bf16_t* kbase = Kc + (static_cast<int64_t>(b) * G + g) * t_cap * DH;
-  const bf16_t* vbase = Vc + (static_cast<int64_t>(b) * G + g) * t_cap * DH;
-  // Keys at or beyond kv_end read as zeros through the buffer range.
-  const uint32_t kv_bytes = static_cast<uint32_t>(kv_end * DH * 2);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, kv_bytes), vrs = make_rsrc(vbase, kv_bytes);
-
   u32x4 rk[KCH], rv[4];
+  PageWindow<PAGED> pw;
+  pw.fill(kv, b, 0);
+  // One tile of BN keys lies in one page (pages hold a multiple of 64 rows);
+  // keys at or beyond kv_end read as zeros through the buffer range.
   auto gload = [&](int j0) {
+    const int64_t off = pw.row(kv, b, g, j0);
+    const uint32_t bytes = static_cast<uint32_t>(min<int64_t>(BN, kv_end - j0) * DH * 2);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kc + off, bytes), vrs = make_rsrc(Vc + off, bytes);
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int c = tid + NT * i, row = c / (DH / 8), col = (c % (DH / 8)) * 8;
-      rk[i] = buffer_load16(krs, static_cast<uint32_t>((j0 + row) * DH + col) * 2);
+      rk[i] = buffer_load16(krs, static_cast<uint32_t>(row * DH + col) * 2);
     }
     if (tid < VITEMS) {
       const int kq = tid & 15, dc = tid >> 4;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        rv[r] = buffer_load16(vrs, static_cast<uint32_t>((j0 + 4 * kq + r) * DH + 8 * dc) * 2);
+        rv[r] = buffer_load16(vrs, static_cast<uint32_t>((4 * kq + r) * DH + 8 * dc) * 2);
     }
   };
   // K row j of the tile goes to LDS row kperm(j), so the MFMA reads of
@@ -200,10 +201,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
 // Prefill, fp32: one thread per query row with the online max-shift over key
 // tiles staged in LDS (the reference-precision path of small fp32 layers).
 // ---------------------------------------------------------------------------
-template <int DH>
+template <int DH, bool PAGED>
 __global__ __launch_bounds__(64) void attn_prefill_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ Kc, const float* __restrict__ Vc,
-    float* __restrict__ O, int seq, int H, int G, int64_t t_cap, int64_t pos0, float scale) {
+    float* __restrict__ O, int seq, int H, int G, KvLayout kv, int64_t pos0, float scale) {
   constexpr int TK = 32;
   __shared__ float Ks[TK][DH];
   __shared__ float Vs[TK][DH];
@@ -219,15 +220,19 @@ __global__ __launch_bounds__(64) void attn_prefill_f32_kernel(
     q[d] = qp[d];
     acc[d] = 0.f;
   }
-  const float* kb = Kc + (static_cast<int64_t>(b) * G + g) * t_cap * DH;
-  const float* vb = Vc + (static_cast<int64_t>(b) * G + g) * t_cap * DH;
   float m = -INFINITY, l = 0.f;
+  PageWindow<PAGED> pw;
+  pw.fill(kv, b, 0);
   for (int64_t j0 = 0; j0 < kv_end; j0 += TK) {
+    // a tile of TK keys lies in one page
+    const int64_t off = pw.row(kv, b, g, j0);
+    const float* kb = Kc + off;
+    const float* vb = Vc + off;
     for (int e = tid; e < TK * DH; e += 64) {
       const int r = e / DH, d = e % DH;
       const bool ok = j0 + r < kv_end;
-      Ks[r][d] = ok ? kb[(j0 + r) * DH + d] : 0.f;
-      Vs[r][d] = ok ? vb[(j0 + r) * DH + d] : 0.f;
+      Ks[r][d] = ok ? kb[r * DH + d] : 0.f;
+      Vs[r][d] = ok ? vb[r * DH + d] : 0.f;
     }
     __syncthreads();
     for (int jj = 0; jj < TK; ++jj) {
@@ -262,34 +267,41 @@ constexpr int kAttnWaves = 4;
 
 template <>
 hipError_t attn_prefill<bf16_t>(const bf16_t* q, const bf16_t* k, const bf16_t* v, bf16_t* o, int B,
-                                int seq, int H, int G, int dh, int64_t t_cap, int64_t pos0,
+                                int seq, int H, int G, int dh, const KvLayout& kv, int64_t pos0,
                                 hipStream_t s) {
   constexpr int NW = kAttnWaves;
   const int n_qblk = (seq + 32 * NW - 1) / (32 * NW);
   const int n_units = n_qblk * B * G;
   const int grid = ((n_units + 7) / 8) * 8 * (H / G);
   const float sl2 = 1.4426950408889634f / sqrtf(static_cast<float>(dh));
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(NW * 64), 0, s, q, k, v, o, B, seq, H, G, kv, pos0,
+                       sl2, n_qblk, n_units);
+  };
   if (dh == 128)
-    hipLaunchKernelGGL((attn_prefill_bf16_kernel<128, NW>), dim3(grid), dim3(NW * 64), 0, s, q, k,
-                       v, o, B, seq, H, G, t_cap, pos0, sl2, n_qblk, n_units);
+    kv.paged() ? launch(attn_prefill_bf16_kernel<128, NW, true>)
+               : launch(attn_prefill_bf16_kernel<128, NW, false>);
   else
-    hipLaunchKernelGGL((attn_prefill_bf16_kernel<64, NW>), dim3(grid), dim3(NW * 64), 0, s, q, k,
-                       v, o, B, seq, H, G, t_cap, pos0, sl2, n_qblk, n_units);
+    kv.paged() ? launch(attn_prefill_bf16_kernel<64, NW, true>)
+               : launch(attn_prefill_bf16_kernel<64, NW, false>);
   return hipGetLastError();
 }
 
 template <>
 hipError_t attn_prefill<float>(const float* q, const float* k, const float* v, float* o, int B,
-                               int seq, int H, int G, int dh, int64_t t_cap, int64_t pos0,
+                               int seq, int H, int G, int dh, const KvLayout& kv, int64_t pos0,
                                hipStream_t s) {
   const dim3 grid((seq + 63) / 64, H, B);
   const float scale = 1.0f / sqrtf(static_cast<float>(dh));
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(64), 0, s, q, k, v, o, seq, H, G, kv, pos0, scale);
+  };
   if (dh == 128)
-    hipLaunchKernelGGL(attn_prefill_f32_kernel<128>, grid, dim3(64), 0, s, q, k, v, o, seq, H, G,
-                       t_cap, pos0, scale);
+    kv.paged() ? launch(attn_prefill_f32_kernel<128, true>)
+               : launch(attn_prefill_f32_kernel<128, false>);
   else
-    hipLaunchKernelGGL(attn_prefill_f32_kernel<64>, grid, dim3(64), 0, s, q, k, v, o, seq, H, G,
-                       t_cap, pos0, scale);
+    kv.paged() ? launch(attn_prefill_f32_kernel<64, true>)
+               : launch(attn_prefill_f32_kernel<64, false>);
   return hipGetLastError();
 }
 
@@ -304,14 +316,14 @@ size_t attn_decode_ws_bytes(int B, int H, int G, int dh, int64_t n_rows) {
   return sizeof(float) * static_cast<size_t>(B) * H * n_chunks * (dh + 2);
 }
 
-template <int DH>
+template <int DH, bool PAGED>
 __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
-    int H, int G, int64_t t_cap, int64_t n_rows, float sl2, int chunk, int n_chunks, int n_hb,
+    int H, int G, KvLayout kv, int64_t n_rows, float sl2, int chunk, int n_chunks, int n_hb,
     float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ part_o) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[split_lds_bytes<DH>()];
   const int g = blockIdx.y / n_hb, hb = blockIdx.y % n_hb;
-  decode_split_chunk<DH>(Q, Kc, Vc, H, G, t_cap, n_rows, sl2, chunk, n_chunks, blockIdx.x, g, hb,
+  decode_split_chunk<DH, PAGED>(Q, Kc, Vc, H, G, kv, n_rows, sl2, chunk, n_chunks, blockIdx.x, g, hb,
                          blockIdx.z, part_m, part_l, part_o, lds);
 }
 
@@ -320,11 +332,11 @@ template <int DH>
 __global__ __launch_bounds__(kMergeThreads) void attn_decode_merge_kernel(
     const float* __restrict__ part_m, const float* __restrict__ part_l,
     const float* __restrict__ part_o, int H, int G, int n_chunks, const bf16_t* __restrict__ Q,
-    const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc, int64_t t_cap,
+    const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc, KvLayout kv,
     int64_t extra_row, float sl2, bf16_t* __restrict__ O) {
   __shared__ MergeLds<DH> sm;
   const int h = blockIdx.x, b = blockIdx.y;
-  const int64_t row = ((static_cast<int64_t>(b) * G + h / (H / G)) * t_cap + extra_row) * DH;
+  const int64_t row = extra_row >= 0 ? kv.row(b, h / (H / G), extra_row) : 0;
   decode_merge_head<DH>(part_m, part_l, part_o, H, n_chunks, h, b, Q, sl2, O, sm,
                         [&](float* kx, float* vx) {
                           if (extra_row < 0) return false;
@@ -339,7 +351,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_decode_merge_kernel(
 
 
 hipError_t attn_decode_split_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* v, int B, int H,
-                                  int G, int dh, int64_t t_cap, int64_t n_old, void* ws,
+                                  int G, int dh, const KvLayout& kv, int64_t n_old, void* ws,
                                   hipStream_t s) {
   if (n_old <= 0) return hipSuccess;
   const int chunk = decode_chunk_keys(decode_units(B, H, G), n_old);
@@ -351,17 +363,21 @@ hipError_t attn_decode_split_bf16(const bf16_t* q, const bf16_t* k, const bf16_t
   const float sl2 = 1.4426950408889634f / sqrtf(static_cast<float>(dh));
   const int n_hb = (H / G + kSplitHeads - 1) / kSplitHeads;
   const dim3 grid(n_chunks, G * n_hb, B);
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, q, k, v, H, G, kv, n_old, sl2, chunk,
+                       n_chunks, n_hb, part_m, part_l, part_o);
+  };
   if (dh == 128)
-    hipLaunchKernelGGL(attn_decode_split_kernel<128>, grid, dim3(256), 0, s, q, k, v, H, G, t_cap,
-                       n_old, sl2, chunk, n_chunks, n_hb, part_m, part_l, part_o);
+    kv.paged() ? launch(attn_decode_split_kernel<128, true>)
+               : launch(attn_decode_split_kernel<128, false>);
   else
-    hipLaunchKernelGGL(attn_decode_split_kernel<64>, grid, dim3(256), 0, s, q, k, v, H, G, t_cap,
-                       n_old, sl2, chunk, n_chunks, n_hb, part_m, part_l, part_o);
+    kv.paged() ? launch(attn_decode_split_kernel<64, true>)
+               : launch(attn_decode_split_kernel<64, false>);
   return hipGetLastError();
 }
 
 hipError_t attn_decode_merge_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* v, bf16_t* o,
-                                  int B, int H, int G, int dh, int64_t t_cap, int64_t n_old,
+                                  int B, int H, int G, int dh, const KvLayout& kv, int64_t n_old,
                                   int64_t extra_row, void* ws, hipStream_t s) {
   const int n_chunks = n_old > 0 ? decode_n_chunks(decode_units(B, H, G), n_old) : 0;
   if (n_chunks > kMaxDecodeChunks) return hipErrorInvalidValue;
@@ -371,20 +387,20 @@ hipError_t attn_decode_merge_bf16(const bf16_t* q, const bf16_t* k, const bf16_t
   const float sl2 = 1.4426950408889634f / sqrtf(static_cast<float>(dh));
   if (dh == 128)
     hipLaunchKernelGGL(attn_decode_merge_kernel<128>, dim3(H, B), dim3(kMergeThreads), 0, s, part_m,
-                       part_l, part_o, H, G, n_chunks, q, k, v, t_cap, extra_row, sl2, o);
+                       part_l, part_o, H, G, n_chunks, q, k, v, kv, extra_row, sl2, o);
   else
     hipLaunchKernelGGL(attn_decode_merge_kernel<64>, dim3(H, B), dim3(kMergeThreads), 0, s, part_m,
-                       part_l, part_o, H, G, n_chunks, q, k, v, t_cap, extra_row, sl2, o);
+                       part_l, part_o, H, G, n_chunks, q, k, v, kv, extra_row, sl2, o);
   return hipGetLastError();
 }
 
 // Rows [0, cache_len - 1) through the split kernel; the last row in the merge.
 hipError_t attn_decode_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* v, bf16_t* o, int B,
-                            int H, int G, int dh, int64_t t_cap, int64_t cache_len, void* ws,
+                            int H, int G, int dh, const KvLayout& kv, int64_t cache_len, void* ws,
                             hipStream_t s) {
-  const hipError_t e = attn_decode_split_bf16(q, k, v, B, H, G, dh, t_cap, cache_len - 1, ws, s);
+  const hipError_t e = attn_decode_split_bf16(q, k, v, B, H, G, dh, kv, cache_len - 1, ws, s);
   if (e != hipSuccess) return e;
-  return attn_decode_merge_bf16(q, k, v, o, B, H, G, dh, t_cap, cache_len - 1, cache_len - 1, ws, s);
+  return attn_decode_merge_bf16(q, k, v, o, B, H, G, dh, kv, cache_len - 1, cache_len - 1, ws, s);
 }
 
 }  // namespace mka

@@ -83,11 +83,11 @@ __device__ __forceinline__ void wave_lds_sync() { __builtin_amdgcn_fence(__ATOMI
 // sequence b, over cache rows [c*chunk, min((c+1)*chunk, n_rows)).  Partial p
 // of query head h lives at (b*H + h) * n_chunks + c of part_m / part_l and
 // p*DH of part_o.  Uses 256 threads and split_lds_bytes<DH>() bytes of ``lds``.
-template <int DH>
+template <int DH, bool PAGED>
 __device__ __forceinline__ void decode_split_chunk(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
-    int H, int G, int64_t t_cap, int64_t n_rows, float sl2, int chunk, int n_chunks, int c, int g,
-    int hb, int b, float* __restrict__ part_m, float* __restrict__ part_l,
+    int H, int G, const KvLayout& kv, int64_t n_rows, float sl2, int chunk, int n_chunks, int c,
+    int g, int hb, int b, float* __restrict__ part_m, float* __restrict__ part_l,
     float* __restrict__ part_o, unsigned char* lds) {
   constexpr int BN = kSplitTile, VP = BN + 8, NKS = DH / 32, NDB = DH / 16, KQ = BN / 4;
   constexpr int VL = KQ * (DH / 8) / 64;  // V load items per lane per tile
@@ -112,10 +112,6 @@ __device__ __forceinline__ void decode_split_chunk(
   const int rows_here = static_cast<int>(min<int64_t>(chunk, n_rows - c0));
   const int n_tiles = (rows_here + BN - 1) / BN;
   const int my_tiles = (n_tiles - wave + 3) / 4;  // tiles wave, wave + 4, ...
-  const int64_t head0 = (static_cast<int64_t>(b) * G + g) * t_cap + c0;
-  // Rows past the chunk's end read as zeros (buffer range check).
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kc + head0 * DH, static_cast<uint32_t>(rows_here) * DH * 2);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(Vc + head0 * DH, static_cast<uint32_t>(rows_here) * DH * 2);
 
   float m_i = -INFINITY, l_i = 0.f;
   f32x4 acc[NDB];
@@ -124,11 +120,18 @@ __device__ __forceinline__ void decode_split_chunk(
 
   const int krow = 8 * (l16 >> 2) + (l16 & 3);  // key of MFMA row l16 in sub-block 0
   u32x4 kbuf[2][2 * NKS], vbuf[2][VL * 4];
+  // A tile of BN keys (chunks start at multiples of BN) lies in one page; rows
+  // past the chunk's end read as zeros through the buffer range.
+  PageWindow<PAGED> pw;
+  pw.fill(kv, b, static_cast<int>(c0 >> kv.page_shift));
   auto issue = [&](int tile, u32x4* kb_, u32x4* vb_) {
     const int jr = (wave + 4 * tile) * BN;
+    const int64_t base = pw.row(kv, b, g, c0 + jr);
+    const uint32_t bytes = static_cast<uint32_t>(min(BN, rows_here - jr)) * DH * 2;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kc + base, bytes), vrs = make_rsrc(Vc + base, bytes);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const uint32_t off = static_cast<uint32_t>((jr + krow + 4 * kb) * DH + 8 * q4) * 2;
+      const uint32_t off = static_cast<uint32_t>((krow + 4 * kb) * DH + 8 * q4) * 2;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) kb_[kb * NKS + ks] = buffer_load16(krs, off + 64 * ks);
     }
@@ -137,7 +140,7 @@ __device__ __forceinline__ void decode_split_chunk(
       const int item = lane + 64 * it, kq = item % KQ, dc = item / KQ;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        vb_[it * 4 + r] = buffer_load16(vrs, static_cast<uint32_t>((jr + 4 * kq + r) * DH + 8 * dc) * 2);
+        vb_[it * 4 + r] = buffer_load16(vrs, static_cast<uint32_t>((4 * kq + r) * DH + 8 * dc) * 2);
     }
   };
   auto compute = [&](int tile, const u32x4* kb_, const u32x4* vb_) {

@@ -177,6 +177,69 @@ __device__ __forceinline__ int xcd_contiguous(int bid, int n) {
 constexpr int kRouteSoft = 0, kRouteFixed = 1, kRouteTop1 = 2, kRouteTop2 = 3;
 constexpr int kTiersAll = 0, kTiersL1L2 = 1, kTiersL1L3 = 2, kTiersL1 = 3;
 
+// Where row t of KV head g of sequence b lives in a K or V cache (element
+// offset).  Contiguous: [B, G, t_cap, dh].  Paged: a pool of pages
+// [n_pages, G, page, dh] and a page table [B, pages_per_seq] (int32), logical
+// row t of sequence b in page table[b][t >> page_shift] at row t & (page - 1).
+struct KvLayout {
+  const int32_t* pt = nullptr;  // page table, or null for the contiguous layout
+  int page_shift = 0;
+  int pps = 0;                  // pages per sequence
+  int G = 1, DH = 128;
+  int64_t t_cap = 0;            // rows per (b, g) when contiguous
+  __host__ __device__ bool paged() const { return pt != nullptr; }
+  // The layout fixed at compile time (the attention kernels' inner loops).
+  template <bool PAGED>
+  __device__ __forceinline__ int64_t row_as(int b, int g, int64_t t) const {
+    if constexpr (!PAGED) {
+      return ((static_cast<int64_t>(b) * G + g) * t_cap + t) * DH;
+    } else {
+      const int64_t page = pt[static_cast<int64_t>(b) * pps + (t >> page_shift)];
+      const int64_t in_page = t & ((static_cast<int64_t>(1) << page_shift) - 1);
+      return ((page * G + g) * (static_cast<int64_t>(1) << page_shift) + in_page) * DH;
+    }
+  }
+  __device__ __forceinline__ int64_t row(int b, int g, int64_t t) const {
+    return pt == nullptr ? row_as<false>(b, g, t) : row_as<true>(b, g, t);
+  }
+  // rows from t to the end of t's page (contiguous: to t_cap)
+  __device__ __forceinline__ int64_t rows_to_boundary(int64_t t) const {
+    if (pt == nullptr) return t_cap - t;
+    const int64_t p = static_cast<int64_t>(1) << page_shift;
+    return p - (t & (p - 1));
+  }
+};
+
+// A wave's window on the page table: lane l holds the pool page of logical
+// page first + l, so a tile finds its page with a register read (readlane of a
+// wave-uniform index) instead of a memory load on its loads' critical path; the
+// window moves (one vector load) when a tile lies outside it.  With the
+// contiguous layout it is the plain formula.
+template <bool PAGED>
+struct PageWindow {
+  int first = -(1 << 30);
+  int entry = 0;
+  __device__ __forceinline__ void fill(const KvLayout& kv, int b, int page) {
+    if constexpr (PAGED) {
+      first = page;
+      const int p = min(page + static_cast<int>(threadIdx.x & 63), kv.pps - 1);
+      entry = kv.pt[static_cast<int64_t>(b) * kv.pps + p];
+    }
+  }
+  // Element offset of row t of KV head g; t must be wave-uniform.
+  __device__ __forceinline__ int64_t row(const KvLayout& kv, int b, int g, int64_t t) {
+    if constexpr (!PAGED) {
+      return kv.row_as<false>(b, g, t);
+    } else {
+      const int page = static_cast<int>(t >> kv.page_shift);
+      if (page < first || page >= first + 64) fill(kv, b, page);
+      const int64_t pool = __builtin_amdgcn_readlane(entry, page - first);
+      const int64_t in_page = t & ((static_cast<int64_t>(1) << kv.page_shift) - 1);
+      return ((pool * kv.G + g) * (static_cast<int64_t>(1) << kv.page_shift) + in_page) * kv.DH;
+    }
+  }
+};
+
 // A constant lambda vector passed by value.
 struct Lam3 {
   float v[3] = {0.f, 0.f, 0.f};

@@ -51,10 +51,10 @@ struct DecodeArgs {
   float* kvl3;
   const float* block_kv;  // [B, nb_cap, 2*kvw] projected block means
   // cache and attention
-  T* k_cache;      // [B, G, t_cap, dh]
+  T* k_cache;      // rows addressed through kv (contiguous or paged)
   T* v_cache;
   int H, G, dh;
-  int64_t t_cap;
+  KvLayout kv;
   float sl2;       // log2(e) / sqrt(dh)
   float* part_m;   // split partials over rows [0, pos)
   float* part_l;

@@ -441,7 +441,7 @@ __global__ __launch_bounds__(256) void decode_inputs_kernel(DecodeArgs<bf16_t> a
         ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
 }
 
-template <int DH, int RMAX>
+template <int DH, int RMAX, bool PAGED>
 __global__ __launch_bounds__(256, 2) void decode_attend_kernel(DecodeArgs<bf16_t> a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[split_lds_bytes<DH>()];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -646,7 +646,7 @@ __global__ __launch_bounds__(256, 2) void decode_attend_kernel(DecodeArgs<bf16_t
   const int per_b = a.n_chunks * a.G * a.n_hb;
   const int b = wg / per_b, rest = wg % per_b;
   const int c = rest % a.n_chunks, ghb = rest / a.n_chunks;
-  decode_split_chunk<DH>(a.q, a.k_cache, a.v_cache, a.H, a.G, a.t_cap, a.pos, a.sl2, a.chunk,
+  decode_split_chunk<DH, PAGED>(a.q, a.k_cache, a.v_cache, a.H, a.G, a.kv, a.pos, a.sl2, a.chunk,
                          a.n_chunks, c, ghb / a.n_hb, ghb % a.n_hb, b, a.part_m, a.part_l,
                          a.part_o, lds);
 }
@@ -700,7 +700,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs<
           kx[tid] = bf16_to_f32(kb);
           vx[tid] = bf16_to_f32(vb);
           if (h % hpg == 0) {
-            const int64_t ro = ((static_cast<int64_t>(b) * a.G + g) * a.t_cap + a.pos) * DH + tid;
+            const int64_t ro = a.kv.row(b, g, a.pos) + tid;
             a.k_cache[ro] = kb;
             a.v_cache[ro] = vb;
           }
@@ -720,16 +720,21 @@ hipError_t decode_attend_bf16(const DecodeArgs<bf16_t>& a, hipStream_t s) {
   const int per_wg = 4 * kGemvCols;
   const int grid = (a.rt.learned() ? (a.r + 3) / 4 : 0) + (2 * a.kvw + per_wg - 1) / per_wg +
                    a.B + a.n_chunks * a.G * a.n_hb * a.B;
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, s, a);
+  };
+  const bool r16 = a.R <= 16, paged = a.kv.paged();
   if (a.dh == 128) {
-    if (a.R <= 16)
-      hipLaunchKernelGGL((decode_attend_kernel<128, 16>), dim3(grid), dim3(256), 0, s, a);
+    if (paged)
+      r16 ? launch(decode_attend_kernel<128, 16, true>) : launch(decode_attend_kernel<128, 32, true>);
     else
-      hipLaunchKernelGGL((decode_attend_kernel<128, 32>), dim3(grid), dim3(256), 0, s, a);
+      r16 ? launch(decode_attend_kernel<128, 16, false>)
+          : launch(decode_attend_kernel<128, 32, false>);
   } else {
-    if (a.R <= 16)
-      hipLaunchKernelGGL((decode_attend_kernel<64, 16>), dim3(grid), dim3(256), 0, s, a);
+    if (paged)
+      r16 ? launch(decode_attend_kernel<64, 16, true>) : launch(decode_attend_kernel<64, 32, true>);
     else
-      hipLaunchKernelGGL((decode_attend_kernel<64, 32>), dim3(grid), dim3(256), 0, s, a);
+      r16 ? launch(decode_attend_kernel<64, 16, false>) : launch(decode_attend_kernel<64, 32, false>);
   }
   return hipGetLastError();
 }

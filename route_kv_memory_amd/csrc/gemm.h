@@ -36,7 +36,7 @@ struct EpiKV {
   int seq;
   int n_kv_heads;
   int head_dim;
-  int64_t t_cap;
+  KvLayout kv;    // the cache layout (contiguous or paged)
   int64_t pos0;
   __device__ __forceinline__ void operator()(int m, int n, float val) const {
     const int kvw = n_kv_heads * head_dim;
@@ -44,8 +44,7 @@ struct EpiKV {
     const int nn = n < kvw ? n : n - kvw;
     const int b = m / seq, t = m - b * seq;
     const int g = nn / head_dim, d = nn - g * head_dim;
-    base[((static_cast<int64_t>(b) * n_kv_heads + g) * t_cap + pos0 + t) * head_dim + d] =
-        Elem<T>::from_f32(val);
+    base[kv.row(b, g, pos0 + t) + d] = Elem<T>::from_f32(val);
   }
   // Columns n .. n+3 (n % 4 == 0) lie in one head row since head_dim % 4 == 0.
   __device__ __forceinline__ void store4(int m, int n, const float* vals, int N) const {
@@ -55,8 +54,7 @@ struct EpiKV {
     const int nn = n < kvw ? n : n - kvw;
     const int b = m / seq, t = m - b * seq;
     const int g = nn / head_dim, d = nn - g * head_dim;
-    mka::store4(base + ((static_cast<int64_t>(b) * n_kv_heads + g) * t_cap + pos0 + t) * head_dim + d,
-                vals);
+    mka::store4(base + kv.row(b, g, pos0 + t) + d, vals);
   }
 };
 

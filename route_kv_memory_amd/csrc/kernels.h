@@ -87,21 +87,21 @@ hipError_t block_kv_project(const float* means, int nb_cap, int first, int n_blo
 // ---- attention --------------------------------------------------------------------
 template <typename T>
 hipError_t attn_prefill(const T* q, const T* k, const T* v, T* o, int B, int seq, int H, int G,
-                        int dh, int64_t t_cap, int64_t pos0, hipStream_t s);
+                        int dh, const KvLayout& kv, int64_t pos0, hipStream_t s);
 // Split decode (bf16): partials in ws (for n_rows rows split into chunks),
 // merged by a second kernel.
 size_t attn_decode_ws_bytes(int B, int H, int G, int dh, int64_t n_rows);
 hipError_t attn_decode_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* v, bf16_t* o, int B,
-                            int H, int G, int dh, int64_t t_cap, int64_t cache_len, void* ws,
+                            int H, int G, int dh, const KvLayout& kv, int64_t cache_len, void* ws,
                             hipStream_t s);
 // The same in two halves, so that work can run between them: the split over
 // cache rows [0, n_old) (nothing when n_old == 0), then the merge, which also
 // folds in row n_old (written in between) as one more part.
 hipError_t attn_decode_split_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* v, int B, int H,
-                                  int G, int dh, int64_t t_cap, int64_t n_old, void* ws,
+                                  int G, int dh, const KvLayout& kv, int64_t n_old, void* ws,
                                   hipStream_t s);
 hipError_t attn_decode_merge_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* v, bf16_t* o,
-                                  int B, int H, int G, int dh, int64_t t_cap, int64_t n_old,
+                                  int B, int H, int G, int dh, const KvLayout& kv, int64_t n_old,
                                   int64_t extra_row, void* ws, hipStream_t s);
 
 }  // namespace mka

@@ -83,6 +83,27 @@ int rows_of(const mka_dims* d) { return d->batch * d->seq; }
 
 Routing routing_of(const mka_dims* d) { return Routing{d->route_mode, d->tiers}; }
 
+KvLayout contiguous(const mka_dims* d, int64_t t_cap) {
+  KvLayout kv;
+  kv.G = d->n_kv_heads;
+  kv.DH = d->head_dim;
+  kv.t_cap = t_cap;
+  return kv;
+}
+
+// The layer state's cache layout: paged when it carries a page table.
+KvLayout layout_of(const mka_dims* d, const mka_state* st) {
+  KvLayout kv = contiguous(d, st->t_cap);
+  if (st->page_table != nullptr) {
+    kv.pt = st->page_table;
+    int shift = 0;
+    while ((1 << shift) < st->page_size) ++shift;
+    kv.page_shift = shift;
+    kv.pps = st->pages_per_seq;
+  }
+  return kv;
+}
+
 size_t ema_ws(const mka_dims* d) { return round256(ema_ws_bytes(d->batch, d->seq, d->d_model)); }
 size_t fuse_ws(const mka_dims* d) {
   return round256(static_cast<size_t>(rows_of(d)) * d->d_model * el_size(d));
@@ -242,11 +263,11 @@ int do_retrieve(const mka_dims* d, const float* l2, const float* proj, const uin
 }
 
 int do_kv_proj(const mka_dims* d, const void* src, const void* w_k, const void* w_v, void* kc,
-               void* vc, int64_t pos0, int64_t t_cap, hipStream_t s);
+               void* vc, int64_t pos0, const KvLayout& kv, hipStream_t s);
 
 int do_fuse_kv(const mka_dims* d, const void* x, const float* l2, const float* means, int nb_cap,
                const int32_t* idx, const float* lam, const void* w_k, const void* w_v, void* kc,
-               void* vc, int64_t pos0, int64_t t_cap, void* ws, hipStream_t s) {
+               void* vc, int64_t pos0, const KvLayout& kv, void* ws, hipStream_t s) {
   const Routing rt = routing_of(d);
   // L1 alone: X_fused = x (lambda = (1, 0, 0)), projected without a fusion pass
   const void* src = x;
@@ -261,19 +282,19 @@ int do_fuse_kv(const mka_dims* d, const void* x, const float* l2, const float* m
                                          static_cast<float*>(ws), s));
     src = ws;
   }
-  return do_kv_proj(d, src, w_k, w_v, kc, vc, pos0, t_cap, s);
+  return do_kv_proj(d, src, w_k, w_v, kc, vc, pos0, kv, s);
 }
 
 // [K|V] rows pos0 .. pos0+seq-1 of one cache from the rows ``src`` [B, seq, D].
 int do_kv_proj(const mka_dims* d, const void* src, const void* w_k, const void* w_v, void* kc,
-               void* vc, int64_t pos0, int64_t t_cap, hipStream_t s) {
+               void* vc, int64_t pos0, const KvLayout& kv, hipStream_t s) {
   const int M = rows_of(d), D = d->d_model, kvw = d->n_kv_heads * d->head_dim;
   if (d->dtype == MKA_BF16) {
     const bf16_t* xs = static_cast<const bf16_t*>(src);
     const bf16_t* wk = static_cast<const bf16_t*>(w_k);
     const bf16_t* wv = static_cast<const bf16_t*>(w_v);
     const EpiKV<bf16_t> epi{static_cast<bf16_t*>(kc), static_cast<bf16_t*>(vc), d->seq,
-                            d->n_kv_heads, d->head_dim, t_cap, pos0};
+                            d->n_kv_heads, d->head_dim, kv, pos0};
     if (M <= kFewRows)
       MKA_LAUNCH("kv_gemv", gemv<bf16_t>(xs, D, M, wk, wv, kvw, 2 * kvw, D, epi, s));
     else
@@ -283,7 +304,7 @@ int do_kv_proj(const mka_dims* d, const void* src, const void* w_k, const void* 
     const float* wk = static_cast<const float*>(w_k);
     const float* wv = static_cast<const float*>(w_v);
     const EpiKV<float> epi{static_cast<float*>(kc), static_cast<float*>(vc), d->seq, d->n_kv_heads,
-                           d->head_dim, t_cap, pos0};
+                           d->head_dim, kv, pos0};
     if (M <= kFewRows)
       MKA_LAUNCH("kv_gemv", gemv<float>(xs, D, M, wk, wv, kvw, 2 * kvw, D, epi, s));
     else
@@ -330,33 +351,33 @@ int do_mix(const mka_dims* d, void* const a[3], const float* lam, void* o, hipSt
 }
 
 int do_attn_prefill(const mka_dims* d, const void* q, const void* kc, const void* vc,
-                    int64_t t_cap, int64_t pos0, void* o, hipStream_t s) {
+                    const KvLayout& kv, int64_t pos0, void* o, hipStream_t s) {
   if (d->dtype == MKA_BF16)
     MKA_LAUNCH("attn_prefill",
                attn_prefill<bf16_t>(static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(kc),
                                     static_cast<const bf16_t*>(vc), static_cast<bf16_t*>(o),
                                     d->batch, d->seq, d->n_heads, d->n_kv_heads, d->head_dim,
-                                    t_cap, pos0, s));
+                                    kv, pos0, s));
   else
     MKA_LAUNCH("attn_prefill",
                attn_prefill<float>(static_cast<const float*>(q), static_cast<const float*>(kc),
                                    static_cast<const float*>(vc), static_cast<float*>(o), d->batch,
-                                   d->seq, d->n_heads, d->n_kv_heads, d->head_dim, t_cap, pos0, s));
+                                   d->seq, d->n_heads, d->n_kv_heads, d->head_dim, kv, pos0, s));
   return MKA_OK;
 }
 
-int do_attn_decode(const mka_dims* d, const void* q, const void* kc, const void* vc, int64_t t_cap,
+int do_attn_decode(const mka_dims* d, const void* q, const void* kc, const void* vc, const KvLayout& kv,
                    int64_t cache_len, void* o, void* ws, hipStream_t s) {
   if (d->dtype == MKA_BF16)
     MKA_LAUNCH("attn_decode",
                attn_decode_bf16(static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(kc),
                                 static_cast<const bf16_t*>(vc), static_cast<bf16_t*>(o), d->batch,
-                                d->n_heads, d->n_kv_heads, d->head_dim, t_cap, cache_len, ws, s));
+                                d->n_heads, d->n_kv_heads, d->head_dim, kv, cache_len, ws, s));
   else  // one query row at position cache_len - 1
     MKA_LAUNCH("attn_decode",
                attn_prefill<float>(static_cast<const float*>(q), static_cast<const float*>(kc),
                                    static_cast<const float*>(vc), static_cast<float*>(o), d->batch,
-                                   1, d->n_heads, d->n_kv_heads, d->head_dim, t_cap, cache_len - 1,
+                                   1, d->n_heads, d->n_kv_heads, d->head_dim, kv, cache_len - 1,
                                    s));
   return MKA_OK;
 }
@@ -487,6 +508,7 @@ int check_full_args(const mka_dims* d, const void* x, int64_t pos0, const mka_we
   MKA_CHECK(pos0 >= 0 && st->nb_cap >= 1 && st->nb_cap < 0xFFFFFF, MKA_ERR_INVALID);
   MKA_CHECK(pos0 + d->seq <= st->t_cap, MKA_ERR_INVALID);
   MKA_CHECK((pos0 + d->seq) / d->block <= st->nb_cap, MKA_ERR_INVALID);
+  MKA_CHECK(st->page_table == nullptr, MKA_ERR_UNSUPPORTED);  // the tier caches are contiguous
   return MKA_OK;
 }
 
@@ -633,7 +655,7 @@ int mka_fuse_kv_proj(const mka_dims* d, const void* x, const float* l2, const fl
   MKA_CHECK(ptrs_ok({ws}), MKA_ERR_WORKSPACE);
   MKA_CHECK(ws_bytes >= fuse_ws(d), MKA_ERR_WORKSPACE);
   return do_fuse_kv(d, x, l2, block_means, nb_cap, idx, lambda, w_k, w_v, k_cache, v_cache, pos0,
-                    t_cap, ws, static_cast<hipStream_t>(stream));
+                    contiguous(d, t_cap), ws, static_cast<hipStream_t>(stream));
 }
 
 int mka_attn_prefill(const mka_dims* d, const void* q, const void* k_cache, const void* v_cache,
@@ -642,7 +664,8 @@ int mka_attn_prefill(const mka_dims* d, const void* q, const void* k_cache, cons
   if (rc) return rc;
   MKA_CHECK(ptrs_ok({q, k_cache, v_cache, o}), MKA_ERR_INVALID);
   MKA_CHECK(pos0 >= 0 && pos0 + d->seq <= t_cap, MKA_ERR_INVALID);
-  return do_attn_prefill(d, q, k_cache, v_cache, t_cap, pos0, o, static_cast<hipStream_t>(stream));
+  return do_attn_prefill(d, q, k_cache, v_cache, contiguous(d, t_cap), pos0, o,
+                         static_cast<hipStream_t>(stream));
 }
 
 int mka_attn_decode(const mka_dims* d, const void* q, const void* k_cache, const void* v_cache,
@@ -659,7 +682,7 @@ int mka_attn_decode(const mka_dims* d, const void* q, const void* k_cache, const
     MKA_CHECK(ptrs_ok({ws}), MKA_ERR_WORKSPACE);
     MKA_CHECK(ws_bytes >= decode_ws(d, cache_len), MKA_ERR_WORKSPACE);
   }
-  return do_attn_decode(d, q, k_cache, v_cache, t_cap, cache_len, o, ws,
+  return do_attn_decode(d, q, k_cache, v_cache, contiguous(d, t_cap), cache_len, o, ws,
                         static_cast<hipStream_t>(stream));
 }
 
@@ -676,6 +699,14 @@ static int check_layer_args(const mka_dims* d, const void* x, int64_t pos0, cons
   MKA_CHECK(pos0 >= 0 && st->nb_cap >= 1 && st->nb_cap < 0xFFFFFF, MKA_ERR_INVALID);
   MKA_CHECK(pos0 + d->seq <= st->t_cap, MKA_ERR_INVALID);
   MKA_CHECK((pos0 + d->seq) / d->block <= st->nb_cap, MKA_ERR_INVALID);
+  if (st->page_table != nullptr) {
+    MKA_CHECK((reinterpret_cast<uintptr_t>(st->page_table) & 3u) == 0, MKA_ERR_INVALID);
+    MKA_CHECK(st->page_size >= 64 && st->page_size <= (1 << 20) &&
+                  (st->page_size & (st->page_size - 1)) == 0 && st->pages_per_seq >= 1,
+              MKA_ERR_INVALID);
+    MKA_CHECK(static_cast<int64_t>(st->pages_per_seq) * st->page_size == st->t_cap,
+              MKA_ERR_INVALID);
+  }
   return MKA_OK;
 }
 
@@ -725,9 +756,10 @@ int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weight
                                    out->key, out->idx, ws_main, s)))
     return rc;
   if ((rc = do_fuse_kv(d, x, out->l2, st->block_means, st->nb_cap, out->idx, out->lambda, w->w_k,
-                       w->w_v, st->k_cache, st->v_cache, pos0, st->t_cap, ws_main, s)))
+                       w->w_v, st->k_cache, st->v_cache, pos0, layout_of(d, st), ws_main, s)))
     return rc;
-  if ((rc = do_attn_prefill(d, out->q, st->k_cache, st->v_cache, st->t_cap, pos0, out->o, s)))
+  if ((rc = do_attn_prefill(d, out->q, st->k_cache, st->v_cache, layout_of(d, st), pos0, out->o,
+                            s)))
     return rc;
   MKA_LAUNCH("prefill/join", hipStreamWaitEvent(s, aux->done, 0));
   return MKA_OK;
@@ -805,7 +837,7 @@ int mka_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_wei
     a.H = H;
     a.G = G;
     a.dh = dh;
-    a.t_cap = st->t_cap;
+    a.kv = layout_of(d, st);
     a.sl2 = 1.4426950408889634f / sqrtf(static_cast<float>(dh));
     a.n_hb = (H / G + kSplitHeads - 1) / kSplitHeads;
     a.chunk = decode_chunk_keys(B * G * a.n_hb, pos);
@@ -825,10 +857,10 @@ int mka_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_wei
     MKA_LAUNCH("decode/mid", decode_mid<float>(a, s));
     MKA_LAUNCH("decode/fuse", decode_fuse<float>(a, s));
     const EpiKV<float> epi{static_cast<float*>(st->k_cache), static_cast<float*>(st->v_cache), 1,
-                           G, dh, st->t_cap, pos};
+                           G, dh, layout_of(d, st), pos};
     MKA_LAUNCH("decode/kv", gemv<float>(a.xf, D, B, static_cast<const float*>(w->w_k),
                                         static_cast<const float*>(w->w_v), kvw, 2 * kvw, D, epi, s));
-    if ((rc = do_attn_decode(d, out->q, st->k_cache, st->v_cache, st->t_cap, pos + 1, out->o,
+    if ((rc = do_attn_decode(d, out->q, st->k_cache, st->v_cache, layout_of(d, st), pos + 1, out->o,
                              nullptr, s)))
       return rc;
   } else {
@@ -889,17 +921,18 @@ int mka_full_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_w
                                    out->key, out->idx, ws_main, s)))
     return rc;
   const bool on[3] = {true, rt.l2(), rt.l3()};
+  const KvLayout tiers_kv = contiguous(d, st->t_cap);
   void* a[3] = {nullptr, nullptr, nullptr};
   for (int l = 0; l < 3; ++l) {
     if (!on[l]) continue;
     const void* src = tier_source(d, l, x, out->l2, st->block_means, st->nb_cap, out->idx, rows,
                                   s, &rc);
     if (rc) return rc;
-    if ((rc = do_kv_proj(d, src, w->w_k, w->w_v, kv->k_cache[l], kv->v_cache[l], pos0, st->t_cap,
+    if ((rc = do_kv_proj(d, src, w->w_k, w->w_v, kv->k_cache[l], kv->v_cache[l], pos0, tiers_kv,
                          s)))
       return rc;
     a[l] = paths + l * L.path;
-    if ((rc = do_attn_prefill(d, out->q, kv->k_cache[l], kv->v_cache[l], st->t_cap, pos0, a[l],
+    if ((rc = do_attn_prefill(d, out->q, kv->k_cache[l], kv->v_cache[l], tiers_kv, pos0, a[l],
                               s)))
       return rc;
   }
@@ -932,17 +965,18 @@ int mka_full_decode_step(const mka_dims* d, const void* x, int64_t pos, const mk
                                    out->key, out->idx, shared, s)))
     return rc;
   const bool on[3] = {true, rt.l2(), rt.l3()};
+  const KvLayout tiers_kv = contiguous(d, st->t_cap);
   void* a[3] = {nullptr, nullptr, nullptr};
   for (int l = 0; l < 3; ++l) {
     if (!on[l]) continue;
     const void* src = tier_source(d, l, x, out->l2, st->block_means, st->nb_cap, out->idx, rows,
                                   s, &rc);
     if (rc) return rc;
-    if ((rc = do_kv_proj(d, src, w->w_k, w->w_v, kv->k_cache[l], kv->v_cache[l], pos, st->t_cap,
+    if ((rc = do_kv_proj(d, src, w->w_k, w->w_v, kv->k_cache[l], kv->v_cache[l], pos, tiers_kv,
                          s)))
       return rc;
     a[l] = paths + l * L.path;
-    if ((rc = do_attn_decode(d, out->q, kv->k_cache[l], kv->v_cache[l], st->t_cap, pos + 1, a[l],
+    if ((rc = do_attn_decode(d, out->q, kv->k_cache[l], kv->v_cache[l], tiers_kv, pos + 1, a[l],
                              shared, s)))
       return rc;
   }

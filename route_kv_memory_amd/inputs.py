@@ -132,6 +132,11 @@ WORKLOADS = {
         n_heads=28, n_kv_heads=4, head_dim=128, router_hidden=64, ema_decay=0.99,
         block=128, hash_bits=64, top_r=16, seed=3, decode_cached=131072,
         decode_steps=256),
+    "qwen7b_decode_32k_b4": LayerShape(
+        name="qwen7b_decode_32k_b4", dtype="bf16", batch=4, seq=1, d_model=3584,
+        n_heads=28, n_kv_heads=4, head_dim=128, router_hidden=64, ema_decay=0.99,
+        block=128, hash_bits=64, top_r=16, seed=5, decode_cached=32768,
+        decode_steps=64),
     "llama8b_prefill_64k": LayerShape(
         name="llama8b_prefill_64k", dtype="bf16", batch=1, seq=65536, d_model=4096,
         n_heads=32, n_kv_heads=8, head_dim=128, router_hidden=64, ema_decay=0.995,

@@ -27,7 +27,8 @@ def to_device(a: np.ndarray, dtype: str | None = None, device="cuda") -> torch.T
 
 class Layer:
     def __init__(self, shape, weights: dict, *, t_cap: int, nb_cap: int, batch: int | None = None,
-                 device="cuda", full: bool = False):
+                 device="cuda", full: bool = False, page_size: int | None = None,
+                 spare_pages: int = 0, page_seed: int = 0):
         self.shape = shape
         self.batch = shape.batch if batch is None else batch
         self.device = device
@@ -39,17 +40,34 @@ class Layer:
         self.weights = mka.Weights(**{k: v.data_ptr() for k, v in self.w.items()})
         B, D, G, dh = self.batch, shape.d_model, shape.n_kv_heads, shape.head_dim
         z = dict(device=device)
+        # Paged cache: t_cap rounds up to whole pages; the pool holds every
+        # sequence's pages (plus spares) in a seeded random order.
+        self.page_size = page_size
+        if page_size:
+            pps = -(-self.t_cap // page_size)
+            self.t_cap = pps * page_size
+            n_pages = B * pps + spare_pages
+            perm = np.random.default_rng(page_seed).permutation(n_pages)[: B * pps]
+            self.page_table = torch.from_numpy(perm.astype(np.int32).reshape(B, pps)).to(device)
+            cache_shape = (n_pages, G, page_size, dh)
+        else:
+            self.page_table = None
+            cache_shape = (B, G, self.t_cap, dh)
         self.st = {
             "ema_state": torch.zeros(B, D, dtype=torch.float32, **z),
             "block_acc": torch.zeros(B, D, dtype=torch.float32, **z),
             "block_means": torch.zeros(B, self.nb_cap, D, dtype=torch.float32, **z),
             "block_hash": torch.zeros(B, self.nb_cap, dtype=torch.int64, **z),
             "block_kv": torch.zeros(B, self.nb_cap, 2 * G * dh, dtype=torch.float32, **z),
-            "k_cache": torch.zeros(B, G, self.t_cap, dh, dtype=self.tdtype, **z),
-            "v_cache": torch.zeros(B, G, self.t_cap, dh, dtype=self.tdtype, **z),
+            "k_cache": torch.zeros(cache_shape, dtype=self.tdtype, **z),
+            "v_cache": torch.zeros(cache_shape, dtype=self.tdtype, **z),
         }
         self.state = mka.State(nb_cap=self.nb_cap, t_cap=self.t_cap,
                                **{k: v.data_ptr() for k, v in self.st.items()})
+        if page_size:
+            self.state.page_table = self.page_table.data_ptr()
+            self.state.page_size = page_size
+            self.state.pages_per_seq = self.page_table.shape[1]
         self._ws = None
         # full MKA: one K/V cache per memory tier (tier 0 = L1, 1 = L2, 2 = L3)
         self.kv3 = None
@@ -136,3 +154,28 @@ class Layer:
         mka.mka_full_decode_step(d, x_t, pos, self.weights, self.state, self.tier_cache,
                                  self._out_struct(out), ws, ws.numel(), stream)
         return out
+
+    def logical_cache(self, which: str) -> torch.Tensor:
+        """The K or V cache as [B, G, t_cap, dh], gathered through the page
+        table when the cache is paged."""
+        c = self.st[f"{which}_cache"]
+        if self.page_table is None:
+            return c
+        B, pps = self.page_table.shape
+        pages = c[self.page_table.long().reshape(-1)]  # [B*pps, G, P, dh]
+        G, P, dh = pages.shape[1:]
+        return pages.reshape(B, pps, G, P, dh).permute(0, 2, 1, 3, 4).reshape(B, G, pps * P, dh)
+
+    def load_cache(self, which: str, rows: torch.Tensor) -> None:
+        """Write rows [B, G, n, dh] as cache rows 0 .. n-1 (through the page
+        table when the cache is paged)."""
+        c = self.st[f"{which}_cache"]
+        n = rows.shape[2]
+        if self.page_table is None:
+            c[:, :, :n].copy_(rows)
+            return
+        P = self.page_size
+        pt = self.page_table.long()
+        for p in range(-(-n // P)):
+            r0, r1 = p * P, min(n, (p + 1) * P)
+            c[pt[:, p], :, : r1 - r0] = rows[:, :, r0:r1].to(c.dtype)

@@ -73,7 +73,8 @@ class State(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("ema_state", "block_acc", "block_means", "block_hash", "block_kv", "k_cache",
                  "v_cache")] + [
-        ("nb_cap", ctypes.c_int32), ("t_cap", ctypes.c_int64)]
+        ("nb_cap", ctypes.c_int32), ("t_cap", ctypes.c_int64), ("page_table", ctypes.c_void_p),
+        ("page_size", ctypes.c_int32), ("pages_per_seq", ctypes.c_int32)]
 
 
 class TierCache(ctypes.Structure):

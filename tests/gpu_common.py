@@ -34,7 +34,7 @@ def gpu_prefill(s, inp, *, x=None, seq=None, t_cap=None, nb_cap=None, batch=None
 
 def state_np(layer):
     st = layer.st
-    return dict(k=to_np(st["k_cache"]), v=to_np(st["v_cache"]),
+    return dict(k=to_np(layer.logical_cache("k")), v=to_np(layer.logical_cache("v")),
                 means=to_np(st["block_means"]), bhash=to_np(st["block_hash"]).view(np.uint64),
                 block_kv=to_np(st["block_kv"]),
                 ema=to_np(st["ema_state"]), acc=to_np(st["block_acc"]))

@@ -190,3 +190,29 @@ def test_full_mka_arguments_rejected():
     assert mka.mka_workspace_bytes(d, mka.MKA_OP_FULL_PREFILL) > 0
     assert mka.mka_workspace_bytes(d1, mka.MKA_OP_FULL_DECODE_STEP, 100) > 0
     assert mka.mka_workspace_bytes(d, mka.MKA_OP_FULL_DECODE_STEP, 100) == 0  # seq != 1
+
+
+def test_paged_state_rejections():
+    d = _d(seq=128)
+    w = mka.Weights(*([FAKE] * 6))
+    out = mka.Outputs(*([FAKE] * 6))
+
+    def state(**kw):
+        st = mka.State(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, nb_cap=64, t_cap=8192)
+        st.page_table, st.page_size, st.pages_per_seq = FAKE, 256, 32
+        for k, v in kw.items():
+            setattr(st, k, v)
+        return st
+
+    for bad in (dict(page_size=100), dict(page_size=32), dict(pages_per_seq=0),
+                dict(pages_per_seq=31), dict(page_table=FAKE + 2)):
+        with pytest.raises(mka.MkaError) as e:
+            mka.mka_prefill(d, FAKE, 0, w, state(**bad), out, FAKE, 1 << 40, 0)
+        assert e.value.status == mka.MKA_ERR_INVALID, bad
+    tc = mka.TierCache()
+    for i in range(3):
+        tc.k_cache[i] = FAKE
+        tc.v_cache[i] = FAKE
+    with pytest.raises(mka.MkaError) as e:  # the full-MKA tier caches are contiguous
+        mka.mka_full_prefill(d, FAKE, 0, w, state(), tc, out, FAKE, 1 << 40, 0)
+    assert e.value.status == mka.MKA_ERR_UNSUPPORTED
