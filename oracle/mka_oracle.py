@@ -35,7 +35,10 @@ subsets, hand-made ties, torch's attention for L1 alone, and invariances
 not matter).  Full MKA (``full_prefill``, ``full_decode_step``) is pinned
 path by path to torch's attention over each tier's keys and values, to
 FastMKA and plain GQA where the tiers coincide, and by decode continuing
-prefill.
+prefill.  The backward (``backward``) is pinned to central differences of
+this module's own forward (every parameter tensor, three routing variants),
+its attention part to torch's autograd of its scaled-dot-product attention,
+the EMA and L3 steps by adjoint identities, GELU' to torch's autograd.
 """
 
 from __future__ import annotations
@@ -52,6 +55,7 @@ __all__ = [
     "l3_mean", "fuse", "kv_proj", "attention", "attention_online", "prefill",
     "DecodeState", "decode_init", "decode_init_from_prefill", "decode_step",
     "full_prefill", "FullDecodeState", "full_decode_init_from_prefill", "full_decode_step",
+    "gelu_grad", "attention_backward", "ema_adjoint", "l3_adjoint", "backward",
 ]
 
 _SQRT2 = math.sqrt(2.0)
@@ -649,3 +653,132 @@ def full_decode_step(st, x_t, w_q, w_k, w_v, w_r1, w_r2, proj, *, n_heads, n_kv_
         st.block_acc = np.zeros_like(st.block_acc)
     st.pos = t + 1
     return dict(q=q, lam=lam, l2=l2, key=key, key_abs=kabs, idx=idx[:, 0], l3=l3, a3=a3, o=o)
+
+
+# --------------------------------------------------------------------------
+# Backward of the FastMKA layer (training).  The abstract page's headline is
+# training throughput (Tables 1, 2, 6; FlashAttention-2 training in bf16); the
+# pages give no backward, so it is the derivative of the forward above taken
+# by the chain rule, step by step in reverse.  The SimHash codes and the top-R
+# choice are discrete: no gradient flows through them (the retrieved set is a
+# constant), nor through a hard router's choice of tiers; the hyperplanes and
+# the EMA decay are fixed.  Gradients flow to x and to W_q, W_k, W_v, W_r1,
+# W_r2, given dO, the gradient of a loss with respect to the layer output.
+# --------------------------------------------------------------------------
+
+def gelu_grad(z):
+    """d/dz of z * Phi(z): Phi(z) + z * phi(z)."""
+    z = _f64(z)
+    return 0.5 * (1.0 + _erf(z / _SQRT2)) + z * np.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
+
+
+def attention_backward(q, k, v, d_o, n_kv_heads):
+    """Gradients of causal GQA attention over every row with respect to q, k, v.
+
+    With S = q k^T / sqrt(dh) (j <= t), P = softmax(S) by rows and O = P v:
+    dV = P^T dO, dP = dO v^T, dS = P * (dP - rowsum(dP * P)), dq = dS k / sqrt(dh),
+    dk = dS^T q / sqrt(dh); a KV head's gradients sum over its query heads.
+    q, d_o: [B, N, H, dh]; k, v: [B, G, N, dh].  Returns dq, dk, dv (same shapes).
+    """
+    q, k, v, d_o = _f64(q), _f64(k), _f64(v), _f64(d_o)
+    B, N, H, dh = q.shape
+    scale = 1.0 / math.sqrt(dh)
+    future = np.arange(N)[None, :] > np.arange(N)[:, None]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            g = _group_of(h, H, n_kv_heads)
+            s = (q[b, :, h] @ k[b, g].T) * scale
+            s[future] = -np.inf
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            dv[b, g] += p.T @ d_o[b, :, h]
+            dp = d_o[b, :, h] @ v[b, g].T
+            ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
+            dq[b, :, h] = (ds @ k[b, g]) * scale
+            dk[b, g] += (ds.T @ q[b, :, h]) * scale
+    return dq, dk, dv
+
+
+def ema_adjoint(u, beta):
+    """The transpose of the EMA map x -> L2: dx_t = (1 - beta) sum_{s >= t} beta^(s-t) u_s,
+    a scan from the last token backwards.  u: [B, N, D]."""
+    u = _f64(u)
+    out = np.empty_like(u)
+    g = np.zeros(u.shape[0:1] + u.shape[2:])
+    for t in range(u.shape[1] - 1, -1, -1):
+        g = u[:, t] + beta * g
+        out[:, t] = (1.0 - beta) * g
+    return out
+
+
+def l3_adjoint(c, idx, n_blocks, n_tokens, block):
+    """The transpose of x -> L3 through the block means, with the retrieval fixed:
+    each token's c[t] / |S_t| goes to the means of its retrieved blocks, and a
+    block mean's gradient spreads evenly (1 / Bs) over the block's tokens.
+    c: [B, n, D]; idx: [B, n, R].  Returns the gradient on x [B, n_tokens, D]."""
+    c = _f64(c)
+    B, n, D = c.shape
+    dm = np.zeros((B, n_blocks, D))
+    for b in range(B):
+        for t in range(n):
+            sel = idx[b, t][idx[b, t] >= 0]
+            for blk in sel:
+                dm[b, blk] += c[b, t] / len(sel)
+    dx = np.zeros((B, n_tokens, D))
+    for blk in range(n_blocks):
+        dx[:, blk * block:(blk + 1) * block] += dm[:, blk][:, None, :] / block
+    return dx
+
+
+def backward(x, w_q, w_k, w_v, w_r1, w_r2, proj, d_o, *, n_heads, n_kv_heads, ema_decay,
+             block, top_r, route_mode="soft", tiers="l1l2l3", decide_q="f64"):
+    """Gradients of sum(O * d_o) for the FastMKA layer over a whole sequence.
+
+    Returns a dict with dx [B,N,D], dw_q, dw_k, dw_v, dw_r1, dw_r2 (the weight
+    shapes, [out, in]), and the intermediates dq [B,N,H*dh] (attention plus
+    router), dk, dv [B,G,N,dh], dxf [B,N,D], dlam [B,N,3], dz [B,N,3], and the
+    forward's dict as ``fwd``.
+    """
+    x = _f64(x)
+    B, N, D = x.shape
+    fwd = prefill(x, w_q, w_k, w_v, w_r1, w_r2, proj, n_heads=n_heads, n_kv_heads=n_kv_heads,
+                  ema_decay=ema_decay, block=block, top_r=top_r, route_mode=route_mode,
+                  tiers=tiers, decide_q=decide_q)
+    q, lam = fwd["q"], fwd["lam"]
+    dh = q.shape[-1] // n_heads
+    G = n_kv_heads
+    w_q, w_k, w_v, w_r1, w_r2 = (_f64(w) for w in (w_q, w_k, w_v, w_r1, w_r2))
+    # attention
+    dq_a, dk, dv = attention_backward(q.reshape(B, N, n_heads, dh), fwd["k"], fwd["v"],
+                                      _f64(d_o), n_kv_heads)
+    dk_t = dk.transpose(0, 2, 1, 3).reshape(B, N, G * dh)  # token-major
+    dv_t = dv.transpose(0, 2, 1, 3).reshape(B, N, G * dh)
+    # K = X_fused W_k^T, V = X_fused W_v^T
+    xf = fwd["x_fused"]
+    dxf = dk_t @ w_k + dv_t @ w_v
+    dw_k = np.einsum("bnk,bnd->kd", dk_t, xf)
+    dw_v = np.einsum("bnk,bnd->kd", dv_t, xf)
+    # X_fused = lam1 x + lam2 L2 + lam3 L3
+    tiers_v = (x, fwd["l2"], fwd["l3"])
+    dlam = np.stack([(dxf * t).sum(axis=-1) for t in tiers_v], axis=-1)
+    dx = lam[..., 0:1] * dxf
+    dx += ema_adjoint(lam[..., 1:2] * dxf, ema_decay)
+    dx += l3_adjoint(lam[..., 2:3] * dxf, fwd["idx"], fwd["block_means"].shape[1], N, block)
+    # router: lambda = softmax over the kept tiers of z = GELU(q W_r1^T) W_r2^T
+    pre = q @ w_r1.T
+    hid = gelu(pre)
+    if route_mode == "fixed" or tiers == "l1":
+        dz = np.zeros_like(lam)  # lambda does not depend on the router
+    else:
+        kept = lam > 0.0
+        dz = np.where(kept, lam * (dlam - (lam * dlam).sum(axis=-1, keepdims=True)), 0.0)
+    dw_r2 = np.einsum("bnc,bnr->cr", dz, hid)
+    dpre = (dz @ w_r2) * gelu_grad(pre)
+    dw_r1 = np.einsum("bnr,bnq->rq", dpre, q)
+    dq = dq_a.reshape(B, N, n_heads * dh) + dpre @ w_r1
+    # Q = x W_q^T
+    dw_q = np.einsum("bnq,bnd->qd", dq, x)
+    dx += dq @ w_q
+    return dict(dx=dx, dw_q=dw_q, dw_k=dw_k, dw_v=dw_v, dw_r1=dw_r1, dw_r2=dw_r2, dq=dq, dk=dk,
+                dv=dv, dxf=dxf, dlam=dlam, dz=dz, fwd=fwd)

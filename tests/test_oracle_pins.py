@@ -666,3 +666,91 @@ def test_full_mka_decode_continues_prefill(mode, tiers):
         else:
             np.testing.assert_allclose(st.k3[ell], full["k3"][ell], rtol=1e-10, atol=1e-13)
             np.testing.assert_allclose(st.v3[ell], full["v3"][ell], rtol=1e-10, atol=1e-13)
+
+
+# ------------------------------------------------------------------ backward
+
+def test_gelu_grad_is_torch_autograd():
+    z = torch.linspace(-6, 6, 241, dtype=torch.float64, requires_grad=True)
+    torch.nn.functional.gelu(z).sum().backward()
+    np.testing.assert_allclose(O.gelu_grad(z.detach().numpy()), z.grad.numpy(), rtol=1e-13,
+                               atol=1e-15)
+
+
+def test_attention_backward_is_torch_autograd_of_sdpa():
+    r = rng(40)
+    B, N, H, G, dh = 2, 37, 4, 2, 8
+    q, k, v = r.standard_normal((B, N, H, dh)), r.standard_normal((B, G, N, dh)), \
+        r.standard_normal((B, G, N, dh))
+    d_o = r.standard_normal((B, N, H, dh))
+    dq, dk, dv = O.attention_backward(q, k, v, d_o, G)
+    tq = torch.tensor(q, requires_grad=True)
+    tk = torch.tensor(k, requires_grad=True)
+    tv = torch.tensor(v, requires_grad=True)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq.transpose(1, 2), tk.repeat_interleave(H // G, 1), tv.repeat_interleave(H // G, 1),
+        is_causal=True).transpose(1, 2)
+    (o * torch.tensor(d_o)).sum().backward()
+    for got, want in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(got, want.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_ema_and_l3_adjoints():
+    # <A a, b> = <a, A^T b> for the EMA map and for x -> L3 through the block means
+    r = rng(41)
+    a, c = r.standard_normal((2, 50, 6)), r.standard_normal((2, 50, 6))
+    l2, _ = O.ema(a, 0.9)
+    assert math.isclose((l2 * c).sum(), (a * O.ema_adjoint(c, 0.9)).sum(), rel_tol=1e-12)
+    block, R = 8, 3
+    means = O.block_means(a, block)
+    codes, _ = O.simhash(means, r.standard_normal((16, 6)))
+    keys, _ = O.simhash(l2, r.standard_normal((16, 6)))
+    idx = O.retrieve(keys, codes, np.arange(50), block, R)
+    l3 = O.l3_mean(means, idx)
+    lhs = (l3 * c).sum()
+    rhs = (a * O.l3_adjoint(c, idx, means.shape[1], 50, block)).sum()
+    assert np.any(idx >= 0) and math.isclose(lhs, rhs, rel_tol=1e-12)
+
+
+def _fd_layer(mode, tiers):
+    s = I.workload("tiny_f32").replace(seq=160)
+    d = I.prefill_inputs(s)
+    args = dict(n_heads=s.n_heads, n_kv_heads=s.n_kv_heads, ema_decay=s.ema_decay,
+                block=s.block, top_r=s.top_r, route_mode=mode, tiers=tiers)
+    params = {k: np.asarray(d[k], np.float64) for k in ("x", "w_q", "w_k", "w_v", "w_r1", "w_r2")}
+    d_o = rng(42).standard_normal((1, s.seq, s.n_heads, s.head_dim))
+    return s, d, args, params, d_o
+
+
+@pytest.mark.parametrize("mode,tiers", [("soft", "l1l2l3"), ("top2", "l1l3"), ("fixed", "l1l2")])
+def test_backward_matches_central_differences(mode, tiers):
+    s, d, args, params, d_o = _fd_layer(mode, tiers)
+    names = ("x", "w_q", "w_k", "w_v", "w_r1", "w_r2")
+
+    def run(p):
+        return O.prefill(p["x"], p["w_q"], p["w_k"], p["w_v"], p["w_r1"], p["w_r2"], d["proj"],
+                         **args)
+
+    grads = O.backward(params["x"], params["w_q"], params["w_k"], params["w_v"], params["w_r1"],
+                       params["w_r2"], d["proj"], d_o, **args)
+    base = run(params)
+    r = rng(43)
+    eps = 1e-5
+    checked = 0
+    for name in names:
+        g = grads["d" + name if name == "x" else "d" + name.replace("w_", "w_")]
+        for _ in range(5):
+            i = tuple(int(r.integers(n)) for n in params[name].shape)
+            vals = []
+            for sign in (1, -1):
+                p = {k: v.copy() for k, v in params.items()}
+                p[name][i] += sign * eps
+                out = run(p)
+                # the discrete choices must not move under the perturbation
+                assert np.array_equal(out["idx"], base["idx"])
+                assert np.array_equal(out["lam"] > 0, base["lam"] > 0)
+                vals.append((out["o"] * d_o).sum())
+            fd = (vals[0] - vals[1]) / (2 * eps)
+            np.testing.assert_allclose(g[i], fd, rtol=2e-6, atol=2e-9, err_msg=f"{name}{i}")
+            checked += 1
+    assert checked == 30
