@@ -58,7 +58,7 @@ enum {
 /* Workspace-using operations, for mka_workspace_bytes(). */
 enum { MKA_OP_EMA_SCAN = 0, MKA_OP_FUSE_KV = 1, MKA_OP_ATTN_DECODE = 2, MKA_OP_PREFILL = 3,
        MKA_OP_DECODE_STEP = 4, MKA_OP_RETRIEVE = 5, MKA_OP_INDEX = 6, MKA_OP_ROUTE = 7,
-       MKA_OP_FULL_PREFILL = 8, MKA_OP_FULL_DECODE_STEP = 9 };
+       MKA_OP_FULL_PREFILL = 8, MKA_OP_FULL_DECODE_STEP = 9, MKA_OP_BACKWARD = 10 };
 
 /* Routing variant (mka_dims.route_mode) and enabled tiers (mka_dims.tiers):
  * the ablations of the abstract page, Table 10 (fixed lambda = 1/3, hard
@@ -280,6 +280,9 @@ typedef struct mka_outputs {
   uint64_t* key;    /* [B, seq] */
   int32_t* idx;     /* [B, seq, R] */
   void* o;          /* [B, seq, H, dh] */
+  float* lse;       /* [B, seq, H] or NULL: natural log of the sum over keys of
+                       exp(q . k / sqrt(dh)) per query row and head, written by
+                       mka_prefill when not NULL (mka_backward reads it) */
 } mka_outputs;
 
 int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weights* w,
@@ -301,6 +304,46 @@ int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weight
 int mka_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_weights* w,
                     const mka_state* st, const mka_outputs* out, void* ws, size_t ws_bytes,
                     void* stream);
+
+/* Backward of the layer (training): the gradients of a loss L with respect to x
+ * and the weights, given dO = dL/dO, for a whole sequence that mka_prefill
+ * processed from pos0 = 0 (its outputs, lse included, and state are the saved
+ * forward).  The pages give no backward; this is the derivative of the forward
+ * by the chain rule.  The SimHash codes, the top-R choice and a hard router's
+ * choice of tiers are discrete: no gradient flows through them (the retrieved
+ * blocks and kept tiers are constants); proj and ema_decay are fixed.
+ *   attention: dV = P^T dO, dP = dO V^T, dS = P (dP - rowsum(dO O)),
+ *              dq = dS K / sqrt(dh), dK = dS^T q / sqrt(dh) (summed per KV head);
+ *   [K|V] = X_fused [W_k|W_v]^T: dX_fused, dW_k, dW_v;
+ *   X_fused = sum lambda_l L_l: dlambda_l = <dX_fused, L_l>; dx gets lambda_1 dX_fused,
+ *              the EMA's adjoint of lambda_2 dX_fused (a reverse scan), and
+ *              lambda_3 dX_fused / |S_t| scattered to the retrieved blocks'
+ *              means, each spread evenly over its block's tokens;
+ *   router: the softmax over the kept tiers, GELU', dW_r2, dW_r1, dq;
+ *   Q = x W_q^T: dW_q, dx.
+ * Arithmetic: float32 accumulation; bf16 layers feed the products bf16
+ * operands (the gradients rounded to bf16 where they enter an MFMA product).
+ *   x [B, seq, D] dtype; d_o [B, seq, H, dh] dtype
+ *   fwd: q, lambda, o, lse, and l2 (unless tiers == MKA_TIERS_L1) and idx
+ *        (with L3) as mka_prefill wrote them; st: k_cache, v_cache (contiguous),
+ *        block_means (with L3), t_cap, nb_cap
+ *   g: float32 gradients, written (not accumulated): dx [B, seq, D], dw_q
+ *      [H*dh, D], dw_k and dw_v [G*dh, D], dw_r1 [r, H*dh], dw_r2 [3, r]
+ *   ws >= mka_workspace_bytes(d, MKA_OP_BACKWARD, 0) bytes
+ * bf16 layers need router_hidden % 32 == 0 (MKA_ERR_UNSUPPORTED otherwise); a
+ * paged state is MKA_ERR_UNSUPPORTED. */
+typedef struct mka_grads {
+  float* dx;
+  float* dw_q;
+  float* dw_k;
+  float* dw_v;
+  float* dw_r1;
+  float* dw_r2;
+} mka_grads;
+
+int mka_backward(const mka_dims* d, const void* x, const mka_weights* w, const mka_state* st,
+                 const mka_outputs* fwd, const void* d_o, const mka_grads* g, void* ws,
+                 size_t ws_bytes, void* stream);
 
 /* Full MKA, the three-path form that FastMKA replaces: each memory tier is
  * attended separately and the outputs are mixed, O_h = sum_l lambda_l a_l with

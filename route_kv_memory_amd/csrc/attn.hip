@@ -34,7 +34,7 @@ template <int DH, int NW, bool PAGED>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
     bf16_t* __restrict__ O, int B, int seq, int H, int G, KvLayout kv, int64_t pos0, float sl2,
-    int n_qblk, int n_units) {
+    int n_qblk, int n_units, float* __restrict__ lse) {
   constexpr int NT = NW * 64, BM = 32 * NW, BN = 64, KP = DH + 8, VP = BN + 8, NKS = DH / 16,
                 NDB = DH / 32;
   constexpr int KCH = BN * DH / 8 / NT;
@@ -186,6 +186,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
   if (q_row < seq) {
     const float inv = 1.0f / l_i;
     bf16_t* op = O + (static_cast<int64_t>(b * seq + q_row) * H + h) * DH;
+    // natural log-sum-exp of the row's scaled scores, for the backward
+    if (lse != nullptr && hl == 0)
+      lse[static_cast<int64_t>(b * seq + q_row) * H + h] = (ms + log2f(l_i)) * 0.69314718055994531f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -204,7 +207,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
 template <int DH, bool PAGED>
 __global__ __launch_bounds__(64) void attn_prefill_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ Kc, const float* __restrict__ Vc,
-    float* __restrict__ O, int seq, int H, int G, KvLayout kv, int64_t pos0, float scale) {
+    float* __restrict__ O, int seq, int H, int G, KvLayout kv, int64_t pos0, float scale,
+    float* __restrict__ lse) {
   constexpr int TK = 32;
   __shared__ float Ks[TK][DH];
   __shared__ float Vs[TK][DH];
@@ -255,6 +259,7 @@ __global__ __launch_bounds__(64) void attn_prefill_f32_kernel(
   if (t < seq) {
     float* op = O + (static_cast<int64_t>(b * seq + t) * H + h) * DH;
     const float inv = 1.0f / l;
+    if (lse != nullptr) lse[static_cast<int64_t>(b * seq + t) * H + h] = m + logf(l);
 #pragma unroll
     for (int d = 0; d < DH; ++d) op[d] = acc[d] * inv;
   }
@@ -268,7 +273,7 @@ constexpr int kAttnWaves = 4;
 template <>
 hipError_t attn_prefill<bf16_t>(const bf16_t* q, const bf16_t* k, const bf16_t* v, bf16_t* o, int B,
                                 int seq, int H, int G, int dh, const KvLayout& kv, int64_t pos0,
-                                hipStream_t s) {
+                                float* lse, hipStream_t s) {
   constexpr int NW = kAttnWaves;
   const int n_qblk = (seq + 32 * NW - 1) / (32 * NW);
   const int n_units = n_qblk * B * G;
@@ -276,7 +281,7 @@ hipError_t attn_prefill<bf16_t>(const bf16_t* q, const bf16_t* k, const bf16_t* 
   const float sl2 = 1.4426950408889634f / sqrtf(static_cast<float>(dh));
   auto launch = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(NW * 64), 0, s, q, k, v, o, B, seq, H, G, kv, pos0,
-                       sl2, n_qblk, n_units);
+                       sl2, n_qblk, n_units, lse);
   };
   if (dh == 128)
     kv.paged() ? launch(attn_prefill_bf16_kernel<128, NW, true>)
@@ -290,11 +295,11 @@ hipError_t attn_prefill<bf16_t>(const bf16_t* q, const bf16_t* k, const bf16_t* 
 template <>
 hipError_t attn_prefill<float>(const float* q, const float* k, const float* v, float* o, int B,
                                int seq, int H, int G, int dh, const KvLayout& kv, int64_t pos0,
-                               hipStream_t s) {
+                               float* lse, hipStream_t s) {
   const dim3 grid((seq + 63) / 64, H, B);
   const float scale = 1.0f / sqrtf(static_cast<float>(dh));
   auto launch = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, grid, dim3(64), 0, s, q, k, v, o, seq, H, G, kv, pos0, scale);
+    hipLaunchKernelGGL(kernel, grid, dim3(64), 0, s, q, k, v, o, seq, H, G, kv, pos0, scale, lse);
   };
   if (dh == 128)
     kv.paged() ? launch(attn_prefill_f32_kernel<128, true>)

@@ -1,0 +1,486 @@
+// Backward of the FastMKA layer: the derivative of the forward taken step by
+// step in reverse (the pages give none; the abstract page's headline is
+// training throughput, Tables 1, 2 and 6).  No gradient flows through the
+// SimHash codes, the top-R choice or a hard router's choice of tiers.
+//
+// Attention (reading note, method sections 3-4; the forward keeps each query
+// row's log-sum-exp): with P = softmax(S), S = q k^T / sqrt(dh),
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D = rowsum(dO * O),
+//   dq = dS k / sqrt(dh),  dk = dS^T q / sqrt(dh),
+// the KV heads' gradients summed over their query heads.  The rest: the
+// transposed products of the projections, the fusion's tier products, the
+// EMA's adjoint (a reverse scan), the block means' adjoint (a scatter to the
+// retrieved blocks, spread over each block's tokens) and the router's chain.
+#include "kernels.h"
+
+namespace mka {
+
+// ---------------------------------------------------------------------------
+// D[m, h] = sum_d dO[m, h, d] * O[m, h, d]: one wave per (row, head).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const T* __restrict__ O,
+                                                            const T* __restrict__ dO, int64_t rows,
+                                                            int DH, float* __restrict__ dsum) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const T* o = O + r * DH;
+  const T* g = dO + r * DH;
+  float acc = 0.f;
+  for (int d = lane; d < DH; d += 64) acc = fmaf(Elem<T>::to_f32(o[d]), Elem<T>::to_f32(g[d]), acc);
+  acc = wave_sum(acc);
+  if (lane == 0) dsum[r] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// Row-parallel attention backward (any storage type, fp32 arithmetic): one
+// thread per query row (dq) or per key row (dk, dv), the other side's rows
+// staged through LDS in tiles of 32.  lse and dsum are [B, N, H] (token-major),
+// dq [B, N, H, DH] and dkv [B, N, 2, G, DH] (K part, then V part) in float32.
+// ---------------------------------------------------------------------------
+template <typename T, int DH>
+__global__ __launch_bounds__(64) void attn_bwd_dq_rows_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ dsum, int N,
+    int H, int G, int64_t t_cap, float scale, float* __restrict__ dq) {
+  constexpr int TK = 32;
+  __shared__ float Ks[TK][DH];
+  __shared__ float Vs[TK][DH];
+  const int tid = threadIdx.x, h = blockIdx.y, b = blockIdx.z, g = h / (H / G);
+  const int t = blockIdx.x * 64 + tid;
+  const int tc = min(t, N - 1);
+  const int64_t row = (static_cast<int64_t>(b) * N + tc) * H + h;
+  float q[DH], go[DH], acc[DH];
+#pragma unroll
+  for (int d = 0; d < DH; ++d) {
+    q[d] = Elem<T>::to_f32(Q[row * DH + d]);
+    go[d] = Elem<T>::to_f32(dO[row * DH + d]);
+    acc[d] = 0.f;
+  }
+  const float l = lse[row], dd = dsum[row];
+  const T* kb = K + (static_cast<int64_t>(b) * G + g) * t_cap * DH;
+  const T* vb = V + (static_cast<int64_t>(b) * G + g) * t_cap * DH;
+  const int kv_end = min(static_cast<int>(blockIdx.x) * 64 + 64, N);
+  for (int j0 = 0; j0 < kv_end; j0 += TK) {
+    for (int e = tid; e < TK * DH; e += 64) {
+      const int r = e / DH, d = e % DH;
+      const bool ok = j0 + r < kv_end;
+      Ks[r][d] = ok ? Elem<T>::to_f32(kb[static_cast<int64_t>(j0 + r) * DH + d]) : 0.f;
+      Vs[r][d] = ok ? Elem<T>::to_f32(vb[static_cast<int64_t>(j0 + r) * DH + d]) : 0.f;
+    }
+    __syncthreads();
+    for (int jj = 0; jj < TK; ++jj) {
+      if (j0 + jj > t || j0 + jj >= kv_end) break;
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int d = 0; d < DH; ++d) {
+        s = fmaf(q[d], Ks[jj][d], s);
+        dp = fmaf(go[d], Vs[jj][d], dp);
+      }
+      const float p = expf(s * scale - l);
+      const float ds = p * (dp - dd);
+#pragma unroll
+      for (int d = 0; d < DH; ++d) acc[d] = fmaf(ds, Ks[jj][d], acc[d]);
+    }
+    __syncthreads();
+  }
+  if (t < N) {
+#pragma unroll
+    for (int d = 0; d < DH; ++d) dq[row * DH + d] = acc[d] * scale;
+  }
+}
+
+// WANT_K: dk (needs k and v rows); otherwise dv (needs k only).
+template <typename T, int DH, bool WANT_K>
+__global__ __launch_bounds__(64) void attn_bwd_dkv_rows_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ dsum, int N,
+    int H, int G, int64_t t_cap, float scale, float* __restrict__ dkv) {
+  constexpr int TQ = 32;
+  __shared__ float Qs[TQ][DH];
+  __shared__ float Gs[TQ][DH];
+  __shared__ float Ls[TQ], Ds[TQ];
+  const int tid = threadIdx.x, g = blockIdx.y, b = blockIdx.z, hpg = H / G;
+  const int j = blockIdx.x * 64 + tid;
+  const int jc = min(j, N - 1);
+  const int64_t kvrow = ((static_cast<int64_t>(b) * G + g) * t_cap + jc) * DH;
+  float k[DH], v[DH], acc[DH];
+#pragma unroll
+  for (int d = 0; d < DH; ++d) {
+    k[d] = Elem<T>::to_f32(K[kvrow + d]);
+    v[d] = WANT_K ? Elem<T>::to_f32(V[kvrow + d]) : 0.f;
+    acc[d] = 0.f;
+  }
+  const int t_begin = blockIdx.x * 64;  // queries before the block see none of its keys
+  for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
+    for (int t0 = t_begin; t0 < N; t0 += TQ) {
+      for (int e = tid; e < TQ * DH; e += 64) {
+        const int r = e / DH, d = e % DH;
+        const int t = min(t0 + r, N - 1);
+        const int64_t row = (static_cast<int64_t>(b) * N + t) * H + h;
+        Qs[r][d] = Elem<T>::to_f32(Q[row * DH + d]);
+        Gs[r][d] = Elem<T>::to_f32(dO[row * DH + d]);
+      }
+      if (tid < TQ) {
+        const int t = min(t0 + tid, N - 1);
+        const int64_t row = (static_cast<int64_t>(b) * N + t) * H + h;
+        Ls[tid] = lse[row];
+        Ds[tid] = dsum[row];
+      }
+      __syncthreads();
+      for (int tt = 0; tt < TQ; ++tt) {
+        const int t = t0 + tt;
+        if (t >= N) break;
+        if (t < j) continue;
+        float s = 0.f;
+#pragma unroll
+        for (int d = 0; d < DH; ++d) s = fmaf(Qs[tt][d], k[d], s);
+        const float p = expf(s * scale - Ls[tt]);
+        if (WANT_K) {
+          float dp = 0.f;
+#pragma unroll
+          for (int d = 0; d < DH; ++d) dp = fmaf(Gs[tt][d], v[d], dp);
+          const float ds = p * (dp - Ds[tt]);
+#pragma unroll
+          for (int d = 0; d < DH; ++d) acc[d] = fmaf(ds, Qs[tt][d], acc[d]);
+        } else {
+#pragma unroll
+          for (int d = 0; d < DH; ++d) acc[d] = fmaf(p, Gs[tt][d], acc[d]);
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (j < N) {
+    float* out = dkv + ((static_cast<int64_t>(b) * N + j) * 2 + (WANT_K ? 0 : 1)) * G * DH +
+                 static_cast<int64_t>(g) * DH;
+#pragma unroll
+    for (int d = 0; d < DH; ++d) out[d] = WANT_K ? acc[d] * scale : acc[d];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Layout helpers for the transposed products.
+// dst[c][r] = src[r][c] for r < R, zero for R <= r < Rp; src rows have stride
+// lds_ elements, dst rows ldd.  32 x 32 tiles through LDS.
+// ---------------------------------------------------------------------------
+template <typename TS, typename TD>
+__global__ __launch_bounds__(256) void transpose_kernel(const TS* __restrict__ src, int64_t lds_,
+                                                        int R, int C, int Rp, int64_t ldd,
+                                                        TD* __restrict__ dst) {
+  __shared__ float tile[32][33];
+  const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  for (int i = ty; i < 32; i += 8) {
+    const int r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < R && c < C) ? Elem<TS>::to_f32(src[static_cast<int64_t>(r) * lds_ + c]) : 0.f;
+  }
+  __syncthreads();
+  for (int i = ty; i < 32; i += 8) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < C && r < Rp) dst[static_cast<int64_t>(c) * ldd + r] = Elem<TD>::from_f32(tile[tx][i]);
+  }
+}
+
+template <typename TS, typename TD>
+__global__ __launch_bounds__(256) void convert_kernel(const TS* __restrict__ src, int64_t n,
+                                                      TD* __restrict__ dst) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) dst[i] = Elem<TD>::from_f32(Elem<TS>::to_f32(src[i]));
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// Fusion backward, one row per workgroup.  X_fused = l1 x + l2 L2 + l3 L3:
+//   dlam_i = <dxf, L_i>;  dx = l1 dxf (written);  dxf <- l2 dxf (in place,
+//   the EMA adjoint's input);  dm[blk] += l3 dxf / |S_t| for the retrieved
+//   blocks (atomics; dm is zeroed first).  L3 is re-formed from the means.
+// ---------------------------------------------------------------------------
+template <typename T, int RMAX>
+__global__ __launch_bounds__(256) void fuse_bwd_kernel(
+    const T* __restrict__ x, const float* __restrict__ l2, const float* __restrict__ means,
+    int nb_cap, const int32_t* __restrict__ idx, const float* __restrict__ lam, int N, int D,
+    int R, float* __restrict__ dxf, float* __restrict__ dx, float* __restrict__ dm, int nbs,
+    float* __restrict__ dlam) {
+  __shared__ float red[3][4];
+  const int64_t row = blockIdx.x;
+  const int b = static_cast<int>(row / N);
+  const int tid = threadIdx.x;
+  const float w1 = lam[row * 3 + 0], w2 = lam[row * 3 + 1], w3 = lam[row * 3 + 2];
+  int blk[RMAX], cnt = 0;
+#pragma unroll
+  for (int i = 0; i < RMAX; ++i) {
+    blk[i] = i < R ? idx[row * R + i] : -1;
+    cnt += blk[i] >= 0;
+  }
+  const float inv = cnt ? 1.0f / static_cast<float>(cnt) : 0.f;
+  const float* mb = means + static_cast<int64_t>(b) * nb_cap * D;
+  float* dmb = dm + static_cast<int64_t>(b) * nbs * D;
+  float a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  for (int c = tid; c < D; c += 256) {
+    const int64_t o = row * D + c;
+    const float gx = dxf[o];
+    float l3 = 0.f;
+#pragma unroll
+    for (int i = 0; i < RMAX; ++i)
+      if (blk[i] >= 0) l3 += mb[static_cast<int64_t>(blk[i]) * D + c];
+    l3 *= inv;
+    a1 = fmaf(gx, Elem<T>::to_f32(x[o]), a1);
+    if (l2) a2 = fmaf(gx, l2[o], a2);  // null: L2 disabled (lambda_2 = 0)
+    a3 = fmaf(gx, l3, a3);
+    dx[o] = w1 * gx;
+    dxf[o] = w2 * gx;
+    const float g3 = w3 * gx * inv;
+#pragma unroll
+    for (int i = 0; i < RMAX; ++i)
+      if (blk[i] >= 0) atomicAdd(dmb + static_cast<int64_t>(blk[i]) * D + c, g3);
+  }
+  a1 = wave_sum(a1);
+  a2 = wave_sum(a2);
+  a3 = wave_sum(a3);
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = a1;
+    red[1][tid >> 6] = a2;
+    red[2][tid >> 6] = a3;
+  }
+  __syncthreads();
+  if (tid < 3) dlam[row * 3 + tid] = ((red[tid][0] + red[tid][1]) + red[tid][2]) + red[tid][3];
+}
+
+// ---------------------------------------------------------------------------
+// EMA adjoint: g_t = u_t + beta g_{t+1} (from the last token back), dx_t +=
+// (1 - beta) g_t; then the block means' spread dx_t += dm[t / Bs] / Bs for
+// tokens of complete blocks.  Chunks of kBwdChunk tokens: pass 1 sums each
+// chunk's contribution to g at its first token, pass 2 carries between chunks
+// (from the last), pass 3 rescans each chunk with its incoming carry.
+// ---------------------------------------------------------------------------
+constexpr int kBwdChunk = 64;
+
+__global__ __launch_bounds__(256) void ema_adj_pass1(const float* __restrict__ u, int N, int D,
+                                                     int n_chunks, float beta,
+                                                     float* __restrict__ part) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int ch = blockIdx.y, b = blockIdx.z;
+  if (c >= D) return;
+  const int t0 = ch * kBwdChunk, t1 = min(N, t0 + kBwdChunk);
+  float g = 0.f;
+  for (int t = t1 - 1; t >= t0; --t) g = fmaf(beta, g, u[(static_cast<int64_t>(b) * N + t) * D + c]);
+  part[(static_cast<int64_t>(b) * n_chunks + ch) * D + c] = g;
+}
+
+__global__ __launch_bounds__(256) void ema_adj_pass2(float* __restrict__ part, int N, int D,
+                                                     int n_chunks, float beta) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int b = blockIdx.y;
+  if (c >= D) return;
+  // carry into chunk ch = g at the first token of chunk ch + 1
+  float carry = 0.f;
+  for (int ch = n_chunks - 1; ch >= 0; --ch) {
+    const int len = min(N, (ch + 1) * kBwdChunk) - ch * kBwdChunk;
+    float* p = part + (static_cast<int64_t>(b) * n_chunks + ch) * D + c;
+    const float local = *p;
+    *p = carry;  // now: g at the first token after the chunk
+    carry = local + powf(beta, static_cast<float>(len)) * carry;
+  }
+}
+
+__global__ __launch_bounds__(256) void ema_adj_pass3(const float* __restrict__ u,
+                                                     const float* __restrict__ part,
+                                                     const float* __restrict__ dm, int nbs,
+                                                     int N, int D, int n_chunks, int block,
+                                                     float beta, float* __restrict__ dx) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int ch = blockIdx.y, b = blockIdx.z;
+  if (c >= D) return;
+  const int t0 = ch * kBwdChunk, t1 = min(N, t0 + kBwdChunk);
+  const int n_full = (N / block) * block;  // tokens of complete blocks
+  const float omb = 1.0f - beta, inv_bs = 1.0f / static_cast<float>(block);
+  float g = part[(static_cast<int64_t>(b) * n_chunks + ch) * D + c];
+  for (int t = t1 - 1; t >= t0; --t) {
+    const int64_t o = (static_cast<int64_t>(b) * N + t) * D + c;
+    g = fmaf(beta, g, u[o]);
+    float add = omb * g;
+    if (t < n_full) add += dm[(static_cast<int64_t>(b) * nbs + t / block) * D + c] * inv_bs;
+    dx[o] += add;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Router backward, one wave per token: dz from dlam through the (kept-tier)
+// softmax, dpre = (dz W_r2) * GELU'(pre) in float32 and in the storage type.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict__ lam,
+                                                         const float* __restrict__ dlam,
+                                                         const float* __restrict__ pre,
+                                                         const T* __restrict__ W2, int r,
+                                                         int64_t M, Routing rt,
+                                                         float* __restrict__ dz_out,
+                                                         T* __restrict__ dpre) {
+  const int lane = threadIdx.x & 63;
+  const int64_t m = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;
+  float dz[3] = {0.f, 0.f, 0.f};
+  if (rt.learned()) {
+    const float l0 = lam[m * 3], l1 = lam[m * 3 + 1], l2 = lam[m * 3 + 2];
+    const float g0 = dlam[m * 3], g1 = dlam[m * 3 + 1], g2 = dlam[m * 3 + 2];
+    const float dot = l0 * g0 + l1 * g1 + l2 * g2;  // tiers outside the kept set have lambda 0
+    dz[0] = l0 > 0.f ? l0 * (g0 - dot) : 0.f;
+    dz[1] = l1 > 0.f ? l1 * (g1 - dot) : 0.f;
+    dz[2] = l2 > 0.f ? l2 * (g2 - dot) : 0.f;
+  }
+  if (lane < 3) dz_out[m * 3 + lane] = dz[lane];
+  for (int n = lane; n < r; n += 64) {
+    const float dh = dz[0] * Elem<T>::to_f32(W2[n]) + dz[1] * Elem<T>::to_f32(W2[r + n]) +
+                     dz[2] * Elem<T>::to_f32(W2[2 * r + n]);
+    const float z = pre[m * r + n];
+    const float gp = 0.5f * (1.0f + erff(z * 0.70710678118654752f)) +
+                     z * 0.39894228040143268f * expf(-0.5f * z * z);
+    dpre[m * r + n] = Elem<T>::from_f32(dh * gp);
+  }
+}
+
+// dW_r2[c][n] = sum_m dz[m][c] * GELU(pre[m][n]): one workgroup per output.
+__global__ __launch_bounds__(256) void router_dw2_kernel(const float* __restrict__ dz,
+                                                         const float* __restrict__ pre, int r,
+                                                         int64_t M, float* __restrict__ dw2) {
+  __shared__ float red[4];
+  const int c = blockIdx.x / r, n = blockIdx.x % r;
+  float acc = 0.f;
+  for (int64_t m = threadIdx.x; m < M; m += 256) acc = fmaf(dz[m * 3 + c], gelu(pre[m * r + n]), acc);
+  acc = wave_sum(acc);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) dw2[blockIdx.x] = ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+template <typename T>
+hipError_t attn_bwd_prep(const T* o, const T* d_o, int64_t rows, int dh, float* dsum,
+                         hipStream_t s) {
+  hipLaunchKernelGGL(attn_bwd_prep_kernel<T>, dim3(static_cast<unsigned>((rows + 3) / 4)),
+                     dim3(256), 0, s, o, d_o, rows, dh, dsum);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t attn_bwd_rows(const T* q, const T* k, const T* v, const T* d_o, const float* lse,
+                         const float* dsum, int B, int N, int H, int G, int dh, int64_t t_cap,
+                         float* dq, float* dkv, hipStream_t s) {
+  const float scale = 1.0f / sqrtf(static_cast<float>(dh));
+  const dim3 gq((N + 63) / 64, H, B), gk((N + 63) / 64, G, B);
+  if (dh == 128) {
+    hipLaunchKernelGGL((attn_bwd_dq_rows_kernel<T, 128>), gq, dim3(64), 0, s, q, k, v, d_o, lse,
+                       dsum, N, H, G, t_cap, scale, dq);
+    hipLaunchKernelGGL((attn_bwd_dkv_rows_kernel<T, 128, true>), gk, dim3(64), 0, s, q, k, v, d_o,
+                       lse, dsum, N, H, G, t_cap, scale, dkv);
+    hipLaunchKernelGGL((attn_bwd_dkv_rows_kernel<T, 128, false>), gk, dim3(64), 0, s, q, k, v, d_o,
+                       lse, dsum, N, H, G, t_cap, scale, dkv);
+  } else {
+    hipLaunchKernelGGL((attn_bwd_dq_rows_kernel<T, 64>), gq, dim3(64), 0, s, q, k, v, d_o, lse,
+                       dsum, N, H, G, t_cap, scale, dq);
+    hipLaunchKernelGGL((attn_bwd_dkv_rows_kernel<T, 64, true>), gk, dim3(64), 0, s, q, k, v, d_o,
+                       lse, dsum, N, H, G, t_cap, scale, dkv);
+    hipLaunchKernelGGL((attn_bwd_dkv_rows_kernel<T, 64, false>), gk, dim3(64), 0, s, q, k, v, d_o,
+                       lse, dsum, N, H, G, t_cap, scale, dkv);
+  }
+  return hipGetLastError();
+}
+
+template <typename TS, typename TD>
+hipError_t transpose(const TS* src, int64_t lds_, int R, int C, int Rp, int64_t ldd, TD* dst,
+                     hipStream_t s) {
+  const dim3 grid((C + 31) / 32, (Rp + 31) / 32);
+  hipLaunchKernelGGL((transpose_kernel<TS, TD>), grid, dim3(256), 0, s, src, lds_, R, C, Rp, ldd,
+                     dst);
+  return hipGetLastError();
+}
+
+template <typename TS, typename TD>
+hipError_t convert(const TS* src, int64_t n, TD* dst, hipStream_t s) {
+  hipLaunchKernelGGL((convert_kernel<TS, TD>), dim3(static_cast<unsigned>((n + 255) / 256)),
+                     dim3(256), 0, s, src, n, dst);
+  return hipGetLastError();
+}
+
+hipError_t fill_zero(float* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                     s, p, n);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t fuse_bwd(const T* x, const float* l2, const float* means, int nb_cap,
+                    const int32_t* idx, const float* lam, int B, int N, int D, int R, float* dxf,
+                    float* dx, float* dm, int nbs, float* dlam, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(B) * N));
+  if (R <= 4)
+    hipLaunchKernelGGL((fuse_bwd_kernel<T, 4>), grid, dim3(256), 0, s, x, l2, means, nb_cap, idx,
+                       lam, N, D, R, dxf, dx, dm, nbs, dlam);
+  else if (R <= 8)
+    hipLaunchKernelGGL((fuse_bwd_kernel<T, 8>), grid, dim3(256), 0, s, x, l2, means, nb_cap, idx,
+                       lam, N, D, R, dxf, dx, dm, nbs, dlam);
+  else if (R <= 16)
+    hipLaunchKernelGGL((fuse_bwd_kernel<T, 16>), grid, dim3(256), 0, s, x, l2, means, nb_cap, idx,
+                       lam, N, D, R, dxf, dx, dm, nbs, dlam);
+  else
+    hipLaunchKernelGGL((fuse_bwd_kernel<T, 32>), grid, dim3(256), 0, s, x, l2, means, nb_cap, idx,
+                       lam, N, D, R, dxf, dx, dm, nbs, dlam);
+  return hipGetLastError();
+}
+
+size_t ema_adj_ws_bytes(int B, int N, int D) {
+  return sizeof(float) * static_cast<size_t>(B) * ((N + kBwdChunk - 1) / kBwdChunk) * D;
+}
+
+hipError_t ema_adjoint_add(const float* u, const float* dm, int nbs, int B, int N, int D,
+                           int block, float beta, float* part, float* dx, hipStream_t s) {
+  const int n_chunks = (N + kBwdChunk - 1) / kBwdChunk;
+  const int cx = (D + 255) / 256;
+  hipLaunchKernelGGL(ema_adj_pass1, dim3(cx, n_chunks, B), dim3(256), 0, s, u, N, D, n_chunks,
+                     beta, part);
+  hipLaunchKernelGGL(ema_adj_pass2, dim3(cx, B), dim3(256), 0, s, part, N, D, n_chunks, beta);
+  hipLaunchKernelGGL(ema_adj_pass3, dim3(cx, n_chunks, B), dim3(256), 0, s, u, part, dm, nbs,
+                     N, D, n_chunks, block, beta, dx);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t router_bwd(const float* lam, const float* dlam, const float* pre, const T* w2, int r,
+                      int64_t M, Routing rt, float* dz, T* dpre, float* dw2, hipStream_t s) {
+  hipLaunchKernelGGL(router_bwd_kernel<T>, dim3(static_cast<unsigned>((M + 3) / 4)), dim3(256), 0,
+                     s, lam, dlam, pre, w2, r, M, rt, dz, dpre);
+  hipLaunchKernelGGL(router_dw2_kernel, dim3(3 * r), dim3(256), 0, s, dz, pre, r, M, dw2);
+  return hipGetLastError();
+}
+
+#define MKA_BWD_INST(T)                                                                            \
+  template hipError_t attn_bwd_prep<T>(const T*, const T*, int64_t, int, float*, hipStream_t);    \
+  template hipError_t attn_bwd_rows<T>(const T*, const T*, const T*, const T*, const float*,     \
+                                       const float*, int, int, int, int, int, int64_t, float*,    \
+                                       float*, hipStream_t);                                      \
+  template hipError_t convert<float, T>(const float*, int64_t, T*, hipStream_t);                 \
+  template hipError_t fuse_bwd<T>(const T*, const float*, const float*, int, const int32_t*,      \
+                                  const float*, int, int, int, int, float*, float*, float*, int,  \
+                                  float*, hipStream_t);                                           \
+  template hipError_t router_bwd<T>(const float*, const float*, const float*, const T*, int,      \
+                                    int64_t, Routing, float*, T*, float*, hipStream_t);
+MKA_BWD_INST(float)
+MKA_BWD_INST(bf16_t)
+#undef MKA_BWD_INST
+template hipError_t transpose<float, float>(const float*, int64_t, int, int, int, int64_t, float*,
+                                            hipStream_t);
+template hipError_t transpose<bf16_t, bf16_t>(const bf16_t*, int64_t, int, int, int, int64_t,
+                                              bf16_t*, hipStream_t);
+template hipError_t transpose<float, bf16_t>(const float*, int64_t, int, int, int, int64_t,
+                                             bf16_t*, hipStream_t);
+
+}  // namespace mka

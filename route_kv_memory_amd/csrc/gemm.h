@@ -26,6 +26,19 @@ struct EpiStore {
   }
 };
 
+// Row-major accumulate C[m * ldc + n] += v (float32 gradients).
+struct EpiAdd {
+  float* c;
+  int ldc;
+  __device__ __forceinline__ void operator()(int m, int n, float v) const {
+    c[static_cast<int64_t>(m) * ldc + n] += v;
+  }
+  __device__ __forceinline__ void store4(int m, int n, const float* v, int N) const {
+    float* p = c + static_cast<int64_t>(m) * ldc + n;
+    for (int i = 0; i < 4 && n + i < N; ++i) p[i] += v[i];
+  }
+};
+
 // Scatter into the head-major fused KV cache [B, G, t_cap, dh]: row m is token
 // t = m % seq of sequence b = m / seq, stored at cache row pos0 + t; columns
 // [0, G*dh) are K and [G*dh, 2*G*dh) are V.

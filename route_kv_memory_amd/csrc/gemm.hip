@@ -302,6 +302,13 @@ template hipError_t gemm_bf16<EpiStore<bf16_t>>(const bf16_t*, int, const bf16_t
                                                  hipStream_t);
 template hipError_t gemm_bf16<EpiKV<bf16_t>>(const bf16_t*, int, const bf16_t*, const bf16_t*, int,
                                               int, int, int, const EpiKV<bf16_t>&, hipStream_t);
+template hipError_t gemm_bf16<EpiStore<float>>(const bf16_t*, int, const bf16_t*, const bf16_t*,
+                                                int, int, int, int, const EpiStore<float>&,
+                                                hipStream_t);
+template hipError_t gemm_bf16<EpiAdd>(const bf16_t*, int, const bf16_t*, const bf16_t*, int, int,
+                                      int, int, const EpiAdd&, hipStream_t);
+template hipError_t gemm_f32<EpiAdd>(const float*, int, const float*, const float*, int, int, int,
+                                     int, const EpiAdd&, hipStream_t);
 template hipError_t gemm_f32<EpiStore<float>>(const float*, int, const float*, const float*, int,
                                                int, int, int, const EpiStore<float>&, hipStream_t);
 template hipError_t gemm_f32<EpiKV<float>>(const float*, int, const float*, const float*, int, int,

@@ -87,7 +87,7 @@ hipError_t block_kv_project(const float* means, int nb_cap, int first, int n_blo
 // ---- attention --------------------------------------------------------------------
 template <typename T>
 hipError_t attn_prefill(const T* q, const T* k, const T* v, T* o, int B, int seq, int H, int G,
-                        int dh, const KvLayout& kv, int64_t pos0, hipStream_t s);
+                        int dh, const KvLayout& kv, int64_t pos0, float* lse, hipStream_t s);
 // Split decode (bf16): partials in ws (for n_rows rows split into chunks),
 // merged by a second kernel.
 size_t attn_decode_ws_bytes(int B, int H, int G, int dh, int64_t n_rows);
@@ -103,5 +103,33 @@ hipError_t attn_decode_split_bf16(const bf16_t* q, const bf16_t* k, const bf16_t
 hipError_t attn_decode_merge_bf16(const bf16_t* q, const bf16_t* k, const bf16_t* v, bf16_t* o,
                                   int B, int H, int G, int dh, const KvLayout& kv, int64_t n_old,
                                   int64_t extra_row, void* ws, hipStream_t s);
+
+// ---- backward (backward.hip) ------------------------------------------------
+// D = rowsum(dO * O) over rows of dh values.
+template <typename T>
+hipError_t attn_bwd_prep(const T* o, const T* d_o, int64_t rows, int dh, float* dsum,
+                         hipStream_t s);
+// Row-parallel attention backward over a contiguous cache: dq [B,N,H,dh] and
+// dkv [B,N,2,G,dh] (K part, then V part), float32; lse and dsum [B,N,H].
+template <typename T>
+hipError_t attn_bwd_rows(const T* q, const T* k, const T* v, const T* d_o, const float* lse,
+                         const float* dsum, int B, int N, int H, int G, int dh, int64_t t_cap,
+                         float* dq, float* dkv, hipStream_t s);
+template <typename TS, typename TD>
+hipError_t transpose(const TS* src, int64_t lds_, int R, int C, int Rp, int64_t ldd, TD* dst,
+                     hipStream_t s);
+template <typename TS, typename TD>
+hipError_t convert(const TS* src, int64_t n, TD* dst, hipStream_t s);
+hipError_t fill_zero(float* p, int64_t n, hipStream_t s);
+template <typename T>
+hipError_t fuse_bwd(const T* x, const float* l2, const float* means, int nb_cap,
+                    const int32_t* idx, const float* lam, int B, int N, int D, int R, float* dxf,
+                    float* dx, float* dm, int nbs, float* dlam, hipStream_t s);
+size_t ema_adj_ws_bytes(int B, int N, int D);
+hipError_t ema_adjoint_add(const float* u, const float* dm, int nbs, int B, int N, int D,
+                           int block, float beta, float* part, float* dx, hipStream_t s);
+template <typename T>
+hipError_t router_bwd(const float* lam, const float* dlam, const float* pre, const T* w2, int r,
+                      int64_t M, Routing rt, float* dz, T* dpre, float* dw2, hipStream_t s);
 
 }  // namespace mka

@@ -351,18 +351,20 @@ int do_mix(const mka_dims* d, void* const a[3], const float* lam, void* o, hipSt
 }
 
 int do_attn_prefill(const mka_dims* d, const void* q, const void* kc, const void* vc,
-                    const KvLayout& kv, int64_t pos0, void* o, hipStream_t s) {
+                    const KvLayout& kv, int64_t pos0, void* o, hipStream_t s,
+                    float* lse = nullptr) {
   if (d->dtype == MKA_BF16)
     MKA_LAUNCH("attn_prefill",
                attn_prefill<bf16_t>(static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(kc),
                                     static_cast<const bf16_t*>(vc), static_cast<bf16_t*>(o),
                                     d->batch, d->seq, d->n_heads, d->n_kv_heads, d->head_dim,
-                                    kv, pos0, s));
+                                    kv, pos0, lse, s));
   else
     MKA_LAUNCH("attn_prefill",
                attn_prefill<float>(static_cast<const float*>(q), static_cast<const float*>(kc),
                                    static_cast<const float*>(vc), static_cast<float*>(o), d->batch,
-                                   d->seq, d->n_heads, d->n_kv_heads, d->head_dim, kv, pos0, s));
+                                   d->seq, d->n_heads, d->n_kv_heads, d->head_dim, kv, pos0, lse,
+                                   s));
   return MKA_OK;
 }
 
@@ -378,7 +380,7 @@ int do_attn_decode(const mka_dims* d, const void* q, const void* kc, const void*
                attn_prefill<float>(static_cast<const float*>(q), static_cast<const float*>(kc),
                                    static_cast<const float*>(vc), static_cast<float*>(o), d->batch,
                                    1, d->n_heads, d->n_kv_heads, d->head_dim, kv, cache_len - 1,
-                                   s));
+                                   nullptr, s));
   return MKA_OK;
 }
 
@@ -493,6 +495,154 @@ FullWs full_layout(const mka_dims* d, bool decode, int64_t cache_len) {
   return w;
 }
 
+// Workspace of the backward: float32 gradients and scratch, then the storage
+// type's product operands (transposed ones padded to Mp = M rounded up to 32
+// tokens, the products' reduction dimension).
+struct BwdWs {
+  size_t dsum, dq, dkv, dxf, dlam, dz, dm, part, pre;           // float32
+  size_t dkv_a, dkv_t, wkv_t, xf, xf_t, dpre, dpre_t, q_t, wr1_t, wq_t, dq_a, dq_t, x_t;  // dtype
+  size_t total;
+  int Mp, nbs;
+};
+BwdWs bwd_layout(const mka_dims* d) {
+  BwdWs w{};
+  const size_t M = rows_of(d), el = el_size(d), f = sizeof(float);
+  const size_t D = d->d_model, qw = static_cast<size_t>(d->n_heads) * d->head_dim;
+  const size_t kvw = static_cast<size_t>(d->n_kv_heads) * d->head_dim, r = d->router_hidden;
+  const size_t H = d->n_heads;
+  w.Mp = static_cast<int>((M + 31) / 32 * 32);
+  w.nbs = d->seq / d->block + 1;
+  const size_t Mp = w.Mp;
+  const bool bf = d->dtype == MKA_BF16;
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = at;
+    at += round256(bytes);
+    return o;
+  };
+  w.dsum = take(f * M * H);
+  w.dq = take(f * M * qw);
+  w.dkv = take(f * M * 2 * kvw);
+  w.dxf = take(f * M * D);
+  w.dlam = take(f * M * 3);
+  w.dz = take(f * M * 3);
+  w.dm = take(f * d->batch * w.nbs * D);
+  w.part = take(ema_adj_ws_bytes(d->batch, d->seq, d->d_model));
+  w.pre = take(f * M * r);
+  w.dkv_a = bf ? take(el * M * 2 * kvw) : 0;
+  w.dkv_t = take(el * 2 * kvw * Mp);
+  w.wkv_t = take(el * D * 2 * kvw);
+  w.xf = take(el * M * D);
+  w.xf_t = take(el * D * Mp);
+  w.dpre = take(el * M * r);
+  w.dpre_t = take(el * r * Mp);
+  w.q_t = take(el * qw * Mp);
+  w.wr1_t = take(el * qw * r);
+  w.wq_t = take(el * D * qw);
+  w.dq_a = bf ? take(el * M * qw) : 0;
+  w.dq_t = take(el * qw * Mp);
+  w.x_t = take(el * D * Mp);
+  w.total = at;
+  return w;
+}
+
+template <typename T>
+hipError_t gemm_t(const T* a, int lda, const T* b, int M, int N, int K, const EpiStore<float>& e,
+                  hipStream_t s) {
+  if constexpr (std::is_same<T, bf16_t>::value) return gemm_bf16(a, lda, b, b, N, M, N, K, e, s);
+  else return gemm_f32(a, lda, b, b, N, M, N, K, e, s);
+}
+template <typename T>
+hipError_t gemm_t(const T* a, int lda, const T* b, int M, int N, int K, const EpiAdd& e,
+                  hipStream_t s) {
+  if constexpr (std::is_same<T, bf16_t>::value) return gemm_bf16(a, lda, b, b, N, M, N, K, e, s);
+  else return gemm_f32(a, lda, b, b, N, M, N, K, e, s);
+}
+
+template <typename T>
+int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const mka_state* st,
+                  const mka_outputs* fwd, const void* d_o_, const mka_grads* gr, char* ws,
+                  hipStream_t s) {
+  const BwdWs L = bwd_layout(d);
+  const int B = d->batch, N = d->seq, D = d->d_model, H = d->n_heads, G = d->n_kv_heads;
+  const int dh = d->head_dim, qw = H * dh, kvw = G * dh, r = d->router_hidden, Mp = L.Mp;
+  const int M = rows_of(d);
+  const Routing rt = routing_of(d);
+  constexpr bool kBf = std::is_same<T, bf16_t>::value;
+  const T* x = static_cast<const T*>(x_);
+  const T* d_o = static_cast<const T*>(d_o_);
+  const T* q = static_cast<const T*>(fwd->q);
+  const T* o = static_cast<const T*>(fwd->o);
+  const T* wq = static_cast<const T*>(w->w_q);
+  const T* wk = static_cast<const T*>(w->w_k);
+  const T* wv = static_cast<const T*>(w->w_v);
+  const T* wr1 = static_cast<const T*>(w->w_r1);
+  const T* wr2 = static_cast<const T*>(w->w_r2);
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  auto E = [&](size_t off) { return reinterpret_cast<T*>(ws + off); };
+  float *dsum = F(L.dsum), *dq = F(L.dq), *dkv = F(L.dkv), *dxf = F(L.dxf), *dlam = F(L.dlam);
+  float *dz = F(L.dz), *dm = F(L.dm), *part = F(L.part), *pre = F(L.pre);
+  T *dkv_t = E(L.dkv_t), *wkv_t = E(L.wkv_t), *xf = E(L.xf), *xf_t = E(L.xf_t);
+  T *dpre = E(L.dpre), *dpre_t = E(L.dpre_t), *q_t = E(L.q_t), *wr1_t = E(L.wr1_t);
+  T *wq_t = E(L.wq_t), *dq_t = E(L.dq_t), *x_t = E(L.x_t);
+  // the float32 gradients as product operands of the storage type
+  const T* dkv_a = kBf ? E(L.dkv_a) : reinterpret_cast<const T*>(dkv);
+  const T* dq_a = kBf ? E(L.dq_a) : reinterpret_cast<const T*>(dq);
+
+  // attention: D = rowsum(dO * O), then dq, dK, dV
+  MKA_LAUNCH("bwd/prep", attn_bwd_prep<T>(o, d_o, static_cast<int64_t>(M) * H, dh, dsum, s));
+  MKA_LAUNCH("bwd/attn", attn_bwd_rows<T>(q, static_cast<const T*>(st->k_cache),
+                                          static_cast<const T*>(st->v_cache), d_o, fwd->lse, dsum,
+                                          B, N, H, G, dh, st->t_cap, dq, dkv, s));
+  // [K|V] = X_fused [W_k|W_v]^T: dX_fused = dKV [W_k; W_v]; dW = dKV^T X_fused
+  MKA_LAUNCH("bwd/t", (transpose<T, T>(wk, D, kvw, D, kvw, 2 * kvw, wkv_t, s)));
+  MKA_LAUNCH("bwd/t", (transpose<T, T>(wv, D, kvw, D, kvw, 2 * kvw, wkv_t + kvw, s)));
+  if (kBf) MKA_LAUNCH("bwd/cvt", (convert<float, T>(dkv, static_cast<int64_t>(M) * 2 * kvw,
+                                                     const_cast<T*>(dkv_a), s)));
+  MKA_LAUNCH("bwd/dxf", gemm_t<T>(dkv_a, 2 * kvw, wkv_t, M, D, 2 * kvw, EpiStore<float>{dxf, D}, s));
+  MKA_LAUNCH("bwd/t", (transpose<float, T>(dkv, 2 * kvw, M, 2 * kvw, Mp, Mp, dkv_t, s)));
+  const T* xf_src = x;
+  if (rt.ema()) {
+    MKA_LAUNCH("bwd/fuse", fuse_mix<T>(x, fwd->l2, st->block_means, st->nb_cap, fwd->idx,
+                                        fwd->lambda, B, N, D, d->top_r, rt, xf, s));
+    xf_src = xf;
+  }
+  MKA_LAUNCH("bwd/t", (transpose<T, T>(xf_src, D, M, D, Mp, Mp, xf_t, s)));
+  MKA_LAUNCH("bwd/dwk", gemm_t<T>(dkv_t, Mp, xf_t, kvw, D, Mp, EpiStore<float>{gr->dw_k, D}, s));
+  MKA_LAUNCH("bwd/dwv", gemm_t<T>(dkv_t + static_cast<size_t>(kvw) * Mp, Mp, xf_t, kvw, D, Mp,
+                                  EpiStore<float>{gr->dw_v, D}, s));
+  // the fusion, the EMA's adjoint and the block means' adjoint
+  MKA_LAUNCH("bwd/zero", fill_zero(dm, static_cast<int64_t>(B) * L.nbs * D, s));
+  MKA_LAUNCH("bwd/fuse", fuse_bwd<T>(x, rt.l2() ? fwd->l2 : nullptr, st->block_means, st->nb_cap,
+                                     rt.l3() ? fwd->idx : nullptr, fwd->lambda, B, N, D,
+                                     rt.l3() ? d->top_r : 0, dxf, gr->dx, dm, L.nbs, dlam, s));
+  MKA_LAUNCH("bwd/ema", ema_adjoint_add(dxf, dm, L.nbs, B, N, D, d->block, d->ema_decay, part,
+                                        gr->dx, s));
+  // router: dz, dW_r2, dpre; dW_r1 = dpre^T q; dq += dpre W_r1
+  if (rt.learned()) {
+    MKA_LAUNCH("bwd/pre", gemm_t<T>(q, qw, wr1, M, r, qw, EpiStore<float>{pre, r}, s));
+    MKA_LAUNCH("bwd/router", router_bwd<T>(fwd->lambda, dlam, pre, wr2, r, M, rt, dz, dpre,
+                                           gr->dw_r2, s));
+    MKA_LAUNCH("bwd/t", (transpose<T, T>(dpre, r, M, r, Mp, Mp, dpre_t, s)));
+    MKA_LAUNCH("bwd/t", (transpose<T, T>(q, qw, M, qw, Mp, Mp, q_t, s)));
+    MKA_LAUNCH("bwd/dwr1", gemm_t<T>(dpre_t, Mp, q_t, r, qw, Mp, EpiStore<float>{gr->dw_r1, qw}, s));
+    MKA_LAUNCH("bwd/t", (transpose<T, T>(wr1, qw, r, qw, r, r, wr1_t, s)));
+    MKA_LAUNCH("bwd/dqr", gemm_t<T>(dpre, r, wr1_t, M, qw, r, EpiAdd{dq, qw}, s));
+  } else {
+    MKA_LAUNCH("bwd/zero", fill_zero(gr->dw_r1, static_cast<int64_t>(r) * qw, s));
+    MKA_LAUNCH("bwd/zero", fill_zero(gr->dw_r2, 3 * r, s));
+  }
+  // Q = x W_q^T: dx += dq W_q; dW_q = dq^T x
+  MKA_LAUNCH("bwd/t", (transpose<T, T>(wq, D, qw, D, qw, qw, wq_t, s)));
+  if (kBf) MKA_LAUNCH("bwd/cvt", (convert<float, T>(dq, static_cast<int64_t>(M) * qw,
+                                                     const_cast<T*>(dq_a), s)));
+  MKA_LAUNCH("bwd/dx", gemm_t<T>(dq_a, qw, wq_t, M, D, qw, EpiAdd{gr->dx, D}, s));
+  MKA_LAUNCH("bwd/t", (transpose<float, T>(dq, qw, M, qw, Mp, Mp, dq_t, s)));
+  MKA_LAUNCH("bwd/t", (transpose<T, T>(x, D, M, D, Mp, Mp, x_t, s)));
+  MKA_LAUNCH("bwd/dwq", gemm_t<T>(dq_t, Mp, x_t, qw, D, Mp, EpiStore<float>{gr->dw_q, D}, s));
+  return MKA_OK;
+}
+
 int check_full_args(const mka_dims* d, const void* x, int64_t pos0, const mka_weights* w,
                     const mka_state* st, const mka_tier_cache* kv, const mka_outputs* out) {
   MKA_CHECK(w != nullptr && st != nullptr && kv != nullptr && out != nullptr, MKA_ERR_INVALID);
@@ -545,6 +695,7 @@ size_t mka_workspace_bytes(const mka_dims* d, int op, int64_t cache_len) {
     case MKA_OP_DECODE_STEP:
       return d->seq == 1 && cache_len > 0 ? decode_layout(d, cache_len).total : 0;
     case MKA_OP_FULL_PREFILL: return full_layout(d, false, 0).total;
+    case MKA_OP_BACKWARD: return bwd_layout(d).total;
     case MKA_OP_FULL_DECODE_STEP:
       return d->seq == 1 && cache_len > 0 ? full_layout(d, true, cache_len).total : 0;
     default: return 0;
@@ -759,7 +910,7 @@ int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weight
                        w->w_v, st->k_cache, st->v_cache, pos0, layout_of(d, st), ws_main, s)))
     return rc;
   if ((rc = do_attn_prefill(d, out->q, st->k_cache, st->v_cache, layout_of(d, st), pos0, out->o,
-                            s)))
+                            s, out->lse)))
     return rc;
   MKA_LAUNCH("prefill/join", hipStreamWaitEvent(s, aux->done, 0));
   return MKA_OK;
@@ -985,6 +1136,31 @@ int mka_full_decode_step(const mka_dims* d, const void* x, int64_t pos, const mk
     return do_index(d, st->block_means, st->nb_cap, static_cast<int>((pos + 1) / d->block - 1), 1,
                     w->proj, st->block_hash, shared, s);
   return MKA_OK;
+}
+
+int mka_backward(const mka_dims* d, const void* x, const mka_weights* w, const mka_state* st,
+                 const mka_outputs* fwd, const void* d_o, const mka_grads* g, void* ws,
+                 size_t ws_bytes, void* stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  MKA_CHECK(w != nullptr && st != nullptr && fwd != nullptr && g != nullptr, MKA_ERR_INVALID);
+  const Routing rt = routing_of(d);
+  MKA_CHECK(ptrs_ok({x, d_o, w->w_q, w->w_k, w->w_v, w->w_r1, w->w_r2}), MKA_ERR_INVALID);
+  MKA_CHECK(ptrs_ok({fwd->q, fwd->lambda, fwd->o, fwd->lse, st->k_cache, st->v_cache}),
+            MKA_ERR_INVALID);
+  MKA_CHECK(!rt.ema() || ptrs_ok({fwd->l2}), MKA_ERR_INVALID);
+  MKA_CHECK(!rt.l3() || ptrs_ok({fwd->idx, st->block_means}), MKA_ERR_INVALID);
+  MKA_CHECK(ptrs_ok({g->dx, g->dw_q, g->dw_k, g->dw_v, g->dw_r1, g->dw_r2}), MKA_ERR_INVALID);
+  MKA_CHECK(d->seq <= st->t_cap && st->nb_cap >= 1 && d->seq / d->block <= st->nb_cap,
+            MKA_ERR_INVALID);
+  MKA_CHECK(st->page_table == nullptr, MKA_ERR_UNSUPPORTED);
+  MKA_CHECK(d->dtype != MKA_BF16 || d->router_hidden % 32 == 0, MKA_ERR_UNSUPPORTED);
+  const BwdWs L = bwd_layout(d);
+  MKA_CHECK(ws_bytes >= L.total && ptrs_ok({ws}), MKA_ERR_WORKSPACE);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  if (d->dtype == MKA_BF16) return backward_body<bf16_t>(d, x, w, st, fwd, d_o, g, base, s);
+  return backward_body<float>(d, x, w, st, fwd, d_o, g, base, s);
 }
 
 }  // extern "C"

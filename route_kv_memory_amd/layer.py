@@ -103,13 +103,15 @@ class Layer:
             "key": torch.empty(B, seq, dtype=torch.int64, **z),
             "idx": torch.empty(B, seq, s.top_r, dtype=torch.int32, **z),
             "o": torch.empty(B, seq, s.n_heads, s.head_dim, dtype=self.tdtype, **z),
+            "lse": torch.empty(B, seq, s.n_heads, dtype=torch.float32, **z),
         }
 
     @staticmethod
     def _out_struct(out: dict) -> mka.Outputs:
         return mka.Outputs(q=out["q"].data_ptr(), lambda_=out["lambda"].data_ptr(),
                            l2=out["l2"].data_ptr(), key=out["key"].data_ptr(),
-                           idx=out["idx"].data_ptr(), o=out["o"].data_ptr())
+                           idx=out["idx"].data_ptr(), o=out["o"].data_ptr(),
+                           lse=out["lse"].data_ptr() if "lse" in out else None)
 
     def workspace(self, nbytes: int) -> torch.Tensor:
         if self._ws is None or self._ws.numel() < nbytes:
@@ -179,3 +181,27 @@ class Layer:
         for p in range(-(-n // P)):
             r0, r1 = p * P, min(n, (p + 1) * P)
             c[pt[:, p], :, : r1 - r0] = rows[:, :, r0:r1].to(c.dtype)
+
+    def grads(self, seq: int) -> dict:
+        """float32 gradient buffers of x and the weights."""
+        s, B, z = self.shape, self.batch, dict(device=self.device, dtype=torch.float32)
+        return {
+            "dx": torch.empty(B, seq, s.d_model, **z),
+            "dw_q": torch.empty(s.q_width, s.d_model, **z),
+            "dw_k": torch.empty(s.kv_width, s.d_model, **z),
+            "dw_v": torch.empty(s.kv_width, s.d_model, **z),
+            "dw_r1": torch.empty(s.router_hidden, s.q_width, **z),
+            "dw_r2": torch.empty(3, s.router_hidden, **z),
+        }
+
+    def backward(self, x: torch.Tensor, out: dict, d_o: torch.Tensor, grads: dict | None = None,
+                 stream=None) -> dict:
+        """Gradients of sum(O * d_o) after ``prefill(x, 0, out)`` (the saved forward)."""
+        seq = x.shape[1]
+        d = self.dims(seq)
+        grads = self.grads(seq) if grads is None else grads
+        ws = self.workspace(mka.mka_workspace_bytes(d, mka.MKA_OP_BACKWARD))
+        g = mka.Grads(**{k: v.data_ptr() for k, v in grads.items()})
+        mka.mka_backward(d, x, self.weights, self.state, self._out_struct(out), d_o, g, ws,
+                         ws.numel(), stream)
+        return grads

@@ -25,6 +25,7 @@ __all__ = [
     "mka_fuse_kv_proj",
     "mka_attn_prefill", "mka_attn_decode", "mka_prefill", "mka_decode_step", "TierCache",
     "mka_full_prefill", "mka_full_decode_step", "MKA_OP_FULL_PREFILL", "MKA_OP_FULL_DECODE_STEP",
+    "Grads", "mka_backward", "MKA_OP_BACKWARD",
     "mka_workspace_bytes", "mka_status_string", "mka_last_error", "mka_version",
     "mka_probe_mfma_bf16", "mka_probe_stream_read", "PROBE_STREAM_WORKGROUPS",
 ]
@@ -43,7 +44,8 @@ TIER_SETS = {"l1l2l3": MKA_TIERS_ALL, "l1l2": MKA_TIERS_L1_L2, "l1l3": MKA_TIERS
              "l1": MKA_TIERS_L1}
 MKA_OK, MKA_ERR_INVALID, MKA_ERR_UNSUPPORTED, MKA_ERR_WORKSPACE, MKA_ERR_HIP = 0, -1, -2, -3, -4
 (MKA_OP_EMA_SCAN, MKA_OP_FUSE_KV, MKA_OP_ATTN_DECODE, MKA_OP_PREFILL, MKA_OP_DECODE_STEP,
- MKA_OP_RETRIEVE, MKA_OP_INDEX, MKA_OP_ROUTE, MKA_OP_FULL_PREFILL, MKA_OP_FULL_DECODE_STEP) = range(10)
+ MKA_OP_RETRIEVE, MKA_OP_INDEX, MKA_OP_ROUTE, MKA_OP_FULL_PREFILL, MKA_OP_FULL_DECODE_STEP,
+ MKA_OP_BACKWARD) = range(11)
 
 
 class MkaError(RuntimeError):
@@ -82,7 +84,11 @@ class TierCache(ctypes.Structure):
 
 
 class Outputs(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("q", "lambda_", "l2", "key", "idx", "o")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("q", "lambda_", "l2", "key", "idx", "o", "lse")]
+
+
+class Grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("dx", "dw_q", "dw_k", "dw_v", "dw_r1", "dw_r2")]
 
 
 _lib = None
@@ -114,6 +120,9 @@ _SIGS = {
     "mka_full_decode_step": (ctypes.c_int, [_PD, _P, _I64, ctypes.POINTER(Weights),
                                             ctypes.POINTER(State), ctypes.POINTER(TierCache),
                                             ctypes.POINTER(Outputs), _P, _SZ, _P]),
+    "mka_backward": (ctypes.c_int, [_PD, _P, ctypes.POINTER(Weights), ctypes.POINTER(State),
+                                    ctypes.POINTER(Outputs), _P, ctypes.POINTER(Grads), _P, _SZ,
+                                    _P]),
     "mka_probe_mfma_bf16": (ctypes.c_int, [_I32, _I32, _P, _P]),
     "mka_probe_stream_read": (ctypes.c_int, [_P, _SZ, _P, _P]),
 }
@@ -264,6 +273,12 @@ def mka_full_decode_step(d, x, pos, weights, state, tiers, outputs, ws, ws_bytes
     _check("mka_full_decode_step", lib().mka_full_decode_step(
         ctypes.byref(d), _ptr(x), pos, ctypes.byref(weights), ctypes.byref(state),
         ctypes.byref(tiers), ctypes.byref(outputs), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def mka_backward(d, x, weights, state, fwd, d_o, grads, ws, ws_bytes, stream=None):
+    _check("mka_backward", lib().mka_backward(
+        ctypes.byref(d), _ptr(x), ctypes.byref(weights), ctypes.byref(state), ctypes.byref(fwd),
+        _ptr(d_o), ctypes.byref(grads), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def mka_workspace_bytes(d, op, cache_len=0) -> int:
