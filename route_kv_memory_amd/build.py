@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmka.so")
 
 SOURCES = ["mka_api.hip", "gemm.hip", "route.hip", "ema.hip", "l3.hip", "fuse.hip", "attn.hip",
-           "decode.hip", "probe.hip", "backward.hip"]
+           "decode.hip", "probe.hip", "backward.hip", "attn_bwd.hip"]
 
 ARCH = os.environ.get("MKA_OFFLOAD_ARCH", "gfx950")
 

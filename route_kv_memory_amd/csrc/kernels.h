@@ -115,6 +115,10 @@ template <typename T>
 hipError_t attn_bwd_rows(const T* q, const T* k, const T* v, const T* d_o, const float* lse,
                          const float* dsum, int B, int N, int H, int G, int dh, int64_t t_cap,
                          float* dq, float* dkv, hipStream_t s);
+// The same on the matrix cores (bf16), from the forward's log-sum-exp.
+hipError_t attn_bwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* d_o,
+                         const float* lse, const float* dsum, int B, int N, int H, int G, int dh,
+                         int64_t t_cap, float* dq, float* dkv, hipStream_t s);
 template <typename TS, typename TD>
 hipError_t transpose(const TS* src, int64_t lds_, int R, int C, int Rp, int64_t ldd, TD* dst,
                      hipStream_t s);

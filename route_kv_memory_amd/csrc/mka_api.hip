@@ -591,9 +591,14 @@ int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const
 
   // attention: D = rowsum(dO * O), then dq, dK, dV
   MKA_LAUNCH("bwd/prep", attn_bwd_prep<T>(o, d_o, static_cast<int64_t>(M) * H, dh, dsum, s));
-  MKA_LAUNCH("bwd/attn", attn_bwd_rows<T>(q, static_cast<const T*>(st->k_cache),
-                                          static_cast<const T*>(st->v_cache), d_o, fwd->lse, dsum,
-                                          B, N, H, G, dh, st->t_cap, dq, dkv, s));
+  if constexpr (kBf)
+    MKA_LAUNCH("bwd/attn", attn_bwd_mfma(q, static_cast<const T*>(st->k_cache),
+                                         static_cast<const T*>(st->v_cache), d_o, fwd->lse, dsum,
+                                         B, N, H, G, dh, st->t_cap, dq, dkv, s));
+  else
+    MKA_LAUNCH("bwd/attn", attn_bwd_rows<T>(q, static_cast<const T*>(st->k_cache),
+                                            static_cast<const T*>(st->v_cache), d_o, fwd->lse,
+                                            dsum, B, N, H, G, dh, st->t_cap, dq, dkv, s));
   // [K|V] = X_fused [W_k|W_v]^T: dX_fused = dKV [W_k; W_v]; dW = dKV^T X_fused
   MKA_LAUNCH("bwd/t", (transpose<T, T>(wk, D, kvw, D, kvw, 2 * kvw, wkv_t, s)));
   MKA_LAUNCH("bwd/t", (transpose<T, T>(wv, D, kvw, D, kvw, 2 * kvw, wkv_t + kvw, s)));

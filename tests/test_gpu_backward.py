@@ -65,6 +65,7 @@ CASES = [
     ("tiny_f32", "soft", "l1l2l3"), ("tiny_f32", "top2", "l1l3"), ("tiny_f32", "fixed", "l1l2"),
     ("tiny_f32", "soft", "l1"), ("small_f32_b2", "soft", "l1l2l3"),
     ("small_bf16_dh128", "soft", "l1l2l3"), ("small_bf16_dh128", "top1", "l1l3"),
+    ("tiny_bf16", "soft", "l1l2l3"), ("tiny_bf16", "fixed", "l1"),
 ]
 
 
