@@ -259,6 +259,47 @@ def bench_prefill(s, steps, warmup, variants=(), settle_ms=0.0, full=False):
                 variants_ms=var_ms, settle_steps=settled, full_ms=full_ms)
 
 
+def bench_train(s, steps, warmup, settle_ms=0.0):
+    """One training step of the layer: mka_prefill (which saves each query row's
+    log-sum-exp) then mka_backward with a seeded dO; HIP events split the two."""
+    import torch
+
+    from route_kv_memory_amd.inputs import prefill_inputs, round_bf16
+    from route_kv_memory_amd.layer import Layer, to_device
+
+    inp = prefill_inputs(s)
+    layer = Layer(s, inp, t_cap=s.seq, nb_cap=s.seq // s.block)
+    x = to_device(inp["x"], s.dtype)
+    del inp
+    d_o = to_device(round_bf16(np.random.default_rng(s.seed + 1000).standard_normal(
+        (s.batch, s.seq, s.n_heads, s.head_dim))), s.dtype)
+    out, grads = layer.outputs(s.seq), layer.grads(s.seq)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        layer.prefill(x, 0, out=out, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        layer.backward(x, out, d_o, grads, stream=stream)
+        if ev:
+            ev[2].record(stream)
+
+    settle(step, settle_ms)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    return dict(ms=wall, fwd_ms=float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
+                bwd_ms=float(np.mean([e[1].elapsed_time(e[2]) for e in evs])))
+
+
 def bench_prefill_paged(s, steps, warmup, page_size, settle_ms=0.0):
     """The composite prefill with a paged fused cache (pages of ``page_size``
     rows, a seeded random order with spare pages in the pool)."""
@@ -470,6 +511,9 @@ def main():
     ap.add_argument("--full-mka", action="store_true",
                     help="also time full MKA (three attention paths mixed by lambda) on the same "
                          "workloads")
+    ap.add_argument("--train", action="store_true",
+                    help="also time a training step (forward with saved log-sum-exp, then the "
+                         "backward) of the prefill workload")
     ap.add_argument("--paged", type=int, default=0, metavar="ROWS",
                     help="also time prefill and decode with a paged fused cache of pages of "
                          "ROWS rows")
@@ -570,6 +614,14 @@ def main():
             k: {"prefill_tokens_per_s": tokens / (v * 1e-3), "prefill_ms": v,
                 "decode_us_per_token": dc["variants_us"].get(k) if not args.no_decode else None}
             for k, v in pf["variants_ms"].items()}
+    if args.train:
+        tr = bench_train(s, args.steps, args.warmup, args.settle_ms)
+        log(f"training step: {tr['ms']:.3f} ms (forward {tr['fwd_ms']:.3f}, backward "
+            f"{tr['bwd_ms']:.3f})")
+        line["train"] = {"tokens_per_s": tokens / (tr["ms"] * 1e-3), "ms_per_step": tr["ms"],
+                         "forward_ms": tr["fwd_ms"], "backward_ms": tr["bwd_ms"],
+                         "note": "mka_prefill (saving log-sum-exp) + mka_backward: gradients of "
+                                 "x and every weight, fp32"}
     if args.paged:
         pms = bench_prefill_paged(s, args.steps, args.warmup, args.paged, args.settle_ms)
         log(f"paged prefill (pages of {args.paged}): {pms:.4f} ms")

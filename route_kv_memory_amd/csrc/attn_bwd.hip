@@ -185,10 +185,13 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV.  Workgroup = 4 waves = 128 key rows of one KV head; query tiles of 64
-// rows of each query head of the group, from the key block's first row (no
+// dK, dV.  Workgroup = 4 waves = 128 key rows of one KV head and ONE of the
+// group's query heads (units ordered heaviest first: the first key blocks see
+// the most queries); query tiles of 64 rows from the key block's first row (no
 // earlier query sees these keys), double-buffered in LDS as rows (Q, dO) and
-// transposed (Q^T, dO^T), with each row's log-sum-exp (log2 units) and D.
+// transposed (Q^T, dO^T), with each row's log-sum-exp (log2 units) and D.  The
+// head's share goes to its own slice of ``dkv`` ([hpg][B, N, 2, G, DH]), summed
+// over the heads afterwards in a fixed order.
 // ---------------------------------------------------------------------------
 template <int DH>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
@@ -204,10 +207,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
   __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
   __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
 
-  // blocks with the most queries (the first key blocks) start first
-  const int u = blockIdx.x;
-  const int kblk = u / (B * G), b = (u % (B * G)) / G, g = u % G;
   const int hpg = H / G;
+  const int u = blockIdx.x, per_kblk = B * G * hpg;
+  const int kblk = u / per_kblk, rest = u % per_kblk;
+  const int hh = rest % hpg, b = rest / (G * hpg), g = (rest / hpg) % G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5, l32 = lane & 31;
   const int k_row = kblk * BK + wave * 32 + l32;
   const int64_t kvoff =
@@ -223,15 +226,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
     }
   }
   const int t_first = kblk * BK;
-  const int tiles_per_head = (N - t_first + BQ - 1) / BQ;
-  const int n_it = hpg * tiles_per_head;
+  const int n_it = (N - t_first + BQ - 1) / BQ;  // query tiles of head g*hpg + hh
 
   u32x4 rq[4], rg[4];
   float rl = 0.f, rd = 0.f;
   // rows past N are loaded from row N-1 and zeroed; their lse is +inf (P = 0)
+  const int h = g * hpg + hh;
   auto gload = [&](int it) {
-    const int h = g * hpg + it / tiles_per_head;
-    const int t0 = t_first + (it % tiles_per_head) * BQ;
+    const int t0 = t_first + it * BQ;
     if (tid < VITEMS) {
       const int kq = tid & 15, dc = tid >> 4;
 #pragma unroll
@@ -280,7 +282,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
   __syncthreads();
   for (int it = 0; it < n_it; ++it) {
     const int buf = it & 1;
-    const int t0 = t_first + (it % tiles_per_head) * BQ;
+    const int t0 = t_first + it * BQ;
     if (it + 1 < n_it) gload(it + 1);
     f32x16 s[2], dp[2];
 #pragma unroll
@@ -331,7 +333,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
     __syncthreads();
   }
   if (k_row < N) {
-    float* out = dkv + static_cast<int64_t>(b * N + k_row) * 2 * G * DH + g * DH;
+    float* out = dkv + static_cast<int64_t>(hh) * B * N * 2 * G * DH +
+                 static_cast<int64_t>(b * N + k_row) * 2 * G * DH + g * DH;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -347,25 +350,52 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
   }
 }
 
+// dkv[i] = sum over the hpg slices (in slice order), four values per thread.
+__global__ __launch_bounds__(256) void sum_slices_kernel(const float* __restrict__ part, int hpg,
+                                                         int64_t n4, float* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n4) return;
+  float4 acc = reinterpret_cast<const float4*>(part)[i];
+  for (int k = 1; k < hpg; ++k) {
+    const float4 v = reinterpret_cast<const float4*>(part)[k * n4 + i];
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  reinterpret_cast<float4*>(out)[i] = acc;
+}
+
+size_t attn_bwd_mfma_ws_bytes(int B, int N, int H, int G, int dh) {
+  return H / G > 1 ? sizeof(float) * static_cast<size_t>(H / G) * B * N * 2 * G * dh : 0;
+}
+
 hipError_t attn_bwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* d_o,
                          const float* lse, const float* dsum, int B, int N, int H, int G, int dh,
-                         int64_t t_cap, float* dq, float* dkv, hipStream_t s) {
+                         int64_t t_cap, float* dq, float* dkv, float* part, hipStream_t s) {
   const float scale = 1.0f / sqrtf(static_cast<float>(dh));
   const float sl2 = kLog2e * scale;
   const int n_qblk = (N + 127) / 128;
   const int n_units = n_qblk * B * G;
   const int grid_q = ((n_units + 7) / 8) * 8 * (H / G);
-  const int grid_k = ((N + 127) / 128) * B * G;
+  const int hpg = H / G;
+  const int grid_k = ((N + 127) / 128) * B * G * hpg;
+  float* dst = hpg > 1 ? part : dkv;  // per-head slices, summed below
   if (dh == 128) {
     hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, dim3(grid_q), dim3(256), 0, s, q, k, v, d_o, lse,
                        dsum, B, N, H, G, t_cap, sl2, scale, n_qblk, n_units, dq);
     hipLaunchKernelGGL(attn_bwd_dkv_kernel<128>, dim3(grid_k), dim3(256), 0, s, q, k, v, d_o, lse,
-                       dsum, B, N, H, G, t_cap, sl2, scale, dkv);
+                       dsum, B, N, H, G, t_cap, sl2, scale, dst);
   } else {
     hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, dim3(grid_q), dim3(256), 0, s, q, k, v, d_o, lse,
                        dsum, B, N, H, G, t_cap, sl2, scale, n_qblk, n_units, dq);
     hipLaunchKernelGGL(attn_bwd_dkv_kernel<64>, dim3(grid_k), dim3(256), 0, s, q, k, v, d_o, lse,
-                       dsum, B, N, H, G, t_cap, sl2, scale, dkv);
+                       dsum, B, N, H, G, t_cap, sl2, scale, dst);
+  }
+  if (hpg > 1) {
+    const int64_t n4 = static_cast<int64_t>(B) * N * 2 * G * dh / 4;
+    hipLaunchKernelGGL(sum_slices_kernel, dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256),
+                       0, s, part, hpg, n4, dkv);
   }
   return hipGetLastError();
 }

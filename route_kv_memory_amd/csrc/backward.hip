@@ -197,21 +197,20 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, i
 
 // ---------------------------------------------------------------------------
 // Fusion backward, one row per workgroup.  X_fused = l1 x + l2 L2 + l3 L3:
-//   dlam_i = <dxf, L_i>;  dx = l1 dxf (written);  dxf <- l2 dxf (in place,
-//   the EMA adjoint's input);  dm[blk] += l3 dxf / |S_t| for the retrieved
-//   blocks (atomics; dm is zeroed first).  L3 is re-formed from the means.
+//   dlam_i = <dxf, L_i> (L3 re-formed from the retrieved means), dx = l1 dxf
+//   (written).  The L2 and L3 parts (l2 dxf and l3 dxf / |S_t|) are taken by
+//   the EMA adjoint and the block gather straight from dxf and lambda.
 // ---------------------------------------------------------------------------
 template <typename T, int RMAX>
 __global__ __launch_bounds__(256) void fuse_bwd_kernel(
     const T* __restrict__ x, const float* __restrict__ l2, const float* __restrict__ means,
     int nb_cap, const int32_t* __restrict__ idx, const float* __restrict__ lam, int N, int D,
-    int R, float* __restrict__ dxf, float* __restrict__ dx, float* __restrict__ dm, int nbs,
-    float* __restrict__ dlam) {
+    int R, const float* __restrict__ dxf, float* __restrict__ dx, float* __restrict__ dlam) {
   __shared__ float red[3][4];
   const int64_t row = blockIdx.x;
   const int b = static_cast<int>(row / N);
   const int tid = threadIdx.x;
-  const float w1 = lam[row * 3 + 0], w2 = lam[row * 3 + 1], w3 = lam[row * 3 + 2];
+  const float w1 = lam[row * 3 + 0];
   int blk[RMAX], cnt = 0;
 #pragma unroll
   for (int i = 0; i < RMAX; ++i) {
@@ -220,7 +219,6 @@ __global__ __launch_bounds__(256) void fuse_bwd_kernel(
   }
   const float inv = cnt ? 1.0f / static_cast<float>(cnt) : 0.f;
   const float* mb = means + static_cast<int64_t>(b) * nb_cap * D;
-  float* dmb = dm + static_cast<int64_t>(b) * nbs * D;
   float a1 = 0.f, a2 = 0.f, a3 = 0.f;
   for (int c = tid; c < D; c += 256) {
     const int64_t o = row * D + c;
@@ -229,16 +227,10 @@ __global__ __launch_bounds__(256) void fuse_bwd_kernel(
 #pragma unroll
     for (int i = 0; i < RMAX; ++i)
       if (blk[i] >= 0) l3 += mb[static_cast<int64_t>(blk[i]) * D + c];
-    l3 *= inv;
     a1 = fmaf(gx, Elem<T>::to_f32(x[o]), a1);
     if (l2) a2 = fmaf(gx, l2[o], a2);  // null: L2 disabled (lambda_2 = 0)
-    a3 = fmaf(gx, l3, a3);
+    a3 = fmaf(gx, l3 * inv, a3);
     dx[o] = w1 * gx;
-    dxf[o] = w2 * gx;
-    const float g3 = w3 * gx * inv;
-#pragma unroll
-    for (int i = 0; i < RMAX; ++i)
-      if (blk[i] >= 0) atomicAdd(dmb + static_cast<int64_t>(blk[i]) * D + c, g3);
   }
   a1 = wave_sum(a1);
   a2 = wave_sum(a2);
@@ -253,6 +245,73 @@ __global__ __launch_bounds__(256) void fuse_bwd_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// The block means' adjoint without atomics: dm[b, blk] = sum over the tokens t
+// that retrieved blk (in token order) of lambda_3[t] / |S_t| * dxf[t].  One
+// workgroup per (block, sequence, 1024 channels): tokens are scanned in chunks
+// of 256 (only t >= (blk + 1) * Bs can retrieve blk), the retrieving ones
+// compacted into LDS in order, then summed four channels per thread.
+// ---------------------------------------------------------------------------
+template <int RMAX>
+__global__ __launch_bounds__(256) void block_gather_kernel(const float* __restrict__ dxf,
+                                                           const float* __restrict__ lam,
+                                                           const int32_t* __restrict__ idx,
+                                                           int N, int D, int R, int block,
+                                                           int nbs, float* __restrict__ dm) {
+  __shared__ int list_t[256];
+  __shared__ float list_w[256];
+  __shared__ int wave_cnt[4];
+  const int blk = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = (blockIdx.z * 256 + tid) * 4;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int t0 = (blk + 1) * block; t0 < N; t0 += 256) {
+    const int t = t0 + tid;
+    bool hit = false;
+    float w = 0.f;
+    if (t < N) {
+      const int64_t row = static_cast<int64_t>(b) * N + t;
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < RMAX; ++i) {
+        const int bi = i < R ? idx[row * R + i] : -1;
+        cnt += bi >= 0;
+        hit |= bi == blk;
+      }
+      if (hit) w = lam[row * 3 + 2] / static_cast<float>(cnt);
+    }
+    const uint64_t m = __ballot(hit);
+    if (lane == 0) wave_cnt[wave] = __popcll(m);
+    __syncthreads();
+    int base = 0, total = 0;
+    for (int k = 0; k < 4; ++k) {
+      base += k < wave ? wave_cnt[k] : 0;
+      total += wave_cnt[k];
+    }
+    if (hit) {
+      const int pos = base + __popcll(m & ((static_cast<uint64_t>(1) << lane) - 1));
+      list_t[pos] = t;
+      list_w[pos] = w;
+    }
+    __syncthreads();
+    if (c < D) {
+      for (int k = 0; k < total; ++k) {
+        const float* src = dxf + (static_cast<int64_t>(b) * N + list_t[k]) * D + c;
+        const float wk = list_w[k];
+        const float4 v = *reinterpret_cast<const float4*>(src);
+        acc[0] = fmaf(wk, v.x, acc[0]);
+        acc[1] = fmaf(wk, v.y, acc[1]);
+        acc[2] = fmaf(wk, v.z, acc[2]);
+        acc[3] = fmaf(wk, v.w, acc[3]);
+      }
+    }
+    __syncthreads();
+  }
+  if (c < D)
+    *reinterpret_cast<float4*>(dm + (static_cast<int64_t>(b) * nbs + blk) * D + c) =
+        make_float4(acc[0], acc[1], acc[2], acc[3]);
+}
+
+// ---------------------------------------------------------------------------
 // EMA adjoint: g_t = u_t + beta g_{t+1} (from the last token back), dx_t +=
 // (1 - beta) g_t; then the block means' spread dx_t += dm[t / Bs] / Bs for
 // tokens of complete blocks.  Chunks of kBwdChunk tokens: pass 1 sums each
@@ -261,7 +320,9 @@ __global__ __launch_bounds__(256) void fuse_bwd_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kBwdChunk = 64;
 
-__global__ __launch_bounds__(256) void ema_adj_pass1(const float* __restrict__ u, int N, int D,
+// u_t = lambda_2[t] * dxf[t] (lam2 = &lambda[1], stride 3)
+__global__ __launch_bounds__(256) void ema_adj_pass1(const float* __restrict__ u,
+                                                     const float* __restrict__ lam2, int N, int D,
                                                      int n_chunks, float beta,
                                                      float* __restrict__ part) {
   const int c = blockIdx.x * 256 + threadIdx.x;
@@ -269,7 +330,10 @@ __global__ __launch_bounds__(256) void ema_adj_pass1(const float* __restrict__ u
   if (c >= D) return;
   const int t0 = ch * kBwdChunk, t1 = min(N, t0 + kBwdChunk);
   float g = 0.f;
-  for (int t = t1 - 1; t >= t0; --t) g = fmaf(beta, g, u[(static_cast<int64_t>(b) * N + t) * D + c]);
+  for (int t = t1 - 1; t >= t0; --t) {
+    const int64_t row = static_cast<int64_t>(b) * N + t;
+    g = fmaf(beta, g, lam2[row * 3] * u[row * D + c]);
+  }
   part[(static_cast<int64_t>(b) * n_chunks + ch) * D + c] = g;
 }
 
@@ -290,6 +354,7 @@ __global__ __launch_bounds__(256) void ema_adj_pass2(float* __restrict__ part, i
 }
 
 __global__ __launch_bounds__(256) void ema_adj_pass3(const float* __restrict__ u,
+                                                     const float* __restrict__ lam2,
                                                      const float* __restrict__ part,
                                                      const float* __restrict__ dm, int nbs,
                                                      int N, int D, int n_chunks, int block,
@@ -302,8 +367,8 @@ __global__ __launch_bounds__(256) void ema_adj_pass3(const float* __restrict__ u
   const float omb = 1.0f - beta, inv_bs = 1.0f / static_cast<float>(block);
   float g = part[(static_cast<int64_t>(b) * n_chunks + ch) * D + c];
   for (int t = t1 - 1; t >= t0; --t) {
-    const int64_t o = (static_cast<int64_t>(b) * N + t) * D + c;
-    g = fmaf(beta, g, u[o]);
+    const int64_t row = static_cast<int64_t>(b) * N + t, o = row * D + c;
+    g = fmaf(beta, g, lam2[row * 3] * u[o]);
     float add = omb * g;
     if (t < n_full) add += dm[(static_cast<int64_t>(b) * nbs + t / block) * D + c] * inv_bs;
     dx[o] += add;
@@ -419,21 +484,41 @@ hipError_t fill_zero(float* p, int64_t n, hipStream_t s) {
 
 template <typename T>
 hipError_t fuse_bwd(const T* x, const float* l2, const float* means, int nb_cap,
-                    const int32_t* idx, const float* lam, int B, int N, int D, int R, float* dxf,
-                    float* dx, float* dm, int nbs, float* dlam, hipStream_t s) {
+                    const int32_t* idx, const float* lam, int B, int N, int D, int R,
+                    const float* dxf, float* dx, float* dlam, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(B) * N));
   if (R <= 4)
     hipLaunchKernelGGL((fuse_bwd_kernel<T, 4>), grid, dim3(256), 0, s, x, l2, means, nb_cap, idx,
-                       lam, N, D, R, dxf, dx, dm, nbs, dlam);
+                       lam, N, D, R, dxf, dx, dlam);
   else if (R <= 8)
     hipLaunchKernelGGL((fuse_bwd_kernel<T, 8>), grid, dim3(256), 0, s, x, l2, means, nb_cap, idx,
-                       lam, N, D, R, dxf, dx, dm, nbs, dlam);
+                       lam, N, D, R, dxf, dx, dlam);
   else if (R <= 16)
     hipLaunchKernelGGL((fuse_bwd_kernel<T, 16>), grid, dim3(256), 0, s, x, l2, means, nb_cap, idx,
-                       lam, N, D, R, dxf, dx, dm, nbs, dlam);
+                       lam, N, D, R, dxf, dx, dlam);
   else
     hipLaunchKernelGGL((fuse_bwd_kernel<T, 32>), grid, dim3(256), 0, s, x, l2, means, nb_cap, idx,
-                       lam, N, D, R, dxf, dx, dm, nbs, dlam);
+                       lam, N, D, R, dxf, dx, dlam);
+  return hipGetLastError();
+}
+
+hipError_t block_gather(const float* dxf, const float* lam, const int32_t* idx, int B, int N,
+                        int D, int R, int block, int nbs, float* dm, hipStream_t s) {
+  const int n_blocks = N / block;  // complete blocks: the only ones retrieved
+  if (n_blocks == 0) return hipSuccess;
+  const dim3 grid(n_blocks, B, (D + 1023) / 1024);
+  if (R <= 4)
+    hipLaunchKernelGGL(block_gather_kernel<4>, grid, dim3(256), 0, s, dxf, lam, idx, N, D, R,
+                       block, nbs, dm);
+  else if (R <= 8)
+    hipLaunchKernelGGL(block_gather_kernel<8>, grid, dim3(256), 0, s, dxf, lam, idx, N, D, R,
+                       block, nbs, dm);
+  else if (R <= 16)
+    hipLaunchKernelGGL(block_gather_kernel<16>, grid, dim3(256), 0, s, dxf, lam, idx, N, D, R,
+                       block, nbs, dm);
+  else
+    hipLaunchKernelGGL(block_gather_kernel<32>, grid, dim3(256), 0, s, dxf, lam, idx, N, D, R,
+                       block, nbs, dm);
   return hipGetLastError();
 }
 
@@ -441,14 +526,16 @@ size_t ema_adj_ws_bytes(int B, int N, int D) {
   return sizeof(float) * static_cast<size_t>(B) * ((N + kBwdChunk - 1) / kBwdChunk) * D;
 }
 
-hipError_t ema_adjoint_add(const float* u, const float* dm, int nbs, int B, int N, int D,
-                           int block, float beta, float* part, float* dx, hipStream_t s) {
+hipError_t ema_adjoint_add(const float* u, const float* lam, const float* dm, int nbs, int B,
+                           int N, int D, int block, float beta, float* part, float* dx,
+                           hipStream_t s) {
   const int n_chunks = (N + kBwdChunk - 1) / kBwdChunk;
   const int cx = (D + 255) / 256;
-  hipLaunchKernelGGL(ema_adj_pass1, dim3(cx, n_chunks, B), dim3(256), 0, s, u, N, D, n_chunks,
-                     beta, part);
+  hipLaunchKernelGGL(ema_adj_pass1, dim3(cx, n_chunks, B), dim3(256), 0, s, u, lam + 1, N, D,
+                     n_chunks, beta, part);
   hipLaunchKernelGGL(ema_adj_pass2, dim3(cx, B), dim3(256), 0, s, part, N, D, n_chunks, beta);
-  hipLaunchKernelGGL(ema_adj_pass3, dim3(cx, n_chunks, B), dim3(256), 0, s, u, part, dm, nbs,
+  hipLaunchKernelGGL(ema_adj_pass3, dim3(cx, n_chunks, B), dim3(256), 0, s, u, lam + 1, part, dm,
+                     nbs,
                      N, D, n_chunks, block, beta, dx);
   return hipGetLastError();
 }
@@ -469,8 +556,8 @@ hipError_t router_bwd(const float* lam, const float* dlam, const float* pre, con
                                        float*, hipStream_t);                                      \
   template hipError_t convert<float, T>(const float*, int64_t, T*, hipStream_t);                 \
   template hipError_t fuse_bwd<T>(const T*, const float*, const float*, int, const int32_t*,      \
-                                  const float*, int, int, int, int, float*, float*, float*, int,  \
-                                  float*, hipStream_t);                                           \
+                                  const float*, int, int, int, int, const float*, float*, float*, \
+                                  hipStream_t);                                                   \
   template hipError_t router_bwd<T>(const float*, const float*, const float*, const T*, int,      \
                                     int64_t, Routing, float*, T*, float*, hipStream_t);
 MKA_BWD_INST(float)

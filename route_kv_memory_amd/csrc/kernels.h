@@ -116,9 +116,11 @@ hipError_t attn_bwd_rows(const T* q, const T* k, const T* v, const T* d_o, const
                          const float* dsum, int B, int N, int H, int G, int dh, int64_t t_cap,
                          float* dq, float* dkv, hipStream_t s);
 // The same on the matrix cores (bf16), from the forward's log-sum-exp.
+// ``part``: attn_bwd_mfma_ws_bytes() of float32 scratch (per-head dK/dV slices).
+size_t attn_bwd_mfma_ws_bytes(int B, int N, int H, int G, int dh);
 hipError_t attn_bwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* d_o,
                          const float* lse, const float* dsum, int B, int N, int H, int G, int dh,
-                         int64_t t_cap, float* dq, float* dkv, hipStream_t s);
+                         int64_t t_cap, float* dq, float* dkv, float* part, hipStream_t s);
 template <typename TS, typename TD>
 hipError_t transpose(const TS* src, int64_t lds_, int R, int C, int Rp, int64_t ldd, TD* dst,
                      hipStream_t s);
@@ -127,11 +129,16 @@ hipError_t convert(const TS* src, int64_t n, TD* dst, hipStream_t s);
 hipError_t fill_zero(float* p, int64_t n, hipStream_t s);
 template <typename T>
 hipError_t fuse_bwd(const T* x, const float* l2, const float* means, int nb_cap,
-                    const int32_t* idx, const float* lam, int B, int N, int D, int R, float* dxf,
-                    float* dx, float* dm, int nbs, float* dlam, hipStream_t s);
+                    const int32_t* idx, const float* lam, int B, int N, int D, int R,
+                    const float* dxf, float* dx, float* dlam, hipStream_t s);
+// dm [B, nbs, D]: rows of the complete blocks (D % 4 == 0).
+hipError_t block_gather(const float* dxf, const float* lam, const int32_t* idx, int B, int N,
+                        int D, int R, int block, int nbs, float* dm, hipStream_t s);
 size_t ema_adj_ws_bytes(int B, int N, int D);
-hipError_t ema_adjoint_add(const float* u, const float* dm, int nbs, int B, int N, int D,
-                           int block, float beta, float* part, float* dx, hipStream_t s);
+// dx += the EMA's adjoint of lambda_2 * dxf, plus dm spread over its blocks' tokens.
+hipError_t ema_adjoint_add(const float* u, const float* lam, const float* dm, int nbs, int B,
+                           int N, int D, int block, float beta, float* part, float* dx,
+                           hipStream_t s);
 template <typename T>
 hipError_t router_bwd(const float* lam, const float* dlam, const float* pre, const T* w2, int r,
                       int64_t M, Routing rt, float* dz, T* dpre, float* dw2, hipStream_t s);

@@ -499,7 +499,7 @@ FullWs full_layout(const mka_dims* d, bool decode, int64_t cache_len) {
 // type's product operands (transposed ones padded to Mp = M rounded up to 32
 // tokens, the products' reduction dimension).
 struct BwdWs {
-  size_t dsum, dq, dkv, dxf, dlam, dz, dm, part, pre;           // float32
+  size_t dsum, dq, dkv, dxf, dlam, dz, dm, part, pre, heads;    // float32
   size_t dkv_a, dkv_t, wkv_t, xf, xf_t, dpre, dpre_t, q_t, wr1_t, wq_t, dq_a, dq_t, x_t;  // dtype
   size_t total;
   int Mp, nbs;
@@ -529,6 +529,9 @@ BwdWs bwd_layout(const mka_dims* d) {
   w.dm = take(f * d->batch * w.nbs * D);
   w.part = take(ema_adj_ws_bytes(d->batch, d->seq, d->d_model));
   w.pre = take(f * M * r);
+  w.heads = bf ? take(attn_bwd_mfma_ws_bytes(d->batch, d->seq, d->n_heads, d->n_kv_heads,
+                                             d->head_dim))
+               : 0;
   w.dkv_a = bf ? take(el * M * 2 * kvw) : 0;
   w.dkv_t = take(el * 2 * kvw * Mp);
   w.wkv_t = take(el * D * 2 * kvw);
@@ -594,7 +597,7 @@ int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const
   if constexpr (kBf)
     MKA_LAUNCH("bwd/attn", attn_bwd_mfma(q, static_cast<const T*>(st->k_cache),
                                          static_cast<const T*>(st->v_cache), d_o, fwd->lse, dsum,
-                                         B, N, H, G, dh, st->t_cap, dq, dkv, s));
+                                         B, N, H, G, dh, st->t_cap, dq, dkv, F(L.heads), s));
   else
     MKA_LAUNCH("bwd/attn", attn_bwd_rows<T>(q, static_cast<const T*>(st->k_cache),
                                             static_cast<const T*>(st->v_cache), d_o, fwd->lse,
@@ -617,12 +620,16 @@ int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const
   MKA_LAUNCH("bwd/dwv", gemm_t<T>(dkv_t + static_cast<size_t>(kvw) * Mp, Mp, xf_t, kvw, D, Mp,
                                   EpiStore<float>{gr->dw_v, D}, s));
   // the fusion, the EMA's adjoint and the block means' adjoint
-  MKA_LAUNCH("bwd/zero", fill_zero(dm, static_cast<int64_t>(B) * L.nbs * D, s));
   MKA_LAUNCH("bwd/fuse", fuse_bwd<T>(x, rt.l2() ? fwd->l2 : nullptr, st->block_means, st->nb_cap,
                                      rt.l3() ? fwd->idx : nullptr, fwd->lambda, B, N, D,
-                                     rt.l3() ? d->top_r : 0, dxf, gr->dx, dm, L.nbs, dlam, s));
-  MKA_LAUNCH("bwd/ema", ema_adjoint_add(dxf, dm, L.nbs, B, N, D, d->block, d->ema_decay, part,
-                                        gr->dx, s));
+                                     rt.l3() ? d->top_r : 0, dxf, gr->dx, dlam, s));
+  if (rt.l3())
+    MKA_LAUNCH("bwd/blocks", block_gather(dxf, fwd->lambda, fwd->idx, B, N, D, d->top_r, d->block,
+                                          L.nbs, dm, s));
+  else
+    MKA_LAUNCH("bwd/zero", fill_zero(dm, static_cast<int64_t>(B) * L.nbs * D, s));
+  MKA_LAUNCH("bwd/ema", ema_adjoint_add(dxf, fwd->lambda, dm, L.nbs, B, N, D, d->block,
+                                        d->ema_decay, part, gr->dx, s));
   // router: dz, dW_r2, dpre; dW_r1 = dpre^T q; dq += dpre W_r1
   if (rt.learned()) {
     MKA_LAUNCH("bwd/pre", gemm_t<T>(q, qw, wr1, M, r, qw, EpiStore<float>{pre, r}, s));
