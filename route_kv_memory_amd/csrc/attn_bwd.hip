@@ -366,6 +366,12 @@ __global__ __launch_bounds__(256) void sum_slices_kernel(const float* __restrict
   reinterpret_cast<float4*>(out)[i] = acc;
 }
 
+hipError_t sum_slices(const float* part, int n_slices, int64_t n4, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(sum_slices_kernel, dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0,
+                     s, part, n_slices, n4, out);
+  return hipGetLastError();
+}
+
 size_t attn_bwd_mfma_ws_bytes(int B, int N, int H, int G, int dh) {
   return H / G > 1 ? sizeof(float) * static_cast<size_t>(H / G) * B * N * 2 * G * dh : 0;
 }

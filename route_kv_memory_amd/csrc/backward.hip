@@ -223,10 +223,14 @@ __global__ __launch_bounds__(256) void fuse_bwd_kernel(
   for (int c = tid; c < D; c += 256) {
     const int64_t o = row * D + c;
     const float gx = dxf[o];
+    // every retrieved row is loaded (unfilled slots read block 0 and are not
+    // added), so the loads are in flight together
+    float m[RMAX];
+#pragma unroll
+    for (int i = 0; i < RMAX; ++i) m[i] = mb[static_cast<int64_t>(max(blk[i], 0)) * D + c];
     float l3 = 0.f;
 #pragma unroll
-    for (int i = 0; i < RMAX; ++i)
-      if (blk[i] >= 0) l3 += mb[static_cast<int64_t>(blk[i]) * D + c];
+    for (int i = 0; i < RMAX; ++i) l3 += blk[i] >= 0 ? m[i] : 0.f;
     a1 = fmaf(gx, Elem<T>::to_f32(x[o]), a1);
     if (l2) a2 = fmaf(gx, l2[o], a2);  // null: L2 disabled (lambda_2 = 0)
     a3 = fmaf(gx, l3 * inv, a3);
@@ -247,28 +251,37 @@ __global__ __launch_bounds__(256) void fuse_bwd_kernel(
 // ---------------------------------------------------------------------------
 // The block means' adjoint without atomics: dm[b, blk] = sum over the tokens t
 // that retrieved blk (in token order) of lambda_3[t] / |S_t| * dxf[t].  One
-// workgroup per (block, sequence, 1024 channels): tokens are scanned in chunks
-// of 256 (only t >= (blk + 1) * Bs can retrieve blk), the retrieving ones
+// workgroup per (block, sequence, 1024 channels, range of kGatherTokens
+// tokens), writing that range's partial sum (summed over the ranges in order
+// afterwards): popular blocks are retrieved by thousands of tokens, so one
+// workgroup per block would be a long serial walk.  Tokens are scanned 256 at
+// a time (only t >= (blk + 1) * Bs can retrieve blk), the retrieving ones
 // compacted into LDS in order, then summed four channels per thread.
 // ---------------------------------------------------------------------------
+constexpr int kGatherTokens = 512;
+
 template <int RMAX>
 __global__ __launch_bounds__(256) void block_gather_kernel(const float* __restrict__ dxf,
                                                            const float* __restrict__ lam,
                                                            const int32_t* __restrict__ idx,
                                                            int N, int D, int R, int block,
-                                                           int nbs, float* __restrict__ dm) {
+                                                           int nbs, int n_slices,
+                                                           float* __restrict__ part) {
   __shared__ int list_t[256];
   __shared__ float list_w[256];
   __shared__ int wave_cnt[4];
-  const int blk = blockIdx.x, b = blockIdx.y;
+  const int blk = blockIdx.x, b = blockIdx.y, B = gridDim.y;
+  const int slice = blockIdx.z % n_slices, range = blockIdx.z / n_slices;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = (blockIdx.z * 256 + tid) * 4;
+  const int c = (slice * 256 + tid) * 4;
+  const int t_lo = max((blk + 1) * block, range * kGatherTokens);
+  const int t_hi = min(N, (range + 1) * kGatherTokens);
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int t0 = (blk + 1) * block; t0 < N; t0 += 256) {
+  for (int t0 = t_lo; t0 < t_hi; t0 += 256) {
     const int t = t0 + tid;
     bool hit = false;
     float w = 0.f;
-    if (t < N) {
+    if (t < t_hi) {
       const int64_t row = static_cast<int64_t>(b) * N + t;
       int cnt = 0;
 #pragma unroll
@@ -294,20 +307,30 @@ __global__ __launch_bounds__(256) void block_gather_kernel(const float* __restri
     }
     __syncthreads();
     if (c < D) {
-      for (int k = 0; k < total; ++k) {
-        const float* src = dxf + (static_cast<int64_t>(b) * N + list_t[k]) * D + c;
-        const float wk = list_w[k];
-        const float4 v = *reinterpret_cast<const float4*>(src);
-        acc[0] = fmaf(wk, v.x, acc[0]);
-        acc[1] = fmaf(wk, v.y, acc[1]);
-        acc[2] = fmaf(wk, v.z, acc[2]);
-        acc[3] = fmaf(wk, v.w, acc[3]);
+      // four listed tokens per step, their loads issued together (a slot past
+      // the list reads the first token with weight 0); the sum stays in list order
+      for (int k0 = 0; k0 < total; k0 += 4) {
+        float4 v[4];
+        float wk[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int k = k0 + u < total ? k0 + u : 0;
+          wk[u] = k0 + u < total ? list_w[k] : 0.f;
+          v[u] = *reinterpret_cast<const float4*>(dxf + (static_cast<int64_t>(b) * N + list_t[k]) * D + c);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          acc[0] = fmaf(wk[u], v[u].x, acc[0]);
+          acc[1] = fmaf(wk[u], v[u].y, acc[1]);
+          acc[2] = fmaf(wk[u], v[u].z, acc[2]);
+          acc[3] = fmaf(wk[u], v[u].w, acc[3]);
+        }
       }
     }
     __syncthreads();
   }
   if (c < D)
-    *reinterpret_cast<float4*>(dm + (static_cast<int64_t>(b) * nbs + blk) * D + c) =
+    *reinterpret_cast<float4*>(part + ((static_cast<int64_t>(range) * B + b) * nbs + blk) * D + c) =
         make_float4(acc[0], acc[1], acc[2], acc[3]);
 }
 
@@ -502,24 +525,27 @@ hipError_t fuse_bwd(const T* x, const float* l2, const float* means, int nb_cap,
   return hipGetLastError();
 }
 
+size_t block_gather_ws_bytes(int B, int N, int D, int block) {
+  return sizeof(float) * static_cast<size_t>((N + kGatherTokens - 1) / kGatherTokens) * B *
+         (N / block + 1) * D;
+}
+
 hipError_t block_gather(const float* dxf, const float* lam, const int32_t* idx, int B, int N,
-                        int D, int R, int block, int nbs, float* dm, hipStream_t s) {
+                        int D, int R, int block, int nbs, float* part, float* dm, hipStream_t s) {
   const int n_blocks = N / block;  // complete blocks: the only ones retrieved
   if (n_blocks == 0) return hipSuccess;
-  const dim3 grid(n_blocks, B, (D + 1023) / 1024);
-  if (R <= 4)
-    hipLaunchKernelGGL(block_gather_kernel<4>, grid, dim3(256), 0, s, dxf, lam, idx, N, D, R,
-                       block, nbs, dm);
-  else if (R <= 8)
-    hipLaunchKernelGGL(block_gather_kernel<8>, grid, dim3(256), 0, s, dxf, lam, idx, N, D, R,
-                       block, nbs, dm);
-  else if (R <= 16)
-    hipLaunchKernelGGL(block_gather_kernel<16>, grid, dim3(256), 0, s, dxf, lam, idx, N, D, R,
-                       block, nbs, dm);
-  else
-    hipLaunchKernelGGL(block_gather_kernel<32>, grid, dim3(256), 0, s, dxf, lam, idx, N, D, R,
-                       block, nbs, dm);
-  return hipGetLastError();
+  const int n_slices = (D + 1023) / 1024, n_ranges = (N + kGatherTokens - 1) / kGatherTokens;
+  const dim3 grid(n_blocks, B, n_slices * n_ranges);
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, dxf, lam, idx, N, D, R, block, nbs,
+                       n_slices, part);
+  };
+  if (R <= 4) launch(block_gather_kernel<4>);
+  else if (R <= 8) launch(block_gather_kernel<8>);
+  else if (R <= 16) launch(block_gather_kernel<16>);
+  else launch(block_gather_kernel<32>);
+  // rows of blocks >= n_blocks stay unset in every range: only rows < n_blocks are read
+  return sum_slices(part, n_ranges, static_cast<int64_t>(B) * nbs * D / 4, dm, s);
 }
 
 size_t ema_adj_ws_bytes(int B, int N, int D) {

@@ -131,9 +131,13 @@ template <typename T>
 hipError_t fuse_bwd(const T* x, const float* l2, const float* means, int nb_cap,
                     const int32_t* idx, const float* lam, int B, int N, int D, int R,
                     const float* dxf, float* dx, float* dlam, hipStream_t s);
-// dm [B, nbs, D]: rows of the complete blocks (D % 4 == 0).
+// dm [B, nbs, D]: rows of the complete blocks (D % 4 == 0), from per-range
+// partials in ``part`` (block_gather_ws_bytes()).
+size_t block_gather_ws_bytes(int B, int N, int D, int block);
 hipError_t block_gather(const float* dxf, const float* lam, const int32_t* idx, int B, int N,
-                        int D, int R, int block, int nbs, float* dm, hipStream_t s);
+                        int D, int R, int block, int nbs, float* part, float* dm, hipStream_t s);
+// out[i] = sum over k < n_slices of part[k * n4 + i] (float4 units, in slice order).
+hipError_t sum_slices(const float* part, int n_slices, int64_t n4, float* out, hipStream_t s);
 size_t ema_adj_ws_bytes(int B, int N, int D);
 // dx += the EMA's adjoint of lambda_2 * dxf, plus dm spread over its blocks' tokens.
 hipError_t ema_adjoint_add(const float* u, const float* lam, const float* dm, int nbs, int B,

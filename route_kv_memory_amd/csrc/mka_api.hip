@@ -499,7 +499,7 @@ FullWs full_layout(const mka_dims* d, bool decode, int64_t cache_len) {
 // type's product operands (transposed ones padded to Mp = M rounded up to 32
 // tokens, the products' reduction dimension).
 struct BwdWs {
-  size_t dsum, dq, dkv, dxf, dlam, dz, dm, part, pre, heads;    // float32
+  size_t dsum, dq, dkv, dxf, dlam, dz, dm, part, pre, heads, gather;  // float32
   size_t dkv_a, dkv_t, wkv_t, xf, xf_t, dpre, dpre_t, q_t, wr1_t, wq_t, dq_a, dq_t, x_t;  // dtype
   size_t total;
   int Mp, nbs;
@@ -529,6 +529,7 @@ BwdWs bwd_layout(const mka_dims* d) {
   w.dm = take(f * d->batch * w.nbs * D);
   w.part = take(ema_adj_ws_bytes(d->batch, d->seq, d->d_model));
   w.pre = take(f * M * r);
+  w.gather = take(block_gather_ws_bytes(d->batch, d->seq, d->d_model, d->block));
   w.heads = bf ? take(attn_bwd_mfma_ws_bytes(d->batch, d->seq, d->n_heads, d->n_kv_heads,
                                              d->head_dim))
                : 0;
@@ -625,7 +626,7 @@ int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const
                                      rt.l3() ? d->top_r : 0, dxf, gr->dx, dlam, s));
   if (rt.l3())
     MKA_LAUNCH("bwd/blocks", block_gather(dxf, fwd->lambda, fwd->idx, B, N, D, d->top_r, d->block,
-                                          L.nbs, dm, s));
+                                          L.nbs, F(L.gather), dm, s));
   else
     MKA_LAUNCH("bwd/zero", fill_zero(dm, static_cast<int64_t>(B) * L.nbs * D, s));
   MKA_LAUNCH("bwd/ema", ema_adjoint_add(dxf, fwd->lambda, dm, L.nbs, B, N, D, d->block,
