@@ -296,8 +296,29 @@ def bench_train(s, steps, warmup, settle_ms=0.0):
         step(evs[k])
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps * 1e3
+    # the attention backward alone (mka_attn_backward), for its roofline
+    from route_kv_memory_amd import mka
+
+    d = layer.dims(s.seq)
+    dq = torch.empty(s.batch, s.seq, s.n_heads, s.head_dim, device="cuda")
+    dkv = torch.empty(s.batch, s.seq, 2, s.n_kv_heads, s.head_dim, device="cuda")
+    ws = torch.empty(max(256, mka.mka_workspace_bytes(d, mka.MKA_OP_ATTN_BACKWARD)),
+                     dtype=torch.uint8, device="cuda")
+
+    def attn_bwd():
+        mka.mka_attn_backward(d, out["q"], layer.st["k_cache"], layer.st["v_cache"], layer.t_cap,
+                              out["o"], out["lse"], d_o, dq, dkv, ws, ws.numel(), stream)
+
+    attn_bwd()
+    a_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    a_ev[0].record(stream)
+    for _ in range(steps):
+        attn_bwd()
+    a_ev[1].record(stream)
+    torch.cuda.synchronize()
     return dict(ms=wall, fwd_ms=float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
-                bwd_ms=float(np.mean([e[1].elapsed_time(e[2]) for e in evs])))
+                bwd_ms=float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
+                attn_bwd_ms=a_ev[0].elapsed_time(a_ev[1]) / steps)
 
 
 def bench_prefill_paged(s, steps, warmup, page_size, settle_ms=0.0):
@@ -618,8 +639,19 @@ def main():
         tr = bench_train(s, args.steps, args.warmup, args.settle_ms)
         log(f"training step: {tr['ms']:.3f} ms (forward {tr['fwd_ms']:.3f}, backward "
             f"{tr['bwd_ms']:.3f})")
+        # the four products of the attention gradient (dV, dP, dQ, dK), 2*dh flops
+        # per causal pair each; recomputing the scores is not counted
+        bwd_flops = 2.0 * flops["attn"]
+        bwd_ach = bwd_flops / (tr["attn_bwd_ms"] * 1e-3)
         line["train"] = {"tokens_per_s": tokens / (tr["ms"] * 1e-3), "ms_per_step": tr["ms"],
                          "forward_ms": tr["fwd_ms"], "backward_ms": tr["bwd_ms"],
+                         "attn_backward_ms": tr["attn_bwd_ms"],
+                         "roofline": {"kernel": "attn_bwd_dkv_kernel + attn_bwd_dq_kernel",
+                                      "bound": "mfma", "achieved": bwd_ach / 1e12,
+                                      "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                                      "frac": bwd_ach / PEAK_BF16_FLOPS,
+                                      "onbox_peak": onbox["mfma_bf16_tflops"],
+                                      "frac_onbox": bwd_ach / 1e12 / onbox["mfma_bf16_tflops"]},
                          "note": "mka_prefill (saving log-sum-exp) + mka_backward: gradients of "
                                  "x and every weight, fp32"}
     if args.paged:

@@ -58,7 +58,8 @@ enum {
 /* Workspace-using operations, for mka_workspace_bytes(). */
 enum { MKA_OP_EMA_SCAN = 0, MKA_OP_FUSE_KV = 1, MKA_OP_ATTN_DECODE = 2, MKA_OP_PREFILL = 3,
        MKA_OP_DECODE_STEP = 4, MKA_OP_RETRIEVE = 5, MKA_OP_INDEX = 6, MKA_OP_ROUTE = 7,
-       MKA_OP_FULL_PREFILL = 8, MKA_OP_FULL_DECODE_STEP = 9, MKA_OP_BACKWARD = 10 };
+       MKA_OP_FULL_PREFILL = 8, MKA_OP_FULL_DECODE_STEP = 9, MKA_OP_BACKWARD = 10,
+       MKA_OP_ATTN_BACKWARD = 11 };
 
 /* Routing variant (mka_dims.route_mode) and enabled tiers (mka_dims.tiers):
  * the ablations of the abstract page, Table 10 (fixed lambda = 1/3, hard
@@ -332,6 +333,15 @@ int mka_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_wei
  *   ws >= mka_workspace_bytes(d, MKA_OP_BACKWARD, 0) bytes
  * bf16 layers need router_hidden % 32 == 0 (MKA_ERR_UNSUPPORTED otherwise); a
  * paged state is MKA_ERR_UNSUPPORTED. */
+/* The attention part of the backward alone (causal GQA over a contiguous
+ * cache, rows 0 .. seq-1, pos0 = 0), as mka_backward runs it:
+ *   dq [B, seq, H, dh] and dkv [B, seq, 2, G, dh] (K part, then V part) float32
+ *   (written), from q, k_cache, v_cache, o and lse of the forward and d_o.
+ *   ws >= mka_workspace_bytes(d, MKA_OP_ATTN_BACKWARD, 0) bytes. */
+int mka_attn_backward(const mka_dims* d, const void* q, const void* k_cache, const void* v_cache,
+                      int64_t t_cap, const void* o, const float* lse, const void* d_o, float* dq,
+                      float* dkv, void* ws, size_t ws_bytes, void* stream);
+
 typedef struct mka_grads {
   float* dx;
   float* dw_q;

@@ -564,6 +564,31 @@ hipError_t gemm_t(const T* a, int lda, const T* b, int M, int N, int K, const Ep
 }
 
 template <typename T>
+int attn_backward_steps(const mka_dims* d, const T* q, const T* kc, const T* vc, int64_t t_cap,
+                        const T* o, const float* lse, const T* d_o, float* dq, float* dkv,
+                        float* dsum, float* heads, hipStream_t s) {
+  const int B = d->batch, N = d->seq, H = d->n_heads, G = d->n_kv_heads, dh = d->head_dim;
+  MKA_LAUNCH("bwd/prep", attn_bwd_prep<T>(o, d_o, static_cast<int64_t>(rows_of(d)) * H, dh, dsum,
+                                          s));
+  if constexpr (std::is_same<T, bf16_t>::value)
+    MKA_LAUNCH("bwd/attn",
+               attn_bwd_mfma(q, kc, vc, d_o, lse, dsum, B, N, H, G, dh, t_cap, dq, dkv, heads, s));
+  else
+    MKA_LAUNCH("bwd/attn",
+               attn_bwd_rows<T>(q, kc, vc, d_o, lse, dsum, B, N, H, G, dh, t_cap, dq, dkv, s));
+  return MKA_OK;
+}
+
+// Workspace of the attention backward alone: D, then the per-head dK/dV slices.
+size_t attn_bwd_ws(const mka_dims* d) {
+  const size_t dsum = round256(sizeof(float) * rows_of(d) * d->n_heads);
+  return dsum + (d->dtype == MKA_BF16 ? round256(attn_bwd_mfma_ws_bytes(
+                                            d->batch, d->seq, d->n_heads, d->n_kv_heads,
+                                            d->head_dim))
+                                      : 0);
+}
+
+template <typename T>
 int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const mka_state* st,
                   const mka_outputs* fwd, const void* d_o_, const mka_grads* gr, char* ws,
                   hipStream_t s) {
@@ -594,15 +619,10 @@ int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const
   const T* dq_a = kBf ? E(L.dq_a) : reinterpret_cast<const T*>(dq);
 
   // attention: D = rowsum(dO * O), then dq, dK, dV
-  MKA_LAUNCH("bwd/prep", attn_bwd_prep<T>(o, d_o, static_cast<int64_t>(M) * H, dh, dsum, s));
-  if constexpr (kBf)
-    MKA_LAUNCH("bwd/attn", attn_bwd_mfma(q, static_cast<const T*>(st->k_cache),
-                                         static_cast<const T*>(st->v_cache), d_o, fwd->lse, dsum,
-                                         B, N, H, G, dh, st->t_cap, dq, dkv, F(L.heads), s));
-  else
-    MKA_LAUNCH("bwd/attn", attn_bwd_rows<T>(q, static_cast<const T*>(st->k_cache),
-                                            static_cast<const T*>(st->v_cache), d_o, fwd->lse,
-                                            dsum, B, N, H, G, dh, st->t_cap, dq, dkv, s));
+  int rc = attn_backward_steps<T>(d, q, static_cast<const T*>(st->k_cache),
+                                  static_cast<const T*>(st->v_cache), st->t_cap, o, fwd->lse, d_o,
+                                  dq, dkv, dsum, F(L.heads), s);
+  if (rc) return rc;
   // [K|V] = X_fused [W_k|W_v]^T: dX_fused = dKV [W_k; W_v]; dW = dKV^T X_fused
   MKA_LAUNCH("bwd/t", (transpose<T, T>(wk, D, kvw, D, kvw, 2 * kvw, wkv_t, s)));
   MKA_LAUNCH("bwd/t", (transpose<T, T>(wv, D, kvw, D, kvw, 2 * kvw, wkv_t + kvw, s)));
@@ -709,6 +729,7 @@ size_t mka_workspace_bytes(const mka_dims* d, int op, int64_t cache_len) {
       return d->seq == 1 && cache_len > 0 ? decode_layout(d, cache_len).total : 0;
     case MKA_OP_FULL_PREFILL: return full_layout(d, false, 0).total;
     case MKA_OP_BACKWARD: return bwd_layout(d).total;
+    case MKA_OP_ATTN_BACKWARD: return attn_bwd_ws(d);
     case MKA_OP_FULL_DECODE_STEP:
       return d->seq == 1 && cache_len > 0 ? full_layout(d, true, cache_len).total : 0;
     default: return 0;
@@ -1174,6 +1195,32 @@ int mka_backward(const mka_dims* d, const void* x, const mka_weights* w, const m
   char* base = static_cast<char*>(ws);
   if (d->dtype == MKA_BF16) return backward_body<bf16_t>(d, x, w, st, fwd, d_o, g, base, s);
   return backward_body<float>(d, x, w, st, fwd, d_o, g, base, s);
+}
+
+int mka_attn_backward(const mka_dims* d, const void* q, const void* k_cache, const void* v_cache,
+                      int64_t t_cap, const void* o, const float* lse, const void* d_o, float* dq,
+                      float* dkv, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  MKA_CHECK(ptrs_ok({q, k_cache, v_cache, o, lse, d_o, dq, dkv}), MKA_ERR_INVALID);
+  MKA_CHECK(d->seq <= t_cap, MKA_ERR_INVALID);
+  const size_t need = attn_bwd_ws(d);
+  MKA_CHECK(ws_bytes >= need && ptrs_ok({ws}), MKA_ERR_WORKSPACE);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  float* dsum = reinterpret_cast<float*>(base);
+  float* heads = reinterpret_cast<float*>(base + round256(sizeof(float) * rows_of(d) * d->n_heads));
+  if (d->dtype == MKA_BF16)
+    return attn_backward_steps<bf16_t>(d, static_cast<const bf16_t*>(q),
+                                       static_cast<const bf16_t*>(k_cache),
+                                       static_cast<const bf16_t*>(v_cache), t_cap,
+                                       static_cast<const bf16_t*>(o), lse,
+                                       static_cast<const bf16_t*>(d_o), dq, dkv, dsum, heads, s);
+  return attn_backward_steps<float>(d, static_cast<const float*>(q),
+                                    static_cast<const float*>(k_cache),
+                                    static_cast<const float*>(v_cache), t_cap,
+                                    static_cast<const float*>(o), lse,
+                                    static_cast<const float*>(d_o), dq, dkv, dsum, heads, s);
 }
 
 }  // extern "C"

@@ -25,7 +25,7 @@ __all__ = [
     "mka_fuse_kv_proj",
     "mka_attn_prefill", "mka_attn_decode", "mka_prefill", "mka_decode_step", "TierCache",
     "mka_full_prefill", "mka_full_decode_step", "MKA_OP_FULL_PREFILL", "MKA_OP_FULL_DECODE_STEP",
-    "Grads", "mka_backward", "MKA_OP_BACKWARD",
+    "Grads", "mka_backward", "MKA_OP_BACKWARD", "mka_attn_backward", "MKA_OP_ATTN_BACKWARD",
     "mka_workspace_bytes", "mka_status_string", "mka_last_error", "mka_version",
     "mka_probe_mfma_bf16", "mka_probe_stream_read", "PROBE_STREAM_WORKGROUPS",
 ]
@@ -45,7 +45,7 @@ TIER_SETS = {"l1l2l3": MKA_TIERS_ALL, "l1l2": MKA_TIERS_L1_L2, "l1l3": MKA_TIERS
 MKA_OK, MKA_ERR_INVALID, MKA_ERR_UNSUPPORTED, MKA_ERR_WORKSPACE, MKA_ERR_HIP = 0, -1, -2, -3, -4
 (MKA_OP_EMA_SCAN, MKA_OP_FUSE_KV, MKA_OP_ATTN_DECODE, MKA_OP_PREFILL, MKA_OP_DECODE_STEP,
  MKA_OP_RETRIEVE, MKA_OP_INDEX, MKA_OP_ROUTE, MKA_OP_FULL_PREFILL, MKA_OP_FULL_DECODE_STEP,
- MKA_OP_BACKWARD) = range(11)
+ MKA_OP_BACKWARD, MKA_OP_ATTN_BACKWARD) = range(12)
 
 
 class MkaError(RuntimeError):
@@ -120,6 +120,7 @@ _SIGS = {
     "mka_full_decode_step": (ctypes.c_int, [_PD, _P, _I64, ctypes.POINTER(Weights),
                                             ctypes.POINTER(State), ctypes.POINTER(TierCache),
                                             ctypes.POINTER(Outputs), _P, _SZ, _P]),
+    "mka_attn_backward": (ctypes.c_int, [_PD, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mka_backward": (ctypes.c_int, [_PD, _P, ctypes.POINTER(Weights), ctypes.POINTER(State),
                                     ctypes.POINTER(Outputs), _P, ctypes.POINTER(Grads), _P, _SZ,
                                     _P]),
@@ -273,6 +274,13 @@ def mka_full_decode_step(d, x, pos, weights, state, tiers, outputs, ws, ws_bytes
     _check("mka_full_decode_step", lib().mka_full_decode_step(
         ctypes.byref(d), _ptr(x), pos, ctypes.byref(weights), ctypes.byref(state),
         ctypes.byref(tiers), ctypes.byref(outputs), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def mka_attn_backward(d, q, k_cache, v_cache, t_cap, o, lse, d_o, dq, dkv, ws, ws_bytes,
+                      stream=None):
+    _check("mka_attn_backward", lib().mka_attn_backward(
+        ctypes.byref(d), _ptr(q), _ptr(k_cache), _ptr(v_cache), t_cap, _ptr(o), _ptr(lse),
+        _ptr(d_o), _ptr(dq), _ptr(dkv), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def mka_backward(d, x, weights, state, fwd, d_o, grads, ws, ws_bytes, stream=None):

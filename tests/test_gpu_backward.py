@@ -91,3 +91,35 @@ def test_backward_matches_oracle(base, mode, tiers):
     np.testing.assert_allclose(to_np(out["lse"]), lse, atol=tol, rtol=0)
     for k in GRADS:
         check_grad(k, to_np(g[k]), ref[k], s.dtype)
+
+
+@pytest.mark.parametrize("base", ["small_bf16_dh128", "tiny_f32"])
+def test_attention_backward_entry_matches_oracle(base):
+    # mka_attn_backward alone: dq, dK, dV against the oracle's attention_backward
+    # on the forward's own q, K, V (as the GPU stored them).
+    from route_kv_memory_amd import mka
+
+    s = SMALL[base]
+    inp = I.prefill_inputs(s)
+    layer = Layer(s, inp, t_cap=s.seq, nb_cap=max(1, s.seq // s.block))
+    x = to_device(inp["x"], s.dtype)
+    out = layer.prefill(x)
+    r = np.random.default_rng(7)
+    d_o_np = r.standard_normal((s.batch, s.seq, s.n_heads, s.head_dim))
+    d_o_np = I.round_bf16(d_o_np) if s.dtype == "bf16" else d_o_np.astype(np.float32)
+    d_o = to_device(d_o_np, s.dtype)
+    d = layer.dims(s.seq)
+    dq = torch.empty(s.batch, s.seq, s.n_heads, s.head_dim, device="cuda")
+    dkv = torch.empty(s.batch, s.seq, 2, s.n_kv_heads, s.head_dim, device="cuda")
+    ws = torch.empty(max(256, mka.mka_workspace_bytes(d, mka.MKA_OP_ATTN_BACKWARD)),
+                     dtype=torch.uint8, device="cuda")
+    mka.mka_attn_backward(d, out["q"], layer.st["k_cache"], layer.st["v_cache"], layer.t_cap,
+                          out["o"], out["lse"], d_o, dq, dkv, ws, ws.numel())
+    torch.cuda.synchronize()
+    k = to_np(layer.st["k_cache"])[:, :, :s.seq]
+    v = to_np(layer.st["v_cache"])[:, :, :s.seq]
+    rq, rk, rv = O.attention_backward(to_np(out["q"]), k, v, d_o_np, s.n_kv_heads)
+    g = to_np(dkv)
+    check_grad("dq", to_np(dq), rq, s.dtype)
+    check_grad("dk", g[:, :, 0].transpose(0, 2, 1, 3), rk, s.dtype)
+    check_grad("dv", g[:, :, 1].transpose(0, 2, 1, 3), rv, s.dtype)
