@@ -17,7 +17,10 @@ workload, 256 decode steps of ``mka_decode_step``: median microseconds per
 token), the roofline position of the dominant kernel and of decode
 attention, and the CPU oracle timed on a bounded sample.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Also by default (``--quick`` skips them): a training step (forward and backward), the paged
+cache, batched decode, full MKA and the routing variants, each as its own object of the line.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
 """
 
 from __future__ import annotations
@@ -532,18 +535,25 @@ def main():
     ap.add_argument("--full-mka", action="store_true",
                     help="also time full MKA (three attention paths mixed by lambda) on the same "
                          "workloads")
+    ap.add_argument("--quick", action="store_true",
+                    help="only the prefill and decode lines (skip the training step, paged "
+                         "cache, batched decode, full MKA and routing variants that the default "
+                         "run adds)")
     ap.add_argument("--train", action="store_true",
-                    help="also time a training step (forward with saved log-sum-exp, then the "
-                         "backward) of the prefill workload")
+                    help="time a training step (forward with saved log-sum-exp, then the "
+                         "backward) of the prefill workload (on by default)")
     ap.add_argument("--paged", type=int, default=0, metavar="ROWS",
-                    help="also time prefill and decode with a paged fused cache of pages of "
-                         "ROWS rows")
+                    help="time prefill and decode with a paged fused cache of pages of ROWS rows "
+                         "(default 256 unless --quick)")
     ap.add_argument("--decode-batch", action="store_true",
-                    help="also time batched decode (4 sequences, 32K cached tokens each)")
+                    help="time batched decode, 4 sequences of 32K cached tokens (on by default)")
     ap.add_argument("--variants", action="store_true",
                     help="also time the routing and tier variants (fixed, hard top-1/top-2; "
                          "L1+L2, L1+L3, L1 alone) on the same workloads")
     args = ap.parse_args()
+    if not args.quick:  # every measured row of the build in the default line
+        args.train = args.decode_batch = args.full_mka = args.variants = True
+        args.paged = args.paged or 256
     if args.traffic_summary:
         res = traffic_summary(*args.traffic_summary, args.copy_calibration or 1024,
                               args.summary_command)

@@ -6,8 +6,9 @@ tokens.  The oracle computes every step for every row (later rows need the
 earlier ones) and attention on sampled rows; router weights, L2, block
 means, codes and retrieved blocks are compared on every row, Q/K/V/O on the
 sampled rows.  Decode: the 131072-token fused-cache workload, 256 steps,
-compared at sampled steps and on the final state.  The launch configuration
-is the one bench.py times.
+compared at sampled steps and on the final state.  Backward: the 4096-token
+workload's training step, every gradient against the oracle's chain rule.
+The launch configuration is the one bench.py times.
 """
 
 import gc
@@ -138,3 +139,65 @@ def test_full_decode_128k():
     check_close("block means (incl. the two completed)", fin["means"], ost.means, "f32")
     check_codes("block codes (incl. the two completed)", fin["bhash"], ost.hash, ost.hash_abs,
                 s.hash_bits)
+
+
+@pytest.mark.timeout(1200)
+def test_full_backward_4k():
+    """mka_prefill + mka_backward, and mka_attn_backward alone, at the 2 x 4096-token
+    Qwen2.5-7B-shaped workload in the launch configuration of the timed training step.
+
+    The loss is sum(O * dO) with dO = 0 on the first sequence, so every gradient is
+    the second sequence's alone: the oracle runs the fp64 chain rule on that sequence
+    (every row, every head), and the first sequence's dx must be exactly zero."""
+    from .test_gpu_backward import check_grad
+
+    s = I.workload("qwen7b_prefill_4k")
+    B, N, H, G, dh = s.batch, s.seq, s.n_heads, s.n_kv_heads, s.head_dim
+    log("[backward 4k] generating inputs")
+    inp = I.prefill_inputs(s)
+    d_o = np.zeros((B, N, H, dh), np.float32)
+    d_o[1] = I.round_bf16(np.random.default_rng(101).standard_normal((N, H, dh)))
+    layer = Layer(s, inp, t_cap=N, nb_cap=N // s.block)
+    x = to_device(inp["x"], s.dtype)
+    d_o_dev = to_device(d_o, s.dtype)
+    log(f"[backward 4k] gpu: mka_prefill + mka_backward B={B} N={N}")
+    out = layer.prefill(x)
+    g = layer.backward(x, out, d_o_dev)
+    d = layer.dims(N)
+    dq = torch.empty(B, N, H, dh, device="cuda")
+    dkv = torch.empty(B, N, 2, G, dh, device="cuda")
+    ws = torch.empty(max(256, mka.mka_workspace_bytes(d, mka.MKA_OP_ATTN_BACKWARD)),
+                     dtype=torch.uint8, device="cuda")
+    log("[backward 4k] gpu: mka_attn_backward")
+    mka.mka_attn_backward(d, out["q"], layer.st["k_cache"], layer.st["v_cache"], layer.t_cap,
+                          out["o"], out["lse"], d_o_dev, dq, dkv, ws, ws.numel())
+    torch.cuda.synchronize()
+    got = {k: to_np(v) for k, v in g.items()}
+    a_dkv = to_np(dkv)
+    lse = to_np(out["lse"])
+    idx = to_np(out["idx"])
+    del out, layer, x, d_o_dev, dq, dkv, ws, g
+    torch.cuda.empty_cache()
+
+    assert np.all(got["dx"][0] == 0.0), "dO = 0 on a sequence must give it dx = 0"
+    assert np.all(a_dkv[0] == 0.0), "dO = 0 on a sequence must give it dK = dV = 0"
+    log("[backward 4k] oracle: forward and chain rule on the second sequence")
+    ref = O.backward(inp["x"][1:2], *[inp[k] for k in WEIGHTS], d_o[1:2], **oracle_kwargs(s))
+    n_diff = int(np.sum(np.any(idx[1] != ref["fwd"]["idx"][0], axis=-1)))
+    log(f"  rows whose retrieved blocks differ from the oracle's (code near-ties): {n_diff}")
+    # the saved log-sum-exp on sampled rows, from the oracle's own q and K
+    qh = ref["fwd"]["q"][0].reshape(N, H, dh)
+    rows = I.sampled_rows(s.replace(n_sampled=64))
+    want = np.empty((len(rows), H))
+    for i, t in enumerate(rows):
+        for h in range(H):
+            sc = ref["fwd"]["k"][0, h // (H // G), :t + 1] @ qh[t, h] / np.sqrt(dh)
+            want[i, h] = sc.max() + np.log(np.exp(sc - sc.max()).sum())
+    check_close("lse (sampled rows)", lse[1, rows], want, s.dtype)
+    check_grad("dx", got["dx"][1], ref["dx"][0], s.dtype)
+    for k in ("dw_q", "dw_k", "dw_v", "dw_r1", "dw_r2"):
+        check_grad(k, got[k], ref[k], s.dtype)
+    check_grad("attn dk", a_dkv[1, :, 0].transpose(1, 0, 2), ref["dk"][0], s.dtype)
+    check_grad("attn dv", a_dkv[1, :, 1].transpose(1, 0, 2), ref["dv"][0], s.dtype)
+    del ref, got, inp
+    gc.collect()
