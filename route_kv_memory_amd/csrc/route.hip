@@ -8,48 +8,62 @@
 namespace mka {
 
 // ---------------------------------------------------------------------------
-// MFMA router (bf16): a workgroup takes 32 tokens; its 4 waves split the
-// q-width reduction into quarters, each producing a 32 x r block of hidden
-// pre-activations with MFMA 32x32x16 (operands read straight from global:
-// the token's q row and the weight row are both contiguous along the
-// reduction).  The quarters are summed in LDS, GELU applied, then the r -> 3
-// layer and the softmax run one thread per token.
+// MFMA router (bf16): a workgroup takes 32 tokens; its NW waves (8 when the
+// q width splits into slices of whole 16-wide k-steps, else 4) split the
+// q-width reduction, each producing a 32 x r block of hidden pre-activations
+// with MFMA 32x32x16 (operands read straight from global: the token's q row
+// and the weight row are both contiguous along the reduction).  The slices
+// are summed in LDS, GELU applied, then the r -> 3 layer and the softmax run
+// one thread per token.
 // ---------------------------------------------------------------------------
-template <int NB>  // NB = r / 32 output blocks
-__global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restrict__ Q, int M, int qw,
+template <int NB, int NW>  // NB = r / 32 output blocks
+__global__ __launch_bounds__(NW * 64) void router_mfma_kernel(const bf16_t* __restrict__ Q, int M, int qw,
                                                           const bf16_t* __restrict__ W1,
                                                           const bf16_t* __restrict__ W2,
                                                           float* __restrict__ lam, Routing rt) {
   constexpr int R = NB * 32;
-  __shared__ float part[4][32][R + 1];
+  __shared__ float part[NW][32][R + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int row0 = blockIdx.x * 32;
   const int row = row0 + l32;
-  const int quarter = qw / 4;
-  const int k_begin = wave * quarter;
+  const int slice = qw / NW;
+  const int k_begin = wave * slice;
 
   f32x16 acc[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) acc[j] = f32x16{};
   const bf16_t* qrow = Q + static_cast<int64_t>(row < M ? row : 0) * qw + 8 * h;
-  for (int k = k_begin; k < k_begin + quarter; k += 16) {
-    bf16x8 a = *reinterpret_cast<const bf16x8*>(qrow + k);
-    if (row >= M) a = bf16x8{};
+  // U k-steps' loads are issued before their products; steps past the
+  // slice re-read its last step (inside the row) and enter as zeros.
+  constexpr int U = 32 / NW;
+  const int k_end = k_begin + slice;
+  for (int k = k_begin; k < k_end; k += 16 * U) {
+    bf16x8 a[U], b[U][NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const bf16x8 b =
-          *reinterpret_cast<const bf16x8*>(W1 + static_cast<int64_t>(j * 32 + l32) * qw + k + 8 * h);
-      acc[j] = mfma32x32x16(a, b, acc[j]);
+    for (int u = 0; u < U; ++u) {
+      const int kk = min(k + 16 * u, k_end - 16);
+      a[u] = *reinterpret_cast<const bf16x8*>(qrow + kk);
+      if (row >= M || k + 16 * u >= k_end) a[u] = bf16x8{};
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        b[u][j] = *reinterpret_cast<const bf16x8*>(W1 + static_cast<int64_t>(j * 32 + l32) * qw +
+                                                   kk + 8 * h);
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[j] = mfma32x32x16(a[u], b[u][j], acc[j]);
   }
 #pragma unroll
   for (int j = 0; j < NB; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) part[wave][acc_row(r, h)][j * 32 + l32] = acc[j][r];
   __syncthreads();
-  for (int e = tid; e < 32 * R; e += 256) {
+  for (int e = tid; e < 32 * R; e += NW * 64) {
     const int rr = e / R, n = e % R;
-    const float z = part[0][rr][n] + part[1][rr][n] + part[2][rr][n] + part[3][rr][n];
+    float z = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) z += part[w][rr][n];
     part[0][rr][n] = gelu(z);
   }
   __syncthreads();
@@ -73,10 +87,14 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restri
 hipError_t router_bf16_mfma(const bf16_t* q, int M, int qw, const bf16_t* w1, int r,
                             const bf16_t* w2, float* lam, Routing rt, hipStream_t s) {
   const dim3 grid((M + 31) / 32);
-  if (r == 64)
-    hipLaunchKernelGGL(router_mfma_kernel<2>, grid, dim3(256), 0, s, q, M, qw, w1, w2, lam, rt);
+  auto launch = [&](auto kernel, int nw) {
+    hipLaunchKernelGGL(kernel, grid, dim3(nw * 64), 0, s, q, M, qw, w1, w2, lam, rt);
+  };
+  // (qw % 64 == 0 is validated: slices of qw/4 are whole k-steps.)
+  if (qw % 128 == 0)
+    r == 64 ? launch(router_mfma_kernel<2, 8>, 8) : launch(router_mfma_kernel<1, 8>, 8);
   else
-    hipLaunchKernelGGL(router_mfma_kernel<1>, grid, dim3(256), 0, s, q, M, qw, w1, w2, lam, rt);
+    r == 64 ? launch(router_mfma_kernel<2, 4>, 4) : launch(router_mfma_kernel<1, 4>, 4);
   return hipGetLastError();
 }
 
