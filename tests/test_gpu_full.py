@@ -201,3 +201,76 @@ def test_full_backward_4k():
     check_grad("attn dv", a_dkv[1, :, 1].transpose(1, 0, 2), ref["dv"][0], s.dtype)
     del ref, got, inp
     gc.collect()
+
+
+def _bitwise_equal(name, a, b):
+    a, b = to_np(a), to_np(b)
+    assert a.shape == b.shape, (name, a.shape, b.shape)
+    same = np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    log(f"  {name}: {'bit-identical' if same else 'DIFFERS'}")
+    assert same, f"{name}: paged and contiguous layers differ"
+
+
+@pytest.mark.timeout(1200)
+def test_full_paged_matches_contiguous():
+    """The paged fused cache at full size, in the launch configuration the bench
+    times (256-row pages in a seeded random order, spare pages in the pool):
+    2 x 4096 prefill and 16 decode steps at 131072 cached tokens give outputs and
+    cache rows bit-identical to the contiguous layer (only addresses differ; both
+    are checked against the oracle at these sizes by the tests above)."""
+    s = I.workload("qwen7b_prefill_4k")
+    log("[paged 4k] generating inputs")
+    inp = I.prefill_inputs(s)
+    x = to_device(inp["x"], s.dtype)
+    res = {}
+    for name, kw in (("contiguous", {}), ("paged", dict(page_size=256, spare_pages=8))):
+        layer = Layer(s, inp, t_cap=s.seq, nb_cap=s.seq // s.block, **kw)
+        log(f"[paged 4k] gpu: mka_prefill, {name}")
+        out = layer.prefill(x)
+        torch.cuda.synchronize()
+        res[name] = (out, layer.logical_cache("k")[:, :, :s.seq].clone(),
+                     layer.logical_cache("v")[:, :, :s.seq].clone())
+        del layer
+    for key in ("q", "lambda", "l2", "key", "idx", "o", "lse"):
+        _bitwise_equal(f"prefill {key}", res["contiguous"][0][key], res["paged"][0][key])
+    _bitwise_equal("prefill K cache", res["contiguous"][1], res["paged"][1])
+    _bitwise_equal("prefill V cache", res["contiguous"][2], res["paged"][2])
+    del res, x, inp
+    torch.cuda.empty_cache()
+
+    s = I.workload("qwen7b_decode_128k")
+    log("[paged 128k] generating state")
+    dec = I.decode_inputs(s)
+    T0, n = s.decode_cached, 16
+    t_cap = T0 + s.decode_steps
+    nb0 = T0 // s.block
+    tokens = to_device(dec["tokens"], s.dtype)
+    res = {}
+    for name, kw in (("contiguous", {}), ("paged", dict(page_size=256, spare_pages=8))):
+        layer = Layer(s, dec, t_cap=t_cap, nb_cap=t_cap // s.block + 1, **kw)
+        st = layer.st
+        layer.load_cache("k", to_device(dec["k_cache"], s.dtype))
+        layer.load_cache("v", to_device(dec["v_cache"], s.dtype))
+        st["ema_state"].copy_(to_device(dec["ema_state"]))
+        st["block_acc"].copy_(to_device(dec["block_acc"]))
+        st["block_means"][:, :nb0].copy_(to_device(dec["block_means"]))
+        d1 = layer.dims(1)
+        layer.workspace(max(mka.mka_workspace_bytes(d1, mka.MKA_OP_INDEX, nb0),
+                            mka.mka_workspace_bytes(d1, mka.MKA_OP_DECODE_STEP, t_cap)))
+        layer.index_blocks(0, nb0)
+        log(f"[paged 128k] gpu: {n} mka_decode_step calls from position {T0}, {name}")
+        outs = []
+        for k in range(n):
+            out = layer.decode_step(tokens[k], T0 + k)
+            outs.append({kk: v.clone() for kk, v in out.items()})
+        torch.cuda.synchronize()
+        res[name] = (outs, layer.logical_cache("k")[:, :, T0:T0 + n].clone(),
+                     layer.logical_cache("v")[:, :, T0:T0 + n].clone())
+        del layer, st
+        torch.cuda.empty_cache()
+    for k in range(n):
+        for key in ("lambda", "l2", "key", "idx", "o"):
+            _bitwise_equal(f"decode step {k} {key}", res["contiguous"][0][k][key],
+                           res["paged"][0][k][key])
+    _bitwise_equal("decode K rows appended", res["contiguous"][1], res["paged"][1])
+    _bitwise_equal("decode V rows appended", res["contiguous"][2], res["paged"][2])
