@@ -17,6 +17,14 @@
 
 namespace mka {
 
+// 16-byte chunk swizzle of LDS row P of a K tile: a row is DH*2 bytes (256 B
+// for DH = 128, 128 B for DH = 64), so 16 consecutive rows with the same
+// logical chunk land in 16 distinct bank groups.
+template <int DH>
+__device__ __forceinline__ int kswz(int P) {
+  return DH == 128 ? (P & 15) : ((P >> 1) & 7);
+}
+
 __device__ __forceinline__ int kperm(int r) {
   const int q = r & 15;
   const int qq = (q >= 4 && q < 8) ? q + 4 : ((q >= 8 && q < 12) ? q - 4 : q);
@@ -35,12 +43,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
     bf16_t* __restrict__ O, int B, int seq, int H, int G, KvLayout kv, int64_t pos0, float sl2,
     int n_qblk, int n_units, float* __restrict__ lse) {
-  constexpr int NT = NW * 64, BM = 32 * NW, BN = 64, KP = DH + 8, VP = BN + 8, NKS = DH / 16,
+  constexpr int NT = NW * 64, BM = 32 * NW, BN = 64, VP = BN + 8, NKS = DH / 16,
                 NDB = DH / 32;
-  constexpr int KCH = BN * DH / 8 / NT;
-  constexpr int VITEMS = (BN / 4) * (DH / 8);  // 16 key quads x DH/8 dim chunks
+  constexpr int KLD = BN * DH * 2 / 1024 / NW;  // 1 KB K-tile loads per wave
+  constexpr int VITEMS = (BN / 4) * (DH / 8);    // 16 key quads x DH/8 dim chunks
   static_assert(BN == 64, "V store mapping assumes 16 key quads");
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][BN * KP];
+  static_assert(KLD * NW * 1024 == BN * DH * 2, "the K tile splits evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) bf16_t Ks[2][BN * DH];
   __shared__ __attribute__((aligned(16))) bf16_t Vt[2][DH * VP];
 
   const int hpg = H / G;
@@ -66,20 +75,30 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
       if (q_row >= seq) qf[ks] = bf16x8{};
     }
   }
-  u32x4 rk[KCH], rv[4];
+  u32x4 rv[4];
   PageWindow<PAGED> pw;
   pw.fill(kv, b, 0);
+  // K tiles go global -> LDS directly (no registers): load instruction i of
+  // wave w fills the 1 KB at LDS chunk w*KLD + i, lane l its 16 bytes at +16*l.
+  // LDS row P holds tile row kperm(P) (kperm is its own inverse), with its
+  // 16-byte chunks XOR-swizzled by kswz(P) so that the 16 rows of an MFMA
+  // fragment read fall in distinct banks.  The lane's source row and chunk:
+  constexpr int RPC = 1024 / (DH * 2);  // rows per 1 KB
+  uint32_t k_src[KLD];
+#pragma unroll
+  for (int i = 0; i < KLD; ++i) {
+    const int P = (wave * KLD + i) * RPC + lane / (DH / 8), c = lane % (DH / 8);
+    k_src[i] = static_cast<uint32_t>(kperm(P) * DH + 8 * (c ^ kswz<DH>(P))) * 2;
+  }
   // One tile of BN keys lies in one page (pages hold a multiple of 64 rows);
   // keys at or beyond kv_end read as zeros through the buffer range.
-  auto gload = [&](int j0) {
+  auto gload = [&](int j0, int buf) {
     const int64_t off = pw.row(kv, b, g, j0);
     const uint32_t bytes = static_cast<uint32_t>(min<int64_t>(BN, kv_end - j0) * DH * 2);
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kc + off, bytes), vrs = make_rsrc(Vc + off, bytes);
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + NT * i, row = c / (DH / 8), col = (c % (DH / 8)) * 8;
-      rk[i] = buffer_load16(krs, static_cast<uint32_t>(row * DH + col) * 2);
-    }
+    for (int i = 0; i < KLD; ++i)
+      buffer_load_lds16(krs, (lds_void_t*)(&Ks[buf][(wave * KLD + i) * 512]), k_src[i]);
     if (tid < VITEMS) {
       const int kq = tid & 15, dc = tid >> 4;
 #pragma unroll
@@ -87,15 +106,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
         rv[r] = buffer_load16(vrs, static_cast<uint32_t>((4 * kq + r) * DH + 8 * dc) * 2);
     }
   };
-  // K row j of the tile goes to LDS row kperm(j), so the MFMA reads of
-  // consecutive lanes hit consecutive rows.  V threads are laid out so that the
-  // 64 lanes of one transposing store cover 16 key quads of 4 d-rows.
+  // V threads are laid out so that the 64 lanes of one transposing store
+  // cover 16 key quads of 4 d-rows.
   auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + NT * i, row = c / (DH / 8), col = (c % (DH / 8)) * 8;
-      *reinterpret_cast<u32x4*>(&Ks[buf][kperm(row) * KP + col]) = rk[i];
-    }
     if (tid < VITEMS) {
       const int kq = tid & 15, dc = tid >> 4;
       store_v_transposed(Vt[buf], VP, 8 * dc, 4 * kq, rv);
@@ -107,22 +120,25 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
-  gload(0);
+  gload(0, 0);
   sstore(0);
+  __builtin_amdgcn_s_waitcnt(kVmcntPending<0>());  // this wave's K-tile loads have landed
   __syncthreads();
   for (int jt = 0; jt < n_tiles; ++jt) {
     const int buf = jt & 1;
     const int j0 = jt * BN;
-    if (jt + 1 < n_tiles) gload(j0 + BN);
+    if (jt + 1 < n_tiles) gload(j0 + BN, buf ^ 1);
 
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
-      const bf16_t* kr = &Ks[buf][(kb * 32 + l32) * KP + 8 * hl];
+      const int P = kb * 32 + l32;
+      const bf16_t* kr = &Ks[buf][P * DH];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
-        s[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kr + 16 * ks), qf[ks], s[kb]);
+        s[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kr + 8 * ((2 * ks + hl) ^ kswz<DH>(P))),
+                             qf[ks], s[kb]);
     }
 
     // Online max-shift in the exp2 domain: ms is the running reference
@@ -179,6 +195,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
                                  pf[kb][st], acc[db]);
     }
     if (jt + 1 < n_tiles) sstore(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(kVmcntPending<0>());  // this wave's K-tile loads have landed
     __syncthreads();
   }
 

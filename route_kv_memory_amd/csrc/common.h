@@ -137,6 +137,13 @@ __device__ __forceinline__ void global_load_lds16(const void* src, lds_void_t* l
   __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
 }
 
+// The same through a buffer resource: byte offset ``off`` from its base; parts
+// outside the resource's range are read as zeros.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, lds_void_t* lds,
+                                                  uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, static_cast<int>(off), 0, 0, 0);
+}
+
 // s_waitcnt immediate that waits until at most N vector-memory operations of
 // the wave are outstanding (expcnt and lgkmcnt left at their maxima): vmcnt
 // occupies bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
