@@ -25,6 +25,14 @@ __device__ __forceinline__ int kswz(int P) {
   return DH == 128 ? (P & 15) : ((P >> 1) & 7);
 }
 
+// 16-byte chunk swizzle of LDS row P of a V tile: the 4 keys x 32 bytes that
+// a 16-lane group of a transposing read touches, and the two groups of a
+// 32-lane half, fall in distinct bank groups.
+template <int DH>
+__device__ __forceinline__ int vswz(int P) {
+  return DH == 128 ? 4 * (P & 3) : 4 * ((P >> 1) & 1);
+}
+
 __device__ __forceinline__ int kperm(int r) {
   const int q = r & 15;
   const int qq = (q >= 4 && q < 8) ? q + 4 : ((q >= 8 && q < 12) ? q - 4 : q);
@@ -43,14 +51,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
     bf16_t* __restrict__ O, int B, int seq, int H, int G, KvLayout kv, int64_t pos0, float sl2,
     int n_qblk, int n_units, float* __restrict__ lse) {
-  constexpr int NT = NW * 64, BM = 32 * NW, BN = 64, VP = BN + 8, NKS = DH / 16,
+  constexpr int BM = 32 * NW, BN = 64, NKS = DH / 16,
                 NDB = DH / 32;
-  constexpr int KLD = BN * DH * 2 / 1024 / NW;  // 1 KB K-tile loads per wave
-  constexpr int VITEMS = (BN / 4) * (DH / 8);    // 16 key quads x DH/8 dim chunks
-  static_assert(BN == 64, "V store mapping assumes 16 key quads");
-  static_assert(KLD * NW * 1024 == BN * DH * 2, "the K tile splits evenly over the waves");
+  constexpr int KLD = BN * DH * 2 / 1024 / NW;  // 1 KB tile loads per wave (K and V each)
+  static_assert(KLD * NW * 1024 == BN * DH * 2, "a tile splits evenly over the waves");
   __shared__ __attribute__((aligned(1024))) bf16_t Ks[2][BN * DH];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[2][DH * VP];
+  __shared__ __attribute__((aligned(1024))) bf16_t Vs[2][BN * DH];
 
   const int hpg = H / G;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -75,20 +81,37 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
       if (q_row >= seq) qf[ks] = bf16x8{};
     }
   }
-  u32x4 rv[4];
   PageWindow<PAGED> pw;
   pw.fill(kv, b, 0);
-  // K tiles go global -> LDS directly (no registers): load instruction i of
-  // wave w fills the 1 KB at LDS chunk w*KLD + i, lane l its 16 bytes at +16*l.
-  // LDS row P holds tile row kperm(P) (kperm is its own inverse), with its
+  // K and V tiles go global -> LDS directly (no registers): load instruction
+  // i of wave w fills the 1 KB at LDS chunk w*KLD + i, lane l its 16 bytes at
+  // +16*l, so each lane fetches the source row and chunk that its slot needs.
+  // K: LDS row P holds tile row kperm(P) (kperm is its own inverse), its
   // 16-byte chunks XOR-swizzled by kswz(P) so that the 16 rows of an MFMA
-  // fragment read fall in distinct banks.  The lane's source row and chunk:
+  // fragment read fall in distinct banks.  V: LDS row P holds key P, chunks
+  // swizzled by vswz(P) for the transposing fragment reads below.
   constexpr int RPC = 1024 / (DH * 2);  // rows per 1 KB
-  uint32_t k_src[KLD];
+  uint32_t k_src[KLD], v_src[KLD];
 #pragma unroll
   for (int i = 0; i < KLD; ++i) {
     const int P = (wave * KLD + i) * RPC + lane / (DH / 8), c = lane % (DH / 8);
     k_src[i] = static_cast<uint32_t>(kperm(P) * DH + 8 * (c ^ kswz<DH>(P))) * 2;
+    v_src[i] = static_cast<uint32_t>(P * DH + 8 * (c ^ vswz<DH>(P))) * 2;
+  }
+  // V^T fragments for O^T += V^T P^T come from two ds_read_b64_tr_b16 each: in
+  // a 16-lane group, lane r of the group addresses 4 consecutive dims of one
+  // key and lane i receives one dim of 4 consecutive keys (dim i, keys 0..3 of
+  // the group's block when lane r reads key r/4, dims 4*(r%4)..).  Lane l of
+  // the wave then holds dim db*32 + l%32 and keys 8*(l/32) .. +7 of a 16-key
+  // step, as the MFMA's A operand wants.  The swizzle of a key's row is a
+  // per-lane constant here, so per dim block a lane keeps one base address
+  // and steps keys by immediate offsets.
+  const int vr = lane & 15, vg = (lane >> 4) & 1;
+  int v_base[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int key0 = 8 * hl + (vr >> 2), d = db * 32 + 16 * vg + 4 * (vr & 3);
+    v_base[db] = key0 * DH + 8 * ((d >> 3) ^ vswz<DH>(key0)) + (d & 7);
   }
   // One tile of BN keys lies in one page (pages hold a multiple of 64 rows);
   // keys at or beyond kv_end read as zeros through the buffer range.
@@ -97,21 +120,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
     const uint32_t bytes = static_cast<uint32_t>(min<int64_t>(BN, kv_end - j0) * DH * 2);
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kc + off, bytes), vrs = make_rsrc(Vc + off, bytes);
 #pragma unroll
-    for (int i = 0; i < KLD; ++i)
+    for (int i = 0; i < KLD; ++i) {
       buffer_load_lds16(krs, (lds_void_t*)(&Ks[buf][(wave * KLD + i) * 512]), k_src[i]);
-    if (tid < VITEMS) {
-      const int kq = tid & 15, dc = tid >> 4;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        rv[r] = buffer_load16(vrs, static_cast<uint32_t>((4 * kq + r) * DH + 8 * dc) * 2);
-    }
-  };
-  // V threads are laid out so that the 64 lanes of one transposing store
-  // cover 16 key quads of 4 d-rows.
-  auto sstore = [&](int buf) {
-    if (tid < VITEMS) {
-      const int kq = tid & 15, dc = tid >> 4;
-      store_v_transposed(Vt[buf], VP, 8 * dc, 4 * kq, rv);
+      buffer_load_lds16(vrs, (lds_void_t*)(&Vs[buf][(wave * KLD + i) * 512]), v_src[i]);
     }
   };
 
@@ -121,8 +132,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
   gload(0, 0);
-  sstore(0);
-  __builtin_amdgcn_s_waitcnt(kVmcntPending<0>());  // this wave's K-tile loads have landed
+  __builtin_amdgcn_s_waitcnt(kVmcntPending<0>());  // this wave's tile loads have landed
   __syncthreads();
   for (int jt = 0; jt < n_tiles; ++jt) {
     const int buf = jt & 1;
@@ -186,16 +196,18 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
 
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const bf16_t* vr = &Vt[buf][(db * 32 + l32) * VP + 8 * hl];
+      const bf16_t* vb = &Vs[buf][v_base[db]];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
-          acc[db] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(vr + kb * 32 + 16 * st),
-                                 pf[kb][st], acc[db]);
+        for (int st = 0; st < 2; ++st) {
+          const int k0 = (kb * 32 + 16 * st) * DH;
+          const bf16x4 lo = ds_read_tr16_b64(vb + k0), hi = ds_read_tr16_b64(vb + k0 + 4 * DH);
+          const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          acc[db] = mfma32x32x16(vf, pf[kb][st], acc[db]);
+        }
     }
-    if (jt + 1 < n_tiles) sstore(buf ^ 1);
-    __builtin_amdgcn_s_waitcnt(kVmcntPending<0>());  // this wave's K-tile loads have landed
+    __builtin_amdgcn_s_waitcnt(kVmcntPending<0>());  // this wave's tile loads have landed
     __syncthreads();
   }
 

@@ -137,8 +137,19 @@ __device__ __forceinline__ void global_load_lds16(const void* src, lds_void_t* l
   __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
 }
 
-// The same through a buffer resource: byte offset ``off`` from its base; parts
-// outside the resource's range are read as zeros.
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane r supplies the address of 4 consecutive 16-bit values (row r of a
+// 16 x 4 block) and lane i receives column i % 4 of rows i/4, i/4+4, i/4+8,
+// i/4+12 (lane layout measured on the GPU).  ``p`` points into LDS.
+__device__ __forceinline__ bf16x4 ds_read_tr16_b64(const bf16_t* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// The same through a buffer resource: byte offset ``off`` from its base; lanes
+// whose bytes lie outside the resource's range write zeros to LDS (measured).
 __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, lds_void_t* lds,
                                                   uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, static_cast<int>(off), 0, 0, 0);
