@@ -75,9 +75,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
   bf16x8 qf[NKS];
   {
     const bf16_t* qp = Q + (static_cast<int64_t>(b * seq + min(q_row, seq - 1)) * H + h) * DH + 8 * hl;
+    // Q enters the products pre-scaled by log2(e)/sqrt(dh) (rounded to bf16
+    // once more), so the scores come out of the MFMA in the exp2 domain.
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
+      const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
+      float f[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = static_cast<float>(qv[j]) * sl2;
+      qf[ks] = pack_bf16x8(f);
       if (q_row >= seq) qf[ks] = bf16x8{};
     }
   }
@@ -126,7 +132,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
     }
   };
 
-  float ms = -INFINITY, l_i = 0.f;
+  // ms: the running reference (exp2 domain); nms holds -ms in every
+  // accumulator register and seeds the score products, which then return the
+  // shifted scores s * log2(e)/sqrt(dh) - ms directly.
+  float ms = 0.f, l_i = 0.f;
+  f32x16 nms = f32x16{};
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
@@ -142,7 +152,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
+      s[kb] = nms;
       const int P = kb * 32 + l32;
       const bf16_t* kr = &Ks[buf][P * DH];
 #pragma unroll
@@ -169,29 +179,51 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
-    const bool raise = mx > ms + 8.0f;
+    {  // the two lanes of a query (l and l^32) exchange their maxima by a lane swap
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    // The reference is raised by the tile's maximum of the shifted scores
+    // when that exceeds 8 (and always on the first tile); the tile's scores
+    // shift with it.
+    const bool raise = jt == 0 || mx > 8.0f;
     if (__any(raise)) {
-      const float ms_new = raise ? mx : ms;
-      const float alpha = raise ? __builtin_amdgcn_exp2f(ms - ms_new) : 1.0f;
+      const float delta = raise ? mx : 0.0f;
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
       l_i *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
-      ms = ms_new;
+      ms += delta;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[0][r] -= delta;
+        s[1][r] -= delta;
+        nms[r] = -ms;
+      }
     }
 
+    // Probabilities as the bf16x8 B operands of O^T += V^T P^T; the row sum
+    // adds the same bf16 values the products use, two per v_dot2 (each pair
+    // is built as a bf16x2 value: bit-casting the words of a packed u32x4
+    // instead made the compiler feed the first word to all four dot products).
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    const bf16x2v ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
     bf16x8 pf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        float p[8];
+        u32x4 w;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          p[j] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * st + j], sl2, -ms));
-          l_i += p[j];
+        for (int i = 0; i < 4; ++i) {
+          const bf16x2v v = {
+              static_cast<__bf16>(__builtin_amdgcn_exp2f(s[kb][8 * st + 2 * i])),
+              static_cast<__bf16>(__builtin_amdgcn_exp2f(s[kb][8 * st + 2 * i + 1]))};
+          l_i = __builtin_amdgcn_fdot2_f32_bf16(v, ones, l_i, false);
+          w[i] = __builtin_bit_cast(uint32_t, v);
         }
-        pf[kb][st] = pack_bf16x8(p);
+        pf[kb][st] = __builtin_bit_cast(bf16x8, w);
       }
 
 #pragma unroll
