@@ -30,6 +30,24 @@ __device__ __forceinline__ int bperm(int r) {
   return (r & ~15) | qq;
 }
 
+// 16-byte chunk swizzle of LDS row P of a row tile that is read both as MFMA
+// row fragments (16 consecutive rows, one chunk) and transposed (4 consecutive
+// rows x 32 bytes per 16-lane group, two groups per 32-lane half): both land
+// on distinct banks (checked on the CPU for dh = 64 and 128).
+template <int DH>
+__device__ __forceinline__ int cswz(int P) {
+  return DH == 128 ? 4 * (P & 3) + ((P >> 2) & 3) : 4 * ((P >> 1) & 1) + ((P >> 2) & 3);
+}
+
+// Transposed operand from a row tile in LDS: the bf16x8 A operand holding dim
+// d of rows r0 .. r0+7 (lane l: d = d0 + l%32, rows 8*(l/32) ..), read with two
+// ds_read_b64_tr_b16 whose per-lane addresses ``a0``/``a1`` select, in each
+// 16-lane group, 4 consecutive dims of row r/4 (see ds_read_tr16_b64).
+__device__ __forceinline__ bf16x8 ld_tr8(const bf16_t* a0, const bf16_t* a1) {
+  const bf16x4 lo = ds_read_tr16_b64(a0), hi = ds_read_tr16_b64(a1);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 __device__ __forceinline__ bf16x8 ld8(const bf16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
@@ -40,7 +58,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
 // dq.  Workgroup = 4 waves = 128 query rows of head h; K/V tiles of 64 keys,
-// double-buffered in LDS as rows (for S^T, dP^T) and transposed K (for dQ).
+// double-buffered in LDS as rows: row fragments for S^T and dP^T, K read
+// transposed for dQ.
 // ---------------------------------------------------------------------------
 template <int DH>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
@@ -48,13 +67,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
     const bf16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ dsum,
     int B, int N, int H, int G, int64_t t_cap, float sl2, float scale, int n_qblk, int n_units,
     float* __restrict__ dq) {
-  constexpr int NT = 256, BM = 128, BN = 64, KP = DH + 8, VP = BN + 8, NKS = DH / 16,
-                NDB = DH / 32;
-  constexpr int KCH = BN * DH / 8 / NT;        // 16-byte V row chunks per thread
-  constexpr int VITEMS = (BN / 4) * (DH / 8);  // threads loading 4 K rows x 8 dims
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][BN * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][BN * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t Kt[2][DH * VP];
+  constexpr int BM = 128, BN = 64, NKS = DH / 16, NDB = DH / 32;
+  constexpr int TLD = BN * DH * 2 / 1024 / 4;  // 1 KB loads per wave per tile (K and V each)
+  constexpr int RPC = 1024 / (DH * 2);         // rows per 1 KB
+  __shared__ __attribute__((aligned(1024))) bf16_t Ks[2][BN * DH];
+  __shared__ __attribute__((aligned(1024))) bf16_t Vs[2][BN * DH];
 
   const int hpg = H / G;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -85,59 +102,57 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
   const bf16_t* kbase = Kc + (static_cast<int64_t>(b) * G + g) * t_cap * DH;
   const bf16_t* vbase = Vc + (static_cast<int64_t>(b) * G + g) * t_cap * DH;
 
-  u32x4 rk[4], rv[KCH];
-  // keys at or beyond kv_end read as zeros through the buffer range
-  auto gload = [&](int j0) {
+  // K and V tiles go global -> LDS directly (as in the dK/dV kernel): LDS row
+  // P holds tile row bperm(P), chunks swizzled by cswz(P); keys at or beyond
+  // kv_end lie outside the buffer range and read as zeros.
+  uint32_t t_src[TLD];
+#pragma unroll
+  for (int i = 0; i < TLD; ++i) {
+    const int P = (wave * TLD + i) * RPC + lane / (DH / 8), c = lane % (DH / 8);
+    t_src[i] = static_cast<uint32_t>((bperm(P) * DH + 8 * (c ^ cswz<DH>(P))) * 2);
+  }
+  int t_base[2][NDB];  // transposed K reads (see the dK/dV kernel)
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int r = lane & 15, G2 = (lane >> 4) & 1;
+      const int P = bperm(8 * hl + 4 * q + (r >> 2)), d = db * 32 + 16 * G2 + 4 * (r & 3);
+      t_base[q][db] = P * DH + 8 * ((d >> 3) ^ cswz<DH>(P)) + (d & 7);
+    }
+  auto gload = [&](int j0, int buf) {
     const uint32_t bytes = static_cast<uint32_t>(min(BN, kv_end - j0) * DH * 2);
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase + static_cast<int64_t>(j0) * DH, bytes);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase + static_cast<int64_t>(j0) * DH, bytes);
-    if (tid < VITEMS) {
-      const int kq = tid & 15, dc = tid >> 4;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        rk[r] = buffer_load16(krs, static_cast<uint32_t>((4 * kq + r) * DH + 8 * dc) * 2);
-    }
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + NT * i, row = c / (DH / 8), col = (c % (DH / 8)) * 8;
-      rv[i] = buffer_load16(vrs, static_cast<uint32_t>(row * DH + col) * 2);
-    }
-  };
-  auto sstore = [&](int buf) {
-    if (tid < VITEMS) {
-      const int kq = tid & 15, dc = tid >> 4;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        *reinterpret_cast<u32x4*>(&Ks[buf][bperm(4 * kq + r) * KP + 8 * dc]) = rk[r];
-      store_v_transposed(Kt[buf], VP, 8 * dc, 4 * kq, rk);
-    }
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + NT * i, row = c / (DH / 8), col = (c % (DH / 8)) * 8;
-      *reinterpret_cast<u32x4*>(&Vs[buf][bperm(row) * KP + col]) = rv[i];
+    for (int i = 0; i < TLD; ++i) {
+      buffer_load_lds16(krs, (lds_void_t*)(&Ks[buf][(wave * TLD + i) * 512]), t_src[i]);
+      buffer_load_lds16(vrs, (lds_void_t*)(&Vs[buf][(wave * TLD + i) * 512]), t_src[i]);
     }
   };
 
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
-  gload(0);
-  sstore(0);
+  gload(0, 0);
+  __builtin_amdgcn_s_waitcnt(kVmcntPending<0>());  // this wave's tile loads have landed
   __syncthreads();
   for (int jt = 0; jt < n_tiles; ++jt) {
     const int buf = jt & 1, j0 = jt * BN;
-    if (jt + 1 < n_tiles) gload(j0 + BN);
+    if (jt + 1 < n_tiles) gload(j0 + BN, buf ^ 1);
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
       dp[kb] = f32x16{};
-      const bf16_t* kr = &Ks[buf][(kb * 32 + l32) * KP + 8 * hl];
-      const bf16_t* vr = &Vs[buf][(kb * 32 + l32) * KP + 8 * hl];
+      const int P = kb * 32 + l32;
+      const bf16_t* kr = &Ks[buf][P * DH];
+      const bf16_t* vr = &Vs[buf][P * DH];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        s[kb] = mfma32x32x16(ld8(kr + 16 * ks), qf[ks], s[kb]);
-        dp[kb] = mfma32x32x16(ld8(vr + 16 * ks), gf[ks], dp[kb]);
+        const int c = 8 * ((2 * ks + hl) ^ cswz<DH>(P));
+        s[kb] = mfma32x32x16(ld8(kr + c), qf[ks], s[kb]);
+        dp[kb] = mfma32x32x16(ld8(vr + c), gf[ks], dp[kb]);
       }
     }
     // dS^T = P^T (dP^T - D); register r of lane half hl holds key
@@ -161,14 +176,16 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
       }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const bf16_t* ktr = &Kt[buf][(db * 32 + l32) * VP + 8 * hl];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
-          acc[db] = mfma32x32x16(ld8(ktr + kb * 32 + 16 * st), dsf[kb][st], acc[db]);
+        for (int st = 0; st < 2; ++st) {
+          const int o = (kb * 32 + 16 * st) * DH;
+          acc[db] = mfma32x32x16(ld_tr8(&Ks[buf][t_base[0][db] + o], &Ks[buf][t_base[1][db] + o]),
+                                 dsf[kb][st], acc[db]);
+        }
     }
-    if (jt + 1 < n_tiles) sstore(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(kVmcntPending<0>());  // this wave's tile loads have landed
     __syncthreads();
   }
   if (q_row < N) {
@@ -198,12 +215,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
     const bf16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ dsum,
     int B, int N, int H, int G, int64_t t_cap, float sl2, float scale, float* __restrict__ dkv) {
-  constexpr int BK = 128, BQ = 64, KP = DH + 8, QP = BQ + 8, NKS = DH / 16, NDB = DH / 32;
-  constexpr int VITEMS = (BQ / 4) * (DH / 8);  // threads loading 4 rows x 8 dims of Q and dO
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[2][BQ * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t Gs[2][BQ * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t Qt[2][DH * QP];
-  __shared__ __attribute__((aligned(16))) bf16_t Gt[2][DH * QP];
+  constexpr int BK = 128, BQ = 64, NKS = DH / 16, NDB = DH / 32;
+  constexpr int TLD = BQ * DH * 2 / 1024 / 4;  // 1 KB loads per wave per tile (Q and dO each)
+  constexpr int RPC = 1024 / (DH * 2);         // rows per 1 KB
+  __shared__ __attribute__((aligned(1024))) bf16_t Qs[2][BQ * DH];
+  __shared__ __attribute__((aligned(1024))) bf16_t Gs[2][BQ * DH];
   __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
   __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
 
@@ -228,23 +244,40 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
   const int t_first = kblk * BK;
   const int n_it = (N - t_first + BQ - 1) / BQ;  // query tiles of head g*hpg + hh
 
-  u32x4 rq[4], rg[4];
-  float rl = 0.f, rd = 0.f;
-  // rows past N are loaded from row N-1 and zeroed; their lse is +inf (P = 0)
+  // Q and dO tiles go global -> LDS directly: load instruction i of wave w
+  // fills the 1 KB at LDS chunk w*TLD + i, lane l its 16 bytes at +16*l.  LDS
+  // row P holds tile row bperm(P) (the permuted feed), chunks swizzled by
+  // cswz(P); the rows of head h are H*DH apart in Q and dO.  Rows past N lie
+  // outside the buffer range and read as zeros; their lse is +inf (P = 0).
   const int h = g * hpg + hh;
-  auto gload = [&](int it) {
-    const int t0 = t_first + it * BQ;
-    if (tid < VITEMS) {
-      const int kq = tid & 15, dc = tid >> 4;
+  uint32_t t_src[TLD];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = t0 + 4 * kq + r;
-        const int64_t off = (static_cast<int64_t>(b * N + min(t, N - 1)) * H + h) * DH + 8 * dc;
-        const u32x4 a = *reinterpret_cast<const u32x4*>(Q + off);
-        const u32x4 c = *reinterpret_cast<const u32x4*>(dO + off);
-        rq[r] = t < N ? a : u32x4{0u, 0u, 0u, 0u};
-        rg[r] = t < N ? c : u32x4{0u, 0u, 0u, 0u};
-      }
+  for (int i = 0; i < TLD; ++i) {
+    const int P = (wave * TLD + i) * RPC + lane / (DH / 8), c = lane % (DH / 8);
+    t_src[i] = static_cast<uint32_t>((bperm(P) * H * DH + 8 * (c ^ cswz<DH>(P))) * 2);
+  }
+  // transposed reads: lane (group row r, group G, half hl) addresses dims
+  // db*32 + 16G + 4(r%4) .. of tile row 8hl + 4q + r/4 (+ 32qb + 16st)
+  int t_base[2][NDB];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int r = lane & 15, G = (lane >> 4) & 1;
+      const int P = bperm(8 * hl + 4 * q + (r >> 2)), d = db * 32 + 16 * G + 4 * (r & 3);
+      t_base[q][db] = P * DH + 8 * ((d >> 3) ^ cswz<DH>(P)) + (d & 7);
+    }
+  float rl = 0.f, rd = 0.f;
+  auto gload = [&](int it, int buf) {
+    const int t0 = t_first + it * BQ;
+    const int nrow = min(BQ, N - t0);
+    const int64_t base = (static_cast<int64_t>(b) * N + t0) * H * DH + static_cast<int64_t>(h) * DH;
+    const uint32_t bytes = static_cast<uint32_t>(((nrow - 1) * H + 1) * DH * 2);
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, bytes), grs = make_rsrc(dO + base, bytes);
+#pragma unroll
+    for (int i = 0; i < TLD; ++i) {
+      buffer_load_lds16(qrs, (lds_void_t*)(&Qs[buf][(wave * TLD + i) * 512]), t_src[i]);
+      buffer_load_lds16(grs, (lds_void_t*)(&Gs[buf][(wave * TLD + i) * 512]), t_src[i]);
     }
     if (tid < BQ) {
       const int t = t0 + tid;
@@ -255,16 +288,6 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
     }
   };
   auto sstore = [&](int buf) {
-    if (tid < VITEMS) {
-      const int kq = tid & 15, dc = tid >> 4;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        *reinterpret_cast<u32x4*>(&Qs[buf][bperm(4 * kq + r) * KP + 8 * dc]) = rq[r];
-        *reinterpret_cast<u32x4*>(&Gs[buf][bperm(4 * kq + r) * KP + 8 * dc]) = rg[r];
-      }
-      store_v_transposed(Qt[buf], QP, 8 * dc, 4 * kq, rq);
-      store_v_transposed(Gt[buf], QP, 8 * dc, 4 * kq, rg);
-    }
     if (tid < BQ) {
       Ls[buf][tid] = rl;
       Ds[buf][tid] = rd;
@@ -277,24 +300,27 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
     adk[db] = f32x16{};
     adv[db] = f32x16{};
   }
-  gload(0);
+  gload(0, 0);
   sstore(0);
+  __builtin_amdgcn_s_waitcnt(kVmcntPending<0>());  // this wave's tile loads have landed
   __syncthreads();
   for (int it = 0; it < n_it; ++it) {
     const int buf = it & 1;
     const int t0 = t_first + it * BQ;
-    if (it + 1 < n_it) gload(it + 1);
+    if (it + 1 < n_it) gload(it + 1, buf ^ 1);
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       s[qb] = f32x16{};
       dp[qb] = f32x16{};
-      const bf16_t* qr = &Qs[buf][(qb * 32 + l32) * KP + 8 * hl];
-      const bf16_t* gr = &Gs[buf][(qb * 32 + l32) * KP + 8 * hl];
+      const int P = qb * 32 + l32;
+      const bf16_t* qr = &Qs[buf][P * DH];
+      const bf16_t* gr = &Gs[buf][P * DH];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        s[qb] = mfma32x32x16(ld8(qr + 16 * ks), kf[ks], s[qb]);
-        dp[qb] = mfma32x32x16(ld8(gr + 16 * ks), vf[ks], dp[qb]);
+        const int c = 8 * ((2 * ks + hl) ^ cswz<DH>(P));
+        s[qb] = mfma32x32x16(ld8(qr + c), kf[ks], s[qb]);
+        dp[qb] = mfma32x32x16(ld8(gr + c), vf[ks], dp[qb]);
       }
     }
     // register r of lane half hl holds query qb*32 + 16*(r/8) + 8*hl + r%8 of
@@ -319,17 +345,19 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
       }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const bf16_t* gtr = &Gt[buf][(db * 32 + l32) * QP + 8 * hl];
-      const bf16_t* qtr = &Qt[buf][(db * 32 + l32) * QP + 8 * hl];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          adv[db] = mfma32x32x16(ld8(gtr + qb * 32 + 16 * st), pf[qb][st], adv[db]);
-          adk[db] = mfma32x32x16(ld8(qtr + qb * 32 + 16 * st), dsf[qb][st], adk[db]);
+          const int o = (qb * 32 + 16 * st) * DH;
+          adv[db] = mfma32x32x16(ld_tr8(&Gs[buf][t_base[0][db] + o], &Gs[buf][t_base[1][db] + o]),
+                                 pf[qb][st], adv[db]);
+          adk[db] = mfma32x32x16(ld_tr8(&Qs[buf][t_base[0][db] + o], &Qs[buf][t_base[1][db] + o]),
+                                 dsf[qb][st], adk[db]);
         }
     }
     if (it + 1 < n_it) sstore(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(kVmcntPending<0>());  // this wave's tile loads have landed
     __syncthreads();
   }
   if (k_row < N) {
