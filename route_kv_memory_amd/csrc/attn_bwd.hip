@@ -62,7 +62,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // transposed for dQ.
 // ---------------------------------------------------------------------------
 template <int DH>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
     const bf16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ dsum,
     int B, int N, int H, int G, int64_t t_cap, float sl2, float scale, int n_qblk, int n_units,
