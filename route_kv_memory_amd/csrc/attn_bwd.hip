@@ -209,9 +209,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 // transposed (Q^T, dO^T), with each row's log-sum-exp (log2 units) and D.  The
 // head's share goes to its own slice of ``dkv`` ([hpg][B, N, 2, G, DH]), summed
 // over the heads afterwards in a fixed order.
+// MODE 0 computes dK and dV together (K, V fragments and both accumulators in
+// registers: one workgroup per CU); MODE 1 computes dK alone and MODE 2 dV
+// alone, each recomputing the scores, in few enough registers for two
+// workgroups per CU (two waves per SIMD).
 // ---------------------------------------------------------------------------
-template <int DH>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
+template <int DH, int MODE>
+__global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void attn_bwd_dkv_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
     const bf16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ dsum,
     int B, int N, int H, int G, int64_t t_cap, float sl2, float scale, float* __restrict__ dkv) {
@@ -231,14 +235,15 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
   const int k_row = kblk * BK + wave * 32 + l32;
   const int64_t kvoff =
       ((static_cast<int64_t>(b) * G + g) * t_cap + min(k_row, N - 1)) * DH + 8 * hl;
+  constexpr bool WK = MODE != 2, WV = MODE != 1;  // dK / dV computed here
   bf16x8 kf[NKS], vf[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     kf[ks] = ld8(Kc + kvoff + 16 * ks);
-    vf[ks] = ld8(Vc + kvoff + 16 * ks);
-    if (k_row >= N) {
-      kf[ks] = bf16x8{};
-      vf[ks] = bf16x8{};
+    if (k_row >= N) kf[ks] = bf16x8{};
+    if constexpr (WK) {
+      vf[ks] = ld8(Vc + kvoff + 16 * ks);
+      if (k_row >= N) vf[ks] = bf16x8{};
     }
   }
   const int t_first = kblk * BK;
@@ -320,7 +325,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
       for (int ks = 0; ks < NKS; ++ks) {
         const int c = 8 * ((2 * ks + hl) ^ cswz<DH>(P));
         s[qb] = mfma32x32x16(ld8(qr + c), kf[ks], s[qb]);
-        dp[qb] = mfma32x32x16(ld8(gr + c), vf[ks], dp[qb]);
+        if constexpr (WK) dp[qb] = mfma32x32x16(ld8(gr + c), vf[ks], dp[qb]);
       }
     }
     // register r of lane half hl holds query qb*32 + 16*(r/8) + 8*hl + r%8 of
@@ -338,10 +343,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
           float p = __builtin_amdgcn_exp2f(fmaf(s[qb][r], sl2, -Ls[buf][q0 + j]));
           if (t0 + q0 + j < k_row) p = 0.f;
           pv[j] = p;
-          dv[j] = p * (dp[qb][r] - Ds[buf][q0 + j]);
+          if constexpr (WK) dv[j] = p * (dp[qb][r] - Ds[buf][q0 + j]);
         }
-        pf[qb][st] = pack_bf16x8(pv);
-        dsf[qb][st] = pack_bf16x8(dv);
+        if constexpr (WV) pf[qb][st] = pack_bf16x8(pv);
+        if constexpr (WK) dsf[qb][st] = pack_bf16x8(dv);
       }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
@@ -350,10 +355,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           const int o = (qb * 32 + 16 * st) * DH;
-          adv[db] = mfma32x32x16(ld_tr8(&Gs[buf][t_base[0][db] + o], &Gs[buf][t_base[1][db] + o]),
-                                 pf[qb][st], adv[db]);
-          adk[db] = mfma32x32x16(ld_tr8(&Qs[buf][t_base[0][db] + o], &Qs[buf][t_base[1][db] + o]),
-                                 dsf[qb][st], adk[db]);
+          if constexpr (WV)
+            adv[db] = mfma32x32x16(ld_tr8(&Gs[buf][t_base[0][db] + o], &Gs[buf][t_base[1][db] + o]),
+                                   pf[qb][st], adv[db]);
+          if constexpr (WK)
+            adk[db] = mfma32x32x16(ld_tr8(&Qs[buf][t_base[0][db] + o], &Qs[buf][t_base[1][db] + o]),
+                                   dsf[qb][st], adk[db]);
         }
     }
     if (it + 1 < n_it) sstore(buf ^ 1);
@@ -372,8 +379,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(
                              adk[db][4 * rq4 + 2] * scale, adk[db][4 * rq4 + 3] * scale};
         const float v4[4] = {adv[db][4 * rq4], adv[db][4 * rq4 + 1], adv[db][4 * rq4 + 2],
                              adv[db][4 * rq4 + 3]};
-        store4(out + d, k4);
-        store4(out + static_cast<int64_t>(G) * DH + d, v4);
+        if constexpr (WK) store4(out + d, k4);
+        if constexpr (WV) store4(out + static_cast<int64_t>(G) * DH + d, v4);
       }
   }
 }
@@ -400,6 +407,9 @@ hipError_t sum_slices(const float* part, int n_slices, int64_t n4, float* out, h
   return hipGetLastError();
 }
 
+// dK and dV in separate passes (MODE 1 then 2) or together (0).
+constexpr int kDkvMode = 1;
+
 size_t attn_bwd_mfma_ws_bytes(int B, int N, int H, int G, int dh) {
   return H / G > 1 ? sizeof(float) * static_cast<size_t>(H / G) * B * N * 2 * G * dh : 0;
 }
@@ -418,13 +428,19 @@ hipError_t attn_bwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, cons
   if (dh == 128) {
     hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, dim3(grid_q), dim3(256), 0, s, q, k, v, d_o, lse,
                        dsum, B, N, H, G, t_cap, sl2, scale, n_qblk, n_units, dq);
-    hipLaunchKernelGGL(attn_bwd_dkv_kernel<128>, dim3(grid_k), dim3(256), 0, s, q, k, v, d_o, lse,
-                       dsum, B, N, H, G, t_cap, sl2, scale, dst);
+    hipLaunchKernelGGL((attn_bwd_dkv_kernel<128, kDkvMode>), dim3(grid_k), dim3(256), 0, s, q, k, v,
+                       d_o, lse, dsum, B, N, H, G, t_cap, sl2, scale, dst);
+    if (kDkvMode != 0)
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<128, 2>), dim3(grid_k), dim3(256), 0, s, q, k, v, d_o,
+                         lse, dsum, B, N, H, G, t_cap, sl2, scale, dst);
   } else {
     hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, dim3(grid_q), dim3(256), 0, s, q, k, v, d_o, lse,
                        dsum, B, N, H, G, t_cap, sl2, scale, n_qblk, n_units, dq);
-    hipLaunchKernelGGL(attn_bwd_dkv_kernel<64>, dim3(grid_k), dim3(256), 0, s, q, k, v, d_o, lse,
-                       dsum, B, N, H, G, t_cap, sl2, scale, dst);
+    hipLaunchKernelGGL((attn_bwd_dkv_kernel<64, kDkvMode>), dim3(grid_k), dim3(256), 0, s, q, k, v,
+                       d_o, lse, dsum, B, N, H, G, t_cap, sl2, scale, dst);
+    if (kDkvMode != 0)
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<64, 2>), dim3(grid_k), dim3(256), 0, s, q, k, v, d_o,
+                         lse, dsum, B, N, H, G, t_cap, sl2, scale, dst);
   }
   if (hpg > 1) {
     const int64_t n4 = static_cast<int64_t>(B) * N * 2 * G * dh / 4;
