@@ -4,6 +4,10 @@
 
 namespace mka {
 
+// s_waitcnt immediate that waits for every LDS operation of the wave
+// (vmcnt and expcnt left at their maxima).
+constexpr int kLgkmcntZero = 0xF | (0x3 << 14) | (0x7 << 4);
+
 // ---------------------------------------------------------------------------
 // bf16 MFMA GEMM.  Workgroup tile 256 (M) x BN (N), 8 waves; each wave owns
 // 128 x BN/4 of C as 4 x BN/128 blocks of MFMA 32x32x16.  The MFMA computes
@@ -38,6 +42,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(
   constexpr int BM = C::BM, BK = C::BK, ROWB = C::ROWB, STAGES = C::STAGES, NB = C::NB;
   constexpr int WN = C::WN;
   static_assert(C::LOADS * NW * 1024 == C::SLICE, "slice must split evenly over the waves");
+  static_assert(STAGES >= 3, "the ring holds the slice in use, the next one and one in flight");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[STAGES * C::SLICE];
 
   const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
@@ -56,7 +61,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(
   }
   const int m0 = tm * BM, n0 = tn * BN;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
   const int wm = wave & 1, wn = wave >> 1, h = lane >> 5, l32 = lane & 31;
 
   // This lane's rows and byte offsets for each of its load instructions of a
@@ -100,37 +106,76 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(
 
   const int nk = K / BK;
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
+  for (int s = 0; s < STAGES; ++s)
     if (s < nk) issue(s, s);
-  for (int kt = 0; kt < nk; ++kt) {
-    // slice kt has landed once at most the STAGES-2 younger slices are pending
-    if (kt + STAGES - 2 < nk) {
-      __builtin_amdgcn_s_waitcnt(kVmcntPending<C::LOADS * (STAGES - 2)>());
-    } else {
-      __builtin_amdgcn_s_waitcnt(kVmcntPending<0>());
-    }
-    // Every wave's part of slice kt is in LDS (each waited for its own loads)
-    // and every wave is done reading slice kt-1 (its MFMAs consumed the
-    // reads).  A bare barrier: a fence here would wait for the prefetches too.
-    __builtin_amdgcn_s_barrier();
-    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+  // Fragments are double-buffered in registers: a slice's fragments are read
+  // from LDS during the previous slice's MFMAs, so no wave starts a slice
+  // waiting on LDS.  The barrier of iteration kt therefore waits until slice
+  // kt+1 has landed; and since every wave has slice kt in registers by then
+  // (reads complete before the barrier), slice kt's stage is refilled with
+  // slice kt+STAGES right after it: STAGES-1 slices stay in flight.
+  typedef bf16x8 FragA[2][4];
+  typedef bf16x8 FragB[2][NB];
+  auto read_slice = [&](int kt, FragA& fa, FragB& fb) {
     const unsigned char* As = lds + (kt % STAGES) * C::SLICE;
     const unsigned char* Bs = As + C::A_BYTES;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 fa[4], fb[NB];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8*>(As + frag(wm * 128 + i * 32 + l32, 2 * ks + h));
+        fa[ks][i] =
+            *reinterpret_cast<const bf16x8*>(As + frag(wm * 128 + i * 32 + l32, 2 * ks + h));
 #pragma unroll
       for (int j = 0; j < NB; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8*>(Bs + frag(wn * WN + j * 32 + l32, 2 * ks + h));
+        fb[ks][j] = *reinterpret_cast<const bf16x8*>(Bs + frag(wn * WN + j * 32 + l32, 2 * ks + h));
+    }
+  };
+  // One slice: wait for slice kt+1, barrier, refill slice kt's stage, read
+  // slice kt+1's fragments into (na, nb) while the MFMAs consume (ca, cb).
+  // After the last slice the read takes a stale stage and is not used.
+  auto step = [&](int kt, const FragA& ca, const FragB& cb, FragA& na, FragB& nb) {
+    if (kt + STAGES - 1 < nk) {
+      __builtin_amdgcn_s_waitcnt(kVmcntPending<C::LOADS * (STAGES - 2)>());
+    } else {
+      __builtin_amdgcn_s_waitcnt(kVmcntPending<0>());
+    }
+    __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
+    // A bare barrier: a fence here would wait for the prefetches too.
+    __builtin_amdgcn_s_barrier();
+    if (kt + STAGES < nk) issue(kt + STAGES, kt % STAGES);
+    read_slice(kt + 1, na, nb);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = mfma32x32x16(fb[j], fa[i], acc[i][j]);
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma32x32x16(cb[ks][j], ca[ks][i], acc[i][j]);
+    // one LDS read after each MFMA, the rest at the end
+    constexpr int R = (BK / 16) * (4 + NB), F = (BK / 16) * 4 * NB;
+    constexpr int P = R < F ? R : F;
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    if constexpr (F > P) __builtin_amdgcn_sched_group_barrier(0x008, F - P, 0);
+    if constexpr (R > P) __builtin_amdgcn_sched_group_barrier(0x100, R - P, 0);
+  };
+  FragA xa, ya;
+  FragB xb, yb;
+  if (STAGES - 1 < nk) {
+    __builtin_amdgcn_s_waitcnt(kVmcntPending<C::LOADS * (STAGES - 1)>());
+  } else {
+    __builtin_amdgcn_s_waitcnt(kVmcntPending<0>());
   }
+  __builtin_amdgcn_s_barrier();
+  read_slice(0, xa, xb);
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, xa, xb, ya, yb);
+    step(kt + 1, ya, yb, xa, xb);
+  }
+  if (kt < nk) step(kt, xa, xb, ya, yb);
 
   // Lane holds output row m = ... + l32 and columns n = ... + 8*(r/4) + 4h + (r%4).
 #pragma unroll

@@ -45,6 +45,15 @@ size_t simhash_ws_bytes(int rows, int B, int D);
 hipError_t simhash_rows(const float* v, int64_t v_bstride, int rows, int B, int D,
                         const float* proj, int nbits, uint64_t* codes, int64_t codes_bstride,
                         void* ws, hipStream_t s);
+// The same in two parts, when the rows take the certified bf16 path
+// (simhash_prepared_path): the hyperplanes split into simhash_prep_bytes(D)
+// bytes of ``prep`` (depends on proj only), then the codes of the rows.
+bool simhash_prepared_path(int rows, int B, int D);
+size_t simhash_prep_bytes(int D);
+hipError_t simhash_prepare(const float* proj, int nbits, int D, void* prep, hipStream_t s);
+hipError_t simhash_rows_prepared(const float* v, int64_t v_bstride, int rows, int B, int D,
+                                 const float* proj, int nbits, const void* prep, uint64_t* codes,
+                                 int64_t codes_bstride, hipStream_t s);
 // Few rows (decode): split over D, partial projections in ws, then select.
 constexpr int kFewRows = 8;
 size_t retrieve_few_ws_bytes(int rows, int D);

@@ -10,6 +10,8 @@
 // The sign of each projection decides an integer, so the dot products are
 // accumulated in float64 from the float32 operands (each product is exact in
 // float64): the code is then the sign of an almost exact value.
+#include <cmath>
+
 #include "kernels.h"
 
 namespace mka {
@@ -158,6 +160,293 @@ __global__ __launch_bounds__(256) void simhash_finalize_kernel(const double* __r
   if (lane == 0) codes[b * c_bstride + row] = code;
 }
 
+// ---------------------------------------------------------------------------
+// SimHash codes of many rows on bf16 MFMA, every sign certified.
+//
+// Each float32 operand is split into bf16 parts x = h + l + r.  The rows a
+// are split by truncation (h is a with its low 16 bits cleared, l the same of
+// a - h, both subtractions exact): |a - h| < 2^-7 |a|, |l| < 2^-7 |a|,
+// |r| < 2^-14 |a|.  The hyperplanes p are split once per call with rounding
+// to nearest even: |p - h| <= 2^-8 |p|, |l| <= 2^-8 (1 + 2^-8) |p|,
+// |r| <= 2^-16 |p|.  The product a . p is approximated by
+// s = sum_k (h_a h_p + h_a l_p + l_a h_p), the bf16 products being exact in
+// float32, on MFMA 32x32x16 with float32 accumulation.  Per channel the
+// dropped terms h_a r_p + l_a l_p + l_a r_p + r_a p are below
+// (2^-14 + 2^-15 + 2^-16 + 2^-21) |a_k||p_k| and the kept ones below
+// (1 + 2^-6) |a_k||p_k|; n float32 additions in any order, each with relative
+// error below 2^-23, add at most gamma_n = n 2^-23 / (1 - n 2^-23) times the
+// sum of their magnitudes.  So
+//   |s - a . p| <= ((1 + 2^-6) gamma_n + 2^-14 + 2^-15 + 2^-16 + 2^-21)
+//                  sum_k |a_k||p_k|,
+// and over a slice of the channels sum |a_k||p_k| <= ||a|| ||p|| (Cauchy-
+// Schwarz).  A bit whose |s| exceeds the bound has the sign of the exact
+// product; the others (about one in a hundred) are recomputed in float64 from
+// the float32 operands, each product exact, as in the kernel above.
+//
+// Workgroup: 32 rows x 64 hyperplanes; wave w of 16 sums one sixteenth of
+// the channels and the slices are added in float64 in slice order.  Per 32
+// channels a lane loads 16 consecutive floats of its row (lanes l and l+32
+// share a row), which feed two MFMA k-steps: the order of the channels inside
+// a k-step is free as long as both operands use the same one.
+// ---------------------------------------------------------------------------
+constexpr int kSplitWaves = 16, kFixChunk = 8;
+
+// bf16 bits of the high halves of x0 (low) and x1 (high): truncation.
+__device__ __forceinline__ uint32_t hi_pair(uint32_t x0, uint32_t x1) {
+  return __builtin_amdgcn_perm(x1, x0, 0x07060302u);
+}
+// Truncated bf16 parts of 8 floats.
+__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+  uint32_t wh[4], wl[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t b0 = __float_as_uint(x[2 * i]), b1 = __float_as_uint(x[2 * i + 1]);
+    const float r0 = x[2 * i] - __uint_as_float(b0 & 0xFFFF0000u);
+    const float r1 = x[2 * i + 1] - __uint_as_float(b1 & 0xFFFF0000u);
+    wh[i] = hi_pair(b0, b1);
+    wl[i] = hi_pair(__float_as_uint(r0), __float_as_uint(r1));
+  }
+  hi = __builtin_bit_cast(bf16x8, u32x4{wh[0], wh[1], wh[2], wh[3]});
+  lo = __builtin_bit_cast(bf16x8, u32x4{wl[0], wl[1], wl[2], wl[3]});
+}
+
+// Sum over the wave in a fixed butterfly: every lane ends with the same value.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// bf16 bits of x rounded to nearest even (finite x).
+__device__ __forceinline__ uint32_t rne_bf16_bits(uint32_t b) {
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) & 0xFFFF0000u;
+}
+
+// Hyperplanes split once per call, in the order the MFMA operands are loaded:
+// for channel pair-block pb (32 channels) and load q = 4 part + 2 t + st,
+// lane l holds 8 channels 32 pb + 16 (l / 32) + 8 st .. of plane 32 t + l % 32
+// (part 0: hi, 1: lo), so each load of the main kernel reads 1 KB
+// contiguous.  Planes j >= nbits are zero.  Blocks npairs.. compute
+// Pn[w][j] = ||proj row j|| over wave w's channel slice instead.
+__global__ __launch_bounds__(1024) void simhash_split_prep_kernel(const float* __restrict__ P,
+                                                                 int nbits, int D, int slice,
+                                                                 bf16_t* __restrict__ Ps,
+                                                                 double* __restrict__ Pn) {
+  const int npairs = D / 32;
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (static_cast<int>(blockIdx.x) < npairs) {
+    if (tid >= 512) return;
+    const int pb = blockIdx.x, q = tid >> 6;
+    const int part_ = q >> 2, t = (q >> 1) & 1, st = q & 1;
+    const int j = 32 * t + (lane & 31), k0 = 32 * pb + 16 * (lane >> 5) + 8 * st;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      uint32_t half[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float x = j < nbits ? P[static_cast<int64_t>(j) * D + k0 + e + u] : 0.f;
+        const uint32_t hb = rne_bf16_bits(__float_as_uint(x));
+        const float r = x - __uint_as_float(hb);  // exact
+        half[u] = (part_ == 0 ? hb : rne_bf16_bits(__float_as_uint(r))) >> 16;
+      }
+      w[e / 2] = half[0] | (half[1] << 16);
+    }
+    *reinterpret_cast<u32x4*>(Ps + ((static_cast<int64_t>(pb) * 8 + q) * 64 + lane) * 8) =
+        u32x4{w[0], w[1], w[2], w[3]};
+    return;
+  }
+  const int j = blockIdx.x - npairs, wv = tid >> 6;
+  const int k0 = wv * slice, k1 = min(D, k0 + slice);
+  double sq = 0.0;
+  for (int k = k0 + lane; k < k1; k += 64) {
+    const float x = j < nbits ? P[static_cast<int64_t>(j) * D + k] : 0.f;
+    sq = fma(static_cast<double>(x), static_cast<double>(x), sq);
+  }
+  sq = wave_sum_f64(sq);
+  if (lane == 0) Pn[wv * 64 + j] = sqrt(sq);
+}
+
+// Staged rows: a wave's 32 rows x 32 channels (4 KB) arrive by 4 direct-to-LDS
+// loads of 8 rows x 128 bytes; 16-byte chunk c of row r sits at
+// (r / 8) * 1024 + (r % 8) * 128 + 16 * (c ^ ((r / 2) % 8)), which keeps the
+// operand reads (lane: row l % 32, chunks 4 (l / 32) ..) free of bank conflicts.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) void*)(p)));
+}
+__device__ __forceinline__ int staged_chunk(int r, int c) {
+  return (r >> 3) * 1024 + (r & 7) * 128 + 16 * (c ^ ((r >> 1) & 7));
+}
+
+__global__ __launch_bounds__(1024) void simhash_split_kernel(
+    const float* __restrict__ v, int64_t v_bstride, int rows, int D, const float* __restrict__ P,
+    int nbits, const bf16_t* __restrict__ Ps, const double* __restrict__ Pn, int pairs_per_wave,
+    double err_factor, uint64_t* __restrict__ codes, int64_t c_bstride) {
+  // staging buffers (2 x 4 KB per wave) during the products, slice sums after
+  __shared__ __attribute__((aligned(1024))) float part[kSplitWaves][32][64];
+  __shared__ float nrm[kSplitWaves][32];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const int row0 = blockIdx.x * 32, b = blockIdx.y;
+  const float* vb = v + b * v_bstride;
+  const int npairs = D / 32;
+  const int p0 = wave * pairs_per_wave, p1 = min(npairs, p0 + pairs_per_wave);
+  unsigned char* stage = reinterpret_cast<unsigned char*>(&part[0][0][0]) + wave * 8192;
+  // load i of a pair: lane L fetches row 8i + L/8, chunk (L % 8) ^ ((row / 2) % 8),
+  // through a resource over this batch's rows (rows past the end read as zeros)
+  const __amdgpu_buffer_rsrc_t rsrc =
+      make_rsrc(vb, static_cast<uint32_t>(static_cast<int64_t>(rows) * D * 4));
+  const uint32_t row_bytes = static_cast<uint32_t>(D) * 4u;
+  uint32_t off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * i + (lane >> 3);
+    off[i] = static_cast<uint32_t>(row0 + r) * row_bytes + 16u * ((lane & 7) ^ ((r >> 1) & 7));
+  }
+  const bf16x8* pq = reinterpret_cast<const bf16x8*>(Ps) + lane;
+  // Loads of pair p (its stage buffer and its hyperplane registers).  The last
+  // iteration fetches its own pair again (p clamped), so every iteration
+  // issues the same loads and the waits below stay exact.
+  auto issue = [&](int p, int buf, bf16x8* pw) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      buffer_load_lds16(rsrc, (lds_void_t*)(stage + buf * 4096 + i * 1024), off[i] + 128u * p);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) pw[q] = pq[(p * 8 + q) * 64];
+  };
+  f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+  float sq = 0.f;
+  // One pair: fetch the next one (into the other stage buffer and register
+  // set), wait for this one, multiply.  Unrolled by two so that the register
+  // sets alternate without copies.
+  auto step = [&](int p, const bf16x8* pw, bf16x8* pn) {
+    const int buf = (p - p0) & 1;
+    issue(min(p + 1, p1 - 1), buf ^ 1, pn);  // the stage read two pairs ago
+    // pair p has landed once at most the 12 loads just issued are pending
+    __builtin_amdgcn_s_waitcnt(kVmcntPending<12>());
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      // The two chunks of this k-step, read in one block that also waits for
+      // them (the compiler would otherwise make every LDS read wait for the
+      // direct-to-LDS prefetch issued above as well).
+      const uint32_t base = lds_addr(stage + buf * 4096);
+      const uint32_t a0 = base + staged_chunk(l32, 4 * h + 2 * st);
+      const uint32_t a1 = base + staged_chunk(l32, 4 * h + 2 * st + 1);
+      f32x4 t0, t1;
+      asm volatile(
+          "ds_read_b128 %0, %2\n\t"
+          "ds_read_b128 %1, %3\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(t0), "=&v"(t1)
+          : "v"(a0), "v"(a1)
+          : "memory");
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        x[u] = t0[u];
+        x[4 + u] = t1[u];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sq = fmaf(x[e], x[e], sq);
+      bf16x8 ah, al;
+      split8(x, ah, al);
+      acc0 = mfma32x32x16(ah, pw[0 + st], acc0);
+      acc0 = mfma32x32x16(ah, pw[4 + st], acc0);
+      acc0 = mfma32x32x16(al, pw[0 + st], acc0);
+      acc1 = mfma32x32x16(ah, pw[2 + st], acc1);
+      acc1 = mfma32x32x16(ah, pw[6 + st], acc1);
+      acc1 = mfma32x32x16(al, pw[2 + st], acc1);
+    }
+  };
+  bf16x8 pa[8], pb[8];
+  if (p0 < p1) issue(p0, 0, pa);
+  int p = p0;
+  for (; p + 1 < p1; p += 2) {
+    step(p, pa, pb);
+    step(p + 1, pb, pa);
+  }
+  if (p < p1) step(p, pa, pb);
+  __builtin_amdgcn_s_waitcnt(kVmcntPending<0>());  // the last, repeated fetch too
+  __syncthreads();  // every wave is done with its staging buffers
+  // slice sums (register r: row acc_row(r, h), hyperplane l32 or 32 + l32)
+  // and the squared row norm over the slice
+  const float sqr = sq + __shfl_xor(sq, 32);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    part[wave][acc_row(r, h)][l32] = acc0[r];
+    part[wave][acc_row(r, h)][32 + l32] = acc1[r];
+  }
+  if (h == 0) nrm[wave][l32] = sqr;
+  __syncthreads();
+
+  // wave: rows 2*wave, 2*wave+1 of the tile; lane: hyperplane
+  constexpr int kRowsPerWave = 32 / kSplitWaves;
+  const bool on = lane < nbits;
+#pragma unroll 1
+  for (int rr = 0; rr < kRowsPerWave; ++rr) {
+    const int i = wave * kRowsPerWave + rr, row = row0 + i;
+    double s = 0.0, e = 0.0;
+#pragma unroll
+    for (int w = 0; w < kSplitWaves; ++w) {
+      s += static_cast<double>(part[w][i][lane]);
+      // the float32 sum of squares is inflated past its own rounding
+      e += sqrt(static_cast<double>(nrm[w][i]) * (1.0 + 1e-4)) * Pn[w * 64 + lane];
+    }
+    e = e * err_factor + 1e-30;
+    uint64_t code = __ballot(on && s > 0.0);
+    uint64_t amb = __ballot(on && fabs(s) <= e);
+    if (amb != 0) {  // uniform over the wave
+      // float64 recomputation: the row (up to kFixChunk float4 per lane at a
+      // time) stays in registers across the undecided hyperplanes, and each
+      // hyperplane's loads are issued together
+      const float* full = vb + static_cast<int64_t>(min(row, rows - 1)) * D;
+      const bool one_chunk = D <= 256 * kFixChunk;
+      f32x4 xa[kFixChunk];
+      auto load_chunk = [&](const float* src, int c0, f32x4* dst) {
+#pragma unroll
+        for (int u = 0; u < kFixChunk; ++u) {
+          const int k = c0 + 256 * u + 4 * lane;
+          dst[u] = k < D ? *reinterpret_cast<const f32x4*>(src + k) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      };
+      if (one_chunk) load_chunk(full, 0, xa);
+      while (amb != 0) {
+        const int j = __builtin_ctzll(amb);
+        amb &= amb - 1;
+        const float* pj = P + static_cast<int64_t>(j) * D;
+        double t[4] = {0.0, 0.0, 0.0, 0.0};
+        for (int c0 = 0; c0 < D; c0 += 256 * kFixChunk) {
+          if (!one_chunk) load_chunk(full, c0, xa);
+          f32x4 xp[kFixChunk];
+          load_chunk(pj, c0, xp);
+#pragma unroll
+          for (int u = 0; u < kFixChunk; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              t[c] = fma(static_cast<double>(xa[u][c]), static_cast<double>(xp[u][c]), t[c]);
+        }
+        const double tt = wave_sum_f64((t[0] + t[1]) + (t[2] + t[3]));
+        code = tt > 0.0 ? (code | (1ull << j)) : (code & ~(1ull << j));
+      }
+    }
+    if (lane == 0 && row < rows) codes[b * c_bstride + row] = code;
+  }
+}
+
+// The certified path: D a multiple of 32, enough rows to fill the GPU, and a
+// batch's rows addressable with 32-bit byte offsets; otherwise the float64
+// kernel.
+static bool simhash_use_split(int rows, int B, int D) {
+  return static_cast<int64_t>(rows) * B >= 256 && D % 32 == 0 &&
+         static_cast<int64_t>(rows) * D * 4 < (int64_t{1} << 31);
+}
+static int split_pairs_per_wave(int D) { return (D / 32 + kSplitWaves - 1) / kSplitWaves; }
+static size_t split_ws_bytes(int D) {
+  return static_cast<size_t>(2) * 64 * D * sizeof(bf16_t) + kSplitWaves * 64 * sizeof(double);
+}
+
 int simhash_splits(int rows, int B, int D) {
   const int tiles = ((rows + 63) / 64) * B;
   const int ktiles = (D + kHashKT - 1) / kHashKT;
@@ -165,9 +454,20 @@ int simhash_splits(int rows, int B, int D) {
   return ns < 1 ? 1 : (ns > ktiles ? ktiles : ns);
 }
 
-size_t simhash_ws_bytes(int rows, int B, int D) {
+static size_t fp64_ws_bytes(int rows, int B, int D) {
   const int ns = simhash_splits(rows, B, D);
   return ns > 1 ? sizeof(double) * static_cast<size_t>(ns) * B * rows * 64 : 0;
+}
+
+// Enough for any call with at most ``rows`` rows: below the certified path's
+// row count the float64 partials grow with the rows (the slice count is
+// capped there), so the largest such call bounds them.
+size_t simhash_ws_bytes(int rows, int B, int D) {
+  if (!simhash_use_split(rows, B, D)) return fp64_ws_bytes(rows, B, D);
+  const int below = (256 + B - 1) / B - 1;  // most rows that still take the float64 path
+  const size_t f = below > 0 ? fp64_ws_bytes(below < rows ? below : rows, B, D) : 0;
+  const size_t w = split_ws_bytes(D);
+  return f > w ? f : w;
 }
 
 // Launch the projections; with more than one slice the partials go to ``part``.
@@ -186,10 +486,48 @@ static hipError_t simhash_launch(const float* v, int64_t v_bstride, int rows, in
   return hipGetLastError();
 }
 
+bool simhash_prepared_path(int rows, int B, int D) { return simhash_use_split(rows, B, D); }
+size_t simhash_prep_bytes(int D) { return split_ws_bytes(D); }
+
+hipError_t simhash_prepare(const float* proj, int nbits, int D, void* prep, hipStream_t s) {
+  bf16_t* ps = static_cast<bf16_t*>(prep);
+  double* pn = reinterpret_cast<double*>(static_cast<char*>(prep) +
+                                         static_cast<size_t>(2) * 64 * D * sizeof(bf16_t));
+  hipLaunchKernelGGL(simhash_split_prep_kernel, dim3(D / 32 + 64), dim3(1024), 0, s, proj, nbits, D,
+                     32 * split_pairs_per_wave(D), ps, pn);
+  return hipGetLastError();
+}
+
+hipError_t simhash_rows_prepared(const float* v, int64_t v_bstride, int rows, int B, int D,
+                                 const float* proj, int nbits, const void* prep, uint64_t* codes,
+                                 int64_t codes_bstride, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const bf16_t* ps = static_cast<const bf16_t*>(prep);
+  const double* pn = reinterpret_cast<const double*>(
+      static_cast<const char*>(prep) + static_cast<size_t>(2) * 64 * D * sizeof(bf16_t));
+  const int ppw = split_pairs_per_wave(D);
+  // (1 + 2^-6) gamma_n + 2^-14 + 2^-15 + 2^-16 + 2^-21 for n = 3 * 32 * ppw
+  // additions, with 2% margin
+  const double n = 3.0 * 32.0 * ppw, u = std::ldexp(1.0, -23);
+  const double gamma = n * u / (1.0 - n * u);
+  const double factor =
+      1.02 * ((1.0 + std::ldexp(1.0, -6)) * gamma + std::ldexp(1.0, -14) + std::ldexp(1.0, -15) +
+              std::ldexp(1.0, -16) + std::ldexp(1.0, -21));
+  hipLaunchKernelGGL(simhash_split_kernel, dim3((rows + 31) / 32, B), dim3(1024), 0, s, v,
+                     v_bstride, rows, D, proj, nbits, ps, pn, ppw, factor, codes, codes_bstride);
+  return hipGetLastError();
+}
+
 hipError_t simhash_rows(const float* v, int64_t v_bstride, int rows, int B, int D,
                         const float* proj, int nbits, uint64_t* codes, int64_t codes_bstride,
                         void* ws, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  if (simhash_use_split(rows, B, D)) {
+    const hipError_t e = simhash_prepare(proj, nbits, D, ws, s);
+    if (e != hipSuccess) return e;
+    return simhash_rows_prepared(v, v_bstride, rows, B, D, proj, nbits, ws, codes, codes_bstride,
+                                 s);
+  }
   return simhash_launch(v, v_bstride, rows, B, D, proj, nbits, simhash_splits(rows, B, D), codes,
                         codes_bstride, static_cast<double*>(ws), s);
 }

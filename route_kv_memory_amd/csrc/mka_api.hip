@@ -405,7 +405,7 @@ constexpr int64_t kMaxDecodeCache = static_cast<int64_t>(1) << 26;  // rows
 // their fork/join records.
 struct Aux {
   hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr, done = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, mid = nullptr, done = nullptr;
   std::mutex lock;
 };
 
@@ -425,6 +425,7 @@ Aux* aux_for_current_device(int* rc) {
   if ((e = hipStreamCreateWithFlags(&a->stream, hipStreamNonBlocking)) != hipSuccess ||
       (e = hipEventCreateWithFlags(&a->fork, hipEventDisableTiming)) != hipSuccess ||
       (e = hipEventCreateWithFlags(&a->join, hipEventDisableTiming)) != hipSuccess ||
+      (e = hipEventCreateWithFlags(&a->mid, hipEventDisableTiming)) != hipSuccess ||
       (e = hipEventCreateWithFlags(&a->done, hipEventDisableTiming)) != hipSuccess) {
     *rc = hip_fail("prefill/aux", e);
     return nullptr;
@@ -440,6 +441,15 @@ Aux* aux_for_current_device(int* rc) {
 size_t prefill_chain_ws(const mka_dims* d) {
   const size_t w = ema_ws(d), wi = index_ws(d, d->seq / d->block + 1);
   return w > wi ? w : wi;
+}
+// The hyperplane split of the certified SimHash path, prepared on the auxiliary
+// stream for the retrieval on the main one: a region of its own.
+bool prefill_prepares_codes(const mka_dims* d) {
+  return routing_of(d).l3() && rows_of(d) > kFewRows &&
+         simhash_prepared_path(d->seq, d->batch, d->d_model);
+}
+size_t prefill_prep_ws(const mka_dims* d) {
+  return prefill_prepares_codes(d) ? round256(simhash_prep_bytes(d->d_model)) : 0;
 }
 size_t prefill_main_ws(const mka_dims* d) {
   size_t w = fuse_ws(d);
@@ -724,7 +734,7 @@ size_t mka_workspace_bytes(const mka_dims* d, int op, int64_t cache_len) {
     case MKA_OP_ROUTE: return route_ws(d);
     case MKA_OP_ATTN_DECODE: return cache_len > 0 ? decode_ws(d, cache_len) : 0;
     case MKA_OP_PREFILL:  // blocks completed by a call at any pos0: at most seq / block + 1
-      return prefill_chain_ws(d) + prefill_main_ws(d);
+      return prefill_chain_ws(d) + prefill_main_ws(d) + prefill_prep_ws(d);
     case MKA_OP_DECODE_STEP:
       return d->seq == 1 && cache_len > 0 ? decode_layout(d, cache_len).total : 0;
     case MKA_OP_FULL_PREFILL: return full_layout(d, false, 0).total;
@@ -912,18 +922,22 @@ int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weight
   if (!rt.l3()) n = 0;  // no block codes or projections without L3
   char* ws_chain = static_cast<char*>(ws);
   char* ws_main = ws_chain + prefill_chain_ws(d);
-  // The EMA scan and the block codes need only x and use no LDS, so they run
-  // on the auxiliary stream beside the query product (which fills every CU's
-  // LDS) and the block projections, needed only by later decode steps, follow
-  // them there; the retrieval joins the scan and codes after the router.  (The
-  // retrieval's fp64 products need LDS: beside the query product they would
-  // get only the CUs of its last tile round.)
+  char* ws_prep = ws_main + prefill_main_ws(d);
+  const bool prep = prefill_prepares_codes(d);
+  // The hyperplane split of the key codes, the EMA scan and the block codes
+  // need only the weights and x, so they run on the auxiliary stream beside the
+  // query product; the retrieval joins them after the router.  (The key codes
+  // beside the query product would get only the CUs of its last tile round.)
+  // The block projections, needed only by later decode steps, follow the
+  // retrieval on the auxiliary stream, so that they do not slow the router.
   Aux* aux = aux_for_current_device(&rc);
   if (aux == nullptr) return rc;
   std::lock_guard<std::mutex> guard(aux->lock);
   hipStream_t s2 = aux->stream;
   MKA_LAUNCH("prefill/fork", hipEventRecord(aux->fork, s));
   MKA_LAUNCH("prefill/fork", hipStreamWaitEvent(s2, aux->fork, 0));
+  if (prep)
+    MKA_LAUNCH("prefill/prep", simhash_prepare(w->proj, d->hash_bits, d->d_model, ws_prep, s2));
   if (rt.ema() && (rc = do_ema(d, x, pos0, st->ema_state, st->block_acc, out->l2,
                                st->block_means, st->nb_cap, ws_chain, s2)))
     return rc;
@@ -931,15 +945,25 @@ int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weight
                      w->proj, st->block_hash, ws_chain, s2)))
     return rc;
   MKA_LAUNCH("prefill/join", hipEventRecord(aux->join, s2));
+  if ((rc = do_route(d, x, w->w_q, w->w_r1, w->w_r2, out->q, out->lambda, ws_main, s))) return rc;
+  MKA_LAUNCH("prefill/join", hipStreamWaitEvent(s, aux->join, 0));
+  if (prep) {
+    MKA_LAUNCH("l3_retrieve/keys",
+               simhash_rows_prepared(out->l2, static_cast<int64_t>(d->seq) * d->d_model, d->seq,
+                                     d->batch, d->d_model, w->proj, d->hash_bits, ws_prep,
+                                     out->key, d->seq, s));
+    MKA_LAUNCH("l3_retrieve/topr", topr_rows(out->key, d->batch, d->seq, pos0, st->block_hash,
+                                             st->nb_cap, d->block, d->top_r, out->idx, s));
+  } else if (rt.l3() && (rc = do_retrieve(d, out->l2, w->proj, st->block_hash, st->nb_cap, pos0,
+                                          out->key, out->idx, ws_main, s))) {
+    return rc;
+  }
+  MKA_LAUNCH("prefill/join", hipEventRecord(aux->mid, s));
+  MKA_LAUNCH("prefill/join", hipStreamWaitEvent(s2, aux->mid, 0));
   if ((rc = do_block_kv(d, st->block_means, st->nb_cap, static_cast<int>(first),
                         static_cast<int>(n), w->w_k, w->w_v, st->block_kv, s2)))
     return rc;
   MKA_LAUNCH("prefill/join", hipEventRecord(aux->done, s2));
-  if ((rc = do_route(d, x, w->w_q, w->w_r1, w->w_r2, out->q, out->lambda, ws_main, s))) return rc;
-  MKA_LAUNCH("prefill/join", hipStreamWaitEvent(s, aux->join, 0));
-  if (rt.l3() && (rc = do_retrieve(d, out->l2, w->proj, st->block_hash, st->nb_cap, pos0,
-                                   out->key, out->idx, ws_main, s)))
-    return rc;
   if ((rc = do_fuse_kv(d, x, out->l2, st->block_means, st->nb_cap, out->idx, out->lambda, w->w_k,
                        w->w_v, st->k_cache, st->v_cache, pos0, layout_of(d, st), ws_main, s)))
     return rc;

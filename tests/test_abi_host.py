@@ -109,8 +109,11 @@ def test_workspace_sizes_and_rejection():
     retr = mka.mka_workspace_bytes(d, mka.MKA_OP_RETRIEVE)
     idx = mka.mka_workspace_bytes(d, mka.MKA_OP_INDEX, 33)
     # prefill: the EMA scan and block index (auxiliary stream) run beside the
-    # main stream's route, retrieval and fusion, so their regions add up
-    assert mka.mka_workspace_bytes(d, mka.MKA_OP_PREFILL) == max(ema, idx) + max(retr, fuse)
+    # main stream's route, retrieval and fusion, so their regions add up; the
+    # key codes' hyperplane split (bf16 hi/lo parts and 16 slice norms per
+    # hyperplane, prepared on the auxiliary stream) has a region of its own
+    prep = 2 * 64 * 3584 * 2 + 16 * 64 * 8
+    assert mka.mka_workspace_bytes(d, mka.MKA_OP_PREFILL) == max(ema, idx) + max(retr, fuse) + prep
     assert idx > 0  # few blocks: the projections are split over d_model
     dd = mka.dims(I.workload("qwen7b_decode_128k"))
     dec = mka.mka_workspace_bytes(dd, mka.MKA_OP_ATTN_DECODE, 131073)
