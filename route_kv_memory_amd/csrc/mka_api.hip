@@ -405,7 +405,7 @@ constexpr int64_t kMaxDecodeCache = static_cast<int64_t>(1) << 26;  // rows
 // their fork/join records.
 struct Aux {
   hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr, mid = nullptr, done = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, done = nullptr;
   std::mutex lock;
 };
 
@@ -425,7 +425,6 @@ Aux* aux_for_current_device(int* rc) {
   if ((e = hipStreamCreateWithFlags(&a->stream, hipStreamNonBlocking)) != hipSuccess ||
       (e = hipEventCreateWithFlags(&a->fork, hipEventDisableTiming)) != hipSuccess ||
       (e = hipEventCreateWithFlags(&a->join, hipEventDisableTiming)) != hipSuccess ||
-      (e = hipEventCreateWithFlags(&a->mid, hipEventDisableTiming)) != hipSuccess ||
       (e = hipEventCreateWithFlags(&a->done, hipEventDisableTiming)) != hipSuccess) {
     *rc = hip_fail("prefill/aux", e);
     return nullptr;
@@ -928,8 +927,8 @@ int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weight
   // need only the weights and x, so they run on the auxiliary stream beside the
   // query product; the retrieval joins them after the router.  (The key codes
   // beside the query product would get only the CUs of its last tile round.)
-  // The block projections, needed only by later decode steps, follow the
-  // retrieval on the auxiliary stream, so that they do not slow the router.
+  // The block projections, needed only by later decode steps, follow them
+  // there.
   Aux* aux = aux_for_current_device(&rc);
   if (aux == nullptr) return rc;
   std::lock_guard<std::mutex> guard(aux->lock);
@@ -945,6 +944,10 @@ int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weight
                      w->proj, st->block_hash, ws_chain, s2)))
     return rc;
   MKA_LAUNCH("prefill/join", hipEventRecord(aux->join, s2));
+  if ((rc = do_block_kv(d, st->block_means, st->nb_cap, static_cast<int>(first),
+                        static_cast<int>(n), w->w_k, w->w_v, st->block_kv, s2)))
+    return rc;
+  MKA_LAUNCH("prefill/join", hipEventRecord(aux->done, s2));
   if ((rc = do_route(d, x, w->w_q, w->w_r1, w->w_r2, out->q, out->lambda, ws_main, s))) return rc;
   MKA_LAUNCH("prefill/join", hipStreamWaitEvent(s, aux->join, 0));
   if (prep) {
@@ -958,12 +961,6 @@ int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weight
                                           out->key, out->idx, ws_main, s))) {
     return rc;
   }
-  MKA_LAUNCH("prefill/join", hipEventRecord(aux->mid, s));
-  MKA_LAUNCH("prefill/join", hipStreamWaitEvent(s2, aux->mid, 0));
-  if ((rc = do_block_kv(d, st->block_means, st->nb_cap, static_cast<int>(first),
-                        static_cast<int>(n), w->w_k, w->w_v, st->block_kv, s2)))
-    return rc;
-  MKA_LAUNCH("prefill/join", hipEventRecord(aux->done, s2));
   if ((rc = do_fuse_kv(d, x, out->l2, st->block_means, st->nb_cap, out->idx, out->lambda, w->w_k,
                        w->w_v, st->k_cache, st->v_cache, pos0, layout_of(d, st), ws_main, s)))
     return rc;

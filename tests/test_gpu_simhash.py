@@ -1,4 +1,5 @@
-"""Query codes of mka_l3_retrieve on the certified bf16 path, against the oracle.
+"""Query codes of mka_l3_retrieve on the certified bf16 path, against the oracle;
+block projections of mka_l3_block_kv at the workloads' widths.
 
 For enough rows (B * seq >= 256, D a multiple of 32) the codes come from
 bf16-split MFMA products whose signs are certified by an error bound, with
@@ -18,7 +19,7 @@ from oracle import mka_oracle as O
 from route_kv_memory_amd import inputs as I
 from route_kv_memory_amd import mka
 
-from .parity import ambiguous_mask, log
+from .parity import ambiguous_mask, check_close, log
 
 pytestmark = pytest.mark.gpu
 
@@ -83,3 +84,33 @@ def test_certified_codes(B, seq, D, nbits, block, top_r):
     want = np.stack([O.retrieve(got[b][None], bhash[b][None], positions, block, top_r)[0]
                      for b in range(B)])
     assert np.array_equal(idx.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("B,nb_cap,first,n_blocks,D,kvw", [
+    (2, 33, 0, 32, 3584, 512),     # Qwen2.5-7B layer, 2 x 4096 tokens of 128-token blocks
+    (1, 300, 3, 257, 4096, 1024),  # Llama-3.1-8B layer; ragged block range across row tiles
+])
+def test_block_projections(B, nb_cap, first, n_blocks, D, kvw):
+    """block_kv[b, blk] = m_blk [W_k; W_v]^T for the bf16 weights (split
+    products on MFMA), against float64 of the same float32 means and bf16
+    weights, at the float32 tolerance."""
+    rng = np.random.default_rng(D + n_blocks)
+    means = rng.normal(0.0, 0.09, (B, nb_cap, D)).astype(np.float32)
+    wk = torch.from_numpy(rng.normal(0.0, D ** -0.5, (kvw, D)).astype(np.float32)).bfloat16()
+    wv = torch.from_numpy(rng.normal(0.0, D ** -0.5, (kvw, D)).astype(np.float32)).bfloat16()
+    base = "llama8b_prefill_64k" if kvw == 1024 else "qwen7b_prefill_4k"
+    s = I.workload(base).replace(name=f"bkv_{D}", batch=B, d_model=D)
+    assert s.n_kv_heads * s.head_dim == kvw
+    d = mka.dims(s)
+    dev = torch.device("cuda")
+    out = torch.full((B, nb_cap, 2 * kvw), 7.0, dtype=torch.float32, device=dev)
+    log(f"  gpu: mka_l3_block_kv B={B} blocks {first}..{first + n_blocks} D={D} kvw={kvw}")
+    mka.mka_l3_block_kv(d, torch.from_numpy(means).to(dev), nb_cap, first, n_blocks,
+                        wk.to(dev), wv.to(dev), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    w = torch.cat([wk, wv]).float().numpy().astype(np.float64)
+    want = means[:, first:first + n_blocks].astype(np.float64) @ w.T
+    check_close("block_kv", got[:, first:first + n_blocks], want, "f32")
+    # rows outside the range are left alone
+    assert np.all(got[:, :first] == 7.0) and np.all(got[:, first + n_blocks:] == 7.0)
