@@ -88,6 +88,13 @@ hipError_t gemm_bf16(const bf16_t* a, int lda, const bf16_t* b0, const bf16_t* b
 template <class Epi>
 hipError_t gemm_f32(const float* a, int lda, const float* b0, const float* b1, int n_split,
                     int M, int N, int K, const Epi& epi, hipStream_t s);
+// The same with one B matrix, the reduction split into ranges when the output
+// has too few tiles to fill the GPU; the float32 partials take
+// gemm_bf16_splitk_ws_bytes(M, N, K) bytes of ``ws`` (none when that is 0).
+size_t gemm_bf16_splitk_ws_bytes(int M, int N, int K);
+template <class Epi>
+hipError_t gemm_bf16_splitk(const bf16_t* a, int lda, const bf16_t* b, int M, int N, int K,
+                            const Epi& epi, float* ws, hipStream_t s);
 // Small-M product (M <= 8), one wave per output column: the decode path.
 template <typename T, class Epi>
 hipError_t gemv(const T* a, int lda, int M, const T* b0, const T* b1, int n_split, int N, int K,

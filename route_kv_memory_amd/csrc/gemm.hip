@@ -34,10 +34,12 @@ struct GemmCfg {
   static constexpr int NB = WN / 32;                        // MFMA blocks per wave in N
 };
 
+// blockIdx.y selects a range of K_len reduction indices starting at
+// blockIdx.y * K_len (split-K; K is the row length of B).
 template <int BN, int NW, class Epi>
 __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(
     const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B0,
-    const bf16_t* __restrict__ B1, int n_split, int M, int N, int K, Epi epi) {
+    const bf16_t* __restrict__ B1, int n_split, int M, int N, int K, int K_len, Epi epi) {
   using C = GemmCfg<BN, NW>;
   constexpr int BM = C::BM, BK = C::BK, ROWB = C::ROWB, STAGES = C::STAGES, NB = C::NB;
   constexpr int WN = C::WN;
@@ -79,11 +81,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(
     const int chunk = (lane & 3) ^ ((row >> 2) & 3);
     if (is_a) {
       const int gm = min(m0 + row, M - 1);
-      src[j] = A + static_cast<int64_t>(gm) * lda + chunk * 8;
+      src[j] = A + static_cast<int64_t>(gm) * lda + blockIdx.y * K_len + chunk * 8;
     } else {
       const int gn = min(n0 + row, N - 1);
       src[j] = (gn < n_split ? B0 + static_cast<int64_t>(gn) * K
-                             : B1 + static_cast<int64_t>(gn - n_split) * K) + chunk * 8;
+                             : B1 + static_cast<int64_t>(gn - n_split) * K) +
+               blockIdx.y * K_len + chunk * 8;
     }
     dst[j] = (is_a ? 0 : C::A_BYTES) + ri * 1024;  // lane's 16 bytes land at +16*lane
   }
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(
   // fragment byte offset of row r, chunk c (16 bytes) within a slice operand
   auto frag = [](int r, int c) { return r * ROWB + ((c ^ ((r >> 2) & 3)) << 4); };
 
-  const int nk = K / BK;
+  const int nk = K_len / BK;
 #pragma unroll
   for (int s = 0; s < STAGES; ++s)
     if (s < nk) issue(s, s);
@@ -202,12 +205,77 @@ hipError_t gemm_bf16(const bf16_t* a, int lda, const bf16_t* b0, const bf16_t* b
   const int tiles256 = ((N + 255) / 256) * ((M + 255) / 256);
   if (tiles256 >= 256) {
     hipLaunchKernelGGL((gemm_bf16_kernel<256, kGemmWaves256, Epi>), dim3(tiles256),
-                       dim3(kGemmWaves256 * 64), 0, s, a, lda, b0, b1, n_split, M, N, K, epi);
+                       dim3(kGemmWaves256 * 64), 0, s, a, lda, b0, b1, n_split, M, N, K, K, epi);
   } else {
     const int tiles = ((N + 127) / 128) * ((M + 255) / 256);
     hipLaunchKernelGGL((gemm_bf16_kernel<128, 8, Epi>), dim3(tiles), dim3(512), 0, s, a, lda, b0,
-                       b1, n_split, M, N, K, epi);
+                       b1, n_split, M, N, K, K, epi);
   }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Split-K for products with few output tiles (the weight gradients: a few
+// hundred rows, thousands of columns, a reduction over all tokens): the
+// reduction is cut into S ranges, one grid row each, whose float32 partials go
+// to a workspace; a second kernel adds them in range order (deterministic)
+// and hands the sum to the epilogue.
+// ---------------------------------------------------------------------------
+struct EpiPart {  // partial of range blockIdx.y: row-major [S][M][N]
+  float* base;
+  int ldc;
+  int64_t stride;
+  __device__ __forceinline__ void store4(int m, int n, const float* v, int N) const {
+    float* p = base + blockIdx.y * stride + static_cast<int64_t>(m) * ldc + n;
+    for (int i = 0; i < 4 && n + i < N; ++i) p[i] = v[i];
+  }
+};
+
+template <class Epi>
+__global__ __launch_bounds__(256) void splitk_sum_kernel(const float* __restrict__ part, int S,
+                                                         int M, int N, Epi epi) {
+  const int64_t e = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  const int64_t total = static_cast<int64_t>(M) * N;
+  if (e >= total) return;
+  const int m = static_cast<int>(e / N), n = static_cast<int>(e - static_cast<int64_t>(m) * N);
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < S; ++sp) {
+    const float* p = part + sp * total + e;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] += p[i];
+  }
+  epi.store4(m, n, v, N);
+}
+
+// Ranges: as many as fill one round of the CUs (at most 8), each a multiple of
+// the k-slice; 1 when the product already has a round of tiles.
+int gemm_splitk_ranges(int M, int N, int K) {
+  const int tm = (M + 255) / 256;
+  if (((N + 255) / 256) * tm >= 256 || N % 4 != 0) return 1;
+  const int tiles = ((N + 127) / 128) * tm;
+  int S = 1;
+  for (int c = 2; c <= 8; ++c)
+    if (c * tiles <= 256 && K % (c * 32) == 0 && K / c >= 256) S = c;
+  return S;
+}
+
+size_t gemm_bf16_splitk_ws_bytes(int M, int N, int K) {
+  const int S = gemm_splitk_ranges(M, N, K);
+  return S > 1 ? sizeof(float) * static_cast<size_t>(S) * M * N : 0;
+}
+
+template <class Epi>
+hipError_t gemm_bf16_splitk(const bf16_t* a, int lda, const bf16_t* b, int M, int N, int K,
+                            const Epi& epi, float* ws, hipStream_t s) {
+  const int S = gemm_splitk_ranges(M, N, K);
+  if (S == 1) return gemm_bf16(a, lda, b, b, N, M, N, K, epi, s);
+  const int tiles = ((N + 127) / 128) * ((M + 255) / 256);
+  const EpiPart part{ws, N, static_cast<int64_t>(M) * N};
+  hipLaunchKernelGGL((gemm_bf16_kernel<128, 8, EpiPart>), dim3(tiles, S), dim3(512), 0, s, a, lda,
+                     b, b, N, M, N, K, K / S, part);
+  const int64_t quads = (static_cast<int64_t>(M) * N + 3) / 4;
+  hipLaunchKernelGGL((splitk_sum_kernel<Epi>), dim3(static_cast<unsigned>((quads + 255) / 256)),
+                     dim3(256), 0, s, ws, S, M, N, epi);
   return hipGetLastError();
 }
 
@@ -352,6 +420,11 @@ template hipError_t gemm_bf16<EpiStore<float>>(const bf16_t*, int, const bf16_t*
                                                 hipStream_t);
 template hipError_t gemm_bf16<EpiAdd>(const bf16_t*, int, const bf16_t*, const bf16_t*, int, int,
                                       int, int, const EpiAdd&, hipStream_t);
+template hipError_t gemm_bf16_splitk<EpiStore<float>>(const bf16_t*, int, const bf16_t*, int, int,
+                                                      int, const EpiStore<float>&, float*,
+                                                      hipStream_t);
+template hipError_t gemm_bf16_splitk<EpiAdd>(const bf16_t*, int, const bf16_t*, int, int, int,
+                                             const EpiAdd&, float*, hipStream_t);
 template hipError_t gemm_f32<EpiAdd>(const float*, int, const float*, const float*, int, int, int,
                                      int, const EpiAdd&, hipStream_t);
 template hipError_t gemm_f32<EpiStore<float>>(const float*, int, const float*, const float*, int,

@@ -508,7 +508,7 @@ FullWs full_layout(const mka_dims* d, bool decode, int64_t cache_len) {
 // type's product operands (transposed ones padded to Mp = M rounded up to 32
 // tokens, the products' reduction dimension).
 struct BwdWs {
-  size_t dsum, dq, dkv, dxf, dlam, dz, dm, part, pre, heads, gather;  // float32
+  size_t dsum, dq, dkv, dxf, dlam, dz, dm, part, pre, heads, gather, splitk;  // float32
   size_t dkv_a, dkv_t, wkv_t, xf, xf_t, dpre, dpre_t, q_t, wr1_t, wq_t, dq_a, dq_t, x_t;  // dtype
   size_t total;
   int Mp, nbs;
@@ -555,20 +555,33 @@ BwdWs bwd_layout(const mka_dims* d) {
   w.dq_a = bf ? take(el * M * qw) : 0;
   w.dq_t = take(el * qw * Mp);
   w.x_t = take(el * D * Mp);
+  if (bf) {  // the largest split-K partials among the products below
+    const int m = static_cast<int>(M), mp = w.Mp, dd = static_cast<int>(D);
+    const int q = static_cast<int>(qw), kv = static_cast<int>(kvw), rr = static_cast<int>(r);
+    size_t sk = 0;
+    for (size_t v : {gemm_bf16_splitk_ws_bytes(m, dd, 2 * kv), gemm_bf16_splitk_ws_bytes(kv, dd, mp),
+                     gemm_bf16_splitk_ws_bytes(m, rr, q), gemm_bf16_splitk_ws_bytes(rr, q, mp),
+                     gemm_bf16_splitk_ws_bytes(m, q, rr), gemm_bf16_splitk_ws_bytes(m, dd, q),
+                     gemm_bf16_splitk_ws_bytes(q, dd, mp)})
+      if (v > sk) sk = v;
+    w.splitk = take(sk);
+  }
   w.total = at;
   return w;
 }
 
+// The backward's products; bf16 ones split their reduction over ``sk`` (the
+// workspace's split-K region) when the output has too few tiles.
 template <typename T>
 hipError_t gemm_t(const T* a, int lda, const T* b, int M, int N, int K, const EpiStore<float>& e,
-                  hipStream_t s) {
-  if constexpr (std::is_same<T, bf16_t>::value) return gemm_bf16(a, lda, b, b, N, M, N, K, e, s);
+                  float* sk, hipStream_t s) {
+  if constexpr (std::is_same<T, bf16_t>::value) return gemm_bf16_splitk(a, lda, b, M, N, K, e, sk, s);
   else return gemm_f32(a, lda, b, b, N, M, N, K, e, s);
 }
 template <typename T>
-hipError_t gemm_t(const T* a, int lda, const T* b, int M, int N, int K, const EpiAdd& e,
+hipError_t gemm_t(const T* a, int lda, const T* b, int M, int N, int K, const EpiAdd& e, float* sk,
                   hipStream_t s) {
-  if constexpr (std::is_same<T, bf16_t>::value) return gemm_bf16(a, lda, b, b, N, M, N, K, e, s);
+  if constexpr (std::is_same<T, bf16_t>::value) return gemm_bf16_splitk(a, lda, b, M, N, K, e, sk, s);
   else return gemm_f32(a, lda, b, b, N, M, N, K, e, s);
 }
 
@@ -619,7 +632,7 @@ int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const
   auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   auto E = [&](size_t off) { return reinterpret_cast<T*>(ws + off); };
   float *dsum = F(L.dsum), *dq = F(L.dq), *dkv = F(L.dkv), *dxf = F(L.dxf), *dlam = F(L.dlam);
-  float *dz = F(L.dz), *dm = F(L.dm), *part = F(L.part), *pre = F(L.pre);
+  float *dz = F(L.dz), *dm = F(L.dm), *part = F(L.part), *pre = F(L.pre), *sk = F(L.splitk);
   T *dkv_t = E(L.dkv_t), *wkv_t = E(L.wkv_t), *xf = E(L.xf), *xf_t = E(L.xf_t);
   T *dpre = E(L.dpre), *dpre_t = E(L.dpre_t), *q_t = E(L.q_t), *wr1_t = E(L.wr1_t);
   T *wq_t = E(L.wq_t), *dq_t = E(L.dq_t), *x_t = E(L.x_t);
@@ -637,7 +650,7 @@ int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const
   MKA_LAUNCH("bwd/t", (transpose<T, T>(wv, D, kvw, D, kvw, 2 * kvw, wkv_t + kvw, s)));
   if (kBf) MKA_LAUNCH("bwd/cvt", (convert<float, T>(dkv, static_cast<int64_t>(M) * 2 * kvw,
                                                      const_cast<T*>(dkv_a), s)));
-  MKA_LAUNCH("bwd/dxf", gemm_t<T>(dkv_a, 2 * kvw, wkv_t, M, D, 2 * kvw, EpiStore<float>{dxf, D}, s));
+  MKA_LAUNCH("bwd/dxf", gemm_t<T>(dkv_a, 2 * kvw, wkv_t, M, D, 2 * kvw, EpiStore<float>{dxf, D}, sk, s));
   MKA_LAUNCH("bwd/t", (transpose<float, T>(dkv, 2 * kvw, M, 2 * kvw, Mp, Mp, dkv_t, s)));
   const T* xf_src = x;
   if (rt.ema()) {
@@ -646,9 +659,9 @@ int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const
     xf_src = xf;
   }
   MKA_LAUNCH("bwd/t", (transpose<T, T>(xf_src, D, M, D, Mp, Mp, xf_t, s)));
-  MKA_LAUNCH("bwd/dwk", gemm_t<T>(dkv_t, Mp, xf_t, kvw, D, Mp, EpiStore<float>{gr->dw_k, D}, s));
+  MKA_LAUNCH("bwd/dwk", gemm_t<T>(dkv_t, Mp, xf_t, kvw, D, Mp, EpiStore<float>{gr->dw_k, D}, sk, s));
   MKA_LAUNCH("bwd/dwv", gemm_t<T>(dkv_t + static_cast<size_t>(kvw) * Mp, Mp, xf_t, kvw, D, Mp,
-                                  EpiStore<float>{gr->dw_v, D}, s));
+                                  EpiStore<float>{gr->dw_v, D}, sk, s));
   // the fusion, the EMA's adjoint and the block means' adjoint
   MKA_LAUNCH("bwd/fuse", fuse_bwd<T>(x, rt.l2() ? fwd->l2 : nullptr, st->block_means, st->nb_cap,
                                      rt.l3() ? fwd->idx : nullptr, fwd->lambda, B, N, D,
@@ -662,14 +675,14 @@ int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const
                                         d->ema_decay, part, gr->dx, s));
   // router: dz, dW_r2, dpre; dW_r1 = dpre^T q; dq += dpre W_r1
   if (rt.learned()) {
-    MKA_LAUNCH("bwd/pre", gemm_t<T>(q, qw, wr1, M, r, qw, EpiStore<float>{pre, r}, s));
+    MKA_LAUNCH("bwd/pre", gemm_t<T>(q, qw, wr1, M, r, qw, EpiStore<float>{pre, r}, sk, s));
     MKA_LAUNCH("bwd/router", router_bwd<T>(fwd->lambda, dlam, pre, wr2, r, M, rt, dz, dpre,
                                            gr->dw_r2, s));
     MKA_LAUNCH("bwd/t", (transpose<T, T>(dpre, r, M, r, Mp, Mp, dpre_t, s)));
     MKA_LAUNCH("bwd/t", (transpose<T, T>(q, qw, M, qw, Mp, Mp, q_t, s)));
-    MKA_LAUNCH("bwd/dwr1", gemm_t<T>(dpre_t, Mp, q_t, r, qw, Mp, EpiStore<float>{gr->dw_r1, qw}, s));
+    MKA_LAUNCH("bwd/dwr1", gemm_t<T>(dpre_t, Mp, q_t, r, qw, Mp, EpiStore<float>{gr->dw_r1, qw}, sk, s));
     MKA_LAUNCH("bwd/t", (transpose<T, T>(wr1, qw, r, qw, r, r, wr1_t, s)));
-    MKA_LAUNCH("bwd/dqr", gemm_t<T>(dpre, r, wr1_t, M, qw, r, EpiAdd{dq, qw}, s));
+    MKA_LAUNCH("bwd/dqr", gemm_t<T>(dpre, r, wr1_t, M, qw, r, EpiAdd{dq, qw}, sk, s));
   } else {
     MKA_LAUNCH("bwd/zero", fill_zero(gr->dw_r1, static_cast<int64_t>(r) * qw, s));
     MKA_LAUNCH("bwd/zero", fill_zero(gr->dw_r2, 3 * r, s));
@@ -678,10 +691,10 @@ int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const
   MKA_LAUNCH("bwd/t", (transpose<T, T>(wq, D, qw, D, qw, qw, wq_t, s)));
   if (kBf) MKA_LAUNCH("bwd/cvt", (convert<float, T>(dq, static_cast<int64_t>(M) * qw,
                                                      const_cast<T*>(dq_a), s)));
-  MKA_LAUNCH("bwd/dx", gemm_t<T>(dq_a, qw, wq_t, M, D, qw, EpiAdd{gr->dx, D}, s));
+  MKA_LAUNCH("bwd/dx", gemm_t<T>(dq_a, qw, wq_t, M, D, qw, EpiAdd{gr->dx, D}, sk, s));
   MKA_LAUNCH("bwd/t", (transpose<float, T>(dq, qw, M, qw, Mp, Mp, dq_t, s)));
   MKA_LAUNCH("bwd/t", (transpose<T, T>(x, D, M, D, Mp, Mp, x_t, s)));
-  MKA_LAUNCH("bwd/dwq", gemm_t<T>(dq_t, Mp, x_t, qw, D, Mp, EpiStore<float>{gr->dw_q, D}, s));
+  MKA_LAUNCH("bwd/dwq", gemm_t<T>(dq_t, Mp, x_t, qw, D, Mp, EpiStore<float>{gr->dw_q, D}, sk, s));
   return MKA_OK;
 }
 
