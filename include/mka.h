@@ -140,9 +140,12 @@ int mka_ema_scan(const mka_dims* d, const void* x, int64_t pos0, float* state_io
 
 /* SimHash codes of block means first_block .. first_block+n_blocks-1.
  * (Reading note, method section 1: vectorised hash index of past blocks.)
- * bit j of a code = [m . proj_j > 0]; the dot product is accumulated in float64
- * from the float32 inputs (fp64 MFMA; split over D, partial sums added in a
- * fixed order, so results are deterministic).
+ * bit j of a code = [m . proj_j > 0], the sign of the exact product of the
+ * float32 inputs: accumulated in float64 (fp64 MFMA; split over D, partial
+ * sums added in a fixed order, so results are deterministic), or, for
+ * B * n_blocks >= 256 rows and D a multiple of 32, from bf16 parts of both
+ * operands on bf16 MFMA with an error bound that certifies each sign, the
+ * bits it leaves undecided recomputed in float64 (the same codes).
  *   block_means [B, nb_cap, D] float32; proj [hash_bits, D] float32 (row j = hyperplane j)
  *   block_hash  [B, nb_cap]    uint64 (rows written)
  *   ws >= mka_workspace_bytes(d, MKA_OP_INDEX, n_blocks) bytes (may be NULL if 0) */
@@ -166,7 +169,7 @@ int mka_l3_block_kv(const mka_dims* d, const float* block_means, int32_t nb_cap,
 /* L3 retrieval for tokens at positions pos0 .. pos0+seq-1.
  * (Reading note, method section 1: recall of R << T past blocks; landing page,
  * Table 8 caption: top-R retrieved chunks per query.)
- * key_t = SimHash(L2[t]) (float64 accumulation, as in mka_l3_index); eligible
+ * key_t = SimHash(L2[t]) (exact signs, as in mka_l3_index); eligible
  * blocks b < floor(t / block); ranked by (popcount(key_t ^ hash_b) ascending,
  * b descending); the first min(R, #eligible) are written in rank order, the
  * remaining slots hold -1.  top_r <= 32.
