@@ -123,3 +123,14 @@ def test_attention_backward_entry_matches_oracle(base):
     check_grad("dq", to_np(dq), rq, s.dtype)
     check_grad("dk", g[:, :, 0].transpose(0, 2, 1, 3), rk, s.dtype)
     check_grad("dv", g[:, :, 1].transpose(0, 2, 1, 3), rv, s.dtype)
+
+
+def test_backward_split_reduction():
+    """A 1024-token bf16 layer (D = 256, 4 / 2 heads of 128): the products with
+    few output tiles and a reduction over the tokens (dW_k, dW_v, dW_q, dW_r1,
+    the router pre-activation, dX_fused, dx) split their reduction into 2-4
+    ranges whose partials are added in order; every gradient against the oracle."""
+    s = SMALL["small_bf16_dh128"].replace(name="bwd_split", seq=1024, seed=13)
+    ref, out, g = run_case(s)
+    for k in GRADS:
+        check_grad(k, to_np(g[k]), ref[k], s.dtype)
