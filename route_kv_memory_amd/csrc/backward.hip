@@ -166,15 +166,21 @@ __global__ __launch_bounds__(64) void attn_bwd_dkv_rows_kernel(
 // lds_ elements, dst rows ldd.  32 x 32 tiles through LDS.
 // ---------------------------------------------------------------------------
 template <typename TS, typename TD>
+// rows_dst (optional): the source converted to TD in place of a separate
+// conversion pass (same layout as src).
 __global__ __launch_bounds__(256) void transpose_kernel(const TS* __restrict__ src, int64_t lds_,
                                                         int R, int C, int Rp, int64_t ldd,
-                                                        TD* __restrict__ dst) {
+                                                        TD* __restrict__ dst,
+                                                        TD* __restrict__ rows_dst) {
   __shared__ float tile[32][33];
   const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
   for (int i = ty; i < 32; i += 8) {
     const int r = r0 + i, c = c0 + tx;
-    tile[i][tx] = (r < R && c < C) ? Elem<TS>::to_f32(src[static_cast<int64_t>(r) * lds_ + c]) : 0.f;
+    const bool in = r < R && c < C;
+    tile[i][tx] = in ? Elem<TS>::to_f32(src[static_cast<int64_t>(r) * lds_ + c]) : 0.f;
+    if (rows_dst != nullptr && in)
+      rows_dst[static_cast<int64_t>(r) * lds_ + c] = Elem<TD>::from_f32(tile[i][tx]);
   }
   __syncthreads();
   for (int i = ty; i < 32; i += 8) {
@@ -487,7 +493,16 @@ hipError_t transpose(const TS* src, int64_t lds_, int R, int C, int Rp, int64_t 
                      hipStream_t s) {
   const dim3 grid((C + 31) / 32, (Rp + 31) / 32);
   hipLaunchKernelGGL((transpose_kernel<TS, TD>), grid, dim3(256), 0, s, src, lds_, R, C, Rp, ldd,
-                     dst);
+                     dst, static_cast<TD*>(nullptr));
+  return hipGetLastError();
+}
+
+template <typename TS, typename TD>
+hipError_t transpose_copy(const TS* src, int64_t lds_, int R, int C, int Rp, int64_t ldd, TD* dst,
+                          TD* rows_dst, hipStream_t s) {
+  const dim3 grid((C + 31) / 32, (Rp + 31) / 32);
+  hipLaunchKernelGGL((transpose_kernel<TS, TD>), grid, dim3(256), 0, s, src, lds_, R, C, Rp, ldd,
+                     dst, rows_dst);
   return hipGetLastError();
 }
 
@@ -593,6 +608,8 @@ template hipError_t transpose<float, float>(const float*, int64_t, int, int, int
                                             hipStream_t);
 template hipError_t transpose<bf16_t, bf16_t>(const bf16_t*, int64_t, int, int, int, int64_t,
                                               bf16_t*, hipStream_t);
+template hipError_t transpose_copy<float, bf16_t>(const float*, int64_t, int, int, int, int64_t,
+                                                  bf16_t*, bf16_t*, hipStream_t);
 template hipError_t transpose<float, bf16_t>(const float*, int64_t, int, int, int, int64_t,
                                              bf16_t*, hipStream_t);
 

@@ -135,6 +135,11 @@ hipError_t transpose(const TS* src, int64_t lds_, int R, int C, int Rp, int64_t 
                      hipStream_t s);
 template <typename TS, typename TD>
 hipError_t convert(const TS* src, int64_t n, TD* dst, hipStream_t s);
+// transpose that also writes the source converted to TD into rows_dst (same
+// layout as src): one read of src for both.
+template <typename TS, typename TD>
+hipError_t transpose_copy(const TS* src, int64_t lds_, int R, int C, int Rp, int64_t ldd, TD* dst,
+                          TD* rows_dst, hipStream_t s);
 hipError_t fill_zero(float* p, int64_t n, hipStream_t s);
 template <typename T>
 hipError_t fuse_bwd(const T* x, const float* l2, const float* means, int nb_cap,

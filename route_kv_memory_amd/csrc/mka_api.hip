@@ -648,10 +648,14 @@ int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const
   // [K|V] = X_fused [W_k|W_v]^T: dX_fused = dKV [W_k; W_v]; dW = dKV^T X_fused
   MKA_LAUNCH("bwd/t", (transpose<T, T>(wk, D, kvw, D, kvw, 2 * kvw, wkv_t, s)));
   MKA_LAUNCH("bwd/t", (transpose<T, T>(wv, D, kvw, D, kvw, 2 * kvw, wkv_t + kvw, s)));
-  if (kBf) MKA_LAUNCH("bwd/cvt", (convert<float, T>(dkv, static_cast<int64_t>(M) * 2 * kvw,
-                                                     const_cast<T*>(dkv_a), s)));
+  // dkv in the storage type, as rows (dX_fused product) and transposed (weight
+  // gradients), from one read
+  if constexpr (kBf)
+    MKA_LAUNCH("bwd/t", (transpose_copy<float, T>(dkv, 2 * kvw, M, 2 * kvw, Mp, Mp, dkv_t,
+                                                  const_cast<T*>(dkv_a), s)));
+  else
+    MKA_LAUNCH("bwd/t", (transpose<float, T>(dkv, 2 * kvw, M, 2 * kvw, Mp, Mp, dkv_t, s)));
   MKA_LAUNCH("bwd/dxf", gemm_t<T>(dkv_a, 2 * kvw, wkv_t, M, D, 2 * kvw, EpiStore<float>{dxf, D}, sk, s));
-  MKA_LAUNCH("bwd/t", (transpose<float, T>(dkv, 2 * kvw, M, 2 * kvw, Mp, Mp, dkv_t, s)));
   const T* xf_src = x;
   if (rt.ema()) {
     MKA_LAUNCH("bwd/fuse", fuse_mix<T>(x, fwd->l2, st->block_means, st->nb_cap, fwd->idx,
@@ -689,10 +693,12 @@ int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const
   }
   // Q = x W_q^T: dx += dq W_q; dW_q = dq^T x
   MKA_LAUNCH("bwd/t", (transpose<T, T>(wq, D, qw, D, qw, qw, wq_t, s)));
-  if (kBf) MKA_LAUNCH("bwd/cvt", (convert<float, T>(dq, static_cast<int64_t>(M) * qw,
-                                                     const_cast<T*>(dq_a), s)));
+  if constexpr (kBf)
+    MKA_LAUNCH("bwd/t", (transpose_copy<float, T>(dq, qw, M, qw, Mp, Mp, dq_t,
+                                                  const_cast<T*>(dq_a), s)));
+  else
+    MKA_LAUNCH("bwd/t", (transpose<float, T>(dq, qw, M, qw, Mp, Mp, dq_t, s)));
   MKA_LAUNCH("bwd/dx", gemm_t<T>(dq_a, qw, wq_t, M, D, qw, EpiAdd{gr->dx, D}, sk, s));
-  MKA_LAUNCH("bwd/t", (transpose<float, T>(dq, qw, M, qw, Mp, Mp, dq_t, s)));
   MKA_LAUNCH("bwd/t", (transpose<T, T>(x, D, M, D, Mp, Mp, x_t, s)));
   MKA_LAUNCH("bwd/dwq", gemm_t<T>(dq_t, Mp, x_t, qw, D, Mp, EpiStore<float>{gr->dw_q, D}, sk, s));
   return MKA_OK;
