@@ -82,9 +82,12 @@ struct EpiGelu {
 
 // Launchers (defined in gemm.hip).  B rows [0, n_split) come from b0, rows
 // [n_split, N) from b1 (row n - n_split); pass n_split = N for one matrix.
+// single_buffer: the register-lean loop, for a product that runs beside other
+// kernels (more of their waves fit on its SIMDs).
 template <class Epi>
 hipError_t gemm_bf16(const bf16_t* a, int lda, const bf16_t* b0, const bf16_t* b1, int n_split,
-                     int M, int N, int K, const Epi& epi, hipStream_t s);
+                     int M, int N, int K, const Epi& epi, hipStream_t s,
+                     bool single_buffer = false);
 template <class Epi>
 hipError_t gemm_f32(const float* a, int lda, const float* b0, const float* b1, int n_split,
                     int M, int N, int K, const Epi& epi, hipStream_t s);

@@ -35,8 +35,11 @@ struct GemmCfg {
 };
 
 // blockIdx.y selects a range of K_len reduction indices starting at
-// blockIdx.y * K_len (split-K; K is the row length of B).
-template <int BN, int NW, class Epi>
+// blockIdx.y * K_len (split-K; K is the row length of B).  DB: fragments
+// double-buffered in registers (below); without it a slice's fragments are
+// read after its barrier, in fewer registers (room for other kernels' waves
+// on the same SIMDs).
+template <int BN, int NW, bool DB, class Epi>
 __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(
     const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B0,
     const bf16_t* __restrict__ B1, int n_split, int M, int N, int K, int K_len, Epi epi) {
@@ -107,7 +110,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(
   // fragment byte offset of row r, chunk c (16 bytes) within a slice operand
   auto frag = [](int r, int c) { return r * ROWB + ((c ^ ((r >> 2) & 3)) << 4); };
 
-  const int nk = K_len / BK;
+  const int nk_all = K_len / BK;
+  if constexpr (DB) {
+  const int nk = nk_all;
 #pragma unroll
   for (int s = 0; s < STAGES; ++s)
     if (s < nk) issue(s, s);
@@ -180,6 +185,43 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(
   }
   if (kt < nk) step(kt, xa, xb, ya, yb);
 
+  } else {
+  const int nk = nk_all;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue(s, s);
+  for (int kt = 0; kt < nk; ++kt) {
+    // slice kt has landed once at most the STAGES-2 younger slices are pending
+    if (kt + STAGES - 2 < nk) {
+      __builtin_amdgcn_s_waitcnt(kVmcntPending<C::LOADS * (STAGES - 2)>());
+    } else {
+      __builtin_amdgcn_s_waitcnt(kVmcntPending<0>());
+    }
+    // Every wave's part of slice kt is in LDS (each waited for its own loads)
+    // and every wave is done reading slice kt-1.  A bare barrier: a fence here
+    // would wait for the prefetches too.
+    __builtin_amdgcn_s_barrier();
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+    const unsigned char* As = lds + (kt % STAGES) * C::SLICE;
+    const unsigned char* Bs = As + C::A_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 fa[4], fb[NB];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        fa[i] = *reinterpret_cast<const bf16x8*>(As + frag(wm * 128 + i * 32 + l32, 2 * ks + h));
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        fb[j] = *reinterpret_cast<const bf16x8*>(Bs + frag(wn * WN + j * 32 + l32, 2 * ks + h));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma32x32x16(fb[j], fa[i], acc[i][j]);
+    }
+  }
+
+  }
+
   // Lane holds output row m = ... + l32 and columns n = ... + 8*(r/4) + 4h + (r%4).
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -201,15 +243,19 @@ constexpr int kGemmWaves256 = 8;
 
 template <class Epi>
 hipError_t gemm_bf16(const bf16_t* a, int lda, const bf16_t* b0, const bf16_t* b1, int n_split,
-                     int M, int N, int K, const Epi& epi, hipStream_t s) {
+                     int M, int N, int K, const Epi& epi, hipStream_t s, bool single_buffer) {
   const int tiles256 = ((N + 255) / 256) * ((M + 255) / 256);
   if (tiles256 >= 256) {
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, kGemmWaves256, Epi>), dim3(tiles256),
-                       dim3(kGemmWaves256 * 64), 0, s, a, lda, b0, b1, n_split, M, N, K, K, epi);
+    if (single_buffer)
+      hipLaunchKernelGGL((gemm_bf16_kernel<256, kGemmWaves256, false, Epi>), dim3(tiles256),
+                         dim3(kGemmWaves256 * 64), 0, s, a, lda, b0, b1, n_split, M, N, K, K, epi);
+    else
+      hipLaunchKernelGGL((gemm_bf16_kernel<256, kGemmWaves256, true, Epi>), dim3(tiles256),
+                         dim3(kGemmWaves256 * 64), 0, s, a, lda, b0, b1, n_split, M, N, K, K, epi);
   } else {
     const int tiles = ((N + 127) / 128) * ((M + 255) / 256);
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 8, Epi>), dim3(tiles), dim3(512), 0, s, a, lda, b0,
-                       b1, n_split, M, N, K, K, epi);
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 8, true, Epi>), dim3(tiles), dim3(512), 0, s, a, lda,
+                       b0, b1, n_split, M, N, K, K, epi);
   }
   return hipGetLastError();
 }
@@ -271,7 +317,7 @@ hipError_t gemm_bf16_splitk(const bf16_t* a, int lda, const bf16_t* b, int M, in
   if (S == 1) return gemm_bf16(a, lda, b, b, N, M, N, K, epi, s);
   const int tiles = ((N + 127) / 128) * ((M + 255) / 256);
   const EpiPart part{ws, N, static_cast<int64_t>(M) * N};
-  hipLaunchKernelGGL((gemm_bf16_kernel<128, 8, EpiPart>), dim3(tiles, S), dim3(512), 0, s, a, lda,
+  hipLaunchKernelGGL((gemm_bf16_kernel<128, 8, true, EpiPart>), dim3(tiles, S), dim3(512), 0, s, a, lda,
                      b, b, N, M, N, K, K / S, part);
   const int64_t quads = (static_cast<int64_t>(M) * N + 3) / 4;
   hipLaunchKernelGGL((splitk_sum_kernel<Epi>), dim3(static_cast<unsigned>((quads + 255) / 256)),
@@ -412,14 +458,15 @@ hipError_t gemv(const T* a, int lda, int M, const T* b0, const T* b1, int n_spli
 // Instantiations used by the host layer.
 template hipError_t gemm_bf16<EpiStore<bf16_t>>(const bf16_t*, int, const bf16_t*, const bf16_t*,
                                                  int, int, int, int, const EpiStore<bf16_t>&,
-                                                 hipStream_t);
+                                                 hipStream_t, bool);
 template hipError_t gemm_bf16<EpiKV<bf16_t>>(const bf16_t*, int, const bf16_t*, const bf16_t*, int,
-                                              int, int, int, const EpiKV<bf16_t>&, hipStream_t);
+                                              int, int, int, const EpiKV<bf16_t>&, hipStream_t,
+                                              bool);
 template hipError_t gemm_bf16<EpiStore<float>>(const bf16_t*, int, const bf16_t*, const bf16_t*,
                                                 int, int, int, int, const EpiStore<float>&,
-                                                hipStream_t);
+                                                hipStream_t, bool);
 template hipError_t gemm_bf16<EpiAdd>(const bf16_t*, int, const bf16_t*, const bf16_t*, int, int,
-                                      int, int, const EpiAdd&, hipStream_t);
+                                      int, int, const EpiAdd&, hipStream_t, bool);
 template hipError_t gemm_bf16_splitk<EpiStore<float>>(const bf16_t*, int, const bf16_t*, int, int,
                                                       int, const EpiStore<float>&, float*,
                                                       hipStream_t);

@@ -149,7 +149,8 @@ int do_qproj(const mka_dims* d, const void* x, const void* w_q, void* q_out, hip
     if (M <= kFewRows)
       MKA_LAUNCH("route/q_gemv", gemv<bf16_t>(xb, D, M, wq, wq, qw, qw, D, epi, s));
     else
-      MKA_LAUNCH("route/q_gemm", gemm_bf16(xb, D, wq, wq, qw, M, qw, D, epi, s));
+      // beside the auxiliary stream's kernels: the register-lean loop
+      MKA_LAUNCH("route/q_gemm", gemm_bf16(xb, D, wq, wq, qw, M, qw, D, epi, s, true));
   } else {
     const float* xf = static_cast<const float*>(x);
     const float* wq = static_cast<const float*>(w_q);
