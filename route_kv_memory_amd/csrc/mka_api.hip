@@ -943,12 +943,11 @@ int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weight
   char* ws_main = ws_chain + prefill_chain_ws(d);
   char* ws_prep = ws_main + prefill_main_ws(d);
   const bool prep = prefill_prepares_codes(d);
-  // The hyperplane split of the key codes, the EMA scan and the block codes
+  // The hyperplane split of the key codes, the EMA scan, the block codes, the
+  // block projections (needed only by later decode steps) and the retrieval
   // need only the weights and x, so they run on the auxiliary stream beside the
-  // query product; the retrieval joins them after the router.  (The key codes
-  // beside the query product would get only the CUs of its last tile round.)
-  // The block projections, needed only by later decode steps, follow them
-  // there.
+  // query product (register-lean, so the scan's waves share its SIMDs) and the
+  // router; the main stream joins them before the fusion.
   Aux* aux = aux_for_current_device(&rc);
   if (aux == nullptr) return rc;
   std::lock_guard<std::mutex> guard(aux->lock);
@@ -963,24 +962,24 @@ int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weight
   if ((rc = do_index(d, st->block_means, st->nb_cap, static_cast<int>(first), static_cast<int>(n),
                      w->proj, st->block_hash, ws_chain, s2)))
     return rc;
-  MKA_LAUNCH("prefill/join", hipEventRecord(aux->join, s2));
   if ((rc = do_block_kv(d, st->block_means, st->nb_cap, static_cast<int>(first),
                         static_cast<int>(n), w->w_k, w->w_v, st->block_kv, s2)))
     return rc;
-  MKA_LAUNCH("prefill/join", hipEventRecord(aux->done, s2));
-  if ((rc = do_route(d, x, w->w_q, w->w_r1, w->w_r2, out->q, out->lambda, ws_main, s))) return rc;
-  MKA_LAUNCH("prefill/join", hipStreamWaitEvent(s, aux->join, 0));
   if (prep) {
     MKA_LAUNCH("l3_retrieve/keys",
                simhash_rows_prepared(out->l2, static_cast<int64_t>(d->seq) * d->d_model, d->seq,
                                      d->batch, d->d_model, w->proj, d->hash_bits, ws_prep,
-                                     out->key, d->seq, s));
+                                     out->key, d->seq, s2));
     MKA_LAUNCH("l3_retrieve/topr", topr_rows(out->key, d->batch, d->seq, pos0, st->block_hash,
-                                             st->nb_cap, d->block, d->top_r, out->idx, s));
-  } else if (rt.l3() && (rc = do_retrieve(d, out->l2, w->proj, st->block_hash, st->nb_cap, pos0,
-                                          out->key, out->idx, ws_main, s))) {
-    return rc;
+                                             st->nb_cap, d->block, d->top_r, out->idx, s2));
   }
+  MKA_LAUNCH("prefill/join", hipEventRecord(aux->join, s2));
+  MKA_LAUNCH("prefill/join", hipEventRecord(aux->done, s2));
+  if ((rc = do_route(d, x, w->w_q, w->w_r1, w->w_r2, out->q, out->lambda, ws_main, s))) return rc;
+  MKA_LAUNCH("prefill/join", hipStreamWaitEvent(s, aux->join, 0));
+  if (!prep && rt.l3() && (rc = do_retrieve(d, out->l2, w->proj, st->block_hash, st->nb_cap, pos0,
+                                            out->key, out->idx, ws_main, s)))
+    return rc;
   if ((rc = do_fuse_kv(d, x, out->l2, st->block_means, st->nb_cap, out->idx, out->lambda, w->w_k,
                        w->w_v, st->k_cache, st->v_cache, pos0, layout_of(d, st), ws_main, s)))
     return rc;
