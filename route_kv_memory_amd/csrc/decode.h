@@ -7,7 +7,7 @@ namespace mka {
 
 constexpr int kDecSlice = 128;   // channels per EMA/key-projection workgroup
 constexpr int kFewRowsDec = 8;   // tokens per decode step (batch) at most
-constexpr int kGemvCols = 4;     // output columns per wave in the decode products
+constexpr int kGemvCols = 2;     // output columns per wave in the decode products
 
 template <typename T>
 struct DecodeArgs {
