@@ -49,7 +49,7 @@ import numpy as np
 from scipy.special import erf as _erf
 
 __all__ = [
-    "q_proj", "gelu", "router", "router_logits", "route_weights", "round_bf16", "ROUTE_MODES",
+    "q_proj", "gelu", "router", "router_logits", "route_choice", "route_weights", "ROUTE_MODES",
     "TIER_SETS",
     "ema", "block_means", "simhash", "retrieve",
     "l3_mean", "fuse", "kv_proj", "attention", "attention_online", "prefill",
@@ -116,19 +116,30 @@ def router_logits(q, w_r1, w_r2):
     return gelu(_f64(q) @ _f64(w_r1).T) @ _f64(w_r2).T
 
 
-def round_bf16(a):
-    """Values rounded to bfloat16 (round to nearest, ties to even), as float64.
+def route_choice(z, mode="soft", tiers="l1l2l3"):
+    """The kept tiers [..., 3] (bool) of a routing variant, from the logits z.
 
-    A float64 value is first rounded to float32, then the low 16 bits of the
-    float32 pattern are rounded off.  Finite inputs only.
+    soft keeps every enabled tier; top1 / top2 keep the k enabled tiers with
+    the largest logits, ties going to the lower tier index (abstract page,
+    Table 10's hard routing); fixed keeps every enabled tier.
     """
-    f = np.asarray(a, dtype=np.float64).astype(np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+    z = _f64(z)
+    en = TIER_SETS[tiers]
+    on = [i for i in range(3) if en[i]]
+    k = {"soft": 3, "fixed": 3, "top1": 1, "top2": 2}[mode]
+    keep = np.zeros(z.shape, dtype=bool)
+    for i in on:
+        # rank of tier i among the enabled tiers: how many beat it
+        rank = np.zeros(z.shape[:-1], dtype=np.int64)
+        for j in on:
+            if j != i:
+                beats = (z[..., j] > z[..., i]) | ((z[..., j] == z[..., i]) & (j < i))
+                rank += beats.astype(np.int64)
+        keep[..., i] = rank < k
+    return keep
 
 
-def route_weights(z, mode="soft", tiers="l1l2l3", z_decide=None):
+def route_weights(z, mode="soft", tiers="l1l2l3", keep=None):
     """lambda from the logits z [..., 3] under a routing variant.
 
     ``tiers`` names the enabled tiers (L1 is always one); the others get
@@ -137,16 +148,17 @@ def route_weights(z, mode="soft", tiers="l1l2l3", z_decide=None):
                learned router of the reading note, section 2);
       fixed -- 1 / (number of enabled tiers) on each, z unused (abstract
                page, Table 10: lambda = 1/3 with all three);
-      top1, top2 -- the k enabled tiers with the largest logits (ties to the
-               lower tier index) and a softmax over those k alone (Table 10's
-               hard routing).  Readings: the kept weights are renormalised,
-               as a softmax restricted to the kept tiers; top-1 is therefore
-               one-hot, and top-k with k >= the enabled count is soft.
-    ``z_decide`` (default z): the logits that choose the kept tiers, when that
-    choice is taken in another precision than the weights.
+      top1, top2 -- the k enabled tiers with the largest logits
+               (``route_choice``) and a softmax over those k alone (Table
+               10's hard routing).  Readings: the kept weights are
+               renormalised, as a softmax restricted to the kept tiers; top-1
+               is therefore one-hot, and top-k with k >= the enabled count is
+               soft.
+    ``keep`` [..., 3] (bool), when given, names the kept tiers instead of the
+    ranking of z: the weights of another choice of tiers (a comparison that
+    accepts either side of an exact tie evaluates both this way).
     """
     z = _f64(z)
-    zd = z if z_decide is None else _f64(z_decide)
     en = TIER_SETS[tiers]
     on = [i for i in range(3) if en[i]]
     lam = np.zeros(z.shape)
@@ -154,40 +166,24 @@ def route_weights(z, mode="soft", tiers="l1l2l3", z_decide=None):
         for i in on:
             lam[..., i] = 1.0 / len(on)
         return lam
-    k = {"soft": 3, "top1": 1, "top2": 2}[mode]
-    keep = np.zeros(z.shape, dtype=bool)
-    for i in on:
-        # rank of tier i among the enabled tiers: how many beat it
-        rank = np.zeros(z.shape[:-1], dtype=np.int64)
-        for j in on:
-            if j != i:
-                beats = (zd[..., j] > zd[..., i]) | ((zd[..., j] == zd[..., i]) & (j < i))
-                rank += beats.astype(np.int64)
-        keep[..., i] = rank < k
+    keep = route_choice(z, mode, tiers) if keep is None else np.asarray(keep, dtype=bool)
     zk = np.where(keep, z, -np.inf)
     e = np.where(keep, np.exp(zk - zk.max(axis=-1, keepdims=True)), 0.0)
     return e / e.sum(axis=-1, keepdims=True)
 
 
-def router(q, w_r1, w_r2, mode="soft", tiers="l1l2l3", decide_q="f64"):
+def router(q, w_r1, w_r2, mode="soft", tiers="l1l2l3", keep=None):
     """lambda = softmax(GELU(q W_r1) W_r2) over the three memory tiers.
 
     MKA reading note, section 2: a learned MLP of the query followed by a
     softmax gives lambda in R^{B x S x 3}, per token and per layer.  Other
-    ``mode`` / ``tiers`` values give the ablation variants (``route_weights``).
-    Output [..., 3]; tier 0 = L1, 1 = L2, 2 = L3.
-
-    ``decide_q = "bf16"``: hard routing chooses its tiers from the logits of q
-    rounded to bfloat16, the query as a bf16 layer stores it; the weights of
-    the kept tiers still come from the float64 logits.  (The pages fix no
-    precision for this choice; taking it from the stored query is how a layer
-    that keeps q in bf16 takes it.)
+    ``mode`` / ``tiers`` values give the ablation variants (``route_weights``;
+    ``keep`` as there).  Output [..., 3]; tier 0 = L1, 1 = L2, 2 = L3.
     """
     z = router_logits(q, w_r1, w_r2)
     if mode == "soft" and tiers == "l1l2l3":
         return _softmax(z)
-    zd = router_logits(round_bf16(q), w_r1, w_r2) if decide_q == "bf16" else None
-    return route_weights(z, mode, tiers, z_decide=zd)
+    return route_weights(z, mode, tiers, keep=keep)
 
 
 # --------------------------------------------------------------------------
@@ -416,7 +412,7 @@ def attention_online(q, k, v, positions, n_kv_heads, tile=64):
 
 def prefill(x, w_q, w_k, w_v, w_r1, w_r2, proj, *, n_heads, n_kv_heads, ema_decay,
             block, top_r, rows=None, lam_override=None, route_mode="soft", tiers="l1l2l3",
-            decide_q="f64"):
+            keep=None):
     """FastMKA layer forward over a whole sequence (every step, in page order).
 
     Returns a dict with q [B,N,H*dh], lam [B,N,3], l2 [B,N,D], block_means
@@ -425,14 +421,14 @@ def prefill(x, w_q, w_k, w_v, w_r1, w_r2, proj, *, n_heads, n_kv_heads, ema_deca
     k, v [B,G,N,dh], rows [n] and o [B,n,H,dh] (attention only at ``rows``;
     every row otherwise).  ``lam_override`` [B,N,3] replaces the router output;
     ``route_mode`` and ``tiers`` select a routing variant (``route_weights``;
-    ``decide_q`` as in ``router``).
+    ``keep`` [B,N,3], when given, names each token's kept tiers).
     Every tier is computed whatever the variant; a disabled tier enters the
     fusion with lambda = 0.
     """
     x = _f64(x)
     B, N, D = x.shape
     q = q_proj(x, w_q)
-    lam = (router(q, w_r1, w_r2, route_mode, tiers, decide_q) if lam_override is None
+    lam = (router(q, w_r1, w_r2, route_mode, tiers, keep) if lam_override is None
            else _f64(lam_override))
     l2, _ = ema(x, ema_decay)
     means = block_means(x, block)
@@ -493,7 +489,7 @@ def decode_init_from_prefill(x, ref, proj, *, block, t_cap):
 
 
 def decode_step(st, x_t, w_q, w_k, w_v, w_r1, w_r2, proj, *, n_heads, n_kv_heads, ema_decay,
-                block, top_r, attend=True, route_mode="soft", tiers="l1l2l3", decide_q="f64"):
+                block, top_r, attend=True, route_mode="soft", tiers="l1l2l3", keep=None):
     """One decode step at position t = st.pos for the token hiddens x_t [B, D].
 
     The same definitions as ``prefill`` applied to one token with the carried
@@ -507,7 +503,7 @@ def decode_step(st, x_t, w_q, w_k, w_v, w_r1, w_r2, proj, *, n_heads, n_kv_heads
     B, D = x_t.shape
     t = st.pos
     q = q_proj(x_t, w_q)
-    lam = router(q, w_r1, w_r2, route_mode, tiers, decide_q)
+    lam = router(q, w_r1, w_r2, route_mode, tiers, keep)
     l2_seq, st.ema_state = ema(x_t[:, None, :], ema_decay, st.ema_state)
     l2 = l2_seq[:, 0]
     st.block_acc = st.block_acc + x_t
@@ -550,7 +546,7 @@ def decode_step(st, x_t, w_q, w_k, w_v, w_r1, w_r2, proj, *, n_heads, n_kv_heads
 # --------------------------------------------------------------------------
 
 def full_prefill(x, w_q, w_k, w_v, w_r1, w_r2, proj, *, n_heads, n_kv_heads, ema_decay,
-                 block, top_r, rows=None, route_mode="soft", tiers="l1l2l3", decide_q="f64"):
+                 block, top_r, rows=None, route_mode="soft", tiers="l1l2l3", keep=None):
     """Full MKA forward over a whole sequence.
 
     Returns a dict with q, lam, l2, block_means, block_hash, block_abs, keys,
@@ -562,7 +558,7 @@ def full_prefill(x, w_q, w_k, w_v, w_r1, w_r2, proj, *, n_heads, n_kv_heads, ema
     x = _f64(x)
     B, N, D = x.shape
     q = q_proj(x, w_q)
-    lam = router(q, w_r1, w_r2, route_mode, tiers, decide_q)
+    lam = router(q, w_r1, w_r2, route_mode, tiers, keep)
     l2, _ = ema(x, ema_decay)
     means = block_means(x, block)
     bhash, babs = simhash(means, proj)
@@ -615,7 +611,7 @@ def full_decode_init_from_prefill(x, ref, proj, *, block, t_cap):
 
 
 def full_decode_step(st, x_t, w_q, w_k, w_v, w_r1, w_r2, proj, *, n_heads, n_kv_heads,
-                     ema_decay, block, top_r, route_mode="soft", tiers="l1l2l3", decide_q="f64"):
+                     ema_decay, block, top_r, route_mode="soft", tiers="l1l2l3", keep=None):
     """One full-MKA decode step at position t = st.pos: the tiers of the token,
     one K/V row appended to each enabled tier's cache, the three attentions over
     rows 0..t and their lambda-weighted sum.  Block finalisation as in
@@ -624,7 +620,7 @@ def full_decode_step(st, x_t, w_q, w_k, w_v, w_r1, w_r2, proj, *, n_heads, n_kv_
     B, D = x_t.shape
     t = st.pos
     q = q_proj(x_t, w_q)
-    lam = router(q, w_r1, w_r2, route_mode, tiers, decide_q)
+    lam = router(q, w_r1, w_r2, route_mode, tiers, keep)
     l2_seq, st.ema_state = ema(x_t[:, None, :], ema_decay, st.ema_state)
     l2 = l2_seq[:, 0]
     st.block_acc = st.block_acc + x_t
@@ -732,7 +728,7 @@ def l3_adjoint(c, idx, n_blocks, n_tokens, block):
 
 
 def backward(x, w_q, w_k, w_v, w_r1, w_r2, proj, d_o, *, n_heads, n_kv_heads, ema_decay,
-             block, top_r, route_mode="soft", tiers="l1l2l3", decide_q="f64"):
+             block, top_r, route_mode="soft", tiers="l1l2l3", keep=None):
     """Gradients of sum(O * d_o) for the FastMKA layer over a whole sequence.
 
     Returns a dict with dx [B,N,D], dw_q, dw_k, dw_v, dw_r1, dw_r2 (the weight
@@ -744,7 +740,7 @@ def backward(x, w_q, w_k, w_v, w_r1, w_r2, proj, d_o, *, n_heads, n_kv_heads, em
     B, N, D = x.shape
     fwd = prefill(x, w_q, w_k, w_v, w_r1, w_r2, proj, n_heads=n_heads, n_kv_heads=n_kv_heads,
                   ema_decay=ema_decay, block=block, top_r=top_r, route_mode=route_mode,
-                  tiers=tiers, decide_q=decide_q)
+                  tiers=tiers, keep=keep)
     q, lam = fwd["q"], fwd["lam"]
     dh = q.shape[-1] // n_heads
     G = n_kv_heads

@@ -1,10 +1,15 @@
 """Comparison helpers shared by the GPU parity tests (the HIP path vs the oracle).
 
-Tolerances: fp32 layers max-abs 1e-4; bf16 layers max-abs 3e-2 and mean-abs
-3e-3 on unit-scale inputs.  Integer results (block indices) are compared
-exactly; SimHash bits whose oracle projection |p| is below 1e-6 are treated as
-undetermined (either value accepted) and a ranking is accepted if it matches
-the oracle's ranking for some assignment of those bits.
+Tolerances: fp32 layers max-abs 1e-4 and relative L2 error 1e-5; bf16
+layers max-abs 3e-2, mean-abs 3e-3 and relative L2 error 1e-2, on unit-scale
+inputs.  The relative L2 bar keeps the absolute bars meaningful where outputs
+are small (a softmax-weighted mean over many keys).  Integer results (block
+indices) are compared exactly; SimHash bits whose oracle projection |p| is
+below 1e-6 are treated as undetermined (either value accepted) and a ranking
+is accepted if it matches the oracle's ranking for some assignment of those
+bits.  Hard routing is treated the same way: where the oracle's float64
+logits put two tiers within twice the logit error bound of the cut, either
+side of the cut is accepted and the oracle evaluates the side the GPU took.
 """
 
 from __future__ import annotations
@@ -19,7 +24,15 @@ from oracle import mka_oracle as O
 AMBIG = 1e-6
 MAX_AMBIG_BITS = 10
 
-TOL = {"f32": dict(max_abs=1e-4, mean_abs=None), "bf16": dict(max_abs=3e-2, mean_abs=3e-3)}
+TOL = {"f32": dict(max_abs=1e-4, mean_abs=None, rel_l2=1e-5),
+       "bf16": dict(max_abs=3e-2, mean_abs=3e-3, rel_l2=1e-2)}
+
+# Bound on |z_gpu - z|, the difference between the GPU's router logits and
+# the oracle's float64 ones.  bf16 layers store q in bf16 (relative rounding
+# 2^-9 per entry): over the D-long first layer and the r-long second layer of
+# unit-scale data that moves a logit by ~1e-3 (rms), so 2e-2 is a bound with
+# a wide margin; fp32 layers accumulate in fp32 (~1e-6).
+ROUTE_TIE = {"bf16": 2e-2, "f32": 1e-5}
 
 
 def log(msg):
@@ -31,8 +44,7 @@ def oracle_kwargs(s):
     """Hyper-parameters as the GPU receives them (the decay as float32)."""
     return dict(n_heads=s.n_heads, n_kv_heads=s.n_kv_heads,
                 ema_decay=float(np.float32(s.ema_decay)), block=s.block, top_r=s.top_r,
-                route_mode=s.route_mode, tiers=s.tiers,
-                decide_q="bf16" if s.dtype == "bf16" else "f64")
+                route_mode=s.route_mode, tiers=s.tiers)
 
 
 def check_close(name, got, ref, dtype, max_abs=None, mean_abs=None, rel_l2=None):
@@ -44,6 +56,7 @@ def check_close(name, got, ref, dtype, max_abs=None, mean_abs=None, rel_l2=None)
     tol = TOL[dtype]
     ma = tol["max_abs"] if max_abs is None else max_abs
     mn = tol["mean_abs"] if mean_abs is None else mean_abs
+    rel_l2 = tol["rel_l2"] if rel_l2 is None else rel_l2
     rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
     log(f"  {name}: max_abs={err.max():.3e} mean_abs={err.mean():.3e} rel_l2={rel:.3e}")
     assert err.max() <= ma, f"{name}: max abs err {err.max():.3e} > {ma:.1e}"
@@ -139,19 +152,42 @@ def check_idx_conditional(name, got_idx, got_keys, gpu_l2, gpu_means, gpu_bhash,
     log(f"  {name}: conditional retrieval exact on {ref.shape[0] * ref.shape[1]} rows")
 
 
-def decision_margin(s, inp):
-    """Smallest gap, over the tokens of the seeded inputs ``inp``, between the
-    router logits on either side of the hard-routing cut (the k-th and
-    (k+1)-th largest enabled logits), in the precision the decision is taken
-    in (oracle arithmetic); inf when the variant takes no decision."""
+def route_keep(s, inp, lam_gpu, x=None):
+    """Each token's kept tiers for the oracle under hard routing, or None.
+
+    The oracle's choice is taken from its float64 logits z.  The GPU's logits
+    differ from z by at most e = ROUTE_TIE[dtype], so where a kept and a
+    dropped enabled tier lie within 2e of each other either side of the cut
+    is a correct choice (a near-tie, as an undetermined SimHash bit).  At
+    such tokens the GPU's choice (the non-zero entries of its lambda) is
+    accepted if it is consistent with z within 2e, and returned for the
+    oracle to evaluate; everywhere else the GPU must match the float64
+    choice exactly (the later lambda comparison checks that).  ``x``: the
+    hiddens the GPU routed (default inp["x"]).
+    """
     k = {"top1": 1, "top2": 2}.get(s.route_mode)
-    on = {"l1l2l3": [0, 1, 2], "l1l2": [0, 1], "l1l3": [0, 2], "l1": [0]}[s.tiers]
+    on = [i for i, e in enumerate(O.TIER_SETS[s.tiers]) if e]
     if k is None or k >= len(on):
-        return np.inf
-    from oracle import mka_oracle as O
-    q = O.q_proj(inp["x"], inp["w_q"])
-    if s.dtype == "bf16":
-        q = O.round_bf16(q)
-    z = O.router_logits(q, inp["w_r1"], inp["w_r2"])[..., on]
-    zs = -np.sort(-z, axis=-1)
-    return float((zs[..., k - 1] - zs[..., k]).min())
+        return None
+    x = inp["x"] if x is None else x
+    z = O.router_logits(O.q_proj(x, inp["w_q"]), inp["w_r1"], inp["w_r2"])
+    keep = O.route_choice(z, s.route_mode, s.tiers)
+    zon = z[..., on]
+    zs = -np.sort(-zon, axis=-1)
+    tie = (zs[..., k - 1] - zs[..., k]) < 2.0 * ROUTE_TIE[s.dtype]
+    got = np.asarray(lam_gpu) > 0.0
+    out = keep.copy()
+    flipped = 0
+    for idx in zip(*np.nonzero(tie)):
+        g = got[idx]
+        assert g.sum() == k and all(g[i] == 0 for i in range(3) if i not in on), \
+            f"token {idx}: GPU keeps tiers {np.nonzero(g)[0]} under {s.route_mode}/{s.tiers}"
+        kept_min = min(z[idx][i] for i in range(3) if g[i])
+        dropped_max = max((z[idx][i] for i in on if not g[i]), default=-np.inf)
+        assert kept_min >= dropped_max - 2.0 * ROUTE_TIE[s.dtype], \
+            f"token {idx}: GPU choice {np.nonzero(g)[0]} is not within the tie bound of z {z[idx]}"
+        flipped += int(not np.array_equal(g, keep[idx]))
+        out[idx] = g
+    log(f"  route_keep: {int(tie.sum())} near-tie tokens of {tie.size} "
+        f"(margin < {2.0 * ROUTE_TIE[s.dtype]:.0e}), {flipped} took the other side")
+    return out

@@ -22,7 +22,7 @@ from route_kv_memory_amd import inputs as I
 from route_kv_memory_amd.layer import Layer, to_device
 
 from .gpu_common import to_np
-from .parity import decision_margin, log, oracle_kwargs
+from .parity import log, oracle_kwargs, route_keep
 from .test_gpu_small import SMALL
 
 pytestmark = pytest.mark.gpu
@@ -46,18 +46,19 @@ def check_grad(name, got, ref, dtype):
 
 def run_case(s, seed=0):
     inp = I.prefill_inputs(s)
-    assert decision_margin(s, inp) >= (1e-3 if s.dtype == "bf16" else 1e-4)
     d_o = I.round_bf16(np.random.default_rng(seed + 100).standard_normal(
         (s.batch, s.seq, s.n_heads, s.head_dim))) if s.dtype == "bf16" else \
         np.random.default_rng(seed + 100).standard_normal(
             (s.batch, s.seq, s.n_heads, s.head_dim)).astype(np.float32)
-    ref = O.backward(inp["x"], *[inp[k] for k in WEIGHTS], d_o, **oracle_kwargs(s))
     layer = Layer(s, inp, t_cap=s.seq, nb_cap=max(1, s.seq // s.block))
     x = to_device(inp["x"], s.dtype)
     log(f"  gpu: mka_prefill + mka_backward {s.name} ({s.route_mode}, {s.tiers})")
     out = layer.prefill(x)
     g = layer.backward(x, out, to_device(d_o, s.dtype))
     torch.cuda.synchronize()
+    # hard-routing near-ties resolved to the GPU's side where that is a correct choice
+    keep = route_keep(s, inp, to_np(out["lambda"]))
+    ref = O.backward(inp["x"], *[inp[k] for k in WEIGHTS], d_o, keep=keep, **oracle_kwargs(s))
     return ref, out, g
 
 
@@ -72,8 +73,6 @@ CASES = [
 @pytest.mark.parametrize("base,mode,tiers", CASES)
 def test_backward_matches_oracle(base, mode, tiers):
     s = SMALL[base].replace(name=f"{base}_bwd", route_mode=mode, tiers=tiers)
-    if base == "small_bf16_dh128":
-        s = s.replace(seed=12)
     ref, out, g = run_case(s)
     # the saved log-sum-exp of the forward
     fwd = ref["fwd"]

@@ -248,6 +248,70 @@ def test_fusion_linearity_second_formula():
     np.testing.assert_allclose(ref["k"], k2, rtol=1e-10, atol=1e-12)
 
 
+@pytest.mark.parametrize("name,seq", [("tiny_f32", 256), ("small_b2", 96)])
+def test_layer_end_to_end_by_an_independent_route(name, seq):
+    # The whole layer with a learned (general) lambda and a non-empty L3, built
+    # a second way from plain definitions and library routines, none of them
+    # the oracle's: lambda by torch's exact GELU and softmax; L2 as the
+    # lower-triangular matrix (1 - beta) beta^(t-i); block means by a reshape;
+    # codes and ranking by a Python sort of (Hamming distance, -block) over the
+    # eligible blocks; K and V by projecting each tier first (linearity of the
+    # fusion, reading note, section 3); attention by torch's causal
+    # scaled-dot-product attention.  The oracle's output must agree.
+    s = I.workload("tiny_f32")
+    if name == "small_b2":
+        s = s.replace(batch=2, d_model=64, n_heads=4, n_kv_heads=2, block=16, top_r=3,
+                      router_hidden=16, hash_bits=24, seed=5)
+    s = s.replace(seq=seq)
+    d = I.prefill_inputs(s)
+    ref = O.prefill(d["x"], d["w_q"], d["w_k"], d["w_v"], d["w_r1"], d["w_r2"], d["proj"],
+                    n_heads=s.n_heads, n_kv_heads=s.n_kv_heads, ema_decay=s.ema_decay,
+                    block=s.block, top_r=s.top_r)
+    x = d["x"].astype(np.float64)
+    B, N, D = x.shape
+    beta = float(s.ema_decay)
+    tx = torch.from_numpy(x)
+    q = tx @ torch.from_numpy(d["w_q"].astype(np.float64)).T
+    hid = torch.nn.functional.gelu(q @ torch.from_numpy(d["w_r1"].astype(np.float64)).T)
+    lam = torch.softmax(hid @ torch.from_numpy(d["w_r2"].astype(np.float64)).T, dim=-1).numpy()
+    assert lam.min() > 0.01 and lam.max() < 0.99  # a general router output
+    ii = np.arange(N)
+    wema = np.where(ii[:, None] >= ii[None, :], (1 - beta) * beta ** (ii[:, None] - ii[None, :]
+                                                                       ).astype(np.float64), 0.0)
+    l2 = np.einsum("ti,bid->btd", wema, x)
+    nb = N // s.block
+    means = x[:, :nb * s.block].reshape(B, nb, s.block, D).mean(axis=2)
+    p = d["proj"].astype(np.float64)
+
+    def code(v):
+        return sum(1 << j for j in range(s.hash_bits) if float(v @ p[j]) > 0.0)
+
+    wk, wv = d["w_k"].astype(np.float64), d["w_v"].astype(np.float64)
+    ks, vs = np.zeros((B, N, wk.shape[0])), np.zeros((B, N, wv.shape[0]))
+    n_l3 = 0
+    for b in range(B):
+        bcodes = [code(means[b, j]) for j in range(nb)]
+        for t in range(N):
+            kc = code(l2[b, t])
+            order = sorted(range(t // s.block), key=lambda j: (bin(kc ^ bcodes[j]).count("1"), -j))
+            sel = order[:s.top_r]
+            l3k = np.mean([means[b, j] @ wk.T for j in sel], axis=0) if sel else 0.0
+            l3v = np.mean([means[b, j] @ wv.T for j in sel], axis=0) if sel else 0.0
+            n_l3 += bool(sel)
+            ks[b, t] = lam[b, t, 0] * (x[b, t] @ wk.T) + lam[b, t, 1] * (l2[b, t] @ wk.T) \
+                + lam[b, t, 2] * l3k
+            vs[b, t] = lam[b, t, 0] * (x[b, t] @ wv.T) + lam[b, t, 1] * (l2[b, t] @ wv.T) \
+                + lam[b, t, 2] * l3v
+    assert n_l3 >= B * (N - s.block)  # every token past the first block uses L3
+    G, dh, H = s.n_kv_heads, s.head_dim, s.n_heads
+    tk = torch.from_numpy(ks).view(B, N, G, dh).transpose(1, 2).repeat_interleave(H // G, 1)
+    tv = torch.from_numpy(vs).view(B, N, G, dh).transpose(1, 2).repeat_interleave(H // G, 1)
+    tq = q.view(B, N, H, dh).transpose(1, 2)
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True)
+    np.testing.assert_allclose(ref["o"], o.transpose(1, 2).numpy(), rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(ref["lam"], lam, rtol=1e-12, atol=0)
+
+
 # -------------------------------------------------------------- attention
 
 def _bruteforce_attention(q, k, v, n_kv):
@@ -571,29 +635,29 @@ def test_decode_continues_prefill_for_variants(mode, tiers):
         np.testing.assert_allclose(r["lam"], full["lam"][:, t], rtol=1e-12, atol=1e-15)
 
 
-def test_round_bf16_matches_torch_conversion():
-    r = rng(37)
-    a = np.concatenate([r.standard_normal(4000) * 10.0 ** r.integers(-8, 8, 4000),
-                        [0.0, -0.0, 1.0, -1.0, 1.00390625, 1.01171875, 65504.0, 3e38]])
-    want = torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).double().numpy()
-    np.testing.assert_array_equal(O.round_bf16(a), want)
-
-
-def test_hard_routing_decision_precision():
-    # The choice follows z_decide, the weights follow z; with z_decide = z it is
-    # the plain definition, and bf16-representable queries decide identically.
+def test_hard_routing_explicit_choice():
+    # route_choice is the ranking route_weights uses by default; an explicit
+    # kept set gives scipy's softmax over exactly those tiers (the weights of
+    # the other side of a tie), and fixed routing ignores it.
     r = rng(38)
     z = r.standard_normal((50, 3))
-    zd = z.copy()
-    zd[:, 0] += 10.0  # force L1 to be chosen
-    lam = O.route_weights(z, "top1", z_decide=zd)
-    np.testing.assert_array_equal(lam[:, 0], 1.0)
-    np.testing.assert_array_equal(O.route_weights(z, "top2", z_decide=z), O.route_weights(z, "top2"))
-    q = O.round_bf16(r.standard_normal((20, 16)))
-    w1, w2 = r.standard_normal((8, 16)), r.standard_normal((3, 8))
     for mode in ("top1", "top2"):
-        np.testing.assert_array_equal(O.router(q, w1, w2, mode, decide_q="bf16"),
-                                      O.router(q, w1, w2, mode))
+        keep = O.route_choice(z, mode)
+        np.testing.assert_array_equal(O.route_weights(z, mode, keep=keep), O.route_weights(z, mode))
+        assert np.all(keep.sum(-1) == {"top1": 1, "top2": 2}[mode])
+    alt = np.zeros((50, 3), dtype=bool)
+    alt[:, 1] = alt[:, 2] = True
+    lam = O.route_weights(z, "top2", keep=alt)
+    want = np.zeros_like(z)
+    from scipy.special import softmax
+
+    want[:, 1:] = softmax(z[:, 1:], axis=-1)
+    np.testing.assert_allclose(lam, want, rtol=1e-14, atol=0)
+    np.testing.assert_array_equal(O.route_weights(z, "fixed", keep=alt), O.route_weights(z, "fixed"))
+    # the choice is the float64 ranking of the logits: a gap of 1e-12 decides it
+    z2 = np.array([[0.5, 0.5 + 1e-12, 0.1], [0.5 + 1e-12, 0.5, 0.1]])
+    np.testing.assert_array_equal(O.route_choice(z2, "top1"),
+                                  [[False, True, False], [True, False, False]])
 
 
 # ----------------------------------------------------- full MKA (three paths)
