@@ -1,24 +1,27 @@
 #!/usr/bin/env python3
 """Benchmark of the FastMKA layer forward on one MI355X (gfx950).
 
-One step = one whole-layer prefill of the Qwen2.5-7B-shaped layer (batch 2,
-4096 tokens, D=3584, 28 query / 4 KV heads of 128, bf16) through the composite
-C-ABI call mka_prefill: route (Q projection + router), EMA scan and block
-means, block index and projections, retrieval, fusion + K/V projection, causal
-flash attention.  Inputs are resident in HBM before timing starts.  ``value``
-is prefill tokens/s.  Before the warmup, untimed back-to-back steps run for
-``--settle-ms`` (the GPU's clocks ramp up over tens of milliseconds of load
-after an idle spell).  A second loop issues the stage calls one by one with
-HIP events between them for the per-stage breakdown and the attention
-roofline.  ``--variants`` adds the routing and tier variants.
+One step = one whole-layer prefill of the Llama-3.1-8B-shaped layer (batch 1,
+65536 tokens, D=4096, 32 query / 8 KV heads of 128, bf16) through the
+composite C-ABI call mka_prefill: route (Q projection + router), EMA scan and
+block means, block index and projections, retrieval, fusion + K/V
+projection, causal flash attention.  Inputs are resident in HBM before timing
+starts.  ``value`` is prefill tokens/s.  Before the warmup, untimed
+back-to-back steps run for ``--settle-ms`` (the GPU's clocks ramp up over tens
+of milliseconds of load after an idle spell).  A second loop issues the stage
+calls one by one with HIP events between them for the per-stage breakdown and
+the attention roofline.
 
-The same line carries the decode measurement (the 131072-token fused cache
-workload, 256 decode steps of ``mka_decode_step``: median microseconds per
-token), the roofline position of the dominant kernel and of decode
-attention, and the CPU oracle timed on a bounded sample.
+The same line carries the Qwen2.5-7B-shaped prefill workloads (2 x 4096 and
+1 x 32768 tokens) with the same figures, the decode measurement (the
+131072-token fused cache workload, 256 decode steps of ``mka_decode_step``:
+median microseconds per token, with three layers' caches taken in turn so
+that every step reads its cache from HBM, and with one layer re-read for
+comparison), and the CPU oracle timed on bounded samples.
 
-Also by default (``--quick`` skips them): a training step (forward and backward), the paged
-cache, batched decode, full MKA and the routing variants, each as its own object of the line.
+Also by default (``--quick`` skips them): a training step (forward and
+backward), the paged cache, batched decode, full MKA and the routing variants
+on the 2 x 4096 workload, each as its own object of the line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
 """
@@ -47,18 +50,32 @@ def log(*a):
 
 # Hardware-counter traffic (rocprofv3 FETCH_SIZE / WRITE_SIZE, KiB per dispatch)
 # is taken in two profiled runs of this script and summarised into a JSON file
-# under profiles/; the counters are scaled by what they read for a plain copy
-# kernel of known size.  Each kernel's entry records a hash of the sources it
-# is built from, and a figure is reported only while that hash still matches.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qwen7b_prefill4k_decode128k.json")
+# per workload under profiles/; the counters are scaled by what they read for a
+# plain copy kernel of known size.  Each kernel's entry records a hash of the
+# sources it is built from, and a figure is reported only while that hash
+# still matches.
 CSRC = os.path.join(ROOT, "route_kv_memory_amd", "csrc")
 KERNEL_SOURCES = {
     "attn_prefill_bf16_kernel": ["attn.hip"],
-    "attn_decode_split_kernel": ["attn.hip"],
+    "attn_decode_split_kernel": ["attn.hip", "attn_split.h"],
+    "decode_attend_kernel": ["decode.hip", "attn_split.h"],
+    "decode_inputs_kernel": ["decode.hip"],
     "gemm_bf16_kernel<256": ["gemm.hip", "gemm.h"],  # Q projection
     "gemm_bf16_kernel<128": ["gemm.hip", "gemm.h"],  # fused K/V projection
+    "ema_pass1": ["ema.hip"],
+    "ema_pass2": ["ema.hip"],
+    "ema_pass3": ["ema.hip"],
+    "router_mfma_kernel": ["route.hip"],
+    "simhash_split_kernel": ["l3.hip"],
+    "fuse_mix_kernel": ["fuse.hip"],
 }
 ROOFLINE_KERNEL = "attn_prefill_bf16_kernel"
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
 # The abstract page's ablations: Table 10 (fixed lambda = 1/3, hard top-2,
 # hard top-1) and Table 9 (L1+L2, L1+L3, L1 alone), as (route_mode, tiers).
 VARIANTS = [("fixed", "l1l2l3"), ("top2", "l1l2l3"), ("top1", "l1l2l3"), ("soft", "l1l2"),
@@ -132,11 +149,11 @@ def traffic_summary(fetch_csv, write_csv, copy_mib, commands):
     return out
 
 
-def traffic_for(kernel):
-    """Calibrated HBM bytes per launch of ``kernel``, or None when no counters
-    were taken for the current source of that kernel."""
+def traffic_for(kernel, workload):
+    """Calibrated HBM bytes per launch of ``kernel`` on ``workload``, or None
+    when no counters were taken for the current source of that kernel."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(traffic_file(workload)) as fh:
             entry = json.load(fh)["kernels"][kernel]
     except (OSError, KeyError, ValueError):
         return None
@@ -350,23 +367,33 @@ def bench_prefill_paged(s, steps, warmup, page_size, settle_ms=0.0):
     return (time.perf_counter() - t0) / steps * 1e3
 
 
-def bench_decode(s, steps, warmup, variants=(), full=False, page_size=None):
+def bench_decode(s, steps, warmup, variants=(), full=False, page_size=None, copies=1):
+    """Decode steps of the workload ``s``.  ``copies`` > 1: that many layers
+    (weights, state and fused cache each), taken in turn step by step, so that
+    a step's cache and weights were last read ``copies - 1`` steps earlier;
+    with three copies (about 0.9 GB) every step reads them from HBM rather than
+    from the 256 MB last-level cache.  Routing variants and full MKA run on the
+    first copy alone."""
     import torch
 
     from route_kv_memory_amd import mka
     from route_kv_memory_amd.inputs import decode_inputs
     from route_kv_memory_amd.layer import Layer, to_device
 
-    log(f"decode: generating {s.name} state")
+    log(f"decode: generating {s.name} state ({copies} cop{'y' if copies == 1 else 'ies'})")
     dec = decode_inputs(s)
     T0, n = s.decode_cached, s.decode_steps
     t_cap = T0 + n
     nb0 = T0 // s.block
-    layer = Layer(s, dec, t_cap=t_cap, nb_cap=t_cap // s.block + 1, full=full, page_size=page_size,
-                  spare_pages=8 if page_size else 0)
+    layers = []
+    for i in range(copies):
+        lay = Layer(s, dec, t_cap=t_cap, nb_cap=t_cap // s.block + 1, full=full and i == 0,
+                    page_size=page_size, spare_pages=8 if page_size else 0)
+        lay.load_cache("k", to_device(dec["k_cache"], s.dtype))
+        lay.load_cache("v", to_device(dec["v_cache"], s.dtype))
+        layers.append(lay)
+    layer = layers[0]
     st = layer.st
-    layer.load_cache("k", to_device(dec["k_cache"], s.dtype))
-    layer.load_cache("v", to_device(dec["v_cache"], s.dtype))
     if full:  # the three tiers' caches hold the same synthetic rows (timing only)
         for c in ("k", "v"):
             for t in layer.kv3[c]:
@@ -376,29 +403,33 @@ def bench_decode(s, steps, warmup, variants=(), full=False, page_size=None):
     tokens = to_device(dec["tokens"], s.dtype)
     del dec
     d1 = layer.dims(1)
-    iws = layer.workspace(max(mka.mka_workspace_bytes(d1, mka.MKA_OP_INDEX, nb0),
-                              mka.mka_workspace_bytes(d1, mka.MKA_OP_DECODE_STEP, t_cap)))
+    for lay in layers:
+        lay.workspace(max(mka.mka_workspace_bytes(d1, mka.MKA_OP_INDEX, nb0),
+                          mka.mka_workspace_bytes(d1, mka.MKA_OP_DECODE_STEP, t_cap)))
 
     def reset():
-        st["ema_state"].copy_(init["ema_state"])
-        st["block_acc"].copy_(init["block_acc"])
-        st["block_means"][:, :nb0].copy_(means0)
-        layer.index_blocks(0, nb0)
+        for lay in layers:
+            lay.st["ema_state"].copy_(init["ema_state"])
+            lay.st["block_acc"].copy_(init["block_acc"])
+            lay.st["block_means"][:, :nb0].copy_(means0)
+            lay.index_blocks(0, nb0)
 
-    out = layer.outputs(1)
+    outs = [lay.outputs(1) for lay in layers]
     stream = torch.cuda.current_stream()
 
-    def run(fn=layer.decode_step):
+    def run(fn=None, n_copies=copies):
+        # step k runs on copy k % n_copies at that copy's next position
+        fns = [fn] if fn is not None else [lay.decode_step for lay in layers[:n_copies]]
         reset()
         for k in range(warmup):
-            fn(tokens[k], T0 + k, out=out)
+            fns[k % n_copies](tokens[k], T0 + k // n_copies, out=outs[k % n_copies])
         reset()
         torch.cuda.synchronize()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         t0 = time.perf_counter()
         ev[0].record(stream)
         for k in range(steps):
-            fn(tokens[k], T0 + k, out=out)
+            fns[k % n_copies](tokens[k], T0 + k // n_copies, out=outs[k % n_copies])
             ev[k + 1].record(stream)
         host_us = (time.perf_counter() - t0) / steps * 1e6  # enqueue cost per step
         torch.cuda.synchronize()
@@ -410,36 +441,48 @@ def bench_decode(s, steps, warmup, variants=(), full=False, page_size=None):
     var_us = {}
     for mode, tiers in variants:
         layer.shape = s.replace(route_mode=mode, tiers=tiers)
-        var_us[f"{mode}/{tiers}"] = float(np.median(run()[0]))
+        var_us[f"{mode}/{tiers}"] = float(np.median(run(n_copies=1)[0]))
         log(f"decode variant {mode}/{tiers}: {var_us[f'{mode}/{tiers}']:.1f} us/token")
     layer.shape = s
     full_us = None
     if full:
-        f_us, f_host, _ = run(layer.full_decode_step)
+        f_us, f_host, _ = run(layer.full_decode_step, n_copies=1)
         full_us = {"median_us": float(np.median(f_us)), "host_us": f_host}
         log(f"decode full MKA: {full_us['median_us']:.1f} us/token")
     step_us, host_us, wall_us = run()
+    warm = None
+    if copies > 1:  # one layer re-read every step (its cache partly stays in the LLC)
+        w_us, w_host, _ = run(n_copies=1)
+        warm = {"median_us": float(np.median(w_us)), "host_us": w_host}
 
     if page_size:  # the single-call attention entry takes contiguous caches
         return dict(median_us=float(np.median(step_us)), host_us=host_us, cached=T0,
                     steps=steps)
-    # Decode attention alone at the first step's length, for its roofline.
+    # Decode attention alone at the first step's length, for its roofline:
+    # the copies' caches in turn (cold), and one cache re-read (warm).
     L = T0 + 1
     nbytes = mka.mka_workspace_bytes(d1, mka.MKA_OP_ATTN_DECODE, L)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    o = torch.empty_like(out["o"])
-    reps = 50
-    a_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    for _ in range(5):
-        mka.mka_attn_decode(d1, out["q"], st["k_cache"], st["v_cache"], t_cap, L, o, ws, nbytes,
-                            stream)
-    a_ev[0].record(stream)
-    for _ in range(reps):
-        mka.mka_attn_decode(d1, out["q"], st["k_cache"], st["v_cache"], t_cap, L, o, ws, nbytes,
-                            stream)
-    a_ev[1].record(stream)
-    torch.cuda.synchronize()
-    attn_us = a_ev[0].elapsed_time(a_ev[1]) * 1e3 / reps
+    o = torch.empty_like(outs[0]["o"])
+    reps = 48
+
+    def attn_time(n_copies):
+        def one(k):
+            lay = layers[k % n_copies]
+            mka.mka_attn_decode(d1, outs[k % n_copies]["q"], lay.st["k_cache"], lay.st["v_cache"],
+                                t_cap, L, o, ws, nbytes, stream)
+        for k in range(6):
+            one(k)
+        a_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        a_ev[0].record(stream)
+        for k in range(reps):
+            one(k)
+        a_ev[1].record(stream)
+        torch.cuda.synchronize()
+        return a_ev[0].elapsed_time(a_ev[1]) * 1e3 / reps
+
+    attn_us = attn_time(copies)
+    attn_warm_us = attn_time(1) if copies > 1 else attn_us
     B = s.batch
     kv_bytes = 2.0 * L * s.n_kv_heads * s.head_dim * 2 * B  # K and V rows of every sequence, bf16
     el = 2
@@ -449,8 +492,9 @@ def bench_decode(s, steps, warmup, variants=(), full=False, page_size=None):
                               + s.router_hidden * s.q_width + 3 * s.router_hidden) * el
                   + s.hash_bits * s.d_model * 4 + B * (s.top_r * s.d_model * 4 + nb0 * 8))
     return dict(median_us=float(np.median(step_us)), mean_us=float(step_us.mean()),
-                wall_us=wall_us, host_us=host_us, attn_us=attn_us, kv_bytes=kv_bytes, step_bytes=step_bytes,
-                cached=T0, steps=steps, variants_us=var_us, full=full_us)
+                wall_us=wall_us, host_us=host_us, attn_us=attn_us, attn_warm_us=attn_warm_us,
+                kv_bytes=kv_bytes, step_bytes=step_bytes, cached=T0, steps=steps,
+                variants_us=var_us, full=full_us, warm=warm, copies=copies)
 
 
 def onbox_peaks():
@@ -489,25 +533,142 @@ def onbox_peaks():
                     "sustained matrix load) and a 4 GiB streaming read"}
 
 
-def cpu_baseline(s, n_tokens, batch):
-    """The oracle, as it stands, on the first ``n_tokens`` of ``batch`` sequences."""
+def host_info():
+    """The host's CPU model, the threads the oracle's BLAS uses and the BLAS
+    library numpy is built against."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    blas, threads = None, cores
+    try:
+        cfg = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{cfg.get('name')} {cfg.get('version')}"
+    except Exception:  # noqa: BLE001 - build info is optional metadata
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if pools:
+            threads = pools[0]["num_threads"]
+            blas = f"{pools[0].get('internal_api')} {pools[0].get('version')}"
+    except Exception:  # noqa: BLE001
+        pass
+    return dict(cpu_model=model, cores=threads, host_cpus=cores, blas=blas)
+
+
+def cpu_prefill(s, rows=None, n_tokens=None, batch=None):
+    """The oracle, as it stands, on a prefill workload: every stage over every
+    token (of the first ``n_tokens`` of ``batch`` sequences), attention on
+    ``rows`` (every row when None).  Returns (seconds, description)."""
     from oracle import mka_oracle as O
     from route_kv_memory_amd.inputs import prefill_inputs
 
+    batch = batch or s.batch
+    n_tokens = n_tokens or s.seq
     inp = prefill_inputs(s.replace(batch=batch), seq=n_tokens)
     w = [inp[k] for k in ("w_q", "w_k", "w_v", "w_r1", "w_r2", "proj")]
     kw = dict(n_heads=s.n_heads, n_kv_heads=s.n_kv_heads,
               ema_decay=float(np.float32(s.ema_decay)), block=s.block, top_r=s.top_r)
     t0 = time.perf_counter()
-    O.prefill(inp["x"], *w, **kw)
+    O.prefill(inp["x"], *w, rows=rows, **kw)
     dt = time.perf_counter() - t0
-    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-    whole = batch == s.batch and n_tokens == s.seq
-    what = ("the whole step" if whole else
-            f"the first {n_tokens} tokens of {batch} of the {s.batch} sequences")
-    return dict(value=batch * n_tokens / dt, unit="tokens/s", cores=cores, kind="oracle",
-                sample=f"whole-layer prefill (every stage, attention on every row) over {what} "
-                       f"({batch}x{n_tokens} tokens, same seeded inputs), fp64 NumPy, {dt:.1f} s")
+    what = f"{batch}x{n_tokens} tokens of {s.name}, every stage over every token, attention "
+    if rows is None:
+        what += "on every row"
+    else:
+        n = len(rows)
+        pairs = float(np.sum(np.asarray(rows) + 1))
+        what += (f"on {n} sampled query rows ({100.0 * n / n_tokens:.2f}% of the rows, "
+                 f"{100.0 * pairs / (n_tokens * (n_tokens + 1) / 2):.2f}% of the causal pairs)")
+    return dt, what
+
+
+def cpu_decode(s, attend_steps):
+    """The oracle on the decode workload: every one of its steps on the carried
+    state, attention at ``attend_steps`` only.  Returns (seconds, description)."""
+    from oracle import mka_oracle as O
+    from route_kv_memory_amd.inputs import decode_inputs
+
+    dec = decode_inputs(s)
+    w = [dec[k] for k in ("w_q", "w_k", "w_v", "w_r1", "w_r2", "proj")]
+    kw = dict(n_heads=s.n_heads, n_kv_heads=s.n_kv_heads,
+              ema_decay=float(np.float32(s.ema_decay)), block=s.block, top_r=s.top_r)
+    T0, n = s.decode_cached, s.decode_steps
+    t0 = time.perf_counter()
+    st = O.decode_init(dec["k_cache"], dec["v_cache"], dec["ema_state"], dec["block_acc"],
+                       dec["block_means"], dec["proj"], t_cap=T0 + n)
+    for k in range(n):
+        O.decode_step(st, dec["tokens"][k], *w, attend=k in attend_steps, **kw)
+    dt = time.perf_counter() - t0
+    return dt, (f"{n} decode steps of {s.name} (state carried through every step, attention "
+                f"at the {len(attend_steps)} steps {sorted(attend_steps)})")
+
+
+def cpu_baselines(s_head, extra):
+    """The oracle timed on bounded samples of every measured workload.  The
+    headline entry is the one of the line's workload; the others are listed
+    under ``workloads``."""
+    from route_kv_memory_amd.inputs import sampled_rows, workload
+
+    info = host_info()
+    out = {}
+
+    def prefill_entry(s):
+        rows = sampled_rows(s) if s.n_sampled else None
+        dt, what = cpu_prefill(s, rows=rows)
+        log(f"cpu baseline {s.name}: {dt:.1f} s")
+        return dict(value=s.batch * s.seq / dt, unit="tokens/s", seconds=dt,
+                    kind="oracle (sampled)" if rows is not None else "oracle", sample=what)
+
+    head = prefill_entry(s_head)
+    for name in extra:
+        s = workload(name)
+        if s.is_decode:
+            steps = {0, 1, 126, 127, 128, 129, 254, 255}
+            dt, what = cpu_decode(s, steps)
+            log(f"cpu baseline {s.name}: {dt:.1f} s")
+            out[name] = dict(value=dt / s.decode_steps * 1e3, unit="ms/token",
+                             seconds=dt, kind="oracle (attention on a step subset)", sample=what)
+        else:
+            out[name] = prefill_entry(s)
+    line = dict(value=head["value"], unit="tokens/s", cores=info["cores"], kind="oracle",
+                sample=f"{head['kind']}: {head['sample']}; fp64 NumPy, {head['seconds']:.1f} s",
+                cpu_model=info["cpu_model"], host_cpus=info["host_cpus"], blas=info["blas"],
+                workloads=out)
+    return line
+
+
+def prefill_entry(s, pf, onbox):
+    """Figures of one timed prefill workload: tokens/s, the attention +
+    projection fraction of bf16 MFMA peak and the attention kernel's roofline."""
+    flops = prefill_flops(s)
+    tokens = s.batch * s.seq
+    stage_ms = pf["stage_ms"]
+    achieved = flops["attn"] / (stage_ms["attn"] * 1e-3)
+    return {
+        "workload": s.name, "batch": s.batch, "seq_len": s.seq,
+        "tokens_per_s": tokens / (pf["wall_ms"] * 1e-3), "ms_per_step": pf["wall_ms"],
+        "gpu_ms_per_step": pf["gpu_ms"],
+        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "sequential_ms_per_step": pf["sequential_ms"],
+        "flops": {k: v for k, v in flops.items()},
+        "prefill_tflops": sum(flops.values()) / (pf["gpu_ms"] * 1e-3) / 1e12,
+        "attn_proj_frac": sum(flops.values()) / (pf["gpu_ms"] * 1e-3) / PEAK_BF16_FLOPS,
+        "roofline": {"kernel": ROOFLINE_KERNEL, "bound": "mfma", "achieved": achieved / 1e12,
+                     "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_FLOPS,
+                     "traffic": traffic_for(ROOFLINE_KERNEL, s.name),
+                     "onbox_peak": onbox["mfma_bf16_tflops"],
+                     "frac_onbox": achieved / 1e12 / onbox["mfma_bf16_tflops"]},
+    }
 
 
 def main():
@@ -515,33 +676,41 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen7b_prefill_4k")
+    ap.add_argument("--workload", default="llama8b_prefill_64k",
+                    help="the headline prefill workload (the line's value and roofline)")
+    ap.add_argument("--extra-workloads", default="qwen7b_prefill_4k,qwen7b_prefill_32k",
+                    help="more prefill workloads reported under 'prefill' (comma list; '' none)")
+    ap.add_argument("--aux-workload", default="qwen7b_prefill_4k",
+                    help="the prefill workload of the training step, paged cache, full MKA and "
+                         "routing variants")
     ap.add_argument("--decode-workload", default="qwen7b_decode_128k")
+    ap.add_argument("--decode-copies", type=int, default=3,
+                    help="layers (cache, weights, state) taken in turn by the decode steps")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain copy of MIB MiB (counter calibration)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write the traffic file under profiles/ from two rocprofv3 --pmc "
-                         "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE); no GPU use")
+                    help="write the traffic file of --workload under profiles/ from two rocprofv3 "
+                         "--pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE); no GPU use")
+    ap.add_argument("--traffic-workload", default=None,
+                    help="with --traffic-summary: the workload the counters belong to (default "
+                         "--workload)")
     ap.add_argument("--summary-command", action="append", default=[],
                     help="with --traffic-summary: the profiling commands, recorded verbatim")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle tokens per sequence "
-                    "(0: the whole sequence)")
-    ap.add_argument("--cpu-batch", type=int, default=0, help="oracle sequences (0: all)")
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed back-to-back prefill steps for this long before the warmup "
                          "(GPU clocks ramp up under load)")
     ap.add_argument("--full-mka", action="store_true",
-                    help="also time full MKA (three attention paths mixed by lambda) on the same "
-                         "workloads")
+                    help="also time full MKA (three attention paths mixed by lambda) on the "
+                         "auxiliary workloads")
     ap.add_argument("--quick", action="store_true",
                     help="only the prefill and decode lines (skip the training step, paged "
                          "cache, batched decode, full MKA and routing variants that the default "
                          "run adds)")
     ap.add_argument("--train", action="store_true",
                     help="time a training step (forward with saved log-sum-exp, then the "
-                         "backward) of the prefill workload (on by default)")
+                         "backward) of the auxiliary workload (on by default)")
     ap.add_argument("--paged", type=int, default=0, metavar="ROWS",
                     help="time prefill and decode with a paged fused cache of pages of ROWS rows "
                          "(default 256 unless --quick)")
@@ -549,7 +718,7 @@ def main():
                     help="time batched decode, 4 sequences of 32K cached tokens (on by default)")
     ap.add_argument("--variants", action="store_true",
                     help="also time the routing and tier variants (fixed, hard top-1/top-2; "
-                         "L1+L2, L1+L3, L1 alone) on the same workloads")
+                         "L1+L2, L1+L3, L1 alone) on the auxiliary workloads")
     args = ap.parse_args()
     if not args.quick:  # every measured row of the build in the default line
         args.train = args.decode_batch = args.full_mka = args.variants = True
@@ -557,7 +726,8 @@ def main():
     if args.traffic_summary:
         res = traffic_summary(*args.traffic_summary, args.copy_calibration or 1024,
                               args.summary_command)
-        with open(TRAFFIC_FILE, "w") as fh:
+        res["workload"] = args.traffic_workload or args.workload
+        with open(traffic_file(res["workload"]), "w") as fh:
             json.dump(res, fh, indent=1)
             fh.write("\n")
         print(json.dumps(res["kernels"], indent=1))
@@ -577,19 +747,19 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
     s = I.workload(args.workload)
+    extra = [w for w in args.extra_workloads.split(",") if w]
     variants = VARIANTS if args.variants else ()
-    pf = bench_prefill(s, args.steps, args.warmup, variants, args.settle_ms, args.full_mka)
-    flops = prefill_flops(s)
+    aux = args.aux_workload
+    # the headline workload (and, when it is also the auxiliary one, its variants)
+    pf = bench_prefill(s, args.steps, args.warmup, variants if s.name == aux else (),
+                       args.settle_ms, args.full_mka and s.name == aux)
+    log(f"prefill {s.name}: {pf['wall_ms']:.3f} ms per step, attention {pf['stage_ms']['attn']:.3f} ms")
     onbox = onbox_peaks()
     log(f"on-box peaks: {onbox['mfma_bf16_tflops']:.0f} TFLOP/s bf16 MFMA, "
         f"{onbox['hbm_read_gbs']:.0f} GB/s streaming read")
+    head = prefill_entry(s, pf, onbox)
     tokens = s.batch * s.seq
     ms = pf["wall_ms"]
-    stage_ms = pf["stage_ms"]
-    # The dominant kernel is causal attention: the "attn" stage is exactly one
-    # launch of it, timed by HIP events on the stream it is launched on.
-    dom = "attn"
-    achieved = flops[dom] / (stage_ms[dom] * 1e-3)
     line = {
         "metric": METRIC,
         "value": tokens / (ms * 1e-3),
@@ -610,50 +780,76 @@ def main():
         "settle": {"ms": args.settle_ms, "steps": pf["settle_steps"],
                    "note": "untimed back-to-back steps before the warmup, so that the timed "
                            "steps run at the clocks of a loaded GPU"},
-        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "stages_ms": head["stages_ms"],
         "stages_note": "stage calls one by one on one stream (the timed composite overlaps the "
                        "ema/index/retrieve chain with route)",
         "sequential_ms_per_step": pf["sequential_ms"],
-        "prefill_tflops": sum(flops.values()) / (pf["gpu_ms"] * 1e-3) / 1e12,
-        "roofline": {"kernel": ROOFLINE_KERNEL, "bound": "mfma", "achieved": achieved / 1e12,
-                     "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_FLOPS, "traffic": traffic_for(ROOFLINE_KERNEL),
-                     "onbox_peak": onbox["mfma_bf16_tflops"],
-                     "frac_onbox": achieved / 1e12 / onbox["mfma_bf16_tflops"]},
+        "prefill_tflops": head["prefill_tflops"],
+        "attn_proj_frac": head["attn_proj_frac"],
+        "roofline": head["roofline"],
         "onbox_peaks": onbox,
+        "prefill": {},
     }
+    pf_aux = pf if s.name == aux else None
+    for name in extra:
+        sw = I.workload(name)
+        pfw = bench_prefill(sw, args.steps, args.warmup, variants if name == aux else (),
+                            args.settle_ms, args.full_mka and name == aux)
+        log(f"prefill {name}: {pfw['wall_ms']:.3f} ms per step, attention "
+            f"{pfw['stage_ms']['attn']:.3f} ms")
+        line["prefill"][name] = prefill_entry(sw, pfw, onbox)
+        if name == aux:
+            pf_aux = pfw
+    s_aux = I.workload(aux)
+    aux_tokens = s_aux.batch * s_aux.seq
+    dc = None
     if not args.no_decode:
         ds = I.workload(args.decode_workload)
-        dc = bench_decode(ds, ds.decode_steps, 8, variants, args.full_mka)
+        dc = bench_decode(ds, ds.decode_steps, 8, variants, args.full_mka,
+                          copies=max(1, args.decode_copies))
         attn_bw = dc["kv_bytes"] / (dc["attn_us"] * 1e-6)
         step_bw = dc["step_bytes"] / (dc["median_us"] * 1e-6)
         line["decode"] = {
             "workload": ds.name, "cached_tokens": dc["cached"], "steps": dc["steps"],
+            "copies": dc["copies"],
+            "copies_note": "the steps take the copies' layers (cache, weights, state) in turn, "
+                           "so each step reads them from HBM (about 0.9 GB between two reads of "
+                           "one copy, against a 256 MB last-level cache)",
             "us_per_token_median": dc["median_us"], "us_per_token_mean": dc["mean_us"],
             "us_per_token_wall": dc["wall_us"], "us_per_token_host_enqueue": dc["host_us"],
+            "step_bytes": dc["step_bytes"],
             "step_hbm_frac": step_bw / PEAK_HBM_BYTES,
+            "warm": None if dc["warm"] is None else {
+                "us_per_token_median": dc["warm"]["median_us"],
+                "step_hbm_frac": dc["step_bytes"] / (dc["warm"]["median_us"] * 1e-6)
+                / PEAK_HBM_BYTES,
+                "attn_us_per_launch": dc["attn_warm_us"],
+                "attn_hbm_frac": dc["kv_bytes"] / (dc["attn_warm_us"] * 1e-6) / PEAK_HBM_BYTES,
+                "note": "one layer's cache and weights re-read every step (part of them stays "
+                        "in the last-level cache)"},
             "roofline": {"kernel": "attn_decode", "bound": "hbm", "achieved": attn_bw / 1e9,
                          "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
                          "frac": attn_bw / PEAK_HBM_BYTES,
-                         "traffic": traffic_for("attn_decode_split_kernel"),
+                         "traffic": traffic_for("attn_decode_split_kernel", ds.name),
                          "us_per_launch": dc["attn_us"],
                          "onbox_peak": onbox["hbm_read_gbs"],
                          "frac_onbox": attn_bw / 1e9 / onbox["hbm_read_gbs"]},
         }
-    if variants:
+    if variants and pf_aux is not None:
         line["variants"] = {
-            k: {"prefill_tokens_per_s": tokens / (v * 1e-3), "prefill_ms": v,
-                "decode_us_per_token": dc["variants_us"].get(k) if not args.no_decode else None}
-            for k, v in pf["variants_ms"].items()}
+            k: {"workload": aux, "prefill_tokens_per_s": aux_tokens / (v * 1e-3), "prefill_ms": v,
+                "decode_us_per_token": dc["variants_us"].get(k) if dc else None}
+            for k, v in pf_aux["variants_ms"].items()}
     if args.train:
-        tr = bench_train(s, args.steps, args.warmup, args.settle_ms)
+        tr = bench_train(s_aux, args.steps, args.warmup, args.settle_ms)
         log(f"training step: {tr['ms']:.3f} ms (forward {tr['fwd_ms']:.3f}, backward "
             f"{tr['bwd_ms']:.3f})")
         # the four products of the attention gradient (dV, dP, dQ, dK), 2*dh flops
         # per causal pair each; recomputing the scores is not counted
-        bwd_flops = 2.0 * flops["attn"]
+        bwd_flops = 2.0 * prefill_flops(s_aux)["attn"]
         bwd_ach = bwd_flops / (tr["attn_bwd_ms"] * 1e-3)
-        line["train"] = {"tokens_per_s": tokens / (tr["ms"] * 1e-3), "ms_per_step": tr["ms"],
+        line["train"] = {"workload": aux, "tokens_per_s": aux_tokens / (tr["ms"] * 1e-3),
+                         "ms_per_step": tr["ms"],
                          "forward_ms": tr["fwd_ms"], "backward_ms": tr["bwd_ms"],
                          "attn_backward_ms": tr["attn_bwd_ms"],
                          "roofline": {"kernel": "attn_bwd_dkv_kernel + attn_bwd_dq_kernel",
@@ -665,16 +861,17 @@ def main():
                          "note": "mka_prefill (saving log-sum-exp) + mka_backward: gradients of "
                                  "x and every weight, fp32"}
     if args.paged:
-        pms = bench_prefill_paged(s, args.steps, args.warmup, args.paged, args.settle_ms)
+        pms = bench_prefill_paged(s_aux, args.steps, args.warmup, args.paged, args.settle_ms)
         log(f"paged prefill (pages of {args.paged}): {pms:.4f} ms")
-        line["paged"] = {"page_size": args.paged, "prefill_ms": pms,
-                         "prefill_tokens_per_s": tokens / (pms * 1e-3)}
+        line["paged"] = {"workload": aux, "page_size": args.paged, "prefill_ms": pms,
+                         "prefill_tokens_per_s": aux_tokens / (pms * 1e-3)}
         if not args.no_decode:
             ds = I.workload(args.decode_workload)
             pdc = bench_decode(ds, ds.decode_steps, 8, page_size=args.paged)
             log(f"paged decode: {pdc['median_us']:.1f} us/token")
             line["paged"].update(decode_us_per_token=pdc["median_us"],
-                                 decode_host_us_per_token=pdc["host_us"])
+                                 decode_host_us_per_token=pdc["host_us"],
+                                 decode_note="one layer re-read every step (compare decode.warm)")
     if args.decode_batch:
         bs = I.workload("qwen7b_decode_32k_b4")
         bdc = bench_decode(bs, bs.decode_steps, 8)
@@ -685,17 +882,21 @@ def main():
             "tokens_per_s": bs.batch / (bdc["median_us"] * 1e-6),
             "step_hbm_frac": bdc["step_bytes"] / (bdc["median_us"] * 1e-6) / PEAK_HBM_BYTES,
             "attn_us_per_launch": bdc["attn_us"],
-            "attn_hbm_frac": bdc["kv_bytes"] / (bdc["attn_us"] * 1e-6) / PEAK_HBM_BYTES}
-    if args.full_mka:
+            "attn_hbm_frac": bdc["kv_bytes"] / (bdc["attn_us"] * 1e-6) / PEAK_HBM_BYTES,
+            "note": "one layer re-read every step (its 4 x 32K cache is 269 MB)"}
+    if args.full_mka and pf_aux is not None and pf_aux["full_ms"] is not None:
         line["full_mka"] = {
-            "prefill_ms": pf["full_ms"], "prefill_tokens_per_s": tokens / (pf["full_ms"] * 1e-3),
-            "decode_us_per_token": dc["full"]["median_us"] if not args.no_decode else None,
-            "decode_host_us_per_token": dc["full"]["host_us"] if not args.no_decode else None,
+            "workload": aux,
+            "prefill_ms": pf_aux["full_ms"],
+            "prefill_tokens_per_s": aux_tokens / (pf_aux["full_ms"] * 1e-3),
+            "decode_us_per_token": dc["full"]["median_us"] if dc else None,
+            "decode_host_us_per_token": dc["full"]["host_us"] if dc else None,
             "note": "three attention paths (one K/V cache per tier) mixed by lambda; same "
-                    "inputs as the FastMKA figures of this line"}
+                    "inputs as the FastMKA figures of this line; decode on one layer re-read"}
     if not args.no_cpu_baseline:
-        log("cpu baseline: oracle on a bounded sample")
-        line["cpu_baseline"] = cpu_baseline(s, args.cpu_tokens or s.seq, args.cpu_batch or s.batch)
+        log("cpu baseline: the oracle on bounded samples")
+        others = [w for w in ["tiny_f32"] + extra + [args.decode_workload] if w != s.name]
+        line["cpu_baseline"] = cpu_baselines(s, others)
     print(json.dumps(line), flush=True)
 
 

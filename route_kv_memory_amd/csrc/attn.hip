@@ -12,7 +12,7 @@
 // register r of lane half hl hold key 16*(r/8) + 8*hl + r%8; the
 // probabilities then form, without any data movement, the B operand of
 // O^T = V^T P^T, whose A operand is read from a transposed V tile in LDS.
-// Scores use exp2 with log2(e)/sqrt(dh) folded into one scale.
+// Scores use exp2 with log2(e)/sqrt(dh) folded into one fp32 scale per score.
 #include "attn_split.h"
 
 namespace mka {
@@ -74,16 +74,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
 
   bf16x8 qf[NKS];
   {
+    // Q enters the products as stored; the scale log2(e)/sqrt(dh) is applied
+    // in fp32 to each score (folding it into Q would round Q to bf16 a second
+    // time, which moves peaked softmax weights by up to ~1%).
     const bf16_t* qp = Q + (static_cast<int64_t>(b * seq + min(q_row, seq - 1)) * H + h) * DH + 8 * hl;
-    // Q enters the products pre-scaled by log2(e)/sqrt(dh) (rounded to bf16
-    // once more), so the scores come out of the MFMA in the exp2 domain.
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
-      float f[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) f[j] = static_cast<float>(qv[j]) * sl2;
-      qf[ks] = pack_bf16x8(f);
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
       if (q_row >= seq) qf[ks] = bf16x8{};
     }
   }
@@ -132,11 +129,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
     }
   };
 
-  // ms: the running reference (exp2 domain); nms holds -ms in every
-  // accumulator register and seeds the score products, which then return the
-  // shifted scores s * log2(e)/sqrt(dh) - ms directly.
+  // ms: the running reference of the row's scores in the exp2 domain
+  // (scores scaled by log2(e)/sqrt(dh)); l_i and acc are relative to it.
   float ms = 0.f, l_i = 0.f;
-  f32x16 nms = f32x16{};
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
@@ -152,7 +147,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = nms;
+      s[kb] = f32x16{};
       const int P = kb * 32 + l32;
       const bf16_t* kr = &Ks[buf][P * DH];
 #pragma unroll
@@ -161,10 +156,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
                              qf[ks], s[kb]);
     }
 
-    // Online max-shift in the exp2 domain: ms is the running reference
-    // (scaled by log2(e)/sqrt(dh)).  It is raised only when a tile's maximum
-    // exceeds it by more than 8, so most tiles need no rescale; probabilities
-    // stay below 2^8, which fp32 sums and bf16 operands carry exactly as well.
+    // Online max-shift in the exp2 domain: ms is the running reference.  It
+    // is raised only when a tile's maximum exceeds it by more than 8, so most
+    // tiles need no rescale; probabilities stay below 2^8, which fp32 sums
+    // and bf16 operands carry as well as values below 1.
     const bool diag = (j0 + BN - 1) > wave_pos0;
     if (diag) {
       const int q_rel = static_cast<int>(q_pos - j0);  // keys of the tile after the query
@@ -184,9 +179,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
                                                        false, false);
       mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
-    // The reference is raised by the tile's maximum of the shifted scores
-    // when that exceeds 8 (and always on the first tile); the tile's scores
-    // shift with it.
+    // The tile's maximum relative to the reference, in the exp2 domain; the
+    // reference is raised to it when that exceeds 8 (and on the first tile,
+    // whose maximum is finite: key 0 is visible to every query row).
+    mx = fmaf(mx, sl2, -ms);
     const bool raise = jt == 0 || mx > 8.0f;
     if (__any(raise)) {
       const float delta = raise ? mx : 0.0f;
@@ -195,13 +191,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
       ms += delta;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[0][r] -= delta;
-        s[1][r] -= delta;
-        nms[r] = -ms;
-      }
     }
+    const float nms = -ms;
 
     // Probabilities as the bf16x8 B operands of O^T += V^T P^T; the row sum
     // adds the same bf16 values the products use, two per v_dot2 (each pair
@@ -218,8 +209,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const bf16x2v v = {
-              static_cast<__bf16>(__builtin_amdgcn_exp2f(s[kb][8 * st + 2 * i])),
-              static_cast<__bf16>(__builtin_amdgcn_exp2f(s[kb][8 * st + 2 * i + 1]))};
+              static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[kb][8 * st + 2 * i], sl2, nms))),
+              static_cast<__bf16>(
+                  __builtin_amdgcn_exp2f(fmaf(s[kb][8 * st + 2 * i + 1], sl2, nms)))};
           l_i = __builtin_amdgcn_fdot2_f32_bf16(v, ones, l_i, false);
           w[i] = __builtin_bit_cast(uint32_t, v);
         }

@@ -1,0 +1,136 @@
+"""GPU parity of the attention kernels on peaked scores, where the online
+max-shift (MKA reading note, method section 4: the running maximum is raised
+and the running numerator and denominator are rescaled by exp(mu_old - mu_new))
+acts on accumulators that already hold earlier tiles.
+
+Unit-scale layer inputs give scores of standard deviation ~1.4 in log2 units,
+so a later 64-key tile rarely beats the first tile's maximum by much.  Two
+input families force the rescale instead:
+  * planted: every query carries a shared direction u (q = z + 4u) and keys in
+    three late tiles are multiples of u whose scores exceed everything before
+    them by about 12, 24 and 36 in log2 units;
+  * scaled: Q multiplied by 8 (score deviation ~11.5 in log2 units), so tile
+    maxima jump by more than 8 many times along a row.
+The number of rescales of a row's accumulators after its first tile is counted
+on the host from the oracle's scores with the prefill kernel's rule (the
+running reference is raised when a 64-key tile's maximum exceeds it by more
+than 8, in log2 units) and must be positive for many rows.  Outputs are
+compared element by element with the oracle (bf16: max-abs 1e-2, relative L2
+1e-2).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mka_oracle as O
+from route_kv_memory_amd import inputs as I
+from route_kv_memory_amd import mka
+from route_kv_memory_amd.layer import to_device
+
+from .gpu_common import to_np
+from .parity import check_close, log
+
+pytestmark = pytest.mark.gpu
+
+TILE = 64          # keys per tile of the prefill kernel
+RAISE_LOG2 = 8.0   # the prefill kernel's raise threshold (log2 units)
+
+
+def peaked_inputs(kind, B, n_keys, H, G, dh, seed):
+    """bf16-exact q [B, n_keys, H, dh] (every position), k, v [B, G, n_keys, dh]."""
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((B, n_keys, H, dh))
+    k = r.standard_normal((B, G, n_keys, dh))
+    v = r.standard_normal((B, G, n_keys, dh))
+    if kind == "planted":
+        u = r.standard_normal(dh)
+        u /= np.linalg.norm(u)
+        q += 4.0 * u
+        sl2 = math.log2(math.e) / math.sqrt(dh)
+        # three late tiles, each with one key whose score beats the earlier
+        # maximum (~3.5 in log2 units) by ~12, ~24, ~36
+        for i, frac in enumerate((0.45, 0.65, 0.85)):
+            j = int(frac * n_keys)
+            k[:, :, j] = ((3.5 + 12.0 * (i + 1)) / (4.0 * sl2)) * u
+    elif kind == "scaled":
+        q *= 8.0
+    else:
+        raise ValueError(kind)
+    return I.round_bf16(q), I.round_bf16(k), I.round_bf16(v)
+
+
+def count_rescales(q, k, rows, G):
+    """Rescales after the first tile under the prefill kernel's rule, from the
+    oracle's (float64) scores; returns (total, rows with at least one)."""
+    B, n, H, dh = q.shape
+    sl2 = math.log2(math.e) / math.sqrt(dh)
+    total = rows_hit = 0
+    for b in range(B):
+        for h in range(H):
+            g = h // (H // G)
+            for i, t in enumerate(rows):
+                s = (k[b, g, :t + 1] @ q[b, i, h]) * sl2
+                ref = s[:TILE].max()
+                hit = 0
+                for j0 in range(TILE, t + 1, TILE):
+                    m = s[j0:j0 + TILE].max()
+                    if m > ref + RAISE_LOG2:
+                        hit += 1
+                        ref = m
+                total += hit
+                rows_hit += hit > 0
+    return total, rows_hit
+
+
+CASES = [("planted", 128, 0), ("planted", 64, 0), ("scaled", 128, 0), ("scaled", 64, 0),
+         ("planted", 128, 200), ("scaled", 128, 137)]
+
+
+@pytest.mark.parametrize("kind,dh,pos0", CASES)
+def test_prefill_attention_rescales_nonzero_accumulators(kind, dh, pos0):
+    # 600 new query rows (pos0 earlier rows already in the cache): 10-13 key
+    # tiles of 64 and a ragged tail; 4 query heads over 2 KV heads.
+    B, H, G, seq = 1, 4, 2, 600
+    n_keys = pos0 + seq
+    q_all, k, v = peaked_inputs(kind, B, n_keys, H, G, dh, seed=dh + pos0)
+    q = q_all[:, pos0:]
+    rows = np.arange(pos0, n_keys)
+    ref = O.attention(q, k, v, rows, G)
+    total, hit = count_rescales(q, k, rows, G)
+    log(f"  {kind} dh={dh} pos0={pos0}: {total} rescales after the first tile on "
+        f"{hit} of {B * H * seq} rows (oracle scores, kernel rule)")
+    assert hit >= 50, "the inputs must drive the rescale on many rows"
+    s = I.workload("tiny_f32").replace(dtype="bf16", n_heads=H, n_kv_heads=G, head_dim=dh,
+                                       d_model=H * dh)
+    d = mka.dims(s, seq=seq, batch=B)
+    o = torch.empty(B, seq, H, dh, dtype=torch.bfloat16, device="cuda")
+    log(f"  gpu: mka_attn_prefill {kind} dh={dh} seq={seq} pos0={pos0}")
+    mka.mka_attn_prefill(d, to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16"),
+                         n_keys, pos0, o)
+    torch.cuda.synchronize()
+    check_close(f"attn {kind}", to_np(o), ref, "bf16", max_abs=1e-2, rel_l2=1e-2)
+
+
+@pytest.mark.parametrize("kind,dh", [("planted", 128), ("scaled", 128), ("scaled", 64)])
+def test_decode_attention_on_peaked_scores(kind, dh):
+    # mka_attn_decode over 3000 and 4097 cache rows (several chunks, several
+    # 32-key tiles per wave), query at the last position.
+    B, H, G = 1, 8, 2
+    for L in (3000, 4097):
+        q_all, k, v = peaked_inputs(kind, B, L, H, G, dh, seed=L + dh)
+        q = q_all[:, L - 1:L]
+        ref = O.attention(q, k, v, np.array([L - 1]), G)
+        s = I.workload("tiny_f32").replace(dtype="bf16", n_heads=H, n_kv_heads=G, head_dim=dh,
+                                           d_model=H * dh)
+        d = mka.dims(s, seq=1, batch=B)
+        nbytes = mka.mka_workspace_bytes(d, mka.MKA_OP_ATTN_DECODE, L)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+        o = torch.empty(B, 1, H, dh, dtype=torch.bfloat16, device="cuda")
+        log(f"  gpu: mka_attn_decode {kind} dh={dh} L={L}")
+        mka.mka_attn_decode(d, to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16"),
+                            L, L, o, ws, ws.numel())
+        torch.cuda.synchronize()
+        check_close(f"decode {kind} L={L}", to_np(o), ref, "bf16", max_abs=1e-2, rel_l2=1e-2)
