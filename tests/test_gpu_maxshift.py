@@ -15,8 +15,12 @@ The number of rescales of a row's accumulators after its first tile is counted
 on the host from the oracle's scores with the prefill kernel's rule (the
 running reference is raised when a 64-key tile's maximum exceeds it by more
 than 8, in log2 units) and must be positive for many rows.  Outputs are
-compared element by element with the oracle (bf16: max-abs 1e-2, relative L2
-1e-2).
+compared element by element with the oracle: relative L2 error 1e-2 and,
+per element, |o - o_ref| <= 8e-3 + 2^-8 |o_ref|.  The second term is the bf16
+storage of O: peaked rows return single value rows of magnitude up to ~4,
+where half a bf16 ulp is up to 2^-9 |O| (7.8e-3 at |O| = 4); the kernel's own
+arithmetic (bf16 probabilities, fp32 sums) stays below ~5e-3 on these inputs
+(a NumPy emulation of it, before the output's rounding).
 """
 
 import math
@@ -34,6 +38,15 @@ from .gpu_common import to_np
 from .parity import check_close, log
 
 pytestmark = pytest.mark.gpu
+
+
+def check_peaked(name, got, ref):
+    check_close(name, got, ref, "bf16", rel_l2=1e-2)
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    worst = float((np.abs(got - ref) / (8e-3 + 2.0 ** -8 * np.abs(ref))).max())
+    log(f"  {name}: largest error / (8e-3 + 2^-8 |ref|) = {worst:.3f}")
+    assert worst <= 1.0, f"{name}: an element exceeds 8e-3 + 2^-8 |ref| ({worst:.3f})"
+
 
 TILE = 64          # keys per tile of the prefill kernel
 RAISE_LOG2 = 8.0   # the prefill kernel's raise threshold (log2 units)
@@ -111,7 +124,7 @@ def test_prefill_attention_rescales_nonzero_accumulators(kind, dh, pos0):
     mka.mka_attn_prefill(d, to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16"),
                          n_keys, pos0, o)
     torch.cuda.synchronize()
-    check_close(f"attn {kind}", to_np(o), ref, "bf16", max_abs=1e-2, rel_l2=1e-2)
+    check_peaked(f"attn {kind}", to_np(o), ref)
 
 
 @pytest.mark.parametrize("kind,dh", [("planted", 128), ("scaled", 128), ("scaled", 64)])
@@ -133,4 +146,4 @@ def test_decode_attention_on_peaked_scores(kind, dh):
         mka.mka_attn_decode(d, to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16"),
                             L, L, o, ws, ws.numel())
         torch.cuda.synchronize()
-        check_close(f"decode {kind} L={L}", to_np(o), ref, "bf16", max_abs=1e-2, rel_l2=1e-2)
+        check_peaked(f"decode {kind} L={L}", to_np(o), ref)
