@@ -221,6 +221,23 @@ int mka_attn_decode(const mka_dims* d, const void* q, const void* k_cache,
                     const void* v_cache, int64_t t_cap, int64_t cache_len, void* o,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* mka_attn_decode without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments and results as mka_attn_decode (the same
+ * kernels).  The split partials (4*B*H*n_chunks*(dh+2) bytes, n_chunks ~ 256 /
+ * (B*G*ceil(H/G/16)); 0.93 MB for one 128K Qwen2.5-7B-shaped sequence) go to a
+ * device array of the library, mka_attn_decode_noalloc_limit() = 4 MiB per
+ * GPU, held from the first call on a GPU until the process ends.  Larger
+ * requests return MKA_ERR_WORKSPACE (mka_last_error() says the sizes) and
+ * enqueue nothing.  Every call on one GPU uses that GPU's array: calls that
+ * overlap on one GPU (other streams, other threads) race and must be ordered
+ * by the caller.  The call allocates nothing (no hipMalloc, no library
+ * allocation); its first call on a GPU looks up the array's device address. */
+int mka_attn_decode_noalloc(const mka_dims* d, const void* q, const void* k_cache,
+                            const void* v_cache, int64_t t_cap, int64_t cache_len, void* o,
+                            void* stream);
+size_t mka_attn_decode_noalloc_limit(void);
+
 /* Composite: the whole layer over a prompt at positions pos0 .. pos0+seq-1 (the
  * calls above: route, ema_scan, l3_index and l3_block_kv of the blocks completed
  * here, l3_retrieve, fuse_kv_proj, attn_prefill).  ema_scan, l3_index and

@@ -900,6 +900,67 @@ int mka_attn_decode(const mka_dims* d, const void* q, const void* k_cache, const
                         static_cast<hipStream_t>(stream));
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free decode attention: the split partials live in a file-scope
+// device array (one copy per GPU, held until the process ends) instead of a
+// caller's workspace.  Host code never passes the array's name to a kernel:
+// the name is a host-side stand-in.  Its device address on each GPU comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = static_cast<size_t>(4) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+static void* scratch_for_current_device(int* rc) {
+  static std::mutex lock;
+  static std::unordered_map<int, void*> table;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *rc = hip_fail("attn_decode_noalloc/device", e);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> g(lock);
+  auto it = table.find(dev);
+  if (it != table.end()) return it->second;
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || ptr == nullptr) {
+    *rc = hip_fail("attn_decode_noalloc/scratch", e != hipSuccess ? e : hipErrorInvalidSymbol);
+    return nullptr;
+  }
+  table.emplace(dev, ptr);
+  return ptr;
+}
+
+int mka_attn_decode_noalloc(const mka_dims* d, const void* q, const void* k_cache,
+                            const void* v_cache, int64_t t_cap, int64_t cache_len, void* o,
+                            void* stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  MKA_CHECK(d->seq == 1, MKA_ERR_INVALID);
+  MKA_CHECK(ptrs_ok({q, k_cache, v_cache, o}), MKA_ERR_INVALID);
+  MKA_CHECK(cache_len >= 1 && cache_len <= t_cap, MKA_ERR_INVALID);
+  MKA_CHECK(cache_len <= kMaxDecodeCache && decode_chunk_fits(d, cache_len - 1),
+            MKA_ERR_UNSUPPORTED);
+  const size_t need = decode_ws(d, cache_len);
+  if (need > kNoAllocScratchBytes) {
+    std::snprintf(g_last_error, sizeof(g_last_error),
+                  "attn_decode_noalloc: the split partials need %zu bytes; the library's device "
+                  "scratch holds %zu",
+                  need, kNoAllocScratchBytes);
+    return MKA_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_for_current_device(&rc);
+    if (ws == nullptr) return rc;
+  }
+  return do_attn_decode(d, q, k_cache, v_cache, contiguous(d, t_cap), cache_len, o, ws,
+                        static_cast<hipStream_t>(stream));
+}
+
+size_t mka_attn_decode_noalloc_limit(void) { return kNoAllocScratchBytes; }
+
 static int check_layer_args(const mka_dims* d, const void* x, int64_t pos0, const mka_weights* w,
                             const mka_state* st, const mka_outputs* out) {
   MKA_CHECK(w != nullptr && st != nullptr && out != nullptr, MKA_ERR_INVALID);

@@ -23,7 +23,8 @@ __all__ = [
     "MKA_OP_PREFILL", "MKA_OP_DECODE_STEP", "MKA_OP_RETRIEVE", "MKA_OP_INDEX", "MKA_OP_ROUTE",
     "mka_route", "mka_ema_scan", "mka_l3_index", "mka_l3_block_kv", "mka_l3_retrieve",
     "mka_fuse_kv_proj",
-    "mka_attn_prefill", "mka_attn_decode", "mka_prefill", "mka_decode_step", "TierCache",
+    "mka_attn_prefill", "mka_attn_decode", "mka_attn_decode_noalloc",
+    "mka_attn_decode_noalloc_limit", "mka_prefill", "mka_decode_step", "TierCache",
     "mka_full_prefill", "mka_full_decode_step", "MKA_OP_FULL_PREFILL", "MKA_OP_FULL_DECODE_STEP",
     "Grads", "mka_backward", "MKA_OP_BACKWARD", "mka_attn_backward", "MKA_OP_ATTN_BACKWARD",
     "mka_workspace_bytes", "mka_status_string", "mka_last_error", "mka_version",
@@ -106,6 +107,8 @@ _SIGS = {
                          [_PD, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P, _I64, _I64, _P, _SZ, _P]),
     "mka_attn_prefill": (ctypes.c_int, [_PD, _P, _P, _P, _I64, _I64, _P, _P]),
     "mka_attn_decode": (ctypes.c_int, [_PD, _P, _P, _P, _I64, _I64, _P, _P, _SZ, _P]),
+    "mka_attn_decode_noalloc": (ctypes.c_int, [_PD, _P, _P, _P, _I64, _I64, _P, _P]),
+    "mka_attn_decode_noalloc_limit": (ctypes.c_size_t, []),
     "mka_prefill": (ctypes.c_int, [_PD, _P, _I64, ctypes.POINTER(Weights), ctypes.POINTER(State),
                                    ctypes.POINTER(Outputs), _P, _SZ, _P]),
     "mka_decode_step": (ctypes.c_int, [_PD, _P, _I64, ctypes.POINTER(Weights),
@@ -250,6 +253,16 @@ def mka_attn_decode(d, q, k_cache, v_cache, t_cap, cache_len, o, ws=None, ws_byt
     _check("mka_attn_decode", lib().mka_attn_decode(
         ctypes.byref(d), _ptr(q), _ptr(k_cache), _ptr(v_cache), t_cap, cache_len, _ptr(o),
         _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def mka_attn_decode_noalloc(d, q, k_cache, v_cache, t_cap, cache_len, o, stream=None):
+    _check("mka_attn_decode_noalloc", lib().mka_attn_decode_noalloc(
+        ctypes.byref(d), _ptr(q), _ptr(k_cache), _ptr(v_cache), t_cap, cache_len, _ptr(o),
+        _stream(stream)))
+
+
+def mka_attn_decode_noalloc_limit():
+    return lib().mka_attn_decode_noalloc_limit()
 
 
 def mka_prefill(d, x, pos0, weights, state, outputs, ws, ws_bytes, stream=None):

@@ -219,3 +219,22 @@ def test_paged_state_rejections():
     with pytest.raises(mka.MkaError) as e:  # the full-MKA tier caches are contiguous
         mka.mka_full_prefill(d, FAKE, 0, w, state(), tc, out, FAKE, 1 << 40, 0)
     assert e.value.status == mka.MKA_ERR_UNSUPPORTED
+
+
+def test_noalloc_decode_rejects_requests_beyond_its_scratch():
+    # 4 MiB of device scratch: one 128K Qwen-shaped sequence needs 0.93 MB of
+    # split partials; 128 sequences of 64 single-head groups need 4.26 MB.
+    assert mka.mka_attn_decode_noalloc_limit() == 4 << 20
+    d = mka.dims(I.workload("qwen7b_decode_128k"), seq=1)
+    assert mka.mka_workspace_bytes(d, mka.MKA_OP_ATTN_DECODE, 131073) <= 4 << 20
+    big = mka.dims(I.workload("qwen7b_decode_128k").replace(batch=128, n_heads=64, n_kv_heads=64,
+                                                             d_model=8192), seq=1)
+    need = mka.mka_workspace_bytes(big, mka.MKA_OP_ATTN_DECODE, 4096)
+    assert need > 4 << 20
+    with pytest.raises(mka.MkaError) as e:
+        mka.mka_attn_decode_noalloc(big, FAKE, FAKE, FAKE, 4096, 4096, FAKE, stream=0)
+    assert e.value.status == mka.MKA_ERR_WORKSPACE
+    assert "scratch" in mka.mka_last_error()
+    with pytest.raises(mka.MkaError) as e:  # the usual argument checks come first
+        mka.mka_attn_decode_noalloc(d, FAKE, FAKE, FAKE, 10, 11, FAKE, stream=0)
+    assert e.value.status == mka.MKA_ERR_INVALID
