@@ -4,6 +4,14 @@ Usage: ``python -m route_kv_memory_amd.build`` (or ``build()`` from Python).
 Every source is recompiled on each call; objects go to ``_build/`` beside the
 package and the shared library into the package directory, where the binding
 loads it from.
+
+``build(sanitize=True)`` (``python -m route_kv_memory_amd.build --sanitize``)
+builds a second library, ``_build/sanitize/libmka.so``, whose host code is
+instrumented with AddressSanitizer and UndefinedBehaviorSanitizer (the
+device code is not: the sanitizer flags apply to the host compilation only,
+``-Xarch_host``).  It is for host-side tests of the C ABI on the CPU: load it
+with the binding's ``MKA_LIB`` variable and the sanitizer runtime
+(``sanitizer_runtime()``) preloaded.
 """
 
 from __future__ import annotations
@@ -46,32 +54,54 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC)")
 
 
-def _compile(hipcc: str, src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-only sanitizers: each -fsanitize= follows -Xarch_host, so no device
+# code is instrumented.
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-fno-omit-frame-pointer", "-shared-libsan"]
+SANITIZE_DIR = os.path.join(BUILD, "sanitize")
+
+
+def sanitizer_runtime() -> str:
+    """The ASan runtime to preload into a process that loads the sanitized library."""
+    hipcc = _hipcc()
+    res = subprocess.run([hipcc, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.isabs(path):
+        raise RuntimeError("the clang ASan runtime was not found")
+    return path
+
+
+def _compile(hipcc: str, src: str, out_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc, *HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr}")
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every kernel source and link ``libmka.so``; returns its path."""
+def build(verbose: bool = True, sanitize: bool = False) -> str:
+    """Compile every kernel source and link ``libmka.so``; returns its path.
+    ``sanitize``: the host-sanitized library under ``_build/sanitize/`` instead."""
     hipcc = _hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+    out_dir = SANITIZE_DIR if sanitize else BUILD
+    extra = SANITIZE_FLAGS if sanitize else []
+    lib = os.path.join(SANITIZE_DIR, "libmka.so") if sanitize else LIB
+    os.makedirs(out_dir, exist_ok=True)
     workers = min(len(SOURCES), max(1, (os.cpu_count() or 4)))
     with cf.ThreadPoolExecutor(max_workers=workers) as ex:
-        objs = list(ex.map(lambda s: _compile(hipcc, s), SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+        objs = list(ex.map(lambda s: _compile(hipcc, s, out_dir, extra), SOURCES))
+    tmp = lib + ".tmp"
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}", file=sys.stderr)
-    return LIB
+        print(f"built {lib}", file=sys.stderr)
+    return lib
 
 
 if __name__ == "__main__":
-    build()
+    build(sanitize="--sanitize" in sys.argv[1:])

@@ -32,7 +32,9 @@ __all__ = [
 ]
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libmka.so")
+# MKA_LIB names another build of the library (the host-sanitized one for the
+# sanitizer tests); by default the in-tree libmka.so.
+LIB_PATH = os.environ.get("MKA_LIB") or os.path.join(PKG, "libmka.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "mka.h")
 HEADERS = [HEADER, os.path.join(os.path.dirname(PKG), "include", "mka_probe.h")]
 
