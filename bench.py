@@ -60,8 +60,10 @@ KERNEL_SOURCES = {
     "attn_decode_split_kernel": ["attn.hip", "attn_split.h"],
     "decode_attend_kernel": ["decode.hip", "attn_split.h"],
     "decode_inputs_kernel": ["decode.hip"],
-    "gemm_bf16_kernel<256": ["gemm.hip", "gemm.h"],  # Q projection
-    "gemm_bf16_kernel<128": ["gemm.hip", "gemm.h"],  # fused K/V projection
+    "mka::decode_merge_kernel": ["decode.hip", "attn_split.h"],
+    "attn_decode_merge_kernel": ["attn.hip", "attn_split.h"],
+    "mka::EpiStore<unsigned short>": ["gemm.hip", "gemm.h"],  # Q projection (bf16 GEMM)
+    "mka::EpiKV<unsigned short>": ["gemm.hip", "gemm.h"],     # fused K/V projection
     "ema_pass1": ["ema.hip"],
     "ema_pass2": ["ema.hip"],
     "ema_pass3": ["ema.hip"],
@@ -671,6 +673,40 @@ def prefill_entry(s, pf, onbox):
     }
 
 
+def decode_entry(ds, dc, onbox):
+    """Figures of the timed decode workload: µs per token (cold: the copies in
+    turn; warm: one layer re-read), the step's HBM fraction and the decode
+    attention kernel's roofline."""
+    attn_bw = dc["kv_bytes"] / (dc["attn_us"] * 1e-6)
+    step_bw = dc["step_bytes"] / (dc["median_us"] * 1e-6)
+    return {
+        "workload": ds.name, "cached_tokens": dc["cached"], "steps": dc["steps"],
+        "copies": dc["copies"],
+        "copies_note": "the steps take the copies' layers (cache, weights, state) in turn, "
+                       "so each step reads them from HBM (about 0.9 GB between two reads of "
+                       "one copy, against a 256 MB last-level cache)",
+        "us_per_token_median": dc["median_us"], "us_per_token_mean": dc["mean_us"],
+        "us_per_token_wall": dc["wall_us"], "us_per_token_host_enqueue": dc["host_us"],
+        "step_bytes": dc["step_bytes"],
+        "step_hbm_frac": step_bw / PEAK_HBM_BYTES,
+        "warm": None if dc["warm"] is None else {
+            "us_per_token_median": dc["warm"]["median_us"],
+            "step_hbm_frac": dc["step_bytes"] / (dc["warm"]["median_us"] * 1e-6)
+            / PEAK_HBM_BYTES,
+            "attn_us_per_launch": dc["attn_warm_us"],
+            "attn_hbm_frac": dc["kv_bytes"] / (dc["attn_warm_us"] * 1e-6) / PEAK_HBM_BYTES,
+            "note": "one layer's cache and weights re-read every step (part of them stays "
+                    "in the last-level cache)"},
+        "roofline": {"kernel": "attn_decode", "bound": "hbm", "achieved": attn_bw / 1e9,
+                     "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                     "frac": attn_bw / PEAK_HBM_BYTES,
+                     "traffic": traffic_for("attn_decode_split_kernel", ds.name),
+                     "us_per_launch": dc["attn_us"],
+                     "onbox_peak": onbox["hbm_read_gbs"],
+                     "frac_onbox": attn_bw / 1e9 / onbox["hbm_read_gbs"]},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -687,6 +723,9 @@ def main():
     ap.add_argument("--decode-copies", type=int, default=3,
                     help="layers (cache, weights, state) taken in turn by the decode steps")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time the decode workload alone (for its counter passes); the line "
+                         "then carries no prefill figures")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain copy of MIB MiB (counter calibration)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -746,6 +785,12 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+    if args.decode_only:
+        ds = I.workload(args.decode_workload)
+        dc = bench_decode(ds, ds.decode_steps, 8, copies=max(1, args.decode_copies))
+        print(json.dumps({"metric": METRIC, "n_gpus": 1, "data": "synthetic",
+                          "decode": decode_entry(ds, dc, onbox_peaks())}), flush=True)
+        return
     s = I.workload(args.workload)
     extra = [w for w in args.extra_workloads.split(",") if w]
     variants = VARIANTS if args.variants else ()
@@ -807,34 +852,7 @@ def main():
         ds = I.workload(args.decode_workload)
         dc = bench_decode(ds, ds.decode_steps, 8, variants, args.full_mka,
                           copies=max(1, args.decode_copies))
-        attn_bw = dc["kv_bytes"] / (dc["attn_us"] * 1e-6)
-        step_bw = dc["step_bytes"] / (dc["median_us"] * 1e-6)
-        line["decode"] = {
-            "workload": ds.name, "cached_tokens": dc["cached"], "steps": dc["steps"],
-            "copies": dc["copies"],
-            "copies_note": "the steps take the copies' layers (cache, weights, state) in turn, "
-                           "so each step reads them from HBM (about 0.9 GB between two reads of "
-                           "one copy, against a 256 MB last-level cache)",
-            "us_per_token_median": dc["median_us"], "us_per_token_mean": dc["mean_us"],
-            "us_per_token_wall": dc["wall_us"], "us_per_token_host_enqueue": dc["host_us"],
-            "step_bytes": dc["step_bytes"],
-            "step_hbm_frac": step_bw / PEAK_HBM_BYTES,
-            "warm": None if dc["warm"] is None else {
-                "us_per_token_median": dc["warm"]["median_us"],
-                "step_hbm_frac": dc["step_bytes"] / (dc["warm"]["median_us"] * 1e-6)
-                / PEAK_HBM_BYTES,
-                "attn_us_per_launch": dc["attn_warm_us"],
-                "attn_hbm_frac": dc["kv_bytes"] / (dc["attn_warm_us"] * 1e-6) / PEAK_HBM_BYTES,
-                "note": "one layer's cache and weights re-read every step (part of them stays "
-                        "in the last-level cache)"},
-            "roofline": {"kernel": "attn_decode", "bound": "hbm", "achieved": attn_bw / 1e9,
-                         "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
-                         "frac": attn_bw / PEAK_HBM_BYTES,
-                         "traffic": traffic_for("attn_decode_split_kernel", ds.name),
-                         "us_per_launch": dc["attn_us"],
-                         "onbox_peak": onbox["hbm_read_gbs"],
-                         "frac_onbox": attn_bw / 1e9 / onbox["hbm_read_gbs"]},
-        }
+        line["decode"] = decode_entry(ds, dc, onbox)
     if variants and pf_aux is not None:
         line["variants"] = {
             k: {"workload": aux, "prefill_tokens_per_s": aux_tokens / (v * 1e-3), "prefill_ms": v,
