@@ -364,7 +364,7 @@ hipError_t attn_prefill<float>(const float* q, const float* k, const float* v, f
 }
 
 // ---------------------------------------------------------------------------
-// Decode, bf16: the split kernel (one chunk of keys per workgroup, see
+// Decode, bf16: the split kernel (one share of the rows per workgroup, see
 // attn_split.h) and the merge of its partials with the last cache row.
 // ---------------------------------------------------------------------------
 static int decode_units(int B, int H, int G) { return B * G * ((H / G + kSplitHeads - 1) / kSplitHeads); }
@@ -377,11 +377,11 @@ size_t attn_decode_ws_bytes(int B, int H, int G, int dh, int64_t n_rows) {
 template <int DH, bool PAGED>
 __global__ __launch_bounds__(256, 2) void attn_decode_split_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
-    int H, int G, KvLayout kv, int64_t n_rows, float sl2, int chunk, int n_chunks, int n_hb,
+    int H, int G, KvLayout kv, int64_t n_rows, float sl2, int n_chunks, int n_hb,
     float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ part_o) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[split_lds_bytes<DH>()];
   const int g = blockIdx.y / n_hb, hb = blockIdx.y % n_hb;
-  decode_split_chunk<DH, PAGED>(Q, Kc, Vc, H, G, kv, n_rows, sl2, chunk, n_chunks, blockIdx.x, g, hb,
+  decode_split_chunk<DH, PAGED>(Q, Kc, Vc, H, G, kv, n_rows, sl2, n_chunks, blockIdx.x, g, hb,
                          blockIdx.z, part_m, part_l, part_o, lds);
 }
 
@@ -412,7 +412,6 @@ hipError_t attn_decode_split_bf16(const bf16_t* q, const bf16_t* k, const bf16_t
                                   int G, int dh, const KvLayout& kv, int64_t n_old, void* ws,
                                   hipStream_t s) {
   if (n_old <= 0) return hipSuccess;
-  const int chunk = decode_chunk_keys(decode_units(B, H, G), n_old);
   const int n_chunks = decode_n_chunks(decode_units(B, H, G), n_old);
   if (n_chunks > kMaxDecodeChunks) return hipErrorInvalidValue;
   float* part_m = static_cast<float*>(ws);
@@ -422,8 +421,8 @@ hipError_t attn_decode_split_bf16(const bf16_t* q, const bf16_t* k, const bf16_t
   const int n_hb = (H / G + kSplitHeads - 1) / kSplitHeads;
   const dim3 grid(n_chunks, G * n_hb, B);
   auto launch = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, q, k, v, H, G, kv, n_old, sl2, chunk,
-                       n_chunks, n_hb, part_m, part_l, part_o);
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, q, k, v, H, G, kv, n_old, sl2, n_chunks,
+                       n_hb, part_m, part_l, part_o);
   };
   if (dh == 128)
     kv.paged() ? launch(attn_decode_split_kernel<128, true>)

@@ -3,13 +3,17 @@
 // section 4: online max-shift).  Shared by the standalone decode attention and
 // the fused decode-step kernel.
 //
-// A workgroup takes one chunk of keys of one (batch, KV group) for a block of
-// up to 16 query heads of that group; its 4 waves take the chunk's 32-key
-// tiles in turn (tile t to wave t % 4), each with its next tile's K and V
-// loads in flight while the current one is computed.  Chunks are sized so that
-// a launch has about one workgroup per CU (decode_chunk_keys): a CU streams
-// one chunk at the rate its memory pipeline allows, so a second chunk on any
-// CU would double the launch time.  Scores are S^T = K Q^T on MFMA 16x16x32 (keys
+// A workgroup takes one share ("chunk" c of n_chunks) of the rows of one
+// (batch, KV group) for a block of up to 16 query heads of that group: the
+// groups of four 32-key tiles c, c + n_chunks, c + 2 n_chunks, ..., one tile
+// of each group per wave, each wave with its next tile's K and V loads in
+// flight while the current one is computed.  Interleaving the shares keeps the
+// reads of all workgroups of a KV head inside one window of the cache at any
+// time, which DRAM serves faster than as many separate streams (contiguous
+// chunks took 8% longer on a cache read from HBM).  There are about as many
+// shares as CUs (decode_chunk_keys): a CU streams one share at the rate its
+// memory pipeline allows, so a second share on any CU would double the launch
+// time.  Scores are S^T = K Q^T on MFMA 16x16x32 (keys
 // as rows, the heads as the 16 columns).  The K rows of a tile are fed in the
 // order key(kb, i) = 8*(i/4) + 4*kb + i%4 for MFMA row i of sub-block kb, which
 // leaves lane l holding keys 8*(l/16) .. 8*(l/16)+7 of head l%16: exactly the
@@ -79,14 +83,14 @@ __device__ __forceinline__ void store_v_transposed(bf16_t* Vt, int pitch, int d0
 // V regions are private to their wave, so no workgroup barrier is needed.
 __device__ __forceinline__ void wave_lds_sync() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup"); }
 
-// Partials of chunk c (``chunk`` keys) for heads hb*16 .. of KV group g,
-// sequence b, over cache rows [c*chunk, min((c+1)*chunk, n_rows)).  Partial p
+// Partials of share c for heads hb*16 .. of KV group g, sequence b, over its
+// tiles of cache rows [0, n_rows) (tile groups c, c + n_chunks, ...).  Partial p
 // of query head h lives at (b*H + h) * n_chunks + c of part_m / part_l and
 // p*DH of part_o.  Uses 256 threads and split_lds_bytes<DH>() bytes of ``lds``.
 template <int DH, bool PAGED>
 __device__ __forceinline__ void decode_split_chunk(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc,
-    int H, int G, const KvLayout& kv, int64_t n_rows, float sl2, int chunk, int n_chunks, int c,
+    int H, int G, const KvLayout& kv, int64_t n_rows, float sl2, int n_chunks, int c,
     int g, int hb, int b, float* __restrict__ part_m, float* __restrict__ part_l,
     float* __restrict__ part_o, unsigned char* lds) {
   constexpr int BN = kSplitTile, VP = BN + 8, NKS = DH / 32, NDB = DH / 16, KQ = BN / 4;
@@ -108,11 +112,18 @@ __device__ __forceinline__ void decode_split_chunk(
       if (l16 >= nh) qf[ks] = bf16x8{};
     }
   }
-  const int64_t c0 = static_cast<int64_t>(c) * chunk;
-  const int rows_here = static_cast<int>(min<int64_t>(chunk, n_rows - c0));
-  const int n_tiles = (rows_here + BN - 1) / BN;
-  const int my_tiles = (n_tiles - wave + 3) / 4;  // tiles wave, wave + 4, ...
-
+  // Rows of the wave's tile t: workgroup c takes the groups of 4 tiles c,
+  // c + n_chunks, c + 2 n_chunks, ... (wave w the w-th tile of each), so the
+  // workgroups of a KV head stream one window of the cache at a time.
+  constexpr int SB = 4 * BN;
+  const int64_t first = static_cast<int64_t>(c) * SB + wave * BN;
+  const int my_tiles =
+      first < n_rows
+          ? static_cast<int>((n_rows - 1 - first) / (static_cast<int64_t>(n_chunks) * SB)) + 1
+          : 0;
+  const auto tile_row = [&](int t) -> int64_t {
+    return first + static_cast<int64_t>(t) * n_chunks * SB;
+  };
   float m_i = -INFINITY, l_i = 0.f;
   f32x4 acc[NDB];
 #pragma unroll
@@ -120,14 +131,30 @@ __device__ __forceinline__ void decode_split_chunk(
 
   const int krow = 8 * (l16 >> 2) + (l16 & 3);  // key of MFMA row l16 in sub-block 0
   u32x4 kbuf[2][2 * NKS], vbuf[2][VL * 4];
-  // A tile of BN keys (chunks start at multiples of BN) lies in one page; rows
-  // past the chunk's end read as zeros through the buffer range.
-  PageWindow<PAGED> pw;
-  pw.fill(kv, b, static_cast<int>(c0 >> kv.page_shift));
+  // Paged cache: a tile of BN rows (tiles start at multiples of BN) lies in
+  // one page (pages hold at least 64 rows); lane l of the wave holds the pool
+  // page of the wave's tile win + l.  Rows past n_rows read as zeros through
+  // the buffer range.
+  int win = -(1 << 30), win_page = 0;
+  const auto tile_base = [&](int t) -> int64_t {  // element offset of the tile's first row
+    const int64_t r0 = tile_row(t);
+    if constexpr (!PAGED) {
+      return kv.row_as<false>(b, g, r0);
+    } else {
+      if (t < win || t >= win + 64) {
+        win = t;
+        const int64_t rl = tile_row(min(t + lane, my_tiles - 1));
+        win_page = kv.pt[static_cast<int64_t>(b) * kv.pps + (rl >> kv.page_shift)];
+      }
+      const int64_t pool = __builtin_amdgcn_readlane(win_page, t - win);
+      const int64_t in_page = r0 & ((static_cast<int64_t>(1) << kv.page_shift) - 1);
+      return ((pool * kv.G + g) * (static_cast<int64_t>(1) << kv.page_shift) + in_page) * kv.DH;
+    }
+  };
   auto issue = [&](int tile, u32x4* kb_, u32x4* vb_) {
-    const int jr = (wave + 4 * tile) * BN;
-    const int64_t base = pw.row(kv, b, g, c0 + jr);
-    const uint32_t bytes = static_cast<uint32_t>(min(BN, rows_here - jr)) * DH * 2;
+    const int64_t r0 = tile_row(tile);
+    const int64_t base = tile_base(tile);
+    const uint32_t bytes = static_cast<uint32_t>(min<int64_t>(BN, n_rows - r0)) * DH * 2;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kc + base, bytes), vrs = make_rsrc(Vc + base, bytes);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -144,8 +171,8 @@ __device__ __forceinline__ void decode_split_chunk(
     }
   };
   auto compute = [&](int tile, const u32x4* kb_, const u32x4* vb_) {
-    const int jr = (wave + 4 * tile) * BN;  // first key of the tile, chunk-relative
-    const bool live = jr < rows_here;
+    const int64_t r0 = tile_row(tile);  // first key of the tile
+    const bool live = r0 < n_rows;
     if (live) {
 #pragma unroll
       for (int it = 0; it < VL; ++it) {
@@ -167,7 +194,7 @@ __device__ __forceinline__ void decode_split_chunk(
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if (jr + 8 * q4 + 4 * kb + r >= rows_here) s[kb][r] = -INFINITY;
+        if (r0 + 8 * q4 + 4 * kb + r >= n_rows) s[kb][r] = -INFINITY;
         mx = fmaxf(mx, s[kb][r]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));

@@ -59,7 +59,7 @@ struct DecodeArgs {
   float* part_m;   // split partials over rows [0, pos)
   float* part_l;
   float* part_o;
-  int chunk, n_chunks, n_hb;  // keys per split chunk, chunks, 16-head blocks per group
+  int n_chunks, n_hb;  // split shares of the cache rows, 16-head blocks per group
   T* o;            // [B, H, dh] attention output
   // routing variant: steps of disabled tiers are skipped, their inputs unread
   Routing rt;

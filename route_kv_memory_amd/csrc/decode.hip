@@ -642,11 +642,11 @@ __global__ __launch_bounds__(256, 2) void decode_attend_kernel(DecodeArgs<bf16_t
     return;
   }
   wg -= a.B;
-  // ---- attention over cache rows [0, pos): one chunk per workgroup.
+  // ---- attention over cache rows [0, pos): one share per workgroup.
   const int per_b = a.n_chunks * a.G * a.n_hb;
   const int b = wg / per_b, rest = wg % per_b;
   const int c = rest % a.n_chunks, ghb = rest / a.n_chunks;
-  decode_split_chunk<DH, PAGED>(a.q, a.k_cache, a.v_cache, a.H, a.G, a.kv, a.pos, a.sl2, a.chunk,
+  decode_split_chunk<DH, PAGED>(a.q, a.k_cache, a.v_cache, a.H, a.G, a.kv, a.pos, a.sl2,
                          a.n_chunks, c, ghb / a.n_hb, ghb % a.n_hb, b, a.part_m, a.part_l,
                          a.part_o, lds);
 }

@@ -1126,7 +1126,6 @@ int mka_decode_step(const mka_dims* d, const void* x, int64_t pos, const mka_wei
     a.kv = layout_of(d, st);
     a.sl2 = 1.4426950408889634f / sqrtf(static_cast<float>(dh));
     a.n_hb = (H / G + kSplitHeads - 1) / kSplitHeads;
-    a.chunk = decode_chunk_keys(B * G * a.n_hb, pos);
     a.n_chunks = pos > 0 ? decode_n_chunks(B * G * a.n_hb, pos) : 0;
     const size_t np = static_cast<size_t>(B) * H * a.n_chunks;
     a.part_m = w_attn;
