@@ -420,45 +420,61 @@ def bench_decode(s, steps, warmup, variants=(), full=False, page_size=None, copi
     stream = torch.cuda.current_stream()
 
     def run(fn=None, n_copies=copies):
-        # step k runs on copy k % n_copies at that copy's next position
+        """Two timed passes over the steps: one bracketed by two events alone
+        (the throughput: recording an event between steps costs the GPU about
+        2 us per step), then one with an event after every step (the per-step
+        distribution).  Step k runs on copy k % n_copies at that copy's next
+        position."""
         fns = [fn] if fn is not None else [lay.decode_step for lay in layers[:n_copies]]
-        reset()
-        for k in range(warmup):
-            fns[k % n_copies](tokens[k], T0 + k // n_copies, out=outs[k % n_copies])
-        reset()
-        torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-        t0 = time.perf_counter()
-        ev[0].record(stream)
-        for k in range(steps):
-            fns[k % n_copies](tokens[k], T0 + k // n_copies, out=outs[k % n_copies])
-            ev[k + 1].record(stream)
-        host_us = (time.perf_counter() - t0) / steps * 1e6  # enqueue cost per step
-        torch.cuda.synchronize()
-        wall_us = (time.perf_counter() - t0) / steps * 1e6
-        return np.array([ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(steps)]), host_us, wall_us
+
+        def steps_from_reset(evs=None):
+            reset()
+            for k in range(warmup):
+                fns[k % n_copies](tokens[k], T0 + k // n_copies, out=outs[k % n_copies])
+            reset()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            e0.record(stream)
+            for k in range(steps):
+                fns[k % n_copies](tokens[k], T0 + k // n_copies, out=outs[k % n_copies])
+                if evs is not None:
+                    evs[k].record(stream)
+            e1.record(stream)
+            host = (time.perf_counter() - t0) / steps * 1e6  # enqueue cost per step
+            torch.cuda.synchronize()
+            wall = (time.perf_counter() - t0) / steps * 1e6
+            return e0, e1, host, wall
+
+        e0, e1, host_us, wall_us = steps_from_reset()
+        mean_us = e0.elapsed_time(e1) * 1e3 / steps
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        f0, _, _, _ = steps_from_reset(ev)
+        per_step = np.array([(f0 if k == 0 else ev[k - 1]).elapsed_time(ev[k]) * 1e3
+                             for k in range(steps)])
+        return mean_us, per_step, host_us, wall_us
 
     # Routing variants first (the same cache and state, the layer's shape
     # swapped); the main measurement runs last, from a reset state.
     var_us = {}
     for mode, tiers in variants:
         layer.shape = s.replace(route_mode=mode, tiers=tiers)
-        var_us[f"{mode}/{tiers}"] = float(np.median(run(n_copies=1)[0]))
+        var_us[f"{mode}/{tiers}"] = run(n_copies=1)[0]
         log(f"decode variant {mode}/{tiers}: {var_us[f'{mode}/{tiers}']:.1f} us/token")
     layer.shape = s
     full_us = None
     if full:
-        f_us, f_host, _ = run(layer.full_decode_step, n_copies=1)
-        full_us = {"median_us": float(np.median(f_us)), "host_us": f_host}
-        log(f"decode full MKA: {full_us['median_us']:.1f} us/token")
-    step_us, host_us, wall_us = run()
+        f_us, _, f_host, _ = run(layer.full_decode_step, n_copies=1)
+        full_us = {"us": f_us, "host_us": f_host}
+        log(f"decode full MKA: {full_us['us']:.1f} us/token")
+    mean_us, step_us, host_us, wall_us = run()
     warm = None
     if copies > 1:  # one layer re-read every step (its cache partly stays in the LLC)
-        w_us, w_host, _ = run(n_copies=1)
-        warm = {"median_us": float(np.median(w_us)), "host_us": w_host}
+        w_us, w_steps, w_host, _ = run(n_copies=1)
+        warm = {"us": w_us, "median_us": float(np.median(w_steps)), "host_us": w_host}
 
     if page_size:  # the single-call attention entry takes contiguous caches
-        return dict(median_us=float(np.median(step_us)), host_us=host_us, cached=T0,
+        return dict(us=mean_us, median_us=float(np.median(step_us)), host_us=host_us, cached=T0,
                     steps=steps)
     # Decode attention alone at the first step's length, for its roofline:
     # the copies' caches in turn (cold), and one cache re-read (warm).
@@ -493,7 +509,7 @@ def bench_decode(s, steps, warmup, variants=(), full=False, page_size=None, copi
     step_bytes = (kv_bytes + (s.q_width * s.d_model + 2 * s.kv_width * s.d_model
                               + s.router_hidden * s.q_width + 3 * s.router_hidden) * el
                   + s.hash_bits * s.d_model * 4 + B * (s.top_r * s.d_model * 4 + nb0 * 8))
-    return dict(median_us=float(np.median(step_us)), mean_us=float(step_us.mean()),
+    return dict(us=mean_us, median_us=float(np.median(step_us)), mean_us=float(step_us.mean()),
                 wall_us=wall_us, host_us=host_us, attn_us=attn_us, attn_warm_us=attn_warm_us,
                 kv_bytes=kv_bytes, step_bytes=step_bytes, cached=T0, steps=steps,
                 variants_us=var_us, full=full_us, warm=warm, copies=copies)
@@ -678,21 +694,25 @@ def decode_entry(ds, dc, onbox):
     turn; warm: one layer re-read), the step's HBM fraction and the decode
     attention kernel's roofline."""
     attn_bw = dc["kv_bytes"] / (dc["attn_us"] * 1e-6)
-    step_bw = dc["step_bytes"] / (dc["median_us"] * 1e-6)
+    step_bw = dc["step_bytes"] / (dc["us"] * 1e-6)
     return {
         "workload": ds.name, "cached_tokens": dc["cached"], "steps": dc["steps"],
         "copies": dc["copies"],
         "copies_note": "the steps take the copies' layers (cache, weights, state) in turn, "
                        "so each step reads them from HBM (about 0.9 GB between two reads of "
                        "one copy, against a 256 MB last-level cache)",
+        "us_per_token": dc["us"],
+        "us_per_token_note": "GPU time of the steps between two events, over the steps; the "
+                             "per-step figures come from a second pass with an event after "
+                             "every step (each costs about 2 us)",
         "us_per_token_median": dc["median_us"], "us_per_token_mean": dc["mean_us"],
         "us_per_token_wall": dc["wall_us"], "us_per_token_host_enqueue": dc["host_us"],
         "step_bytes": dc["step_bytes"],
         "step_hbm_frac": step_bw / PEAK_HBM_BYTES,
         "warm": None if dc["warm"] is None else {
+            "us_per_token": dc["warm"]["us"],
             "us_per_token_median": dc["warm"]["median_us"],
-            "step_hbm_frac": dc["step_bytes"] / (dc["warm"]["median_us"] * 1e-6)
-            / PEAK_HBM_BYTES,
+            "step_hbm_frac": dc["step_bytes"] / (dc["warm"]["us"] * 1e-6) / PEAK_HBM_BYTES,
             "attn_us_per_launch": dc["attn_warm_us"],
             "attn_hbm_frac": dc["kv_bytes"] / (dc["attn_warm_us"] * 1e-6) / PEAK_HBM_BYTES,
             "note": "one layer's cache and weights re-read every step (part of them stays "
@@ -886,19 +906,19 @@ def main():
         if not args.no_decode:
             ds = I.workload(args.decode_workload)
             pdc = bench_decode(ds, ds.decode_steps, 8, page_size=args.paged)
-            log(f"paged decode: {pdc['median_us']:.1f} us/token")
-            line["paged"].update(decode_us_per_token=pdc["median_us"],
+            log(f"paged decode: {pdc['us']:.1f} us/token")
+            line["paged"].update(decode_us_per_token=pdc["us"],
                                  decode_host_us_per_token=pdc["host_us"],
                                  decode_note="one layer re-read every step (compare decode.warm)")
     if args.decode_batch:
         bs = I.workload("qwen7b_decode_32k_b4")
         bdc = bench_decode(bs, bs.decode_steps, 8)
-        log(f"batched decode B={bs.batch}: {bdc['median_us']:.1f} us/step")
+        log(f"batched decode B={bs.batch}: {bdc['us']:.1f} us/step")
         line["decode_batch"] = {
             "workload": bs.name, "batch": bs.batch, "cached_tokens": bdc["cached"],
-            "us_per_step_median": bdc["median_us"],
-            "tokens_per_s": bs.batch / (bdc["median_us"] * 1e-6),
-            "step_hbm_frac": bdc["step_bytes"] / (bdc["median_us"] * 1e-6) / PEAK_HBM_BYTES,
+            "us_per_step": bdc["us"], "us_per_step_median": bdc["median_us"],
+            "tokens_per_s": bs.batch / (bdc["us"] * 1e-6),
+            "step_hbm_frac": bdc["step_bytes"] / (bdc["us"] * 1e-6) / PEAK_HBM_BYTES,
             "attn_us_per_launch": bdc["attn_us"],
             "attn_hbm_frac": bdc["kv_bytes"] / (bdc["attn_us"] * 1e-6) / PEAK_HBM_BYTES,
             "note": "one layer re-read every step (its 4 x 32K cache is 269 MB)"}
@@ -907,7 +927,7 @@ def main():
             "workload": aux,
             "prefill_ms": pf_aux["full_ms"],
             "prefill_tokens_per_s": aux_tokens / (pf_aux["full_ms"] * 1e-3),
-            "decode_us_per_token": dc["full"]["median_us"] if dc else None,
+            "decode_us_per_token": dc["full"]["us"] if dc else None,
             "decode_host_us_per_token": dc["full"]["host_us"] if dc else None,
             "note": "three attention paths (one K/V cache per tier) mixed by lambda; same "
                     "inputs as the FastMKA figures of this line; decode on one layer re-read"}
