@@ -6,17 +6,18 @@
 // A workgroup takes one share ("chunk" c of n_chunks) of the rows of one
 // (batch, KV group) for a block of up to 16 query heads of that group: the
 // groups of four 32-key tiles c, c + n_chunks, c + 2 n_chunks, ..., one tile
-// of each group per wave, each wave with its next tile's K and V loads in
-// flight while the current one is computed.  Interleaving the shares keeps the
-// reads of all workgroups of a KV head inside one window of the cache at any
-// time, which DRAM serves faster than as many separate streams (contiguous
-// chunks took 8% longer on a cache read from HBM).  There are about as many
-// shares as CUs (decode_chunk_keys): a CU streams one share at the rate its
-// memory pipeline allows, so a second share on any CU would double the launch
-// time.  Scores are S^T = K Q^T on MFMA 16x16x32 (keys
-// as rows, the heads as the 16 columns).  The K rows of a tile are fed in the
-// order key(kb, i) = 8*(i/4) + 4*kb + i%4 for MFMA row i of sub-block kb, which
-// leaves lane l holding keys 8*(l/16) .. 8*(l/16)+7 of head l%16: exactly the
+// of each group per wave, each wave with the K and V loads of its next two
+// tiles in flight while the probabilities and P V products of the current
+// one are computed.  Interleaving the shares keeps the reads of all
+// workgroups of a KV head inside one window of the cache at any time, which
+// DRAM serves faster than as many separate streams (contiguous chunks took 8%
+// longer on a cache read from HBM).  There are about as many shares as CUs
+// (decode_chunk_keys): a CU streams one share at the rate its memory pipeline
+// allows, so a second share on any CU would double the launch time.  Scores
+// are S^T = K Q^T on MFMA 16x16x32 (keys as rows, the heads as the 16
+// columns).  The K rows of a tile are fed in the order key(kb, i) =
+// 8*(i/4) + 4*kb + i%4 for MFMA row i of sub-block kb, which leaves lane l
+// holding keys 8*(l/16) .. 8*(l/16)+7 of head l%16: exactly the
 // B operand of O^T = V^T P^T, so the probabilities go to the second product
 // without data movement.  V is transposed through a per-wave LDS region.
 // The 4 waves merge in LDS into one partial (max, sum, unnormalised output)
@@ -170,17 +171,17 @@ __device__ __forceinline__ void decode_split_chunk(
         vb_[it * 4 + r] = buffer_load16(vrs, static_cast<uint32_t>((4 * kq + r) * DH + 8 * dc) * 2);
     }
   };
-  auto compute = [&](int tile, const u32x4* kb_, const u32x4* vb_) {
-    const int64_t r0 = tile_row(tile);  // first key of the tile
-    const bool live = r0 < n_rows;
-    if (live) {
+  // A tile in two parts: scores() takes the tile's registers (V to the LDS,
+  // K into the score products), so the loads of the wave's tile after next
+  // go out before accumulate() forms the probabilities and the P V products.
+  auto scores = [&](int tile, const u32x4* kb_, const u32x4* vb_, f32x4 (&s)[2]) {
+    if (tile_row(tile) < n_rows) {
 #pragma unroll
       for (int it = 0; it < VL; ++it) {
         const int item = lane + 64 * it, kq = item % KQ, dc = item / KQ;
         store_v_transposed(Vt, VP, 8 * dc, 4 * kq, vb_ + it * 4);
       }
     }
-    f32x4 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x4{};
@@ -188,6 +189,10 @@ __device__ __forceinline__ void decode_split_chunk(
       for (int ks = 0; ks < NKS; ++ks)
         s[kb] = mfma16x16x32(__builtin_bit_cast(bf16x8, kb_[kb * NKS + ks]), qf[ks], s[kb]);
     }
+  };
+  auto accumulate = [&](int tile, f32x4 (&s)[2]) {
+    const int64_t r0 = tile_row(tile);  // first key of the tile
+    const bool live = r0 < n_rows;
     wave_lds_sync();  // V tile stores before the wave's reads of them
     float mx = -INFINITY;
 #pragma unroll
@@ -224,11 +229,17 @@ __device__ __forceinline__ void decode_split_chunk(
     wave_lds_sync();  // the reads of this tile before the next tile's stores
   };
   if (my_tiles > 0) issue(0, kbuf[0], vbuf[0]);
+  if (my_tiles > 1) issue(1, kbuf[1], vbuf[1]);
   for (int tile = 0; tile < my_tiles; tile += 2) {
-    if (tile + 1 < my_tiles) issue(tile + 1, kbuf[1], vbuf[1]);
-    compute(tile, kbuf[0], vbuf[0]);
+    f32x4 s[2];
+    scores(tile, kbuf[0], vbuf[0], s);
     if (tile + 2 < my_tiles) issue(tile + 2, kbuf[0], vbuf[0]);
-    if (tile + 1 < my_tiles) compute(tile + 1, kbuf[1], vbuf[1]);
+    accumulate(tile, s);
+    if (tile + 1 < my_tiles) {
+      scores(tile + 1, kbuf[1], vbuf[1], s);
+      if (tile + 3 < my_tiles) issue(tile + 3, kbuf[1], vbuf[1]);
+      accumulate(tile + 1, s);
+    }
   }
 
   // Merge the 4 waves (the V regions are reused for the exchange).
@@ -311,12 +322,18 @@ __device__ __forceinline__ void decode_merge_head(const float* __restrict__ part
     const int c = grp + GR * i;
     po[i] = c < n_chunks ? part_o[(p0 + c) * DH + d] : 0.f;
   }
+  float qv[DH / 64];  // the query, loaded with the partials
+  {
+    const bf16_t* qh = Q + (static_cast<int64_t>(b) * H + h) * DH;
+#pragma unroll
+    for (int i = 0; i < DH / 64; ++i) qv[i] = tid < 64 ? bf16_to_f32(qh[lane + 64 * i]) : 0.f;
+  }
   const bool has_extra = extra(sm.kx, sm.vx);
   __syncthreads();
   if (has_extra && tid < 64) {  // score of the extra row, scaled like the partials
-    const bf16_t* qh = Q + (static_cast<int64_t>(b) * H + h) * DH;
     float dot = 0.f;
-    for (int e = lane; e < DH; e += 64) dot = fmaf(bf16_to_f32(qh[e]), sm.kx[e], dot);
+#pragma unroll
+    for (int i = 0; i < DH / 64; ++i) dot = fmaf(qv[i], sm.kx[lane + 64 * i], dot);
     dot = wave_sum(dot);
     if (lane == 0) sm.sx = dot * sl2;
   }
