@@ -10,9 +10,10 @@
 // channels (8 in pass 1), a workgroup 512 (1024) channels of one 64-token chunk.
 //   pass 1  each chunk's local result from a zero start: the EMA end value and
 //           the block-sum tail (sum since the chunk's last block end);
-//   pass 2  per channel, a sequential scan over chunks turns those into the
-//           carry entering every chunk (EMA: s <- beta^L s + a; block sum:
-//           restart at a chunk that contains a block end);
+//   pass 2  per channel, a scan over chunks (two levels: segments of
+//           chunks, then the segments) turns those into the carry entering
+//           every chunk (EMA: s <- beta^L s + a; block sum: restart at a
+//           chunk that contains a block end);
 //   pass 3  each chunk rescans from its carry, writes L2, writes the mean of
 //           every block that ends inside it, and the last chunk writes the
 //           outgoing EMA state and partial block sum.
@@ -85,48 +86,90 @@ __global__ __launch_bounds__(kEmaThreads) void ema_pass1(const T* __restrict__ x
   }
 }
 
-// One thread per (batch, channel): exclusive scan of the chunk results, in place.
-__global__ __launch_bounds__(64) void ema_pass2(float* __restrict__ agg_s, float* __restrict__ agg_a,
-                                                 const float* __restrict__ state_in,
-                                                 const float* __restrict__ acc_in, int B, int D,
-                                                 int seq, int64_t pos0, int pos_rem, int block,
-                                                 float beta_L, int n_chunks) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= B * D) return;
-  const int b = e / D, ch = e - b * D;
-  // An empty prefix (pos0 == 0) and an empty partial block (pos0 at a block
-  // start) contribute zero whatever the buffers hold.
-  float cs = pos0 == 0 ? 0.f : state_in[e], ca = pos0 % block == 0 ? 0.f : acc_in[e];
+// Exclusive scan of the chunk results, in place, per (batch, channel), in
+// two levels: the chunks of a channel split into kEmaSegs segments of
+// seg_len chunks; a workgroup holds 16 channels x kEmaSegs segments (lane ->
+// channel, so a wave's loads of one chunk are 64 contiguous bytes).  Each
+// thread folds its segment from a zero carry (EMA: s <- beta^L s + a; block
+// sum: restart at a chunk that contains a block end), one thread per channel
+// chains the segments' results, and each thread rewalks its segment from its
+// carry, writing the carry entering every chunk.  The sequential depth is
+// 2 seg_len + kEmaSegs chunk steps instead of n_chunks.
+constexpr int kEmaSegs = 16;
+
+__global__ __launch_bounds__(16 * kEmaSegs) void ema_pass2(float* __restrict__ agg_s,
+                                                        float* __restrict__ agg_a,
+                                                        const float* __restrict__ state_in,
+                                                        const float* __restrict__ acc_in, int B,
+                                                        int D, int seq, int64_t pos0, int block,
+                                                        float beta_L, int n_chunks, int seg_len) {
+  __shared__ float seg_s[kEmaSegs][16], seg_a[kEmaSegs][16], carry_s[kEmaSegs][16],
+      carry_a[kEmaSegs][16];
+  __shared__ int seg_c[kEmaSegs][16];
+  const int chl = threadIdx.x & 15, seg = threadIdx.x >> 4;
+  const int e = blockIdx.x * 16 + chl;
+  const bool on = e < B * D;
+  const int b = on ? e / D : 0, ch = on ? e - b * D : 0;
   float* ps = agg_s + static_cast<int64_t>(b) * n_chunks * D + ch;
   float* pa = agg_a + static_cast<int64_t>(b) * n_chunks * D + ch;
-  // position of the next token within its block, kept without divisions
-  int rem = pos_rem;
+  const int c_begin = min(seg * seg_len, n_chunks), c_end = min(c_begin + seg_len, n_chunks);
   const int step = kEmaChunk % block;
-  // chunk results are loaded kEmaBatch at a time before the sequential carry
-  for (int c0 = 0; c0 < n_chunks; c0 += kEmaBatch) {
-    float sc[kEmaBatch], ac[kEmaBatch];
+  const int rem0 = static_cast<int>((pos0 + static_cast<int64_t>(c_begin) * kEmaChunk) % block);
+  // the segment's chunks, kEmaBatch results loaded before their sequential use
+  auto walk = [&](float cs, float ca, bool write, bool& closed) {
+    int rem = rem0;
+    closed = false;
+    for (int c0 = c_begin; c0 < c_end; c0 += kEmaBatch) {
+      float sc[kEmaBatch], ac[kEmaBatch];
 #pragma unroll
-    for (int u = 0; u < kEmaBatch; ++u) {
-      const int64_t o = static_cast<int64_t>(min(c0 + u, n_chunks - 1)) * D;
-      sc[u] = ps[o];
-      ac[u] = pa[o];
-    }
+      for (int u = 0; u < kEmaBatch; ++u) {
+        const int64_t o = static_cast<int64_t>(min(c0 + u, c_end - 1)) * D;
+        sc[u] = on ? ps[o] : 0.f;
+        ac[u] = on ? pa[o] : 0.f;
+      }
 #pragma unroll
-    for (int u = 0; u < kEmaBatch; ++u) {
-      const int c = c0 + u;
-      if (c < n_chunks) {
-        const int64_t o = static_cast<int64_t>(c) * D;
-        ps[o] = cs;
-        pa[o] = ca;
-        const int len = min((c + 1) * kEmaChunk, seq) - c * kEmaChunk;
-        const bool closes = rem + len >= block;  // a block ends inside this chunk
-        cs = fmaf(beta_L, cs, sc[u]);
-        ca = closes ? ac[u] : ca + ac[u];
-        rem += step;
-        if (rem >= block) rem -= block;
+      for (int u = 0; u < kEmaBatch; ++u) {
+        const int c = c0 + u;
+        if (c < c_end) {
+          if (write && on) {
+            const int64_t o = static_cast<int64_t>(c) * D;
+            ps[o] = cs;
+            pa[o] = ca;
+          }
+          const int len = min((c + 1) * kEmaChunk, seq) - c * kEmaChunk;
+          const bool closes = rem + len >= block;  // a block ends inside this chunk
+          closed |= closes;
+          cs = fmaf(beta_L, cs, sc[u]);
+          ca = closes ? ac[u] : ca + ac[u];
+          rem += step;
+          if (rem >= block) rem -= block;
+        }
       }
     }
+    return make_float2(cs, ca);
+  };
+  bool closed;
+  const float2 loc = walk(0.f, 0.f, false, closed);
+  seg_s[seg][chl] = loc.x;
+  seg_a[seg][chl] = loc.y;
+  seg_c[seg][chl] = closed;
+  __syncthreads();
+  if (seg == 0) {
+    // An empty prefix (pos0 == 0) and an empty partial block (pos0 at a block
+    // start) contribute zero whatever the buffers hold.
+    float cs = pos0 == 0 || !on ? 0.f : state_in[e];
+    float ca = pos0 % block == 0 || !on ? 0.f : acc_in[e];
+    float pw = 1.f;  // beta^L over a whole segment (only whole segments feed later ones)
+    for (int i = 0; i < seg_len; ++i) pw *= beta_L;
+    for (int g = 0; g < kEmaSegs; ++g) {
+      carry_s[g][chl] = cs;
+      carry_a[g][chl] = ca;
+      cs = fmaf(pw, cs, seg_s[g][chl]);
+      ca = seg_c[g][chl] ? seg_a[g][chl] : ca + seg_a[g][chl];
+    }
   }
+  __syncthreads();
+  walk(carry_s[seg][chl], carry_a[seg][chl], true, closed);
 }
 
 template <typename T>
@@ -276,9 +319,10 @@ hipError_t ema_scan(const T* x, int B, int seq, int D, int64_t pos0, int block, 
   double bl = 1.0;
   for (int i = 0; i < kEmaChunk; ++i) bl *= static_cast<double>(beta);
   // one channel per thread, 64-thread workgroups: the scan is spread over many CUs
-  hipLaunchKernelGGL(ema_pass2, dim3((B * D + 63) / 64), dim3(64), 0, s, agg_s, agg_a, state_io,
-                     acc_io, B, D, seq, pos0, static_cast<int>(pos0 % block), block,
-                     static_cast<float>(bl), n_chunks);
+  const int seg_len = (n_chunks + kEmaSegs - 1) / kEmaSegs;
+  hipLaunchKernelGGL(ema_pass2, dim3((B * D + 15) / 16), dim3(16 * kEmaSegs), 0, s, agg_s, agg_a,
+                     state_io, acc_io, B, D, seq, pos0, block, static_cast<float>(bl), n_chunks,
+                     seg_len);
   hipLaunchKernelGGL(ema_pass3<T>, grid, dim3(kEmaThreads), 0, s, x, seq, D, pos0, block, beta, omb,
                      agg_s, agg_a, n_chunks, l2, means, nb_cap, state_io, acc_io, n_chunks);
   return hipGetLastError();

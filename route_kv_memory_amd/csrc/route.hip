@@ -8,71 +8,107 @@
 namespace mka {
 
 // ---------------------------------------------------------------------------
-// MFMA router (bf16): a workgroup takes 32 tokens; its NW waves (8 when the
-// q width splits into slices of whole 16-wide k-steps, else 4) split the
-// q-width reduction, each producing a 32 x r block of hidden pre-activations
-// with MFMA 32x32x16 (operands read straight from global: the token's q row
-// and the weight row are both contiguous along the reduction).  The slices
-// are summed in LDS, GELU applied, then the r -> 3 layer and the softmax run
-// one thread per token.
+// MFMA router (bf16).  A workgroup of 4 waves takes TOK = 128 / NB tokens
+// (NB = r / 32 blocks of 32 hidden units) and the whole q-width reduction:
+// wave w computes the 32 x 32 block (tokens 32 (w / NB) .., hidden units
+// 32 (w % NB) ..) with MFMA 32x32x16.  The q rows and W_r1 pass through LDS
+// in chunks of 64 channels (128 bytes per row), three chunks in flight, each
+// 16-byte piece loaded global -> LDS directly by the lane whose LDS slot it
+// fills: a load instruction covers 8 whole 128-byte row segments, so every
+// byte of a fetched line is used (a lane-per-token layout read 32 partial
+// lines per instruction).  LDS rows are unpadded with 16-byte chunk c of row
+// i at slot c ^ ((i / 2) % 8), so the 16 lanes of an operand read (16 rows,
+// one chunk) fall in 16 distinct bank groups.  Then GELU, the r -> 3 layer
+// and the routing variant, one thread per token.
 // ---------------------------------------------------------------------------
-template <int NB, int NW>  // NB = r / 32 output blocks
-__global__ __launch_bounds__(NW * 64) void router_mfma_kernel(const bf16_t* __restrict__ Q, int M, int qw,
+constexpr int kRouterKC = 64;      // channels per chunk
+constexpr int kRouterStages = 4;  // chunks in flight: kRouterStages - 1
+
+__device__ __forceinline__ int router_slot(int row, int c) { return c ^ ((row >> 1) & 7); }
+
+template <int NB>
+__global__ __launch_bounds__(256, 2) void router_mfma_kernel(const bf16_t* __restrict__ Q, int M, int qw,
                                                           const bf16_t* __restrict__ W1,
                                                           const bf16_t* __restrict__ W2,
                                                           float* __restrict__ lam, Routing rt) {
-  constexpr int R = NB * 32;
-  __shared__ float part[NW][32][R + 1];
+  constexpr int R = NB * 32, TOK = 128 / NB;
+  constexpr int A_BYTES = TOK * kRouterKC * 2, W_BYTES = R * kRouterKC * 2;
+  constexpr int STAGE = A_BYTES + W_BYTES;
+  constexpr int A_LD = A_BYTES / 1024 / 4, W_LD = W_BYTES / 1024 / 4;  // 1 KB loads per wave
+  static_assert(A_LD >= 1 && W_LD >= 1 && (A_LD + W_LD) * 4096 == STAGE, "loads split over 4 waves");
+  static_assert(TOK * (R + 1) * 4 <= kRouterStages * STAGE, "the hidden block fits the stages");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kRouterStages * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
-  const int row0 = blockIdx.x * 32;
-  const int row = row0 + l32;
-  const int slice = qw / NW;
-  const int k_begin = wave * slice;
+  const int row0 = blockIdx.x * TOK;
+  const int rb = wave / NB, jb = wave % NB;
 
-  f32x16 acc[NB];
+  // Source of this lane's 16 bytes in load i of a chunk: LDS row 8 i' + lane / 8
+  // (i' counts the 1 KB loads of the operand), slot lane % 8.
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(
+      Q + static_cast<int64_t>(row0) * qw,
+      static_cast<uint32_t>(static_cast<int64_t>(max(0, min(TOK, M - row0))) * qw * 2));
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(W1, static_cast<uint32_t>(R * qw * 2));
+  uint32_t a_src[A_LD], w_src[W_LD];
 #pragma unroll
-  for (int j = 0; j < NB; ++j) acc[j] = f32x16{};
-  const bf16_t* qrow = Q + static_cast<int64_t>(row < M ? row : 0) * qw + 8 * h;
-  // U k-steps' loads are issued before their products; steps past the
-  // slice re-read its last step (inside the row) and enter as zeros.
-  constexpr int U = 32 / NW;
-  const int k_end = k_begin + slice;
-  for (int k = k_begin; k < k_end; k += 16 * U) {
-    bf16x8 a[U], b[U][NB];
+  for (int i = 0; i < A_LD; ++i) {
+    const int row = 8 * (wave * A_LD + i) + (lane >> 3), slot = lane & 7;
+    a_src[i] = static_cast<uint32_t>(row * qw + 8 * router_slot(row, slot)) * 2;
+  }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kk = min(k + 16 * u, k_end - 16);
-      a[u] = *reinterpret_cast<const bf16x8*>(qrow + kk);
-      if (row >= M || k + 16 * u >= k_end) a[u] = bf16x8{};
+  for (int i = 0; i < W_LD; ++i) {
+    const int row = 8 * (wave * W_LD + i) + (lane >> 3), slot = lane & 7;
+    w_src[i] = static_cast<uint32_t>(row * qw + 8 * router_slot(row, slot)) * 2;
+  }
+  auto issue = [&](int chunk) {
+    unsigned char* st = smem + (chunk % kRouterStages) * STAGE;
+    const uint32_t k0 = static_cast<uint32_t>(chunk * kRouterKC) * 2;
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
-        b[u][j] = *reinterpret_cast<const bf16x8*>(W1 + static_cast<int64_t>(j * 32 + l32) * qw +
-                                                   kk + 8 * h);
+    for (int i = 0; i < A_LD; ++i)
+      buffer_load_lds16(qrs, (lds_void_t*)(st + (wave * A_LD + i) * 1024), a_src[i] + k0);
+#pragma unroll
+    for (int i = 0; i < W_LD; ++i)
+      buffer_load_lds16(wrs, (lds_void_t*)(st + A_BYTES + (wave * W_LD + i) * 1024), w_src[i] + k0);
+  };
+
+  f32x16 acc = f32x16{};
+  const int n_chunks = qw / kRouterKC;
+  const int arow = 32 * rb + l32, wrow = 32 * jb + l32;
+  constexpr int AHEAD = kRouterStages - 1;
+#pragma unroll
+  for (int c = 0; c < AHEAD; ++c)
+    if (c < n_chunks) issue(c);
+  for (int c = 0; c < n_chunks; ++c) {
+    // chunk c has landed once at most the later chunks' loads are pending
+    const int later = min(AHEAD - 1, n_chunks - 1 - c);
+    if (later >= 2)
+      __builtin_amdgcn_s_waitcnt(kVmcntPending<2 * (A_LD + W_LD)>());
+    else if (later == 1)
+      __builtin_amdgcn_s_waitcnt(kVmcntPending<A_LD + W_LD>());
+    else
+      __builtin_amdgcn_s_waitcnt(kVmcntPending<0>());
+    __syncthreads();  // every wave's pieces of chunk c are in; chunk c - 1's reads are done
+    if (c + AHEAD < n_chunks) issue(c + AHEAD);
+    const unsigned char* st = smem + (c % kRouterStages) * STAGE;
+    const bf16_t* As = reinterpret_cast<const bf16_t*>(st) + arow * kRouterKC;
+    const bf16_t* Ws = reinterpret_cast<const bf16_t*>(st + A_BYTES) + wrow * kRouterKC;
+#pragma unroll
+    for (int ks = 0; ks < kRouterKC / 16; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(As + 8 * router_slot(arow, 2 * ks + h));
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(Ws + 8 * router_slot(wrow, 2 * ks + h));
+      acc = mfma32x32x16(a, b, acc);
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int j = 0; j < NB; ++j) acc[j] = mfma32x32x16(a[u], b[u][j], acc[j]);
   }
+  __syncthreads();  // the stages become the hidden block
+  float(*hid)[R + 1] = reinterpret_cast<float(*)[R + 1]>(smem);
 #pragma unroll
-  for (int j = 0; j < NB; ++j)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) part[wave][acc_row(r, h)][j * 32 + l32] = acc[j][r];
+  for (int r = 0; r < 16; ++r) hid[32 * rb + acc_row(r, h)][32 * jb + l32] = gelu(acc[r]);
   __syncthreads();
-  for (int e = tid; e < 32 * R; e += NW * 64) {
-    const int rr = e / R, n = e % R;
-    float z = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) z += part[w][rr][n];
-    part[0][rr][n] = gelu(z);
-  }
-  __syncthreads();
-  if (tid < 32 && row0 + tid < M) {
+  if (tid < TOK && row0 + tid < M) {
     float z[3];
 #pragma unroll
     for (int c = 0; c < 3; ++c) {
       float sum = 0.f;
-      for (int n = 0; n < R; ++n) sum = fmaf(part[0][tid][n], bf16_to_f32(W2[c * R + n]), sum);
+      for (int n = 0; n < R; ++n) sum = fmaf(hid[tid][n], bf16_to_f32(W2[c * R + n]), sum);
       z[c] = sum;
     }
     float out[3];
@@ -86,15 +122,13 @@ __global__ __launch_bounds__(NW * 64) void router_mfma_kernel(const bf16_t* __re
 
 hipError_t router_bf16_mfma(const bf16_t* q, int M, int qw, const bf16_t* w1, int r,
                             const bf16_t* w2, float* lam, Routing rt, hipStream_t s) {
-  const dim3 grid((M + 31) / 32);
-  auto launch = [&](auto kernel, int nw) {
-    hipLaunchKernelGGL(kernel, grid, dim3(nw * 64), 0, s, q, M, qw, w1, w2, lam, rt);
-  };
-  // (qw % 64 == 0 is validated: slices of qw/4 are whole k-steps.)
-  if (qw % 128 == 0)
-    r == 64 ? launch(router_mfma_kernel<2, 8>, 8) : launch(router_mfma_kernel<1, 8>, 8);
+  // (qw % 64 == 0 is validated: the chunks are whole.)
+  if (r == 64)
+    hipLaunchKernelGGL(router_mfma_kernel<2>, dim3((M + 63) / 64), dim3(256), 0, s, q, M, qw, w1,
+                       w2, lam, rt);
   else
-    r == 64 ? launch(router_mfma_kernel<2, 4>, 4) : launch(router_mfma_kernel<1, 4>, 4);
+    hipLaunchKernelGGL(router_mfma_kernel<1>, dim3((M + 127) / 128), dim3(256), 0, s, q, M, qw,
+                       w1, w2, lam, rt);
   return hipGetLastError();
 }
 
