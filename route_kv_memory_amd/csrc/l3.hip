@@ -287,6 +287,10 @@ __global__ __launch_bounds__(1024) void simhash_split_kernel(
   // staging buffers (2 x 4 KB per wave) during the products, slice sums after
   __shared__ __attribute__((aligned(1024))) float part[kSplitWaves][32][64];
   __shared__ float nrm[kSplitWaves][32];
+  // codes of the tile's rows and the list of its undecided (row, hyperplane) bits
+  __shared__ uint64_t code_s[32];
+  __shared__ uint32_t undecided[32 * 64];
+  __shared__ int n_undecided;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
@@ -380,6 +384,7 @@ __global__ __launch_bounds__(1024) void simhash_split_kernel(
     part[wave][acc_row(r, h)][32 + l32] = acc1[r];
   }
   if (h == 0) nrm[wave][l32] = sqr;
+  if (tid == 0) n_undecided = 0;
   __syncthreads();
 
   // wave: rows 2*wave, 2*wave+1 of the tile; lane: hyperplane
@@ -387,7 +392,7 @@ __global__ __launch_bounds__(1024) void simhash_split_kernel(
   const bool on = lane < nbits;
 #pragma unroll 1
   for (int rr = 0; rr < kRowsPerWave; ++rr) {
-    const int i = wave * kRowsPerWave + rr, row = row0 + i;
+    const int i = wave * kRowsPerWave + rr;
     double s = 0.0, e = 0.0;
 #pragma unroll
     for (int w = 0; w < kSplitWaves; ++w) {
@@ -396,44 +401,55 @@ __global__ __launch_bounds__(1024) void simhash_split_kernel(
       e += sqrt(static_cast<double>(nrm[w][i]) * (1.0 + 1e-4)) * Pn[w * 64 + lane];
     }
     e = e * err_factor + 1e-30;
-    uint64_t code = __ballot(on && s > 0.0);
-    uint64_t amb = __ballot(on && fabs(s) <= e);
-    if (amb != 0) {  // uniform over the wave
-      // float64 recomputation: the row (up to kFixChunk float4 per lane at a
-      // time) stays in registers across the undecided hyperplanes, and each
-      // hyperplane's loads are issued together
-      const float* full = vb + static_cast<int64_t>(min(row, rows - 1)) * D;
-      const bool one_chunk = D <= 256 * kFixChunk;
-      f32x4 xa[kFixChunk];
-      auto load_chunk = [&](const float* src, int c0, f32x4* dst) {
-#pragma unroll
-        for (int u = 0; u < kFixChunk; ++u) {
-          const int k = c0 + 256 * u + 4 * lane;
-          dst[u] = k < D ? *reinterpret_cast<const f32x4*>(src + k) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-      };
-      if (one_chunk) load_chunk(full, 0, xa);
-      while (amb != 0) {
-        const int j = __builtin_ctzll(amb);
-        amb &= amb - 1;
-        const float* pj = P + static_cast<int64_t>(j) * D;
-        double t[4] = {0.0, 0.0, 0.0, 0.0};
-        for (int c0 = 0; c0 < D; c0 += 256 * kFixChunk) {
-          if (!one_chunk) load_chunk(full, c0, xa);
-          f32x4 xp[kFixChunk];
-          load_chunk(pj, c0, xp);
-#pragma unroll
-          for (int u = 0; u < kFixChunk; ++u)
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-              t[c] = fma(static_cast<double>(xa[u][c]), static_cast<double>(xp[u][c]), t[c]);
-        }
-        const double tt = wave_sum_f64((t[0] + t[1]) + (t[2] + t[3]));
-        code = tt > 0.0 ? (code | (1ull << j)) : (code & ~(1ull << j));
-      }
+    const uint64_t code = __ballot(on && s > 0.0);
+    const uint64_t amb = __ballot(on && fabs(s) <= e);
+    if (lane == 0) code_s[i] = code;
+    if (amb != 0) {  // uniform over the wave: list the undecided bits
+      int first = 0;
+      if (lane == 0) first = atomicAdd(&n_undecided, __popcll(amb));
+      first = __shfl(first, 0, 64);
+      if ((amb >> lane) & 1)
+        undecided[first + __popcll(amb & ((1ull << lane) - 1))] = (i << 8) | lane;
     }
-    if (lane == 0 && row < rows) codes[b * c_bstride + row] = code;
   }
+  __syncthreads();
+  // Float64 recomputation of the undecided bits, spread over all the waves of
+  // the workgroup: the row (up to kFixChunk float4 per lane at a time) and the
+  // hyperplane are loaded together, each product exact.
+  const int n_fix = n_undecided;
+  for (int w = wave; w < n_fix; w += kSplitWaves) {
+    const uint32_t entry = undecided[w];
+    const int i = static_cast<int>(entry >> 8), j = static_cast<int>(entry & 255);
+    const float* full = vb + static_cast<int64_t>(min(row0 + i, rows - 1)) * D;
+    const float* pj = P + static_cast<int64_t>(j) * D;
+    auto load_chunk = [&](const float* src, int c0, f32x4* dst) {
+#pragma unroll
+      for (int u = 0; u < kFixChunk; ++u) {
+        const int k = c0 + 256 * u + 4 * lane;
+        dst[u] = k < D ? *reinterpret_cast<const f32x4*>(src + k) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    };
+    double t[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int c0 = 0; c0 < D; c0 += 256 * kFixChunk) {
+      f32x4 xa[kFixChunk], xp[kFixChunk];
+      load_chunk(full, c0, xa);
+      load_chunk(pj, c0, xp);
+#pragma unroll
+      for (int u = 0; u < kFixChunk; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          t[c] = fma(static_cast<double>(xa[u][c]), static_cast<double>(xp[u][c]), t[c]);
+    }
+    const double tt = wave_sum_f64((t[0] + t[1]) + (t[2] + t[3]));
+    if (lane == 0) {
+      if (tt > 0.0)
+        atomicOr(reinterpret_cast<unsigned long long*>(&code_s[i]), 1ull << j);
+      else
+        atomicAnd(reinterpret_cast<unsigned long long*>(&code_s[i]), ~(1ull << j));
+    }
+  }
+  __syncthreads();
+  if (tid < 32 && row0 + tid < rows) codes[b * c_bstride + row0 + tid] = code_s[tid];
 }
 
 // The certified path: D a multiple of 32, enough rows to fill the GPU, and a
@@ -553,7 +569,16 @@ __global__ __launch_bounds__(256) void topr_rows_kernel(const uint64_t* __restri
   uint32_t top[RMAX];
 #pragma unroll
   for (int i = 0; i < RMAX; ++i) top[i] = kEmpty;
-  for (int j = 0; j < ne; ++j) insert_sorted(top, cand_key(key, codes[j], j));
+  // block codes loaded 16 at a time before their insertions (one load per
+  // insertion had made the loop wait on every code)
+  for (int j0 = 0; j0 < ne; j0 += 16) {
+    uint64_t cv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) cv[u] = codes[min(j0 + u, ne - 1)];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (j0 + u < ne) insert_sorted(top, cand_key(key, cv[u], j0 + u));
+  }
   int32_t* out = idx + e * R;
 #pragma unroll
   for (int i = 0; i < RMAX; ++i)
