@@ -76,6 +76,14 @@ template <typename T>
 hipError_t fuse_mix(const T* x, const float* l2, const float* means, int nb_cap,
                     const int32_t* idx, const float* lam, int B, int seq, int D, int R,
                     Routing rt, T* xf, hipStream_t s);
+// The same for bf16 layers with many tokens, L3 as a selection product on the
+// matrix cores (``n_blk`` = the blocks idx may name, at most 256; ``ws`` holds
+// fuse_sel_ws_bytes(B, D) bytes), used where fuse_sel_applies(...).
+bool fuse_sel_applies(int B, int seq, int D, int R, int n_blk, Routing rt);
+size_t fuse_sel_ws_bytes(int B, int D);
+hipError_t fuse_mix_sel(const bf16_t* x, const float* l2, const float* means, int nb_cap,
+                        const int32_t* idx, const float* lam, int B, int seq, int D, int R,
+                        Routing rt, bf16_t* xf, int n_blk, void* ws, hipStream_t s);
 // One tier's rows alone, rounded once to the storage type: tier 1 = L2, tier 2 =
 // L3 (mean of the retrieved block means).  Full MKA projects each tier apart.
 template <typename T>

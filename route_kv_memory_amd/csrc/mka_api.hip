@@ -1,7 +1,9 @@
 // C ABI of the FastMKA layer forward: argument validation, workspace layout and
 // dispatch to the kernels.  Every check runs before the first launch of a call,
 // so a rejected call has enqueued nothing.
+#include <algorithm>
 #include <cmath>
+#include <cstdint>
 #include <initializer_list>
 #include <cstdio>
 #include <cstring>
@@ -105,8 +107,11 @@ KvLayout layout_of(const mka_dims* d, const mka_state* st) {
 }
 
 size_t ema_ws(const mka_dims* d) { return round256(ema_ws_bytes(d->batch, d->seq, d->d_model)); }
+// X_fused, then (bf16) the transposed bf16 planes of the block means that the
+// selection-product fusion stages.
 size_t fuse_ws(const mka_dims* d) {
-  return round256(static_cast<size_t>(rows_of(d)) * d->d_model * el_size(d));
+  return round256(static_cast<size_t>(rows_of(d)) * d->d_model * el_size(d)) +
+         (d->dtype == MKA_BF16 ? round256(fuse_sel_ws_bytes(d->batch, d->d_model)) : 0);
 }
 size_t retrieve_ws(const mka_dims* d) {
   return rows_of(d) <= kFewRows ? round256(retrieve_few_ws_bytes(rows_of(d), d->d_model))
@@ -273,7 +278,17 @@ int do_fuse_kv(const mka_dims* d, const void* x, const float* l2, const float* m
   // L1 alone: X_fused = x (lambda = (1, 0, 0)), projected without a fusion pass
   const void* src = x;
   if (rt.ema()) {
-    if (d->dtype == MKA_BF16)
+    // blocks a token of this call may retrieve: those before the last token's block
+    const int64_t n_elig = std::min<int64_t>((pos0 + d->seq - 1) / d->block, nb_cap);
+    const size_t xf_bytes = round256(static_cast<size_t>(rows_of(d)) * d->d_model * el_size(d));
+    if (d->dtype == MKA_BF16 &&
+        fuse_sel_applies(d->batch, d->seq, d->d_model, d->top_r,
+                         static_cast<int>(std::min<int64_t>(n_elig, 1 << 30)), rt))
+      MKA_LAUNCH("fuse", fuse_mix_sel(static_cast<const bf16_t*>(x), l2, means, nb_cap, idx, lam,
+                                      d->batch, d->seq, d->d_model, d->top_r, rt,
+                                      static_cast<bf16_t*>(ws), static_cast<int>(n_elig),
+                                      static_cast<char*>(ws) + xf_bytes, s));
+    else if (d->dtype == MKA_BF16)
       MKA_LAUNCH("fuse", fuse_mix<bf16_t>(static_cast<const bf16_t*>(x), l2, means, nb_cap, idx,
                                           lam, d->batch, d->seq, d->d_model, d->top_r, rt,
                                           static_cast<bf16_t*>(ws), s));

@@ -104,7 +104,9 @@ def test_workspace_sizes_and_rejection():
     d = _d()
     ema = mka.mka_workspace_bytes(d, mka.MKA_OP_EMA_SCAN)
     fuse = mka.mka_workspace_bytes(d, mka.MKA_OP_FUSE_KV)
-    assert fuse == 2 * 4096 * 3584 * 2                 # X_fused in bf16
+    # X_fused in bf16, then the two transposed bf16 planes of up to 256 block
+    # means per sequence that the matrix-core L3 path stages
+    assert fuse == 2 * 4096 * 3584 * 2 + 2 * 2 * 3584 * 256 * 2
     assert ema == 2 * 4 * 2 * (4096 // 64) * 3584       # chunk carries, 2 floats
     retr = mka.mka_workspace_bytes(d, mka.MKA_OP_RETRIEVE)
     idx = mka.mka_workspace_bytes(d, mka.MKA_OP_INDEX, 33)
