@@ -70,6 +70,9 @@ KERNEL_SOURCES = {
     "router_mfma_kernel": ["route.hip"],
     "simhash_split_kernel": ["l3.hip"],
     "fuse_mix_kernel": ["fuse.hip"],
+    "fuse_mix_sel_kernel": ["fuse.hip"],
+    "fuse_split_kernel": ["fuse.hip"],
+    "topr_rows_kernel": ["l3.hip"],
 }
 ROOFLINE_KERNEL = "attn_prefill_bf16_kernel"
 
