@@ -15,6 +15,8 @@
 // Scores use exp2 with log2(e)/sqrt(dh) folded into one fp32 scale per score.
 #include "attn_split.h"
 
+#include <type_traits>
+
 namespace mka {
 
 // 16-byte chunk swizzle of LDS row P of a K tile: a row is DH*2 bytes (256 B
@@ -32,6 +34,11 @@ template <int DH>
 __device__ __forceinline__ int vswz(int P) {
   return DH == 128 ? 4 * (P & 3) : 4 * ((P >> 1) & 1);
 }
+
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002 | 0x400;  // vector ALU, transcendentals included
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
 __device__ __forceinline__ int kperm(int r) {
   const int q = r & 15;
@@ -55,8 +62,14 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
                 NDB = DH / 32;
   constexpr int KLD = BN * DH * 2 / 1024 / NW;  // 1 KB tile loads per wave (K and V each)
   static_assert(KLD * NW * 1024 == BN * DH * 2, "a tile splits evenly over the waves");
-  __shared__ __attribute__((aligned(1024))) bf16_t Ks[2][BN * DH];
-  __shared__ __attribute__((aligned(1024))) bf16_t Vs[2][BN * DH];
+  // The two buffers of each tile are distinct objects and the tile loop is
+  // unrolled by two, so every LDS access names a fixed buffer: the compiler
+  // then sees that the next tile's direct loads do not touch the tile being
+  // read and waits for them only where the loop waits explicitly.
+  __shared__ __attribute__((aligned(1024))) bf16_t Ks0[BN * DH];
+  __shared__ __attribute__((aligned(1024))) bf16_t Ks1[BN * DH];
+  __shared__ __attribute__((aligned(1024))) bf16_t Vs0[BN * DH];
+  __shared__ __attribute__((aligned(1024))) bf16_t Vs1[BN * DH];
 
   const int hpg = H / G;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -118,14 +131,14 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
   }
   // One tile of BN keys lies in one page (pages hold a multiple of 64 rows);
   // keys at or beyond kv_end read as zeros through the buffer range.
-  auto gload = [&](int j0, int buf) {
+  auto gload = [&](int j0, bf16_t* ks, bf16_t* vs) __attribute__((always_inline)) {
     const int64_t off = pw.row(kv, b, g, j0);
     const uint32_t bytes = static_cast<uint32_t>(min<int64_t>(BN, kv_end - j0) * DH * 2);
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kc + off, bytes), vrs = make_rsrc(Vc + off, bytes);
 #pragma unroll
     for (int i = 0; i < KLD; ++i) {
-      buffer_load_lds16(krs, (lds_void_t*)(&Ks[buf][(wave * KLD + i) * 512]), k_src[i]);
-      buffer_load_lds16(vrs, (lds_void_t*)(&Vs[buf][(wave * KLD + i) * 512]), v_src[i]);
+      buffer_load_lds16(krs, (lds_void_t*)(ks + (wave * KLD + i) * 512), k_src[i]);
+      buffer_load_lds16(vrs, (lds_void_t*)(vs + (wave * KLD + i) * 512), v_src[i]);
     }
   };
 
@@ -136,32 +149,45 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
-  gload(0, 0);
+  gload(0, Ks0, Vs0);
   __builtin_amdgcn_s_waitcnt(kVmcntPending<0>());  // this wave's tile loads have landed
   __syncthreads();
-  for (int jt = 0; jt < n_tiles; ++jt) {
-    const int buf = jt & 1;
-    const int j0 = jt * BN;
-    if (jt + 1 < n_tiles) gload(j0 + BN, buf ^ 1);
-
+  // One key tile; MASKED: the tile holds keys after some of the wave's query
+  // rows (a diagonal tile), which are masked out.  The tiles without a mask
+  // take a separate copy of the body so that nothing branches between the
+  // score products and the probabilities.
+  auto body = [&](int jt, int j0, const bf16_t* kt, const bf16_t* vt, auto MASKED)
+                  __attribute__((always_inline)) {
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
       const int P = kb * 32 + l32;
-      const bf16_t* kr = &Ks[buf][P * DH];
+      const bf16_t* kr = kt + P * DH;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
         s[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kr + 8 * ((2 * ks + hl) ^ kswz<DH>(P))),
                              qf[ks], s[kb]);
+      if constexpr (!decltype(MASKED)::value) {
+        if (kb == 0) {
+          // first half's products with their K reads a few ahead; the second
+          // half is scheduled together with the first half's probabilities
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+          for (int i = 0; i < NKS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            if (i < NKS - 4) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
     }
 
     // Online max-shift in the exp2 domain: ms is the running reference.  It
     // is raised only when a tile's maximum exceeds it by more than 8, so most
     // tiles need no rescale; probabilities stay below 2^8, which fp32 sums
     // and bf16 operands carry as well as values below 1.
-    const bool diag = (j0 + BN - 1) > wave_pos0;
-    if (diag) {
+    if constexpr (decltype(MASKED)::value) {
       const int q_rel = static_cast<int>(q_pos - j0);  // keys of the tile after the query
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -169,11 +195,59 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
         for (int r = 0; r < 16; ++r)
           if (kb * 32 + 16 * (r >> 3) + 8 * hl + (r & 7) > q_rel) s[kb][r] = -INFINITY;
     }
+
+    // Probabilities of key half kb as the bf16x8 B operands of
+    // O^T += V^T P^T; the row sum adds the same bf16 values the products use,
+    // two per v_dot2 (each pair is built as a bf16x2 value: bit-casting the
+    // words of a packed u32x4 instead made the compiler feed the first word to
+    // all four dot products).
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    const bf16x2v ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    bf16x8 pf[2][2];
+    auto probs = [&](int kb, float nms, float& l) __attribute__((always_inline)) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x2v v = {
+              static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[kb][8 * st + 2 * i], sl2, nms))),
+              static_cast<__bf16>(
+                  __builtin_amdgcn_exp2f(fmaf(s[kb][8 * st + 2 * i + 1], sl2, nms)))};
+          l = __builtin_amdgcn_fdot2_f32_bf16(v, ones, l, false);
+          w[i] = __builtin_bit_cast(uint32_t, v);
+        }
+        pf[kb][st] = __builtin_bit_cast(bf16x8, w);
+      }
+    };
+    // The first key half's probabilities are formed with the current
+    // reference before the tile's maximum is known, so that they overlap the
+    // second half's score products; a tile that raises the reference (the
+    // first tile always does) forms them again.  The results are those of
+    // forming every probability after the raise decision.
+    float l_new = l_i;
+    probs(0, -ms, l_new);
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+    if constexpr (!decltype(MASKED)::value) {
+      // The second half's products (K reads a few ahead) with the first
+      // half's probabilities and maximum between them: the matrix cores and
+      // the vector ALU work on them at the same time.  The empty asm takes
+      // the probabilities as inputs, so that they are formed before the
+      // scheduling fence below and not next to their later uses.
+      asm volatile("" ::"v"(pf[0][0]), "v"(pf[0][1]), "v"(l_new), "v"(mx));
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      for (int i = 0; i < NKS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        if (i < NKS - 4) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 56 / NKS, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
     {  // the two lanes of a query (l and l^32) exchange their maxima by a lane swap
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                        false, false);
@@ -191,38 +265,16 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
       ms += delta;
+      l_new = l_i;
+      probs(0, -ms, l_new);
     }
-    const float nms = -ms;
 
-    // Probabilities as the bf16x8 B operands of O^T += V^T P^T; the row sum
-    // adds the same bf16 values the products use, two per v_dot2 (each pair
-    // is built as a bf16x2 value: bit-casting the words of a packed u32x4
-    // instead made the compiler feed the first word to all four dot products).
-    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-    const bf16x2v ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-    bf16x8 pf[2][2];
+    // O^T += V^T P^T, first key half while the second half's probabilities
+    // are formed.
+    auto pv = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        u32x4 w;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bf16x2v v = {
-              static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[kb][8 * st + 2 * i], sl2, nms))),
-              static_cast<__bf16>(
-                  __builtin_amdgcn_exp2f(fmaf(s[kb][8 * st + 2 * i + 1], sl2, nms)))};
-          l_i = __builtin_amdgcn_fdot2_f32_bf16(v, ones, l_i, false);
-          w[i] = __builtin_bit_cast(uint32_t, v);
-        }
-        pf[kb][st] = __builtin_bit_cast(bf16x8, w);
-      }
-
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const bf16_t* vb = &Vs[buf][v_base[db]];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int db = 0; db < NDB; ++db) {
+        const bf16_t* vb = vt + v_base[db];
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           const int k0 = (kb * 32 + 16 * st) * DH;
@@ -230,9 +282,43 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
           const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           acc[db] = mfma32x32x16(vf, pf[kb][st], acc[db]);
         }
+      }
+    };
+    pv(0);
+    probs(1, -ms, l_new);
+    pv(1);
+    l_i = l_new;
+    if constexpr (!decltype(MASKED)::value) {
+      // The first half's value products with the second half's probabilities
+      // between them; then the second half's products.
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        if (i < 6) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      }
     }
+  };
+  auto tile = [&](int jt, const bf16_t* kt, const bf16_t* vt, bf16_t* kn, bf16_t* vn)
+                  __attribute__((always_inline)) {
+    const int j0 = jt * BN;
+    if (jt + 1 < n_tiles) gload(j0 + BN, kn, vn);
+    if ((j0 + BN - 1) > wave_pos0)
+      body(jt, j0, kt, vt, std::true_type{});
+    else
+      body(jt, j0, kt, vt, std::false_type{});
     __builtin_amdgcn_s_waitcnt(kVmcntPending<0>());  // this wave's tile loads have landed
     __syncthreads();
+  };
+  for (int jt = 0; jt < n_tiles; jt += 2) {
+    tile(jt, Ks0, Vs0, Ks1, Vs1);
+    if (jt + 1 < n_tiles) tile(jt + 1, Ks1, Vs1, Ks0, Vs0);
   }
 
   l_i += __shfl_xor(l_i, 32, 64);

@@ -222,8 +222,13 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void attn_bwd_dkv_kernel(
   constexpr int BK = 128, BQ = 64, NKS = DH / 16, NDB = DH / 32;
   constexpr int TLD = BQ * DH * 2 / 1024 / 4;  // 1 KB loads per wave per tile (Q and dO each)
   constexpr int RPC = 1024 / (DH * 2);         // rows per 1 KB
-  __shared__ __attribute__((aligned(1024))) bf16_t Qs[2][BQ * DH];
-  __shared__ __attribute__((aligned(1024))) bf16_t Gs[2][BQ * DH];
+  // Each buffer is an object of its own and the tile loop is unrolled by
+  // two, so the compiler sees that the next tile's direct loads do not touch
+  // the tile being read (it would otherwise wait for them before each read).
+  __shared__ __attribute__((aligned(1024))) bf16_t Qs0[BQ * DH];
+  __shared__ __attribute__((aligned(1024))) bf16_t Qs1[BQ * DH];
+  __shared__ __attribute__((aligned(1024))) bf16_t Gs0[BQ * DH];
+  __shared__ __attribute__((aligned(1024))) bf16_t Gs1[BQ * DH];
   __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
   __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
 
@@ -272,8 +277,12 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void attn_bwd_dkv_kernel(
       const int P = bperm(8 * hl + 4 * q + (r >> 2)), d = db * 32 + 16 * G + 4 * (r & 3);
       t_base[q][db] = P * DH + 8 * ((d >> 3) ^ cswz<DH>(P)) + (d & 7);
     }
+  // rl, rd: the raw log-sum-exp and D of the next tile's rows; they are
+  // converted where they are stored to LDS, at the end of the tile, because
+  // waiting for these loads earlier would also wait for the tile loads issued
+  // before them.
   float rl = 0.f, rd = 0.f;
-  auto gload = [&](int it, int buf) {
+  auto gload = [&](int it, bf16_t* qs, bf16_t* gs) __attribute__((always_inline)) {
     const int t0 = t_first + it * BQ;
     const int nrow = min(BQ, N - t0);
     const int64_t base = (static_cast<int64_t>(b) * N + t0) * H * DH + static_cast<int64_t>(h) * DH;
@@ -281,21 +290,21 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void attn_bwd_dkv_kernel(
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, bytes), grs = make_rsrc(dO + base, bytes);
 #pragma unroll
     for (int i = 0; i < TLD; ++i) {
-      buffer_load_lds16(qrs, (lds_void_t*)(&Qs[buf][(wave * TLD + i) * 512]), t_src[i]);
-      buffer_load_lds16(grs, (lds_void_t*)(&Gs[buf][(wave * TLD + i) * 512]), t_src[i]);
+      buffer_load_lds16(qrs, (lds_void_t*)(qs + (wave * TLD + i) * 512), t_src[i]);
+      buffer_load_lds16(grs, (lds_void_t*)(gs + (wave * TLD + i) * 512), t_src[i]);
     }
     if (tid < BQ) {
       const int t = t0 + tid;
       const int64_t row = static_cast<int64_t>(b * N + min(t, N - 1)) * H + h;
-      const float l = lse[row], dv = dsum[row];
-      rl = t < N ? l * kLog2e : INFINITY;
-      rd = t < N ? dv : 0.f;
+      rl = lse[row];
+      rd = dsum[row];
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int it, int buf) {
     if (tid < BQ) {
-      Ls[buf][tid] = rl;
-      Ds[buf][tid] = rd;
+      const bool in = t_first + it * BQ + tid < N;
+      Ls[buf][tid] = in ? rl * kLog2e : INFINITY;
+      Ds[buf][tid] = in ? rd : 0.f;
     }
   };
 
@@ -305,22 +314,29 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void attn_bwd_dkv_kernel(
     adk[db] = f32x16{};
     adv[db] = f32x16{};
   }
-  gload(0, 0);
-  sstore(0);
+  gload(0, Qs0, Gs0);
+  sstore(0, 0);
   __builtin_amdgcn_s_waitcnt(kVmcntPending<0>());  // this wave's tile loads have landed
   __syncthreads();
-  for (int it = 0; it < n_it; ++it) {
-    const int buf = it & 1;
+  auto tile = [&](int it, int buf, const bf16_t* qt, const bf16_t* gt, bf16_t* qn, bf16_t* gn)
+                  __attribute__((always_inline)) {
+    // An opaque zero offset keeps the LDS address arithmetic inside the loop
+    // (hoisted for both buffers it would not fit in the registers); the
+    // pointers still derive from their own buffer objects.
+    int z = 0;
+    asm volatile("" : "+s"(z));
+    qt += z;
+    gt += z;
     const int t0 = t_first + it * BQ;
-    if (it + 1 < n_it) gload(it + 1, buf ^ 1);
+    if (it + 1 < n_it) gload(it + 1, qn, gn);
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       s[qb] = f32x16{};
       dp[qb] = f32x16{};
       const int P = qb * 32 + l32;
-      const bf16_t* qr = &Qs[buf][P * DH];
-      const bf16_t* gr = &Gs[buf][P * DH];
+      const bf16_t* qr = qt + P * DH;
+      const bf16_t* gr = gt + P * DH;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const int c = 8 * ((2 * ks + hl) ^ cswz<DH>(P));
@@ -356,16 +372,21 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void attn_bwd_dkv_kernel(
         for (int st = 0; st < 2; ++st) {
           const int o = (qb * 32 + 16 * st) * DH;
           if constexpr (WV)
-            adv[db] = mfma32x32x16(ld_tr8(&Gs[buf][t_base[0][db] + o], &Gs[buf][t_base[1][db] + o]),
+            adv[db] = mfma32x32x16(ld_tr8(gt + t_base[0][db] + o, gt + t_base[1][db] + o),
                                    pf[qb][st], adv[db]);
           if constexpr (WK)
-            adk[db] = mfma32x32x16(ld_tr8(&Qs[buf][t_base[0][db] + o], &Qs[buf][t_base[1][db] + o]),
+            adk[db] = mfma32x32x16(ld_tr8(qt + t_base[0][db] + o, qt + t_base[1][db] + o),
                                    dsf[qb][st], adk[db]);
         }
     }
-    if (it + 1 < n_it) sstore(buf ^ 1);
+    if (it + 1 < n_it) sstore(it + 1, buf ^ 1);
     __builtin_amdgcn_s_waitcnt(kVmcntPending<0>());  // this wave's tile loads have landed
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);  // the two copies of the body are scheduled apart
+  };
+  for (int it = 0; it < n_it; it += 2) {
+    tile(it, 0, Qs0, Gs0, Qs1, Gs1);
+    if (it + 1 < n_it) tile(it + 1, 1, Qs1, Gs1, Qs0, Gs0);
   }
   if (k_row < N) {
     float* out = dkv + static_cast<int64_t>(hh) * B * N * 2 * G * DH +
