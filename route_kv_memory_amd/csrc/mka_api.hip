@@ -1019,11 +1019,10 @@ int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weight
   char* ws_main = ws_chain + prefill_chain_ws(d);
   char* ws_prep = ws_main + prefill_main_ws(d);
   const bool prep = prefill_prepares_codes(d);
-  // The hyperplane split of the key codes, the EMA scan, the block codes, the
-  // block projections (needed only by later decode steps) and the retrieval
-  // need only the weights and x, so they run on the auxiliary stream beside the
-  // query product (register-lean, so the scan's waves share its SIMDs) and the
-  // router; the main stream joins them before the fusion.
+  // The hyperplane split of the key codes, the EMA scan, the block codes and
+  // the retrieval need only the weights and x, so they run on the auxiliary
+  // stream beside the query product (register-lean, so the scan's waves share
+  // its SIMDs) and the router; the main stream joins them before the fusion.
   Aux* aux = aux_for_current_device(&rc);
   if (aux == nullptr) return rc;
   std::lock_guard<std::mutex> guard(aux->lock);
@@ -1038,9 +1037,6 @@ int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weight
   if ((rc = do_index(d, st->block_means, st->nb_cap, static_cast<int>(first), static_cast<int>(n),
                      w->proj, st->block_hash, ws_chain, s2)))
     return rc;
-  if ((rc = do_block_kv(d, st->block_means, st->nb_cap, static_cast<int>(first),
-                        static_cast<int>(n), w->w_k, w->w_v, st->block_kv, s2)))
-    return rc;
   if (prep) {
     MKA_LAUNCH("l3_retrieve/keys",
                simhash_rows_prepared(out->l2, static_cast<int64_t>(d->seq) * d->d_model, d->seq,
@@ -1050,6 +1046,12 @@ int mka_prefill(const mka_dims* d, const void* x, int64_t pos0, const mka_weight
                                              st->nb_cap, d->block, d->top_r, out->idx, s2));
   }
   MKA_LAUNCH("prefill/join", hipEventRecord(aux->join, s2));
+  // The block projections serve later decode steps only: they run after the
+  // join, beside the fusion and the attention, and the caller's stream waits
+  // for them at the end.
+  if ((rc = do_block_kv(d, st->block_means, st->nb_cap, static_cast<int>(first),
+                        static_cast<int>(n), w->w_k, w->w_v, st->block_kv, s2)))
+    return rc;
   MKA_LAUNCH("prefill/join", hipEventRecord(aux->done, s2));
   if ((rc = do_route(d, x, w->w_q, w->w_r1, w->w_r2, out->q, out->lambda, ws_main, s))) return rc;
   MKA_LAUNCH("prefill/join", hipStreamWaitEvent(s, aux->join, 0));
