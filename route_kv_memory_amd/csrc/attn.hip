@@ -235,14 +235,17 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
       // half's probabilities and maximum between them: the matrix cores and
       // the vector ALU work on them at the same time.  The empty asm takes
       // the probabilities as inputs, so that they are formed before the
-      // scheduling fence below and not next to their later uses.
+      // scheduling fence below and not next to their later uses.  With
+      // dh = 128, 5 vector instructions per product here and 8 in the value
+      // products below (the rest of this half's work goes there) measured
+      // best (7 and 6: 1% slower; 9 and 4: 2% slower).
       asm volatile("" ::"v"(pf[0][0]), "v"(pf[0][1]), "v"(l_new), "v"(mx));
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
       for (int i = 0; i < NKS; ++i) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
         if (i < NKS - 4) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedValu, 56 / NKS, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, DH == 128 ? 5 : 56 / NKS, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -296,7 +299,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
       for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, DH == 128 ? 8 : 6, 0);
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
