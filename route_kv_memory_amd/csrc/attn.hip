@@ -293,8 +293,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
     l_i = l_new;
     if constexpr (!decltype(MASKED)::value) {
       // The first half's value products with the second half's probabilities
-      // between them; then the second half's products.
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+      // between them; then the second half's products.  Six V^T fragment
+      // reads go out ahead of the first product (two: 2% slower; four: 0.3%).
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
@@ -304,7 +305,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_prefill_bf16_ke
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        if (i < 6) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        if (i < 5) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
       }
     }
   };
