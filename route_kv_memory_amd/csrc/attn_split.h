@@ -97,7 +97,7 @@ __device__ __forceinline__ void decode_split_chunk(
   constexpr int BN = kSplitTile, VP = BN + 8, NKS = DH / 32, NDB = DH / 16, KQ = BN / 4;
   constexpr int VL = KQ * (DH / 8) / 64;  // V load items per lane per tile
   static_assert(4 * kSplitHeads * (DH + 2) * 4 <= split_lds_bytes<DH>(), "merge buffer must fit");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l16 = lane & 15, q4 = lane >> 4;
   const int hpg = H / G, h_lo = hb * kSplitHeads;
   const int nh = min(kSplitHeads, hpg - h_lo);
   bf16_t* Vt = reinterpret_cast<bf16_t*>(lds) + wave * DH * VP;

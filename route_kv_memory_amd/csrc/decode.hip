@@ -70,7 +70,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void decode_front_kernel(DecodeArgs<T> a) {
   __shared__ float Ls[kDecSlice];
   __shared__ double red[4][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nq_wg = (a.qw + 3) / 4;
   if (static_cast<int>(blockIdx.x) < nq_wg) {
     // ---- Q projection: one wave per output column, lanes stride D with 16-byte loads.
@@ -148,7 +148,7 @@ template <typename T, int RMAX>
 __global__ __launch_bounds__(256) void decode_mid_kernel(DecodeArgs<T> a) {
   __shared__ uint64_t key_s;
   __shared__ uint32_t cand[4][RMAX];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nh_wg = a.rt.learned() ? (a.r + 3) / 4 : 0;
   if (static_cast<int>(blockIdx.x) < nh_wg) {
     // ---- router hidden unit n for every token: GELU(q . W_r1[n]).
@@ -370,7 +370,7 @@ __device__ __forceinline__ void decode_products(int D, int B, WRow wrow, Feed fe
 __global__ __launch_bounds__(256) void decode_inputs_kernel(DecodeArgs<bf16_t> a) {
   __shared__ float Ls[kDecSlice];
   __shared__ double red[4][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nq_wg = (a.qw + 4 * kGemvCols - 1) / (4 * kGemvCols);
   int wg = blockIdx.x;
   if (wg < nq_wg) {
@@ -444,7 +444,7 @@ __global__ __launch_bounds__(256) void decode_inputs_kernel(DecodeArgs<bf16_t> a
 template <int DH, int RMAX, bool PAGED>
 __global__ __launch_bounds__(256, 2) void decode_attend_kernel(DecodeArgs<bf16_t> a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[split_lds_bytes<DH>()];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nh_wg = a.rt.learned() ? (a.r + 3) / 4 : 0;
   int wg = blockIdx.x;
   if (wg < nh_wg) {

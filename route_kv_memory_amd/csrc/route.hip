@@ -38,15 +38,18 @@ __global__ __launch_bounds__(256, 2) void router_mfma_kernel(const bf16_t* __res
   static_assert(A_LD >= 1 && W_LD >= 1 && (A_LD + W_LD) * 4096 == STAGE, "loads split over 4 waves");
   static_assert(TOK * (R + 1) * 4 <= kRouterStages * STAGE, "the hidden block fits the stages");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kRouterStages * STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), h = lane >> 5, l32 = lane & 31;
   const int row0 = blockIdx.x * TOK;
   const int rb = wave / NB, jb = wave % NB;
 
   // Source of this lane's 16 bytes in load i of a chunk: LDS row 8 i' + lane / 8
   // (i' counts the 1 KB loads of the operand), slot lane % 8.
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(
-      Q + static_cast<int64_t>(row0) * qw,
+  // The byte count is made scalar explicitly: the clamp compiles to a vector
+  // instruction, and a descriptor with a vector dword turns every load of it
+  // into a loop over the lanes' distinct descriptors.
+  const uint32_t q_bytes = __builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>(static_cast<int64_t>(max(0, min(TOK, M - row0))) * qw * 2));
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + static_cast<int64_t>(row0) * qw, q_bytes);
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(W1, static_cast<uint32_t>(R * qw * 2));
   uint32_t a_src[A_LD], w_src[W_LD];
 #pragma unroll
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(256) void router_rowwise_kernel(const T* __restrict
                                                              const T* __restrict__ W2,
                                                              float* __restrict__ lam, Routing rt) {
   __shared__ float hid[256];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t row = blockIdx.x;
   const T* q = Q + row * qw;
   constexpr int V = Vec16<T>::kN;
