@@ -163,29 +163,68 @@ __global__ __launch_bounds__(64) void attn_bwd_dkv_rows_kernel(
 // ---------------------------------------------------------------------------
 // Layout helpers for the transposed products.
 // dst[c][r] = src[r][c] for r < R, zero for R <= r < Rp; src rows have stride
-// lds_ elements, dst rows ldd.  32 x 32 tiles through LDS.
-// ---------------------------------------------------------------------------
-template <typename TS, typename TD>
+// lds_ elements, dst rows ldd.  64 x 64 tiles through LDS, moved as 16-byte
+// vectors where the tile lies inside both matrices and the strides and bases
+// allow it (VEC), element by element otherwise.
 // rows_dst (optional): the source converted to TD in place of a separate
 // conversion pass (same layout as src).
+// ---------------------------------------------------------------------------
+template <typename T> constexpr int kPer16 = 16 / sizeof(T);  // elements per 16 bytes
+
+template <typename TS, typename TD>
 __global__ __launch_bounds__(256) void transpose_kernel(const TS* __restrict__ src, int64_t lds_,
                                                         int R, int C, int Rp, int64_t ldd,
                                                         TD* __restrict__ dst,
-                                                        TD* __restrict__ rows_dst) {
-  __shared__ float tile[32][33];
-  const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
-  for (int i = ty; i < 32; i += 8) {
-    const int r = r0 + i, c = c0 + tx;
-    const bool in = r < R && c < C;
-    tile[i][tx] = in ? Elem<TS>::to_f32(src[static_cast<int64_t>(r) * lds_ + c]) : 0.f;
-    if (rows_dst != nullptr && in)
-      rows_dst[static_cast<int64_t>(r) * lds_ + c] = Elem<TD>::from_f32(tile[i][tx]);
+                                                        TD* __restrict__ rows_dst, bool vec_in,
+                                                        bool vec_out) {
+  constexpr int T = 64, NS = kPer16<TS>, ND = kPer16<TD>;
+  __shared__ float tile[T][T + 1];
+  const int r0 = blockIdx.y * T, c0 = blockIdx.x * T, tid = threadIdx.x;
+  if (vec_in && r0 + T <= R && c0 + T <= C) {
+    // T rows of T / NS vectors each
+#pragma unroll
+    for (int e = tid; e < T * (T / NS); e += 256) {
+      const int i = e / (T / NS), cv = (e % (T / NS)) * NS;
+      const int64_t o = static_cast<int64_t>(r0 + i) * lds_ + c0 + cv;
+      TS v[NS];
+      *reinterpret_cast<u32x4*>(v) = *reinterpret_cast<const u32x4*>(src + o);
+      TD w[NS];
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        tile[i][cv + k] = Elem<TS>::to_f32(v[k]);
+        w[k] = Elem<TD>::from_f32(tile[i][cv + k]);
+      }
+      if (rows_dst != nullptr) {
+#pragma unroll
+        for (int k = 0; k < NS; ++k) rows_dst[o + k] = w[k];
+      }
+    }
+  } else {
+    for (int e = tid; e < T * T; e += 256) {
+      const int i = e / T, c = e % T, r = r0 + i;
+      const bool in = r < R && c0 + c < C;
+      const int64_t o = static_cast<int64_t>(r) * lds_ + c0 + c;
+      tile[i][c] = in ? Elem<TS>::to_f32(src[o]) : 0.f;
+      if (rows_dst != nullptr && in) rows_dst[o] = Elem<TD>::from_f32(tile[i][c]);
+    }
   }
   __syncthreads();
-  for (int i = ty; i < 32; i += 8) {
-    const int c = c0 + i, r = r0 + tx;
-    if (c < C && r < Rp) dst[static_cast<int64_t>(c) * ldd + r] = Elem<TD>::from_f32(tile[tx][i]);
+  if (vec_out && c0 + T <= C && r0 + T <= Rp) {
+    // T destination rows (source columns) of T / ND vectors each
+#pragma unroll
+    for (int e = tid; e < T * (T / ND); e += 256) {
+      const int c = e / (T / ND), rv = (e % (T / ND)) * ND;
+      TD w[ND];
+#pragma unroll
+      for (int k = 0; k < ND; ++k) w[k] = Elem<TD>::from_f32(tile[rv + k][c]);
+      *reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(c0 + c) * ldd + r0 + rv) =
+          *reinterpret_cast<const u32x4*>(w);
+    }
+  } else {
+    for (int e = tid; e < T * T; e += 256) {
+      const int c = e / T, i = e % T, r = r0 + i;
+      if (c0 + c < C && r < Rp) dst[static_cast<int64_t>(c0 + c) * ldd + r] = Elem<TD>::from_f32(tile[i][c]);
+    }
   }
 }
 
@@ -488,22 +527,27 @@ hipError_t attn_bwd_rows(const T* q, const T* k, const T* v, const T* d_o, const
   return hipGetLastError();
 }
 
-template <typename TS, typename TD>
-hipError_t transpose(const TS* src, int64_t lds_, int R, int C, int Rp, int64_t ldd, TD* dst,
-                     hipStream_t s) {
-  const dim3 grid((C + 31) / 32, (Rp + 31) / 32);
-  hipLaunchKernelGGL((transpose_kernel<TS, TD>), grid, dim3(256), 0, s, src, lds_, R, C, Rp, ldd,
-                     dst, static_cast<TD*>(nullptr));
-  return hipGetLastError();
+// 16-byte vectors apply when the base is 16-byte aligned and the row stride a
+// multiple of the vector.
+template <typename E>
+static bool vec_ok(const E* p, int64_t ld) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0 && ld % kPer16<E> == 0;
 }
 
 template <typename TS, typename TD>
 hipError_t transpose_copy(const TS* src, int64_t lds_, int R, int C, int Rp, int64_t ldd, TD* dst,
                           TD* rows_dst, hipStream_t s) {
-  const dim3 grid((C + 31) / 32, (Rp + 31) / 32);
+  const dim3 grid((C + 63) / 64, (Rp + 63) / 64);
+  const bool vec_in = vec_ok(src, lds_) && (rows_dst == nullptr || vec_ok(rows_dst, lds_));
   hipLaunchKernelGGL((transpose_kernel<TS, TD>), grid, dim3(256), 0, s, src, lds_, R, C, Rp, ldd,
-                     dst, rows_dst);
+                     dst, rows_dst, vec_in, vec_ok(dst, ldd));
   return hipGetLastError();
+}
+
+template <typename TS, typename TD>
+hipError_t transpose(const TS* src, int64_t lds_, int R, int C, int Rp, int64_t ldd, TD* dst,
+                     hipStream_t s) {
+  return transpose_copy(src, lds_, R, C, Rp, ldd, dst, static_cast<TD*>(nullptr), s);
 }
 
 template <typename TS, typename TD>
