@@ -34,8 +34,29 @@ struct EpiAdd {
     c[static_cast<int64_t>(m) * ldc + n] += v;
   }
   __device__ __forceinline__ void store4(int m, int n, const float* v, int N) const {
+    float old[4];
+    load4(m, n, N, old);
+    const float sum[4] = {old[0] + v[0], old[1] + v[1], old[2] + v[2], old[3] + v[3]};
+    put4(m, n, sum, N);
+  }
+  // The two halves of store4, so that a kernel can issue the reads of many
+  // quads before their writes (one wait for the lot instead of one per quad).
+  // Columns n .. n+3 (n % 4 == 0); those at or past N are neither read nor written.
+  __device__ __forceinline__ void load4(int m, int n, int N, float* old) const {
+    const float* p = c + static_cast<int64_t>(m) * ldc + n;
+    if (n + 3 < N) {
+      mka::load4(p, old);
+    } else {
+      for (int i = 0; i < 4; ++i) old[i] = n + i < N ? p[i] : 0.f;
+    }
+  }
+  __device__ __forceinline__ void put4(int m, int n, const float* v, int N) const {
     float* p = c + static_cast<int64_t>(m) * ldc + n;
-    for (int i = 0; i < 4 && n + i < N; ++i) p[i] += v[i];
+    if (n + 3 < N) {
+      mka::store4(p, v);
+    } else {
+      for (int i = 0; i < 4 && n + i < N; ++i) p[i] = v[i];
+    }
   }
 };
 

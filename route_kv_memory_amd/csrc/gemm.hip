@@ -227,15 +227,34 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + wm * 128 + i * 32 + l32;
     if (m >= M) continue;
+    if constexpr (std::is_same<Epi, EpiAdd>::value) {
+      // accumulate: the row's 4*NB quads are read together, then written
+      float old[NB][4][4];
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int n = n0 + wn * WN + j * 32 + 8 * rq + 4 * h;
-        const float v[4] = {acc[i][j][4 * rq], acc[i][j][4 * rq + 1], acc[i][j][4 * rq + 2],
-                            acc[i][j][4 * rq + 3]};
-        epi.store4(m, n, v, N);
-      }
+        for (int rq = 0; rq < 4; ++rq)
+          epi.load4(m, n0 + wn * WN + j * 32 + 8 * rq + 4 * h, N, old[j][rq]);
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = old[j][rq][e] + acc[i][j][4 * rq + e];
+          epi.put4(m, n0 + wn * WN + j * 32 + 8 * rq + 4 * h, v, N);
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int n = n0 + wn * WN + j * 32 + 8 * rq + 4 * h;
+          const float v[4] = {acc[i][j][4 * rq], acc[i][j][4 * rq + 1], acc[i][j][4 * rq + 2],
+                              acc[i][j][4 * rq + 3]};
+          epi.store4(m, n, v, N);
+        }
+    }
   }
 }
 
@@ -273,7 +292,11 @@ struct EpiPart {  // partial of range blockIdx.y: row-major [S][M][N]
   int64_t stride;
   __device__ __forceinline__ void store4(int m, int n, const float* v, int N) const {
     float* p = base + blockIdx.y * stride + static_cast<int64_t>(m) * ldc + n;
-    for (int i = 0; i < 4 && n + i < N; ++i) p[i] = v[i];
+    if (n + 3 < N) {
+      mka::store4(p, v);
+    } else {
+      for (int i = 0; i < 4 && n + i < N; ++i) p[i] = v[i];
+    }
   }
 };
 
