@@ -228,11 +228,20 @@ __global__ __launch_bounds__(256) void transpose_kernel(const TS* __restrict__ s
   }
 }
 
-template <typename TS, typename TD>
+// Four elements per thread as vectors when VEC (n % 4 == 0, aligned), else one.
+template <typename TS, typename TD, bool VEC>
 __global__ __launch_bounds__(256) void convert_kernel(const TS* __restrict__ src, int64_t n,
                                                       TD* __restrict__ dst) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i < n) dst[i] = Elem<TD>::from_f32(Elem<TS>::to_f32(src[i]));
+  if constexpr (VEC) {
+    if (4 * i < n) {
+      float v[4];
+      load4(src + 4 * i, v);
+      store4(dst + 4 * i, v);
+    }
+  } else {
+    if (i < n) dst[i] = Elem<TD>::from_f32(Elem<TS>::to_f32(src[i]));
+  }
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
@@ -552,8 +561,15 @@ hipError_t transpose(const TS* src, int64_t lds_, int R, int C, int Rp, int64_t 
 
 template <typename TS, typename TD>
 hipError_t convert(const TS* src, int64_t n, TD* dst, hipStream_t s) {
-  hipLaunchKernelGGL((convert_kernel<TS, TD>), dim3(static_cast<unsigned>((n + 255) / 256)),
-                     dim3(256), 0, s, src, n, dst);
+  const bool vec = n % 4 == 0 && (reinterpret_cast<uintptr_t>(src) % (4 * sizeof(TS))) == 0 &&
+                   (reinterpret_cast<uintptr_t>(dst) % (4 * sizeof(TD))) == 0;
+  if (vec)
+    hipLaunchKernelGGL((convert_kernel<TS, TD, true>),
+                       dim3(static_cast<unsigned>((n / 4 + 255) / 256)), dim3(256), 0, s, src, n,
+                       dst);
+  else
+    hipLaunchKernelGGL((convert_kernel<TS, TD, false>), dim3(static_cast<unsigned>((n + 255) / 256)),
+                       dim3(256), 0, s, src, n, dst);
   return hipGetLastError();
 }
 

@@ -119,6 +119,16 @@ size_t gemm_bf16_splitk_ws_bytes(int M, int N, int K);
 template <class Epi>
 hipError_t gemm_bf16_splitk(const bf16_t* a, int lda, const bf16_t* b, int M, int N, int K,
                             const Epi& epi, float* ws, hipStream_t s);
+// C[m][n] = sum_k A(m, k) B(n, k) with B stored K-major (element (n, k) at
+// b[k * ldb + n]) and A stored K-major (a[k * lda + m]) when ``a_kmajor``, else
+// K-contiguous (a[m * lda + k]).  K is a multiple of 32; reduction indices at or
+// past k_rows (<= K) count as zeros and are not read (k_rows < K needs both
+// operands K-major).  lda and ldb are multiples of 8, a and b 16-byte aligned, N % 4
+// == 0; hipErrorInvalidValue otherwise.  The reduction is split as in
+// gemm_bf16_splitk, its partials in ``ws`` (gemm_bf16_splitk_ws_bytes(M, N, K)).
+template <class Epi>
+hipError_t gemm_bf16_km(const bf16_t* a, int lda, bool a_kmajor, const bf16_t* b, int ldb, int M,
+                        int N, int K, int k_rows, const Epi& epi, float* ws, hipStream_t s);
 // Small-M product (M <= 8), one wave per output column: the decode path.
 template <typename T, class Epi>
 hipError_t gemv(const T* a, int lda, int M, const T* b0, const T* b1, int n_split, int N, int K,

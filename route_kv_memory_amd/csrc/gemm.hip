@@ -1,5 +1,7 @@
 // Dense NT products on gfx950: bf16 MFMA tiles, a plain fp32 tiled kernel and a
 // small-M (decode) kernel.
+#include <utility>
+
 #include "gemm.h"
 
 namespace mka {
@@ -33,6 +35,47 @@ struct GemmCfg {
   static constexpr int WN = BN / (NW / 2);                  // wave tile: 128 x WN
   static constexpr int NB = WN / 32;                        // MFMA blocks per wave in N
 };
+
+// The epilogue of a workgroup's tile: lane (h, l32) of wave (wm, wn) holds
+// output row m = m0 + wm*128 + 32i + l32 and columns n = n0 + wn*WN + 32j +
+// 8*(r/4) + 4h + (r%4) of accumulator acc[i][j][r].
+template <int NB, int WN, class Epi>
+__device__ __forceinline__ void gemm_store(const f32x16 (&acc)[4][NB], int m0, int n0, int wm,
+                                           int wn, int h, int l32, int M, int N, const Epi& epi) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + wm * 128 + i * 32 + l32;
+    if (m >= M) continue;
+    if constexpr (std::is_same<Epi, EpiAdd>::value) {
+      // accumulate: the row's 4*NB quads are read together, then written
+      float old[NB][4][4];
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq)
+          epi.load4(m, n0 + wn * WN + j * 32 + 8 * rq + 4 * h, N, old[j][rq]);
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = old[j][rq][e] + acc[i][j][4 * rq + e];
+          epi.put4(m, n0 + wn * WN + j * 32 + 8 * rq + 4 * h, v, N);
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int n = n0 + wn * WN + j * 32 + 8 * rq + 4 * h;
+          const float v[4] = {acc[i][j][4 * rq], acc[i][j][4 * rq + 1], acc[i][j][4 * rq + 2],
+                              acc[i][j][4 * rq + 3]};
+          epi.store4(m, n, v, N);
+        }
+    }
+  }
+}
 
 // blockIdx.y selects a range of K_len reduction indices starting at
 // blockIdx.y * K_len (split-K; K is the row length of B).  DB: fragments
@@ -222,40 +265,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_bf16_kernel(
 
   }
 
-  // Lane holds output row m = ... + l32 and columns n = ... + 8*(r/4) + 4h + (r%4).
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + wm * 128 + i * 32 + l32;
-    if (m >= M) continue;
-    if constexpr (std::is_same<Epi, EpiAdd>::value) {
-      // accumulate: the row's 4*NB quads are read together, then written
-      float old[NB][4][4];
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq)
-          epi.load4(m, n0 + wn * WN + j * 32 + 8 * rq + 4 * h, N, old[j][rq]);
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = old[j][rq][e] + acc[i][j][4 * rq + e];
-          epi.put4(m, n0 + wn * WN + j * 32 + 8 * rq + 4 * h, v, N);
-        }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int n = n0 + wn * WN + j * 32 + 8 * rq + 4 * h;
-          const float v[4] = {acc[i][j][4 * rq], acc[i][j][4 * rq + 1], acc[i][j][4 * rq + 2],
-                              acc[i][j][4 * rq + 3]};
-          epi.store4(m, n, v, N);
-        }
-    }
-  }
+  gemm_store<NB, WN>(acc, m0, n0, wm, wn, h, l32, M, N, epi);
 }
 
 constexpr int kGemmWaves256 = 8;
@@ -277,6 +287,258 @@ hipError_t gemm_bf16(const bf16_t* a, int lda, const bf16_t* b0, const bf16_t* b
                        b0, b1, n_split, M, N, K, K, epi);
   }
   return hipGetLastError();
+}
+
+// f(std::integral_constant<int, 0>{}) .. f(std::integral_constant<int, N-1>{}).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// ---------------------------------------------------------------------------
+// The same product with operands stored K-major: an operand marked so is given
+// as [K][rows] (its rows contiguous along the output dimension, ``ld`` apart
+// per reduction index), e.g. the token-major activations of a weight gradient
+// dW = dY^T X or a weight [in][out] used as stored.  Both operands stream
+// global -> LDS through buffer resources (direct loads, 16 bytes per lane):
+// - a K-major slice is stored as its 32 reduction rows of BM (or BN) values;
+//   16-byte chunk c of slice row kr sits at chunk position c ^ 4*(kr % 4);
+// - its MFMA fragment (8 consecutive reduction indices of one output row per
+//   lane) comes from two transposing LDS reads (ds_read_b64_tr_b16): in each
+//   16-lane group, lane r addresses slice row kb + r/4 at output rows
+//   mb + 4*(r%4) .. +3, and lane i receives output row mb + i at slice rows
+//   kb .. kb+3.  Within each 32-lane half the 4 slice rows x 64 bytes read fall
+//   in distinct banks.
+// - K-major reduction rows at or past ``k_rows`` read as zeros (the buffer
+//   range ends there), so K_len may run past the valid rows; output rows past
+//   M (or N) read whatever follows in memory and are not stored.
+// K-contiguous operands use the swizzled row layout of gemm_bf16_kernel.
+// ---------------------------------------------------------------------------
+template <int BN, bool AK, bool BKM, class Epi>
+__global__ __launch_bounds__(512) void gemm_bf16_km_kernel(
+    const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B, int ldb, int M, int N,
+    int K_len, int k_rows, Epi epi) {
+  constexpr int NW = 8;
+  using C = GemmCfg<BN, NW>;
+  constexpr int BM = C::BM, BK = C::BK, ROWB = C::ROWB, NB = C::NB;
+  constexpr int WN = C::WN;
+  // An even number of stages, each a shared object of its own: the loop is
+  // unrolled over the ring, so every load and read names its stage at
+  // compile time and the compiler can see that a slice's loads do not write
+  // the stage being read (otherwise it waits for all loads in flight before
+  // each transposing read).
+  constexpr int STAGES = BN == 256 ? 4 : 6;
+  constexpr int A_RB = BM * 2, B_RB = BN * 2;  // bytes per K-major slice row
+  static_assert(C::LOADS * NW * 1024 == C::SLICE, "slice must split evenly over the waves");
+  static_assert(STAGES * C::SLICE <= 160 * 1024, "the ring fits the LDS");
+  __shared__ __attribute__((aligned(1024))) unsigned char ra0[C::A_BYTES], rb0[C::B_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char ra1[C::A_BYTES], rb1[C::B_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char ra2[C::A_BYTES], rb2[C::B_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char ra3[C::A_BYTES], rb3[C::B_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char ra4[STAGES > 4 ? C::A_BYTES : 16],
+      rb4[STAGES > 4 ? C::B_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char ra5[STAGES > 5 ? C::A_BYTES : 16],
+      rb5[STAGES > 5 ? C::B_BYTES : 16];
+  // stage u's A and B operands
+  auto stage_a = [&](auto u) -> unsigned char* {
+    constexpr int k = decltype(u)::value % STAGES;
+    if constexpr (k == 0) return ra0;
+    else if constexpr (k == 1) return ra1;
+    else if constexpr (k == 2) return ra2;
+    else if constexpr (k == 3) return ra3;
+    else if constexpr (k == 4) return ra4;
+    else return ra5;
+  };
+  auto stage_b = [&](auto u) -> unsigned char* {
+    constexpr int k = decltype(u)::value % STAGES;
+    if constexpr (k == 0) return rb0;
+    else if constexpr (k == 1) return rb1;
+    else if constexpr (k == 2) return rb2;
+    else if constexpr (k == 3) return rb3;
+    else if constexpr (k == 4) return rb4;
+    else return rb5;
+  };
+
+  const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
+  int tm, tn;
+  if (tiles_m % 4 == 0 && tiles_n % 2 == 0) {
+    const int xcd = blockIdx.x % 8, local = blockIdx.x / 8, bn = tiles_n / 2;
+    tm = (xcd >> 1) * (tiles_m / 4) + local / bn;
+    tn = (xcd & 1) * bn + local % bn;
+  } else {
+    const int item = xcd_contiguous(blockIdx.x, tiles_n * tiles_m);
+    tm = item / tiles_n;
+    tn = item % tiles_n;
+  }
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int k_begin = blockIdx.y * K_len;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1, h = lane >> 5, l32 = lane & 31;
+
+  // Load instruction j of this wave: operand (A first), LDS offset, and the
+  // lane's byte offset from the slice's resource base (the same every slice).
+  bool is_a[C::LOADS];
+  int dst[C::LOADS];
+  uint32_t voff[C::LOADS];
+#pragma unroll
+  for (int j = 0; j < C::LOADS; ++j) {
+    const int gi = wave * C::LOADS + j;
+    is_a[j] = gi < C::A_BYTES / 1024;
+    const int ri = is_a[j] ? gi : gi - C::A_BYTES / 1024;
+    dst[j] = ri * 1024;  // within the operand's stage buffer
+    const bool km = is_a[j] ? AK : BKM;
+    const int rb = is_a[j] ? A_RB : B_RB, ld = is_a[j] ? lda : ldb;
+    if (km) {
+      const int kr = ri * (1024 / rb) + (16 * lane) / rb, c = (16 * lane % rb) / 16;
+      voff[j] = static_cast<uint32_t>(kr * ld * 2 + 16 * (c ^ (4 * (kr & 3))));
+    } else {
+      const int row = 16 * ri + (lane >> 2);
+      const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+      const int r0 = is_a[j] ? m0 : n0, rows = is_a[j] ? M : N;
+      voff[j] = static_cast<uint32_t>((min(r0 + row, rows - 1) - r0) * ld * 2 + chunk * 16);
+    }
+  }
+  // The resources of slice `slice`: K-major ones end after the last valid
+  // reduction row.  Base and size go through readfirstlane so that the
+  // resource lives in scalar registers (the clamp is a vector instruction,
+  // and a resource in vector registers makes every load a loop over lanes).
+  auto rsrc = [&](bool km, const bf16_t* X, int ld, int r0, int slice) {
+    const int k0 = k_begin + slice * BK;
+    const bf16_t* p;
+    uint32_t bytes;
+    if (km) {
+      const int rows = max(0, min(BK, k_rows - k0));
+      bytes = rows > 0 ? static_cast<uint32_t>((static_cast<int64_t>(rows) * ld - r0) * 2) : 0u;
+      p = X + static_cast<int64_t>(k0) * ld + r0;
+    } else {
+      bytes = 0xFFFFFFFFu;
+      p = X + static_cast<int64_t>(r0) * ld + k0;
+    }
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+    return make_rsrc(reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo),
+                     __builtin_amdgcn_readfirstlane(bytes));
+  };
+  auto issue = [&](int slice, unsigned char* abase, unsigned char* bbase) {
+    const __amdgpu_buffer_rsrc_t ra = rsrc(AK, A, lda, m0, slice);
+    const __amdgpu_buffer_rsrc_t rb = rsrc(BKM, B, ldb, n0, slice);
+#pragma unroll
+    for (int j = 0; j < C::LOADS; ++j) {
+      if (wave * C::LOADS + j < C::A_BYTES / 1024)  // uniform: a scalar branch
+        buffer_load_lds16(ra, (lds_void_t*)(abase + dst[j]), voff[j]);
+      else
+        buffer_load_lds16(rb, (lds_void_t*)(bbase + dst[j]), voff[j]);
+    }
+  };
+
+  f32x16 acc[4][NB];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
+
+  // K-contiguous fragment: 8 reduction indices (chunk c) of slice row r.
+  auto frag = [](const unsigned char* Xs, int r, int c) {
+    return *reinterpret_cast<const bf16x8*>(Xs + r * ROWB + ((c ^ ((r >> 2) & 3)) << 4));
+  };
+  // K-major fragment: output rows rb0 + l32, reduction indices 16ks + 8h ..
+  const int tq = lane >> 4, tr = lane & 15;
+  auto frag_km = [&](const unsigned char* Xs, int row_bytes, int rb0, int ks) {
+    bf16x4 v[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int kr = 16 * ks + 8 * (tq >> 1) + 4 * t + (tr >> 2);
+      const int m = rb0 + 16 * (tq & 1) + 4 * (tr & 3);
+      v[t] = ds_read_tr16_b64(reinterpret_cast<const bf16_t*>(
+          Xs + kr * row_bytes + (((m >> 3) ^ (4 * (kr & 3))) << 4) + (m & 7) * 2));
+    }
+    return bf16x8{v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
+  };
+
+  const int nk = K_len / BK;
+  static_for<STAGES>([&](auto u) {
+    if (decltype(u)::value < nk) issue(decltype(u)::value, stage_a(u), stage_b(u));
+  });
+  // Fragments double-buffered in registers, as in gemm_bf16_kernel.
+  typedef bf16x8 FragA[2][4];
+  typedef bf16x8 FragB[2][NB];
+  auto read_slice = [&](const unsigned char* As, const unsigned char* Bs, FragA& fa, FragB& fb) {
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        fa[ks][i] = AK ? frag_km(As, A_RB, wm * 128 + i * 32, ks)
+                       : frag(As, wm * 128 + i * 32 + l32, 2 * ks + h);
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        fb[ks][j] = BKM ? frag_km(Bs, B_RB, wn * WN + j * 32, ks)
+                        : frag(Bs, wn * WN + j * 32 + l32, 2 * ks + h);
+    }
+  };
+  // Slice kt (kt % STAGES == u): wait for slice kt+1, barrier, refill stage u
+  // with slice kt+STAGES, read slice kt+1's fragments while the MFMAs consume
+  // slice kt's.  After the last slice the read takes a stale stage and is
+  // not used.
+  auto step = [&](auto u, int kt, const FragA& ca, const FragB& cb, FragA& na, FragB& nb) {
+    constexpr int U = decltype(u)::value;
+    if (kt + STAGES - 1 < nk) {
+      __builtin_amdgcn_s_waitcnt(kVmcntPending<C::LOADS * (STAGES - 2)>());
+    } else {
+      __builtin_amdgcn_s_waitcnt(kVmcntPending<0>());
+    }
+    __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
+    __builtin_amdgcn_s_barrier();
+    if (kt + STAGES < nk) issue(kt + STAGES, stage_a(u), stage_b(u));
+    read_slice(stage_a(std::integral_constant<int, U + 1>{}),
+               stage_b(std::integral_constant<int, U + 1>{}), na, nb);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma32x32x16(cb[ks][j], ca[ks][i], acc[i][j]);
+    // one LDS read after each MFMA, the rest at the end (a K-major fragment
+    // is two reads)
+    constexpr int R = (BK / 16) * ((AK ? 2 : 1) * 4 + (BKM ? 2 : 1) * NB);
+    constexpr int F = (BK / 16) * 4 * NB;
+    constexpr int P = R < F ? R : F;
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if constexpr (F > P) __builtin_amdgcn_sched_group_barrier(0x008, F - P, 0);
+    if constexpr (R > P) __builtin_amdgcn_sched_group_barrier(0x100, R - P, 0);
+  };
+  FragA xa, ya;
+  FragB xb, yb;
+  if (STAGES - 1 < nk) {
+    __builtin_amdgcn_s_waitcnt(kVmcntPending<C::LOADS * (STAGES - 1)>());
+  } else {
+    __builtin_amdgcn_s_waitcnt(kVmcntPending<0>());
+  }
+  __builtin_amdgcn_s_barrier();
+  read_slice(ra0, rb0, xa, xb);
+  for (int k0 = 0; k0 < nk; k0 += STAGES) {
+    static_for<STAGES>([&](auto u) {
+      constexpr int U = decltype(u)::value;
+      if (k0 + U < nk) {
+        if constexpr (U % 2 == 0)
+          step(u, k0 + U, xa, xb, ya, yb);
+        else
+          step(u, k0 + U, ya, yb, xa, xb);
+      }
+    });
+  }
+
+  gemm_store<NB, WN>(acc, m0, n0, wm, wn, h, l32, M, N, epi);
 }
 
 // ---------------------------------------------------------------------------
@@ -345,6 +607,44 @@ hipError_t gemm_bf16_splitk(const bf16_t* a, int lda, const bf16_t* b, int M, in
   const int64_t quads = (static_cast<int64_t>(M) * N + 3) / 4;
   hipLaunchKernelGGL((splitk_sum_kernel<Epi>), dim3(static_cast<unsigned>((quads + 255) / 256)),
                      dim3(256), 0, s, ws, S, M, N, epi);
+  return hipGetLastError();
+}
+
+template <class Epi>
+hipError_t gemm_bf16_km(const bf16_t* a, int lda, bool a_kmajor, const bf16_t* b, int ldb, int M,
+                        int N, int K, int k_rows, const Epi& epi, float* ws, hipStream_t s) {
+  const bool aligned = ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b)) & 15) == 0;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 32 != 0 || N % 4 != 0 || lda % 8 != 0 || ldb % 8 != 0 ||
+      !aligned || k_rows < 0 || k_rows > K || (a_kmajor && lda < M) || ldb < N ||
+      (!a_kmajor && k_rows != K))
+    return hipErrorInvalidValue;
+  const int S = gemm_splitk_ranges(M, N, K);
+  const int tm = (M + 255) / 256;
+  auto run = [&](auto kernel, int tiles, int ranges, auto e) {
+    hipLaunchKernelGGL(kernel, dim3(tiles, ranges), dim3(512), 0, s, a, lda, b, ldb, M, N,
+                       K / ranges, k_rows, e);
+  };
+  if (S > 1) {
+    const int tiles = ((N + 127) / 128) * tm;
+    const EpiPart part{ws, N, static_cast<int64_t>(M) * N};
+    if (a_kmajor)
+      run(gemm_bf16_km_kernel<128, true, true, EpiPart>, tiles, S, part);
+    else
+      run(gemm_bf16_km_kernel<128, false, true, EpiPart>, tiles, S, part);
+    const int64_t quads = (static_cast<int64_t>(M) * N + 3) / 4;
+    hipLaunchKernelGGL((splitk_sum_kernel<Epi>), dim3(static_cast<unsigned>((quads + 255) / 256)),
+                       dim3(256), 0, s, ws, S, M, N, epi);
+  } else if (((N + 255) / 256) * tm >= 256) {
+    if (a_kmajor)
+      run(gemm_bf16_km_kernel<256, true, true, Epi>, ((N + 255) / 256) * tm, 1, epi);
+    else
+      run(gemm_bf16_km_kernel<256, false, true, Epi>, ((N + 255) / 256) * tm, 1, epi);
+  } else {
+    if (a_kmajor)
+      run(gemm_bf16_km_kernel<128, true, true, Epi>, ((N + 127) / 128) * tm, 1, epi);
+    else
+      run(gemm_bf16_km_kernel<128, false, true, Epi>, ((N + 127) / 128) * tm, 1, epi);
+  }
   return hipGetLastError();
 }
 
@@ -495,6 +795,11 @@ template hipError_t gemm_bf16_splitk<EpiStore<float>>(const bf16_t*, int, const 
                                                       hipStream_t);
 template hipError_t gemm_bf16_splitk<EpiAdd>(const bf16_t*, int, const bf16_t*, int, int, int,
                                              const EpiAdd&, float*, hipStream_t);
+template hipError_t gemm_bf16_km<EpiStore<float>>(const bf16_t*, int, bool, const bf16_t*, int,
+                                                   int, int, int, int, const EpiStore<float>&,
+                                                   float*, hipStream_t);
+template hipError_t gemm_bf16_km<EpiAdd>(const bf16_t*, int, bool, const bf16_t*, int, int, int,
+                                          int, int, const EpiAdd&, float*, hipStream_t);
 template hipError_t gemm_f32<EpiAdd>(const float*, int, const float*, const float*, int, int, int,
                                      int, const EpiAdd&, hipStream_t);
 template hipError_t gemm_f32<EpiStore<float>>(const float*, int, const float*, const float*, int,

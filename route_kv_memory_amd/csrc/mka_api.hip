@@ -558,19 +558,21 @@ BwdWs bwd_layout(const mka_dims* d) {
   w.heads = bf ? take(attn_bwd_mfma_ws_bytes(d->batch, d->seq, d->n_heads, d->n_kv_heads,
                                              d->head_dim))
                : 0;
+  // bf16 layers read the token-major rows as K-major product operands; the
+  // transposed copies are for float32 layers only
   w.dkv_a = bf ? take(el * M * 2 * kvw) : 0;
-  w.dkv_t = take(el * 2 * kvw * Mp);
+  w.dkv_t = bf ? 0 : take(el * 2 * kvw * Mp);
   w.wkv_t = take(el * D * 2 * kvw);
   w.xf = take(el * M * D);
-  w.xf_t = take(el * D * Mp);
+  w.xf_t = bf ? 0 : take(el * D * Mp);
   w.dpre = take(el * M * r);
-  w.dpre_t = take(el * r * Mp);
-  w.q_t = take(el * qw * Mp);
-  w.wr1_t = take(el * qw * r);
-  w.wq_t = take(el * D * qw);
+  w.dpre_t = bf ? 0 : take(el * r * Mp);
+  w.q_t = bf ? 0 : take(el * qw * Mp);
+  w.wr1_t = bf ? 0 : take(el * qw * r);
+  w.wq_t = bf ? 0 : take(el * D * qw);
   w.dq_a = bf ? take(el * M * qw) : 0;
-  w.dq_t = take(el * qw * Mp);
-  w.x_t = take(el * D * Mp);
+  w.dq_t = bf ? 0 : take(el * qw * Mp);
+  w.x_t = bf ? 0 : take(el * D * Mp);
   if (bf) {  // the largest split-K partials among the products below
     const int m = static_cast<int>(M), mp = w.Mp, dd = static_cast<int>(D);
     const int q = static_cast<int>(qw), kv = static_cast<int>(kvw), rr = static_cast<int>(r);
@@ -664,11 +666,12 @@ int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const
   // [K|V] = X_fused [W_k|W_v]^T: dX_fused = dKV [W_k; W_v]; dW = dKV^T X_fused
   MKA_LAUNCH("bwd/t", (transpose<T, T>(wk, D, kvw, D, kvw, 2 * kvw, wkv_t, s)));
   MKA_LAUNCH("bwd/t", (transpose<T, T>(wv, D, kvw, D, kvw, 2 * kvw, wkv_t + kvw, s)));
-  // dkv in the storage type, as rows (dX_fused product) and transposed (weight
-  // gradients), from one read
+  // dkv in the storage type: as rows (bf16: the products read the token-major
+  // rows directly, K-major where the reduction runs over tokens), or also
+  // transposed (float32 products)
   if constexpr (kBf)
-    MKA_LAUNCH("bwd/t", (transpose_copy<float, T>(dkv, 2 * kvw, M, 2 * kvw, Mp, Mp, dkv_t,
-                                                  const_cast<T*>(dkv_a), s)));
+    MKA_LAUNCH("bwd/cvt", (convert<float, T>(dkv, static_cast<int64_t>(M) * 2 * kvw,
+                                             const_cast<T*>(dkv_a), s)));
   else
     MKA_LAUNCH("bwd/t", (transpose<float, T>(dkv, 2 * kvw, M, 2 * kvw, Mp, Mp, dkv_t, s)));
   MKA_LAUNCH("bwd/dxf", gemm_t<T>(dkv_a, 2 * kvw, wkv_t, M, D, 2 * kvw, EpiStore<float>{dxf, D}, sk, s));
@@ -678,10 +681,17 @@ int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const
                                         fwd->lambda, B, N, D, d->top_r, rt, xf, s));
     xf_src = xf;
   }
-  MKA_LAUNCH("bwd/t", (transpose<T, T>(xf_src, D, M, D, Mp, Mp, xf_t, s)));
-  MKA_LAUNCH("bwd/dwk", gemm_t<T>(dkv_t, Mp, xf_t, kvw, D, Mp, EpiStore<float>{gr->dw_k, D}, sk, s));
-  MKA_LAUNCH("bwd/dwv", gemm_t<T>(dkv_t + static_cast<size_t>(kvw) * Mp, Mp, xf_t, kvw, D, Mp,
-                                  EpiStore<float>{gr->dw_v, D}, sk, s));
+  if constexpr (kBf) {
+    MKA_LAUNCH("bwd/dwk", gemm_bf16_km(dkv_a, 2 * kvw, true, xf_src, D, kvw, D, Mp, M,
+                                       EpiStore<float>{gr->dw_k, D}, sk, s));
+    MKA_LAUNCH("bwd/dwv", gemm_bf16_km(dkv_a + kvw, 2 * kvw, true, xf_src, D, kvw, D, Mp, M,
+                                       EpiStore<float>{gr->dw_v, D}, sk, s));
+  } else {
+    MKA_LAUNCH("bwd/t", (transpose<T, T>(xf_src, D, M, D, Mp, Mp, xf_t, s)));
+    MKA_LAUNCH("bwd/dwk", gemm_t<T>(dkv_t, Mp, xf_t, kvw, D, Mp, EpiStore<float>{gr->dw_k, D}, sk, s));
+    MKA_LAUNCH("bwd/dwv", gemm_t<T>(dkv_t + static_cast<size_t>(kvw) * Mp, Mp, xf_t, kvw, D, Mp,
+                                    EpiStore<float>{gr->dw_v, D}, sk, s));
+  }
   // the fusion, the EMA's adjoint and the block means' adjoint
   MKA_LAUNCH("bwd/fuse", fuse_bwd<T>(x, rt.l2() ? fwd->l2 : nullptr, st->block_means, st->nb_cap,
                                      rt.l3() ? fwd->idx : nullptr, fwd->lambda, B, N, D,
@@ -698,25 +708,37 @@ int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const
     MKA_LAUNCH("bwd/pre", gemm_t<T>(q, qw, wr1, M, r, qw, EpiStore<float>{pre, r}, sk, s));
     MKA_LAUNCH("bwd/router", router_bwd<T>(fwd->lambda, dlam, pre, wr2, r, M, rt, dz, dpre,
                                            gr->dw_r2, s));
-    MKA_LAUNCH("bwd/t", (transpose<T, T>(dpre, r, M, r, Mp, Mp, dpre_t, s)));
-    MKA_LAUNCH("bwd/t", (transpose<T, T>(q, qw, M, qw, Mp, Mp, q_t, s)));
-    MKA_LAUNCH("bwd/dwr1", gemm_t<T>(dpre_t, Mp, q_t, r, qw, Mp, EpiStore<float>{gr->dw_r1, qw}, sk, s));
-    MKA_LAUNCH("bwd/t", (transpose<T, T>(wr1, qw, r, qw, r, r, wr1_t, s)));
-    MKA_LAUNCH("bwd/dqr", gemm_t<T>(dpre, r, wr1_t, M, qw, r, EpiAdd{dq, qw}, sk, s));
+    if constexpr (kBf) {
+      MKA_LAUNCH("bwd/dwr1", gemm_bf16_km(dpre, r, true, q, qw, r, qw, Mp, M,
+                                          EpiStore<float>{gr->dw_r1, qw}, sk, s));
+      MKA_LAUNCH("bwd/dqr", gemm_bf16_km(dpre, r, false, wr1, qw, M, qw, r, r, EpiAdd{dq, qw}, sk,
+                                         s));
+    } else {
+      MKA_LAUNCH("bwd/t", (transpose<T, T>(dpre, r, M, r, Mp, Mp, dpre_t, s)));
+      MKA_LAUNCH("bwd/t", (transpose<T, T>(q, qw, M, qw, Mp, Mp, q_t, s)));
+      MKA_LAUNCH("bwd/dwr1", gemm_t<T>(dpre_t, Mp, q_t, r, qw, Mp, EpiStore<float>{gr->dw_r1, qw}, sk, s));
+      MKA_LAUNCH("bwd/t", (transpose<T, T>(wr1, qw, r, qw, r, r, wr1_t, s)));
+      MKA_LAUNCH("bwd/dqr", gemm_t<T>(dpre, r, wr1_t, M, qw, r, EpiAdd{dq, qw}, sk, s));
+    }
   } else {
     MKA_LAUNCH("bwd/zero", fill_zero(gr->dw_r1, static_cast<int64_t>(r) * qw, s));
     MKA_LAUNCH("bwd/zero", fill_zero(gr->dw_r2, 3 * r, s));
   }
   // Q = x W_q^T: dx += dq W_q; dW_q = dq^T x
-  MKA_LAUNCH("bwd/t", (transpose<T, T>(wq, D, qw, D, qw, qw, wq_t, s)));
-  if constexpr (kBf)
-    MKA_LAUNCH("bwd/t", (transpose_copy<float, T>(dq, qw, M, qw, Mp, Mp, dq_t,
-                                                  const_cast<T*>(dq_a), s)));
-  else
+  if constexpr (kBf) {
+    MKA_LAUNCH("bwd/cvt", (convert<float, T>(dq, static_cast<int64_t>(M) * qw,
+                                             const_cast<T*>(dq_a), s)));
+    MKA_LAUNCH("bwd/dx", gemm_bf16_km(dq_a, qw, false, wq, D, M, D, qw, qw, EpiAdd{gr->dx, D}, sk,
+                                      s));
+    MKA_LAUNCH("bwd/dwq", gemm_bf16_km(dq_a, qw, true, x, D, qw, D, Mp, M,
+                                       EpiStore<float>{gr->dw_q, D}, sk, s));
+  } else {
+    MKA_LAUNCH("bwd/t", (transpose<T, T>(wq, D, qw, D, qw, qw, wq_t, s)));
     MKA_LAUNCH("bwd/t", (transpose<float, T>(dq, qw, M, qw, Mp, Mp, dq_t, s)));
-  MKA_LAUNCH("bwd/dx", gemm_t<T>(dq_a, qw, wq_t, M, D, qw, EpiAdd{gr->dx, D}, sk, s));
-  MKA_LAUNCH("bwd/t", (transpose<T, T>(x, D, M, D, Mp, Mp, x_t, s)));
-  MKA_LAUNCH("bwd/dwq", gemm_t<T>(dq_t, Mp, x_t, qw, D, Mp, EpiStore<float>{gr->dw_q, D}, sk, s));
+    MKA_LAUNCH("bwd/dx", gemm_t<T>(dq_a, qw, wq_t, M, D, qw, EpiAdd{gr->dx, D}, sk, s));
+    MKA_LAUNCH("bwd/t", (transpose<T, T>(x, D, M, D, Mp, Mp, x_t, s)));
+    MKA_LAUNCH("bwd/dwq", gemm_t<T>(dq_t, Mp, x_t, qw, D, Mp, EpiStore<float>{gr->dw_q, D}, sk, s));
+  }
   return MKA_OK;
 }
 
