@@ -397,21 +397,35 @@ __global__ __launch_bounds__(256) void block_gather_kernel(const float* __restri
 // ---------------------------------------------------------------------------
 constexpr int kBwdChunk = 64;
 
-// u_t = lambda_2[t] * dxf[t] (lam2 = &lambda[1], stride 3)
+// u_t = lambda_2[t] * dxf[t] (lam2 = &lambda[1], stride 3).  Each thread takes
+// 4 channels (D % 4 == 0); the loads of kAdjUnroll tokens are issued before
+// their sequential updates.
+constexpr int kAdjUnroll = 8;
+
 __global__ __launch_bounds__(256) void ema_adj_pass1(const float* __restrict__ u,
                                                      const float* __restrict__ lam2, int N, int D,
                                                      int n_chunks, float beta,
                                                      float* __restrict__ part) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
   const int ch = blockIdx.y, b = blockIdx.z;
   if (c >= D) return;
   const int t0 = ch * kBwdChunk, t1 = min(N, t0 + kBwdChunk);
-  float g = 0.f;
-  for (int t = t1 - 1; t >= t0; --t) {
-    const int64_t row = static_cast<int64_t>(b) * N + t;
-    g = fmaf(beta, g, lam2[row * 3] * u[row * D + c]);
+  float g[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int tb = t1 - 1; tb >= t0; tb -= kAdjUnroll) {
+    float uv[kAdjUnroll][4], lw[kAdjUnroll];
+#pragma unroll
+    for (int k = 0; k < kAdjUnroll; ++k) {  // tokens before the chunk re-read its first (unused)
+      const int64_t row = static_cast<int64_t>(b) * N + max(tb - k, t0);
+      lw[k] = lam2[row * 3];
+      load4(u + row * D + c, uv[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < kAdjUnroll; ++k)
+      if (tb - k >= t0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) g[i] = fmaf(beta, g[i], lw[k] * uv[k][i]);
   }
-  part[(static_cast<int64_t>(b) * n_chunks + ch) * D + c] = g;
+  store4(part + (static_cast<int64_t>(b) * n_chunks + ch) * D + c, g);
 }
 
 __global__ __launch_bounds__(256) void ema_adj_pass2(float* __restrict__ part, int N, int D,
@@ -436,19 +450,41 @@ __global__ __launch_bounds__(256) void ema_adj_pass3(const float* __restrict__ u
                                                      const float* __restrict__ dm, int nbs,
                                                      int N, int D, int n_chunks, int block,
                                                      float beta, float* __restrict__ dx) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
   const int ch = blockIdx.y, b = blockIdx.z;
   if (c >= D) return;
   const int t0 = ch * kBwdChunk, t1 = min(N, t0 + kBwdChunk);
   const int n_full = (N / block) * block;  // tokens of complete blocks
   const float omb = 1.0f - beta, inv_bs = 1.0f / static_cast<float>(block);
-  float g = part[(static_cast<int64_t>(b) * n_chunks + ch) * D + c];
-  for (int t = t1 - 1; t >= t0; --t) {
-    const int64_t row = static_cast<int64_t>(b) * N + t, o = row * D + c;
-    g = fmaf(beta, g, lam2[row * 3] * u[o]);
-    float add = omb * g;
-    if (t < n_full) add += dm[(static_cast<int64_t>(b) * nbs + t / block) * D + c] * inv_bs;
-    dx[o] += add;
+  float g[4];
+  load4(part + (static_cast<int64_t>(b) * n_chunks + ch) * D + c, g);
+  for (int tb = t1 - 1; tb >= t0; tb -= kAdjUnroll) {
+    float uv[kAdjUnroll][4], xv[kAdjUnroll][4], mv[kAdjUnroll][4], lw[kAdjUnroll];
+#pragma unroll
+    for (int k = 0; k < kAdjUnroll; ++k) {  // tokens before the chunk re-read its first (unused)
+      const int t = max(tb - k, t0);
+      const int64_t row = static_cast<int64_t>(b) * N + t, o = row * D + c;
+      lw[k] = lam2[row * 3];
+      load4(u + o, uv[k]);
+      load4(dx + o, xv[k]);
+      // tokens of the incomplete last block take no block-mean term (row 0 read, unused)
+      load4(dm + (static_cast<int64_t>(b) * nbs + (t < n_full ? t / block : 0)) * D + c, mv[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < kAdjUnroll; ++k) {
+      const int t = tb - k;
+      if (t >= t0) {
+        float out[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          g[i] = fmaf(beta, g[i], lw[k] * uv[k][i]);
+          float add = omb * g[i];
+          if (t < n_full) add += mv[k][i] * inv_bs;
+          out[i] = xv[k][i] + add;
+        }
+        store4(dx + (static_cast<int64_t>(b) * N + t) * D + c, out);
+      }
+    }
   }
 }
 
@@ -631,11 +667,11 @@ hipError_t ema_adjoint_add(const float* u, const float* lam, const float* dm, in
                            int N, int D, int block, float beta, float* part, float* dx,
                            hipStream_t s) {
   const int n_chunks = (N + kBwdChunk - 1) / kBwdChunk;
-  const int cx = (D + 255) / 256;
-  hipLaunchKernelGGL(ema_adj_pass1, dim3(cx, n_chunks, B), dim3(256), 0, s, u, lam + 1, N, D,
+  const int cx = (D + 255) / 256, cx4 = (D / 4 + 255) / 256;  // D % 4 == 0
+  hipLaunchKernelGGL(ema_adj_pass1, dim3(cx4, n_chunks, B), dim3(256), 0, s, u, lam + 1, N, D,
                      n_chunks, beta, part);
   hipLaunchKernelGGL(ema_adj_pass2, dim3(cx, B), dim3(256), 0, s, part, N, D, n_chunks, beta);
-  hipLaunchKernelGGL(ema_adj_pass3, dim3(cx, n_chunks, B), dim3(256), 0, s, u, lam + 1, part, dm,
+  hipLaunchKernelGGL(ema_adj_pass3, dim3(cx4, n_chunks, B), dim3(256), 0, s, u, lam + 1, part, dm,
                      nbs,
                      N, D, n_chunks, block, beta, dx);
   return hipGetLastError();
