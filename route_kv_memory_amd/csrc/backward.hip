@@ -16,21 +16,28 @@
 namespace mka {
 
 // ---------------------------------------------------------------------------
-// D[m, h] = sum_d dO[m, h, d] * O[m, h, d]: one wave per (row, head).
+// D[m, h] = sum_d dO[m, h, d] * O[m, h, d]: LPR = DH / V lanes per (row, head),
+// V elements (16 bytes) per lane, the lanes' sums added by butterfly shuffles.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int DH>
 __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const T* __restrict__ O,
                                                             const T* __restrict__ dO, int64_t rows,
-                                                            int DH, float* __restrict__ dsum) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
-  const T* o = O + r * DH;
-  const T* g = dO + r * DH;
+                                                            float* __restrict__ dsum) {
+  constexpr int V = Vec16<T>::kN, LPR = DH / V, RPB = 256 / LPR;
+  static_assert(DH % V == 0 && LPR <= 64 && (LPR & (LPR - 1)) == 0, "lanes per row");
+  const int sub = threadIdx.x % LPR;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / LPR;
   float acc = 0.f;
-  for (int d = lane; d < DH; d += 64) acc = fmaf(Elem<T>::to_f32(o[d]), Elem<T>::to_f32(g[d]), acc);
-  acc = wave_sum(acc);
-  if (lane == 0) dsum[r] = acc;
+  if (r < rows) {
+    float o[V], g[V];
+    Vec16<T>::load(O + r * DH + sub * V, o);
+    Vec16<T>::load(dO + r * DH + sub * V, g);
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc = fmaf(o[i], g[i], acc);
+  }
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off /= 2) acc += __shfl_xor(acc, off);
+  if (r < rows && sub == 0) dsum[r] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -250,45 +257,65 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, i
 }
 
 // ---------------------------------------------------------------------------
-// Fusion backward, one row per workgroup.  X_fused = l1 x + l2 L2 + l3 L3:
-//   dlam_i = <dxf, L_i> (L3 re-formed from the retrieved means), dx = l1 dxf
-//   (written).  The L2 and L3 parts (l2 dxf and l3 dxf / |S_t|) are taken by
-//   the EMA adjoint and the block gather straight from dxf and lambda.
+// Fusion backward, one row per workgroup, 4 channels per thread (D % 4 == 0).
+// X_fused = l1 x + l2 L2 + l3 L3 with L3 the mean of the retrieved means:
+//   dlam_i = <dxf, L_i>, dx = l1 dxf (written), and, when xf is given,
+//   X_fused itself (re-formed as the fusion forms it: float32, rounded once),
+//   from the same reads of x, L2 and the retrieved means.  The L2 and L3
+//   parts of dx (l2 dxf and l3 dxf / |S_t|) are taken by the EMA adjoint and
+//   the block gather straight from dxf and lambda.  RMAX = 0: no L3 (idx is
+//   not read); l2 == nullptr: no L2.
 // ---------------------------------------------------------------------------
 template <typename T, int RMAX>
 __global__ __launch_bounds__(256) void fuse_bwd_kernel(
     const T* __restrict__ x, const float* __restrict__ l2, const float* __restrict__ means,
     int nb_cap, const int32_t* __restrict__ idx, const float* __restrict__ lam, int N, int D,
-    int R, const float* __restrict__ dxf, float* __restrict__ dx, float* __restrict__ dlam) {
+    int R, const float* __restrict__ dxf, float* __restrict__ dx, float* __restrict__ dlam,
+    T* __restrict__ xf) {
   __shared__ float red[3][4];
   const int64_t row = blockIdx.x;
   const int b = static_cast<int>(row / N);
   const int tid = threadIdx.x;
-  const float w1 = lam[row * 3 + 0];
-  int blk[RMAX], cnt = 0;
+  const float w1 = lam[row * 3 + 0], w2 = lam[row * 3 + 1], w3 = lam[row * 3 + 2];
+  int blk[RMAX > 0 ? RMAX : 1], cnt = 0;
 #pragma unroll
   for (int i = 0; i < RMAX; ++i) {
     blk[i] = i < R ? idx[row * R + i] : -1;
     cnt += blk[i] >= 0;
   }
-  const float inv = cnt ? 1.0f / static_cast<float>(cnt) : 0.f;
   const float* mb = means + static_cast<int64_t>(b) * nb_cap * D;
   float a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  for (int c = tid; c < D; c += 256) {
+  for (int c = 4 * tid; c < D; c += 4 * 256) {
     const int64_t o = row * D + c;
-    const float gx = dxf[o];
-    // every retrieved row is loaded (unfilled slots read block 0 and are not
-    // added), so the loads are in flight together
-    float m[RMAX];
+    float gx[4], xv[4], sv[4] = {0.f, 0.f, 0.f, 0.f}, mean[4] = {0.f, 0.f, 0.f, 0.f};
+    load4(dxf + o, gx);
+    load4(x + o, xv);
+    if (l2) load4(l2 + o, sv);
+    if constexpr (RMAX > 0) {
+      // every retrieved row is loaded (unfilled slots read block 0 and are
+      // not added), so the loads are in flight together; rank order
+      float m[RMAX][4];
 #pragma unroll
-    for (int i = 0; i < RMAX; ++i) m[i] = mb[static_cast<int64_t>(max(blk[i], 0)) * D + c];
-    float l3 = 0.f;
+      for (int i = 0; i < RMAX; ++i) load4(mb + static_cast<int64_t>(max(blk[i], 0)) * D + c, m[i]);
+      float l3[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < RMAX; ++i) l3 += blk[i] >= 0 ? m[i] : 0.f;
-    a1 = fmaf(gx, Elem<T>::to_f32(x[o]), a1);
-    if (l2) a2 = fmaf(gx, l2[o], a2);  // null: L2 disabled (lambda_2 = 0)
-    a3 = fmaf(gx, l3 * inv, a3);
-    dx[o] = w1 * gx;
+      for (int i = 0; i < RMAX; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) l3[k] += blk[i] >= 0 ? m[i][k] : 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) mean[k] = cnt ? l3[k] / static_cast<float>(cnt) : 0.f;
+    }
+    float d1[4], out[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      a1 = fmaf(gx[k], xv[k], a1);
+      a2 = fmaf(gx[k], sv[k], a2);
+      a3 = fmaf(gx[k], mean[k], a3);
+      d1[k] = w1 * gx[k];
+      out[k] = w1 * xv[k] + w2 * sv[k] + w3 * mean[k];
+    }
+    store4(dx + o, d1);
+    if (xf) store4(xf + o, out);
   }
   a1 = wave_sum(a1);
   a2 = wave_sum(a2);
@@ -543,8 +570,18 @@ __global__ __launch_bounds__(256) void router_dw2_kernel(const float* __restrict
 template <typename T>
 hipError_t attn_bwd_prep(const T* o, const T* d_o, int64_t rows, int dh, float* dsum,
                          hipStream_t s) {
-  hipLaunchKernelGGL(attn_bwd_prep_kernel<T>, dim3(static_cast<unsigned>((rows + 3) / 4)),
-                     dim3(256), 0, s, o, d_o, rows, dh, dsum);
+  auto launch = [&](auto kernel, int lanes_per_row) {
+    const int64_t per_block = 256 / lanes_per_row;
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>((rows + per_block - 1) / per_block)),
+                       dim3(256), 0, s, o, d_o, rows, dsum);
+  };
+  constexpr int V = Vec16<T>::kN;
+  if (dh == 128)
+    launch(attn_bwd_prep_kernel<T, 128>, 128 / V);
+  else if (dh == 64)
+    launch(attn_bwd_prep_kernel<T, 64>, 64 / V);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -619,20 +656,22 @@ hipError_t fill_zero(float* p, int64_t n, hipStream_t s) {
 template <typename T>
 hipError_t fuse_bwd(const T* x, const float* l2, const float* means, int nb_cap,
                     const int32_t* idx, const float* lam, int B, int N, int D, int R,
-                    const float* dxf, float* dx, float* dlam, hipStream_t s) {
+                    const float* dxf, float* dx, float* dlam, T* xf, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(B) * N));
-  if (R <= 4)
-    hipLaunchKernelGGL((fuse_bwd_kernel<T, 4>), grid, dim3(256), 0, s, x, l2, means, nb_cap, idx,
-                       lam, N, D, R, dxf, dx, dlam);
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, x, l2, means, nb_cap, idx, lam, N, D, R, dxf,
+                       dx, dlam, xf);
+  };
+  if (idx == nullptr || R == 0)
+    launch(fuse_bwd_kernel<T, 0>);
+  else if (R <= 4)
+    launch(fuse_bwd_kernel<T, 4>);
   else if (R <= 8)
-    hipLaunchKernelGGL((fuse_bwd_kernel<T, 8>), grid, dim3(256), 0, s, x, l2, means, nb_cap, idx,
-                       lam, N, D, R, dxf, dx, dlam);
+    launch(fuse_bwd_kernel<T, 8>);
   else if (R <= 16)
-    hipLaunchKernelGGL((fuse_bwd_kernel<T, 16>), grid, dim3(256), 0, s, x, l2, means, nb_cap, idx,
-                       lam, N, D, R, dxf, dx, dlam);
+    launch(fuse_bwd_kernel<T, 16>);
   else
-    hipLaunchKernelGGL((fuse_bwd_kernel<T, 32>), grid, dim3(256), 0, s, x, l2, means, nb_cap, idx,
-                       lam, N, D, R, dxf, dx, dlam);
+    launch(fuse_bwd_kernel<T, 32>);
   return hipGetLastError();
 }
 
@@ -694,7 +733,7 @@ hipError_t router_bwd(const float* lam, const float* dlam, const float* pre, con
   template hipError_t convert<float, T>(const float*, int64_t, T*, hipStream_t);                 \
   template hipError_t fuse_bwd<T>(const T*, const float*, const float*, int, const int32_t*,      \
                                   const float*, int, int, int, int, const float*, float*, float*, \
-                                  hipStream_t);                                                   \
+                                  T*, hipStream_t);                                               \
   template hipError_t router_bwd<T>(const float*, const float*, const float*, const T*, int,      \
                                     int64_t, Routing, float*, T*, float*, hipStream_t);
 MKA_BWD_INST(float)

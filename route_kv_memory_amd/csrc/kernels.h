@@ -152,7 +152,7 @@ hipError_t fill_zero(float* p, int64_t n, hipStream_t s);
 template <typename T>
 hipError_t fuse_bwd(const T* x, const float* l2, const float* means, int nb_cap,
                     const int32_t* idx, const float* lam, int B, int N, int D, int R,
-                    const float* dxf, float* dx, float* dlam, hipStream_t s);
+                    const float* dxf, float* dx, float* dlam, T* xf, hipStream_t s);
 // dm [B, nbs, D]: rows of the complete blocks (D % 4 == 0), from per-range
 // partials in ``part`` (block_gather_ws_bytes()).
 size_t block_gather_ws_bytes(int B, int N, int D, int block);

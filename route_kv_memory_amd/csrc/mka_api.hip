@@ -675,12 +675,13 @@ int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const
   else
     MKA_LAUNCH("bwd/t", (transpose<float, T>(dkv, 2 * kvw, M, 2 * kvw, Mp, Mp, dkv_t, s)));
   MKA_LAUNCH("bwd/dxf", gemm_t<T>(dkv_a, 2 * kvw, wkv_t, M, D, 2 * kvw, EpiStore<float>{dxf, D}, sk, s));
-  const T* xf_src = x;
-  if (rt.ema()) {
-    MKA_LAUNCH("bwd/fuse", fuse_mix<T>(x, fwd->l2, st->block_means, st->nb_cap, fwd->idx,
-                                        fwd->lambda, B, N, D, d->top_r, rt, xf, s));
-    xf_src = xf;
-  }
+  // the fusion's adjoint (dx = l1 dxf, dlambda) and X_fused re-formed for the
+  // weight gradients (with the EMA tiers; otherwise X_fused is x), one pass
+  MKA_LAUNCH("bwd/fuse", fuse_bwd<T>(x, rt.l2() ? fwd->l2 : nullptr, st->block_means, st->nb_cap,
+                                     rt.l3() ? fwd->idx : nullptr, fwd->lambda, B, N, D,
+                                     rt.l3() ? d->top_r : 0, dxf, gr->dx, dlam,
+                                     rt.ema() ? xf : nullptr, s));
+  const T* xf_src = rt.ema() ? xf : x;
   if constexpr (kBf) {
     MKA_LAUNCH("bwd/dwk", gemm_bf16_km(dkv_a, 2 * kvw, true, xf_src, D, kvw, D, Mp, M,
                                        EpiStore<float>{gr->dw_k, D}, sk, s));
@@ -692,10 +693,7 @@ int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const
     MKA_LAUNCH("bwd/dwv", gemm_t<T>(dkv_t + static_cast<size_t>(kvw) * Mp, Mp, xf_t, kvw, D, Mp,
                                     EpiStore<float>{gr->dw_v, D}, sk, s));
   }
-  // the fusion, the EMA's adjoint and the block means' adjoint
-  MKA_LAUNCH("bwd/fuse", fuse_bwd<T>(x, rt.l2() ? fwd->l2 : nullptr, st->block_means, st->nb_cap,
-                                     rt.l3() ? fwd->idx : nullptr, fwd->lambda, B, N, D,
-                                     rt.l3() ? d->top_r : 0, dxf, gr->dx, dlam, s));
+  // the EMA's adjoint and the block means' adjoint
   if (rt.l3())
     MKA_LAUNCH("bwd/blocks", block_gather(dxf, fwd->lambda, fwd->idx, B, N, D, d->top_r, d->block,
                                           L.nbs, F(L.gather), dm, s));
