@@ -339,7 +339,7 @@ __global__ __launch_bounds__(256) void fuse_bwd_kernel(
 // a time (only t >= (blk + 1) * Bs can retrieve blk), the retrieving ones
 // compacted into LDS in order, then summed four channels per thread.
 // ---------------------------------------------------------------------------
-constexpr int kGatherTokens = 512;
+constexpr int kGatherTokens = 512, kGatherBatch = 8;
 
 template <int RMAX>
 __global__ __launch_bounds__(256) void block_gather_kernel(const float* __restrict__ dxf,
@@ -388,19 +388,20 @@ __global__ __launch_bounds__(256) void block_gather_kernel(const float* __restri
     }
     __syncthreads();
     if (c < D) {
-      // four listed tokens per step, their loads issued together (a slot past
-      // the list reads the first token with weight 0); the sum stays in list order
-      for (int k0 = 0; k0 < total; k0 += 4) {
-        float4 v[4];
-        float wk[4];
+      // kGatherBatch listed tokens per step, their loads issued together (a
+      // slot past the list reads the first token with weight 0); the sum stays
+      // in list order
+      for (int k0 = 0; k0 < total; k0 += kGatherBatch) {
+        float4 v[kGatherBatch];
+        float wk[kGatherBatch];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kGatherBatch; ++u) {
           const int k = k0 + u < total ? k0 + u : 0;
           wk[u] = k0 + u < total ? list_w[k] : 0.f;
           v[u] = *reinterpret_cast<const float4*>(dxf + (static_cast<int64_t>(b) * N + list_t[k]) * D + c);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kGatherBatch; ++u) {
           acc[0] = fmaf(wk[u], v[u].x, acc[0]);
           acc[1] = fmaf(wk[u], v[u].y, acc[1]);
           acc[2] = fmaf(wk[u], v[u].z, acc[2]);
@@ -455,19 +456,31 @@ __global__ __launch_bounds__(256) void ema_adj_pass1(const float* __restrict__ u
   store4(part + (static_cast<int64_t>(b) * n_chunks + ch) * D + c, g);
 }
 
-__global__ __launch_bounds__(256) void ema_adj_pass2(float* __restrict__ part, int N, int D,
+__global__ __launch_bounds__(64) void ema_adj_pass2(float* __restrict__ part, int N, int D,
                                                      int n_chunks, float beta) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int c = blockIdx.x * 64 + threadIdx.x;
   const int b = blockIdx.y;
   if (c >= D) return;
-  // carry into chunk ch = g at the first token of chunk ch + 1
+  // carry into chunk ch = g at the first token of chunk ch + 1; the chunk
+  // sums of kAdjBatch chunks are loaded before their sequential use
+  constexpr int kAdjBatch = 16;
+  float* pb = part + static_cast<int64_t>(b) * n_chunks * D + c;
+  const float decay_full = powf(beta, static_cast<float>(kBwdChunk));
   float carry = 0.f;
-  for (int ch = n_chunks - 1; ch >= 0; --ch) {
-    const int len = min(N, (ch + 1) * kBwdChunk) - ch * kBwdChunk;
-    float* p = part + (static_cast<int64_t>(b) * n_chunks + ch) * D + c;
-    const float local = *p;
-    *p = carry;  // now: g at the first token after the chunk
-    carry = local + powf(beta, static_cast<float>(len)) * carry;
+  for (int c1 = n_chunks - 1; c1 >= 0; c1 -= kAdjBatch) {
+    float local[kAdjBatch];
+#pragma unroll
+    for (int k = 0; k < kAdjBatch; ++k) local[k] = pb[static_cast<int64_t>(max(c1 - k, 0)) * D];
+#pragma unroll
+    for (int k = 0; k < kAdjBatch; ++k) {
+      const int ch = c1 - k;
+      if (ch >= 0) {
+        const int len = min(N, (ch + 1) * kBwdChunk) - ch * kBwdChunk;
+        pb[static_cast<int64_t>(ch) * D] = carry;  // now: g at the first token after the chunk
+        const float decay = len == kBwdChunk ? decay_full : powf(beta, static_cast<float>(len));
+        carry = local[k] + decay * carry;
+      }
+    }
   }
 }
 
@@ -706,10 +719,11 @@ hipError_t ema_adjoint_add(const float* u, const float* lam, const float* dm, in
                            int N, int D, int block, float beta, float* part, float* dx,
                            hipStream_t s) {
   const int n_chunks = (N + kBwdChunk - 1) / kBwdChunk;
-  const int cx = (D + 255) / 256, cx4 = (D / 4 + 255) / 256;  // D % 4 == 0
+  const int cx4 = (D / 4 + 255) / 256;  // D % 4 == 0
   hipLaunchKernelGGL(ema_adj_pass1, dim3(cx4, n_chunks, B), dim3(256), 0, s, u, lam + 1, N, D,
                      n_chunks, beta, part);
-  hipLaunchKernelGGL(ema_adj_pass2, dim3(cx, B), dim3(256), 0, s, part, N, D, n_chunks, beta);
+  hipLaunchKernelGGL(ema_adj_pass2, dim3((D + 63) / 64, B), dim3(64), 0, s, part, N, D, n_chunks,
+                     beta);
   hipLaunchKernelGGL(ema_adj_pass3, dim3(cx4, n_chunks, B), dim3(256), 0, s, u, lam + 1, part, dm,
                      nbs,
                      N, D, n_chunks, block, beta, dx);
