@@ -435,6 +435,9 @@ size_t attn_bwd_mfma_ws_bytes(int B, int N, int H, int G, int dh) {
   return H / G > 1 ? sizeof(float) * static_cast<size_t>(H / G) * B * N * 2 * G * dh : 0;
 }
 
+// A null dq skips the dq kernel and a null dkv the dK/dV passes, so that a
+// caller can put the two halves (independent: both only read q, K, V, dO,
+// the log-sum-exp and D) on different streams.
 hipError_t attn_bwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* d_o,
                          const float* lse, const float* dsum, int B, int N, int H, int G, int dh,
                          int64_t t_cap, float* dq, float* dkv, float* part, hipStream_t s) {
@@ -446,17 +449,22 @@ hipError_t attn_bwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, cons
   const int hpg = H / G;
   const int grid_k = ((N + 127) / 128) * B * G * hpg;
   float* dst = hpg > 1 ? part : dkv;  // per-head slices, summed below
+  if (dq != nullptr) {
+    if (dh == 128)
+      hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, dim3(grid_q), dim3(256), 0, s, q, k, v, d_o, lse,
+                         dsum, B, N, H, G, t_cap, sl2, scale, n_qblk, n_units, dq);
+    else
+      hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, dim3(grid_q), dim3(256), 0, s, q, k, v, d_o, lse,
+                         dsum, B, N, H, G, t_cap, sl2, scale, n_qblk, n_units, dq);
+  }
+  if (dkv == nullptr) return hipGetLastError();
   if (dh == 128) {
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, dim3(grid_q), dim3(256), 0, s, q, k, v, d_o, lse,
-                       dsum, B, N, H, G, t_cap, sl2, scale, n_qblk, n_units, dq);
     hipLaunchKernelGGL((attn_bwd_dkv_kernel<128, kDkvMode>), dim3(grid_k), dim3(256), 0, s, q, k, v,
                        d_o, lse, dsum, B, N, H, G, t_cap, sl2, scale, dst);
     if (kDkvMode != 0)
       hipLaunchKernelGGL((attn_bwd_dkv_kernel<128, 2>), dim3(grid_k), dim3(256), 0, s, q, k, v, d_o,
                          lse, dsum, B, N, H, G, t_cap, sl2, scale, dst);
   } else {
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, dim3(grid_q), dim3(256), 0, s, q, k, v, d_o, lse,
-                       dsum, B, N, H, G, t_cap, sl2, scale, n_qblk, n_units, dq);
     hipLaunchKernelGGL((attn_bwd_dkv_kernel<64, kDkvMode>), dim3(grid_k), dim3(256), 0, s, q, k, v,
                        d_o, lse, dsum, B, N, H, G, t_cap, sl2, scale, dst);
     if (kDkvMode != 0)

@@ -603,17 +603,28 @@ hipError_t gemm_t(const T* a, int lda, const T* b, int M, int N, int K, const Ep
   else return gemm_f32(a, lda, b, b, N, M, N, K, e, s);
 }
 
+// With ``aux`` (bf16 only; its lock held by the caller) the dq kernel runs on
+// the auxiliary stream beside the dK/dV passes; the caller joins it (records
+// aux->join there and waits for it on s) before dq is next used.
 template <typename T>
 int attn_backward_steps(const mka_dims* d, const T* q, const T* kc, const T* vc, int64_t t_cap,
                         const T* o, const float* lse, const T* d_o, float* dq, float* dkv,
-                        float* dsum, float* heads, hipStream_t s) {
+                        float* dsum, float* heads, hipStream_t s, Aux* aux) {
   const int B = d->batch, N = d->seq, H = d->n_heads, G = d->n_kv_heads, dh = d->head_dim;
   MKA_LAUNCH("bwd/prep", attn_bwd_prep<T>(o, d_o, static_cast<int64_t>(rows_of(d)) * H, dh, dsum,
                                           s));
-  if constexpr (std::is_same<T, bf16_t>::value)
-    MKA_LAUNCH("bwd/attn",
-               attn_bwd_mfma(q, kc, vc, d_o, lse, dsum, B, N, H, G, dh, t_cap, dq, dkv, heads, s));
-  else
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    hipStream_t s_dq = s;
+    if (aux != nullptr) {
+      MKA_LAUNCH("bwd/fork", hipEventRecord(aux->fork, s));
+      MKA_LAUNCH("bwd/fork", hipStreamWaitEvent(aux->stream, aux->fork, 0));
+      s_dq = aux->stream;
+    }
+    MKA_LAUNCH("bwd/attn", attn_bwd_mfma(q, kc, vc, d_o, lse, dsum, B, N, H, G, dh, t_cap, dq,
+                                         nullptr, heads, s_dq));
+    MKA_LAUNCH("bwd/attn", attn_bwd_mfma(q, kc, vc, d_o, lse, dsum, B, N, H, G, dh, t_cap,
+                                         nullptr, dkv, heads, s));
+  } else
     MKA_LAUNCH("bwd/attn",
                attn_bwd_rows<T>(q, kc, vc, d_o, lse, dsum, B, N, H, G, dh, t_cap, dq, dkv, s));
   return MKA_OK;
@@ -658,11 +669,27 @@ int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const
   const T* dkv_a = kBf ? E(L.dkv_a) : reinterpret_cast<const T*>(dkv);
   const T* dq_a = kBf ? E(L.dq_a) : reinterpret_cast<const T*>(dq);
 
-  // attention: D = rowsum(dO * O), then dq, dK, dV
+  // attention: D = rowsum(dO * O), then dq (bf16: on the auxiliary stream, beside
+  // the dK/dV passes and the work below, joined before dq is next used), dK, dV
+  Aux* aux = nullptr;
+  std::unique_lock<std::mutex> aux_guard;
+  if constexpr (kBf) {
+    int arc = MKA_OK;
+    aux = aux_for_current_device(&arc);
+    if (aux == nullptr) return arc;
+    aux_guard = std::unique_lock<std::mutex>(aux->lock);
+  }
   int rc = attn_backward_steps<T>(d, q, static_cast<const T*>(st->k_cache),
                                   static_cast<const T*>(st->v_cache), st->t_cap, o, fwd->lse, d_o,
-                                  dq, dkv, dsum, F(L.heads), s);
+                                  dq, dkv, dsum, F(L.heads), s, aux);
   if (rc) return rc;
+  auto join_dq = [&]() -> int {
+    if (aux != nullptr) {
+      MKA_LAUNCH("bwd/join", hipEventRecord(aux->join, aux->stream));
+      MKA_LAUNCH("bwd/join", hipStreamWaitEvent(s, aux->join, 0));
+    }
+    return MKA_OK;
+  };
   // [K|V] = X_fused [W_k|W_v]^T: dX_fused = dKV [W_k; W_v]; dW = dKV^T X_fused
   MKA_LAUNCH("bwd/t", (transpose<T, T>(wk, D, kvw, D, kvw, 2 * kvw, wkv_t, s)));
   MKA_LAUNCH("bwd/t", (transpose<T, T>(wv, D, kvw, D, kvw, 2 * kvw, wkv_t + kvw, s)));
@@ -702,6 +729,7 @@ int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const
   MKA_LAUNCH("bwd/ema", ema_adjoint_add(dxf, fwd->lambda, dm, L.nbs, B, N, D, d->block,
                                         d->ema_decay, part, gr->dx, s));
   // router: dz, dW_r2, dpre; dW_r1 = dpre^T q; dq += dpre W_r1
+  if ((rc = join_dq()) != MKA_OK) return rc;
   if (rt.learned()) {
     MKA_LAUNCH("bwd/pre", gemm_t<T>(q, qw, wr1, M, r, qw, EpiStore<float>{pre, r}, sk, s));
     MKA_LAUNCH("bwd/router", router_bwd<T>(fwd->lambda, dlam, pre, wr2, r, M, rt, dz, dpre,
@@ -1347,17 +1375,27 @@ int mka_attn_backward(const mka_dims* d, const void* q, const void* k_cache, con
   char* base = static_cast<char*>(ws);
   float* dsum = reinterpret_cast<float*>(base);
   float* heads = reinterpret_cast<float*>(base + round256(sizeof(float) * rows_of(d) * d->n_heads));
-  if (d->dtype == MKA_BF16)
-    return attn_backward_steps<bf16_t>(d, static_cast<const bf16_t*>(q),
-                                       static_cast<const bf16_t*>(k_cache),
-                                       static_cast<const bf16_t*>(v_cache), t_cap,
-                                       static_cast<const bf16_t*>(o), lse,
-                                       static_cast<const bf16_t*>(d_o), dq, dkv, dsum, heads, s);
+  if (d->dtype == MKA_BF16) {
+    // dq on the auxiliary stream beside the dK/dV passes, joined before returning
+    Aux* aux = aux_for_current_device(&rc);
+    if (aux == nullptr) return rc;
+    std::lock_guard<std::mutex> guard(aux->lock);
+    rc = attn_backward_steps<bf16_t>(d, static_cast<const bf16_t*>(q),
+                                     static_cast<const bf16_t*>(k_cache),
+                                     static_cast<const bf16_t*>(v_cache), t_cap,
+                                     static_cast<const bf16_t*>(o), lse,
+                                     static_cast<const bf16_t*>(d_o), dq, dkv, dsum, heads, s, aux);
+    if (rc) return rc;
+    MKA_LAUNCH("attn_bwd/join", hipEventRecord(aux->join, aux->stream));
+    MKA_LAUNCH("attn_bwd/join", hipStreamWaitEvent(s, aux->join, 0));
+    return MKA_OK;
+  }
   return attn_backward_steps<float>(d, static_cast<const float*>(q),
                                     static_cast<const float*>(k_cache),
                                     static_cast<const float*>(v_cache), t_cap,
                                     static_cast<const float*>(o), lse,
-                                    static_cast<const float*>(d_o), dq, dkv, dsum, heads, s);
+                                    static_cast<const float*>(d_o), dq, dkv, dsum, heads, s,
+                                    nullptr);
 }
 
 }  // extern "C"
