@@ -92,6 +92,17 @@ def test_backward_matches_oracle(base, mode, tiers):
         check_grad(k, to_np(g[k]), ref[k], s.dtype)
 
 
+def test_backward_two_ragged_sequences_bf16():
+    """Two 333-token bf16 sequences: the weight-gradient products reduce over
+    666 token rows (not a multiple of the 32-row slice, rows of both
+    sequences in one reduction), read K-major with the rows past the last
+    token as zeros; the dq kernel runs beside the dK/dV passes."""
+    s = SMALL["small_bf16_dh128"].replace(name="bwd_b2_ragged", batch=2, seed=14)
+    ref, out, g = run_case(s)
+    for k in GRADS:
+        check_grad(k, to_np(g[k]), ref[k], s.dtype)
+
+
 @pytest.mark.parametrize("base", ["small_bf16_dh128", "tiny_f32"])
 def test_attention_backward_entry_matches_oracle(base):
     # mka_attn_backward alone: dq, dK, dV against the oracle's attention_backward
