@@ -524,7 +524,7 @@ FullWs full_layout(const mka_dims* d, bool decode, int64_t cache_len) {
 // type's product operands (transposed ones padded to Mp = M rounded up to 32
 // tokens, the products' reduction dimension).
 struct BwdWs {
-  size_t dsum, dq, dkv, dxf, dlam, dz, dm, part, pre, heads, gather, splitk;  // float32
+  size_t dsum, dq, dkv, dxf, dlam, dz, dm, part, pre, heads, gather, splitk, splitk_aux;  // float32
   size_t dkv_a, dkv_t, wkv_t, xf, xf_t, dpre, dpre_t, q_t, wr1_t, wq_t, dq_a, dq_t, x_t;  // dtype
   size_t total;
   int Mp, nbs;
@@ -583,6 +583,9 @@ BwdWs bwd_layout(const mka_dims* d) {
                      gemm_bf16_splitk_ws_bytes(q, dd, mp)})
       if (v > sk) sk = v;
     w.splitk = take(sk);
+    // dW_k and dW_v run on the auxiliary stream beside the main stream's
+    // products: a partials region of their own
+    w.splitk_aux = take(gemm_bf16_splitk_ws_bytes(kv, dd, mp));
   }
   w.total = at;
   return w;
@@ -710,10 +713,15 @@ int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const
                                      rt.ema() ? xf : nullptr, s));
   const T* xf_src = rt.ema() ? xf : x;
   if constexpr (kBf) {
+    // on the auxiliary stream (after the dq kernel there), beside the block
+    // gather and the EMA adjoint; joined with dq before the router's steps
+    MKA_LAUNCH("bwd/fork", hipEventRecord(aux->done, s));
+    MKA_LAUNCH("bwd/fork", hipStreamWaitEvent(aux->stream, aux->done, 0));
+    float* sk_aux = F(L.splitk_aux);
     MKA_LAUNCH("bwd/dwk", gemm_bf16_km(dkv_a, 2 * kvw, true, xf_src, D, kvw, D, Mp, M,
-                                       EpiStore<float>{gr->dw_k, D}, sk, s));
+                                       EpiStore<float>{gr->dw_k, D}, sk_aux, aux->stream));
     MKA_LAUNCH("bwd/dwv", gemm_bf16_km(dkv_a + kvw, 2 * kvw, true, xf_src, D, kvw, D, Mp, M,
-                                       EpiStore<float>{gr->dw_v, D}, sk, s));
+                                       EpiStore<float>{gr->dw_v, D}, sk_aux, aux->stream));
   } else {
     MKA_LAUNCH("bwd/t", (transpose<T, T>(xf_src, D, M, D, Mp, Mp, xf_t, s)));
     MKA_LAUNCH("bwd/dwk", gemm_t<T>(dkv_t, Mp, xf_t, kvw, D, Mp, EpiStore<float>{gr->dw_k, D}, sk, s));
