@@ -583,9 +583,10 @@ BwdWs bwd_layout(const mka_dims* d) {
                      gemm_bf16_splitk_ws_bytes(q, dd, mp)})
       if (v > sk) sk = v;
     w.splitk = take(sk);
-    // dW_k and dW_v run on the auxiliary stream beside the main stream's
-    // products: a partials region of their own
-    w.splitk_aux = take(gemm_bf16_splitk_ws_bytes(kv, dd, mp));
+    // the router's pre-activation, dW_k and dW_v run on the auxiliary stream
+    // beside the main stream's products: a partials region of their own
+    w.splitk_aux = take(std::max(gemm_bf16_splitk_ws_bytes(kv, dd, mp),
+                                 gemm_bf16_splitk_ws_bytes(m, rr, q)));
   }
   w.total = at;
   return w;
@@ -686,6 +687,13 @@ int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const
                                   static_cast<const T*>(st->v_cache), st->t_cap, o, fwd->lse, d_o,
                                   dq, dkv, dsum, F(L.heads), s, aux);
   if (rc) return rc;
+  if constexpr (kBf) {
+    // the router's pre-activation needs only q and W_r1: on the auxiliary
+    // stream after the dq kernel
+    if (rt.learned())
+      MKA_LAUNCH("bwd/pre", gemm_t<T>(q, qw, wr1, M, r, qw, EpiStore<float>{pre, r},
+                                      F(L.splitk_aux), aux->stream));
+  }
   auto join_dq = [&]() -> int {
     if (aux != nullptr) {
       MKA_LAUNCH("bwd/join", hipEventRecord(aux->join, aux->stream));
@@ -739,7 +747,8 @@ int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const
   // router: dz, dW_r2, dpre; dW_r1 = dpre^T q; dq += dpre W_r1
   if ((rc = join_dq()) != MKA_OK) return rc;
   if (rt.learned()) {
-    MKA_LAUNCH("bwd/pre", gemm_t<T>(q, qw, wr1, M, r, qw, EpiStore<float>{pre, r}, sk, s));
+    if constexpr (!kBf)
+      MKA_LAUNCH("bwd/pre", gemm_t<T>(q, qw, wr1, M, r, qw, EpiStore<float>{pre, r}, sk, s));
     MKA_LAUNCH("bwd/router", router_bwd<T>(fwd->lambda, dlam, pre, wr2, r, M, rt, dz, dpre,
                                            gr->dw_r2, s));
     if constexpr (kBf) {
@@ -762,10 +771,17 @@ int backward_body(const mka_dims* d, const void* x_, const mka_weights* w, const
   if constexpr (kBf) {
     MKA_LAUNCH("bwd/cvt", (convert<float, T>(dq, static_cast<int64_t>(M) * qw,
                                              const_cast<T*>(dq_a), s)));
+    // dW_q on the auxiliary stream beside dx += dq W_q: neither splits its
+    // reduction, and each fills the other's partial last round of tiles
+    MKA_LAUNCH("bwd/fork", hipEventRecord(aux->fork, s));
+    MKA_LAUNCH("bwd/fork", hipStreamWaitEvent(aux->stream, aux->fork, 0));
+    MKA_LAUNCH("bwd/dwq", gemm_bf16_km(dq_a, qw, true, x, D, qw, D, Mp, M,
+                                       EpiStore<float>{gr->dw_q, D}, F(L.splitk_aux),
+                                       aux->stream));
     MKA_LAUNCH("bwd/dx", gemm_bf16_km(dq_a, qw, false, wq, D, M, D, qw, qw, EpiAdd{gr->dx, D}, sk,
                                       s));
-    MKA_LAUNCH("bwd/dwq", gemm_bf16_km(dq_a, qw, true, x, D, qw, D, Mp, M,
-                                       EpiStore<float>{gr->dw_q, D}, sk, s));
+    MKA_LAUNCH("bwd/join", hipEventRecord(aux->join, aux->stream));
+    MKA_LAUNCH("bwd/join", hipStreamWaitEvent(s, aux->join, 0));
   } else {
     MKA_LAUNCH("bwd/t", (transpose<T, T>(wq, D, qw, D, qw, qw, wq_t, s)));
     MKA_LAUNCH("bwd/t", (transpose<float, T>(dq, qw, M, qw, Mp, Mp, dq_t, s)));
